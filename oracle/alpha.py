@@ -1,0 +1,102 @@
+"""alpha-CROWN: projected Adam ascent on per-neuron, per-spec lower ReLU slopes.
+
+Test infrastructure only (see the package docstring).
+
+Page: "Scaling Neural Network Verification with Tensor Parallelism and Fully
+Sharded Data Parallelism" -- the per-neuron alpha tensors are ReLU slopes
+(Sec. 3, Sec. 4.3).  Reading used here (the page gives no formulas): every
+unstable ReLU neuron gets its own lower slope alpha in [0, 1] per input and
+per spec row, initialised with the adaptive CROWN slope; the objective is the
+sum of the spec lower bounds; the ascent is bias-corrected Adam followed by
+clipping to [0, 1]; the result is the best lower bound seen over the
+iterates.  The gradient is torch's reverse mode through the float64 CROWN
+evaluation of ``bounds.backward`` (at Psi = 0 the branch Psi >= 0 is taken,
+|.| has derivative sign(.) with sign(0) = 0).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from .bounds import Oracle, backward, relaxation, _domain, _t
+
+f64 = torch.float64
+
+
+def adam_ascent_step(x, g, m, v, t: int, lr: float, b1: float = 0.9, b2: float = 0.999,
+                     eps: float = 1e-8):
+    """One bias-corrected Adam step that increases the objective, then clip to [0, 1].
+    Returns new (x, m, v)."""
+    m = b1 * m + (1 - b1) * g
+    v = b2 * v + (1 - b2) * g * g
+    mh = m / (1 - b1 ** t)
+    vh = v / (1 - b2 ** t)
+    x = (x + lr * mh / (vh.sqrt() + eps)).clamp(0.0, 1.0)
+    return x, m, v
+
+
+def alpha_init(net: Oracle, lo, hi, b: int, m: int):
+    """Adaptive CROWN slopes broadcast over the m spec rows, one tensor per ReLU node."""
+    out = {}
+    for r in net.relu_nodes():
+        z = net.nodes[r].inputs[0]
+        a, _, _, _ = relaxation(lo[z][b], hi[z][b])
+        out[r] = a.unsqueeze(0).expand((m,) + tuple(a.shape)).clone()
+    return out
+
+
+def alpha_crown(wl, lo, hi, steps: int = None, lr: float = None, stop: int = 0,
+                batch_idx=None, b1=0.9, b2=0.999, adam_eps=1e-8):
+    """Lower bounds of C f(x) over the iterates of alpha optimisation.
+
+    For each input: `steps` rounds of (evaluate lb_t, gradient of sum(lb_t), Adam
+    ascent + clip), then one final evaluation.  Returns dict with
+    "lb_steps" [steps+1][B][m], "best" [B][m] (max over the iterates) and the
+    final alphas per input.
+    """
+    net = Oracle(wl.nodes)
+    steps = wl.alpha_steps if steps is None else steps
+    lr = wl.alpha_lr if lr is None else lr
+    C = _t(wl.C)
+    B, m = C.shape[0], C.shape[1]
+    batch_idx = range(B) if batch_idx is None else batch_idx
+    L = len(net.nodes) - 1
+    lb_steps = torch.full((steps + 1, B, m), float("nan"), dtype=f64)
+    alphas_out = {}
+    for b in batch_idx:
+        dc, dr = _domain(net, lo, hi, wl.x0, wl.eps, b, stop)
+        al = alpha_init(net, lo, hi, b, m)
+        mom = {k: torch.zeros_like(v) for k, v in al.items()}
+        vel = {k: torch.zeros_like(v) for k, v in al.items()}
+        for t in range(1, steps + 1):
+            leaf = {k: v.clone().requires_grad_(True) for k, v in al.items()}
+            lb = backward(net, lo, hi, b, L, C[b], stop, dc, dr, alpha=leaf)
+            lb_steps[t - 1, b] = lb.detach()
+            lb.sum().backward()
+            for k in al:
+                g = leaf[k].grad if leaf[k].grad is not None else torch.zeros_like(al[k])
+                al[k], mom[k], vel[k] = adam_ascent_step(al[k], g, mom[k], vel[k], t, lr, b1, b2, adam_eps)
+        with torch.no_grad():
+            lb_steps[steps, b] = backward(net, lo, hi, b, L, C[b], stop, dc, dr, alpha=al)
+        alphas_out[b] = al
+    best = lb_steps.max(dim=0).values
+    return {"lb_steps": lb_steps, "best": best, "alpha": alphas_out}
+
+
+def alpha_gradient(wl, lo, hi, b: int, alpha: dict, stop: int = 0):
+    """(lb, d sum(lb) / d alpha) for one input at the given slopes (float64 autograd)."""
+    net = Oracle(wl.nodes)
+    C = _t(wl.C)
+    dc, dr = _domain(net, lo, hi, wl.x0, wl.eps, b, stop)
+    leaf = {k: v.clone().requires_grad_(True) for k, v in alpha.items()}
+    lb = backward(net, lo, hi, b, len(net.nodes) - 1, C[b], stop, dc, dr, alpha=leaf)
+    lb.sum().backward()
+    return lb.detach(), {k: (v.grad if v.grad is not None else torch.zeros_like(v)) for k, v in leaf.items()}
+
+
+def evaluate(wl, lo, hi, b: int, alpha: dict, stop: int = 0) -> torch.Tensor:
+    net = Oracle(wl.nodes)
+    C = _t(wl.C)
+    dc, dr = _domain(net, lo, hi, wl.x0, wl.eps, b, stop)
+    with torch.no_grad():
+        return backward(net, lo, hi, b, len(net.nodes) - 1, C[b], stop, dc, dr, alpha=alpha)
