@@ -1,0 +1,197 @@
+"""Benchmark of the bound-propagation hot path on one MI355X.
+
+One step = one whole bound computation for one batch: IBP of every node, the
+intermediate bounds of every ReLU input (CROWN back-substitution per layer for
+the MLP workloads), and the spec bounds by IBP and by CROWN.  Inputs are
+resident in HBM before the timed region.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload N] [--no-cpu]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CROWN bound-propagation TFLOP/s (fp32, % MFMA peak) + verified specs/sec"
+PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix peak (AMD public spec)
+
+
+def _mac_per_row(nd, nodes):
+    """Forward multiply-adds of one affine node for one row of Lambda."""
+    if nd.op == "linear":
+        return nd.weight.shape[0] * nd.weight.shape[1]
+    co, ci, kh, kw = nd.weight.shape
+    return co * ci * kh * kw * nd.shape[1] * nd.shape[2]
+
+
+def _active(nodes, start, stop):
+    act, stack = set(), [start]
+    while stack:
+        k = stack.pop()
+        if k in act or k < stop:
+            continue
+        act.add(k)
+        if k != stop and k != 0:
+            stack.extend(nodes[k].inputs)
+    return act
+
+
+def _src(nodes, k):
+    while nodes[k].op == "flatten":
+        k = nodes[k].inputs[0]
+    return k
+
+
+def algorithmic_flops(wl):
+    """FLOPs the method itself performs for the whole batch (no padding, no tile waste):
+    2 * rows * multiply-adds of each affine node a row of Lambda passes through; the
+    first step of identity rows through a Linear (rows of +-W) costs nothing; IBP is
+    two passes (centre and radius) of the forward multiply-adds."""
+    nodes, B, m = wl.nodes, wl.batch, wl.m
+    total = {"ibp": 0.0, "intermediate": 0.0, "spec": 0.0}
+    for nd in nodes:
+        if nd.op in ("linear", "conv"):
+            total["ibp"] += 2 * 2 * _mac_per_row(nd, nodes) * B
+    L = len(nodes) - 1
+    # spec IBP: C folded into the last Linear
+    total["spec"] += 2 * (2 * m * B) * _mac_per_row(nodes[L], nodes)
+    stop = 0 if wl.intermediate != "hybrid" else wl.region_start
+    if wl.intermediate != "ibp":
+        for r, nd in enumerate(nodes):
+            if nd.op != "relu":
+                continue
+            z = nd.inputs[0]
+            zn = nodes[z]
+            if z <= stop or (zn.op in ("linear", "conv") and _src(nodes, zn.inputs[0]) == stop):
+                continue
+            rows = 2 * zn.size * B
+            for k in _active(nodes, z, stop):
+                if nodes[k].op not in ("linear", "conv"):
+                    continue
+                if k == z and zn.op == "linear":
+                    continue           # identity rows through their own Linear: rows of +-W
+                total["intermediate"] += 2 * rows * _mac_per_row(nodes[k], nodes)
+    rows = 2 * m * B
+    for k in _active(nodes, L, stop):
+        if nodes[k].op in ("linear", "conv"):
+            total["spec"] += 2 * rows * _mac_per_row(nodes[k], nodes)
+    total["all"] = total["ibp"] + total["intermediate"] + total["spec"]
+    return total
+
+
+def cpu_baseline(wl, flops_total, budget_s=12.0):
+    """The float64 oracle on the host cores over the first k inputs (k grows until
+    about budget_s of CPU work), scaled to TFLOP/s of the same algorithmic work."""
+    import torch
+    from oracle import crown_bounds
+    k, elapsed = 0, 0.0
+    while k < wl.batch and elapsed < budget_s:
+        t0 = time.perf_counter()
+        crown_bounds(wl, batch_idx=[k])
+        elapsed += time.perf_counter() - t0
+        k += 1
+    per_input = flops_total / wl.batch
+    return {"value": per_input * k / elapsed / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(),
+            "kind": "oracle", "specs_per_s": k * wl.m / elapsed,
+            "sample": f"first {k} of {wl.batch} inputs, all {wl.m} specs, float64 torch-CPU oracle, {elapsed:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the bound computation is not "
+              "sharded across GPUs in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as wk
+    import linear_bound_propagation_amd as lbp
+
+    wl = wk.config(args.workload)
+    print(f"[bench] workload {wl.name}: building device copies", file=sys.stderr, flush=True)
+    net, x, C = lbp.prepare(wl, "cuda:0")
+    lo, hi = net.alloc_bounds(wl.batch)
+    out = {"lo": lo, "hi": hi}
+    for k in ("ibp_lb", "ibp_ub", "lb", "ub"):
+        out[k] = torch.empty(wl.batch, wl.m, device=net.device)
+    ws_bytes = net.workspace_size(wl.batch, wl.m, wl.intermediate, wl.region_start or 0)
+    free = torch.cuda.mem_get_info()[0]
+    ws = net.workspace(min(ws_bytes, int(free * 0.85)))
+    step = lambda: lbp.crown(net, x, float(wl.eps), C, wl.intermediate, wl.region_start, ws=ws, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    lbp.profile_start()
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    k_ms, k_flops, k_launches = lbp.profile_stop()
+    ms = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    fl = algorithmic_flops(wl)
+    tflops = fl["all"] / (ms * 1e-3) / 1e12
+    lb = out["lb"]
+    verified = float((lb > 0).all(dim=1).float().mean().item())
+    achieved = k_flops / (k_ms * 1e-3) / 1e12 if k_ms > 0 else None
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "specs": wl.m, "eps": float(wl.eps),
+                   "intermediate": wl.intermediate,
+                   "algorithmic_tflop_per_step": round(fl["all"] / 1e12, 4)},
+        "frac_of_fp32_mfma_peak": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4),
+        "specs_per_s": round(wl.batch * wl.m / (ms * 1e-3), 1),
+        "verified_frac": verified,
+        "roofline": {
+            "kernel": "back-substitution GEMM with ReLU-relaxation epilogue",
+            "bound": "mfma",
+            "achieved": None if achieved is None else round(achieved, 3),
+            "peak": PEAK_FP32_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": None if achieved is None else round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
+            "traffic": None,
+            "launches": k_launches,
+            "avg_launch_ms": round(k_ms / max(k_launches, 1), 4),
+            "alg_flop_per_launch": k_flops / max(k_launches, 1),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        print("[bench] timing the float64 oracle on the host cores", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl, fl["all"])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

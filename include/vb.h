@@ -1,0 +1,180 @@
+/* vb.h -- C ABI of the MI355X linear bound propagation library (libvbprop.so).
+ *
+ * Computes certified output bounds of ReLU networks over an input domain with
+ * the bound-propagation algorithms named in "Scaling Neural Network
+ * Verification with Tensor Parallelism and Fully Sharded Data Parallelism"
+ * (Sec. 1, problem definition: a network, an input domain and a property; IBP,
+ * CROWN and alpha-CROWN with their linear relaxation matrices A; Sec. 2.1:
+ * relaxation slopes from intermediate bounds; Sec. 2.2: bound propagation
+ * through convolutions; Sec. 3 / Sec. 4.3: per-neuron alpha slope tensors).
+ *
+ * Conventions shared by every call
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    keeps no pointer after a call returns and allocates no device memory:
+ *    scratch space comes from the caller's workspace (`ws`, `ws_bytes`).
+ *  - Every call validates its arguments on the host first.  On an error
+ *    nothing is enqueued and a negative status is returned; vb_last_error()
+ *    then describes it.  Otherwise the work is enqueued on `stream` (a
+ *    hipStream_t, passed as void*) and the call returns without synchronising.
+ *    Asynchronous device faults surface at the caller's next synchronisation.
+ *  - Results are deterministic: identical inputs give bitwise-identical
+ *    outputs (all reductions run in a fixed order, no float atomics).
+ *  - All data is float32.  Flat tensors are [batch][n].  Spatial tensors are
+ *    channels-last: [batch][h][w][c].  A FLATTEN node reinterprets a
+ *    [h][w][c] tensor as a vector in (h, w, c) order (no data movement).
+ *  - Linear weights are [n_out][n_in] row-major.  Conv2d weights are
+ *    [kh][kw][c_out][c_in] ("HWOI").  Biases are [n_out] / [c_out] or NULL.
+ *  - The input domain is the L-inf box |x - x_center| <= r with
+ *    r = x_radius[b][i] if x_radius is non-NULL, else the scalar eps.
+ */
+#ifndef VB_H
+#define VB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t vb_status;
+#define VB_OK            0
+#define VB_EINVAL       (-1)  /* null pointer, bad enum value, non-positive size */
+#define VB_ESHAPE       (-2)  /* inconsistent graph or shapes                     */
+#define VB_ENOMEM       (-3)  /* workspace too small (see vb_workspace_size)      */
+#define VB_EDEVICE      (-4)  /* a HIP call or kernel launch failed               */
+#define VB_EUNSUPPORTED (-5)  /* graph pattern this library does not handle       */
+
+/* Node kinds.  Nodes are listed in topological order; node 0 is the input. */
+#define VB_INPUT   0
+#define VB_LINEAR  1
+#define VB_CONV2D  2
+#define VB_RELU    3
+#define VB_ADD     4   /* elementwise sum of in0 and in1 (same shape)          */
+#define VB_GAP     5   /* global average pool [h][w][c] -> [c]                  */
+#define VB_FLATTEN 6   /* [h][w][c] -> [h*w*c]                                  */
+
+typedef struct {
+  int32_t op;                 /* VB_*                                            */
+  int32_t in0, in1;           /* producer node indices, -1 if unused             */
+  int32_t c, h, w;            /* output shape; flat nodes have h = w = 1         */
+  int32_t kh, kw, stride, pad;/* conv2d only (zero padding, same in both dims)   */
+  const float* weight;        /* device, borrowed for the call                   */
+  const float* bias;          /* device or NULL                                  */
+} vb_node;
+
+typedef struct {
+  int32_t n_nodes;
+  const vb_node* nodes;       /* host array, borrowed for the call               */
+} vb_graph;
+
+/* Intermediate-bound methods for vb_crown. */
+#define VB_METHOD_IBP    0   /* IBP bounds feed every ReLU relaxation             */
+#define VB_METHOD_CROWN  1   /* CROWN bounds for every ReLU input (IBP where the  */
+                             /* input is one affine step from the domain)         */
+#define VB_METHOD_HYBRID 2   /* IBP up to node region_start, CROWN after it with  */
+                             /* region_start's IBP box as the domain              */
+
+/* Thread-local description of the last error on this thread. */
+const char* vb_last_error(void);
+
+/* Bytes of workspace that lets every call below run on the whole batch at once
+ * for this graph, batch size and spec count m.  A smaller workspace is accepted
+ * as long as one batch element fits: the library then processes the batch in
+ * chunks (same results). */
+vb_status vb_workspace_size(const vb_graph* g, int32_t batch, int32_t m, int32_t method,
+                            int32_t region_start, size_t* bytes);
+
+/* IBP (interval bound propagation, centre/radius form; Sec. 1 and Sec. 2.1 of
+ * the page).  For every non-input node k with node_lo[k] != NULL, writes its
+ * interval bounds [batch][size_k].  Affine nodes compute c' = W c + b and
+ * r' = |W| r from (c, r) = ((l+u)/2, (u-l)/2) of their producer (the input
+ * node hands over (x_center, radius) directly); ReLU clamps at 0; ADD sums;
+ * GAP averages.  Every node that feeds another node must have bounds storage
+ * (node_lo[k] and node_hi[k] non-NULL) except the input node.
+ * If C != NULL (C: [batch][m][n_out] over the last node, which must be
+ * LINEAR), also writes spec bounds spec_lo/spec_hi [batch][m] with C folded
+ * into the last layer. */
+vb_status vb_ibp(const vb_graph* g, int32_t batch,
+                 const float* x_center, const float* x_radius, float eps,
+                 float* const* node_lo, float* const* node_hi,
+                 const float* C, int32_t m, float* spec_lo, float* spec_hi,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* One CROWN back-substitution (Sec. 1: the A matrices; Sec. 2.1: slopes from
+ * intermediate bounds).  Rows over node `start`:
+ *   C == NULL: identity rows; writes node bounds lb = l_start, ub = u_start,
+ *              each [batch][size_start] (lb = lb(I), ub = -lb(-I));
+ *   C != NULL: spec rows C [batch][m][size_start]; writes lb = lb(C) and
+ *              ub = -lb(-C), each [batch][m].
+ * The rows are pushed to `stop` through every node in between using the ReLU
+ * relaxation of node_lo/node_hi of each ReLU input (adaptive lower slope),
+ * then concretised over the domain: the input box if stop == 0, else the box
+ * [node_lo[stop], node_hi[stop]].  lb or ub may be NULL.
+ * If A_out != NULL, the linear bounds over `stop` are returned instead of being
+ * concretised: A_out [batch][2R][size_stop] and bias_out [batch][2R] with
+ * R = m (spec) or size_start (identity); the first R rows bound +rows from
+ * below, the last R bound -rows from below. */
+vb_status vb_crown_backward(const vb_graph* g, int32_t batch, int32_t start, int32_t stop,
+                            const float* C, int32_t m,
+                            const float* const* node_lo, const float* const* node_hi,
+                            const float* x_center, const float* x_radius, float eps,
+                            float* lb, float* ub, float* A_out, float* bias_out,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Concretisation of linear bounds over a box (Sec. 1: the A matrices).
+ * A: [rows][n], bias: [rows] or NULL; row r belongs to batch element
+ * r / rows_per_batch; center, radius: [batch][n] (radius NULL -> scalar eps).
+ * lb[r] = A c - |A| r + bias, ub[r] = A c + |A| r + bias; either may be NULL. */
+vb_status vb_concretize(int32_t rows, int32_t n, int32_t rows_per_batch,
+                        const float* A, const float* bias,
+                        const float* center, const float* radius, float eps,
+                        float* lb, float* ub, void* stream);
+
+/* One alpha-CROWN step on the lower bounds of spec rows C [batch][m][n_out]
+ * (Sec. 3 and Sec. 4.3 of the page: per-neuron alpha slope tensors).
+ * alpha, adam_m, adam_v: per node, NULL except for ReLU nodes, each
+ * [batch][m][size_k] (one lower slope per input, spec row and neuron; only the
+ * unstable neurons' entries are read or changed).  Evaluates the CROWN lower
+ * bound with these slopes into lb_out [batch][m] and folds it into best_lb
+ * (elementwise max; best_lb may be NULL).  If step >= 1, then also takes one
+ * bias-corrected Adam ascent step (step = Adam's 1-based t, learning rate lr,
+ * beta1, beta2, adam_eps) on sum(lb) and clips alpha to [0, 1].  step == 0
+ * only evaluates.  The domain is the input box (stop = node 0). */
+vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float* C, int32_t m,
+                        const float* const* node_lo, const float* const* node_hi,
+                        const float* x_center, const float* x_radius, float eps,
+                        float* const* alpha, float* const* adam_m, float* const* adam_v,
+                        int32_t step, float lr, float beta1, float beta2, float adam_eps,
+                        float* lb_out, float* best_lb,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* The whole bound computation for one batch: IBP for every node, then the
+ * intermediate bounds of every ReLU input by `method`, overwriting node_lo /
+ * node_hi of those nodes in topological order, then the spec bounds of C by
+ * IBP (ibp_lb/ibp_ub, may be NULL) and by CROWN (lb/ub).  node_lo / node_hi
+ * must be given for every non-input node. */
+vb_status vb_crown(const vb_graph* g, int32_t batch,
+                   const float* x_center, const float* x_radius, float eps,
+                   int32_t method, int32_t region_start,
+                   float* const* node_lo, float* const* node_hi,
+                   const float* C, int32_t m,
+                   float* ibp_lb, float* ibp_ub, float* lb, float* ub,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Measurement of the back-substitution GEMM (the dominant kernel).
+ * vb_profile_start() begins recording a pair of HIP events around every
+ * back-substitution GEMM launch whose epilogue applies the ReLU relaxation,
+ * on the stream of that launch, together with its algorithmic FLOPs
+ * (2 x rows x multiply-adds of the layer, without padding or tile waste).
+ * vb_profile_stop() stops recording, waits for the recorded events and
+ * returns the summed kernel time (ms), summed FLOPs and launch count.
+ * Not thread-safe; meant for benchmarks. */
+vb_status vb_profile_start(void);
+vb_status vb_profile_stop(double* ms, double* flops, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VB_H */

@@ -1,0 +1,283 @@
+"""MI355X-native linear bound propagation (IBP, CROWN, alpha-CROWN).
+
+Thin ctypes binding over libvbprop.so (the C ABI declared in include/vb.h).
+PyTorch is used only for device memory and the current HIP stream; every
+step of the bound computation runs in the library's HIP kernels.  The
+binding marshals arguments: it lays a network out in the library's formats
+(channels-last activations, [kh][kw][c_out][c_in] conv weights, Linear
+columns after a flatten in (h, w, c) order) and passes device pointers.
+
+The shared library is loaded on first use; if it is missing, that first call
+raises ImportError: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvbprop.so")
+
+VB_INPUT, VB_LINEAR, VB_CONV2D, VB_RELU, VB_ADD, VB_GAP, VB_FLATTEN = range(7)
+METHODS = {"ibp": 0, "crown": 1, "hybrid": 2}
+STATUS = {0: "VB_OK", -1: "VB_EINVAL", -2: "VB_ESHAPE", -3: "VB_ENOMEM", -4: "VB_EDEVICE",
+          -5: "VB_EUNSUPPORTED"}
+_OPS = {"input": VB_INPUT, "linear": VB_LINEAR, "conv": VB_CONV2D, "relu": VB_RELU, "add": VB_ADD,
+        "gap": VB_GAP, "flatten": VB_FLATTEN}
+
+EXPORTS = ["vb_last_error", "vb_workspace_size", "vb_ibp", "vb_crown_backward", "vb_concretize",
+           "vb_alpha_step", "vb_crown", "vb_profile_start", "vb_profile_stop"]
+
+
+class vb_node(ctypes.Structure):
+    _fields_ = [("op", ctypes.c_int32), ("in0", ctypes.c_int32), ("in1", ctypes.c_int32),
+                ("c", ctypes.c_int32), ("h", ctypes.c_int32), ("w", ctypes.c_int32),
+                ("kh", ctypes.c_int32), ("kw", ctypes.c_int32), ("stride", ctypes.c_int32),
+                ("pad", ctypes.c_int32), ("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
+
+
+class vb_graph(ctypes.Structure):
+    _fields_ = [("n_nodes", ctypes.c_int32), ("nodes", ctypes.POINTER(vb_node))]
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built: run `python -m linear_bound_propagation_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    PP = ctypes.POINTER(ctypes.c_void_p)
+    G = ctypes.POINTER(vb_graph)
+    i32, f32, sz = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.vb_last_error.restype = ctypes.c_char_p
+    lib.vb_last_error.argtypes = []
+    lib.vb_workspace_size.restype = i32
+    lib.vb_workspace_size.argtypes = [G, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.vb_ibp.restype = i32
+    lib.vb_ibp.argtypes = [G, i32, P, P, f32, PP, PP, P, i32, P, P, P, sz, P]
+    lib.vb_crown_backward.restype = i32
+    lib.vb_crown_backward.argtypes = [G, i32, i32, i32, P, i32, PP, PP, P, P, f32, P, P, P, P, P, sz, P]
+    lib.vb_concretize.restype = i32
+    lib.vb_concretize.argtypes = [i32, i32, i32, P, P, P, P, f32, P, P, P]
+    lib.vb_alpha_step.restype = i32
+    lib.vb_alpha_step.argtypes = [G, i32, P, i32, PP, PP, P, P, f32, PP, PP, PP, i32, f32, f32, f32, f32,
+                                  P, P, P, sz, P]
+    lib.vb_crown.restype = i32
+    lib.vb_crown.argtypes = [G, i32, P, P, f32, i32, i32, PP, PP, P, i32, P, P, P, P, P, sz, P]
+    lib.vb_profile_start.restype = i32
+    lib.vb_profile_start.argtypes = []
+    lib.vb_profile_stop.restype = i32
+    lib.vb_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_int64)]
+    return lib
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libvbprop.so (loaded once; raises ImportError if it is not built)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = load_library()
+    return _LIB
+
+
+class VBError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        msg = lib().vb_last_error().decode(errors="replace")
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _check(status: int, fn: str):
+    if status != 0:
+        raise VBError(status, fn)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _ptr_array(ts: Sequence[Optional[torch.Tensor]]):
+    arr = (ctypes.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = None if t is None else t.data_ptr()
+    return arr
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _f32(x, device):
+    return torch.as_tensor(np.ascontiguousarray(x), dtype=torch.float32, device=device)
+
+
+def to_channels_last(x: np.ndarray) -> np.ndarray:
+    """[B][C][H][W] -> [B][H][W][C] (flat [B][n] unchanged)."""
+    x = np.asarray(x)
+    return np.ascontiguousarray(x.transpose(0, 2, 3, 1)) if x.ndim == 4 else x
+
+
+def from_channels_last(t: torch.Tensor, shape) -> torch.Tensor:
+    """Device bounds [B][h*w*c] (or [B][h][w][c]) of a node with shape (C, H, W) -> [B][C][H][W]."""
+    if len(shape) == 1:
+        return t.reshape(t.shape[0], -1)
+    c, h, w = shape
+    return t.reshape(t.shape[0], h, w, c).permute(0, 3, 1, 2)
+
+
+class DeviceNet:
+    """A network from ``workloads`` laid out on the device in the library's formats."""
+
+    def __init__(self, nodes, device="cuda"):
+        self.device = torch.device(device)
+        self.shapes = [tuple(n.shape) for n in nodes]
+        self.ops = [n.op for n in nodes]
+        self.inputs = [tuple(n.inputs) for n in nodes]
+        self._keep: List[torch.Tensor] = []
+        arr = (vb_node * len(nodes))()
+        for k, n in enumerate(nodes):
+            v = arr[k]
+            v.op = _OPS[n.op]
+            v.in0 = n.inputs[0] if len(n.inputs) > 0 else -1
+            v.in1 = n.inputs[1] if len(n.inputs) > 1 else -1
+            if len(n.shape) == 3:
+                v.c, v.h, v.w = n.shape
+            else:
+                v.c, v.h, v.w = n.shape[0], 1, 1
+            w = b = None
+            if n.op == "linear":
+                W = np.asarray(n.weight, dtype=np.float32)
+                src = n.inputs[0]
+                while nodes[src].op == "flatten":
+                    src = nodes[src].inputs[0]
+                if len(nodes[src].shape) == 3:      # columns (c, h, w) -> (h, w, c)
+                    c_, h_, w_ = nodes[src].shape
+                    W = W.reshape(W.shape[0], c_, h_, w_).transpose(0, 2, 3, 1).reshape(W.shape[0], -1)
+                w = _f32(W, self.device)
+                b = _f32(n.bias, self.device)
+            elif n.op == "conv":
+                W = np.asarray(n.weight, dtype=np.float32)       # OIHW -> [kh][kw][O][I]
+                v.kh, v.kw = W.shape[2], W.shape[3]
+                v.stride, v.pad = n.stride, n.pad
+                w = _f32(W.transpose(2, 3, 0, 1), self.device)
+                b = _f32(n.bias, self.device)
+            if w is not None:
+                self._keep += [w, b]
+                v.weight = w.data_ptr()
+                v.bias = b.data_ptr()
+        self.nodes_c = arr
+        self.graph = vb_graph(len(nodes), arr)
+        self.gp = ctypes.pointer(self.graph)
+        self.n_nodes = len(nodes)
+        self.sizes = [int(np.prod(s)) for s in self.shapes]
+
+    # ------------------------------------------------------------------
+    def alloc_bounds(self, batch: int):
+        lo = [None] + [torch.empty(batch, s, device=self.device) for s in self.sizes[1:]]
+        hi = [None] + [torch.empty(batch, s, device=self.device) for s in self.sizes[1:]]
+        return lo, hi
+
+    def workspace_size(self, batch: int, m: int, method: str = "crown", region_start: int = 0) -> int:
+        out = ctypes.c_size_t(0)
+        _check(lib().vb_workspace_size(self.gp, batch, m, METHODS[method], region_start or 0, ctypes.byref(out)),
+               "vb_workspace_size")
+        return int(out.value)
+
+    def workspace(self, nbytes: int) -> torch.Tensor:
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+
+
+def ibp(net: DeviceNet, x_center: torch.Tensor, eps: float, lo=None, hi=None, C: torch.Tensor = None,
+        spec_lo=None, spec_hi=None, ws: torch.Tensor = None, x_radius: torch.Tensor = None):
+    batch = x_center.shape[0]
+    if lo is None:
+        lo, hi = net.alloc_bounds(batch)
+    m = 0 if C is None else C.shape[1]
+    if C is not None and spec_lo is None:
+        spec_lo = torch.empty(batch, m, device=net.device)
+        spec_hi = torch.empty(batch, m, device=net.device)
+    _check(lib().vb_ibp(net.gp, batch, _ptr(x_center), _ptr(x_radius), float(eps), _ptr_array(lo), _ptr_array(hi),
+                       _ptr(C), m, _ptr(spec_lo), _ptr(spec_hi), _ptr(ws), 0 if ws is None else ws.numel(),
+                       _stream()), "vb_ibp")
+    return lo, hi, spec_lo, spec_hi
+
+
+def crown_backward(net: DeviceNet, start: int, stop: int, lo, hi, x_center: torch.Tensor, eps: float,
+                   ws: torch.Tensor, C: torch.Tensor = None, lb=None, ub=None, x_radius=None):
+    batch = lo[start].shape[0]
+    R = C.shape[1] if C is not None else net.sizes[start]
+    if lb is None:
+        lb = torch.empty(batch, R, device=net.device)
+        ub = torch.empty(batch, R, device=net.device)
+    _check(lib().vb_crown_backward(net.gp, batch, start, stop, _ptr(C), 0 if C is None else C.shape[1],
+                                  _ptr_array(lo), _ptr_array(hi), _ptr(x_center), _ptr(x_radius), float(eps),
+                                  _ptr(lb), _ptr(ub), None, None, _ptr(ws), ws.numel(), _stream()),
+           "vb_crown_backward")
+    return lb, ub
+
+
+def concretize(A: torch.Tensor, bias: Optional[torch.Tensor], center: torch.Tensor, eps: float, rows_per_batch: int,
+               radius: torch.Tensor = None, lb=None, ub=None):
+    rows, n = A.shape
+    if lb is None:
+        lb = torch.empty(rows, device=A.device)
+        ub = torch.empty(rows, device=A.device)
+    _check(lib().vb_concretize(rows, n, rows_per_batch, _ptr(A), _ptr(bias), _ptr(center), _ptr(radius), float(eps),
+                              _ptr(lb), _ptr(ub), _stream()), "vb_concretize")
+    return lb, ub
+
+
+def crown(net: DeviceNet, x_center: torch.Tensor, eps: float, C: torch.Tensor, method: str = "crown",
+          region_start: Optional[int] = None, ws: torch.Tensor = None, out=None, x_radius=None):
+    """Whole pipeline (vb_crown).  Returns dict of device tensors:
+    lo/hi per node (channels-last), ibp_lb/ibp_ub and lb/ub [B][m]."""
+    batch = x_center.shape[0]
+    m = C.shape[1]
+    if out is None:
+        lo, hi = net.alloc_bounds(batch)
+        out = {"lo": lo, "hi": hi}
+        for k in ("ibp_lb", "ibp_ub", "lb", "ub"):
+            out[k] = torch.empty(batch, m, device=net.device)
+    if ws is None:
+        ws = net.workspace(net.workspace_size(batch, m, method, region_start or 0))
+    _check(lib().vb_crown(net.gp, batch, _ptr(x_center), _ptr(x_radius), float(eps), METHODS[method],
+                         region_start or 0, _ptr_array(out["lo"]), _ptr_array(out["hi"]), _ptr(C), m,
+                         _ptr(out["ibp_lb"]), _ptr(out["ibp_ub"]), _ptr(out["lb"]), _ptr(out["ub"]), _ptr(ws),
+                         ws.numel(), _stream()), "vb_crown")
+    return out
+
+
+def alpha_step(net: DeviceNet, C: torch.Tensor, lo, hi, x_center: torch.Tensor, eps: float, alpha, adam_m, adam_v,
+               step: int, lr: float, lb_out: torch.Tensor, best_lb: Optional[torch.Tensor], ws: torch.Tensor,
+               beta1: float = 0.9, beta2: float = 0.999, adam_eps: float = 1e-8, x_radius=None):
+    batch, m = C.shape[0], C.shape[1]
+    _check(lib().vb_alpha_step(net.gp, batch, _ptr(C), m, _ptr_array(lo), _ptr_array(hi), _ptr(x_center),
+                              _ptr(x_radius), float(eps), _ptr_array(alpha), _ptr_array(adam_m), _ptr_array(adam_v),
+                              step, lr, beta1, beta2, adam_eps, _ptr(lb_out), _ptr(best_lb), _ptr(ws), ws.numel(),
+                              _stream()), "vb_alpha_step")
+    return lb_out
+
+
+def profile_start():
+    _check(lib().vb_profile_start(), "vb_profile_start")
+
+
+def profile_stop():
+    """(total ms, total algorithmic FLOPs, launches) of the relaxation-epilogue GEMMs since profile_start()."""
+    ms, fl, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
+    _check(lib().vb_profile_stop(ctypes.byref(ms), ctypes.byref(fl), ctypes.byref(n)), "vb_profile_stop")
+    return ms.value, fl.value, n.value
+
+
+def prepare(wl, device="cuda"):
+    """Device copies of a workload's network, input centres and spec matrix."""
+    net = DeviceNet(wl.nodes, device)
+    x = _f32(to_channels_last(wl.x0).reshape(wl.batch, -1), net.device)
+    C = _f32(wl.C, net.device)
+    return net, x, C

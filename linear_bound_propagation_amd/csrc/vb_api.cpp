@@ -1,0 +1,1042 @@
+// C ABI entry points and the host-side planner of the bound propagation library.
+//
+// The planner validates the graph, sizes the caller's workspace, and walks
+// the graph: forward for IBP, backward for CROWN back-substitution ("Scaling
+// Neural Network Verification with Tensor Parallelism and Fully Sharded Data
+// Parallelism", Sec. 1: the A matrices; Sec. 2.1: relaxation slopes from
+// intermediate bounds; Sec. 2.2: convolutions).  For every Linear / Conv node
+// on the backward path it chooses the GEMM epilogue: relax into the ReLU below
+// (when this node is that ReLU's last pending consumer), concretise at the
+// domain node, or store the product for a later accumulation.  Lambda buffers
+// come from a small reference-counted pool inside the workspace; when the
+// workspace cannot hold the whole batch, the batch is processed in chunks.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "vb.h"
+#include "vb_internal.h"
+
+using namespace vb;
+
+namespace {
+
+thread_local std::string g_err;
+
+vb_status fail(vb_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+#define HIPCHK(expr)                                                                    \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess) return fail(VB_EDEVICE, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr int NPOOL = 4;
+constexpr size_t ALIGN = 256;
+
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct NodeInfo {
+  int op, in0, in1;
+  int c, h, w;
+  long long size;
+  int kh, kw, stride, pad;
+  const float* W;
+  const float* b;
+  std::vector<int> cons;  // consumers (direct)
+};
+
+struct Graph {
+  std::vector<NodeInfo> n;
+  int L = 0;  // last node
+};
+
+vb_status parse_graph(const vb_graph* g, Graph& G) {
+  if (!g || !g->nodes || g->n_nodes < 2) return fail(VB_EINVAL, "graph is NULL or has fewer than 2 nodes");
+  const int N = g->n_nodes;
+  G.n.resize(N);
+  for (int k = 0; k < N; ++k) {
+    const vb_node& s = g->nodes[k];
+    NodeInfo& d = G.n[k];
+    d.op = s.op;
+    d.in0 = s.in0;
+    d.in1 = s.in1;
+    d.c = s.c;
+    d.h = s.h;
+    d.w = s.w;
+    d.kh = s.kh;
+    d.kw = s.kw;
+    d.stride = s.stride;
+    d.pad = s.pad;
+    d.W = s.weight;
+    d.b = s.bias;
+    if (d.c <= 0 || d.h <= 0 || d.w <= 0) return fail(VB_ESHAPE, "node %d: non-positive shape", k);
+    d.size = (long long)d.c * d.h * d.w;
+    if (d.size >= (1LL << 31)) return fail(VB_ESHAPE, "node %d: size too large", k);
+    if (k == 0) {
+      if (d.op != VB_INPUT) return fail(VB_ESHAPE, "node 0 must be VB_INPUT");
+      continue;
+    }
+    if (d.op < VB_INPUT || d.op > VB_FLATTEN) return fail(VB_EINVAL, "node %d: unknown op %d", k, d.op);
+    if (d.op == VB_INPUT) return fail(VB_ESHAPE, "node %d: only node 0 may be VB_INPUT", k);
+    if (d.in0 < 0 || d.in0 >= k) return fail(VB_ESHAPE, "node %d: in0 %d is not an earlier node", k, d.in0);
+    if (d.op == VB_ADD) {
+      if (d.in1 < 0 || d.in1 >= k) return fail(VB_ESHAPE, "node %d: in1 %d is not an earlier node", k, d.in1);
+    } else if (d.in1 != -1) {
+      return fail(VB_ESHAPE, "node %d: in1 must be -1 for this op", k);
+    }
+    const NodeInfo& p = G.n[d.in0];
+    switch (d.op) {
+      case VB_LINEAR:
+        if (!d.W) return fail(VB_EINVAL, "node %d: linear weight is NULL", k);
+        if (p.h != 1 || p.w != 1) return fail(VB_ESHAPE, "node %d: linear input must be flat", k);
+        if (d.h != 1 || d.w != 1) return fail(VB_ESHAPE, "node %d: linear output must be flat", k);
+        break;
+      case VB_CONV2D: {
+        if (!d.W) return fail(VB_EINVAL, "node %d: conv weight is NULL", k);
+        if (d.kh <= 0 || d.kw <= 0 || d.kh * d.kw > MAX_TAPS || d.stride <= 0 || d.pad < 0)
+          return fail(VB_EUNSUPPORTED, "node %d: conv kernel %dx%d stride %d pad %d unsupported", k, d.kh, d.kw,
+                      d.stride, d.pad);
+        int ho = (p.h + 2 * d.pad - d.kh) / d.stride + 1;
+        int wo = (p.w + 2 * d.pad - d.kw) / d.stride + 1;
+        if (ho != d.h || wo != d.w) return fail(VB_ESHAPE, "node %d: conv output %dx%d, expected %dx%d", k, d.h, d.w, ho, wo);
+        break;
+      }
+      case VB_RELU:
+        if (d.c != p.c || d.h != p.h || d.w != p.w) return fail(VB_ESHAPE, "node %d: relu shape mismatch", k);
+        break;
+      case VB_ADD: {
+        const NodeInfo& q = G.n[d.in1];
+        if (d.c != p.c || d.h != p.h || d.w != p.w || d.c != q.c || d.h != q.h || d.w != q.w)
+          return fail(VB_ESHAPE, "node %d: add shape mismatch", k);
+        break;
+      }
+      case VB_GAP:
+        if (d.c != p.c || d.h != 1 || d.w != 1) return fail(VB_ESHAPE, "node %d: gap shape mismatch", k);
+        break;
+      case VB_FLATTEN:
+        if (d.size != p.size || d.h != 1 || d.w != 1) return fail(VB_ESHAPE, "node %d: flatten shape mismatch", k);
+        break;
+      default:
+        break;
+    }
+    G.n[d.in0].cons.push_back(k);
+    if (d.op == VB_ADD && d.in1 != d.in0) G.n[d.in1].cons.push_back(k);
+  }
+  G.L = N - 1;
+  return VB_OK;
+}
+
+// producer of node k's data, skipping flatten (identity on memory)
+int src_of(const Graph& G, int k) {
+  while (G.n[k].op == VB_FLATTEN) k = G.n[k].in0;
+  return k;
+}
+
+// ---------------------------------------------------------------------------
+// GEMM descriptors
+
+GemmDesc base_desc() {
+  GemmDesc d;
+  std::memset(&d, 0, sizeof d);
+  d.gh = d.gw = d.hs = d.ws = 1;
+  d.sy = d.sx = 1;
+  d.ntaps = 1;
+  d.ho = d.wo = 1;
+  d.oym = d.oxm = 1;
+  d.rows_per_b = 1;
+  return d;
+}
+
+// Dense backward: Psi[rows][n_in] = Lam[rows][n_out] . W[n_out][n_in]
+GemmDesc linear_backward(const NodeInfo& nd, const NodeInfo& in, const float* lam, int rows) {
+  GemmDesc d = base_desc();
+  d.M = rows;
+  d.K = (int)nd.size;
+  d.N = (int)in.size;
+  d.A = lam;
+  d.cs = d.K;
+  d.a_row_stride = d.K;
+  d.B = nd.W;
+  d.btrans = 0;
+  return d;
+}
+
+// Conv backward for one output-parity class (py, px): Psi over the conv input.
+// Returns false if the class has no positions.
+bool conv_backward(const NodeInfo& nd, const NodeInfo& in, const float* lam, int rows, int py, int px, GemmDesc& d) {
+  d = base_desc();
+  const int s = nd.stride, p = nd.pad;
+  const int gh = (in.h - py + s - 1) / s, gw = (in.w - px + s - 1) / s;
+  if (gh <= 0 || gw <= 0) return false;
+  d.gh = gh;
+  d.gw = gw;
+  d.hs = nd.h;
+  d.ws = nd.w;
+  d.cs = nd.c;
+  d.sy = d.sx = 1;
+  d.a_row_stride = nd.size;
+  d.ntaps = 0;
+  for (int ky = 0; ky < nd.kh; ++ky) {
+    if (((py + p - ky) % s + s) % s != 0) continue;
+    for (int kx = 0; kx < nd.kw; ++kx) {
+      if (((px + p - kx) % s + s) % s != 0) continue;
+      d.tap_dy[d.ntaps] = (py + p - ky) / s;  // exact division
+      d.tap_dx[d.ntaps] = (px + p - kx) / s;
+      d.tap_w[d.ntaps] = ky * nd.kw + kx;
+      d.ntaps++;
+    }
+  }
+  d.K = d.ntaps * nd.c;
+  d.N = in.c;
+  d.M = rows * gh * gw;
+  d.A = lam;
+  d.B = nd.W;
+  d.btrans = 0;
+  d.ho = in.h;
+  d.wo = in.w;
+  d.oym = s;
+  d.oy0 = py;
+  d.oxm = s;
+  d.ox0 = px;
+  return true;
+}
+
+// Forward (IBP) affine step of node nd over its producer `in` for `batch` rows.
+GemmDesc affine_forward(const NodeInfo& nd, const NodeInfo& in, int batch) {
+  GemmDesc d = base_desc();
+  if (nd.op == VB_LINEAR) {
+    d.M = batch;
+    d.K = (int)in.size;
+    d.N = nd.c;
+    d.cs = d.K;
+    d.a_row_stride = d.K;
+    d.B = nd.W;
+    d.btrans = 1;
+    return d;
+  }
+  d.gh = nd.h;
+  d.gw = nd.w;
+  d.hs = in.h;
+  d.ws = in.w;
+  d.cs = in.c;
+  d.sy = d.sx = nd.stride;
+  d.a_row_stride = in.size;
+  d.ntaps = nd.kh * nd.kw;
+  for (int ky = 0; ky < nd.kh; ++ky)
+    for (int kx = 0; kx < nd.kw; ++kx) {
+      int t = ky * nd.kw + kx;
+      d.tap_dy[t] = ky - nd.pad;
+      d.tap_dx[t] = kx - nd.pad;
+      d.tap_w[t] = t;
+    }
+  d.K = d.ntaps * in.c;
+  d.N = nd.c;
+  d.M = batch * nd.h * nd.w;
+  d.B = nd.W;
+  d.btrans = 1;
+  d.ho = nd.h;
+  d.wo = nd.w;
+  return d;
+}
+
+// ---------------------------------------------------------------------------
+// backward walk
+
+struct Domain {
+  const float* xc;
+  const float* xr;
+  float eps;
+};
+
+struct Backward {
+  const Graph& G;
+  hipStream_t st;
+  const float* const* lo;
+  const float* const* hi;
+  Domain dom;
+  // pool
+  float* pool[NPOOL];
+  int refs[NPOOL];
+  float* part;
+  float* rowacc;
+  size_t part_floats;
+  // alpha-CROWN extras (per node, may be NULL)
+  const float* const* alpha = nullptr;
+  float* const* psi_keep = nullptr;
+
+  int alloc() {
+    for (int i = 0; i < NPOOL; ++i)
+      if (refs[i] == 0) {
+        refs[i] = 1;
+        return i;
+      }
+    return -1;
+  }
+  void release(int b) {
+    if (b >= 0) refs[b]--;
+  }
+};
+
+// Bias that a Lambda over node z carries into beta: z's own bias if it is an
+// affine node; the sum over both inputs of an ADD (through nested ADDs).
+// Returns number of bias vectors written into `out` (up to 4).
+void bias_terms(const Graph& G, int z, std::vector<const float*>& out) {
+  const NodeInfo& n = G.n[z];
+  if (n.op == VB_LINEAR || n.op == VB_CONV2D) {
+    if (n.b) out.push_back(n.b);
+  } else if (n.op == VB_ADD) {
+    bias_terms(G, n.in0, out);
+    if (n.in1 != n.in0) bias_terms(G, n.in1, out);
+  }
+}
+
+// Is node k the lowest-index active consumer of t (through flatten)?
+bool lowest_consumer(const Graph& G, const std::vector<char>& active, int t, int k) {
+  std::vector<int> stack(G.n[t].cons.begin(), G.n[t].cons.end());
+  while (!stack.empty()) {
+    int c = stack.back();
+    stack.pop_back();
+    if (G.n[c].op == VB_FLATTEN) {
+      for (int cc : G.n[c].cons) stack.push_back(cc);
+      continue;
+    }
+    if (c != k && active[c] && c < k) return false;
+  }
+  return true;
+}
+
+// Per-chunk parameters of one back-substitution.
+struct BwdCall {
+  int start, stop;
+  const float* C;   // spec rows [chunk][m][n_start] (already offset to the chunk) or NULL: identity
+  int m;            // spec rows per batch element (C != NULL)
+  int split;        // 1: rows +C and -C (2m rows per element); 0: +C only
+  int b0, cb;       // batch offset and chunk size
+  int batch_total;
+};
+
+vb_status effective_bias(Backward& B, const Graph& G, int z, const float*& bias) {
+  std::vector<const float*> terms;
+  bias_terms(G, z, terms);
+  if (terms.empty()) {
+    bias = nullptr;
+  } else if (terms.size() == 1) {
+    bias = terms[0];
+  } else {
+    return fail(VB_EUNSUPPORTED, "node %d: more than one affine bias reaches this node (sum them on the host)", z);
+  }
+  (void)B;
+  return VB_OK;
+}
+
+// ---- optional event timing of relaxation-epilogue GEMM launches
+struct ProfRec {
+  hipEvent_t a, b;
+  double flops;
+};
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+
+vb_status run_gemm_reduce(Backward& B, GemmDesc& d, int rows, int P, bool reduce, double alg_flops = 0.0) {
+  d.part = reduce ? B.part : nullptr;
+  d.part_ld = gemm_ntiles(d);
+  if (reduce && (size_t)d.M * d.part_ld > B.part_floats)
+    return fail(VB_ENOMEM, "internal: partial buffer too small (%lld > %zu)", (long long)d.M * d.part_ld, B.part_floats);
+  const bool prof = g_prof_on && d.epi == E_RELAX;
+  ProfRec rec{};
+  if (prof) {
+    HIPCHK(hipEventCreate(&rec.a));
+    HIPCHK(hipEventCreate(&rec.b));
+    HIPCHK(hipEventRecord(rec.a, B.st));
+  }
+  HIPCHK(launch_gemm(d, B.st));
+  if (prof) {
+    HIPCHK(hipEventRecord(rec.b, B.st));
+    rec.flops = alg_flops;
+    g_prof.push_back(rec);
+  }
+  if (reduce) HIPCHK(launch_rows_reduce(B.part, 1, rows, P, d.part_ld, d.part_ld, B.rowacc, 1, B.st));
+  return VB_OK;
+}
+
+// Execute the back-substitution of call `c`; rowacc receives the lower bound
+// of every row (rows = cb * R).  Returns status.
+vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
+  const Graph& G = B.G;
+  const int N = (int)G.n.size();
+  const int rows = (int)(c.cb * R);
+  std::vector<int> lam(N, -1);
+  for (int i = 0; i < NPOOL; ++i) B.refs[i] = 0;
+
+  // active nodes: reachable backwards from start without passing below stop
+  std::vector<char> active(N, 0);
+  {
+    std::vector<int> stack{c.start};
+    while (!stack.empty()) {
+      int k = stack.back();
+      stack.pop_back();
+      if (active[k]) continue;
+      active[k] = 1;
+      if (k == c.stop) continue;
+      if (k == 0) return fail(VB_ESHAPE, "node %d is not bounded by domain node %d", c.start, c.stop);
+      stack.push_back(G.n[k].in0);
+      if (G.n[k].op == VB_ADD) stack.push_back(G.n[k].in1);
+    }
+    if (!active[c.stop]) return fail(VB_ESHAPE, "domain node %d does not feed node %d", c.stop, c.start);
+    for (int k = 0; k < c.stop; ++k) active[k] = 0;
+  }
+
+  const NodeInfo& S = G.n[c.start];
+  int from = c.start;
+  if (c.C) {
+    int b = B.alloc();
+    const float* bias = nullptr;
+    vb_status s = effective_bias(B, G, c.start, bias);
+    if (s) return s;
+    HIPCHK(launch_spec_init(c.C, c.cb, c.m, (int)S.size, bias, B.pool[b], B.rowacc, c.split, B.st));
+    lam[c.start] = b;
+  } else {
+    // identity rows; fast path: Linear start whose input is a ReLU
+    int t = (S.op == VB_LINEAR) ? src_of(G, S.in0) : -1;
+    if (t >= 0 && t != c.stop && G.n[t].op == VB_RELU && lowest_consumer(G, active, t, c.start) &&
+        G.n[G.n[t].in0].cons.size() == 1) {
+      int z = G.n[t].in0;
+      int b = B.alloc();
+      const float* bias_z = nullptr;
+      vb_status s = effective_bias(B, G, z, bias_z);
+      if (s) return s;
+      const long long off = (long long)c.b0 * G.n[z].size;
+      HIPCHK(launch_identity_linear(S.W, (int)S.size, (int)G.n[z].size, S.b, B.lo[z] + off, B.hi[z] + off, bias_z,
+                                    c.cb, B.pool[b], B.rowacc, B.st));
+      lam[z] = b;
+      from = z;
+    } else {
+      int b = B.alloc();
+      HIPCHK(launch_identity_fill(c.cb, (int)S.size, B.pool[b], B.st));
+      const float* bias = nullptr;
+      vb_status s = effective_bias(B, G, c.start, bias);
+      if (s) return s;
+      HIPCHK(launch_fill(B.rowacc, 0.f, rows, B.st));
+      if (bias) {
+        // beta of identity rows = +-bias[i]; reuse the spec-init kernel on the identity
+        HIPCHK(launch_spec_init(B.pool[b], c.cb, (int)(R), (int)S.size, bias, B.pool[b], B.rowacc, 0, B.st));
+      }
+      lam[c.start] = b;
+    }
+  }
+
+  auto chunk_off = [&](int node) -> long long { return (long long)c.b0 * G.n[node].size; };
+
+  for (int k = from; k > c.stop; --k) {
+    if (lam[k] < 0) continue;
+    const NodeInfo& nd = G.n[k];
+    const int cur = lam[k];
+    float* Lk = B.pool[cur];
+    if (nd.op == VB_LINEAR || nd.op == VB_CONV2D) {
+      const int t = src_of(G, nd.in0);
+      const NodeInfo& tn = G.n[t];
+      const bool lowest = lowest_consumer(G, active, t, k);
+      const int pend = lam[t];
+      int epi;
+      int z = -1;
+      if (t == c.stop)
+        epi = lowest ? E_CONCRETIZE : E_STORE;
+      else if (tn.op == VB_RELU && lowest) {
+        epi = E_RELAX;
+        z = tn.in0;
+        if (G.n[z].cons.size() != 1)
+          return fail(VB_EUNSUPPORTED, "node %d feeds more than its ReLU; cannot relax", z);
+      } else
+        epi = E_STORE;
+      int outb = -1;
+      if (epi == E_RELAX || epi == E_STORE) {
+        if (epi == E_STORE && pend >= 0 && B.refs[pend] == 1)
+          outb = pend;  // accumulate in place
+        else
+          outb = B.alloc();
+        if (outb < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted at node %d", k);
+      }
+      const float* bias = nullptr;
+      if (epi == E_RELAX) {
+        vb_status s = effective_bias(B, G, z, bias);
+        if (s) return s;
+      } else if (epi == E_STORE && (tn.op == VB_LINEAR || tn.op == VB_CONV2D || tn.op == VB_ADD)) {
+        vb_status s = effective_bias(B, G, t, bias);
+        if (s) return s;
+      }
+      // one launch (dense) or one per output-parity class (conv)
+      std::vector<GemmDesc> descs;
+      if (nd.op == VB_LINEAR) {
+        descs.push_back(linear_backward(nd, tn, Lk, rows));
+      } else {
+        for (int py = 0; py < nd.stride; ++py)
+          for (int px = 0; px < nd.stride; ++px) {
+            GemmDesc d;
+            if (conv_backward(nd, tn, Lk, rows, py, px, d)) descs.push_back(d);
+          }
+      }
+      const int tgt_bounds = (epi == E_RELAX) ? z : t;
+      for (GemmDesc& d : descs) {
+        d.epi = epi;
+        d.rows_per_b = (int)R;
+        d.addend = (pend >= 0) ? B.pool[pend] : nullptr;
+        d.bias = bias;
+        if (epi != E_CONCRETIZE) d.out = B.pool[outb];
+        if (epi == E_RELAX) {
+          d.lo = B.lo[tgt_bounds] + chunk_off(tgt_bounds);
+          d.hi = B.hi[tgt_bounds] + chunk_off(tgt_bounds);
+          if (B.alpha && B.alpha[t]) d.alpha = B.alpha[t];
+          if (B.psi_keep && B.psi_keep[t]) d.psi_out = B.psi_keep[t];
+        }
+        if (epi == E_CONCRETIZE) {
+          if (t == 0) {
+            d.center = B.dom.xc + chunk_off(0);
+            d.radius = B.dom.xr ? B.dom.xr + chunk_off(0) : nullptr;
+            d.eps = B.dom.eps;
+          } else {
+            d.lo = B.lo[t] + chunk_off(t);
+            d.hi = B.hi[t] + chunk_off(t);
+          }
+        }
+        const bool reduce = (epi != E_STORE) || bias != nullptr;
+        const int P = d.gh * d.gw;
+        // algorithmic multiply-adds of this layer for these rows (conv: the
+        // forward count C_out*C_in*kh*kw*H_out*W_out per row, split evenly
+        // over the output-parity launches)
+        const double macs = (nd.op == VB_LINEAR)
+                                ? (double)rows * nd.size * tn.size
+                                : (double)rows * nd.c * tn.c * nd.kh * nd.kw * nd.h * nd.w / descs.size();
+        vb_status s = run_gemm_reduce(B, d, rows, P, reduce, 2.0 * macs);
+        if (s) return s;
+      }
+      B.release(cur);
+      lam[k] = -1;
+      if (epi == E_RELAX) {
+        if (pend >= 0) {
+          B.release(pend);
+          lam[t] = -1;
+        }
+        lam[z] = outb;
+      } else if (epi == E_CONCRETIZE) {
+        if (pend >= 0) {
+          B.release(pend);
+          lam[t] = -1;
+        }
+      } else {
+        if (outb != pend) {
+          if (pend >= 0) B.release(pend);
+        }
+        lam[t] = outb;
+      }
+    } else if (nd.op == VB_RELU) {
+      // Lambda accumulated without a fused consumer: standalone relaxation
+      const int z = nd.in0;
+      if (G.n[z].cons.size() != 1) return fail(VB_EUNSUPPORTED, "node %d feeds more than its ReLU", z);
+      int outb = B.alloc();
+      if (outb < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted at node %d", k);
+      const float* bias_z = nullptr;
+      vb_status s = effective_bias(B, G, z, bias_z);
+      if (s) return s;
+      const int P = nd.h * nd.w;
+      HIPCHK(launch_relax(Lk, 0, 1.f, nullptr, rows, (int)R, P, nd.c, B.lo[z] + chunk_off(z), B.hi[z] + chunk_off(z),
+                          bias_z, B.alpha ? B.alpha[k] : nullptr, B.psi_keep ? B.psi_keep[k] : nullptr, B.pool[outb],
+                          B.rowacc, B.st));
+      B.release(cur);
+      lam[k] = -1;
+      lam[z] = outb;
+    } else if (nd.op == VB_ADD) {
+      const int ins[2] = {nd.in0, nd.in1};
+      for (int q = 0; q < (nd.in0 == nd.in1 ? 1 : 2); ++q) {
+        const int t = ins[q];
+        const float scale = (nd.in0 == nd.in1) ? 2.f : 1.f;
+        if (lam[t] < 0 && scale == 1.f) {
+          lam[t] = cur;
+          B.refs[cur]++;
+        } else {
+          int outb = (lam[t] >= 0 && B.refs[lam[t]] == 1) ? lam[t] : B.alloc();
+          if (outb < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted at node %d", k);
+          if (lam[t] >= 0)
+            HIPCHK(launch_add(B.pool[lam[t]], Lk, scale, B.pool[outb], (long long)rows * G.n[t].size, B.st));
+          else
+            HIPCHK(launch_add(Lk, Lk, 1.f, B.pool[outb], (long long)rows * G.n[t].size, B.st));
+          if (lam[t] >= 0 && lam[t] != outb) B.release(lam[t]);
+          lam[t] = outb;
+        }
+        // bias contributions of affine inputs are carried by effective_bias of the producer of Lambda
+      }
+      B.release(cur);
+      lam[k] = -1;
+    } else if (nd.op == VB_GAP) {
+      const int t = nd.in0;
+      const NodeInfo& tn = G.n[t];
+      const int P = tn.h * tn.w;
+      const float scale = 1.f / (float)P;
+      const int pend = lam[t];
+      if (tn.op == VB_RELU && lowest_consumer(G, active, t, k) && t != c.stop) {
+        const int z = tn.in0;
+        if (G.n[z].cons.size() != 1) return fail(VB_EUNSUPPORTED, "node %d feeds more than its ReLU", z);
+        int outb = B.alloc();
+        if (outb < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted at node %d", k);
+        const float* bias_z = nullptr;
+        vb_status s = effective_bias(B, G, z, bias_z);
+        if (s) return s;
+        HIPCHK(launch_relax(Lk, 1, scale, pend >= 0 ? B.pool[pend] : nullptr, rows, (int)R, P, tn.c,
+                            B.lo[z] + chunk_off(z), B.hi[z] + chunk_off(z), bias_z, B.alpha ? B.alpha[t] : nullptr,
+                            B.psi_keep ? B.psi_keep[t] : nullptr, B.pool[outb], B.rowacc, B.st));
+        if (pend >= 0) {
+          B.release(pend);
+          lam[t] = -1;
+        }
+        lam[z] = outb;
+      } else {
+        int outb = (pend >= 0 && B.refs[pend] == 1) ? pend : B.alloc();
+        if (outb < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted at node %d", k);
+        HIPCHK(launch_gap_expand(Lk, rows, P, tn.c, scale, pend >= 0 ? B.pool[pend] : nullptr, B.pool[outb], B.st));
+        if (pend >= 0 && pend != outb) B.release(pend);
+        lam[t] = outb;
+      }
+      B.release(cur);
+      lam[k] = -1;
+    } else if (nd.op == VB_FLATTEN) {
+      const int t = nd.in0;
+      if (lam[t] >= 0) {
+        int outb = B.refs[lam[t]] == 1 ? lam[t] : B.alloc();
+        HIPCHK(launch_add(B.pool[lam[t]], Lk, 1.f, B.pool[outb], (long long)rows * nd.size, B.st));
+        if (outb != lam[t]) B.release(lam[t]);
+        lam[t] = outb;
+        B.release(cur);
+      } else {
+        lam[t] = cur;
+      }
+      lam[k] = -1;
+    } else {
+      return fail(VB_EUNSUPPORTED, "cannot back-substitute through node %d (op %d)", k, nd.op);
+    }
+  }
+  if (lam[c.stop] >= 0) {
+    const NodeInfo& sn = G.n[c.stop];
+    const long long off = (long long)c.b0 * sn.size;
+    if (c.stop == 0)
+      HIPCHK(launch_concretize_rows(B.pool[lam[c.stop]], rows, (int)sn.size, (int)R, B.dom.xc + off,
+                                    B.dom.xr ? B.dom.xr + off : nullptr, B.dom.eps, nullptr, nullptr, nullptr,
+                                    nullptr, nullptr, B.rowacc, B.st));
+    else
+      HIPCHK(launch_concretize_rows(B.pool[lam[c.stop]], rows, (int)sn.size, (int)R, nullptr, nullptr, 0.f,
+                                    B.lo[c.stop] + off, B.hi[c.stop] + off, nullptr, nullptr, nullptr, B.rowacc,
+                                    B.st));
+  }
+  return VB_OK;
+}
+
+// Widest Lambda and largest partial buffer of a back-substitution, per batch element.
+void bwd_requirements(const Graph& G, int start, int stop, long long R, long long& maxw, long long& part_per_b) {
+  maxw = 0;
+  part_per_b = 0;
+  std::vector<char> active(G.n.size(), 0);
+  std::vector<int> stack{start};
+  while (!stack.empty()) {
+    int k = stack.back();
+    stack.pop_back();
+    if (active[k] || k < stop) continue;
+    active[k] = 1;
+    if (k == stop || k == 0) continue;
+    stack.push_back(G.n[k].in0);
+    if (G.n[k].op == VB_ADD) stack.push_back(G.n[k].in1);
+  }
+  for (size_t k = 0; k < G.n.size(); ++k) {
+    if (!active[k]) continue;
+    const NodeInfo& nd = G.n[k];
+    maxw = std::max(maxw, nd.size);
+    if ((nd.op == VB_LINEAR || nd.op == VB_CONV2D) && (int)k != stop) {
+      const NodeInfo& in = G.n[src_of(G, nd.in0)];
+      const long long n_ch = (nd.op == VB_LINEAR) ? in.size : in.c;
+      const int bn = n_ch > 64 ? 128 : (n_ch > 32 ? 64 : 32);
+      const long long S = (n_ch + bn - 1) / bn;
+      const long long P = (nd.op == VB_LINEAR) ? 1 : (long long)in.h * in.w;
+      part_per_b = std::max(part_per_b, R * P * S);
+    }
+  }
+}
+
+struct WsLayout {
+  size_t pool_floats;  // per buffer
+  size_t part_floats;
+  size_t rows;
+  size_t bytes;
+};
+
+WsLayout layout_for(long long maxw, long long part_per_b, long long R, int cb, size_t extra_floats) {
+  WsLayout L;
+  L.pool_floats = (size_t)cb * R * maxw;
+  L.part_floats = (size_t)cb * part_per_b;
+  L.rows = (size_t)cb * R;
+  L.bytes = NPOOL * align_up(L.pool_floats * 4) + align_up(L.part_floats * 4) + align_up(L.rows * 4) +
+            align_up(extra_floats * 4);
+  return L;
+}
+
+// Run a back-substitution over the whole batch in chunks that fit `ws`.
+// For each chunk, `after` is called with (rowacc, b0, cb) to consume the row bounds.
+template <class After>
+vb_status backward_all(Backward& B, int start, int stop, const float* C, int m, int split, int batch, long long R,
+                       char* ws, size_t ws_bytes, size_t reserved_floats, After after) {
+  long long maxw, ppb;
+  bwd_requirements(B.G, start, stop, R, maxw, ppb);
+  if (C) maxw = std::max(maxw, B.G.n[start].size);
+  int cb = batch;
+  while (cb > 1 && layout_for(maxw, ppb, R, cb, reserved_floats).bytes > ws_bytes) cb = (cb + 1) / 2;
+  WsLayout L = layout_for(maxw, ppb, R, cb, reserved_floats);
+  if (L.bytes > ws_bytes)
+    return fail(VB_ENOMEM, "workspace of %zu bytes is too small: one batch element needs %zu", ws_bytes, L.bytes);
+  char* p = ws + align_up(reserved_floats * 4);
+  for (int i = 0; i < NPOOL; ++i) {
+    B.pool[i] = (float*)p;
+    p += align_up(L.pool_floats * 4);
+  }
+  B.part = (float*)p;
+  B.part_floats = L.part_floats;
+  p += align_up(L.part_floats * 4);
+  B.rowacc = (float*)p;
+  for (int b0 = 0; b0 < batch; b0 += cb) {
+    const int n = std::min(cb, batch - b0);
+    BwdCall c;
+    c.start = start;
+    c.stop = stop;
+    c.C = C ? C + (long long)b0 * m * B.G.n[start].size : nullptr;
+    c.m = m;
+    c.split = split;
+    c.b0 = b0;
+    c.cb = n;
+    c.batch_total = batch;
+    vb_status s = backward_chunk(B, c, R);
+    if (s) return s;
+    s = after(B.rowacc, b0, n);
+    if (s) return s;
+  }
+  return VB_OK;
+}
+
+bool one_affine_step(const Graph& G, int z, int stop) {
+  const NodeInfo& n = G.n[z];
+  if (n.op != VB_LINEAR && n.op != VB_CONV2D) return false;
+  return src_of(G, n.in0) == stop;
+}
+
+vb_status check_stream_ptrs(const void* p, const char* what) {
+  if (!p) return fail(VB_EINVAL, "%s is NULL", what);
+  return VB_OK;
+}
+
+// ---------------------------------------------------------------------------
+// IBP
+
+vb_status ibp_impl(const Graph& G, int batch, const float* xc, const float* xr, float eps, float* const* lo,
+                   float* const* hi, hipStream_t st) {
+  const int N = (int)G.n.size();
+  std::vector<char> done(N, 0);
+  for (int k = 1; k < N; ++k) {
+    const NodeInfo& nd = G.n[k];
+    if (done[k]) continue;
+    if (!lo[k] || !hi[k]) return fail(VB_EINVAL, "node %d: IBP needs node_lo/node_hi storage", k);
+    const int p = nd.in0;
+    const int ps = src_of(G, p);
+    switch (nd.op) {
+      case VB_LINEAR:
+      case VB_CONV2D: {
+        GemmDesc d = affine_forward(nd, G.n[ps], batch);
+        d.epi = E_IBP;
+        if (ps == 0) {
+          d.amode = A_IBP_BALL;
+          d.A = xc;
+          d.A2 = xr;
+          d.eps = eps;
+        } else {
+          d.amode = A_IBP_BOX;
+          d.A = lo[ps];
+          d.A2 = hi[ps];
+        }
+        d.out = lo[k];
+        d.out2 = hi[k];
+        d.bias = nd.b;
+        if (nd.cons.size() == 1 && G.n[nd.cons[0]].op == VB_RELU && lo[nd.cons[0]] && hi[nd.cons[0]]) {
+          d.relu_lo = lo[nd.cons[0]];
+          d.relu_hi = hi[nd.cons[0]];
+          done[nd.cons[0]] = 1;
+        }
+        HIPCHK(launch_gemm(d, st));
+        break;
+      }
+      case VB_RELU:
+        if (p == 0) {
+          return fail(VB_EUNSUPPORTED, "ReLU directly on the input node");
+        }
+        HIPCHK(launch_ibp_eltwise(0, lo[p], hi[p], nullptr, nullptr, lo[k], hi[k], (long long)batch * nd.size, st));
+        break;
+      case VB_ADD:
+        if (nd.in0 == 0 || nd.in1 == 0) return fail(VB_EUNSUPPORTED, "ADD directly on the input node");
+        HIPCHK(launch_ibp_eltwise(1, lo[nd.in0], hi[nd.in0], lo[nd.in1], hi[nd.in1], lo[k], hi[k],
+                                  (long long)batch * nd.size, st));
+        break;
+      case VB_GAP:
+        if (p == 0) return fail(VB_EUNSUPPORTED, "GAP directly on the input node");
+        HIPCHK(launch_ibp_gap(lo[p], hi[p], batch, G.n[p].h * G.n[p].w, G.n[p].c, lo[k], hi[k], st));
+        break;
+      case VB_FLATTEN:
+        if (p == 0) return fail(VB_EUNSUPPORTED, "FLATTEN directly on the input node");
+        if (lo[k] != lo[p]) HIPCHK(launch_add(lo[p], nullptr, 0.f, lo[k], (long long)batch * nd.size, st));
+        if (hi[k] != hi[p]) HIPCHK(launch_add(hi[p], nullptr, 0.f, hi[k], (long long)batch * nd.size, st));
+        break;
+      default:
+        return fail(VB_EUNSUPPORTED, "IBP through node %d (op %d)", k, nd.op);
+    }
+  }
+  return VB_OK;
+}
+
+vb_status check_domain(const float* xc) {
+  if (!xc) return fail(VB_EINVAL, "x_center is NULL");
+  return VB_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+
+extern "C" const char* vb_last_error(void) { return g_err.c_str(); }
+
+static size_t crown_workspace(const Graph& G, int batch, int m, int method, int region_start) {
+  size_t best = 0;
+  auto consider = [&](int start, int stop, long long R, bool spec) {
+    long long maxw, ppb;
+    bwd_requirements(G, start, stop, R, maxw, ppb);
+    if (spec) maxw = std::max(maxw, G.n[start].size);
+    best = std::max(best, layout_for(maxw, ppb, R, batch, 0).bytes);
+  };
+  const int L = G.L;
+  if (m > 0) {
+    consider(L, src_of(G, G.n[L].in0), 2LL * m, true);  // IBP spec fold
+    consider(L, 0, 2LL * m, true);
+  }
+  if (method != VB_METHOD_IBP) {
+    const int stop = method == VB_METHOD_CROWN ? 0 : region_start;
+    for (size_t r = 0; r < G.n.size(); ++r) {
+      if (G.n[r].op != VB_RELU) continue;
+      int z = G.n[r].in0;
+      if (z <= stop || one_affine_step(G, z, stop)) continue;
+      consider(z, stop, 2LL * G.n[z].size, false);
+    }
+    if (m > 0 && method == VB_METHOD_HYBRID) consider(L, stop, 2LL * m, true);
+  }
+  if (m > 0) {
+    // alpha-CROWN evaluation (lower rows only) plus its kept products
+    consider(L, 0, m, true);
+  }
+  return best;
+}
+
+extern "C" vb_status vb_workspace_size(const vb_graph* g, int32_t batch, int32_t m, int32_t method,
+                                       int32_t region_start, size_t* bytes) {
+  Graph G;
+  vb_status s = parse_graph(g, G);
+  if (s) return s;
+  if (!bytes) return fail(VB_EINVAL, "bytes is NULL");
+  if (batch <= 0 || m < 0) return fail(VB_EINVAL, "batch must be > 0 and m >= 0");
+  if (method < VB_METHOD_IBP || method > VB_METHOD_HYBRID) return fail(VB_EINVAL, "unknown method %d", method);
+  if (method == VB_METHOD_HYBRID && (region_start <= 0 || region_start >= G.L))
+    return fail(VB_EINVAL, "region_start %d out of range", region_start);
+  *bytes = crown_workspace(G, batch, m, method, region_start);
+  return VB_OK;
+}
+
+static vb_status spec_ibp(const Graph& G, int batch, const float* C, int m, const float* const* lo,
+                          const float* const* hi, float* spec_lo, float* spec_hi, void* ws, size_t ws_bytes,
+                          hipStream_t st) {
+  const int L = G.L;
+  if (G.n[L].op != VB_LINEAR) return fail(VB_EUNSUPPORTED, "spec bounds need a LINEAR last node");
+  const int stop = src_of(G, G.n[L].in0);
+  if (stop == 0) return fail(VB_EUNSUPPORTED, "spec IBP over a single affine layer: use CROWN (exact)");
+  Backward B{G, st, lo, hi, {nullptr, nullptr, 0.f}};
+  return backward_all(B, L, stop, C, m, 1, batch, 2LL * m, (char*)ws, ws_bytes, 0,
+                      [&](float* acc, int b0, int cb) -> vb_status {
+                        HIPCHK(launch_finish(acc, cb, m, spec_lo ? spec_lo + (long long)b0 * m : nullptr,
+                                             spec_hi ? spec_hi + (long long)b0 * m : nullptr, nullptr, st));
+                        return VB_OK;
+                      });
+}
+
+extern "C" vb_status vb_ibp(const vb_graph* g, int32_t batch, const float* x_center, const float* x_radius,
+                            float eps, float* const* node_lo, float* const* node_hi, const float* C, int32_t m,
+                            float* spec_lo, float* spec_hi, void* ws, size_t ws_bytes, void* stream) {
+  Graph G;
+  vb_status s = parse_graph(g, G);
+  if (s) return s;
+  if (batch <= 0) return fail(VB_EINVAL, "batch must be positive");
+  if ((s = check_domain(x_center))) return s;
+  if (!node_lo || !node_hi) return fail(VB_EINVAL, "node_lo/node_hi arrays are NULL");
+  if (!x_radius && !(eps >= 0.f)) return fail(VB_EINVAL, "eps must be >= 0");
+  if (C && m <= 0) return fail(VB_EINVAL, "m must be positive with C");
+  if (C && !ws) return fail(VB_EINVAL, "spec bounds need a workspace");
+  if (C) {
+    const size_t need = crown_workspace(G, 1, m, VB_METHOD_IBP, 0);
+    if (ws_bytes < need)
+      return fail(VB_ENOMEM, "workspace of %zu bytes is too small: one batch element needs %zu", ws_bytes, need);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  s = ibp_impl(G, batch, x_center, x_radius, eps, node_lo, node_hi, st);
+  if (s) return s;
+  if (C) return spec_ibp(G, batch, C, m, node_lo, node_hi, spec_lo, spec_hi, ws, ws_bytes, st);
+  return VB_OK;
+}
+
+static vb_status crown_backward_impl(const Graph& G, int batch, int start, int stop, const float* C, int m,
+                                     const float* const* lo, const float* const* hi, Domain dom, float* lb,
+                                     float* ub, void* ws, size_t ws_bytes, hipStream_t st) {
+  Backward B{G, st, lo, hi, dom};
+  const long long R = C ? 2LL * m : 2LL * G.n[start].size;
+  const int half = (int)(R / 2);
+  return backward_all(B, start, stop, C, m, 1, batch, R, (char*)ws, ws_bytes, 0,
+                      [&](float* acc, int b0, int cb) -> vb_status {
+                        HIPCHK(launch_finish(acc, cb, half, lb ? lb + (long long)b0 * half : nullptr,
+                                             ub ? ub + (long long)b0 * half : nullptr, nullptr, st));
+                        return VB_OK;
+                      });
+}
+
+extern "C" vb_status vb_crown_backward(const vb_graph* g, int32_t batch, int32_t start, int32_t stop, const float* C,
+                                       int32_t m, const float* const* node_lo, const float* const* node_hi,
+                                       const float* x_center, const float* x_radius, float eps, float* lb, float* ub,
+                                       float* A_out, float* bias_out, void* ws, size_t ws_bytes, void* stream) {
+  Graph G;
+  vb_status s = parse_graph(g, G);
+  if (s) return s;
+  if (batch <= 0) return fail(VB_EINVAL, "batch must be positive");
+  if (start <= 0 || start >= (int)G.n.size()) return fail(VB_EINVAL, "start %d out of range", start);
+  if (stop < 0 || stop >= start) return fail(VB_EINVAL, "stop %d must be in [0, start)", stop);
+  if (C && m <= 0) return fail(VB_EINVAL, "m must be positive with C");
+  if (!node_lo || !node_hi) return fail(VB_EINVAL, "node_lo/node_hi arrays are NULL");
+  if (stop == 0 && (s = check_domain(x_center))) return s;
+  if (stop == 0 && !x_radius && !(eps >= 0.f)) return fail(VB_EINVAL, "eps must be >= 0");
+  if (!ws) return fail(VB_EINVAL, "workspace is NULL");
+  if (A_out || bias_out) return fail(VB_EUNSUPPORTED, "A_out: returning linear bounds is not implemented");
+  return crown_backward_impl(G, batch, start, stop, C, m, node_lo, node_hi, {x_center, x_radius, eps}, lb, ub, ws,
+                             ws_bytes, (hipStream_t)stream);
+}
+
+extern "C" vb_status vb_concretize(int32_t rows, int32_t n, int32_t rows_per_batch, const float* A, const float* bias,
+                                   const float* center, const float* radius, float eps, float* lb, float* ub,
+                                   void* stream) {
+  if (rows <= 0 || n <= 0 || rows_per_batch <= 0) return fail(VB_EINVAL, "rows, n and rows_per_batch must be > 0");
+  if (!A || !center) return fail(VB_EINVAL, "A and center must be non-NULL");
+  if (!radius && !(eps >= 0.f)) return fail(VB_EINVAL, "eps must be >= 0");
+  HIPCHK(launch_concretize_rows(A, rows, n, rows_per_batch, center, radius, eps, nullptr, nullptr, bias, lb, ub,
+                                nullptr, (hipStream_t)stream));
+  return VB_OK;
+}
+
+extern "C" vb_status vb_crown(const vb_graph* g, int32_t batch, const float* x_center, const float* x_radius,
+                              float eps, int32_t method, int32_t region_start, float* const* node_lo,
+                              float* const* node_hi, const float* C, int32_t m, float* ibp_lb, float* ibp_ub,
+                              float* lb, float* ub, void* ws, size_t ws_bytes, void* stream) {
+  Graph G;
+  vb_status s = parse_graph(g, G);
+  if (s) return s;
+  if (batch <= 0) return fail(VB_EINVAL, "batch must be positive");
+  if ((s = check_domain(x_center))) return s;
+  if (!x_radius && !(eps >= 0.f)) return fail(VB_EINVAL, "eps must be >= 0");
+  if (!node_lo || !node_hi) return fail(VB_EINVAL, "node_lo/node_hi arrays are NULL");
+  if (method < VB_METHOD_IBP || method > VB_METHOD_HYBRID) return fail(VB_EINVAL, "unknown method %d", method);
+  if (method == VB_METHOD_HYBRID && (region_start <= 0 || region_start >= G.L))
+    return fail(VB_EINVAL, "region_start %d out of range", region_start);
+  if (C && m <= 0) return fail(VB_EINVAL, "m must be positive with C");
+  if (!ws) return fail(VB_EINVAL, "workspace is NULL");
+  for (size_t k = 1; k < G.n.size(); ++k)
+    if (!node_lo[k] || !node_hi[k]) return fail(VB_EINVAL, "node %zu: bounds storage is NULL", k);
+  {
+    const size_t need = crown_workspace(G, 1, C ? m : 0, method, region_start);
+    if (ws_bytes < need)
+      return fail(VB_ENOMEM, "workspace of %zu bytes is too small: one batch element needs %zu", ws_bytes, need);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  s = ibp_impl(G, batch, x_center, x_radius, eps, node_lo, node_hi, st);
+  if (s) return s;
+  if (C && (ibp_lb || ibp_ub)) {
+    s = spec_ibp(G, batch, C, m, node_lo, node_hi, ibp_lb, ibp_ub, ws, ws_bytes, st);
+    if (s) return s;
+  }
+  const Domain dom{x_center, x_radius, eps};
+  int stop = 0;
+  if (method != VB_METHOD_IBP) {
+    stop = method == VB_METHOD_CROWN ? 0 : region_start;
+    for (size_t r = 0; r < G.n.size(); ++r) {
+      if (G.n[r].op != VB_RELU) continue;
+      const int z = G.n[r].in0;
+      if (z <= stop || one_affine_step(G, z, stop)) continue;
+      s = crown_backward_impl(G, batch, z, stop, nullptr, 0, node_lo, node_hi, dom, node_lo[z], node_hi[z], ws,
+                              ws_bytes, st);
+      if (s) return s;
+    }
+  }
+  if (C && (lb || ub)) {
+    s = crown_backward_impl(G, batch, G.L, stop, C, m, node_lo, node_hi, dom, lb, ub, ws, ws_bytes, st);
+    if (s) return s;
+  }
+  return VB_OK;
+}
+
+extern "C" vb_status vb_profile_start(void) {
+  for (auto& r : g_prof) {
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  g_prof.clear();
+  g_prof_on = true;
+  return VB_OK;
+}
+
+extern "C" vb_status vb_profile_stop(double* ms, double* flops, int64_t* launches) {
+  g_prof_on = false;
+  double t = 0.0, f = 0.0;
+  for (auto& r : g_prof) {
+    HIPCHK(hipEventSynchronize(r.b));
+    float e = 0.f;
+    HIPCHK(hipEventElapsedTime(&e, r.a, r.b));
+    t += e;
+    f += r.flops;
+  }
+  if (ms) *ms = t;
+  if (flops) *flops = f;
+  if (launches) *launches = (int64_t)g_prof.size();
+  for (auto& r : g_prof) {
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  g_prof.clear();
+  return VB_OK;
+}
+
+extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float* C, int32_t m,
+                                   const float* const* node_lo, const float* const* node_hi, const float* x_center,
+                                   const float* x_radius, float eps, float* const* alpha, float* const* adam_m,
+                                   float* const* adam_v, int32_t step, float lr, float beta1, float beta2,
+                                   float adam_eps, float* lb_out, float* best_lb, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  (void)g; (void)batch; (void)C; (void)m; (void)node_lo; (void)node_hi; (void)x_center; (void)x_radius; (void)eps;
+  (void)alpha; (void)adam_m; (void)adam_v; (void)step; (void)lr; (void)beta1; (void)beta2; (void)adam_eps;
+  (void)lb_out; (void)best_lb; (void)ws; (void)ws_bytes; (void)stream;
+  return fail(VB_EUNSUPPORTED, "vb_alpha_step: not implemented yet");
+}

@@ -1,0 +1,129 @@
+// Internal interface between the host planner (vb_api.cpp) and the HIP kernels
+// (vb_kernels.hip).  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <cstdint>
+
+namespace vb {
+
+// How the A operand of the implicit GEMM is read.
+enum AMode : int {
+  A_PLAIN = 0,     // A values as stored
+  A_IBP_BOX = 1,   // A = lo, A2 = hi: operands c = (lo+hi)/2 and r = (hi-lo)/2
+  A_IBP_BALL = 2,  // A = centre, A2 = radius array or NULL (scalar eps): c and r
+};
+
+// What the GEMM epilogue does with each output element v = acc (+ addend).
+enum EpiMode : int {
+  E_STORE = 0,       // out = v; row partial += v . bias (if bias)
+  E_RELAX = 1,       // out = v>=0 ? a v : s v with (a,s,t) from target bounds;
+                     // row partial += out . bias + min(v,0) t
+  E_CONCRETIZE = 2,  // row partial += v c - |v| r over the domain box
+  E_IBP = 3,         // lo = acc_c + bias - acc_r, hi = acc_c + bias + acc_r
+};
+
+constexpr int MAX_TAPS = 9;
+
+struct GemmDesc {
+  int M, N, K;                 // output positions x output channels x reduction length
+  int amode;                   // AMode of the A operand (E_IBP: A_IBP_BOX or A_IBP_BALL)
+  // ---- A operand: position m -> (row, Y, X) on a gh x gw grid per row;
+  //      reduction index k -> (tap j, channel c) with k = j*cs + c;
+  //      element = A[row*a_row_stride + ((Y*sy + dy_j)*ws + (X*sx + dx_j))*cs + c],
+  //      zero outside [0,hs) x [0,ws).  Dense GEMM: gh=gw=hs=ws=1, cs=K, 1 tap.
+  const float* A;              // A_IBP_BOX: lo;  A_IBP_BALL: centre
+  const float* A2;             // A_IBP_BOX: hi;  A_IBP_BALL: radius array or NULL (eps)
+  float eps;
+  int gh, gw, hs, ws, cs, sy, sx;
+  long long a_row_stride;
+  int ntaps;
+  int tap_dy[MAX_TAPS], tap_dx[MAX_TAPS], tap_w[MAX_TAPS];
+  // ---- B operand (weights), tap-major.  k = j*cs + c:
+  //      !btrans: B[(tap_w[j]*cs + c)*N + n];  btrans: B[(tap_w[j]*N + n)*cs + c]
+  const float* B;
+  int btrans;
+  // ---- output mapping: (row, Y, X) -> row*ho*wo + (Y*oym+oy0)*wo + (X*oxm+ox0)
+  int ho, wo, oym, oy0, oxm, ox0;
+  int rows_per_b;              // batch element of a row = row / rows_per_b
+  // ---- epilogue
+  int epi;
+  float* out;                  // [opos][N]   (E_IBP: lo)
+  float* out2;                 // E_IBP: hi
+  float* relu_lo;              // E_IBP: bounds of a consumer ReLU (or NULL)
+  float* relu_hi;
+  const float* addend;         // [opos][N] or NULL, added to acc before the epilogue
+  const float* lo;             // target-node bounds at [b-pos][N] (E_RELAX, E_CONCRETIZE box)
+  const float* hi;
+  const float* bias;           // per output channel n (E_STORE / E_RELAX / E_IBP)
+  const float* alpha;          // E_RELAX: per [opos][N] lower slope of unstable neurons, or NULL
+  float* psi_out;              // E_RELAX: store the pre-relaxation value v, or NULL
+  const float* center;         // E_CONCRETIZE: centre/radius at [b-pos][N]; NULL -> from lo/hi
+  const float* radius;         // NULL -> eps (when center != NULL)
+  float* part;                 // row partials [M][part_ld] (column = N-tile index)
+  int part_ld;
+};
+
+// Launch the implicit GEMM; returns hipSuccess or the launch error.
+hipError_t launch_gemm(const GemmDesc& d, hipStream_t st);
+// Number of N-tiles launch_gemm uses for this descriptor (= partial columns).
+int gemm_ntiles(const GemmDesc& d);
+
+// rowacc[r] (+)= sum over z < Z, p < P, s < S of part[((z*rows + r)*P + p)*ld + s]
+hipError_t launch_rows_reduce(const float* part, int Z, int rows, int P, int S, int ld,
+                              float* rowacc, int accumulate, hipStream_t st);
+
+// Write the final outputs from row accumulators.  rows per batch element = 2R:
+// lb[b*R + i] = acc[b*2R + i], ub[b*R + i] = -acc[b*2R + R + i]  (NULL skips)
+hipError_t launch_finish(const float* rowacc, int batch, int R, float* lb, float* ub,
+                         float* best, hipStream_t st);
+
+// Spec rows: lam[b][r][:] = +C[b][r][:] for r < m and -C[b][r-m][:] for r >= m;
+// rowacc[b*2m + r] = lam[b][r][:] . bias (bias may be NULL).
+hipError_t launch_spec_init(const float* C, int batch, int m, int n, const float* bias,
+                            float* lam, float* rowacc, int rows_sign_split, hipStream_t st);
+
+// Identity rows through a Linear node followed (backwards) by a ReLU relaxation:
+// row (b, s, i), s in {+1,-1}: psi = s*W[i][:]; lam = relax(psi; lo/hi[b][:]);
+// rowacc = s*bias_start[i] + sum_j lam_j bias_z[j] + min(psi_j,0) t_j
+hipError_t launch_identity_linear(const float* W, int n_out, int n_in, const float* bias_start,
+                                  const float* lo, const float* hi, const float* bias_z,
+                                  int batch, float* lam, float* rowacc, hipStream_t st);
+
+// Identity rows materialised as a dense matrix: rows (b, s, i) over n, +-1 on the diagonal.
+hipError_t launch_identity_fill(int batch, int n, float* lam, hipStream_t st);
+
+// Standalone relaxation of lam over a ReLU with input bounds lo/hi [b][P*N]:
+// src is [rows][P*N] (or [rows][N] broadcast over P positions with scale, for GAP);
+// out = relax(src + addend); rowacc[r] += sum out.bias_z + min(v,0) t
+hipError_t launch_relax(const float* src, int src_broadcast, float scale, const float* addend,
+                        int rows, int rows_per_b, int P, int N, const float* lo, const float* hi,
+                        const float* bias_z, const float* alpha, float* psi_out,
+                        float* out, float* rowacc, hipStream_t st);
+
+// dst[i] = a[i] + b[i] (b may be NULL: copy), i < n
+hipError_t launch_add(const float* a, const float* b, float scale_b, float* dst, long long n,
+                      hipStream_t st);
+
+// Broadcast lam over GAP: dst[r][p][c] = src[r][c] * scale (+ addend)
+hipError_t launch_gap_expand(const float* src, int rows, int P, int C, float scale,
+                             const float* addend, float* dst, hipStream_t st);
+
+// Standalone concretisation: rowacc[r] (+)= sum_j A[r][j] c - |A[r][j]| rad
+// with c/rad at [r/rows_per_b][j] (center NULL -> from lo/hi box; radius NULL -> eps)
+hipError_t launch_concretize_rows(const float* A, int rows, int n, int rows_per_b,
+                                  const float* center, const float* radius, float eps,
+                                  const float* lo, const float* hi, const float* bias,
+                                  float* lb, float* ub, float* rowacc, hipStream_t st);
+
+// IBP elementwise nodes on [batch][n]: op 0 relu clamp, 1 add
+hipError_t launch_ibp_eltwise(int op, const float* lo0, const float* hi0, const float* lo1,
+                              const float* hi1, float* lo, float* hi, long long n, hipStream_t st);
+// IBP GAP: lo/hi [b][c] = mean over P positions of [b][p][c]
+hipError_t launch_ibp_gap(const float* lo_in, const float* hi_in, int batch, int P, int C,
+                          float* lo, float* hi, hipStream_t st);
+
+// Fill with a constant
+hipError_t launch_fill(float* p, float v, long long n, hipStream_t st);
+
+}  // namespace vb

@@ -1,0 +1,106 @@
+"""C-ABI contract on the CPU: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from helpers import ROOT, ensure_built
+
+ensure_built()
+import linear_bound_propagation_amd as lbp  # noqa: E402
+
+HEADER = os.path.join(ROOT, "include", "vb.h")
+
+
+def test_exports_every_declared_symbol():
+    src = open(HEADER).read()
+    declared = set(re.findall(r"^(?:vb_status|const char\*)\s+(vb_\w+)\s*\(", src, flags=re.M))
+    assert declared == set(lbp.EXPORTS)
+    lib = ctypes.CDLL(lbp.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def _graph(nodes):
+    arr = (lbp.vb_node * len(nodes))()
+    for i, nd in enumerate(nodes):
+        for k, v in nd.items():
+            setattr(arr[i], k, v)
+    g = lbp.vb_graph(len(nodes), arr)
+    return g, arr
+
+
+def _mlp_graph(weight=16):
+    return _graph([dict(op=0, in0=-1, in1=-1, c=4, h=1, w=1),
+                   dict(op=1, in0=0, in1=-1, c=5, h=1, w=1, weight=weight, bias=32),
+                   dict(op=3, in0=1, in1=-1, c=5, h=1, w=1),
+                   dict(op=1, in0=2, in1=-1, c=3, h=1, w=1, weight=weight, bias=32)])
+
+
+def ws_size(g, batch=2, m=2, method=1, region=0):
+    out = ctypes.c_size_t(0)
+    st = lbp.lib().vb_workspace_size(ctypes.pointer(g), batch, m, method, region, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_size_and_shape_errors():
+    g, keep = _mlp_graph()
+    st, n = ws_size(g)
+    assert st == 0 and n > 0
+    # whole-batch workspace grows with the batch
+    assert ws_size(g, batch=8)[1] > n
+    # NULL weight, bad input index, bad op, shape mismatch, bad method
+    g2, k2 = _mlp_graph(weight=None)
+    assert ws_size(g2)[0] == -1 and b"weight is NULL" in lbp.lib().vb_last_error()
+    g3, k3 = _graph([dict(op=0, in0=-1, in1=-1, c=4, h=1, w=1), dict(op=1, in0=3, in1=-1, c=5, h=1, w=1, weight=16)])
+    assert ws_size(g3)[0] == -2
+    g4, k4 = _graph([dict(op=0, in0=-1, in1=-1, c=4, h=1, w=1), dict(op=9, in0=0, in1=-1, c=5, h=1, w=1)])
+    assert ws_size(g4)[0] == -1
+    g5, k5 = _graph([dict(op=0, in0=-1, in1=-1, c=4, h=1, w=1), dict(op=3, in0=0, in1=-1, c=5, h=1, w=1)])
+    assert ws_size(g5)[0] == -2 and b"relu shape" in lbp.lib().vb_last_error()
+    assert ws_size(g, method=7)[0] == -1
+    assert ws_size(g, batch=0)[0] == -1
+
+
+def test_conv_shape_checks():
+    base = dict(op=0, in0=-1, in1=-1, c=3, h=8, w=8)
+    ok = dict(op=2, in0=0, in1=-1, c=4, h=4, w=4, kh=3, kw=3, stride=2, pad=1, weight=16, bias=0)
+    g, k = _graph([base, ok])
+    assert ws_size(g, m=0, method=0)[0] == 0
+    bad = dict(ok, h=5)
+    g, k = _graph([base, bad])
+    assert ws_size(g, m=0, method=0)[0] == -2 and b"conv output" in lbp.lib().vb_last_error()
+    big = dict(ok, kh=5, kw=5, h=3, w=3)
+    g, k = _graph([base, big])
+    assert ws_size(g, m=0, method=0)[0] == -5
+
+
+def test_entry_points_reject_bad_arguments_without_launching():
+    g, keep = _mlp_graph()
+    gp = ctypes.pointer(g)
+    P = ctypes.c_void_p
+    nulls = (ctypes.c_void_p * 4)()
+    # NULL x_center
+    assert lbp.lib().vb_crown(gp, 2, None, None, 0.1, 1, 0, nulls, nulls, None, 0, None, None, None, None,
+                             P(64), 1 << 20, None) == -1
+    # NULL bounds storage for a node
+    assert lbp.lib().vb_crown(gp, 2, P(64), None, 0.1, 1, 0, nulls, nulls, None, 0, None, None, None, None,
+                             P(64), 1 << 20, None) == -1
+    assert b"bounds storage" in lbp.lib().vb_last_error()
+    # negative eps without a radius array
+    assert lbp.lib().vb_ibp(gp, 2, P(64), None, -1.0, nulls, nulls, None, 0, None, None, None, 0, None) == -1
+    # crown_backward: stop >= start, missing workspace
+    assert lbp.lib().vb_crown_backward(gp, 2, 1, 1, None, 0, nulls, nulls, P(64), None, 0.1, None, None, None, None,
+                                      P(64), 1 << 20, None) == -1
+    assert lbp.lib().vb_crown_backward(gp, 2, 3, 0, None, 0, nulls, nulls, P(64), None, 0.1, None, None, None, None,
+                                      None, 0, None) == -1
+    # workspace too small: reported before any launch
+    bounds = (ctypes.c_void_p * 4)(None, 64, 64, 64)
+    assert lbp.lib().vb_crown(gp, 2, P(64), None, 0.1, 1, 0, bounds, bounds, P(64), 2, None, None, P(64), P(64),
+                             P(64), 16, None) in (-3,)
+    assert b"too small" in lbp.lib().vb_last_error()
+    # concretize argument checks
+    assert lbp.lib().vb_concretize(0, 4, 1, P(64), None, P(64), None, 0.1, None, None, None) == -1
+    assert lbp.lib().vb_concretize(2, 4, 1, None, None, P(64), None, 0.1, None, None, None) == -1

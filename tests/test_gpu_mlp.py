@@ -1,0 +1,98 @@
+"""GPU parity: IBP and CROWN on MLPs through the C ABI against the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wk
+from helpers import assert_close, ensure_built, near_ties
+from oracle import crown_bounds
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lbp():
+    ensure_built()
+    import linear_bound_propagation_amd as m
+    return m
+
+
+def _run(lbp, wl, method=None):
+    net, x, C = lbp.prepare(wl)
+    out = lbp.crown(net, x, float(wl.eps), C, method or wl.intermediate, wl.region_start)
+    torch.cuda.synchronize()
+    return net, out
+
+
+def _compare(wl, out, ref, batch_idx=None, check_nodes=True):
+    idx = list(range(wl.batch)) if batch_idx is None else list(batch_idx)
+    relu_inputs = [wl.nodes[k].inputs[0] for k, n in enumerate(wl.nodes) if n.op == "relu"]
+    ties = near_ties({z: ref["lo"][z][idx] for z in relu_inputs},
+                     {z: ref["hi"][z][idx] for z in relu_inputs}, relu_inputs)
+    print(f"{wl.name}: near-tie neurons in the oracle: {ties}", flush=True)
+    for key in ("lb", "ub", "ibp_lb", "ibp_ub"):
+        assert_close(out[key][idx], ref[key][idx], key)
+    if check_nodes:
+        for k, nd in enumerate(wl.nodes):
+            if k == 0 or nd.op not in ("linear", "conv", "add"):
+                continue
+            assert_close(out["lo"][k][idx], ref["lo"][k][idx].reshape(len(idx), -1), f"lo[{k}]")
+            assert_close(out["hi"][k][idx], ref["hi"][k][idx].reshape(len(idx), -1), f"hi[{k}]")
+
+
+@pytest.mark.parametrize("widths,batch,eps,seed", [
+    ([50, 130, 97, 200, 11], 5, 0.05, 1),      # ragged: no dimension a multiple of the tiles
+    ([37, 64, 128, 33, 7], 3, 0.1, 2),
+    ([300, 257, 129, 10], 9, 0.02, 3),
+])
+def test_mlp_small_ragged(lbp, widths, batch, eps, seed):
+    print(f"mlp {widths} batch {batch} eps {eps}", flush=True)
+    wl = wk.tiny_mlp(widths, eps, seed, batch=batch)
+    for method in ("crown", "ibp"):
+        wl.intermediate = method
+        ref = crown_bounds(wl)
+        _, out = _run(lbp, wl)
+        _compare(wl, out, ref)
+
+
+def test_config1_full(lbp):
+    wl = wk.config(1)
+    print(wl.name, flush=True)
+    ref = crown_bounds(wl)
+    _, out = _run(lbp, wl)
+    _compare(wl, out, ref)
+    # sound and ordered
+    assert bool((out["lb"] <= out["ub"]).all())
+
+
+def test_config2_full_size_sampled_inputs(lbp):
+    wl = wk.config(2)
+    print(wl.name, flush=True)
+    _, out = _run(lbp, wl)
+    idx = [0, 37, 63]
+    ref = crown_bounds(wl, batch_idx=idx)
+    _compare(wl, out, ref, batch_idx=idx)
+
+
+def test_determinism_bitwise(lbp):
+    wl = wk.tiny_mlp([300, 257, 129, 10], 0.02, 3, batch=9)
+    net, x, C = lbp.prepare(wl)
+    a = lbp.crown(net, x, float(wl.eps), C, "crown")
+    b = lbp.crown(net, x, float(wl.eps), C, "crown")
+    torch.cuda.synchronize()
+    for key in ("lb", "ub", "ibp_lb", "ibp_ub"):
+        assert torch.equal(a[key], b[key]), key
+    for k in range(1, len(wl.nodes)):
+        assert torch.equal(a["lo"][k], b["lo"][k]) and torch.equal(a["hi"][k], b["hi"][k])
+
+
+def test_chunked_workspace_matches_whole_batch(lbp):
+    wl = wk.tiny_mlp([120, 90, 80, 6], 0.05, 4, batch=7)
+    net, x, C = lbp.prepare(wl)
+    full = lbp.crown(net, x, float(wl.eps), C, "crown")
+    per_b = net.workspace_size(1, C.shape[1], "crown")
+    ws = net.workspace(per_b * 2)           # room for about two batch elements at a time
+    part = lbp.crown(net, x, float(wl.eps), C, "crown", ws=ws)
+    torch.cuda.synchronize()
+    for key in ("lb", "ub"):
+        assert torch.equal(full[key], part[key]), key
