@@ -170,8 +170,7 @@ GemmDesc linear_backward(const NodeInfo& nd, const NodeInfo& in, const float* la
   d.A = lam;
   d.cs = d.K;
   d.a_row_stride = d.K;
-  d.B = nd.W;
-  d.btrans = 0;
+  d.B = nd.W;  // replaced by the transposed copy [n_in][n_out]
   return d;
 }
 
@@ -204,8 +203,7 @@ bool conv_backward(const NodeInfo& nd, const NodeInfo& in, const float* lam, int
   d.N = in.c;
   d.M = rows * gh * gw;
   d.A = lam;
-  d.B = nd.W;
-  d.btrans = 0;
+  d.B = nd.W;  // replaced by the transposed copy [tap][c_in][c_out]
   d.ho = in.h;
   d.wo = in.w;
   d.oym = s;
@@ -224,8 +222,7 @@ GemmDesc affine_forward(const NodeInfo& nd, const NodeInfo& in, int batch) {
     d.N = nd.c;
     d.cs = d.K;
     d.a_row_stride = d.K;
-    d.B = nd.W;
-    d.btrans = 1;
+    d.B = nd.W;  // [n_out][n_in] = [N][K]
     return d;
   }
   d.gh = nd.h;
@@ -246,8 +243,7 @@ GemmDesc affine_forward(const NodeInfo& nd, const NodeInfo& in, int batch) {
   d.K = d.ntaps * in.c;
   d.N = nd.c;
   d.M = batch * nd.h * nd.w;
-  d.B = nd.W;
-  d.btrans = 1;
+  d.B = nd.W;  // [tap][c_out][c_in] = [tap][N][cs]
   d.ho = nd.h;
   d.wo = nd.w;
   return d;
@@ -277,6 +273,8 @@ struct Backward {
   // alpha-CROWN extras (per node, may be NULL)
   const float* const* alpha = nullptr;
   float* const* psi_keep = nullptr;
+  // K-contiguous weight copies for back-substitution, per node
+  std::vector<const float*> wt;
 
   int alloc() {
     for (int i = 0; i < NPOOL; ++i)
@@ -407,7 +405,7 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
     const float* bias = nullptr;
     vb_status s = effective_bias(B, G, c.start, bias);
     if (s) return s;
-    HIPCHK(launch_spec_init(c.C, c.cb, c.m, (int)S.size, bias, B.pool[b], B.rowacc, c.split, B.st));
+    HIPCHK(launch_spec_init(c.C, c.cb, c.m, (int)S.size, bias, S.c, B.pool[b], B.rowacc, c.split, B.st));
     lam[c.start] = b;
   } else {
     // identity rows; fast path: Linear start whose input is a ReLU
@@ -421,7 +419,7 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
       if (s) return s;
       const long long off = (long long)c.b0 * G.n[z].size;
       HIPCHK(launch_identity_linear(S.W, (int)S.size, (int)G.n[z].size, S.b, B.lo[z] + off, B.hi[z] + off, bias_z,
-                                    c.cb, B.pool[b], B.rowacc, B.st));
+                                    G.n[z].c, c.cb, B.pool[b], B.rowacc, B.st));
       lam[z] = b;
       from = z;
     } else {
@@ -433,7 +431,7 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
       HIPCHK(launch_fill(B.rowacc, 0.f, rows, B.st));
       if (bias) {
         // beta of identity rows = +-bias[i]; reuse the spec-init kernel on the identity
-        HIPCHK(launch_spec_init(B.pool[b], c.cb, (int)(R), (int)S.size, bias, B.pool[b], B.rowacc, 0, B.st));
+        HIPCHK(launch_spec_init(B.pool[b], c.cb, (int)(R), (int)S.size, bias, S.c, B.pool[b], B.rowacc, 0, B.st));
       }
       lam[c.start] = b;
     }
@@ -491,10 +489,13 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
       }
       const int tgt_bounds = (epi == E_RELAX) ? z : t;
       for (GemmDesc& d : descs) {
+        d.B = B.wt[k];
         d.epi = epi;
         d.rows_per_b = (int)R;
         d.addend = (pend >= 0) ? B.pool[pend] : nullptr;
         d.bias = bias;
+        // a Lambda over a flattened [h][w][c] node indexes its per-channel bias by n % c
+        d.bias_c = G.n[epi == E_RELAX ? z : t].c;
         if (epi != E_CONCRETIZE) d.out = B.pool[outb];
         if (epi == E_RELAX) {
           d.lo = B.lo[tgt_bounds] + chunk_off(tgt_bounds);
@@ -672,6 +673,38 @@ void bwd_requirements(const Graph& G, int start, int stop, long long R, long lon
   }
 }
 
+// Floats of the transposed weight copies at the head of the workspace.
+size_t wt_floats(const Graph& G) {
+  size_t f = 0;
+  for (const NodeInfo& n : G.n) {
+    if (n.op == VB_LINEAR) f += align_up((size_t)n.size * G.n[n.in0].size * 4) / 4;
+    if (n.op == VB_CONV2D) f += align_up((size_t)n.kh * n.kw * n.c * G.n[n.in0].c * 4) / 4;
+  }
+  return f;
+}
+
+// Write W^T of every affine node into ws (Linear: [n_in][n_out]; Conv: per tap
+// [c_in][c_out]) and return the per-node pointers.
+vb_status prepare_wt(const Graph& G, char* ws, hipStream_t st, std::vector<const float*>& wt) {
+  wt.assign(G.n.size(), nullptr);
+  float* p = (float*)ws;
+  for (size_t k = 0; k < G.n.size(); ++k) {
+    const NodeInfo& n = G.n[k];
+    if (n.op == VB_LINEAR) {
+      const int nin = (int)G.n[n.in0].size;
+      HIPCHK(launch_transpose(n.W, 1, (int)n.size, nin, p, st));
+      wt[k] = p;
+      p += align_up((size_t)n.size * nin * 4) / 4;
+    } else if (n.op == VB_CONV2D) {
+      const int cin = G.n[n.in0].c;
+      HIPCHK(launch_transpose(n.W, n.kh * n.kw, n.c, cin, p, st));
+      wt[k] = p;
+      p += align_up((size_t)n.kh * n.kw * n.c * cin * 4) / 4;
+    }
+  }
+  return VB_OK;
+}
+
 struct WsLayout {
   size_t pool_floats;  // per buffer
   size_t part_floats;
@@ -825,7 +858,7 @@ static size_t crown_workspace(const Graph& G, int batch, int m, int method, int 
     long long maxw, ppb;
     bwd_requirements(G, start, stop, R, maxw, ppb);
     if (spec) maxw = std::max(maxw, G.n[start].size);
-    best = std::max(best, layout_for(maxw, ppb, R, batch, 0).bytes);
+    best = std::max(best, layout_for(maxw, ppb, R, batch, wt_floats(G)).bytes);
   };
   const int L = G.L;
   if (m > 0) {
@@ -871,7 +904,9 @@ static vb_status spec_ibp(const Graph& G, int batch, const float* C, int m, cons
   const int stop = src_of(G, G.n[L].in0);
   if (stop == 0) return fail(VB_EUNSUPPORTED, "spec IBP over a single affine layer: use CROWN (exact)");
   Backward B{G, st, lo, hi, {nullptr, nullptr, 0.f}};
-  return backward_all(B, L, stop, C, m, 1, batch, 2LL * m, (char*)ws, ws_bytes, 0,
+  vb_status s = prepare_wt(G, (char*)ws, st, B.wt);
+  if (s) return s;
+  return backward_all(B, L, stop, C, m, 1, batch, 2LL * m, (char*)ws, ws_bytes, wt_floats(G),
                       [&](float* acc, int b0, int cb) -> vb_status {
                         HIPCHK(launch_finish(acc, cb, m, spec_lo ? spec_lo + (long long)b0 * m : nullptr,
                                              spec_hi ? spec_hi + (long long)b0 * m : nullptr, nullptr, st));
@@ -907,9 +942,11 @@ static vb_status crown_backward_impl(const Graph& G, int batch, int start, int s
                                      const float* const* lo, const float* const* hi, Domain dom, float* lb,
                                      float* ub, void* ws, size_t ws_bytes, hipStream_t st) {
   Backward B{G, st, lo, hi, dom};
+  vb_status s = prepare_wt(G, (char*)ws, st, B.wt);
+  if (s) return s;
   const long long R = C ? 2LL * m : 2LL * G.n[start].size;
   const int half = (int)(R / 2);
-  return backward_all(B, start, stop, C, m, 1, batch, R, (char*)ws, ws_bytes, 0,
+  return backward_all(B, start, stop, C, m, 1, batch, R, (char*)ws, ws_bytes, wt_floats(G),
                       [&](float* acc, int b0, int cb) -> vb_status {
                         HIPCHK(launch_finish(acc, cb, half, lb ? lb + (long long)b0 * half : nullptr,
                                              ub ? ub + (long long)b0 * half : nullptr, nullptr, st));

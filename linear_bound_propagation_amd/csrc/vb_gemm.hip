@@ -1,0 +1,520 @@
+// fp32 MFMA implicit GEMM for CDNA4 (gfx950): CROWN back-substitution and IBP.
+//
+// The hot operation of CROWN back-substitution (the A matrices of "Scaling
+// Neural Network Verification with Tensor Parallelism and Fully Sharded Data
+// Parallelism", Sec. 1 and Sec. 4.1) is Psi = Lambda W for Linear nodes and
+// Psi = conv^T(Lambda, W) for Conv nodes, followed by the ReLU relaxation with
+// slopes taken from intermediate bounds (Sec. 2.1).  Both are one implicit
+// GEMM here: an output position gathers its A row from up to 9 shifted
+// positions of a channels-last source (one "tap" each) and the reduction runs
+// over (tap, channel); a plain GEMM is the one-tap, one-position case.  IBP's
+// W c and |W| r share the same kernel (two accumulator sets, one B tile).
+//
+// Work decomposition: 256 threads = 4 wavefronts of 64 per workgroup, a
+// BM x BN output tile, 32-deep K stages double-buffered in LDS.  Each
+// wavefront owns a (BM/WM) x (BN/WN) sub-tile made of 32x32 blocks computed
+// with v_mfma_f32_32x32x2f32.  LDS rows are K-contiguous (A as [m][k], B as
+// [n][k]) and padded to 36 floats, so a lane fetches four consecutive k of its
+// row with one 128-bit LDS read and eight lanes of a read cover 32 distinct
+// banks.  The B operand is always stored K-contiguous in HBM ([tap][N][K]):
+// the host transposes weights once per call where needed.  When every K
+// stage lies inside one tap and rows are 16-byte aligned ("fast" path), the
+// global loads are float4 with one bounds decision per row and stage;
+// otherwise a scalar path handles ragged K, C_in = 3 and odd alignments.
+//
+// The epilogue applies the ReLU relaxation (or concretisation, or the IBP
+// interval arithmetic) to each output element and reduces each output row to
+// one partial sum per N-tile; those partials are summed later in a fixed
+// order, so results are bitwise reproducible without float atomics.
+#include <hip/hip_runtime.h>
+
+#include "vb_internal.h"
+
+namespace vb {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+namespace {
+
+constexpr int BK = 32;
+constexpr int LDK = BK + 4;  // LDS row stride in floats
+
+struct Pos {
+  long long a_base;
+  int Y, X;
+  bool valid;
+};
+
+template <bool DENSE>
+__device__ __forceinline__ Pos pos_of(const GemmDesc& d, int m) {
+  Pos p;
+  p.valid = m < d.M;
+  const int mm = p.valid ? m : 0;
+  if (DENSE) {
+    p.a_base = (long long)mm * d.a_row_stride;
+    p.Y = p.X = 0;
+  } else {
+    const int P = d.gh * d.gw;
+    const int row = mm / P;
+    const int q = mm - row * P;
+    p.Y = q / d.gw;
+    p.X = q - p.Y * d.gw;
+    p.a_base = (long long)row * d.a_row_stride;
+  }
+  return p;
+}
+
+// A offset of (position, reduction index k), or -1 for padding.
+template <bool DENSE>
+__device__ __forceinline__ long long a_off(const GemmDesc& d, const Pos& p, int k) {
+  if (!p.valid || k >= d.K) return -1;
+  if (DENSE) return p.a_base + k;
+  const int j = (d.ntaps == 1) ? 0 : k / d.cs;
+  const int c = k - j * d.cs;
+  const int yy = p.Y * d.sy + d.tap_dy[j];
+  const int xx = p.X * d.sx + d.tap_dx[j];
+  if (yy < 0 || yy >= d.hs || xx < 0 || xx >= d.ws) return -1;
+  return p.a_base + ((long long)yy * d.ws + xx) * d.cs + c;
+}
+
+// B offset of (k, n) in the [tap][N][cs] layout, or -1.
+__device__ __forceinline__ long long b_off(const GemmDesc& d, int k, int n) {
+  if (k >= d.K || n >= d.N) return -1;
+  const int j = (d.ntaps == 1) ? 0 : k / d.cs;
+  const int c = k - j * d.cs;
+  return ((long long)d.tap_w[j] * d.N + n) * d.cs + c;
+}
+
+template <int AMODE>
+__device__ __forceinline__ void a_val(const GemmDesc& d, long long off, float& c, float& r) {
+  if (off < 0) {
+    c = r = 0.f;
+  } else if (AMODE == A_PLAIN) {
+    c = d.A[off];
+    r = 0.f;
+  } else if (AMODE == A_IBP_BOX) {
+    const float l = d.A[off], u = d.A2[off];
+    c = (l + u) * 0.5f;
+    r = (u - l) * 0.5f;
+  } else {
+    c = d.A[off];
+    r = d.A2 ? d.A2[off] : d.eps;
+  }
+}
+
+template <int AMODE>
+__device__ __forceinline__ void a_val4(const GemmDesc& d, long long off, float4& c, float4& r) {
+  if (off < 0) {
+    c = r = make_float4(0.f, 0.f, 0.f, 0.f);
+  } else if (AMODE == A_PLAIN) {
+    c = *reinterpret_cast<const float4*>(d.A + off);
+  } else if (AMODE == A_IBP_BOX) {
+    const float4 l = *reinterpret_cast<const float4*>(d.A + off);
+    const float4 u = *reinterpret_cast<const float4*>(d.A2 + off);
+    c = make_float4((l.x + u.x) * 0.5f, (l.y + u.y) * 0.5f, (l.z + u.z) * 0.5f, (l.w + u.w) * 0.5f);
+    r = make_float4((u.x - l.x) * 0.5f, (u.y - l.y) * 0.5f, (u.z - l.z) * 0.5f, (u.w - l.w) * 0.5f);
+  } else {
+    c = *reinterpret_cast<const float4*>(d.A + off);
+    r = d.A2 ? *reinterpret_cast<const float4*>(d.A2 + off) : make_float4(d.eps, d.eps, d.eps, d.eps);
+  }
+}
+
+}  // namespace
+
+template <int BM, int BN, int WM, int WN, bool DENSE, int AMODE, int EPI, bool FAST>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
+  constexpr int NTHR = WM * WN * 64;
+  constexpr int NA = (AMODE == A_PLAIN) ? 1 : 2;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int NR = (AMODE == A_PLAIN) ? 1 : FM;   // radius accumulators (IBP)
+  constexpr int NC = (AMODE == A_PLAIN) ? 1 : FN;
+  // per-thread load slots
+  constexpr int AV = BM * (BK / 4) / NTHR;                 // float4 of A
+  constexpr int BV = (BN * (BK / 4) + NTHR - 1) / NTHR;    // float4 of B
+  constexpr int AS = BM * BK / NTHR;                       // scalars of A (slow path)
+  constexpr int BS = (BN * BK + NTHR - 1) / NTHR;          // scalars of B (slow path)
+  static_assert(FM >= 1 && FN >= 1 && AV >= 1, "tile");
+
+  __shared__ __attribute__((aligned(16))) float As[2][NA][BM * LDK];
+  __shared__ __attribute__((aligned(16))) float Bs[2][BN * LDK];
+  __shared__ float red[WN][BM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int l32 = lane & 31, half = lane >> 5;
+
+  // XCD-aware tile order: workgroups go round-robin over the 8 XCDs, so each
+  // XCD gets a contiguous run of tiles with the N-tiles of one M-tile next to
+  // each other; an M-tile's A rows are then fetched into one XCD's L2 once.
+  const int mt = (d.M + BM - 1) / BM;
+  const int nt = (d.N + BN - 1) / BN;
+  const int total = mt * nt;
+  const int per_xcd = (total + 7) / 8;
+  const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (tile >= total) return;
+  const int tm = tile / nt, tn = tile - tm * nt;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // register staging of the next K stage
+  float4 ra[NA][FAST ? AV : 1];
+  float4 rb[FAST ? BV : 1];
+  float sa[NA][FAST ? 1 : AS];
+  float sb[FAST ? 1 : BS];
+  Pos apos[FAST ? AV : 1];
+  if (FAST) {
+#pragma unroll
+    for (int i = 0; i < AV; ++i) apos[i] = pos_of<DENSE>(d, m0 + (tid + NTHR * i) / (BK / 4));
+  }
+
+  auto load = [&](int k0) {
+    if (FAST) {
+      // one tap per stage: k0 .. k0+31 share tap j
+      const int j = (d.ntaps == 1) ? 0 : k0 / d.cs;
+      const int c0 = k0 - j * d.cs;
+#pragma unroll
+      for (int i = 0; i < AV; ++i) {
+        const int f = tid + NTHR * i;
+        const int kq = (f % (BK / 4)) * 4;
+        long long off = -1;
+        const Pos& p = apos[i];
+        if (p.valid) {
+          if (DENSE) {
+            off = p.a_base + k0 + kq;
+          } else {
+            const int yy = p.Y * d.sy + d.tap_dy[j];
+            const int xx = p.X * d.sx + d.tap_dx[j];
+            if (yy >= 0 && yy < d.hs && xx >= 0 && xx < d.ws)
+              off = p.a_base + ((long long)yy * d.ws + xx) * d.cs + c0 + kq;
+          }
+        }
+        float4 r4;
+        a_val4<AMODE>(d, off, ra[0][i], r4);
+        if (NA == 2) ra[NA - 1][i] = r4;
+      }
+      const long long bt = (long long)d.tap_w[j] * d.N;
+#pragma unroll
+      for (int i = 0; i < BV; ++i) {
+        const int f = tid + NTHR * i;
+        const int n = f / (BK / 4), kq = (f % (BK / 4)) * 4;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (f < BN * (BK / 4) && n0 + n < d.N)
+          v = *reinterpret_cast<const float4*>(d.B + (bt + n0 + n) * d.cs + c0 + kq);
+        rb[i] = v;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < AS; ++i) {
+        const int e = tid + NTHR * i;
+        const Pos p = pos_of<DENSE>(d, m0 + e / BK);
+        float c, r;
+        a_val<AMODE>(d, a_off<DENSE>(d, p, k0 + (e % BK)), c, r);
+        sa[0][i] = c;
+        if (NA == 2) sa[NA - 1][i] = r;
+      }
+#pragma unroll
+      for (int i = 0; i < BS; ++i) {
+        const int e = tid + NTHR * i;
+        float v = 0.f;
+        if (e < BN * BK) {
+          const long long off = b_off(d, k0 + (e % BK), n0 + e / BK);
+          if (off >= 0) v = d.B[off];
+        }
+        sb[i] = v;
+      }
+    }
+  };
+  auto store = [&](int buf) {
+    if (FAST) {
+#pragma unroll
+      for (int i = 0; i < AV; ++i) {
+        const int f = tid + NTHR * i;
+        const int row = f / (BK / 4), kq = (f % (BK / 4)) * 4;
+        *reinterpret_cast<float4*>(&As[buf][0][row * LDK + kq]) = ra[0][i];
+        if (NA == 2) *reinterpret_cast<float4*>(&As[buf][NA - 1][row * LDK + kq]) = ra[NA - 1][i];
+      }
+#pragma unroll
+      for (int i = 0; i < BV; ++i) {
+        const int f = tid + NTHR * i;
+        if (f < BN * (BK / 4)) {
+          const int n = f / (BK / 4), kq = (f % (BK / 4)) * 4;
+          *reinterpret_cast<float4*>(&Bs[buf][n * LDK + kq]) = rb[i];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < AS; ++i) {
+        const int e = tid + NTHR * i;
+        As[buf][0][(e / BK) * LDK + (e % BK)] = sa[0][i];
+        if (NA == 2) As[buf][NA - 1][(e / BK) * LDK + (e % BK)] = sa[NA - 1][i];
+      }
+#pragma unroll
+      for (int i = 0; i < BS; ++i) {
+        const int e = tid + NTHR * i;
+        if (e < BN * BK) Bs[buf][(e / BK) * LDK + (e % BK)] = sb[i];
+      }
+    }
+  };
+
+  f32x16 acc[FM][FN];
+  f32x16 accr[NR][NC];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) accr[i][j][v] = 0.f;
+
+  const int nk = (d.K + BK - 1) / BK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int t = 0; t < nk; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < nk) load((t + 1) * BK);
+    // MFMA step (q, s): lane half h supplies k = 16h + 4q + s
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float4 a4[FM], b4[FN], r4[NR];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        a4[i] = *reinterpret_cast<const float4*>(&As[cur][0][(wm * WTM + i * 32 + l32) * LDK + 16 * half + 4 * q]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        b4[j] = *reinterpret_cast<const float4*>(&Bs[cur][(wn * WTN + j * 32 + l32) * LDK + 16 * half + 4 * q]);
+      if (NA == 2) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+          r4[i] = *reinterpret_cast<const float4*>(
+              &As[cur][NA - 1][(wm * WTM + i * 32 + l32) * LDK + 16 * half + 4 * q]);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[i][s], b4[j][s], acc[i][j], 0, 0, 0);
+        if (NA == 2) {
+#pragma unroll
+          for (int i = 0; i < NR; ++i)
+#pragma unroll
+            for (int j = 0; j < NC; ++j)
+              accr[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(r4[i][s], fabsf(b4[j][s]), accr[i][j], 0, 0, 0);
+        }
+      }
+    }
+    if (t + 1 < nk) store(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue.  Register v of lane l of a 32x32 fp32 MFMA result holds
+  // row 8*(v/4) + 4*(l/32) + v%4 and column l%32 of the block.
+  constexpr bool ROWSUM = (EPI != E_IBP);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int lr = wm * WTM + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+      const int m = m0 + lr;
+      float rowsum = 0.f;
+      if (m < d.M) {
+        long long opos, bpos;
+        if (DENSE) {
+          opos = m;
+          bpos = m / d.rows_per_b;
+        } else {
+          const int P = d.gh * d.gw;
+          const int row = m / P;
+          const int q = m - row * P;
+          const int Y = q / d.gw;
+          const int X = q - Y * d.gw;
+          const long long sp = (long long)(Y * d.oym + d.oy0) * d.wo + (X * d.oxm + d.ox0);
+          opos = (long long)row * d.ho * d.wo + sp;
+          bpos = (long long)(row / d.rows_per_b) * d.ho * d.wo + sp;
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int n = n0 + wn * WTN + j * 32 + l32;
+          if (n < d.N) {
+            const long long oi = opos * d.N + n;
+            const long long bi = bpos * d.N + n;
+            const int nb = d.bias_c ? n % d.bias_c : n;
+            float val = acc[i][j][v];
+            if (EPI == E_IBP) {
+              const float cc = val + (d.bias ? d.bias[nb] : 0.f);
+              const float rr = accr[NR == 1 ? 0 : i][NC == 1 ? 0 : j][v];
+              const float l = cc - rr, u = cc + rr;
+              d.out[oi] = l;
+              d.out2[oi] = u;
+              if (d.relu_lo) {
+                d.relu_lo[oi] = fmaxf(l, 0.f);
+                d.relu_hi[oi] = fmaxf(u, 0.f);
+              }
+            } else {
+              if (d.addend) val += d.addend[oi];
+              if (EPI == E_STORE) {
+                d.out[oi] = val;
+                if (d.bias) rowsum += val * d.bias[nb];
+              } else if (EPI == E_RELAX) {
+                const float l = d.lo[bi], u = d.hi[bi];
+                float a, s, tt;
+                if (u <= 0.f) {
+                  a = 0.f; s = 0.f; tt = 0.f;
+                } else if (l >= 0.f) {
+                  a = 1.f; s = 1.f; tt = 0.f;
+                } else {
+                  s = u / (u - l);
+                  tt = -s * l;
+                  a = d.alpha ? d.alpha[oi] : ((u >= -l) ? 1.f : 0.f);
+                }
+                const float o = (val >= 0.f) ? val * a : val * s;
+                d.out[oi] = o;
+                if (d.psi_out) d.psi_out[oi] = val;
+                if (d.bias) rowsum += o * d.bias[nb];
+                rowsum += fminf(val, 0.f) * tt;
+              } else {  // E_CONCRETIZE
+                float c, r;
+                if (d.center) {
+                  c = d.center[bi];
+                  r = d.radius ? d.radius[bi] : d.eps;
+                } else {
+                  const float l = d.lo[bi], u = d.hi[bi];
+                  c = (l + u) * 0.5f;
+                  r = (u - l) * 0.5f;
+                }
+                rowsum += val * c - fabsf(val) * r;
+              }
+            }
+          }
+        }
+      }
+      if (ROWSUM) {
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) rowsum += __shfl_xor(rowsum, o, 32);
+        if (l32 == 0) red[wn][lr] = rowsum;
+      }
+    }
+  }
+  if (ROWSUM) {
+    __syncthreads();
+    if (d.part) {
+      for (int r = tid; r < BM; r += NTHR) {
+        const int m = m0 + r;
+        if (m < d.M) {
+          float s = 0.f;
+#pragma unroll
+          for (int w = 0; w < WN; ++w) s += red[w][r];
+          d.part[(long long)m * d.part_ld + tn] = s;
+        }
+      }
+    }
+  }
+}
+
+namespace {
+
+template <int BM, int BN, int WM, int WN, bool DENSE, bool FAST>
+hipError_t launch_tile(const GemmDesc& d, hipStream_t st) {
+  const int mt = (d.M + BM - 1) / BM;
+  const int nt = (d.N + BN - 1) / BN;
+  const dim3 g(((mt * nt + 7) / 8) * 8), b(WM * WN * 64);
+  switch (d.epi) {
+    case E_STORE:
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_STORE, FAST>), g, b, 0, st, d);
+      break;
+    case E_RELAX:
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_RELAX, FAST>), g, b, 0, st, d);
+      break;
+    case E_CONCRETIZE:
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_CONCRETIZE, FAST>), g, b, 0, st, d);
+      break;
+    case E_IBP:
+      if (d.amode == A_IBP_BOX)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_IBP_BOX, E_IBP, FAST>), g, b, 0, st, d);
+      else
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_IBP_BALL, E_IBP, FAST>), g, b, 0, st, d);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_shape(const GemmDesc& d, bool dense, bool fast, hipStream_t st) {
+  if (dense) return fast ? launch_tile<BM, BN, WM, WN, true, true>(d, st) : launch_tile<BM, BN, WM, WN, true, false>(d, st);
+  return fast ? launch_tile<BM, BN, WM, WN, false, true>(d, st) : launch_tile<BM, BN, WM, WN, false, false>(d, st);
+}
+
+// 256 x 256 tiles on 8 wavefronts (128 x 64 each) for the large back-substitution
+// GEMMs with the fast path, when the grid still has at least two workgroups per CU.
+bool use_big(const GemmDesc& d, bool fast) {
+  if (!fast || d.epi == E_IBP || d.N < 256) return false;
+  const long long tiles = (long long)((d.M + 255) / 256) * ((d.N + 255) / 256);
+  return tiles >= 512;
+}
+
+int tile_n(const GemmDesc& d, bool fast) {
+  if (use_big(d, fast)) return 256;
+  return d.N > 64 ? 128 : (d.N > 32 ? 64 : 32);
+}
+
+bool is_fast(const GemmDesc& d);
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+namespace {
+// fast path: every 32-deep K stage inside one tap, float4-aligned rows
+bool is_fast(const GemmDesc& d) {
+  return d.K > 0 && d.cs % BK == 0 && d.a_row_stride % 4 == 0 && aligned16(d.A) &&
+         (d.A2 == nullptr || aligned16(d.A2)) && aligned16(d.B);
+}
+}  // namespace
+
+int gemm_ntiles(const GemmDesc& d) {
+  const int bn = tile_n(d, is_fast(d));
+  return (d.N + bn - 1) / bn;
+}
+
+hipError_t launch_gemm(const GemmDesc& d, hipStream_t st) {
+  if (d.M <= 0 || d.N <= 0) return hipSuccess;
+  const bool dense = d.gh == 1 && d.gw == 1 && d.hs == 1 && d.ws == 1 && d.ntaps == 1 && d.cs == d.K &&
+                     d.tap_dy[0] == 0 && d.tap_dx[0] == 0 && d.tap_w[0] == 0 && d.ho == 1 && d.wo == 1;
+  const bool fast = is_fast(d);
+  const int bn = tile_n(d, fast);
+  if (bn == 256) {
+    // plain epilogues only (checked in use_big); IBP never takes this tile
+    const int mt = (d.M + 255) / 256, nt = (d.N + 255) / 256;
+    const dim3 g(((mt * nt + 7) / 8) * 8), b(512);
+    if (dense) {
+      switch (d.epi) {
+        case E_STORE: hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 4, true, A_PLAIN, E_STORE, true>), g, b, 0, st, d); break;
+        case E_RELAX: hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 4, true, A_PLAIN, E_RELAX, true>), g, b, 0, st, d); break;
+        default: hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 4, true, A_PLAIN, E_CONCRETIZE, true>), g, b, 0, st, d); break;
+      }
+    } else {
+      switch (d.epi) {
+        case E_STORE: hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 4, false, A_PLAIN, E_STORE, true>), g, b, 0, st, d); break;
+        case E_RELAX: hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 4, false, A_PLAIN, E_RELAX, true>), g, b, 0, st, d); break;
+        default: hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 4, false, A_PLAIN, E_CONCRETIZE, true>), g, b, 0, st, d); break;
+      }
+    }
+    return hipGetLastError();
+  }
+  if (bn == 128) return launch_shape<128, 128, 2, 2>(d, dense, fast, st);
+  if (bn == 64) return launch_shape<128, 64, 2, 2>(d, dense, fast, st);
+  return launch_shape<128, 32, 4, 1>(d, dense, fast, st);
+}
+
+}  // namespace vb

@@ -1,5 +1,5 @@
 // Internal interface between the host planner (vb_api.cpp) and the HIP kernels
-// (vb_kernels.hip).  Not part of the C ABI.
+// (vb_gemm.hip, vb_kernels.hip).  Not part of the C ABI.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
@@ -39,10 +39,9 @@ struct GemmDesc {
   long long a_row_stride;
   int ntaps;
   int tap_dy[MAX_TAPS], tap_dx[MAX_TAPS], tap_w[MAX_TAPS];
-  // ---- B operand (weights), tap-major.  k = j*cs + c:
-  //      !btrans: B[(tap_w[j]*cs + c)*N + n];  btrans: B[(tap_w[j]*N + n)*cs + c]
+  // ---- B operand (weights), tap-major and K-contiguous: k = j*cs + c,
+  //      element (k, n) = B[(tap_w[j]*N + n)*cs + c]
   const float* B;
-  int btrans;
   // ---- output mapping: (row, Y, X) -> row*ho*wo + (Y*oym+oy0)*wo + (X*oxm+ox0)
   int ho, wo, oym, oy0, oxm, ox0;
   int rows_per_b;              // batch element of a row = row / rows_per_b
@@ -55,7 +54,8 @@ struct GemmDesc {
   const float* addend;         // [opos][N] or NULL, added to acc before the epilogue
   const float* lo;             // target-node bounds at [b-pos][N] (E_RELAX, E_CONCRETIZE box)
   const float* hi;
-  const float* bias;           // per output channel n (E_STORE / E_RELAX / E_IBP)
+  const float* bias;           // per output channel (E_STORE / E_RELAX / E_IBP)
+  int bias_c;                  // channels of the bias: index = n % bias_c (0: index = n)
   const float* alpha;          // E_RELAX: per [opos][N] lower slope of unstable neurons, or NULL
   float* psi_out;              // E_RELAX: store the pre-relaxation value v, or NULL
   const float* center;         // E_CONCRETIZE: centre/radius at [b-pos][N]; NULL -> from lo/hi
@@ -79,15 +79,16 @@ hipError_t launch_finish(const float* rowacc, int batch, int R, float* lb, float
                          float* best, hipStream_t st);
 
 // Spec rows: lam[b][r][:] = +C[b][r][:] for r < m and -C[b][r-m][:] for r >= m;
-// rowacc[b*2m + r] = lam[b][r][:] . bias (bias may be NULL).
-hipError_t launch_spec_init(const float* C, int batch, int m, int n, const float* bias,
+// rowacc[b*2m + r] = lam[b][r][:] . bias (bias may be NULL; per channel: index j % bias_c).
+hipError_t launch_spec_init(const float* C, int batch, int m, int n, const float* bias, int bias_c,
                             float* lam, float* rowacc, int rows_sign_split, hipStream_t st);
 
 // Identity rows through a Linear node followed (backwards) by a ReLU relaxation:
 // row (b, s, i), s in {+1,-1}: psi = s*W[i][:]; lam = relax(psi; lo/hi[b][:]);
 // rowacc = s*bias_start[i] + sum_j lam_j bias_z[j] + min(psi_j,0) t_j
+// bias_z is per channel of z: index j % bias_zc (z flattened from a [h][w][c] tensor).
 hipError_t launch_identity_linear(const float* W, int n_out, int n_in, const float* bias_start,
-                                  const float* lo, const float* hi, const float* bias_z,
+                                  const float* lo, const float* hi, const float* bias_z, int bias_zc,
                                   int batch, float* lam, float* rowacc, hipStream_t st);
 
 // Identity rows materialised as a dense matrix: rows (b, s, i) over n, +-1 on the diagonal.
@@ -122,6 +123,9 @@ hipError_t launch_ibp_eltwise(int op, const float* lo0, const float* hi0, const 
 // IBP GAP: lo/hi [b][c] = mean over P positions of [b][p][c]
 hipError_t launch_ibp_gap(const float* lo_in, const float* hi_in, int batch, int P, int C,
                           float* lo, float* hi, hipStream_t st);
+
+// dst[b][c][r] = src[b][r][c] for b < batch (weight layout changes)
+hipError_t launch_transpose(const float* src, int batch, int R, int C, float* dst, hipStream_t st);
 
 // Fill with a constant
 hipError_t launch_fill(float* p, float v, long long n, hipStream_t st);

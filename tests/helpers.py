@@ -52,3 +52,23 @@ def near_ties(lo, hi, relu_inputs, tau=1e-5):
         unst = (l < 0) & (u > 0)
         n += int((unst & ((u + l).abs() <= tau * (u - l))).sum())
     return n
+
+
+def compare_workload(wl, out, ref, batch_idx=None, check_nodes=True, keys=("lb", "ub", "ibp_lb", "ibp_ub")):
+    """Elementwise parity of a vb_crown result with the oracle's crown_bounds result."""
+    idx = list(range(wl.batch)) if batch_idx is None else list(batch_idx)
+    relu_inputs = [wl.nodes[k].inputs[0] for k, n in enumerate(wl.nodes) if n.op == "relu"]
+    ties = near_ties({z: ref["lo"][z][idx] for z in relu_inputs},
+                     {z: ref["hi"][z][idx] for z in relu_inputs}, relu_inputs)
+    print(f"{wl.name} ({wl.intermediate}): near-tie neurons in the oracle: {ties}", flush=True)
+    worst = 0.0
+    for key in keys:
+        worst = max(worst, assert_close(out[key][idx], ref[key][idx], key))
+    if check_nodes:
+        for k, nd in enumerate(wl.nodes):
+            if k == 0 or nd.op not in ("linear", "conv", "add"):
+                continue
+            worst = max(worst, assert_close(out["lo"][k][idx], nhwc(ref["lo"][k][idx], nd.shape), f"lo[{k}]"))
+            worst = max(worst, assert_close(out["hi"][k][idx], nhwc(ref["hi"][k][idx], nd.shape), f"hi[{k}]"))
+    print(f"  worst |d| / allowed = {worst:.3g}", flush=True)
+    return worst
