@@ -131,16 +131,31 @@ vb_status vb_concretize(int32_t rows, int32_t n, int32_t rows_per_batch,
                         const float* center, const float* radius, float eps,
                         float* lb, float* ub, void* stream);
 
+/* alpha-CROWN set-up (Sec. 3 / Sec. 4.3 of the page: per-neuron alpha slope
+ * tensors).  For every ReLU node k, alpha[k] [batch][m][size_k] receives the
+ * adaptive CROWN lower slope of each neuron from the bounds of the ReLU's
+ * input (1 if u >= -l else 0 for unstable neurons; 1 active; 0 inactive),
+ * identical for the m spec rows of an input, and adam_m[k], adam_v[k] are
+ * zeroed.  Entries for non-ReLU nodes are ignored (may be NULL). */
+vb_status vb_alpha_init(const vb_graph* g, int32_t batch, int32_t m,
+                        const float* const* node_lo, const float* const* node_hi,
+                        float* const* alpha, float* const* adam_m, float* const* adam_v, void* stream);
+
 /* One alpha-CROWN step on the lower bounds of spec rows C [batch][m][n_out]
  * (Sec. 3 and Sec. 4.3 of the page: per-neuron alpha slope tensors).
  * alpha, adam_m, adam_v: per node, NULL except for ReLU nodes, each
  * [batch][m][size_k] (one lower slope per input, spec row and neuron; only the
  * unstable neurons' entries are read or changed).  Evaluates the CROWN lower
  * bound with these slopes into lb_out [batch][m] and folds it into best_lb
- * (elementwise max; best_lb may be NULL).  If step >= 1, then also takes one
+ * (elementwise max; at step == 1 best_lb is set to lb; best_lb may be NULL).
+ * If step >= 1, then also takes one
  * bias-corrected Adam ascent step (step = Adam's 1-based t, learning rate lr,
  * beta1, beta2, adam_eps) on sum(lb) and clips alpha to [0, 1].  step == 0
- * only evaluates.  The domain is the input box (stop = node 0). */
+ * only evaluates.  The domain is the input box (stop = node 0).  The graph
+ * must be a chain (Linear/Conv, ReLU, Flatten; every affine node except the
+ * last feeding one ReLU).  The gradient is the exact reverse-mode derivative of
+ * sum(lb) (derivative branch psi >= 0 at psi = 0, sign(0) = 0 at the domain).
+ * The workspace must hold the whole batch (see vb_workspace_size). */
 vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float* C, int32_t m,
                         const float* const* node_lo, const float* const* node_hi,
                         const float* x_center, const float* x_radius, float eps,

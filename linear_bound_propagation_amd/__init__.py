@@ -30,7 +30,7 @@ _OPS = {"input": VB_INPUT, "linear": VB_LINEAR, "conv": VB_CONV2D, "relu": VB_RE
         "gap": VB_GAP, "flatten": VB_FLATTEN}
 
 EXPORTS = ["vb_last_error", "vb_workspace_size", "vb_ibp", "vb_crown_backward", "vb_concretize",
-           "vb_alpha_step", "vb_crown", "vb_profile_start", "vb_profile_stop"]
+           "vb_alpha_init", "vb_alpha_step", "vb_crown", "vb_profile_start", "vb_profile_stop"]
 
 
 class vb_node(ctypes.Structure):
@@ -62,6 +62,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vb_crown_backward.argtypes = [G, i32, i32, i32, P, i32, PP, PP, P, P, f32, P, P, P, P, P, sz, P]
     lib.vb_concretize.restype = i32
     lib.vb_concretize.argtypes = [i32, i32, i32, P, P, P, P, f32, P, P, P]
+    lib.vb_alpha_init.restype = i32
+    lib.vb_alpha_init.argtypes = [G, i32, i32, PP, PP, PP, PP, PP, P]
     lib.vb_alpha_step.restype = i32
     lib.vb_alpha_step.argtypes = [G, i32, P, i32, PP, PP, P, P, f32, PP, PP, PP, i32, f32, f32, f32, f32,
                                   P, P, P, sz, P]
@@ -253,6 +255,19 @@ def crown(net: DeviceNet, x_center: torch.Tensor, eps: float, C: torch.Tensor, m
     return out
 
 
+def alpha_state(net: DeviceNet, batch: int, m: int):
+    """Device tensors alpha, adam_m, adam_v per node ([batch][m][size] for ReLU nodes, None elsewhere)."""
+    mk = lambda: [torch.empty(batch, m, s, device=net.device) if op == "relu" else None
+                  for op, s in zip(net.ops, net.sizes)]
+    return mk(), mk(), mk()
+
+
+def alpha_init(net: DeviceNet, lo, hi, alpha, adam_m, adam_v, m: int):
+    batch = lo[1].shape[0]
+    _check(lib().vb_alpha_init(net.gp, batch, m, _ptr_array(lo), _ptr_array(hi), _ptr_array(alpha),
+                               _ptr_array(adam_m), _ptr_array(adam_v), _stream()), "vb_alpha_init")
+
+
 def alpha_step(net: DeviceNet, C: torch.Tensor, lo, hi, x_center: torch.Tensor, eps: float, alpha, adam_m, adam_v,
                step: int, lr: float, lb_out: torch.Tensor, best_lb: Optional[torch.Tensor], ws: torch.Tensor,
                beta1: float = 0.9, beta2: float = 0.999, adam_eps: float = 1e-8, x_radius=None):
@@ -262,6 +277,30 @@ def alpha_step(net: DeviceNet, C: torch.Tensor, lo, hi, x_center: torch.Tensor, 
                               step, lr, beta1, beta2, adam_eps, _ptr(lb_out), _ptr(best_lb), _ptr(ws), ws.numel(),
                               _stream()), "vb_alpha_step")
     return lb_out
+
+
+def alpha_crown(net: DeviceNet, x_center: torch.Tensor, eps: float, C: torch.Tensor, lo, hi, steps: int,
+                lr: float, ws: torch.Tensor = None, state=None, lb_steps: torch.Tensor = None,
+                best: torch.Tensor = None, x_radius=None):
+    """alpha-CROWN over fixed intermediate bounds lo/hi: vb_alpha_init, then `steps` calls of
+    vb_alpha_step (evaluate, gradient, Adam ascent; the first sets `best`) and one
+    evaluation-only call.  steps must be >= 1.
+    Returns (best [B][m], lb per evaluation [steps+1][B][m], (alpha, adam_m, adam_v))."""
+    batch, m = C.shape[0], C.shape[1]
+    if state is None:
+        state = alpha_state(net, batch, m)
+    alpha, am, av = state
+    if ws is None:
+        ws = net.workspace(net.workspace_size(batch, m, "ibp"))
+    if lb_steps is None:
+        lb_steps = torch.empty(steps + 1, batch, m, device=net.device)
+    if best is None:
+        best = torch.empty(batch, m, device=net.device)
+    alpha_init(net, lo, hi, alpha, am, av, m)
+    for t in range(1, steps + 1):
+        alpha_step(net, C, lo, hi, x_center, eps, alpha, am, av, t, lr, lb_steps[t - 1], best, ws, x_radius=x_radius)
+    alpha_step(net, C, lo, hi, x_center, eps, alpha, am, av, 0, lr, lb_steps[steps], best, ws, x_radius=x_radius)
+    return best, lb_steps, state
 
 
 def profile_start():

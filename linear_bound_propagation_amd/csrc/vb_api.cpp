@@ -13,6 +13,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -504,6 +505,7 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
           if (B.psi_keep && B.psi_keep[t]) d.psi_out = B.psi_keep[t];
         }
         if (epi == E_CONCRETIZE) {
+          if (B.psi_keep && B.psi_keep[t]) d.psi_out = B.psi_keep[t];
           if (t == 0) {
             d.center = B.dom.xc + chunk_off(0);
             d.radius = B.dom.xr ? B.dom.xr + chunk_off(0) : nullptr;
@@ -875,12 +877,13 @@ static size_t crown_workspace(const Graph& G, int batch, int m, int method, int 
     }
     if (m > 0 && method == VB_METHOD_HYBRID) consider(L, stop, 2LL * m, true);
   }
-  if (m > 0) {
-    // alpha-CROWN evaluation (lower rows only) plus its kept products
-    consider(L, 0, m, true);
-  }
   return best;
 }
+
+namespace {
+bool alpha_chain(const Graph& G, std::vector<std::pair<int, int>>& chain);
+size_t alpha_workspace(const Graph& G, int batch, int m);
+}  // namespace
 
 extern "C" vb_status vb_workspace_size(const vb_graph* g, int32_t batch, int32_t m, int32_t method,
                                        int32_t region_start, size_t* bytes) {
@@ -893,6 +896,8 @@ extern "C" vb_status vb_workspace_size(const vb_graph* g, int32_t batch, int32_t
   if (method == VB_METHOD_HYBRID && (region_start <= 0 || region_start >= G.L))
     return fail(VB_EINVAL, "region_start %d out of range", region_start);
   *bytes = crown_workspace(G, batch, m, method, region_start);
+  std::vector<std::pair<int, int>> chain;
+  if (m > 0 && alpha_chain(G, chain)) *bytes = std::max(*bytes, alpha_workspace(G, batch, m));
   return VB_OK;
 }
 
@@ -1066,14 +1071,167 @@ extern "C" vb_status vb_profile_stop(double* ms, double* flops, int64_t* launche
   return VB_OK;
 }
 
+// ---------------------------------------------------------------------------
+// alpha-CROWN
+
+namespace {
+
+// Affine nodes of a chain network in forward order, each with the ReLU that
+// follows it (-1 for the last node).  Returns false if the graph is not a chain.
+bool alpha_chain(const Graph& G, std::vector<std::pair<int, int>>& chain) {
+  chain.clear();
+  for (size_t k = 1; k < G.n.size(); ++k) {
+    const NodeInfo& n = G.n[k];
+    if (n.op == VB_ADD || n.op == VB_GAP) return false;
+    if (n.op != VB_LINEAR && n.op != VB_CONV2D) continue;
+    if ((int)k == G.L) {
+      chain.push_back({(int)k, -1});
+      continue;
+    }
+    if (n.cons.size() != 1 || G.n[n.cons[0]].op != VB_RELU) return false;
+    const int r = n.cons[0];
+    // the ReLU feeds exactly one affine node, possibly through flatten
+    std::vector<int> c = G.n[r].cons;
+    while (c.size() == 1 && G.n[c[0]].op == VB_FLATTEN) c = G.n[c[0]].cons;
+    if (c.size() != 1) return false;
+    chain.push_back({(int)k, r});
+  }
+  return !chain.empty() && chain.back().first == G.L && G.n[G.L].op == VB_LINEAR;
+}
+
+size_t alpha_psi_floats(const Graph& G, long long rows) {
+  size_t f = align_up((size_t)rows * G.n[0].size * 4) / 4;
+  for (const NodeInfo& n : G.n)
+    if (n.op == VB_RELU) f += align_up((size_t)rows * n.size * 4) / 4;
+  return f;
+}
+
+size_t alpha_workspace(const Graph& G, int batch, int m) {
+  const long long R = m;
+  long long maxw, ppb;
+  bwd_requirements(G, G.L, 0, R, maxw, ppb);
+  maxw = std::max(maxw, G.n[G.L].size);
+  return layout_for(maxw, ppb, R, batch, wt_floats(G) + alpha_psi_floats(G, (long long)batch * m)).bytes;
+}
+
+}  // namespace
+
+extern "C" vb_status vb_alpha_init(const vb_graph* g, int32_t batch, int32_t m, const float* const* node_lo,
+                                   const float* const* node_hi, float* const* alpha, float* const* adam_m,
+                                   float* const* adam_v, void* stream) {
+  Graph G;
+  vb_status s = parse_graph(g, G);
+  if (s) return s;
+  if (batch <= 0 || m <= 0) return fail(VB_EINVAL, "batch and m must be positive");
+  if (!node_lo || !node_hi || !alpha || !adam_m || !adam_v) return fail(VB_EINVAL, "NULL pointer array");
+  for (size_t k = 0; k < G.n.size(); ++k) {
+    if (G.n[k].op != VB_RELU) continue;
+    const int z = G.n[k].in0;
+    if (!alpha[k] || !adam_m[k] || !adam_v[k] || !node_lo[z] || !node_hi[z])
+      return fail(VB_EINVAL, "ReLU node %zu: alpha / adam state / input bounds missing", k);
+  }
+  for (size_t k = 0; k < G.n.size(); ++k) {
+    if (G.n[k].op != VB_RELU) continue;
+    const int z = G.n[k].in0;
+    HIPCHK(launch_alpha_init(node_lo[z], node_hi[z], batch, m, G.n[z].size, alpha[k], adam_m[k], adam_v[k],
+                             (hipStream_t)stream));
+  }
+  return VB_OK;
+}
+
 extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float* C, int32_t m,
                                    const float* const* node_lo, const float* const* node_hi, const float* x_center,
                                    const float* x_radius, float eps, float* const* alpha, float* const* adam_m,
                                    float* const* adam_v, int32_t step, float lr, float beta1, float beta2,
                                    float adam_eps, float* lb_out, float* best_lb, void* ws, size_t ws_bytes,
                                    void* stream) {
-  (void)g; (void)batch; (void)C; (void)m; (void)node_lo; (void)node_hi; (void)x_center; (void)x_radius; (void)eps;
-  (void)alpha; (void)adam_m; (void)adam_v; (void)step; (void)lr; (void)beta1; (void)beta2; (void)adam_eps;
-  (void)lb_out; (void)best_lb; (void)ws; (void)ws_bytes; (void)stream;
-  return fail(VB_EUNSUPPORTED, "vb_alpha_step: not implemented yet");
+  Graph G;
+  vb_status s = parse_graph(g, G);
+  if (s) return s;
+  if (batch <= 0 || m <= 0 || !C) return fail(VB_EINVAL, "batch, m must be positive and C non-NULL");
+  if ((s = check_domain(x_center))) return s;
+  if (!x_radius && !(eps >= 0.f)) return fail(VB_EINVAL, "eps must be >= 0");
+  if (!node_lo || !node_hi || !alpha) return fail(VB_EINVAL, "NULL pointer array");
+  if (step < 0) return fail(VB_EINVAL, "step must be >= 0");
+  if (step > 0 && (!adam_m || !adam_v)) return fail(VB_EINVAL, "Adam state arrays are NULL");
+  if (!(lr >= 0.f) || !(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f) || !(adam_eps > 0.f))
+    return fail(VB_EINVAL, "bad Adam hyper-parameters");
+  if (!lb_out && !best_lb) return fail(VB_EINVAL, "lb_out and best_lb are both NULL");
+  std::vector<std::pair<int, int>> chain;
+  if (!alpha_chain(G, chain)) return fail(VB_EUNSUPPORTED, "alpha-CROWN needs a chain of Linear/Conv + ReLU nodes");
+  for (size_t k = 0; k < G.n.size(); ++k) {
+    if (G.n[k].op != VB_RELU) continue;
+    const int z = G.n[k].in0;
+    if (!alpha[k] || !node_lo[z] || !node_hi[z] || (step > 0 && (!adam_m[k] || !adam_v[k])))
+      return fail(VB_EINVAL, "ReLU node %zu: alpha / adam state / input bounds missing", k);
+  }
+  if (!ws) return fail(VB_EINVAL, "workspace is NULL");
+  const size_t need = alpha_workspace(G, batch, m);
+  if (ws_bytes < need)
+    return fail(VB_ENOMEM, "alpha step needs %zu bytes of workspace for the whole batch (got %zu)", need, ws_bytes);
+  hipStream_t st = (hipStream_t)stream;
+  const long long rows = (long long)batch * m;
+
+  // workspace: [transposed weights][kept psi per ReLU + domain][backward pool ...]
+  char* base = (char*)ws;
+  Backward B{G, st, node_lo, node_hi, {x_center, x_radius, eps}};
+  s = prepare_wt(G, base, st, B.wt);
+  if (s) return s;
+  size_t off = align_up(wt_floats(G) * 4);
+  std::vector<float*> psi(G.n.size(), nullptr);
+  psi[0] = (float*)(base + off);
+  off += align_up((size_t)rows * G.n[0].size * 4);
+  for (size_t k = 0; k < G.n.size(); ++k)
+    if (G.n[k].op == VB_RELU) {
+      psi[k] = (float*)(base + off);
+      off += align_up((size_t)rows * G.n[k].size * 4);
+    }
+  std::vector<const float*> al(G.n.size(), nullptr);
+  for (size_t k = 0; k < G.n.size(); ++k) al[k] = alpha[k];
+  B.alpha = al.data();
+  B.psi_keep = psi.data();
+  // evaluation: lower bounds of the m spec rows with the current slopes
+  s = backward_all(B, G.L, 0, C, m, 0, batch, m, base, ws_bytes, off / 4, [&](float* acc, int b0, int cb) -> vb_status {
+    if (b0 != 0 || cb != batch) return fail(VB_ENOMEM, "internal: alpha step was chunked");
+    HIPCHK(launch_finish_lower(acc, rows, lb_out, best_lb, step == 1, st));
+    return VB_OK;
+  });
+  if (s) return s;
+  if (step == 0) return VB_OK;
+
+  // adjoint, forward through the chain; the evaluation's pool buffers are free now
+  float* gbuf[2] = {B.pool[0], B.pool[1]};
+  HIPCHK(launch_adj_domain(psi[0], (int)rows, (int)G.n[0].size, m, x_center, x_radius, eps, gbuf[0], st));
+  const double bc1 = 1.0 / (1.0 - std::pow((double)beta1, step));
+  const double bc2 = 1.0 / (1.0 - std::pow((double)beta2, step));
+  int cur = 0;
+  for (const auto& kr : chain) {
+    const int k = kr.first, r = kr.second;
+    if (r < 0) break;  // the last affine node: its adjoint is not needed
+    const NodeInfo& nd = G.n[k];
+    GemmDesc d = affine_forward(nd, G.n[src_of(G, nd.in0)], (int)rows);
+    d.epi = E_ADJOINT;
+    d.amode = A_PLAIN;
+    d.A = gbuf[cur];
+    d.out = gbuf[cur ^ 1];
+    d.bias = nd.b;
+    d.bias_c = 0;
+    d.lo = node_lo[k];
+    d.hi = node_hi[k];
+    d.rows_per_b = m;
+    d.psi_in = psi[r];
+    d.alpha_rw = alpha[r];
+    d.adam_m = adam_m[r];
+    d.adam_v = adam_v[r];
+    d.do_update = 1;
+    d.lr = lr;
+    d.beta1 = beta1;
+    d.beta2 = beta2;
+    d.bc1 = (float)bc1;
+    d.bc2 = (float)bc2;
+    d.adam_eps = adam_eps;
+    HIPCHK(launch_gemm(d, st));
+    cur ^= 1;
+  }
+  return VB_OK;
 }

@@ -318,7 +318,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
 
   // ---- epilogue.  Register v of lane l of a 32x32 fp32 MFMA result holds
   // row 8*(v/4) + 4*(l/32) + v%4 and column l%32 of the block.
-  constexpr bool ROWSUM = (EPI != E_IBP);
+  constexpr bool ROWSUM = (EPI != E_IBP && EPI != E_ADJOINT);
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -381,7 +381,33 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
                 if (d.psi_out) d.psi_out[oi] = val;
                 if (d.bias) rowsum += o * d.bias[nb];
                 rowsum += fminf(val, 0.f) * tt;
+              } else if (EPI == E_ADJOINT) {
+                const float l = d.lo[bi], u = d.hi[bi];
+                const float g = val + (d.bias ? d.bias[nb] : 0.f);
+                const float psi = d.psi_in[oi];
+                float o;
+                if (u <= 0.f) {
+                  o = 0.f;
+                } else if (l >= 0.f) {
+                  o = g;
+                } else {
+                  const float s = u / (u - l);
+                  const float tt = -s * l;
+                  const float a_old = d.alpha_rw[oi];
+                  o = (psi >= 0.f) ? g * a_old : g * s + tt;
+                  if (d.do_update) {
+                    const float grad = g * fmaxf(psi, 0.f);
+                    const float mm = d.beta1 * d.adam_m[oi] + (1.f - d.beta1) * grad;
+                    const float vv = d.beta2 * d.adam_v[oi] + (1.f - d.beta2) * grad * grad;
+                    d.adam_m[oi] = mm;
+                    d.adam_v[oi] = vv;
+                    const float step = d.lr * (mm * d.bc1) / (sqrtf(vv * d.bc2) + d.adam_eps);
+                    d.alpha_rw[oi] = fminf(fmaxf(a_old + step, 0.f), 1.f);
+                  }
+                }
+                d.out[oi] = o;
               } else {  // E_CONCRETIZE
+                if (d.psi_out) d.psi_out[oi] = val;
                 float c, r;
                 if (d.center) {
                   c = d.center[bi];
@@ -436,6 +462,9 @@ hipError_t launch_tile(const GemmDesc& d, hipStream_t st) {
       break;
     case E_CONCRETIZE:
       hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_CONCRETIZE, FAST>), g, b, 0, st, d);
+      break;
+    case E_ADJOINT:
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_ADJOINT, FAST>), g, b, 0, st, d);
       break;
     case E_IBP:
       if (d.amode == A_IBP_BOX)

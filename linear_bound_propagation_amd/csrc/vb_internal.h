@@ -21,6 +21,10 @@ enum EpiMode : int {
                      // row partial += out . bias + min(v,0) t
   E_CONCRETIZE = 2,  // row partial += v c - |v| r over the domain box
   E_IBP = 3,         // lo = acc_c + bias - acc_r, hi = acc_c + bias + acc_r
+  E_ADJOINT = 4,     // alpha-CROWN adjoint through a ReLU: g = acc + bias over z;
+                     // d(sum lb)/d alpha = g * max(psi, 0) on unstable neurons ->
+                     // Adam ascent on alpha (in place); out = g * (psi>=0 ? alpha_old : s)
+                     // + (psi<0 ? t : 0)
 };
 
 constexpr int MAX_TAPS = 9;
@@ -62,6 +66,13 @@ struct GemmDesc {
   const float* radius;         // NULL -> eps (when center != NULL)
   float* part;                 // row partials [M][part_ld] (column = N-tile index)
   int part_ld;
+  // ---- E_ADJOINT (alpha-CROWN step): per [opos][N] of the ReLU after this node
+  const float* psi_in;         // pre-relaxation product kept by the evaluation
+  float* alpha_rw;             // lower slopes, updated in place
+  float* adam_m;
+  float* adam_v;
+  int do_update;               // 0: gradient pass without the Adam update
+  float lr, beta1, beta2, bc1, bc2, adam_eps;  // bc = 1 / (1 - beta^t)
 };
 
 // Launch the implicit GEMM; returns hipSuccess or the launch error.
@@ -77,6 +88,9 @@ hipError_t launch_rows_reduce(const float* part, int Z, int rows, int P, int S, 
 // lb[b*R + i] = acc[b*2R + i], ub[b*R + i] = -acc[b*2R + R + i]  (NULL skips)
 hipError_t launch_finish(const float* rowacc, int batch, int R, float* lb, float* ub,
                          float* best, hipStream_t st);
+// Lower-only rows (R per batch element): lb[i] = acc[i], best[i] = max(best[i], acc[i])
+// (best[i] = acc[i] when init).
+hipError_t launch_finish_lower(const float* rowacc, long long n, float* lb, float* best, int init, hipStream_t st);
 
 // Spec rows: lam[b][r][:] = +C[b][r][:] for r < m and -C[b][r-m][:] for r >= m;
 // rowacc[b*2m + r] = lam[b][r][:] . bias (bias may be NULL; per channel: index j % bias_c).
@@ -126,6 +140,16 @@ hipError_t launch_ibp_gap(const float* lo_in, const float* hi_in, int batch, int
 
 // dst[b][c][r] = src[b][r][c] for b < batch (weight layout changes)
 hipError_t launch_transpose(const float* src, int batch, int R, int C, float* dst, hipStream_t st);
+
+// alpha-CROWN set-up: alpha = adaptive lower slope of each neuron (1 if u >= -l
+// else 0 when unstable; 1 active; 0 inactive) for every one of `rows_per_b`
+// spec rows of each batch element; m = v = 0.  Bounds lo/hi [batch][n].
+hipError_t launch_alpha_init(const float* lo, const float* hi, int batch, int rows_per_b, long long n,
+                             float* alpha, float* adam_m, float* adam_v, hipStream_t st);
+
+// Adjoint at the input box: g[r][j] = c[b][j] - rad[b][j] * sign(psi[r][j]), b = r / rows_per_b
+hipError_t launch_adj_domain(const float* psi, int rows, int n, int rows_per_b, const float* center,
+                             const float* radius, float eps, float* g, hipStream_t st);
 
 // Fill with a constant
 hipError_t launch_fill(float* p, float v, long long n, hipStream_t st);

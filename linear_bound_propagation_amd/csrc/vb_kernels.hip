@@ -78,6 +78,20 @@ hipError_t launch_finish(const float* rowacc, int batch, int R, float* lb, float
   return hipGetLastError();
 }
 
+__global__ void finish_lower_kernel(const float* __restrict__ acc, long long n, float* lb, float* best, int init) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float l = acc[i];
+  if (lb) lb[i] = l;
+  if (best) best[i] = init ? l : fmaxf(best[i], l);
+}
+
+hipError_t launch_finish_lower(const float* rowacc, long long n, float* lb, float* best, int init, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(finish_lower_kernel, dim3((n + 255) / 256), dim3(256), 0, st, rowacc, n, lb, best, init);
+  return hipGetLastError();
+}
+
 // one wave per spec row
 __global__ __launch_bounds__(256) void spec_init_kernel(const float* __restrict__ C, int batch, int m, int n,
                                                         const float* __restrict__ bias, int bias_c,
@@ -362,6 +376,53 @@ hipError_t launch_fill(float* p, float v, long long n, hipStream_t st) {
   long long blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, v, n);
+  return hipGetLastError();
+}
+
+__global__ void alpha_init_kernel(const float* __restrict__ lo, const float* __restrict__ hi, int batch,
+                                  int rows_per_b, long long n, float* __restrict__ alpha,
+                                  float* __restrict__ am, float* __restrict__ av) {
+  const long long total = (long long)batch * rows_per_b * n;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (long long)gridDim.x * blockDim.x) {
+    const long long row = e / n, j = e - row * n;
+    const long long b = row / rows_per_b;
+    const float l = lo[b * n + j], u = hi[b * n + j];
+    float a, s, t;
+    relax_coeffs(l, u, a, s, t);
+    alpha[e] = a;
+    am[e] = 0.f;
+    av[e] = 0.f;
+  }
+}
+
+hipError_t launch_alpha_init(const float* lo, const float* hi, int batch, int rows_per_b, long long n, float* alpha,
+                             float* am, float* av, hipStream_t st) {
+  if (batch <= 0 || n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(alpha_init_kernel, dim3(4096), dim3(256), 0, st, lo, hi, batch, rows_per_b, n, alpha, am, av);
+  return hipGetLastError();
+}
+
+__global__ void adj_domain_kernel(const float* __restrict__ psi, int rows, int n, int rows_per_b,
+                                  const float* __restrict__ center, const float* __restrict__ radius, float eps,
+                                  float* __restrict__ g) {
+  const long long total = (long long)rows * n;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (long long)gridDim.x * blockDim.x) {
+    const long long row = e / n, j = e - row * n;
+    const long long bj = (row / rows_per_b) * n + j;
+    const float p = psi[e];
+    const float r = radius ? radius[bj] : eps;
+    const float sg = p > 0.f ? 1.f : (p < 0.f ? -1.f : 0.f);
+    g[e] = center[bj] - r * sg;
+  }
+}
+
+hipError_t launch_adj_domain(const float* psi, int rows, int n, int rows_per_b, const float* center,
+                             const float* radius, float eps, float* g, hipStream_t st) {
+  if (rows <= 0 || n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(adj_domain_kernel, dim3(2048), dim3(256), 0, st, psi, rows, n, rows_per_b, center, radius, eps,
+                     g);
   return hipGetLastError();
 }
 
