@@ -276,6 +276,8 @@ struct Backward {
   float* const* psi_keep = nullptr;
   // K-contiguous weight copies for back-substitution, per node
   std::vector<const float*> wt;
+  // bias a Lambda over each node carries into beta (ADD nodes: summed over inputs)
+  std::vector<const float*> beff;
 
   int alloc() {
     for (int i = 0; i < NPOOL; ++i)
@@ -329,16 +331,8 @@ struct BwdCall {
 };
 
 vb_status effective_bias(Backward& B, const Graph& G, int z, const float*& bias) {
-  std::vector<const float*> terms;
-  bias_terms(G, z, terms);
-  if (terms.empty()) {
-    bias = nullptr;
-  } else if (terms.size() == 1) {
-    bias = terms[0];
-  } else {
-    return fail(VB_EUNSUPPORTED, "node %d: more than one affine bias reaches this node (sum them on the host)", z);
-  }
-  (void)B;
+  (void)G;
+  bias = B.beff.empty() ? nullptr : B.beff[z];
   return VB_OK;
 }
 
@@ -373,7 +367,11 @@ vb_status run_gemm_reduce(Backward& B, GemmDesc& d, int rows, int P, bool reduce
 }
 
 // Execute the back-substitution of call `c`; rowacc receives the lower bound
-// of every row (rows = cb * R).  Returns status.
+// of every row (rows = cb * R).  Lambda of a node is a pool buffer, or IDENT:
+// the implicit +-I over the start node (identity rows), which Linear and Conv
+// nodes consume through footprint kernels instead of a GEMM over an identity.
+constexpr int IDENT = -2;
+
 vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
   const Graph& G = B.G;
   const int N = (int)G.n.size();
@@ -395,11 +393,39 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
       stack.push_back(G.n[k].in0);
       if (G.n[k].op == VB_ADD) stack.push_back(G.n[k].in1);
     }
-    if (!active[c.stop]) return fail(VB_ESHAPE, "domain node %d does not feed node %d", c.stop, c.start);
+    if (!active[c.stop]) return fail(VB_ESHAPE, "domain node %d does not feed node %d", c.start, c.stop);
     for (int k = 0; k < c.stop; ++k) active[k] = 0;
   }
-
+  auto chunk_off = [&](int node) -> long long { return (long long)c.b0 * G.n[node].size; };
   const NodeInfo& S = G.n[c.start];
+
+  // materialise the implicit identity of node k (dense +-I rows over it)
+  auto materialise = [&](int k) -> vb_status {
+    int b = B.alloc();
+    if (b < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted at node %d", k);
+    HIPCHK(launch_identity_fill(c.cb, (int)S.size, B.pool[b], B.st));
+    lam[k] = b;
+    return VB_OK;
+  };
+  // accumulate a buffer into node t's pending Lambda (takes over one reference of `buf`)
+  auto accumulate = [&](int t, int buf) -> vb_status {
+    if (lam[t] == -1) {
+      lam[t] = buf;
+      return VB_OK;
+    }
+    if (lam[t] == IDENT) {
+      vb_status s = materialise(t);
+      if (s) return s;
+    }
+    int outb = B.refs[lam[t]] == 1 ? lam[t] : B.alloc();
+    if (outb < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted at node %d", t);
+    HIPCHK(launch_add(B.pool[lam[t]], B.pool[buf], 1.f, B.pool[outb], (long long)rows * G.n[t].size, B.st));
+    if (outb != lam[t]) B.release(lam[t]);
+    B.release(buf);
+    lam[t] = outb;
+    return VB_OK;
+  };
+
   int from = c.start;
   if (c.C) {
     int b = B.alloc();
@@ -409,47 +435,48 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
     HIPCHK(launch_spec_init(c.C, c.cb, c.m, (int)S.size, bias, S.c, B.pool[b], B.rowacc, c.split, B.st));
     lam[c.start] = b;
   } else {
-    // identity rows; fast path: Linear start whose input is a ReLU
+    const float* bias = nullptr;
+    vb_status s = effective_bias(B, G, c.start, bias);
+    if (s) return s;
+    // fast path: Linear start whose input is a ReLU -> relaxed rows of +-W in one kernel
     int t = (S.op == VB_LINEAR) ? src_of(G, S.in0) : -1;
     if (t >= 0 && t != c.stop && G.n[t].op == VB_RELU && lowest_consumer(G, active, t, c.start) &&
         G.n[G.n[t].in0].cons.size() == 1) {
       int z = G.n[t].in0;
       int b = B.alloc();
       const float* bias_z = nullptr;
-      vb_status s = effective_bias(B, G, z, bias_z);
+      s = effective_bias(B, G, z, bias_z);
       if (s) return s;
-      const long long off = (long long)c.b0 * G.n[z].size;
+      const long long off = chunk_off(z);
       HIPCHK(launch_identity_linear(S.W, (int)S.size, (int)G.n[z].size, S.b, B.lo[z] + off, B.hi[z] + off, bias_z,
                                     G.n[z].c, c.cb, B.pool[b], B.rowacc, B.st));
       lam[z] = b;
       from = z;
     } else {
-      int b = B.alloc();
-      HIPCHK(launch_identity_fill(c.cb, (int)S.size, B.pool[b], B.st));
-      const float* bias = nullptr;
-      vb_status s = effective_bias(B, G, c.start, bias);
-      if (s) return s;
-      HIPCHK(launch_fill(B.rowacc, 0.f, rows, B.st));
-      if (bias) {
-        // beta of identity rows = +-bias[i]; reuse the spec-init kernel on the identity
-        HIPCHK(launch_spec_init(B.pool[b], c.cb, (int)(R), (int)S.size, bias, S.c, B.pool[b], B.rowacc, 0, B.st));
-      }
-      lam[c.start] = b;
+      HIPCHK(launch_identity_bias(c.cb, (int)S.size, bias, S.c, B.rowacc, B.st));
+      lam[c.start] = IDENT;
     }
   }
 
-  auto chunk_off = [&](int node) -> long long { return (long long)c.b0 * G.n[node].size; };
-
   for (int k = from; k > c.stop; --k) {
-    if (lam[k] < 0) continue;
+    if (lam[k] == -1) continue;
     const NodeInfo& nd = G.n[k];
+    const bool ident = lam[k] == IDENT;
+    if (ident && nd.op != VB_ADD && nd.op != VB_CONV2D) {
+      vb_status s = materialise(k);
+      if (s) return s;
+    }
     const int cur = lam[k];
-    float* Lk = B.pool[cur];
     if (nd.op == VB_LINEAR || nd.op == VB_CONV2D) {
       const int t = src_of(G, nd.in0);
       const NodeInfo& tn = G.n[t];
       const bool lowest = lowest_consumer(G, active, t, k);
       const int pend = lam[t];
+      if (pend == IDENT) {
+        vb_status s = materialise(t);
+        if (s) return s;
+      }
+      const int pbuf = lam[t];
       int epi;
       int z = -1;
       if (t == c.stop)
@@ -463,8 +490,8 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
         epi = E_STORE;
       int outb = -1;
       if (epi == E_RELAX || epi == E_STORE) {
-        if (epi == E_STORE && pend >= 0 && B.refs[pend] == 1)
-          outb = pend;  // accumulate in place
+        if (epi == E_STORE && pbuf >= 0 && B.refs[pbuf] == 1)
+          outb = pbuf;  // accumulate in place
         else
           outb = B.alloc();
         if (outb < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted at node %d", k);
@@ -477,72 +504,105 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
         vb_status s = effective_bias(B, G, t, bias);
         if (s) return s;
       }
-      // one launch (dense) or one per output-parity class (conv)
-      std::vector<GemmDesc> descs;
-      if (nd.op == VB_LINEAR) {
-        descs.push_back(linear_backward(nd, tn, Lk, rows));
-      } else {
-        for (int py = 0; py < nd.stride; ++py)
-          for (int px = 0; px < nd.stride; ++px) {
-            GemmDesc d;
-            if (conv_backward(nd, tn, Lk, rows, py, px, d)) descs.push_back(d);
-          }
-      }
       const int tgt_bounds = (epi == E_RELAX) ? z : t;
-      for (GemmDesc& d : descs) {
-        d.B = B.wt[k];
-        d.epi = epi;
-        d.rows_per_b = (int)R;
-        d.addend = (pend >= 0) ? B.pool[pend] : nullptr;
-        d.bias = bias;
-        // a Lambda over a flattened [h][w][c] node indexes its per-channel bias by n % c
-        d.bias_c = G.n[epi == E_RELAX ? z : t].c;
-        if (epi != E_CONCRETIZE) d.out = B.pool[outb];
+      if (ident) {
+        // rows +-I over this conv's output: footprint kernel, no GEMM
+        IdConv a{};
+        a.W = nd.W;
+        a.Co = nd.c;
+        a.Ho = nd.h;
+        a.Wo = nd.w;
+        a.Ci = tn.c;
+        a.Hi = tn.h;
+        a.Wi = tn.w;
+        a.kh = nd.kh;
+        a.kw = nd.kw;
+        a.stride = nd.stride;
+        a.pad = nd.pad;
+        a.mode = epi;
+        a.addend = pbuf >= 0 ? B.pool[pbuf] : nullptr;
+        a.out = outb >= 0 ? B.pool[outb] : nullptr;
+        a.bias = bias;
         if (epi == E_RELAX) {
-          d.lo = B.lo[tgt_bounds] + chunk_off(tgt_bounds);
-          d.hi = B.hi[tgt_bounds] + chunk_off(tgt_bounds);
-          if (B.alpha && B.alpha[t]) d.alpha = B.alpha[t];
-          if (B.psi_keep && B.psi_keep[t]) d.psi_out = B.psi_keep[t];
-        }
-        if (epi == E_CONCRETIZE) {
-          if (B.psi_keep && B.psi_keep[t]) d.psi_out = B.psi_keep[t];
+          a.lo = B.lo[z] + chunk_off(z);
+          a.hi = B.hi[z] + chunk_off(z);
+        } else if (epi == E_CONCRETIZE) {
           if (t == 0) {
-            d.center = B.dom.xc + chunk_off(0);
-            d.radius = B.dom.xr ? B.dom.xr + chunk_off(0) : nullptr;
-            d.eps = B.dom.eps;
+            a.center = B.dom.xc + chunk_off(0);
+            a.radius = B.dom.xr ? B.dom.xr + chunk_off(0) : nullptr;
+            a.eps = B.dom.eps;
           } else {
-            d.lo = B.lo[t] + chunk_off(t);
-            d.hi = B.hi[t] + chunk_off(t);
+            a.lo = B.lo[t] + chunk_off(t);
+            a.hi = B.hi[t] + chunk_off(t);
           }
         }
-        const bool reduce = (epi != E_STORE) || bias != nullptr;
-        const int P = d.gh * d.gw;
-        // algorithmic multiply-adds of this layer for these rows (conv: the
-        // forward count C_out*C_in*kh*kw*H_out*W_out per row, split evenly
-        // over the output-parity launches)
-        const double macs = (nd.op == VB_LINEAR)
-                                ? (double)rows * nd.size * tn.size
-                                : (double)rows * nd.c * tn.c * nd.kh * nd.kw * nd.h * nd.w / descs.size();
-        vb_status s = run_gemm_reduce(B, d, rows, P, reduce, 2.0 * macs);
-        if (s) return s;
+        if ((long long)2 * nd.size != R) return fail(VB_ESHAPE, "internal: identity rows do not match node %d", k);
+        HIPCHK(launch_identity_conv(a, c.cb, B.rowacc, B.st));
+      } else {
+        // one launch (dense) or one per output-parity class (conv)
+        std::vector<GemmDesc> descs;
+        if (nd.op == VB_LINEAR) {
+          descs.push_back(linear_backward(nd, tn, B.pool[cur], rows));
+        } else {
+          for (int py = 0; py < nd.stride; ++py)
+            for (int px = 0; px < nd.stride; ++px) {
+              GemmDesc d;
+              if (conv_backward(nd, tn, B.pool[cur], rows, py, px, d)) descs.push_back(d);
+            }
+        }
+        for (GemmDesc& d : descs) {
+          d.B = B.wt[k];
+          d.epi = epi;
+          d.rows_per_b = (int)R;
+          d.addend = (pbuf >= 0) ? B.pool[pbuf] : nullptr;
+          d.bias = bias;
+          // a Lambda over a flattened [h][w][c] node indexes its per-channel bias by n % c
+          d.bias_c = G.n[tgt_bounds].c;
+          if (epi != E_CONCRETIZE) d.out = B.pool[outb];
+          if (epi == E_RELAX) {
+            d.lo = B.lo[tgt_bounds] + chunk_off(tgt_bounds);
+            d.hi = B.hi[tgt_bounds] + chunk_off(tgt_bounds);
+            if (B.alpha && B.alpha[t]) d.alpha = B.alpha[t];
+            if (B.psi_keep && B.psi_keep[t]) d.psi_out = B.psi_keep[t];
+          }
+          if (epi == E_CONCRETIZE) {
+            if (B.psi_keep && B.psi_keep[t]) d.psi_out = B.psi_keep[t];
+            if (t == 0) {
+              d.center = B.dom.xc + chunk_off(0);
+              d.radius = B.dom.xr ? B.dom.xr + chunk_off(0) : nullptr;
+              d.eps = B.dom.eps;
+            } else {
+              d.lo = B.lo[t] + chunk_off(t);
+              d.hi = B.hi[t] + chunk_off(t);
+            }
+          }
+          const bool reduce = (epi != E_STORE) || bias != nullptr;
+          const int P = d.gh * d.gw;
+          // algorithmic multiply-adds of this layer for these rows (conv: the
+          // forward count C_out*C_in*kh*kw*H_out*W_out per row, split evenly
+          // over the output-parity launches)
+          const double macs = (nd.op == VB_LINEAR)
+                                  ? (double)rows * nd.size * tn.size
+                                  : (double)rows * nd.c * tn.c * nd.kh * nd.kw * nd.h * nd.w / descs.size();
+          vb_status s = run_gemm_reduce(B, d, rows, P, reduce, 2.0 * macs);
+          if (s) return s;
+        }
+        B.release(cur);
       }
-      B.release(cur);
       lam[k] = -1;
       if (epi == E_RELAX) {
-        if (pend >= 0) {
-          B.release(pend);
+        if (pbuf >= 0) {
+          B.release(pbuf);
           lam[t] = -1;
         }
         lam[z] = outb;
       } else if (epi == E_CONCRETIZE) {
-        if (pend >= 0) {
-          B.release(pend);
+        if (pbuf >= 0) {
+          B.release(pbuf);
           lam[t] = -1;
         }
       } else {
-        if (outb != pend) {
-          if (pend >= 0) B.release(pend);
-        }
+        if (pbuf >= 0 && outb != pbuf) B.release(pbuf);
         lam[t] = outb;
       }
     } else if (nd.op == VB_RELU) {
@@ -555,39 +615,52 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
       vb_status s = effective_bias(B, G, z, bias_z);
       if (s) return s;
       const int P = nd.h * nd.w;
-      HIPCHK(launch_relax(Lk, 0, 1.f, nullptr, rows, (int)R, P, nd.c, B.lo[z] + chunk_off(z), B.hi[z] + chunk_off(z),
-                          bias_z, B.alpha ? B.alpha[k] : nullptr, B.psi_keep ? B.psi_keep[k] : nullptr, B.pool[outb],
-                          B.rowacc, B.st));
+      HIPCHK(launch_relax(B.pool[cur], 0, 1.f, nullptr, rows, (int)R, P, nd.c, B.lo[z] + chunk_off(z),
+                          B.hi[z] + chunk_off(z), bias_z, B.alpha ? B.alpha[k] : nullptr,
+                          B.psi_keep ? B.psi_keep[k] : nullptr, B.pool[outb], B.rowacc, B.st));
       B.release(cur);
       lam[k] = -1;
+      if (lam[z] != -1) return fail(VB_EUNSUPPORTED, "internal: node %d already has a pending Lambda", z);
       lam[z] = outb;
     } else if (nd.op == VB_ADD) {
       const int ins[2] = {nd.in0, nd.in1};
-      for (int q = 0; q < (nd.in0 == nd.in1 ? 1 : 2); ++q) {
+      const int nin = nd.in0 == nd.in1 ? 1 : 2;
+      for (int q = 0; q < nin; ++q) {
         const int t = ins[q];
-        const float scale = (nd.in0 == nd.in1) ? 2.f : 1.f;
-        if (lam[t] < 0 && scale == 1.f) {
-          lam[t] = cur;
-          B.refs[cur]++;
+        if (nin == 1) {
+          // x + x: Lambda flows twice into x
+          int b = B.alloc();
+          if (b < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted at node %d", k);
+          HIPCHK(launch_add(B.pool[cur], B.pool[cur], 1.f, B.pool[b], (long long)rows * G.n[t].size, B.st));
+          vb_status s = accumulate(t, b);
+          if (s) return s;
+        } else if (cur == IDENT) {
+          if (lam[t] == -1) {
+            lam[t] = IDENT;
+          } else {
+            int b = B.alloc();
+            if (b < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted at node %d", k);
+            HIPCHK(launch_identity_fill(c.cb, (int)S.size, B.pool[b], B.st));
+            vb_status s = accumulate(t, b);
+            if (s) return s;
+          }
         } else {
-          int outb = (lam[t] >= 0 && B.refs[lam[t]] == 1) ? lam[t] : B.alloc();
-          if (outb < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted at node %d", k);
-          if (lam[t] >= 0)
-            HIPCHK(launch_add(B.pool[lam[t]], Lk, scale, B.pool[outb], (long long)rows * G.n[t].size, B.st));
-          else
-            HIPCHK(launch_add(Lk, Lk, 1.f, B.pool[outb], (long long)rows * G.n[t].size, B.st));
-          if (lam[t] >= 0 && lam[t] != outb) B.release(lam[t]);
-          lam[t] = outb;
+          B.refs[cur]++;
+          vb_status s = accumulate(t, cur);
+          if (s) return s;
         }
-        // bias contributions of affine inputs are carried by effective_bias of the producer of Lambda
       }
-      B.release(cur);
+      if (cur >= 0) B.release(cur);
       lam[k] = -1;
     } else if (nd.op == VB_GAP) {
       const int t = nd.in0;
       const NodeInfo& tn = G.n[t];
       const int P = tn.h * tn.w;
       const float scale = 1.f / (float)P;
+      if (lam[t] == IDENT) {
+        vb_status s = materialise(t);
+        if (s) return s;
+      }
       const int pend = lam[t];
       if (tn.op == VB_RELU && lowest_consumer(G, active, t, k) && t != c.stop) {
         const int z = tn.in0;
@@ -597,7 +670,7 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
         const float* bias_z = nullptr;
         vb_status s = effective_bias(B, G, z, bias_z);
         if (s) return s;
-        HIPCHK(launch_relax(Lk, 1, scale, pend >= 0 ? B.pool[pend] : nullptr, rows, (int)R, P, tn.c,
+        HIPCHK(launch_relax(B.pool[cur], 1, scale, pend >= 0 ? B.pool[pend] : nullptr, rows, (int)R, P, tn.c,
                             B.lo[z] + chunk_off(z), B.hi[z] + chunk_off(z), bias_z, B.alpha ? B.alpha[t] : nullptr,
                             B.psi_keep ? B.psi_keep[t] : nullptr, B.pool[outb], B.rowacc, B.st));
         if (pend >= 0) {
@@ -608,27 +681,24 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
       } else {
         int outb = (pend >= 0 && B.refs[pend] == 1) ? pend : B.alloc();
         if (outb < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted at node %d", k);
-        HIPCHK(launch_gap_expand(Lk, rows, P, tn.c, scale, pend >= 0 ? B.pool[pend] : nullptr, B.pool[outb], B.st));
+        HIPCHK(launch_gap_expand(B.pool[cur], rows, P, tn.c, scale, pend >= 0 ? B.pool[pend] : nullptr,
+                                 B.pool[outb], B.st));
         if (pend >= 0 && pend != outb) B.release(pend);
         lam[t] = outb;
       }
       B.release(cur);
       lam[k] = -1;
     } else if (nd.op == VB_FLATTEN) {
-      const int t = nd.in0;
-      if (lam[t] >= 0) {
-        int outb = B.refs[lam[t]] == 1 ? lam[t] : B.alloc();
-        HIPCHK(launch_add(B.pool[lam[t]], Lk, 1.f, B.pool[outb], (long long)rows * nd.size, B.st));
-        if (outb != lam[t]) B.release(lam[t]);
-        lam[t] = outb;
-        B.release(cur);
-      } else {
-        lam[t] = cur;
-      }
+      vb_status s = accumulate(nd.in0, cur);
+      if (s) return s;
       lam[k] = -1;
     } else {
       return fail(VB_EUNSUPPORTED, "cannot back-substitute through node %d (op %d)", k, nd.op);
     }
+  }
+  if (lam[c.stop] == IDENT) {
+    vb_status s = materialise(c.stop);
+    if (s) return s;
   }
   if (lam[c.stop] >= 0) {
     const NodeInfo& sn = G.n[c.stop];
@@ -675,20 +745,25 @@ void bwd_requirements(const Graph& G, int start, int stop, long long R, long lon
   }
 }
 
-// Floats of the transposed weight copies at the head of the workspace.
+// Floats of the transposed weight copies (and summed ADD biases) at the head
+// of the workspace.
 size_t wt_floats(const Graph& G) {
   size_t f = 0;
   for (const NodeInfo& n : G.n) {
     if (n.op == VB_LINEAR) f += align_up((size_t)n.size * G.n[n.in0].size * 4) / 4;
     if (n.op == VB_CONV2D) f += align_up((size_t)n.kh * n.kw * n.c * G.n[n.in0].c * 4) / 4;
+    if (n.op == VB_ADD) f += align_up((size_t)n.c * 4) / 4;
   }
   return f;
 }
 
 // Write W^T of every affine node into ws (Linear: [n_in][n_out]; Conv: per tap
-// [c_in][c_out]) and return the per-node pointers.
-vb_status prepare_wt(const Graph& G, char* ws, hipStream_t st, std::vector<const float*>& wt) {
+// [c_in][c_out]) and the per-node bias a Lambda carries into beta (for an ADD:
+// the sum of its inputs' biases); return the per-node pointers.
+vb_status prepare_weights(const Graph& G, char* ws, hipStream_t st, std::vector<const float*>& wt,
+                          std::vector<const float*>& beff) {
   wt.assign(G.n.size(), nullptr);
+  beff.assign(G.n.size(), nullptr);
   float* p = (float*)ws;
   for (size_t k = 0; k < G.n.size(); ++k) {
     const NodeInfo& n = G.n[k];
@@ -696,12 +771,25 @@ vb_status prepare_wt(const Graph& G, char* ws, hipStream_t st, std::vector<const
       const int nin = (int)G.n[n.in0].size;
       HIPCHK(launch_transpose(n.W, 1, (int)n.size, nin, p, st));
       wt[k] = p;
+      beff[k] = n.b;
       p += align_up((size_t)n.size * nin * 4) / 4;
     } else if (n.op == VB_CONV2D) {
       const int cin = G.n[n.in0].c;
       HIPCHK(launch_transpose(n.W, n.kh * n.kw, n.c, cin, p, st));
       wt[k] = p;
+      beff[k] = n.b;
       p += align_up((size_t)n.kh * n.kw * n.c * cin * 4) / 4;
+    } else if (n.op == VB_ADD) {
+      std::vector<const float*> terms;
+      bias_terms(G, (int)k, terms);
+      if (terms.size() == 1) {
+        beff[k] = terms[0];
+      } else if (terms.size() > 1) {
+        HIPCHK(launch_add(terms[0], terms[1], 1.f, p, n.c, st));
+        for (size_t i = 2; i < terms.size(); ++i) HIPCHK(launch_add(p, terms[i], 1.f, p, n.c, st));
+        beff[k] = p;
+      }
+      p += align_up((size_t)n.c * 4) / 4;
     }
   }
   return VB_OK;
@@ -909,7 +997,7 @@ static vb_status spec_ibp(const Graph& G, int batch, const float* C, int m, cons
   const int stop = src_of(G, G.n[L].in0);
   if (stop == 0) return fail(VB_EUNSUPPORTED, "spec IBP over a single affine layer: use CROWN (exact)");
   Backward B{G, st, lo, hi, {nullptr, nullptr, 0.f}};
-  vb_status s = prepare_wt(G, (char*)ws, st, B.wt);
+  vb_status s = prepare_weights(G, (char*)ws, st, B.wt, B.beff);
   if (s) return s;
   return backward_all(B, L, stop, C, m, 1, batch, 2LL * m, (char*)ws, ws_bytes, wt_floats(G),
                       [&](float* acc, int b0, int cb) -> vb_status {
@@ -947,7 +1035,7 @@ static vb_status crown_backward_impl(const Graph& G, int batch, int start, int s
                                      const float* const* lo, const float* const* hi, Domain dom, float* lb,
                                      float* ub, void* ws, size_t ws_bytes, hipStream_t st) {
   Backward B{G, st, lo, hi, dom};
-  vb_status s = prepare_wt(G, (char*)ws, st, B.wt);
+  vb_status s = prepare_weights(G, (char*)ws, st, B.wt, B.beff);
   if (s) return s;
   const long long R = C ? 2LL * m : 2LL * G.n[start].size;
   const int half = (int)(R / 2);
@@ -1175,7 +1263,7 @@ extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float
   // workspace: [transposed weights][kept psi per ReLU + domain][backward pool ...]
   char* base = (char*)ws;
   Backward B{G, st, node_lo, node_hi, {x_center, x_radius, eps}};
-  s = prepare_wt(G, base, st, B.wt);
+  s = prepare_weights(G, base, st, B.wt, B.beff);
   if (s) return s;
   size_t off = align_up(wt_floats(G) * 4);
   std::vector<float*> psi(G.n.size(), nullptr);

@@ -105,6 +105,31 @@ hipError_t launch_identity_linear(const float* W, int n_out, int n_in, const flo
                                   const float* lo, const float* hi, const float* bias_z, int bias_zc,
                                   int batch, float* lam, float* rowacc, hipStream_t st);
 
+// Identity rows through a Conv node: rows (b, s, i) with i = (y*Wo + x)*Co + c over
+// the conv output; psi over the conv input [Hi][Wi][Ci] is s*W[ky][kx][c][ci] on the
+// kernel footprint (yy = y*stride + ky - pad) and 0 elsewhere.  mode E_STORE:
+// out = psi (+ addend), row += psi . bias[ci] (if bias); E_RELAX: out = relax(psi +
+// addend; lo/hi of the target [b][e]), row += out . bias[ci] + min(v,0) t;
+// E_CONCRETIZE: row += v c - |v| r over the box (center/radius or lo/hi).
+// W layout [kh][kw][Co][Ci].  rowacc[row] += row partial.
+struct IdConv {
+  const float* W;
+  int Co, Ho, Wo, Ci, Hi, Wi, kh, kw, stride, pad;
+  int mode;
+  const float* addend;
+  float* out;
+  const float* lo;
+  const float* hi;
+  const float* bias;
+  const float* center;
+  const float* radius;
+  float eps;
+};
+hipError_t launch_identity_conv(const IdConv& a, int batch, float* rowacc, hipStream_t st);
+
+// rowacc[b*2n + r] = s * bias[i % bias_c] for identity rows (s = +1 for r < n, -1 after; i = r mod n)
+hipError_t launch_identity_bias(int batch, int n, const float* bias, int bias_c, float* rowacc, hipStream_t st);
+
 // Identity rows materialised as a dense matrix: rows (b, s, i) over n, +-1 on the diagonal.
 hipError_t launch_identity_fill(int batch, int n, float* lam, hipStream_t st);
 

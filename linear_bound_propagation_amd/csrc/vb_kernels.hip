@@ -19,6 +19,18 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+__device__ __forceinline__ void relax_coeffs(float l, float u, float& a, float& s, float& t) {
+  if (u <= 0.f) {
+    a = 0.f; s = 0.f; t = 0.f;
+  } else if (l >= 0.f) {
+    a = 1.f; s = 1.f; t = 0.f;
+  } else {
+    s = u / (u - l);
+    t = -s * l;
+    a = (u >= -l) ? 1.f : 0.f;
+  }
+}
+
 // Fixed-order block sum of one value per thread (256 threads); result valid in thread 0.
 __device__ __forceinline__ float block_sum(float v, float* sh) {
   v = wave_sum(v);
@@ -125,18 +137,6 @@ hipError_t launch_spec_init(const float* C, int batch, int m, int n, const float
   return hipGetLastError();
 }
 
-__device__ __forceinline__ void relax_coeffs(float l, float u, float& a, float& s, float& t) {
-  if (u <= 0.f) {
-    a = 0.f; s = 0.f; t = 0.f;
-  } else if (l >= 0.f) {
-    a = 1.f; s = 1.f; t = 0.f;
-  } else {
-    s = u / (u - l);
-    t = -s * l;
-    a = (u >= -l) ? 1.f : 0.f;
-  }
-}
-
 // one wave per identity row (b, sign, i)
 __global__ __launch_bounds__(256) void identity_linear_kernel(const float* __restrict__ W, int n_out, int n_in,
                                                               const float* __restrict__ bias_start,
@@ -178,6 +178,83 @@ hipError_t launch_identity_linear(const float* W, int n_out, int n_in, const flo
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(identity_linear_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, W, n_out, n_in,
                      bias_start, lo, hi, bias_z, bias_zc > 0 ? bias_zc : n_in, batch, lam, rowacc);
+  return hipGetLastError();
+}
+
+// one block per identity row
+__global__ __launch_bounds__(256) void identity_conv_kernel(const IdConv a, float* __restrict__ rowacc) {
+  __shared__ float sh[4];
+  const long long row = blockIdx.x;
+  const long long n_out = (long long)a.Co * a.Ho * a.Wo;
+  const long long R = 2 * n_out;
+  const long long b = row / R;
+  const long long r = row - b * R;
+  const float sg = r < n_out ? 1.f : -1.f;
+  const long long i = r < n_out ? r : r - n_out;
+  const int c = (int)(i % a.Co);
+  const long long p = i / a.Co;
+  const int y = (int)(p / a.Wo), x = (int)(p % a.Wo);
+  const long long L = (long long)a.Hi * a.Wi * a.Ci;
+  float s = 0.f;
+  for (long long e = threadIdx.x; e < L; e += 256) {
+    const int ci = (int)(e % a.Ci);
+    const long long q = e / a.Ci;
+    const int yy = (int)(q / a.Wi), xx = (int)(q % a.Wi);
+    const int ky = yy - y * a.stride + a.pad, kx = xx - x * a.stride + a.pad;
+    float v = 0.f;
+    if (ky >= 0 && ky < a.kh && kx >= 0 && kx < a.kw)
+      v = sg * a.W[(((long long)ky * a.kw + kx) * a.Co + c) * a.Ci + ci];
+    if (a.addend) v += a.addend[row * L + e];
+    if (a.mode == E_STORE) {
+      a.out[row * L + e] = v;
+      if (a.bias) s += v * a.bias[ci];
+    } else if (a.mode == E_RELAX) {
+      const float l = a.lo[b * L + e], u = a.hi[b * L + e];
+      float al, sl, t;
+      relax_coeffs(l, u, al, sl, t);
+      const float o = v >= 0.f ? v * al : v * sl;
+      a.out[row * L + e] = o;
+      if (a.bias) s += o * a.bias[ci];
+      s += fminf(v, 0.f) * t;
+    } else {
+      float cc, rr;
+      if (a.center) {
+        cc = a.center[b * L + e];
+        rr = a.radius ? a.radius[b * L + e] : a.eps;
+      } else {
+        const float l = a.lo[b * L + e], u = a.hi[b * L + e];
+        cc = (l + u) * 0.5f;
+        rr = (u - l) * 0.5f;
+      }
+      s += v * cc - fabsf(v) * rr;
+    }
+  }
+  s = block_sum(s, sh);
+  if (threadIdx.x == 0) rowacc[row] += s;
+}
+
+hipError_t launch_identity_conv(const IdConv& a, int batch, float* rowacc, hipStream_t st) {
+  const long long rows = (long long)batch * 2 * a.Co * a.Ho * a.Wo;
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(identity_conv_kernel, dim3((unsigned)rows), dim3(256), 0, st, a, rowacc);
+  return hipGetLastError();
+}
+
+__global__ void identity_bias_kernel(int batch, int n, const float* __restrict__ bias, int bias_c,
+                                     float* __restrict__ rowacc) {
+  const long long total = (long long)batch * 2 * n;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (long long)gridDim.x * blockDim.x) {
+    const long long r = e % (2 * n);
+    const float sg = r < n ? 1.f : -1.f;
+    const long long i = r < n ? r : r - n;
+    rowacc[e] = bias ? sg * bias[i % bias_c] : 0.f;
+  }
+}
+
+hipError_t launch_identity_bias(int batch, int n, const float* bias, int bias_c, float* rowacc, hipStream_t st) {
+  hipLaunchKernelGGL(identity_bias_kernel, dim3(1024), dim3(256), 0, st, batch, n, bias, bias_c > 0 ? bias_c : n,
+                     rowacc);
   return hipGetLastError();
 }
 
