@@ -48,11 +48,25 @@ def _src(nodes, k):
     return k
 
 
+def _identity_consumers(nodes, z):
+    """Affine nodes that receive identity rows over z directly (z itself, or the
+    affine inputs of an ADD z): their step is a copy of the weight footprint."""
+    nd = nodes[z]
+    if nd.op in ("linear", "conv"):
+        return {z}
+    if nd.op == "add":
+        out = set()
+        for i in nd.inputs:
+            out |= _identity_consumers(nodes, i)
+        return out
+    return set()
+
+
 def algorithmic_flops(wl):
     """FLOPs the method itself performs for the whole batch (no padding, no tile waste):
     2 * rows * multiply-adds of each affine node a row of Lambda passes through; the
-    first step of identity rows through a Linear (rows of +-W) costs nothing; IBP is
-    two passes (centre and radius) of the forward multiply-adds."""
+    first step of identity rows (a copy of the weight footprint) costs nothing; IBP
+    is two passes (centre and radius) of the forward multiply-adds."""
     nodes, B, m = wl.nodes, wl.batch, wl.m
     total = {"ibp": 0.0, "intermediate": 0.0, "spec": 0.0}
     for nd in nodes:
@@ -71,17 +85,24 @@ def algorithmic_flops(wl):
             if z <= stop or (zn.op in ("linear", "conv") and _src(nodes, zn.inputs[0]) == stop):
                 continue
             rows = 2 * zn.size * B
+            free = _identity_consumers(nodes, z)
             for k in _active(nodes, z, stop):
-                if nodes[k].op not in ("linear", "conv"):
+                if nodes[k].op not in ("linear", "conv") or k in free:
                     continue
-                if k == z and zn.op == "linear":
-                    continue           # identity rows through their own Linear: rows of +-W
                 total["intermediate"] += 2 * rows * _mac_per_row(nodes[k], nodes)
     rows = 2 * m * B
     for k in _active(nodes, L, stop):
         if nodes[k].op in ("linear", "conv"):
             total["spec"] += 2 * rows * _mac_per_row(nodes[k], nodes)
-    total["all"] = total["ibp"] + total["intermediate"] + total["spec"]
+    if wl.alpha_steps:
+        # alpha loop: steps+1 evaluations of the m lower rows (spec fold + every
+        # affine node) and `steps` adjoints (forward through every affine node but the last)
+        rows = m * B
+        ev = sum(2 * rows * _mac_per_row(nodes[k], nodes) for k in _active(nodes, L, 0)
+                 if nodes[k].op in ("linear", "conv"))
+        adj = ev - 2 * rows * _mac_per_row(nodes[L], nodes)
+        total["alpha"] = (wl.alpha_steps + 1) * ev + wl.alpha_steps * adj
+    total["all"] = sum(v for k, v in total.items())
     return total
 
 
@@ -129,7 +150,19 @@ def main():
     ws_bytes = net.workspace_size(wl.batch, wl.m, wl.intermediate, wl.region_start or 0)
     free = torch.cuda.mem_get_info()[0]
     ws = net.workspace(min(ws_bytes, int(free * 0.85)))
-    step = lambda: lbp.crown(net, x, float(wl.eps), C, wl.intermediate, wl.region_start, ws=ws, out=out)
+    if wl.alpha_steps:
+        state = lbp.alpha_state(net, wl.batch, wl.m)
+        lb_steps = torch.empty(wl.alpha_steps + 1, wl.batch, wl.m, device=net.device)
+        best = torch.empty(wl.batch, wl.m, device=net.device)
+
+        def step():
+            lbp.crown(net, x, float(wl.eps), C, wl.intermediate, wl.region_start, ws=ws, out=out)
+            lbp.alpha_crown(net, x, float(wl.eps), C, out["lo"], out["hi"], wl.alpha_steps, wl.alpha_lr, ws=ws,
+                            state=state, lb_steps=lb_steps, best=best)
+            out["lb"] = best
+    else:
+        def step():
+            lbp.crown(net, x, float(wl.eps), C, wl.intermediate, wl.region_start, ws=ws, out=out)
 
     for _ in range(args.warmup):
         step()
@@ -168,8 +201,9 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "specs": wl.m, "eps": float(wl.eps),
-                   "intermediate": wl.intermediate,
-                   "algorithmic_tflop_per_step": round(fl["all"] / 1e12, 4)},
+                   "intermediate": wl.intermediate, "alpha_steps": wl.alpha_steps,
+                   "algorithmic_tflop_per_step": round(fl["all"] / 1e12, 4),
+                   "workspace_gb": round(ws.numel() / 1e9, 2)},
         "frac_of_fp32_mfma_peak": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4),
         "specs_per_s": round(wl.batch * wl.m / (ms * 1e-3), 1),
         "verified_frac": verified,

@@ -64,6 +64,19 @@ __device__ __forceinline__ Pos pos_of(const GemmDesc& d, int m) {
   return p;
 }
 
+// Tap table entry j, read with static indices only (dynamic indexing of the
+// by-value descriptor would make the compiler copy it to scratch).
+struct Tap {
+  int dy, dx, w;
+};
+__device__ __forceinline__ Tap tap_of(const GemmDesc& d, int j) {
+  Tap t{d.tap_dy[0], d.tap_dx[0], d.tap_w[0]};
+#pragma unroll
+  for (int i = 1; i < MAX_TAPS; ++i)
+    if (j == i) t = Tap{d.tap_dy[i], d.tap_dx[i], d.tap_w[i]};
+  return t;
+}
+
 // A offset of (position, reduction index k), or -1 for padding.
 template <bool DENSE>
 __device__ __forceinline__ long long a_off(const GemmDesc& d, const Pos& p, int k) {
@@ -71,8 +84,9 @@ __device__ __forceinline__ long long a_off(const GemmDesc& d, const Pos& p, int 
   if (DENSE) return p.a_base + k;
   const int j = (d.ntaps == 1) ? 0 : k / d.cs;
   const int c = k - j * d.cs;
-  const int yy = p.Y * d.sy + d.tap_dy[j];
-  const int xx = p.X * d.sx + d.tap_dx[j];
+  const Tap t = tap_of(d, j);
+  const int yy = p.Y * d.sy + t.dy;
+  const int xx = p.X * d.sx + t.dx;
   if (yy < 0 || yy >= d.hs || xx < 0 || xx >= d.ws) return -1;
   return p.a_base + ((long long)yy * d.ws + xx) * d.cs + c;
 }
@@ -82,40 +96,56 @@ __device__ __forceinline__ long long b_off(const GemmDesc& d, int k, int n) {
   if (k >= d.K || n >= d.N) return -1;
   const int j = (d.ntaps == 1) ? 0 : k / d.cs;
   const int c = k - j * d.cs;
-  return ((long long)d.tap_w[j] * d.N + n) * d.cs + c;
+  return ((long long)tap_of(d, j).w * d.N + n) * d.cs + c;
+}
+
+__device__ __forceinline__ float ld1(const float* base, long long off) {
+  const bool ok = off >= 0;
+  const float v = base[ok ? off : 0];
+  return ok ? v : 0.f;
 }
 
 template <int AMODE>
 __device__ __forceinline__ void a_val(const GemmDesc& d, long long off, float& c, float& r) {
-  if (off < 0) {
-    c = r = 0.f;
-  } else if (AMODE == A_PLAIN) {
-    c = d.A[off];
+  if (AMODE == A_PLAIN) {
+    c = ld1(d.A, off);
     r = 0.f;
   } else if (AMODE == A_IBP_BOX) {
-    const float l = d.A[off], u = d.A2[off];
+    const float l = ld1(d.A, off), u = ld1(d.A2, off);
     c = (l + u) * 0.5f;
     r = (u - l) * 0.5f;
   } else {
-    c = d.A[off];
-    r = d.A2 ? d.A2[off] : d.eps;
+    c = ld1(d.A, off);
+    r = d.A2 ? ld1(d.A2, off) : (off >= 0 ? d.eps : 0.f);
   }
+}
+
+// Unconditional global float4 load at a clamped offset, zeroed afterwards when
+// the element is padding: keeps every load a plain global load (a conditional
+// load lets the compiler route zeros through scratch and a flat load).
+__device__ __forceinline__ float4 ld4(const float* base, long long off) {
+  const bool ok = off >= 0;
+  float4 v = *reinterpret_cast<const float4*>(base + (ok ? off : 0));
+  return ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 template <int AMODE>
 __device__ __forceinline__ void a_val4(const GemmDesc& d, long long off, float4& c, float4& r) {
-  if (off < 0) {
-    c = r = make_float4(0.f, 0.f, 0.f, 0.f);
-  } else if (AMODE == A_PLAIN) {
-    c = *reinterpret_cast<const float4*>(d.A + off);
+  if (AMODE == A_PLAIN) {
+    c = ld4(d.A, off);
   } else if (AMODE == A_IBP_BOX) {
-    const float4 l = *reinterpret_cast<const float4*>(d.A + off);
-    const float4 u = *reinterpret_cast<const float4*>(d.A2 + off);
+    const float4 l = ld4(d.A, off);
+    const float4 u = ld4(d.A2, off);
     c = make_float4((l.x + u.x) * 0.5f, (l.y + u.y) * 0.5f, (l.z + u.z) * 0.5f, (l.w + u.w) * 0.5f);
     r = make_float4((u.x - l.x) * 0.5f, (u.y - l.y) * 0.5f, (u.z - l.z) * 0.5f, (u.w - l.w) * 0.5f);
   } else {
-    c = *reinterpret_cast<const float4*>(d.A + off);
-    r = d.A2 ? *reinterpret_cast<const float4*>(d.A2 + off) : make_float4(d.eps, d.eps, d.eps, d.eps);
+    c = ld4(d.A, off);
+    if (d.A2) {
+      r = ld4(d.A2, off);
+    } else {
+      const float e = off >= 0 ? d.eps : 0.f;
+      r = make_float4(e, e, e, e);
+    }
   }
 }
 
@@ -174,6 +204,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
       // one tap per stage: k0 .. k0+31 share tap j
       const int j = (d.ntaps == 1) ? 0 : k0 / d.cs;
       const int c0 = k0 - j * d.cs;
+      const Tap tp = tap_of(d, j);
 #pragma unroll
       for (int i = 0; i < AV; ++i) {
         const int f = tid + NTHR * i;
@@ -184,8 +215,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
           if (DENSE) {
             off = p.a_base + k0 + kq;
           } else {
-            const int yy = p.Y * d.sy + d.tap_dy[j];
-            const int xx = p.X * d.sx + d.tap_dx[j];
+            const int yy = p.Y * d.sy + tp.dy;
+            const int xx = p.X * d.sx + tp.dx;
             if (yy >= 0 && yy < d.hs && xx >= 0 && xx < d.ws)
               off = p.a_base + ((long long)yy * d.ws + xx) * d.cs + c0 + kq;
           }
@@ -194,15 +225,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
         a_val4<AMODE>(d, off, ra[0][i], r4);
         if (NA == 2) ra[NA - 1][i] = r4;
       }
-      const long long bt = (long long)d.tap_w[j] * d.N;
+      const long long bt = (long long)tp.w * d.N;
 #pragma unroll
       for (int i = 0; i < BV; ++i) {
         const int f = tid + NTHR * i;
         const int n = f / (BK / 4), kq = (f % (BK / 4)) * 4;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (f < BN * (BK / 4) && n0 + n < d.N)
-          v = *reinterpret_cast<const float4*>(d.B + (bt + n0 + n) * d.cs + c0 + kq);
-        rb[i] = v;
+        const bool ok = f < BN * (BK / 4) && n0 + n < d.N;
+        rb[i] = ld4(d.B, ok ? (bt + n0 + n) * d.cs + c0 + kq : -1);
       }
     } else {
 #pragma unroll
@@ -217,12 +246,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
 #pragma unroll
       for (int i = 0; i < BS; ++i) {
         const int e = tid + NTHR * i;
-        float v = 0.f;
-        if (e < BN * BK) {
-          const long long off = b_off(d, k0 + (e % BK), n0 + e / BK);
-          if (off >= 0) v = d.B[off];
-        }
-        sb[i] = v;
+        sb[i] = ld1(d.B, e < BN * BK ? b_off(d, k0 + (e % BK), n0 + e / BK) : -1);
       }
     }
   };
@@ -280,6 +304,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   for (int t = 0; t < nk; ++t) {
     const int cur = t & 1;
     if (t + 1 < nk) load((t + 1) * BK);
+    // keep the next stage's global loads ahead of this stage's MFMAs and its
+    // LDS stores (and their wait for those loads) behind them
+    __builtin_amdgcn_sched_barrier(0);
     // MFMA step (q, s): lane half h supplies k = 16h + 4q + s
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -312,6 +339,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
     if (t + 1 < nk) store(cur ^ 1);
     __syncthreads();
   }
