@@ -271,6 +271,7 @@ struct Backward {
   float* part;
   float* rowacc;
   size_t part_floats;
+  size_t pool_floats = 0;
   // alpha-CROWN extras (per node, may be NULL)
   const float* const* alpha = nullptr;
   float* const* psi_keep = nullptr;
@@ -278,6 +279,9 @@ struct Backward {
   std::vector<const float*> wt;
   // bias a Lambda over each node carries into beta (ADD nodes: summed over inputs)
   std::vector<const float*> beff;
+  // centre / radius of a box domain (stop > 0) for the current chunk
+  float* box_c = nullptr;
+  float* box_r = nullptr;
 
   int alloc() {
     for (int i = 0; i < NPOOL; ++i)
@@ -398,6 +402,9 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
   }
   auto chunk_off = [&](int node) -> long long { return (long long)c.b0 * G.n[node].size; };
   const NodeInfo& S = G.n[c.start];
+  if (c.stop != 0)
+    HIPCHK(launch_box_center_radius(B.lo[c.stop] + chunk_off(c.stop), B.hi[c.stop] + chunk_off(c.stop),
+                                    (long long)c.cb * G.n[c.stop].size, B.box_c, B.box_r, B.st));
 
   // materialise the implicit identity of node k (dense +-I rows over it)
   auto materialise = [&](int k) -> vb_status {
@@ -538,6 +545,56 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
         }
         if ((long long)2 * nd.size != R) return fail(VB_ESHAPE, "internal: identity rows do not match node %d", k);
         HIPCHK(launch_identity_conv(a, c.cb, B.rowacc, B.st));
+      } else if (nd.op == VB_CONV2D && tn.c <= 8 && nd.kh * nd.kw * tn.c <= 64 && epi != E_STORE &&
+                 (size_t)rows * nd.h * nd.w * nd.kh * nd.kw * tn.c <= B.pool_floats &&
+                 (B.alpha == nullptr || B.alpha[t] == nullptr)) {
+        // few input channels: Q = Lambda . W over (tap, c_in) columns as a dense GEMM,
+        // then sum the taps per input pixel with the epilogue (no 3-of-32-column tiles)
+        const int qb = B.alloc();
+        if (qb < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted at node %d", k);
+        GemmDesc d = base_desc();
+        d.M = rows * nd.h * nd.w;
+        d.K = nd.c;
+        d.N = nd.kh * nd.kw * tn.c;
+        d.cs = d.K;
+        d.a_row_stride = d.K;
+        d.A = B.pool[cur];
+        d.B = B.wt[k];
+        d.epi = E_STORE;
+        d.out = B.pool[qb];
+        vb_status s = run_gemm_reduce(B, d, rows, 1, false);
+        if (s) return s;
+        Col2Im a{};
+        a.Q = B.pool[qb];
+        a.Ho = nd.h;
+        a.Wo = nd.w;
+        a.Ci = tn.c;
+        a.Hi = tn.h;
+        a.Wi = tn.w;
+        a.kh = nd.kh;
+        a.kw = nd.kw;
+        a.stride = nd.stride;
+        a.pad = nd.pad;
+        a.rows_per_b = (int)R;
+        a.mode = epi;
+        a.addend = pbuf >= 0 ? B.pool[pbuf] : nullptr;
+        a.out = outb >= 0 ? B.pool[outb] : nullptr;
+        a.psi_out = (B.psi_keep && B.psi_keep[t]) ? B.psi_keep[t] : nullptr;
+        a.bias = bias;
+        if (epi == E_RELAX) {
+          a.lo = B.lo[z] + chunk_off(z);
+          a.hi = B.hi[z] + chunk_off(z);
+        } else if (t == 0) {
+          a.center = B.dom.xc + chunk_off(0);
+          a.radius = B.dom.xr ? B.dom.xr + chunk_off(0) : nullptr;
+          a.eps = B.dom.eps;
+        } else {
+          a.center = B.box_c;
+          a.radius = B.box_r;
+        }
+        HIPCHK(launch_col2im(a, rows, B.rowacc, B.st));
+        B.release(qb);
+        B.release(cur);
       } else {
         // one launch (dense) or one per output-parity class (conv)
         std::vector<GemmDesc> descs;
@@ -572,8 +629,8 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
               d.radius = B.dom.xr ? B.dom.xr + chunk_off(0) : nullptr;
               d.eps = B.dom.eps;
             } else {
-              d.lo = B.lo[t] + chunk_off(t);
-              d.hi = B.hi[t] + chunk_off(t);
+              d.center = B.box_c;  // centre / radius of the domain box, this chunk
+              d.radius = B.box_r;
             }
           }
           const bool reduce = (epi != E_STORE) || bias != nullptr;
@@ -799,16 +856,19 @@ struct WsLayout {
   size_t pool_floats;  // per buffer
   size_t part_floats;
   size_t rows;
+  size_t box_floats;   // centre and radius of a box domain, each
   size_t bytes;
 };
 
-WsLayout layout_for(long long maxw, long long part_per_b, long long R, int cb, size_t extra_floats) {
+WsLayout layout_for(long long maxw, long long part_per_b, long long R, int cb, size_t extra_floats,
+                    long long box_per_b = 0) {
   WsLayout L;
   L.pool_floats = (size_t)cb * R * maxw;
   L.part_floats = (size_t)cb * part_per_b;
   L.rows = (size_t)cb * R;
+  L.box_floats = (size_t)cb * box_per_b;
   L.bytes = NPOOL * align_up(L.pool_floats * 4) + align_up(L.part_floats * 4) + align_up(L.rows * 4) +
-            align_up(extra_floats * 4);
+            2 * align_up(L.box_floats * 4) + align_up(extra_floats * 4);
   return L;
 }
 
@@ -820,9 +880,10 @@ vb_status backward_all(Backward& B, int start, int stop, const float* C, int m, 
   long long maxw, ppb;
   bwd_requirements(B.G, start, stop, R, maxw, ppb);
   if (C) maxw = std::max(maxw, B.G.n[start].size);
+  const long long box = stop > 0 ? B.G.n[stop].size : 0;
   int cb = batch;
-  while (cb > 1 && layout_for(maxw, ppb, R, cb, reserved_floats).bytes > ws_bytes) cb = (cb + 1) / 2;
-  WsLayout L = layout_for(maxw, ppb, R, cb, reserved_floats);
+  while (cb > 1 && layout_for(maxw, ppb, R, cb, reserved_floats, box).bytes > ws_bytes) cb = (cb + 1) / 2;
+  WsLayout L = layout_for(maxw, ppb, R, cb, reserved_floats, box);
   if (L.bytes > ws_bytes)
     return fail(VB_ENOMEM, "workspace of %zu bytes is too small: one batch element needs %zu", ws_bytes, L.bytes);
   char* p = ws + align_up(reserved_floats * 4);
@@ -830,10 +891,15 @@ vb_status backward_all(Backward& B, int start, int stop, const float* C, int m, 
     B.pool[i] = (float*)p;
     p += align_up(L.pool_floats * 4);
   }
+  B.pool_floats = L.pool_floats;
   B.part = (float*)p;
   B.part_floats = L.part_floats;
   p += align_up(L.part_floats * 4);
   B.rowacc = (float*)p;
+  p += align_up(L.rows * 4);
+  B.box_c = (float*)p;
+  p += align_up(L.box_floats * 4);
+  B.box_r = (float*)p;
   for (int b0 = 0; b0 < batch; b0 += cb) {
     const int n = std::min(cb, batch - b0);
     BwdCall c;
@@ -868,7 +934,7 @@ vb_status check_stream_ptrs(const void* p, const char* what) {
 // IBP
 
 vb_status ibp_impl(const Graph& G, int batch, const float* xc, const float* xr, float eps, float* const* lo,
-                   float* const* hi, hipStream_t st) {
+                   float* const* hi, hipStream_t st, void* ws = nullptr, size_t ws_bytes = 0) {
   const int N = (int)G.n.size();
   std::vector<char> done(N, 0);
   for (int k = 1; k < N; ++k) {
@@ -900,7 +966,25 @@ vb_status ibp_impl(const Graph& G, int batch, const float* xc, const float* xr, 
           d.relu_hi = hi[nd.cons[0]];
           done[nd.cons[0]] = 1;
         }
-        HIPCHK(launch_gemm(d, st));
+        // small grids (a Linear over a small batch): split K over more workgroups
+        const long long tiles = (long long)((d.M + 127) / 128) * ((d.N + 127) / 128);
+        const int stages = (d.K + 31) / 32;
+        int S = 1;
+        while (tiles * S * 2 <= 512 && stages / (S * 2) >= 4) S *= 2;
+        const size_t need = 2ull * S * d.M * d.N * sizeof(float);
+        if (S > 1 && ws && need <= ws_bytes) {
+          float* pc = (float*)ws;
+          float* pr = pc + (size_t)S * d.M * d.N;
+          GemmDesc e = d;
+          e.ksplit = S;
+          e.out = pc;
+          e.out2 = pr;
+          HIPCHK(launch_gemm(e, st));
+          HIPCHK(launch_ibp_splitk_finish(pc, pr, S, (long long)d.M * d.N, d.N, nd.b, lo[k], hi[k], d.relu_lo,
+                                          d.relu_hi, st));
+        } else {
+          HIPCHK(launch_gemm(d, st));
+        }
         break;
       }
       case VB_RELU:
@@ -948,7 +1032,7 @@ static size_t crown_workspace(const Graph& G, int batch, int m, int method, int 
     long long maxw, ppb;
     bwd_requirements(G, start, stop, R, maxw, ppb);
     if (spec) maxw = std::max(maxw, G.n[start].size);
-    best = std::max(best, layout_for(maxw, ppb, R, batch, wt_floats(G)).bytes);
+    best = std::max(best, layout_for(maxw, ppb, R, batch, wt_floats(G), stop > 0 ? G.n[stop].size : 0).bytes);
   };
   const int L = G.L;
   if (m > 0) {
@@ -1025,7 +1109,7 @@ extern "C" vb_status vb_ibp(const vb_graph* g, int32_t batch, const float* x_cen
       return fail(VB_ENOMEM, "workspace of %zu bytes is too small: one batch element needs %zu", ws_bytes, need);
   }
   hipStream_t st = (hipStream_t)stream;
-  s = ibp_impl(G, batch, x_center, x_radius, eps, node_lo, node_hi, st);
+  s = ibp_impl(G, batch, x_center, x_radius, eps, node_lo, node_hi, st, ws, ws_bytes);
   if (s) return s;
   if (C) return spec_ibp(G, batch, C, m, node_lo, node_hi, spec_lo, spec_hi, ws, ws_bytes, st);
   return VB_OK;
@@ -1102,7 +1186,7 @@ extern "C" vb_status vb_crown(const vb_graph* g, int32_t batch, const float* x_c
       return fail(VB_ENOMEM, "workspace of %zu bytes is too small: one batch element needs %zu", ws_bytes, need);
   }
   hipStream_t st = (hipStream_t)stream;
-  s = ibp_impl(G, batch, x_center, x_radius, eps, node_lo, node_hi, st);
+  s = ibp_impl(G, batch, x_center, x_radius, eps, node_lo, node_hi, st, ws, ws_bytes);
   if (s) return s;
   if (C && (ibp_lb || ibp_ub)) {
     s = spec_ibp(G, batch, C, m, node_lo, node_hi, ibp_lb, ibp_ub, ws, ws_bytes, st);

@@ -39,6 +39,10 @@ namespace {
 constexpr int BK = 32;
 constexpr int LDK = BK + 4;  // LDS row stride in floats
 
+__device__ __forceinline__ int fdiv(int x, const FastDiv& f) {
+  return f.d == 1 ? x : (int)(__umulhi((unsigned)x, f.mul) >> f.shr);
+}
+
 struct Pos {
   long long a_base;
   int Y, X;
@@ -54,10 +58,9 @@ __device__ __forceinline__ Pos pos_of(const GemmDesc& d, int m) {
     p.a_base = (long long)mm * d.a_row_stride;
     p.Y = p.X = 0;
   } else {
-    const int P = d.gh * d.gw;
-    const int row = mm / P;
-    const int q = mm - row * P;
-    p.Y = q / d.gw;
+    const int row = fdiv(mm, d.div_p);
+    const int q = mm - row * d.div_p.d;
+    p.Y = fdiv(q, d.div_gw);
     p.X = q - p.Y * d.gw;
     p.a_base = (long long)row * d.a_row_stride;
   }
@@ -181,10 +184,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   // each other; an M-tile's A rows are then fetched into one XCD's L2 once.
   const int mt = (d.M + BM - 1) / BM;
   const int nt = (d.N + BN - 1) / BN;
-  const int total = mt * nt;
+  const int ks_n = (EPI == E_IBP && d.ksplit > 1) ? d.ksplit : 1;
+  const int total = mt * nt * ks_n;
   const int per_xcd = (total + 7) / 8;
-  const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (tile >= total) return;
+  const int tile0 = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (tile0 >= total) return;
+  const int ks = tile0 / (mt * nt);
+  const int tile = tile0 - ks * (mt * nt);
   const int tm = tile / nt, tn = tile - tm * nt;
   const int m0 = tm * BM, n0 = tn * BN;
 
@@ -297,13 +303,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) accr[i][j][v] = 0.f;
 
-  const int nk = (d.K + BK - 1) / BK;
-  load(0);
+  // K stages of this workgroup (all of them unless IBP splits K)
+  const int nk_all = (d.K + BK - 1) / BK;
+  const int per_slice = (nk_all + ks_n - 1) / ks_n;
+  const int kb = ks * per_slice;
+  const int nk = min(nk_all - kb, per_slice);
+  load(kb * BK);
   store(0);
   __syncthreads();
   for (int t = 0; t < nk; ++t) {
     const int cur = t & 1;
-    if (t + 1 < nk) load((t + 1) * BK);
+    if (t + 1 < nk) load((kb + t + 1) * BK);
     // keep the next stage's global loads ahead of this stage's MFMAs and its
     // LDS stores (and their wait for those loads) behind them
     __builtin_amdgcn_sched_barrier(0);
@@ -358,16 +368,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
         long long opos, bpos;
         if (DENSE) {
           opos = m;
-          bpos = m / d.rows_per_b;
+          bpos = fdiv(m, d.div_rows);
         } else {
-          const int P = d.gh * d.gw;
-          const int row = m / P;
-          const int q = m - row * P;
-          const int Y = q / d.gw;
+          const int row = fdiv(m, d.div_p);
+          const int q = m - row * d.div_p.d;
+          const int Y = fdiv(q, d.div_gw);
           const int X = q - Y * d.gw;
           const long long sp = (long long)(Y * d.oym + d.oy0) * d.wo + (X * d.oxm + d.ox0);
           opos = (long long)row * d.ho * d.wo + sp;
-          bpos = (long long)(row / d.rows_per_b) * d.ho * d.wo + sp;
+          bpos = (long long)fdiv(row, d.div_rows) * d.ho * d.wo + sp;
         }
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
@@ -377,7 +386,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
             const long long bi = bpos * d.N + n;
             const int nb = d.bias_c ? n % d.bias_c : n;
             float val = acc[i][j][v];
-            if (EPI == E_IBP) {
+            if (EPI == E_IBP && ks_n > 1) {
+              const long long so = (long long)ks * d.M * d.N;
+              d.out[so + oi] = val;
+              d.out2[so + oi] = accr[NR == 1 ? 0 : i][NC == 1 ? 0 : j][v];
+            } else if (EPI == E_IBP) {
               const float cc = val + (d.bias ? d.bias[nb] : 0.f);
               const float rr = accr[NR == 1 ? 0 : i][NC == 1 ? 0 : j][v];
               const float l = cc - rr, u = cc + rr;
@@ -436,15 +449,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
                 d.out[oi] = o;
               } else {  // E_CONCRETIZE
                 if (d.psi_out) d.psi_out[oi] = val;
-                float c, r;
-                if (d.center) {
-                  c = d.center[bi];
-                  r = d.radius ? d.radius[bi] : d.eps;
-                } else {
-                  const float l = d.lo[bi], u = d.hi[bi];
-                  c = (l + u) * 0.5f;
-                  r = (u - l) * 0.5f;
-                }
+                const float c = d.center[bi];
+                const float r = d.radius ? d.radius[bi] : d.eps;
                 rowsum += val * c - fabsf(val) * r;
               }
             }
@@ -480,7 +486,8 @@ template <int BM, int BN, int WM, int WN, bool DENSE, bool FAST>
 hipError_t launch_tile(const GemmDesc& d, hipStream_t st) {
   const int mt = (d.M + BM - 1) / BM;
   const int nt = (d.N + BN - 1) / BN;
-  const dim3 g(((mt * nt + 7) / 8) * 8), b(WM * WN * 64);
+  const int ks = (d.epi == E_IBP && d.ksplit > 1) ? d.ksplit : 1;
+  const dim3 g(((mt * nt * ks + 7) / 8) * 8), b(WM * WN * 64);
   switch (d.epi) {
     case E_STORE:
       hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_STORE, FAST>), g, b, 0, st, d);
@@ -544,8 +551,12 @@ int gemm_ntiles(const GemmDesc& d) {
   return (d.N + bn - 1) / bn;
 }
 
-hipError_t launch_gemm(const GemmDesc& d, hipStream_t st) {
-  if (d.M <= 0 || d.N <= 0) return hipSuccess;
+hipError_t launch_gemm(const GemmDesc& desc, hipStream_t st) {
+  if (desc.M <= 0 || desc.N <= 0) return hipSuccess;
+  GemmDesc d = desc;
+  d.div_p = make_fastdiv(d.gh * d.gw);
+  d.div_gw = make_fastdiv(d.gw);
+  d.div_rows = make_fastdiv(d.rows_per_b);
   const bool dense = d.gh == 1 && d.gw == 1 && d.hs == 1 && d.ws == 1 && d.ntaps == 1 && d.cs == d.K &&
                      d.tap_dy[0] == 0 && d.tap_dx[0] == 0 && d.tap_w[0] == 0 && d.ho == 1 && d.wo == 1;
   const bool fast = is_fast(d);

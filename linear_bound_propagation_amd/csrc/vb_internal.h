@@ -29,6 +29,26 @@ enum EpiMode : int {
 
 constexpr int MAX_TAPS = 9;
 
+// Division by a runtime constant d >= 1 for 0 <= x < 2^31 by multiply-high:
+// with l = ceil(log2 d), mul = ceil(2^(31+l) / d) (< 2^32), x / d =
+// umulhi(x, mul) >> (l - 1); exact because x * (mul - 2^(31+l)/d) / 2^(31+l)
+// < 2^-l <= 1/d.  d = 1 is passed through (mul = 0).
+struct FastDiv {
+  uint32_t mul;
+  uint32_t shr;
+  int32_t d;
+};
+inline FastDiv make_fastdiv(int d) {
+  FastDiv f{0u, 0u, d};
+  if (d > 1) {
+    uint32_t l = 0;
+    while ((1ull << l) < (unsigned long long)d) ++l;
+    f.mul = (uint32_t)(((1ull << (31 + l)) + (unsigned long long)d - 1) / (unsigned long long)d);
+    f.shr = l - 1;
+  }
+  return f;
+}
+
 struct GemmDesc {
   int M, N, K;                 // output positions x output channels x reduction length
   int amode;                   // AMode of the A operand (E_IBP: A_IBP_BOX or A_IBP_BALL)
@@ -49,6 +69,7 @@ struct GemmDesc {
   // ---- output mapping: (row, Y, X) -> row*ho*wo + (Y*oym+oy0)*wo + (X*oxm+ox0)
   int ho, wo, oym, oy0, oxm, ox0;
   int rows_per_b;              // batch element of a row = row / rows_per_b
+  FastDiv div_p, div_gw, div_rows;  // filled by launch_gemm: gh*gw, gw, rows_per_b
   // ---- epilogue
   int epi;
   float* out;                  // [opos][N]   (E_IBP: lo)
@@ -62,10 +83,12 @@ struct GemmDesc {
   int bias_c;                  // channels of the bias: index = n % bias_c (0: index = n)
   const float* alpha;          // E_RELAX: per [opos][N] lower slope of unstable neurons, or NULL
   float* psi_out;              // E_RELAX: store the pre-relaxation value v, or NULL
-  const float* center;         // E_CONCRETIZE: centre/radius at [b-pos][N]; NULL -> from lo/hi
-  const float* radius;         // NULL -> eps (when center != NULL)
+  const float* center;         // E_CONCRETIZE: centre/radius of the domain box at [b-pos][N]
+  const float* radius;         // NULL -> eps
   float* part;                 // row partials [M][part_ld] (column = N-tile index)
   int part_ld;
+  int ksplit;                  // E_IBP only: > 1 splits K into slices; slice s writes its raw
+                               // products to out/out2 + s*M*N (reduced by launch_ibp_splitk_finish)
   // ---- E_ADJOINT (alpha-CROWN step): per [opos][N] of the ReLU after this node
   const float* psi_in;         // pre-relaxation product kept by the evaluation
   float* alpha_rw;             // lower slopes, updated in place
@@ -127,6 +150,28 @@ struct IdConv {
 };
 hipError_t launch_identity_conv(const IdConv& a, int batch, float* rowacc, hipStream_t st);
 
+// Transposed conv from tap-expanded products: Q [rows][Ho*Wo][taps*Ci] holds
+// Lambda . W[tap][:, ci] per output position; psi over the conv input is
+// psi[row][y][x][ci] = sum over taps (ky, kx) with oy = (y + pad - ky) / stride
+// integral and in range of Q[row][oy*Wo + ox][(ky*kw + kx)*Ci + ci].  The epilogue
+// is E_STORE / E_RELAX / E_CONCRETIZE as for IdConv (plus psi_out); rowacc += row sum.
+struct Col2Im {
+  const float* Q;
+  int Ho, Wo, Ci, Hi, Wi, kh, kw, stride, pad;
+  int rows_per_b;
+  int mode;
+  const float* addend;
+  float* out;
+  float* psi_out;
+  const float* lo;
+  const float* hi;
+  const float* bias;
+  const float* center;
+  const float* radius;
+  float eps;
+};
+hipError_t launch_col2im(const Col2Im& a, int rows, float* rowacc, hipStream_t st);
+
 // rowacc[b*2n + r] = s * bias[i % bias_c] for identity rows (s = +1 for r < n, -1 after; i = r mod n)
 hipError_t launch_identity_bias(int batch, int n, const float* bias, int bias_c, float* rowacc, hipStream_t st);
 
@@ -175,6 +220,16 @@ hipError_t launch_alpha_init(const float* lo, const float* hi, int batch, int ro
 // Adjoint at the input box: g[r][j] = c[b][j] - rad[b][j] * sign(psi[r][j]), b = r / rows_per_b
 hipError_t launch_adj_domain(const float* psi, int rows, int n, int rows_per_b, const float* center,
                              const float* radius, float eps, float* g, hipStream_t st);
+
+// Box centre and radius of bounds: c = (lo+hi)/2, r = (hi-lo)/2, n elements
+hipError_t launch_box_center_radius(const float* lo, const float* hi, long long n, float* c, float* r,
+                                    hipStream_t st);
+
+// lo = sum_s pc[s] + bias - sum_s pr[s], hi = ... + sum_s pr[s] over S slices of M*N
+// (fixed order); relu bounds too if given.  bias per column n = e % N.
+hipError_t launch_ibp_splitk_finish(const float* pc, const float* pr, int S, long long MN, int N,
+                                    const float* bias, float* lo, float* hi, float* relu_lo,
+                                    float* relu_hi, hipStream_t st);
 
 // Fill with a constant
 hipError_t launch_fill(float* p, float v, long long n, hipStream_t st);

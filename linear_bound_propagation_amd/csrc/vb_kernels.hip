@@ -240,6 +240,62 @@ hipError_t launch_identity_conv(const IdConv& a, int batch, float* rowacc, hipSt
   return hipGetLastError();
 }
 
+// one block per row
+__global__ __launch_bounds__(256) void col2im_kernel(const Col2Im a, float* __restrict__ rowacc) {
+  __shared__ float sh[4];
+  const long long row = blockIdx.x;
+  const long long b = row / a.rows_per_b;
+  const long long L = (long long)a.Hi * a.Wi * a.Ci;
+  const int NQ = a.kh * a.kw * a.Ci;
+  const float* q = a.Q + row * (long long)a.Ho * a.Wo * NQ;
+  float s = 0.f;
+  for (long long e = threadIdx.x; e < L; e += 256) {
+    const int ci = (int)(e % a.Ci);
+    const long long p = e / a.Ci;
+    const int y = (int)(p / a.Wi), x = (int)(p % a.Wi);
+    float v = 0.f;
+    for (int ky = 0; ky < a.kh; ++ky) {
+      const int ty = y + a.pad - ky;
+      if (ty < 0 || ty % a.stride) continue;
+      const int oy = ty / a.stride;
+      if (oy >= a.Ho) continue;
+      for (int kx = 0; kx < a.kw; ++kx) {
+        const int tx = x + a.pad - kx;
+        if (tx < 0 || tx % a.stride) continue;
+        const int ox = tx / a.stride;
+        if (ox >= a.Wo) continue;
+        v += q[((long long)oy * a.Wo + ox) * NQ + (ky * a.kw + kx) * a.Ci + ci];
+      }
+    }
+    if (a.addend) v += a.addend[row * L + e];
+    if (a.psi_out) a.psi_out[row * L + e] = v;
+    if (a.mode == E_STORE) {
+      a.out[row * L + e] = v;
+      if (a.bias) s += v * a.bias[ci];
+    } else if (a.mode == E_RELAX) {
+      const float l = a.lo[b * L + e], u = a.hi[b * L + e];
+      float al, sl, t;
+      relax_coeffs(l, u, al, sl, t);
+      const float o = v >= 0.f ? v * al : v * sl;
+      a.out[row * L + e] = o;
+      if (a.bias) s += o * a.bias[ci];
+      s += fminf(v, 0.f) * t;
+    } else {
+      const float c = a.center[b * L + e];
+      const float r = a.radius ? a.radius[b * L + e] : a.eps;
+      s += v * c - fabsf(v) * r;
+    }
+  }
+  s = block_sum(s, sh);
+  if (threadIdx.x == 0) rowacc[row] += s;
+}
+
+hipError_t launch_col2im(const Col2Im& a, int rows, float* rowacc, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(col2im_kernel, dim3(rows), dim3(256), 0, st, a, rowacc);
+  return hipGetLastError();
+}
+
 __global__ void identity_bias_kernel(int batch, int n, const float* __restrict__ bias, int bias_c,
                                      float* __restrict__ rowacc) {
   const long long total = (long long)batch * 2 * n;
@@ -440,6 +496,54 @@ hipError_t launch_ibp_gap(const float* lo_in, const float* hi_in, int batch, int
   long long n = (long long)batch * C;
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(ibp_gap_kernel, dim3((n + 255) / 256), dim3(256), 0, st, lo_in, hi_in, batch, P, C, lo, hi);
+  return hipGetLastError();
+}
+
+__global__ void box_cr_kernel(const float* __restrict__ lo, const float* __restrict__ hi, long long n,
+                              float* __restrict__ c, float* __restrict__ r) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x) {
+    const float l = lo[i], u = hi[i];
+    c[i] = (l + u) * 0.5f;
+    r[i] = (u - l) * 0.5f;
+  }
+}
+
+hipError_t launch_box_center_radius(const float* lo, const float* hi, long long n, float* c, float* r,
+                                    hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  long long blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(box_cr_kernel, dim3((unsigned)blocks), dim3(256), 0, st, lo, hi, n, c, r);
+  return hipGetLastError();
+}
+
+__global__ void ibp_splitk_kernel(const float* __restrict__ pc, const float* __restrict__ pr, int S, long long MN,
+                                  int N, const float* __restrict__ bias, float* __restrict__ lo,
+                                  float* __restrict__ hi, float* __restrict__ rlo, float* __restrict__ rhi) {
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < MN; e += (long long)gridDim.x * blockDim.x) {
+    float c = 0.f, r = 0.f;
+    for (int q = 0; q < S; ++q) {
+      c += pc[q * MN + e];
+      r += pr[q * MN + e];
+    }
+    c += bias ? bias[e % N] : 0.f;
+    const float l = c - r, u = c + r;
+    lo[e] = l;
+    hi[e] = u;
+    if (rlo) {
+      rlo[e] = fmaxf(l, 0.f);
+      rhi[e] = fmaxf(u, 0.f);
+    }
+  }
+}
+
+hipError_t launch_ibp_splitk_finish(const float* pc, const float* pr, int S, long long MN, int N, const float* bias,
+                                    float* lo, float* hi, float* rlo, float* rhi, hipStream_t st) {
+  if (MN <= 0) return hipSuccess;
+  long long blocks = (MN + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(ibp_splitk_kernel, dim3((unsigned)blocks), dim3(256), 0, st, pc, pr, S, MN, N, bias, lo, hi,
+                     rlo, rhi);
   return hipGetLastError();
 }
 

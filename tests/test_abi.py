@@ -104,3 +104,25 @@ def test_entry_points_reject_bad_arguments_without_launching():
     # concretize argument checks
     assert lbp.lib().vb_concretize(0, 4, 1, P(64), None, P(64), None, 0.1, None, None, None) == -1
     assert lbp.lib().vb_concretize(2, 4, 1, None, None, P(64), None, 0.1, None, None, None) == -1
+
+
+def _fastdiv(d):
+    # the host-side magic numbers of the library's division by a runtime constant
+    if d == 1:
+        return 0, 0
+    l = (d - 1).bit_length()
+    return ((1 << (31 + l)) + d - 1) // d, l - 1
+
+
+def test_fastdiv_magic_numbers_are_exact():
+    import numpy as np
+    rng = np.random.default_rng(0)
+    for d in list(range(1, 300)) + [1024, 3072, 4097, 65536, 65537, 99991, 2 ** 20 + 7, 2 ** 30 + 1]:
+        mul, shr = _fastdiv(d)
+        xs = np.concatenate([np.arange(0, 3000), rng.integers(0, 2 ** 31, 3000),
+                             np.array([2 ** 31 - 1, d - 1, d, d + 1, 2 * d - 1, 2 * d])])
+        for x in xs.tolist():
+            if x < 0 or x >= 2 ** 31:
+                continue
+            q = x if d == 1 else ((x * mul) >> 32) >> shr
+            assert mul < 2 ** 32 and q == x // d, (x, d, q)
