@@ -282,6 +282,8 @@ struct Backward {
   // centre / radius of a box domain (stop > 0) for the current chunk
   float* box_c = nullptr;
   float* box_r = nullptr;
+  // relaxation coefficients of the current target node, this chunk
+  float4* coef = nullptr;
 
   int alloc() {
     for (int i = 0; i < NPOOL; ++i)
@@ -366,7 +368,9 @@ vb_status run_gemm_reduce(Backward& B, GemmDesc& d, int rows, int P, bool reduce
     rec.flops = alg_flops;
     g_prof.push_back(rec);
   }
-  if (reduce) HIPCHK(launch_rows_reduce(B.part, 1, rows, P, d.part_ld, d.part_ld, B.rowacc, 1, B.st));
+  const bool gather = !gemm_is_dense(d);
+  if (reduce)
+    HIPCHK(launch_rows_reduce(B.part, 1, rows, P, d.part_ld, d.part_ld, B.rowacc, 1, gather ? 1 : 0, B.st));
   return VB_OK;
 }
 
@@ -607,8 +611,12 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
               if (conv_backward(nd, tn, B.pool[cur], rows, py, px, d)) descs.push_back(d);
             }
         }
+        if (epi == E_RELAX)
+          HIPCHK(launch_relax_coef(B.lo[z] + chunk_off(z), B.hi[z] + chunk_off(z), (long long)c.cb * G.n[z].size,
+                                   B.coef, B.st));
         for (GemmDesc& d : descs) {
           d.B = B.wt[k];
+          d.coef = B.coef;
           d.epi = epi;
           d.rows_per_b = (int)R;
           d.addend = (pbuf >= 0) ? B.pool[pbuf] : nullptr;
@@ -857,6 +865,7 @@ struct WsLayout {
   size_t part_floats;
   size_t rows;
   size_t box_floats;   // centre and radius of a box domain, each
+  size_t coef_floats;  // relaxation coefficients (float4 per neuron of one batch chunk)
   size_t bytes;
 };
 
@@ -867,8 +876,9 @@ WsLayout layout_for(long long maxw, long long part_per_b, long long R, int cb, s
   L.part_floats = (size_t)cb * part_per_b;
   L.rows = (size_t)cb * R;
   L.box_floats = (size_t)cb * box_per_b;
+  L.coef_floats = 4 * (size_t)cb * maxw;
   L.bytes = NPOOL * align_up(L.pool_floats * 4) + align_up(L.part_floats * 4) + align_up(L.rows * 4) +
-            2 * align_up(L.box_floats * 4) + align_up(extra_floats * 4);
+            2 * align_up(L.box_floats * 4) + align_up(L.coef_floats * 4) + align_up(extra_floats * 4);
   return L;
 }
 
@@ -900,6 +910,8 @@ vb_status backward_all(Backward& B, int start, int stop, const float* C, int m, 
   B.box_c = (float*)p;
   p += align_up(L.box_floats * 4);
   B.box_r = (float*)p;
+  p += align_up(L.box_floats * 4);
+  B.coef = (float4*)p;
   for (int b0 = 0; b0 < batch; b0 += cb) {
     const int n = std::min(cb, batch - b0);
     BwdCall c;
@@ -1388,8 +1400,9 @@ extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float
     d.out = gbuf[cur ^ 1];
     d.bias = nd.b;
     d.bias_c = 0;
-    d.lo = node_lo[k];
-    d.hi = node_hi[k];
+    // coefficient buffer of the evaluation's layout: 4 * batch * (widest node) floats
+    HIPCHK(launch_relax_coef(node_lo[k], node_hi[k], (long long)batch * nd.size, B.coef, st));
+    d.coef = B.coef;
     d.rows_per_b = m;
     d.psi_in = psi[r];
     d.alpha_rw = alpha[r];

@@ -58,8 +58,8 @@ __device__ __forceinline__ Pos pos_of(const GemmDesc& d, int m) {
     p.a_base = (long long)mm * d.a_row_stride;
     p.Y = p.X = 0;
   } else {
-    const int row = fdiv(mm, d.div_p);
-    const int q = mm - row * d.div_p.d;
+    const int q = fdiv(mm, d.div_nrows);  // position-major
+    const int row = mm - q * d.div_nrows.d;
     p.Y = fdiv(q, d.div_gw);
     p.X = q - p.Y * d.gw;
     p.a_base = (long long)row * d.a_row_stride;
@@ -317,36 +317,48 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
     // keep the next stage's global loads ahead of this stage's MFMAs and its
     // LDS stores (and their wait for those loads) behind them
     __builtin_amdgcn_sched_barrier(0);
-    // MFMA step (q, s): lane half h supplies k = 16h + 4q + s
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float4 a4[FM], b4[FN], r4[NR];
+    // MFMA step (q, s): lane half h supplies k = 16h + 4q + s.  Fragments are
+    // double-buffered in registers: the LDS reads of chunk q+1 are issued
+    // before the MFMAs of chunk q, so their latency hides behind those MFMAs.
+    float4 fa[2][FM], fb[2][FN], fr[2][NR];
+    auto frag = [&](int slot, int q) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        a4[i] = *reinterpret_cast<const float4*>(&As[cur][0][(wm * WTM + i * 32 + l32) * LDK + 16 * half + 4 * q]);
+        fa[slot][i] = *reinterpret_cast<const float4*>(&As[cur][0][(wm * WTM + i * 32 + l32) * LDK + 16 * half + 4 * q]);
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        b4[j] = *reinterpret_cast<const float4*>(&Bs[cur][(wn * WTN + j * 32 + l32) * LDK + 16 * half + 4 * q]);
+        fb[slot][j] = *reinterpret_cast<const float4*>(&Bs[cur][(wn * WTN + j * 32 + l32) * LDK + 16 * half + 4 * q]);
       if (NA == 2) {
 #pragma unroll
         for (int i = 0; i < NR; ++i)
-          r4[i] = *reinterpret_cast<const float4*>(
+          fr[slot][i] = *reinterpret_cast<const float4*>(
               &As[cur][NA - 1][(wm * WTM + i * 32 + l32) * LDK + 16 * half + 4 * q]);
       }
+    };
+    frag(0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int sl = q & 1;
+      if (q < 3) frag(sl ^ 1, q + 1);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[i][s], b4[j][s], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[sl][i][s], fb[sl][j][s], acc[i][j], 0, 0, 0);
         if (NA == 2) {
 #pragma unroll
           for (int i = 0; i < NR; ++i)
 #pragma unroll
             for (int j = 0; j < NC; ++j)
-              accr[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(r4[i][s], fabsf(b4[j][s]), accr[i][j], 0, 0, 0);
+              accr[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fr[sl][i][s], fabsf(fb[sl][j][s]), accr[i][j], 0, 0, 0);
         }
+      }
+      if (q < 3) {
+        // keep the reads of chunk q+1 in front of this chunk's MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, FM + FN + (NA == 2 ? NR : 0), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * FM * FN * NA, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -370,8 +382,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
           opos = m;
           bpos = fdiv(m, d.div_rows);
         } else {
-          const int row = fdiv(m, d.div_p);
-          const int q = m - row * d.div_p.d;
+          const int q = fdiv(m, d.div_nrows);  // position-major
+          const int row = m - q * d.div_nrows.d;
           const int Y = fdiv(q, d.div_gw);
           const int X = q - Y * d.gw;
           const long long sp = (long long)(Y * d.oym + d.oy0) * d.wo + (X * d.oxm + d.ox0);
@@ -406,34 +418,23 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
                 d.out[oi] = val;
                 if (d.bias) rowsum += val * d.bias[nb];
               } else if (EPI == E_RELAX) {
-                const float l = d.lo[bi], u = d.hi[bi];
-                float a, s, tt;
-                if (u <= 0.f) {
-                  a = 0.f; s = 0.f; tt = 0.f;
-                } else if (l >= 0.f) {
-                  a = 1.f; s = 1.f; tt = 0.f;
-                } else {
-                  s = u / (u - l);
-                  tt = -s * l;
-                  a = d.alpha ? d.alpha[oi] : ((u >= -l) ? 1.f : 0.f);
-                }
+                const float4 cf = d.coef[bi];
+                const float a = (d.alpha && cf.w != 0.f) ? d.alpha[oi] : cf.x;
+                const float s = cf.y, tt = cf.z;
                 const float o = (val >= 0.f) ? val * a : val * s;
                 d.out[oi] = o;
                 if (d.psi_out) d.psi_out[oi] = val;
                 if (d.bias) rowsum += o * d.bias[nb];
                 rowsum += fminf(val, 0.f) * tt;
               } else if (EPI == E_ADJOINT) {
-                const float l = d.lo[bi], u = d.hi[bi];
+                const float4 cf = d.coef[bi];
                 const float g = val + (d.bias ? d.bias[nb] : 0.f);
-                const float psi = d.psi_in[oi];
                 float o;
-                if (u <= 0.f) {
-                  o = 0.f;
-                } else if (l >= 0.f) {
-                  o = g;
+                if (cf.w == 0.f) {
+                  o = g * cf.y;  // stable: a = s (0 inactive, 1 active)
                 } else {
-                  const float s = u / (u - l);
-                  const float tt = -s * l;
+                  const float psi = d.psi_in[oi];
+                  const float s = cf.y, tt = cf.z;
                   const float a_old = d.alpha_rw[oi];
                   o = (psi >= 0.f) ? g * a_old : g * s + tt;
                   if (d.do_update) {
@@ -557,8 +558,8 @@ hipError_t launch_gemm(const GemmDesc& desc, hipStream_t st) {
   d.div_p = make_fastdiv(d.gh * d.gw);
   d.div_gw = make_fastdiv(d.gw);
   d.div_rows = make_fastdiv(d.rows_per_b);
-  const bool dense = d.gh == 1 && d.gw == 1 && d.hs == 1 && d.ws == 1 && d.ntaps == 1 && d.cs == d.K &&
-                     d.tap_dy[0] == 0 && d.tap_dx[0] == 0 && d.tap_w[0] == 0 && d.ho == 1 && d.wo == 1;
+  d.div_nrows = make_fastdiv(d.M / (d.gh * d.gw));
+  const bool dense = gemm_is_dense(d);
   const bool fast = is_fast(d);
   const int bn = tile_n(d, fast);
   if (bn == 256) {

@@ -52,7 +52,9 @@ inline FastDiv make_fastdiv(int d) {
 struct GemmDesc {
   int M, N, K;                 // output positions x output channels x reduction length
   int amode;                   // AMode of the A operand (E_IBP: A_IBP_BOX or A_IBP_BALL)
-  // ---- A operand: position m -> (row, Y, X) on a gh x gw grid per row;
+  // ---- A operand: position m -> (row, Y, X) on a gh x gw grid per row; for a
+  //      gather (conv) GEMM m is position-major, m = (Y*gw + X)*rows + row, so
+  //      a tile holds many rows of one pixel and their relaxation data is shared;
   //      reduction index k -> (tap j, channel c) with k = j*cs + c;
   //      element = A[row*a_row_stride + ((Y*sy + dy_j)*ws + (X*sx + dx_j))*cs + c],
   //      zero outside [0,hs) x [0,ws).  Dense GEMM: gh=gw=hs=ws=1, cs=K, 1 tap.
@@ -69,7 +71,7 @@ struct GemmDesc {
   // ---- output mapping: (row, Y, X) -> row*ho*wo + (Y*oym+oy0)*wo + (X*oxm+ox0)
   int ho, wo, oym, oy0, oxm, ox0;
   int rows_per_b;              // batch element of a row = row / rows_per_b
-  FastDiv div_p, div_gw, div_rows;  // filled by launch_gemm: gh*gw, gw, rows_per_b
+  FastDiv div_p, div_gw, div_rows, div_nrows;  // filled by launch_gemm: gh*gw, gw, rows_per_b, M/(gh*gw)
   // ---- epilogue
   int epi;
   float* out;                  // [opos][N]   (E_IBP: lo)
@@ -77,8 +79,10 @@ struct GemmDesc {
   float* relu_lo;              // E_IBP: bounds of a consumer ReLU (or NULL)
   float* relu_hi;
   const float* addend;         // [opos][N] or NULL, added to acc before the epilogue
-  const float* lo;             // target-node bounds at [b-pos][N] (E_RELAX, E_CONCRETIZE box)
+  const float* lo;             // (unused by the GEMM epilogues; kept for descriptors)
   const float* hi;
+  const float4* coef;          // E_RELAX / E_ADJOINT: relaxation of the target at [b-pos][N]:
+                               // {a (adaptive lower slope), s, t, 1 if unstable else 0}
   const float* bias;           // per output channel (E_STORE / E_RELAX / E_IBP)
   int bias_c;                  // channels of the bias: index = n % bias_c (0: index = n)
   const float* alpha;          // E_RELAX: per [opos][N] lower slope of unstable neurons, or NULL
@@ -98,14 +102,22 @@ struct GemmDesc {
   float lr, beta1, beta2, bc1, bc2, adam_eps;  // bc = 1 / (1 - beta^t)
 };
 
+// A one-tap, one-position descriptor is a plain GEMM (row-major m); anything
+// else is a gather GEMM (position-major m).
+inline bool gemm_is_dense(const GemmDesc& d) {
+  return d.gh == 1 && d.gw == 1 && d.hs == 1 && d.ws == 1 && d.ntaps == 1 && d.cs == d.K && d.tap_dy[0] == 0 &&
+         d.tap_dx[0] == 0 && d.tap_w[0] == 0 && d.ho == 1 && d.wo == 1;
+}
+
 // Launch the implicit GEMM; returns hipSuccess or the launch error.
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t st);
 // Number of N-tiles launch_gemm uses for this descriptor (= partial columns).
 int gemm_ntiles(const GemmDesc& d);
 
 // rowacc[r] (+)= sum over z < Z, p < P, s < S of part[((z*rows + r)*P + p)*ld + s]
+// (pos_major: part[((z*P + p)*rows + r)*ld + s])
 hipError_t launch_rows_reduce(const float* part, int Z, int rows, int P, int S, int ld,
-                              float* rowacc, int accumulate, hipStream_t st);
+                              float* rowacc, int accumulate, int pos_major, hipStream_t st);
 
 // Write the final outputs from row accumulators.  rows per batch element = 2R:
 // lb[b*R + i] = acc[b*2R + i], ub[b*R + i] = -acc[b*2R + R + i]  (NULL skips)
@@ -220,6 +232,10 @@ hipError_t launch_alpha_init(const float* lo, const float* hi, int batch, int ro
 // Adjoint at the input box: g[r][j] = c[b][j] - rad[b][j] * sign(psi[r][j]), b = r / rows_per_b
 hipError_t launch_adj_domain(const float* psi, int rows, int n, int rows_per_b, const float* center,
                              const float* radius, float eps, float* g, hipStream_t st);
+
+// Relaxation coefficients of n neurons from their bounds: {a, s, t, unstable}
+// (inactive u <= 0: 0,0,0; active l >= 0: 1,1,0; unstable: adaptive a, s = u/(u-l), t = -s l)
+hipError_t launch_relax_coef(const float* lo, const float* hi, long long n, float4* coef, hipStream_t st);
 
 // Box centre and radius of bounds: c = (lo+hi)/2, r = (hi-lo)/2, n elements
 hipError_t launch_box_center_radius(const float* lo, const float* hi, long long n, float* c, float* r,

@@ -45,7 +45,7 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
 
 __global__ __launch_bounds__(256) void rows_reduce_kernel(const float* __restrict__ part, int Z, int rows,
                                                           int P, int S, int ld, float* __restrict__ rowacc,
-                                                          int accumulate) {
+                                                          int accumulate, int pos_major) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
@@ -57,17 +57,18 @@ __global__ __launch_bounds__(256) void rows_reduce_kernel(const float* __restric
     int q = e - z * PS;
     int p = q / S;
     int c = q - p * S;
-    s += part[(((long long)z * rows + row) * P + p) * ld + c];
+    s += pos_major ? part[(((long long)z * P + p) * rows + row) * ld + c]
+                   : part[(((long long)z * rows + row) * P + p) * ld + c];
   }
   s = wave_sum(s);
   if (lane == 0) rowacc[row] = accumulate ? rowacc[row] + s : s;
 }
 
 hipError_t launch_rows_reduce(const float* part, int Z, int rows, int P, int S, int ld, float* rowacc,
-                              int accumulate, hipStream_t st) {
+                              int accumulate, int pos_major, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(rows_reduce_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, part, Z, rows, P, S, ld,
-                     rowacc, accumulate);
+                     rowacc, accumulate, pos_major);
   return hipGetLastError();
 }
 
@@ -496,6 +497,24 @@ hipError_t launch_ibp_gap(const float* lo_in, const float* hi_in, int batch, int
   long long n = (long long)batch * C;
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(ibp_gap_kernel, dim3((n + 255) / 256), dim3(256), 0, st, lo_in, hi_in, batch, P, C, lo, hi);
+  return hipGetLastError();
+}
+
+__global__ void relax_coef_kernel(const float* __restrict__ lo, const float* __restrict__ hi, long long n,
+                                  float4* __restrict__ coef) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x) {
+    const float l = lo[i], u = hi[i];
+    float a, s, t;
+    relax_coeffs(l, u, a, s, t);
+    coef[i] = make_float4(a, s, t, (u > 0.f && l < 0.f) ? 1.f : 0.f);
+  }
+}
+
+hipError_t launch_relax_coef(const float* lo, const float* hi, long long n, float4* coef, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  long long blocks = (n + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(relax_coef_kernel, dim3((unsigned)blocks), dim3(256), 0, st, lo, hi, n, coef);
   return hipGetLastError();
 }
 
