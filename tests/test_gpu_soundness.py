@@ -1,0 +1,126 @@
+"""GPU soundness: bounds from the HIP library hold on 1e5 sampled points per instance.
+
+The sampled network values are computed by a plain float64 torch forward pass
+on the GPU (test infrastructure; the library is not involved), for points drawn
+uniformly in the L-inf ball plus random ball corners.  A bound passes if every
+sampled value lies within it up to the parity tolerance 1e-5 + 1e-4 |bound|.
+"""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import workloads as wk
+from helpers import ensure_built
+
+pytestmark = pytest.mark.gpu
+N_SAMPLES = 100_000
+
+
+@pytest.fixture(scope="module")
+def lbp():
+    ensure_built()
+    import linear_bound_propagation_amd as m
+    return m
+
+
+def _forward(nodes, x, dtype=torch.float64):
+    """Values of every node for a batch x [n][*input shape] (NCHW), on x's device."""
+    dev = x.device
+    vals = []
+    for nd in nodes:
+        if nd.op == "input":
+            v = x
+        elif nd.op == "linear":
+            v = vals[nd.inputs[0]] @ torch.as_tensor(nd.weight, dtype=dtype, device=dev).T + \
+                torch.as_tensor(nd.bias, dtype=dtype, device=dev)
+        elif nd.op == "conv":
+            v = F.conv2d(vals[nd.inputs[0]], torch.as_tensor(nd.weight, dtype=dtype, device=dev),
+                         torch.as_tensor(nd.bias, dtype=dtype, device=dev), stride=nd.stride, padding=nd.pad)
+        elif nd.op == "relu":
+            v = vals[nd.inputs[0]].clamp(min=0)
+        elif nd.op == "add":
+            v = vals[nd.inputs[0]] + vals[nd.inputs[1]]
+        elif nd.op == "gap":
+            v = vals[nd.inputs[0]].mean(dim=(2, 3))
+        elif nd.op == "flatten":
+            v = vals[nd.inputs[0]].reshape(x.shape[0], -1)
+        vals.append(v)
+    return vals
+
+
+def _check(wl, b, bounds, node_bounds=None, chunk=10_000, dtype=torch.float64, seed=0):
+    """Sample N_SAMPLES points around input b; check spec bounds (list of (lb, ub) [m])
+    and optionally node bounds {k: (lo [size], hi [size])} (channels-last flattening)."""
+    g = torch.Generator(device="cuda").manual_seed(seed + 7919 * b)
+    x0 = torch.as_tensor(wl.x0[b], dtype=dtype, device="cuda")
+    eps = float(wl.eps)
+    C = torch.as_tensor(wl.C[b], dtype=dtype, device="cuda")
+    worst = -float("inf")
+    for start in range(0, N_SAMPLES, chunk):
+        n = min(chunk, N_SAMPLES - start)
+        u = torch.rand((n,) + x0.shape, generator=g, device="cuda", dtype=dtype) * 2 - 1
+        n_corner = n // 5
+        u[:n_corner] = torch.sign(u[:n_corner])
+        x = x0 + eps * u
+        vals = _forward(wl.nodes, x, dtype)
+        spec = vals[-1] @ C.T
+        for lb, ub in bounds:
+            lb = lb.to(dtype)
+            ub = ub.to(dtype)
+            tl = 1e-5 + 1e-4 * lb.abs()
+            tu = 1e-5 + 1e-4 * ub.abs()
+            assert bool((spec >= lb - tl).all()), f"input {b}: spec value below its lower bound"
+            assert bool((spec <= ub + tu).all()), f"input {b}: spec value above its upper bound"
+            worst = max(worst, float((lb - spec.min(0).values).max()), float((spec.max(0).values - ub).max()))
+        for k, (lo, hi) in (node_bounds or {}).items():
+            v = vals[k]
+            if v.dim() == 4:
+                v = v.permute(0, 2, 3, 1)
+            v = v.reshape(n, -1)
+            lo = lo.to(dtype)
+            hi = hi.to(dtype)
+            assert bool((v >= lo - (1e-5 + 1e-4 * lo.abs())).all()), f"input {b}: node {k} below its lower bound"
+            assert bool((v <= hi + (1e-5 + 1e-4 * hi.abs())).all()), f"input {b}: node {k} above its upper bound"
+    return worst
+
+
+def _crown(lbp, wl):
+    net, x, C = lbp.prepare(wl)
+    out = lbp.crown(net, x, float(wl.eps), C, wl.intermediate, wl.region_start)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("cfg,instances", [(1, range(16)), (2, (0, 21, 42, 63)), (3, (0, 31))])
+def test_sound_crown_and_ibp(lbp, cfg, instances):
+    wl = wk.config(cfg)
+    print(wl.name, flush=True)
+    out = _crown(lbp, wl)
+    relu_inputs = [wl.nodes[k].inputs[0] for k, n in enumerate(wl.nodes) if n.op == "relu"]
+    for b in instances:
+        nb = {z: (out["lo"][z][b], out["hi"][z][b]) for z in relu_inputs}
+        w = _check(wl, b, [(out["lb"][b], out["ub"][b]), (out["ibp_lb"][b], out["ibp_ub"][b])], nb)
+        print(f"  input {b}: sound; smallest gap between a sampled value and a bound: {-w:.4g}", flush=True)
+
+
+def test_sound_alpha_crown_iterates(lbp):
+    wl = wk.config(4)
+    print(wl.name, flush=True)
+    net, x, C = lbp.prepare(wl)
+    out = lbp.crown(net, x, float(wl.eps), C, "ibp")
+    best, lb_steps, _ = lbp.alpha_crown(net, x, float(wl.eps), C, out["lo"], out["hi"], wl.alpha_steps, wl.alpha_lr)
+    torch.cuda.synchronize()
+    for b in (0, 15):
+        bounds = [(lb_steps[t][b], torch.full_like(best[b], float("inf"))) for t in range(lb_steps.shape[0])]
+        bounds.append((best[b], out["ub"][b]))
+        _check(wl, b, bounds)
+
+
+def test_sound_residual(lbp):
+    wl = wk.config(5, batch=1)
+    print(wl.name, flush=True)
+    out = _crown(lbp, wl)
+    # float32 forward for this network (float64 convolutions are slow); the
+    # tolerance of the check covers float32 rounding of the sampled values
+    _check(wl, 0, [(out["lb"][0], out["ub"][0]), (out["ibp_lb"][0], out["ibp_ub"][0])], dtype=torch.float32)
