@@ -123,6 +123,42 @@ def cpu_baseline(wl, flops_total, budget_s=12.0):
             "sample": f"first {k} of {wl.batch} inputs, all {wl.m} specs, float64 torch-CPU oracle, {elapsed:.1f} s"}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_backsub_traffic_mlp3072.txt")
+GEMM_SOURCE = os.path.join(ROOT, "linear_bound_propagation_amd", "csrc", "vb_gemm.hip")
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per back-substitution GEMM launch from the committed counter summary,
+    or None when it is missing, for another workload, or taken on a different kernel source."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    if kv.get("kernel_source_sha256") != sha or kv.get("workload") != workload_name:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(nbytes):
+    """A plain device-to-device copy of `nbytes` (read + write), run a few times:
+    the calibration kernel for the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    x = torch.empty(nbytes // 4, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "launches": 3}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,7 +166,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the bound computation is not "
               "sharded across GPUs in this build", file=sys.stderr)
@@ -208,13 +249,13 @@ def main():
         "specs_per_s": round(wl.batch * wl.m / (ms * 1e-3), 1),
         "verified_frac": verified,
         "roofline": {
-            "kernel": "back-substitution GEMM with ReLU-relaxation epilogue",
+            "kernel": "gemm_kernel: back-substitution GEMM (relaxation / concretisation epilogues)",
             "bound": "mfma",
             "achieved": None if achieved is None else round(achieved, 3),
             "peak": PEAK_FP32_MFMA_TFLOPS,
             "unit": "TFLOP/s",
             "frac": None if achieved is None else round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(wl.name),
             "launches": k_launches,
             "avg_launch_ms": round(k_ms / max(k_launches, 1), 4),
             "alg_flop_per_launch": k_flops / max(k_launches, 1),

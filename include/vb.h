@@ -179,8 +179,8 @@ vb_status vb_crown(const vb_graph* g, int32_t batch,
 
 /* Measurement of the back-substitution GEMM (the dominant kernel).
  * vb_profile_start() begins recording a pair of HIP events around every
- * back-substitution GEMM launch whose epilogue applies the ReLU relaxation,
- * on the stream of that launch, together with its algorithmic FLOPs
+ * back-substitution GEMM launch (relaxation, concretisation or store
+ * epilogue), on the stream of that launch, together with its algorithmic FLOPs
  * (2 x rows x multiply-adds of the layer, without padding or tile waste).
  * vb_profile_stop() stops recording, waits for the recorded events and
  * returns the summed kernel time (ms), summed FLOPs and launch count.

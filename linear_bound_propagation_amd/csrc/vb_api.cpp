@@ -355,7 +355,7 @@ vb_status run_gemm_reduce(Backward& B, GemmDesc& d, int rows, int P, bool reduce
   d.part_ld = gemm_ntiles(d);
   if (reduce && (size_t)d.M * d.part_ld > B.part_floats)
     return fail(VB_ENOMEM, "internal: partial buffer too small (%lld > %zu)", (long long)d.M * d.part_ld, B.part_floats);
-  const bool prof = g_prof_on && d.epi == E_RELAX;
+  const bool prof = g_prof_on && alg_flops > 0.0;
   ProfRec rec{};
   if (prof) {
     HIPCHK(hipEventCreate(&rec.a));
@@ -566,7 +566,9 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
         d.B = B.wt[k];
         d.epi = E_STORE;
         d.out = B.pool[qb];
-        vb_status s = run_gemm_reduce(B, d, rows, 1, false);
+        // algorithmic work of this layer: the forward multiply-adds per row
+        const double macs = (double)rows * nd.c * tn.c * nd.kh * nd.kw * nd.h * nd.w;
+        vb_status s = run_gemm_reduce(B, d, rows, 1, false, 2.0 * macs);
         if (s) return s;
         Col2Im a{};
         a.Q = B.pool[qb];
