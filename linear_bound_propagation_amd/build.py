@@ -18,6 +18,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 VALU instructions stay off: plain float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the GEMM epilogues index the MFMA accumulators by unrolled loop counters;
+    # a partially unrolled loop would move the accumulators to scratch memory
+    "-mllvm", "-pragma-unroll-threshold=200000",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -317,10 +317,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
     // keep the next stage's global loads ahead of this stage's MFMAs and its
     // LDS stores (and their wait for those loads) behind them
     __builtin_amdgcn_sched_barrier(0);
-    // MFMA step (q, s): lane half h supplies k = 16h + 4q + s.  Fragments are
-    // double-buffered in registers: the LDS reads of chunk q+1 are issued
-    // before the MFMAs of chunk q, so their latency hides behind those MFMAs.
-    float4 fa[2][FM], fb[2][FN], fr[2][NR];
+    // MFMA step (q, s): lane half h supplies k = 16h + 4q + s.  On the smaller
+    // wave tiles the fragments are double-buffered in registers: the LDS reads
+    // of chunk q+1 are issued before the MFMAs of chunk q, so their latency
+    // hides behind those MFMAs.  The largest wave tile has no registers to
+    // spare for a second set and relies on its 8 MFMAs per read instead.
+    constexpr bool DBUF = FM * FN < 8;
+    constexpr int NS = DBUF ? 2 : 1;
+    float4 fa[NS][FM], fb[NS][FN], fr[NS][NR];
     auto frag = [&](int slot, int q) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -335,11 +339,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
               &As[cur][NA - 1][(wm * WTM + i * 32 + l32) * LDK + 16 * half + 4 * q]);
       }
     };
-    frag(0, 0);
+    if (DBUF) frag(0, 0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int sl = q & 1;
-      if (q < 3) frag(sl ^ 1, q + 1);
+      const int sl = DBUF ? (q & 1) : 0;
+      if (DBUF && q < 3) frag(sl ^ 1, q + 1);
+      if (!DBUF) frag(0, q);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -355,7 +360,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
               accr[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fr[sl][i][s], fabsf(fb[sl][j][s]), accr[i][j], 0, 0, 0);
         }
       }
-      if (q < 3) {
+      if (DBUF && q < 3) {
         // keep the reads of chunk q+1 in front of this chunk's MFMAs
         __builtin_amdgcn_sched_group_barrier(0x100, FM + FN + (NA == 2 ? NR : 0), 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 4 * FM * FN * NA, 0);
@@ -367,101 +372,184 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   }
 
   // ---- epilogue.  Register v of lane l of a 32x32 fp32 MFMA result holds
-  // row 8*(v/4) + 4*(l/32) + v%4 and column l%32 of the block.
+  // row 8*(v/4) + 4*(l/32) + v%4 and column l%32 of the block.  The elements
+  // are handled 8 rows at a time: indices first (clamped in range), then every
+  // load of the group (unconditional, so they can all be in flight together),
+  // then the arithmetic with predicated stores.
   constexpr bool ROWSUM = (EPI != E_IBP && EPI != E_ADJOINT);
+  constexpr int G = (FM * FN >= 8) ? 4 : 8;  // rows per group (fewer where registers are short)
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int lr = wm * WTM + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-      const int m = m0 + lr;
-      float rowsum = 0.f;
-      if (m < d.M) {
-        long long opos, bpos;
+    for (int v0 = 0; v0 < 16; v0 += G) {
+      long long opos[G], bpos[G];
+      bool mok[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int v = v0 + g;
+        const int m = m0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+        mok[g] = m < d.M;
+        const int mm = mok[g] ? m : 0;
         if (DENSE) {
-          opos = m;
-          bpos = fdiv(m, d.div_rows);
+          opos[g] = mm;
+          bpos[g] = fdiv(mm, d.div_rows);
         } else {
-          const int q = fdiv(m, d.div_nrows);  // position-major
-          const int row = m - q * d.div_nrows.d;
+          const int q = fdiv(mm, d.div_nrows);  // position-major
+          const int row = mm - q * d.div_nrows.d;
           const int Y = fdiv(q, d.div_gw);
           const int X = q - Y * d.gw;
           const long long sp = (long long)(Y * d.oym + d.oy0) * d.wo + (X * d.oxm + d.ox0);
-          opos = (long long)row * d.ho * d.wo + sp;
-          bpos = (long long)fdiv(row, d.div_rows) * d.ho * d.wo + sp;
+          opos[g] = (long long)row * d.ho * d.wo + sp;
+          bpos[g] = (long long)fdiv(row, d.div_rows) * d.ho * d.wo + sp;
         }
+      }
+      float rowsum[G];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int n = n0 + wn * WTN + j * 32 + l32;
-          if (n < d.N) {
-            const long long oi = opos * d.N + n;
-            const long long bi = bpos * d.N + n;
-            const int nb = d.bias_c ? n % d.bias_c : n;
-            float val = acc[i][j][v];
-            if (EPI == E_IBP && ks_n > 1) {
+      for (int g = 0; g < G; ++g) rowsum[g] = 0.f;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = n0 + wn * WTN + j * 32 + l32;
+        const bool nok = n < d.N;
+        const int nn = nok ? n : 0;
+        const int nb = d.bias_c ? nn % d.bias_c : nn;
+        const float bias = d.bias ? d.bias[nb] : 0.f;
+        long long oi[G], bi[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          oi[g] = opos[g] * d.N + nn;
+          bi[g] = bpos[g] * d.N + nn;
+        }
+        float val[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) val[g] = acc[i][j][v0 + g];
+        if (EPI == E_IBP) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            if (!(mok[g] && nok)) continue;
+            const float rr = accr[NR == 1 ? 0 : i][NC == 1 ? 0 : j][v0 + g];
+            if (ks_n > 1) {
               const long long so = (long long)ks * d.M * d.N;
-              d.out[so + oi] = val;
-              d.out2[so + oi] = accr[NR == 1 ? 0 : i][NC == 1 ? 0 : j][v];
-            } else if (EPI == E_IBP) {
-              const float cc = val + (d.bias ? d.bias[nb] : 0.f);
-              const float rr = accr[NR == 1 ? 0 : i][NC == 1 ? 0 : j][v];
-              const float l = cc - rr, u = cc + rr;
-              d.out[oi] = l;
-              d.out2[oi] = u;
-              if (d.relu_lo) {
-                d.relu_lo[oi] = fmaxf(l, 0.f);
-                d.relu_hi[oi] = fmaxf(u, 0.f);
-              }
+              d.out[so + oi[g]] = val[g];
+              d.out2[so + oi[g]] = rr;
             } else {
-              if (d.addend) val += d.addend[oi];
-              if (EPI == E_STORE) {
-                d.out[oi] = val;
-                if (d.bias) rowsum += val * d.bias[nb];
-              } else if (EPI == E_RELAX) {
-                const float4 cf = d.coef[bi];
-                const float a = (d.alpha && cf.w != 0.f) ? d.alpha[oi] : cf.x;
-                const float s = cf.y, tt = cf.z;
-                const float o = (val >= 0.f) ? val * a : val * s;
-                d.out[oi] = o;
-                if (d.psi_out) d.psi_out[oi] = val;
-                if (d.bias) rowsum += o * d.bias[nb];
-                rowsum += fminf(val, 0.f) * tt;
-              } else if (EPI == E_ADJOINT) {
-                const float4 cf = d.coef[bi];
-                const float g = val + (d.bias ? d.bias[nb] : 0.f);
-                float o;
-                if (cf.w == 0.f) {
-                  o = g * cf.y;  // stable: a = s (0 inactive, 1 active)
-                } else {
-                  const float psi = d.psi_in[oi];
-                  const float s = cf.y, tt = cf.z;
-                  const float a_old = d.alpha_rw[oi];
-                  o = (psi >= 0.f) ? g * a_old : g * s + tt;
-                  if (d.do_update) {
-                    const float grad = g * fmaxf(psi, 0.f);
-                    const float mm = d.beta1 * d.adam_m[oi] + (1.f - d.beta1) * grad;
-                    const float vv = d.beta2 * d.adam_v[oi] + (1.f - d.beta2) * grad * grad;
-                    d.adam_m[oi] = mm;
-                    d.adam_v[oi] = vv;
-                    const float step = d.lr * (mm * d.bc1) / (sqrtf(vv * d.bc2) + d.adam_eps);
-                    d.alpha_rw[oi] = fminf(fmaxf(a_old + step, 0.f), 1.f);
-                  }
-                }
-                d.out[oi] = o;
-              } else {  // E_CONCRETIZE
-                if (d.psi_out) d.psi_out[oi] = val;
-                const float c = d.center[bi];
-                const float r = d.radius ? d.radius[bi] : d.eps;
-                rowsum += val * c - fabsf(val) * r;
+              const float cc = val[g] + bias;
+              const float l = cc - rr, u = cc + rr;
+              d.out[oi[g]] = l;
+              d.out2[oi[g]] = u;
+              if (d.relu_lo) {
+                d.relu_lo[oi[g]] = fmaxf(l, 0.f);
+                d.relu_hi[oi[g]] = fmaxf(u, 0.f);
               }
+            }
+          }
+          continue;
+        }
+        if (d.addend) {
+          float ad[G];
+#pragma unroll
+          for (int g = 0; g < G; ++g) ad[g] = d.addend[oi[g]];
+#pragma unroll
+          for (int g = 0; g < G; ++g) val[g] += ad[g];
+        }
+        if (EPI == E_STORE) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            if (mok[g] && nok) {
+              d.out[oi[g]] = val[g];
+              rowsum[g] += val[g] * bias;
+            }
+          }
+        } else if (EPI == E_RELAX) {
+          float4 cf[G];
+#pragma unroll
+          for (int g = 0; g < G; ++g) cf[g] = d.coef[bi[g]];
+          // slope of the lower relaxation: the optimised alpha on unstable
+          // neurons when one is given, else the adaptive choice
+          float al[G];
+#pragma unroll
+          for (int g = 0; g < G; ++g) al[g] = cf[g].x;
+          if (d.alpha) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+              const float t = d.alpha[oi[g]];
+              al[g] = cf[g].w != 0.f ? t : al[g];
+            }
+          }
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float a = al[g];
+            const float o = (val[g] >= 0.f) ? val[g] * a : val[g] * cf[g].y;
+            if (mok[g] && nok) {
+              d.out[oi[g]] = o;
+              if (d.psi_out) d.psi_out[oi[g]] = val[g];
+              rowsum[g] += o * bias + fminf(val[g], 0.f) * cf[g].z;
+            }
+          }
+        } else if (EPI == E_ADJOINT) {
+          // the accumulator is the adjoint over z: add z's bias
+          float4 cf[G];
+          float psi[G], aold[G], am[G], av[G];
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            cf[g] = d.coef[bi[g]];
+            psi[g] = d.psi_in[oi[g]];
+            aold[g] = d.alpha_rw[oi[g]];
+          }
+          if (d.do_update) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+              am[g] = d.adam_m[oi[g]];
+              av[g] = d.adam_v[oi[g]];
+            }
+          }
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float gz = val[g] + bias;
+            const bool unstable = cf[g].w != 0.f;
+            // stable neurons: a = s (0 inactive, 1 active); unstable: the Psi >= 0 branch takes alpha
+            const float o = !unstable ? gz * cf[g].y : (psi[g] >= 0.f ? gz * aold[g] : gz * cf[g].y + cf[g].z);
+            if (mok[g] && nok) {
+              d.out[oi[g]] = o;
+              if (unstable && d.do_update) {
+                const float grad = gz * fmaxf(psi[g], 0.f);
+                const float mm = d.beta1 * am[g] + (1.f - d.beta1) * grad;
+                const float vv = d.beta2 * av[g] + (1.f - d.beta2) * grad * grad;
+                d.adam_m[oi[g]] = mm;
+                d.adam_v[oi[g]] = vv;
+                const float step = d.lr * (mm * d.bc1) / (sqrtf(vv * d.bc2) + d.adam_eps);
+                d.alpha_rw[oi[g]] = fminf(fmaxf(aold[g] + step, 0.f), 1.f);
+              }
+            }
+          }
+        } else {  // E_CONCRETIZE: centre and radius of the domain box
+          float c[G], r[G];
+#pragma unroll
+          for (int g = 0; g < G; ++g) c[g] = d.center[bi[g]];
+          if (d.radius) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) r[g] = d.radius[bi[g]];
+          } else {
+#pragma unroll
+            for (int g = 0; g < G; ++g) r[g] = d.eps;  // L-infinity ball of one radius
+          }
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            if (mok[g] && nok) {
+              if (d.psi_out) d.psi_out[oi[g]] = val[g];
+              rowsum[g] += val[g] * c[g] - fabsf(val[g]) * r[g];
             }
           }
         }
       }
       if (ROWSUM) {
 #pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) rowsum += __shfl_xor(rowsum, o, 32);
-        if (l32 == 0) red[wn][lr] = rowsum;
+        for (int g = 0; g < G; ++g) {
+          float rs = rowsum[g];
+#pragma unroll
+          for (int o = 16; o >= 1; o >>= 1) rs += __shfl_xor(rs, o, 32);
+          const int v = v0 + g;
+          if (l32 == 0) red[wn][wm * WTM + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3)] = rs;
+        }
       }
     }
   }
