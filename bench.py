@@ -159,6 +159,79 @@ def copy_probe(nbytes):
     print(json.dumps({"copy_probe_bytes": nbytes, "launches": 3}))
 
 
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E (AMD public spec)
+
+
+def _time_calls(fn, reps, warmup=2):
+    """Average ms per call of fn() over reps calls, HIP events on torch's current stream
+    (the stream the library launches on)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        fn()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def hbm_kernels(reps=20):
+    """The memory-bound kernels, timed live: IBP over the wide one-hidden-layer network
+    (weights read once per call), a standalone concretisation of an intermediate-layer
+    Lambda of the MLP workload, and a plain device copy for scale."""
+    import torch
+    import workloads as wk
+    import linear_bound_propagation_amd as lbp
+    out = []
+    dev = "cuda:0"
+    # plain copy of 1 GiB: read + write
+    a = torch.empty(1 << 28, device=dev)
+    b = torch.empty_like(a)
+    ms = _time_calls(lambda: b.copy_(a), reps)
+    copy_gbps = 2 * a.numel() * 4 / (ms * 1e-3) / 1e9
+    del a, b
+    # IBP over the 4096-262144-100 network, batch 8
+    print("[bench] hbm: building the wide network", file=sys.stderr, flush=True)
+    wl = wk.wide()
+    net, x, _ = lbp.prepare(wl, dev)
+    lo, hi = net.alloc_bounds(wl.batch)
+    ws = net.workspace(net.workspace_size(wl.batch, 0, "ibp"))
+    ms = _time_calls(lambda: lbp.ibp(net, x, float(wl.eps), lo=lo, hi=hi, ws=ws), reps)
+    n_w = sum(nd.weight.size + nd.bias.size for nd in wl.nodes if nd.op == "linear")
+    # activations: input read; hidden bounds and their ReLU written (4 arrays) and two read back; outputs
+    hid = wl.nodes[1].size
+    act = wl.batch * (wl.nodes[0].size + 6 * hid + 2 * wl.nodes[-1].size)
+    nbytes = 4 * (n_w + act)
+    out.append({"kernel": "ibp_narrow_kernel (+ split-K finish): vb_ibp over every node", "workload": wl.name,
+                "bound": "hbm", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                "frac_of_copy": round(nbytes / (ms * 1e-3) / 1e9 / copy_gbps, 4),
+                "bytes_per_call": nbytes, "ms_per_call": round(ms, 4)})
+    del net, x, lo, hi, ws, wl
+    torch.cuda.empty_cache()
+    # standalone concretisation: 64 inputs x 2048 rows over a 3072-wide input (1.6 GB of Lambda)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    B, R, n = 64, 2048, 3072
+    A = torch.randn(B * R, n, device=dev, generator=g)
+    center = torch.rand(B, n, device=dev, generator=g)
+    lb = torch.empty(B * R, device=dev)
+    ub = torch.empty_like(lb)
+    ms = _time_calls(lambda: lbp.concretize(A, None, center, 2.0 / 255, R, lb=lb, ub=ub), reps)
+    nbytes = 4 * A.numel() + 8 * B * R
+    out.append({"kernel": "concretize_rows_kernel: vb_concretize", "workload": f"Lambda {B}x{R}x{n} fp32, ball",
+                "bound": "hbm", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                "frac_of_copy": round(nbytes / (ms * 1e-3) / 1e9 / copy_gbps, 4),
+                "bytes_per_call": nbytes, "ms_per_call": round(ms, 4)})
+    return out, round(copy_gbps, 1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +239,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-hbm", action="store_true", help="skip the memory-bound kernel measurements")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -262,6 +336,11 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not args.no_hbm:
+        print("[bench] timing the memory-bound kernels", file=sys.stderr, flush=True)
+        del ws
+        torch.cuda.empty_cache()
+        line["hbm_kernels"], line["copy_GBps"] = hbm_kernels()
     if not args.no_cpu:
         print("[bench] timing the float64 oracle on the host cores", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, fl["all"])

@@ -94,7 +94,10 @@ vb_status vb_workspace_size(const vb_graph* g, int32_t batch, int32_t m, int32_t
  * (node_lo[k] and node_hi[k] non-NULL) except the input node.
  * If C != NULL (C: [batch][m][n_out] over the last node, which must be
  * LINEAR), also writes spec bounds spec_lo/spec_hi [batch][m] with C folded
- * into the last layer. */
+ * into the last layer.  The workspace is optional without C: when it holds
+ * the split-K partial sums (vb_workspace_size with m = 0), layers whose output
+ * grid is small split their reduction over more workgroups; results are the
+ * same up to the order of the fp32 sums. */
 vb_status vb_ibp(const vb_graph* g, int32_t batch,
                  const float* x_center, const float* x_radius, float eps,
                  float* const* node_lo, float* const* node_hi,

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvbprop.so")
 
-SOURCES = ["vb_gemm.hip", "vb_kernels.hip", "vb_api.cpp"]
+SOURCES = ["vb_gemm.hip", "vb_ibp_narrow.hip", "vb_kernels.hip", "vb_api.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -616,7 +616,14 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
         if (epi == E_RELAX)
           HIPCHK(launch_relax_coef(B.lo[z] + chunk_off(z), B.hi[z] + chunk_off(z), (long long)c.cb * G.n[z].size,
                                    B.coef, B.st));
+        // output-parity classes that no tap reaches (a 1x1 stride-2 conv) contribute
+        // nothing: with no bias term their positions keep the pending Lambda, or zero
+        bool zero_first = false;
+        for (const GemmDesc& d : descs)
+          if (d.K == 0 && epi == E_STORE && bias == nullptr && pbuf < 0) zero_first = true;
+        if (zero_first) HIPCHK(launch_fill(B.pool[outb], 0.f, (long long)rows * tn.size, B.st));
         for (GemmDesc& d : descs) {
+          if (d.K == 0 && epi == E_STORE && bias == nullptr && (pbuf < 0 || pbuf == outb)) continue;
           d.B = B.wt[k];
           d.coef = B.coef;
           d.epi = epi;
@@ -947,6 +954,35 @@ vb_status check_stream_ptrs(const void* p, const char* what) {
 // ---------------------------------------------------------------------------
 // IBP
 
+// Split-K factor of the IBP GEMM of an affine node (small grids split K over
+// more workgroups) and the workspace its partial sums take.
+int ibp_gemm_split(const GemmDesc& d) {
+  const long long tiles = (long long)((d.M + 127) / 128) * ((d.N + 127) / 128);
+  const int stages = (d.K + 31) / 32;
+  int S = 1;
+  while (tiles * S * 2 <= 512 && stages / (S * 2) >= 4) S *= 2;
+  return S;
+}
+
+// Workspace that lets every affine node's IBP take its split-K path.
+size_t ibp_workspace(const Graph& G, int batch) {
+  size_t best = 0;
+  for (size_t k = 1; k < G.n.size(); ++k) {
+    const NodeInfo& nd = G.n[k];
+    if (nd.op != VB_LINEAR && nd.op != VB_CONV2D) continue;
+    const NodeInfo& in = G.n[src_of(G, nd.in0)];
+    size_t need;
+    if (nd.op == VB_LINEAR && batch <= 16 && in.size % 4 == 0) {
+      need = 2ull * ibp_narrow_slices(nd.c, (int)in.size) * batch * nd.c * sizeof(float);
+    } else {
+      const GemmDesc d = affine_forward(nd, in, batch);
+      need = 2ull * ibp_gemm_split(d) * d.M * d.N * sizeof(float);
+    }
+    best = std::max(best, need);
+  }
+  return best;
+}
+
 vb_status ibp_impl(const Graph& G, int batch, const float* xc, const float* xr, float eps, float* const* lo,
                    float* const* hi, hipStream_t st, void* ws = nullptr, size_t ws_bytes = 0) {
   const int N = (int)G.n.size();
@@ -960,6 +996,37 @@ vb_status ibp_impl(const Graph& G, int batch, const float* xc, const float* xr, 
     switch (nd.op) {
       case VB_LINEAR:
       case VB_CONV2D: {
+        const float* a1 = ps == 0 ? xc : lo[ps];
+        const float* a2 = ps == 0 ? xr : hi[ps];
+        if (nd.op == VB_LINEAR && ibp_narrow_fits(batch, (int)G.n[ps].size, nd.W, a1, a2)) {
+          // small batch: stream the weights once (batch on the MFMA columns)
+          NarrowIbp q{};
+          q.batch = batch;
+          q.K = (int)G.n[ps].size;
+          q.N = nd.c;
+          q.amode = ps == 0 ? A_IBP_BALL : A_IBP_BOX;
+          q.A = a1;
+          q.A2 = a2;
+          q.eps = eps;
+          q.W = nd.W;
+          q.bias = nd.b;
+          q.lo = lo[k];
+          q.hi = hi[k];
+          if (nd.cons.size() == 1 && G.n[nd.cons[0]].op == VB_RELU && lo[nd.cons[0]] && hi[nd.cons[0]]) {
+            q.relu_lo = lo[nd.cons[0]];
+            q.relu_hi = hi[nd.cons[0]];
+            done[nd.cons[0]] = 1;
+          }
+          int S = ibp_narrow_slices(q.N, q.K);
+          const size_t need = 2ull * S * batch * q.N * sizeof(float);
+          if (S > 1 && (!ws || need > ws_bytes)) S = 1;
+          if (S > 1) {
+            q.pc = (float*)ws;
+            q.pr = q.pc + (size_t)S * batch * q.N;
+          }
+          HIPCHK(launch_ibp_narrow(q, S, st));
+          break;
+        }
         GemmDesc d = affine_forward(nd, G.n[ps], batch);
         d.epi = E_IBP;
         if (ps == 0) {
@@ -981,10 +1048,7 @@ vb_status ibp_impl(const Graph& G, int batch, const float* xc, const float* xr, 
           done[nd.cons[0]] = 1;
         }
         // small grids (a Linear over a small batch): split K over more workgroups
-        const long long tiles = (long long)((d.M + 127) / 128) * ((d.N + 127) / 128);
-        const int stages = (d.K + 31) / 32;
-        int S = 1;
-        while (tiles * S * 2 <= 512 && stages / (S * 2) >= 4) S *= 2;
+        const int S = ibp_gemm_split(d);
         const size_t need = 2ull * S * d.M * d.N * sizeof(float);
         if (S > 1 && ws && need <= ws_bytes) {
           float* pc = (float*)ws;
@@ -1081,7 +1145,7 @@ extern "C" vb_status vb_workspace_size(const vb_graph* g, int32_t batch, int32_t
   if (method < VB_METHOD_IBP || method > VB_METHOD_HYBRID) return fail(VB_EINVAL, "unknown method %d", method);
   if (method == VB_METHOD_HYBRID && (region_start <= 0 || region_start >= G.L))
     return fail(VB_EINVAL, "region_start %d out of range", region_start);
-  *bytes = crown_workspace(G, batch, m, method, region_start);
+  *bytes = std::max(crown_workspace(G, batch, m, method, region_start), ibp_workspace(G, batch));
   std::vector<std::pair<int, int>> chain;
   if (m > 0 && alpha_chain(G, chain)) *bytes = std::max(*bytes, alpha_workspace(G, batch, m));
   return VB_OK;

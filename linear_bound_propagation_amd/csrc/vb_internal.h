@@ -250,4 +250,26 @@ hipError_t launch_ibp_splitk_finish(const float* pc, const float* pr, int S, lon
 // Fill with a constant
 hipError_t launch_fill(float* p, float v, long long n, hipStream_t st);
 
+// IBP through a Linear layer for a batch of at most 16 (vb_ibp_narrow.hip):
+// weights streamed once, batch on the MFMA column dimension.
+struct NarrowIbp {
+  int batch, K, N;          // inputs, n_in, n_out
+  int amode;                // A_IBP_BALL (A = centre, A2 = radius or NULL -> eps) or A_IBP_BOX (A = lo, A2 = hi)
+  const float* A;
+  const float* A2;
+  float eps;
+  const float* W;           // [N][K]
+  const float* bias;        // [N] or NULL
+  float* lo;                // [batch][N]
+  float* hi;
+  float* relu_lo;           // optional ReLU of the bounds
+  float* relu_hi;
+  float* pc;                // split-K partial sums [slices][batch][N] (centre, radius)
+  float* pr;
+  int kchunk;               // set by the launcher
+};
+bool ibp_narrow_fits(int batch, int K, const float* W, const float* A, const float* A2);
+int ibp_narrow_slices(int N, int K);
+hipError_t launch_ibp_narrow(NarrowIbp d, int S, hipStream_t st);
+
 }  // namespace vb

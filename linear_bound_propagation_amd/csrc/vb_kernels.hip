@@ -408,7 +408,10 @@ hipError_t launch_gap_expand(const float* src, int rows, int P, int C, float sca
   return hipGetLastError();
 }
 
-// one block per row: rowacc[r] (+)= sum A c - |A| r  (+ bias), optional lb/ub
+// one block per row: rowacc[r] (+)= sum A c - |A| r  (+ bias), optional lb/ub.
+// VEC: n % 4 == 0 and 16-byte aligned rows; each thread issues the float4 loads
+// of up to four strides before accumulating, so a row's whole read is in flight.
+template <bool VEC>
 __global__ __launch_bounds__(256) void concretize_rows_kernel(const float* __restrict__ A, int n, int rows_per_b,
                                                               const float* __restrict__ center,
                                                               const float* __restrict__ radius, float eps,
@@ -420,19 +423,50 @@ __global__ __launch_bounds__(256) void concretize_rows_kernel(const float* __res
   const int row = blockIdx.x;
   const long long b = row / rows_per_b;
   float sc = 0.f, sr = 0.f;
-  for (int j = threadIdx.x; j < n; j += 256) {
-    const float a = A[(long long)row * n + j];
-    float c, r;
-    if (center) {
-      c = center[b * n + j];
-      r = radius ? radius[b * n + j] : eps;
-    } else {
-      const float l = lo[b * n + j], u = hi[b * n + j];
-      c = (l + u) * 0.5f;
-      r = (u - l) * 0.5f;
+  if (VEC) {
+    const int n4 = n >> 2;
+    const float4* a4 = reinterpret_cast<const float4*>(A + (long long)row * n);
+    const long long bo = b * n4;
+    for (int j0 = threadIdx.x; j0 < n4; j0 += 4 * 256) {
+      float4 a[4], c[4], r[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + 256 * u;
+        const bool ok = j < n4;
+        const int jj = ok ? j : j0;
+        a[u] = a4[jj];
+        if (center) {
+          c[u] = reinterpret_cast<const float4*>(center)[bo + jj];
+          r[u] = radius ? reinterpret_cast<const float4*>(radius)[bo + jj] : make_float4(eps, eps, eps, eps);
+        } else {
+          const float4 l = reinterpret_cast<const float4*>(lo)[bo + jj];
+          const float4 h = reinterpret_cast<const float4*>(hi)[bo + jj];
+          c[u] = make_float4((l.x + h.x) * 0.5f, (l.y + h.y) * 0.5f, (l.z + h.z) * 0.5f, (l.w + h.w) * 0.5f);
+          r[u] = make_float4((h.x - l.x) * 0.5f, (h.y - l.y) * 0.5f, (h.z - l.z) * 0.5f, (h.w - l.w) * 0.5f);
+        }
+        if (!ok) a[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sc += a[u].x * c[u].x + a[u].y * c[u].y + a[u].z * c[u].z + a[u].w * c[u].w;
+        sr += fabsf(a[u].x) * r[u].x + fabsf(a[u].y) * r[u].y + fabsf(a[u].z) * r[u].z + fabsf(a[u].w) * r[u].w;
+      }
     }
-    sc += a * c;
-    sr += fabsf(a) * r;
+  } else {
+    for (int j = threadIdx.x; j < n; j += 256) {
+      const float a = A[(long long)row * n + j];
+      float c, r;
+      if (center) {
+        c = center[b * n + j];
+        r = radius ? radius[b * n + j] : eps;
+      } else {
+        const float l = lo[b * n + j], u = hi[b * n + j];
+        c = (l + u) * 0.5f;
+        r = (u - l) * 0.5f;
+      }
+      sc += a * c;
+      sr += fabsf(a) * r;
+    }
   }
   sc = block_sum(sc, sh);
   sr = block_sum(sr, sh);
@@ -448,8 +482,14 @@ hipError_t launch_concretize_rows(const float* A, int rows, int n, int rows_per_
                                   const float* radius, float eps, const float* lo, const float* hi,
                                   const float* bias, float* lb, float* ub, float* rowacc, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(concretize_rows_kernel, dim3(rows), dim3(256), 0, st, A, n, rows_per_b, center, radius, eps,
-                     lo, hi, bias, lb, ub, rowacc);
+  auto al = [](const float* p) { return ((uintptr_t)p & 15) == 0; };
+  const bool vec = n % 4 == 0 && al(A) && al(center) && al(radius) && al(lo) && al(hi);
+  if (vec)
+    hipLaunchKernelGGL(concretize_rows_kernel<true>, dim3(rows), dim3(256), 0, st, A, n, rows_per_b, center, radius,
+                       eps, lo, hi, bias, lb, ub, rowacc);
+  else
+    hipLaunchKernelGGL(concretize_rows_kernel<false>, dim3(rows), dim3(256), 0, st, A, n, rows_per_b, center, radius,
+                       eps, lo, hi, bias, lb, ub, rowacc);
   return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ import numpy as np
 
 __all__ = [
     "Node", "Workload", "NetBuilder", "forward", "margin_specs",
-    "mlp", "cnn", "resnet", "config", "CONFIG_NAMES", "tiny_mlp",
+    "mlp", "cnn", "resnet", "wide", "WIDE_NAME", "config", "CONFIG_NAMES", "tiny_mlp",
 ]
 
 
@@ -90,9 +90,10 @@ class Workload:
 class NetBuilder:
     """Appends nodes in topological order, drawing parameters from one generator."""
 
-    def __init__(self, rng: np.random.Generator, init: str):
+    def __init__(self, rng: np.random.Generator, init: str, draw32: bool = False):
         self.rng = rng
         self.init = init          # "lecun": N(0, 1/fan_in); "he": N(0, 2/fan_in)
+        self.draw32 = draw32      # draw directly in float32 (same distributions; for > 1e9 weights)
         self.nodes: List[Node] = []
 
     def _add(self, node: Node) -> int:
@@ -101,6 +102,11 @@ class NetBuilder:
 
     def _w(self, shape, fan_in, zero=False):
         var = (1.0 if self.init == "lecun" else 2.0) / fan_in
+        if self.draw32:
+            w = self.rng.standard_normal(shape, dtype=np.float32)
+            w *= np.float32(np.sqrt(var))
+            b = self.rng.standard_normal(shape[0], dtype=np.float32) * np.float32(0.1)
+            return w, b
         w = self.rng.standard_normal(shape) * np.sqrt(var)
         b = self.rng.standard_normal(shape[0]) * 0.1
         if zero:
@@ -213,6 +219,27 @@ def mlp(widths, batch, eps, cfg, intermediate="crown", name=None, init="lecun") 
     labels, C = margin_specs(nb.nodes, x0)
     return Workload(name or "mlp_" + "-".join(map(str, widths)), cfg, nb.nodes, x0, np.float32(eps),
                     labels, C, intermediate, seeds={"weights": [cfg, 0], "inputs": [cfg, 1]})
+
+
+WIDE_NAME = "wide_4096-262144-100_b8_ibp"
+
+
+def wide(batch=8, eps=2.0 / 255, n_in=4096, width=262144, n_out=100, cfg=6, name=None) -> Workload:
+    """One hidden ReLU layer n_in-width-n_out, the shape of the page's widest networks
+    (Sec. 1: a 262 144-wide layer whose weights exceed 4 GB in fp32).  Interval bounds
+    over it are limited by reading the weights once: the memory-bound IBP case.
+    Same recipe as `mlp` (N(0, 1/fan_in) weights, N(0, 0.01) biases, U[0,1] inputs),
+    drawn directly in float32 so the 1.07e9 weights take seconds."""
+    rng_w = np.random.default_rng([cfg, 0])
+    rng_x = np.random.default_rng([cfg, 1])
+    nb = NetBuilder(rng_w, "lecun", draw32=True)
+    x = nb.input((n_in,))
+    x = nb.relu(nb.linear(x, width))
+    nb.linear(x, n_out)
+    x0 = rng_x.random((batch, n_in)).astype(np.float32)
+    labels, C = margin_specs(nb.nodes, x0)
+    return Workload(name or f"wide_{n_in}-{width}-{n_out}_b{batch}_ibp", cfg, nb.nodes, x0, np.float32(eps),
+                    labels, C, "ibp", seeds={"weights": [cfg, 0], "inputs": [cfg, 1]})
 
 
 def cnn(batch, eps, cfg, convs=((64, 1), (64, 2), (128, 1), (128, 2)), fcs=(512, 100),
