@@ -43,6 +43,22 @@ __device__ __forceinline__ int fdiv(int x, const FastDiv& f) {
   return f.d == 1 ? x : (int)(__umulhi((unsigned)x, f.mul) >> f.shr);
 }
 
+// Gather GEMM: tile index m -> (row, pixel q); rows past the last are padding.
+struct GPos {
+  int row, q;
+  bool valid;
+};
+__device__ __forceinline__ GPos gdecode(const GemmDesc& d, int m) {
+  const int t = m >> d.rb_shift;
+  const int rb = fdiv(t, d.div_p);
+  GPos g;
+  g.q = t - rb * d.div_p.d;
+  g.row = (rb << d.rb_shift) + (m & ((1 << d.rb_shift) - 1));
+  g.valid = m < d.Mt && g.row < d.div_nrows.d;
+  if (!g.valid) g.row = g.q = 0;
+  return g;
+}
+
 struct Pos {
   long long a_base;
   int Y, X;
@@ -52,17 +68,17 @@ struct Pos {
 template <bool DENSE>
 __device__ __forceinline__ Pos pos_of(const GemmDesc& d, int m) {
   Pos p;
-  p.valid = m < d.M;
-  const int mm = p.valid ? m : 0;
   if (DENSE) {
+    p.valid = m < d.M;
+    const int mm = p.valid ? m : 0;
     p.a_base = (long long)mm * d.a_row_stride;
     p.Y = p.X = 0;
   } else {
-    const int q = fdiv(mm, d.div_nrows);  // position-major
-    const int row = mm - q * d.div_nrows.d;
-    p.Y = fdiv(q, d.div_gw);
-    p.X = q - p.Y * d.gw;
-    p.a_base = (long long)row * d.a_row_stride;
+    const GPos g = gdecode(d, m);
+    p.valid = g.valid;
+    p.Y = fdiv(g.q, d.div_gw);
+    p.X = g.q - p.Y * d.gw;
+    p.a_base = (long long)g.row * d.a_row_stride;
   }
   return p;
 }
@@ -182,7 +198,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   // XCD-aware tile order: workgroups go round-robin over the 8 XCDs, so each
   // XCD gets a contiguous run of tiles with the N-tiles of one M-tile next to
   // each other; an M-tile's A rows are then fetched into one XCD's L2 once.
-  const int mt = (d.M + BM - 1) / BM;
+  const int mt = (d.Mt + BM - 1) / BM;
   const int nt = (d.N + BN - 1) / BN;
   const int ks_n = (EPI == E_IBP && d.ksplit > 1) ? d.ksplit : 1;
   const int total = mt * nt * ks_n;
@@ -388,19 +404,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
       for (int g = 0; g < G; ++g) {
         const int v = v0 + g;
         const int m = m0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-        mok[g] = m < d.M;
-        const int mm = mok[g] ? m : 0;
         if (DENSE) {
+          mok[g] = m < d.M;
+          const int mm = mok[g] ? m : 0;
           opos[g] = mm;
           bpos[g] = fdiv(mm, d.div_rows);
         } else {
-          const int q = fdiv(mm, d.div_nrows);  // position-major
-          const int row = mm - q * d.div_nrows.d;
-          const int Y = fdiv(q, d.div_gw);
-          const int X = q - Y * d.gw;
+          const GPos gp = gdecode(d, m);
+          mok[g] = gp.valid;
+          const int Y = fdiv(gp.q, d.div_gw);
+          const int X = gp.q - Y * d.gw;
           const long long sp = (long long)(Y * d.oym + d.oy0) * d.wo + (X * d.oxm + d.ox0);
-          opos[g] = (long long)row * d.ho * d.wo + sp;
-          bpos[g] = (long long)fdiv(row, d.div_rows) * d.ho * d.wo + sp;
+          opos[g] = (long long)gp.row * d.ho * d.wo + sp;
+          bpos[g] = (long long)fdiv(gp.row, d.div_rows) * d.ho * d.wo + sp;
         }
       }
       float rowsum[G];
@@ -558,11 +574,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
     if (d.part) {
       for (int r = tid; r < BM; r += NTHR) {
         const int m = m0 + r;
-        if (m < d.M) {
+        long long pm = m;
+        bool ok = m < d.M;
+        if (!DENSE) {
+          const GPos gp = gdecode(d, m);
+          ok = gp.valid;
+          pm = (long long)gp.q * d.div_nrows.d + gp.row;  // position-major partial row
+        }
+        if (ok) {
           float s = 0.f;
 #pragma unroll
           for (int w = 0; w < WN; ++w) s += red[w][r];
-          d.part[(long long)m * d.part_ld + tn] = s;
+          d.part[pm * d.part_ld + tn] = s;
         }
       }
     }
@@ -573,7 +596,7 @@ namespace {
 
 template <int BM, int BN, int WM, int WN, bool DENSE, bool FAST>
 hipError_t launch_tile(const GemmDesc& d, hipStream_t st) {
-  const int mt = (d.M + BM - 1) / BM;
+  const int mt = (d.Mt + BM - 1) / BM;
   const int nt = (d.N + BN - 1) / BN;
   const int ks = (d.epi == E_IBP && d.ksplit > 1) ? d.ksplit : 1;
   const dim3 g(((mt * nt * ks + 7) / 8) * 8), b(WM * WN * 64);
@@ -612,7 +635,7 @@ hipError_t launch_shape(const GemmDesc& d, bool dense, bool fast, hipStream_t st
 // GEMMs with the fast path, when the grid still has at least two workgroups per CU.
 bool use_big(const GemmDesc& d, bool fast) {
   if (!fast || d.epi == E_IBP || d.N < 256) return false;
-  const long long tiles = (long long)((d.M + 255) / 256) * ((d.N + 255) / 256);
+  const long long tiles = (long long)((d.Mt + 255) / 256) * ((d.N + 255) / 256);
   return tiles >= 512;
 }
 
@@ -635,7 +658,33 @@ bool is_fast(const GemmDesc& d) {
 }
 }  // namespace
 
-int gemm_ntiles(const GemmDesc& d) {
+namespace {
+// Launch-time fields of a descriptor: division constants and the tile index space.
+bool finalize(GemmDesc& d) {
+  d.div_p = make_fastdiv(d.gh * d.gw);
+  d.div_gw = make_fastdiv(d.gw);
+  d.div_rows = make_fastdiv(d.rows_per_b);
+  d.div_nrows = make_fastdiv(d.M / (d.gh * d.gw));
+  d.Mt = d.M;
+  d.rb_shift = 0;
+  if (!gemm_is_dense(d)) {
+    // blocks of up to 64 rows, fewer where padding the rows to a whole block
+    // would waste more than an eighth of the tiles
+    const long long rows = d.M / (d.gh * d.gw), P = (long long)d.gh * d.gw;
+    int sh = 6;
+    while (sh > 0 && (((rows + (1LL << sh) - 1) >> sh << sh) - rows) * 8 > rows) --sh;
+    const long long mt = ((rows + (1LL << sh) - 1) >> sh << sh) * P;
+    if (mt > INT32_MAX - 256) return false;
+    d.rb_shift = sh;
+    d.Mt = (int)mt;
+  }
+  return true;
+}
+}  // namespace
+
+int gemm_ntiles(const GemmDesc& desc) {
+  GemmDesc d = desc;
+  finalize(d);  // the N-tile width can depend on the tile count
   const int bn = tile_n(d, is_fast(d));
   return (d.N + bn - 1) / bn;
 }
@@ -643,16 +692,13 @@ int gemm_ntiles(const GemmDesc& d) {
 hipError_t launch_gemm(const GemmDesc& desc, hipStream_t st) {
   if (desc.M <= 0 || desc.N <= 0) return hipSuccess;
   GemmDesc d = desc;
-  d.div_p = make_fastdiv(d.gh * d.gw);
-  d.div_gw = make_fastdiv(d.gw);
-  d.div_rows = make_fastdiv(d.rows_per_b);
-  d.div_nrows = make_fastdiv(d.M / (d.gh * d.gw));
+  if (!finalize(d)) return hipErrorInvalidValue;
   const bool dense = gemm_is_dense(d);
   const bool fast = is_fast(d);
   const int bn = tile_n(d, fast);
   if (bn == 256) {
     // plain epilogues only (checked in use_big); IBP never takes this tile
-    const int mt = (d.M + 255) / 256, nt = (d.N + 255) / 256;
+    const int mt = (d.Mt + 255) / 256, nt = (d.N + 255) / 256;
     const dim3 g(((mt * nt + 7) / 8) * 8), b(512);
     if (dense) {
       switch (d.epi) {

@@ -53,8 +53,12 @@ struct GemmDesc {
   int M, N, K;                 // output positions x output channels x reduction length
   int amode;                   // AMode of the A operand (E_IBP: A_IBP_BOX or A_IBP_BALL)
   // ---- A operand: position m -> (row, Y, X) on a gh x gw grid per row; for a
-  //      gather (conv) GEMM m is position-major, m = (Y*gw + X)*rows + row, so
-  //      a tile holds many rows of one pixel and their relaxation data is shared;
+  //      gather (conv) GEMM, M = rows * gh * gw and the tiles walk a padded
+  //      index space of blocks of 2^rb_shift rows: m = (rb*gh*gw + Y*gw + X) *
+  //      2^rb_shift + (row mod 2^rb_shift), rb = row >> rb_shift.  A tile thus
+  //      holds a few rows at a few neighbouring pixels (their relaxation data is
+  //      shared), and consecutive tiles sweep one block of rows over all pixels,
+  //      so the neighbouring pixels that the taps read are still in L2;
   //      reduction index k -> (tap j, channel c) with k = j*cs + c;
   //      element = A[row*a_row_stride + ((Y*sy + dy_j)*ws + (X*sx + dx_j))*cs + c],
   //      zero outside [0,hs) x [0,ws).  Dense GEMM: gh=gw=hs=ws=1, cs=K, 1 tap.
@@ -72,6 +76,8 @@ struct GemmDesc {
   int ho, wo, oym, oy0, oxm, ox0;
   int rows_per_b;              // batch element of a row = row / rows_per_b
   FastDiv div_p, div_gw, div_rows, div_nrows;  // filled by launch_gemm: gh*gw, gw, rows_per_b, M/(gh*gw)
+  int Mt;                      // filled by launch_gemm: size of the tile index space (gather: padded)
+  int rb_shift;                // filled by launch_gemm: log2 of the rows per block (gather)
   // ---- epilogue
   int epi;
   float* out;                  // [opos][N]   (E_IBP: lo)
@@ -89,7 +95,8 @@ struct GemmDesc {
   float* psi_out;              // E_RELAX: store the pre-relaxation value v, or NULL
   const float* center;         // E_CONCRETIZE: centre/radius of the domain box at [b-pos][N]
   const float* radius;         // NULL -> eps
-  float* part;                 // row partials [M][part_ld] (column = N-tile index)
+  float* part;                 // row partials [M][part_ld] (column = N-tile index; gather:
+                               // row index (Y*gw + X)*rows + row)
   int part_ld;
   int ksplit;                  // E_IBP only: > 1 splits K into slices; slice s writes its raw
                                // products to out/out2 + s*M*N (reduced by launch_ibp_splitk_finish)
