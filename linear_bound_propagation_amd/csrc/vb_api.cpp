@@ -1459,10 +1459,30 @@ extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float
     const int k = kr.first, r = kr.second;
     if (r < 0) break;  // the last affine node: its adjoint is not needed
     const NodeInfo& nd = G.n[k];
-    GemmDesc d = affine_forward(nd, G.n[src_of(G, nd.in0)], (int)rows);
+    const NodeInfo& in = G.n[src_of(G, nd.in0)];
+    GemmDesc d = affine_forward(nd, in, (int)rows);
+    d.A = gbuf[cur];
+    const int Kp = (nd.kh * nd.kw * in.c + 31) / 32 * 32;
+    if (nd.op == VB_CONV2D && in.c % 32 != 0 && (size_t)rows * nd.h * nd.w * Kp <= B.pool_floats &&
+        (size_t)nd.c * Kp <= B.pool_floats) {
+      // few input channels: im2col of the adjoint, then a 1x1 conv over that image
+      // with K padded to whole 32-deep stages (the GEMM's fast path)
+      HIPCHK(launch_im2col(gbuf[cur], (int)rows, in.h, in.w, in.c, nd.kh, nd.kw, nd.stride, nd.pad, nd.h, nd.w, Kp,
+                           B.pool[2], st));
+      HIPCHK(launch_pad_weights(nd.W, nd.kh * nd.kw, nd.c, in.c, Kp, B.pool[3], st));
+      NodeInfo n1 = nd, i1 = in;
+      n1.kh = n1.kw = n1.stride = 1;
+      n1.pad = 0;
+      i1.c = Kp;
+      i1.h = nd.h;
+      i1.w = nd.w;
+      i1.size = (long long)nd.h * nd.w * Kp;
+      d = affine_forward(n1, i1, (int)rows);
+      d.A = B.pool[2];
+      d.B = B.pool[3];
+    }
     d.epi = E_ADJOINT;
     d.amode = A_PLAIN;
-    d.A = gbuf[cur];
     d.out = gbuf[cur ^ 1];
     d.bias = nd.b;
     d.bias_c = 0;
@@ -1481,7 +1501,38 @@ extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float
     d.bc1 = (float)bc1;
     d.bc2 = (float)bc2;
     d.adam_eps = adam_eps;
-    HIPCHK(launch_gemm(d, st));
+    const int S = gemm_is_dense(d) ? ibp_gemm_split(d) : 1;
+    if (S > 1 && (size_t)S * d.M * d.N <= B.pool_floats) {
+      // few output tiles (a Linear over batch x specs rows): split K, then
+      // apply the adjoint epilogue to the summed slices
+      GemmDesc e = d;
+      e.ksplit = S;
+      e.out = B.pool[2];
+      HIPCHK(launch_gemm(e, st));
+      AdjFinish a{};
+      a.part = B.pool[2];
+      a.S = S;
+      a.M = d.M;
+      a.N = d.N;
+      a.rows_per_b = d.rows_per_b;
+      a.bias = d.bias;
+      a.coef = d.coef;
+      a.psi_in = d.psi_in;
+      a.alpha_rw = d.alpha_rw;
+      a.adam_m = d.adam_m;
+      a.adam_v = d.adam_v;
+      a.do_update = d.do_update;
+      a.lr = d.lr;
+      a.beta1 = d.beta1;
+      a.beta2 = d.beta2;
+      a.bc1 = d.bc1;
+      a.bc2 = d.bc2;
+      a.adam_eps = d.adam_eps;
+      a.out = d.out;
+      HIPCHK(launch_adjoint_finish(a, st));
+    } else {
+      HIPCHK(launch_gemm(d, st));
+    }
     cur ^= 1;
   }
   return VB_OK;

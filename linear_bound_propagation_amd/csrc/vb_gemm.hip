@@ -200,7 +200,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   // each other; an M-tile's A rows are then fetched into one XCD's L2 once.
   const int mt = (d.Mt + BM - 1) / BM;
   const int nt = (d.N + BN - 1) / BN;
-  const int ks_n = (EPI == E_IBP && d.ksplit > 1) ? d.ksplit : 1;
+  const int ks_n = ((EPI == E_IBP || EPI == E_ADJOINT) && d.ksplit > 1) ? d.ksplit : 1;
   const int total = mt * nt * ks_n;
   const int per_xcd = (total + 7) / 8;
   const int tile0 = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
@@ -460,6 +460,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
           }
           continue;
         }
+        if (EPI == E_ADJOINT && ks_n > 1) {
+          // split K: raw products of this slice (summed by launch_adjoint_finish)
+          const long long so = (long long)ks * d.M * d.N;
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+            if (mok[g] && nok) d.out[so + oi[g]] = val[g];
+          continue;
+        }
         if (d.addend) {
           float ad[G];
 #pragma unroll
@@ -598,7 +606,7 @@ template <int BM, int BN, int WM, int WN, bool DENSE, bool FAST>
 hipError_t launch_tile(const GemmDesc& d, hipStream_t st) {
   const int mt = (d.Mt + BM - 1) / BM;
   const int nt = (d.N + BN - 1) / BN;
-  const int ks = (d.epi == E_IBP && d.ksplit > 1) ? d.ksplit : 1;
+  const int ks = ((d.epi == E_IBP || d.epi == E_ADJOINT) && d.ksplit > 1) ? d.ksplit : 1;
   const dim3 g(((mt * nt * ks + 7) / 8) * 8), b(WM * WN * 64);
   switch (d.epi) {
     case E_STORE:

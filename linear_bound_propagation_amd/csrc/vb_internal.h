@@ -98,8 +98,9 @@ struct GemmDesc {
   float* part;                 // row partials [M][part_ld] (column = N-tile index; gather:
                                // row index (Y*gw + X)*rows + row)
   int part_ld;
-  int ksplit;                  // E_IBP only: > 1 splits K into slices; slice s writes its raw
-                               // products to out/out2 + s*M*N (reduced by launch_ibp_splitk_finish)
+  int ksplit;                  // E_IBP / E_ADJOINT: > 1 splits K into slices; slice s writes its raw
+                               // products to out (and out2) + s*M*N, reduced by
+                               // launch_ibp_splitk_finish / launch_adjoint_finish
   // ---- E_ADJOINT (alpha-CROWN step): per [opos][N] of the ReLU after this node
   const float* psi_in;         // pre-relaxation product kept by the evaluation
   float* alpha_rw;             // lower slopes, updated in place
@@ -256,6 +257,30 @@ hipError_t launch_ibp_splitk_finish(const float* pc, const float* pr, int S, lon
 
 // Fill with a constant
 hipError_t launch_fill(float* p, float v, long long n, hipStream_t st);
+
+// E_ADJOINT epilogue of a dense GEMM whose K was split: sums the S slices of
+// part [S][M][N] and applies the ReLU adjoint and the Adam step (vb_kernels.hip).
+struct AdjFinish {
+  const float* part;
+  int S, M, N, rows_per_b;
+  const float* bias;
+  const float4* coef;
+  const float* psi_in;
+  float* alpha_rw;
+  float* adam_m;
+  float* adam_v;
+  int do_update;
+  float lr, beta1, beta2, bc1, bc2, adam_eps;
+  float* out;
+};
+hipError_t launch_adjoint_finish(const AdjFinish& a, hipStream_t st);
+
+// im2col of a [rows][H][W][C] tensor for a kh x kw conv (stride, pad) into
+// [rows][Ho][Wo][Kp] with k = tap*C + c and zeros for k >= kh*kw*C; and the
+// matching weights [tap][N][C] -> [N][Kp] (vb_kernels.hip).
+hipError_t launch_im2col(const float* src, int rows, int H, int W, int C, int kh, int kw, int stride, int pad,
+                         int Ho, int Wo, int Kp, float* dst, hipStream_t st);
+hipError_t launch_pad_weights(const float* W, int taps, int N, int C, int Kp, float* dst, hipStream_t st);
 
 // IBP through a Linear layer for a batch of at most 16 (vb_ibp_narrow.hip):
 // weights streamed once, batch on the MFMA column dimension.

@@ -606,6 +606,91 @@ hipError_t launch_ibp_splitk_finish(const float* pc, const float* pr, int S, lon
   return hipGetLastError();
 }
 
+__global__ void adjoint_finish_kernel(AdjFinish a) {
+  const long long MN = (long long)a.M * a.N;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < MN; e += (long long)gridDim.x * blockDim.x) {
+    float g = 0.f;
+    for (int q = 0; q < a.S; ++q) g += a.part[q * MN + e];
+    const long long m = e / a.N;
+    const int n = (int)(e - m * a.N);
+    const float gz = g + (a.bias ? a.bias[n] : 0.f);
+    const float4 cf = a.coef[(m / a.rows_per_b) * a.N + n];
+    const float psi = a.psi_in[e];
+    const float aold = a.alpha_rw[e];
+    const bool unstable = cf.w != 0.f;
+    a.out[e] = !unstable ? gz * cf.y : (psi >= 0.f ? gz * aold : gz * cf.y + cf.z);
+    if (unstable && a.do_update) {
+      const float grad = gz * fmaxf(psi, 0.f);
+      const float mm = a.beta1 * a.adam_m[e] + (1.f - a.beta1) * grad;
+      const float vv = a.beta2 * a.adam_v[e] + (1.f - a.beta2) * grad * grad;
+      a.adam_m[e] = mm;
+      a.adam_v[e] = vv;
+      const float step = a.lr * (mm * a.bc1) / (sqrtf(vv * a.bc2) + a.adam_eps);
+      a.alpha_rw[e] = fminf(fmaxf(aold + step, 0.f), 1.f);
+    }
+  }
+}
+
+hipError_t launch_adjoint_finish(const AdjFinish& a, hipStream_t st) {
+  const long long MN = (long long)a.M * a.N;
+  if (MN <= 0) return hipSuccess;
+  long long blocks = (MN + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(adjoint_finish_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// one thread per output element of the im2col image (coalesced writes)
+__global__ void im2col_kernel(const float* __restrict__ src, int rows, int H, int W, int C, int kh, int kw,
+                              int stride, int pad, int Ho, int Wo, int Kp, float* __restrict__ dst) {
+  const long long total = (long long)rows * Ho * Wo * Kp;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (long long)gridDim.x * blockDim.x) {
+    const int k = (int)(e % Kp);
+    const long long p = e / Kp;  // (row, oy, ox)
+    const int ox = (int)(p % Wo);
+    const long long t = p / Wo;
+    const int oy = (int)(t % Ho);
+    const long long row = t / Ho;
+    float v = 0.f;
+    if (k < kh * kw * C) {
+      const int tap = k / C, c = k - tap * C;
+      const int y = oy * stride - pad + tap / kw, x = ox * stride - pad + tap % kw;
+      if (y >= 0 && y < H && x >= 0 && x < W) v = src[((row * H + y) * W + x) * C + c];
+    }
+    dst[e] = v;
+  }
+}
+
+hipError_t launch_im2col(const float* src, int rows, int H, int W, int C, int kh, int kw, int stride, int pad,
+                         int Ho, int Wo, int Kp, float* dst, hipStream_t st) {
+  const long long total = (long long)rows * Ho * Wo * Kp;
+  if (total <= 0) return hipSuccess;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(im2col_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, rows, H, W, C, kh, kw, stride,
+                     pad, Ho, Wo, Kp, dst);
+  return hipGetLastError();
+}
+
+__global__ void pad_weights_kernel(const float* __restrict__ Wt, int taps, int N, int C, int Kp,
+                                   float* __restrict__ dst) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= N * Kp) return;
+  const int n = e / Kp, k = e - n * Kp;
+  float v = 0.f;
+  if (k < taps * C) {
+    const int tap = k / C, c = k - tap * C;
+    v = Wt[((long long)tap * N + n) * C + c];
+  }
+  dst[e] = v;
+}
+
+hipError_t launch_pad_weights(const float* W, int taps, int N, int C, int Kp, float* dst, hipStream_t st) {
+  if (N * Kp <= 0) return hipSuccess;
+  hipLaunchKernelGGL(pad_weights_kernel, dim3((N * Kp + 255) / 256), dim3(256), 0, st, W, taps, N, C, Kp, dst);
+  return hipGetLastError();
+}
+
 __global__ void fill_kernel(float* p, float v, long long n) {
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
     p[i] = v;
