@@ -1292,8 +1292,8 @@ extern "C" vb_status vb_crown(const vb_graph* g, int32_t batch, const float* x_c
 
 extern "C" vb_status vb_profile_start(void) {
   for (auto& r : g_prof) {
-    hipEventDestroy(r.a);
-    hipEventDestroy(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
   }
   g_prof.clear();
   g_prof_on = true;
@@ -1314,8 +1314,8 @@ extern "C" vb_status vb_profile_stop(double* ms, double* flops, int64_t* launche
   if (flops) *flops = f;
   if (launches) *launches = (int64_t)g_prof.size();
   for (auto& r : g_prof) {
-    hipEventDestroy(r.a);
-    hipEventDestroy(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
   }
   g_prof.clear();
   return VB_OK;
