@@ -639,10 +639,11 @@ hipError_t launch_shape(const GemmDesc& d, bool dense, bool fast, hipStream_t st
   return fast ? launch_tile<BM, BN, WM, WN, false, true>(d, st) : launch_tile<BM, BN, WM, WN, false, false>(d, st);
 }
 
-// 256 x 256 tiles on 8 wavefronts (128 x 64 each) for the large back-substitution
-// GEMMs with the fast path, when the grid still has at least two workgroups per CU.
+// 256 x 256 tiles on 8 wavefronts (128 x 64 each) for the large convolution
+// GEMMs with the fast path, when the grid still has at least two workgroups per CU
+// (dense GEMMs ran faster on two 128 x 128 workgroups per CU).
 bool use_big(const GemmDesc& d, bool fast) {
-  if (!fast || d.epi == E_IBP || d.N < 256) return false;
+  if (!fast || d.epi == E_IBP || d.N < 256 || gemm_is_dense(d)) return false;
   const long long tiles = (long long)((d.Mt + 255) / 256) * ((d.N + 255) / 256);
   return tiles >= 512;
 }
@@ -723,8 +724,8 @@ hipError_t launch_gemm(const GemmDesc& desc, hipStream_t st) {
     }
     return hipGetLastError();
   }
-  if (bn == 128) return launch_shape<128, 128, 2, 2>(d, dense, fast, st);
-  if (bn == 64) return launch_shape<128, 64, 2, 2>(d, dense, fast, st);
+  if (bn == 128) return launch_shape<128, 128, 4, 2>(d, dense, fast, st);
+  if (bn == 64) return launch_shape<128, 64, 4, 2>(d, dense, fast, st);
   return launch_shape<128, 32, 4, 1>(d, dense, fast, st);
 }
 
