@@ -900,8 +900,21 @@ vb_status backward_all(Backward& B, int start, int stop, const float* C, int m, 
   bwd_requirements(B.G, start, stop, R, maxw, ppb);
   if (C) maxw = std::max(maxw, B.G.n[start].size);
   const long long box = stop > 0 ? B.G.n[stop].size : 0;
+  // GEMM index spaces are 32-bit: rows x pixels (padded to whole row blocks) per launch
+  long long maxp = 1;
+  for (size_t k = 1; k < B.G.n.size(); ++k) {
+    const NodeInfo& nd = B.G.n[k];
+    if (nd.op != VB_CONV2D || (int)k > start || (int)k <= stop) continue;
+    const NodeInfo& in = B.G.n[src_of(B.G, nd.in0)];
+    maxp = std::max(maxp, std::max((long long)in.h * in.w, (long long)nd.h * nd.w));
+  }
+  auto fits_index = [&](long long cbn) { return cbn * R * maxp + 64 * maxp + 256 <= (long long)INT32_MAX; };
   int cb = batch;
-  while (cb > 1 && layout_for(maxw, ppb, R, cb, reserved_floats, box).bytes > ws_bytes) cb = (cb + 1) / 2;
+  while (cb > 1 && (!fits_index(cb) || layout_for(maxw, ppb, R, cb, reserved_floats, box).bytes > ws_bytes))
+    cb = (cb + 1) / 2;
+  if (!fits_index(cb))
+    return fail(VB_EUNSUPPORTED, "one batch element has %lld rows x %lld pixels: beyond the 32-bit GEMM index range",
+                R, maxp);
   WsLayout L = layout_for(maxw, ppb, R, cb, reserved_floats, box);
   if (L.bytes > ws_bytes)
     return fail(VB_ENOMEM, "workspace of %zu bytes is too small: one batch element needs %zu", ws_bytes, L.bytes);
