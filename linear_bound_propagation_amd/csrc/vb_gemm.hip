@@ -196,8 +196,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   const int l32 = lane & 31, half = lane >> 5;
 
   // XCD-aware tile order: workgroups go round-robin over the 8 XCDs, so each
-  // XCD gets a contiguous run of tiles with the N-tiles of one M-tile next to
-  // each other; an M-tile's A rows are then fetched into one XCD's L2 once.
+  // XCD gets a contiguous run of tiles; within it the N-tiles of an M-tile (or
+  // of a group of M-tiles) are next to each other, so the A rows are fetched
+  // into one XCD's L2 once.
   const int mt = (d.Mt + BM - 1) / BM;
   const int nt = (d.N + BN - 1) / BN;
   const int ks_n = ((EPI == E_IBP || EPI == E_ADJOINT) && d.ksplit > 1) ? d.ksplit : 1;
@@ -207,7 +208,22 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   if (tile0 >= total) return;
   const int ks = tile0 / (mt * nt);
   const int tile = tile0 - ks * (mt * nt);
-  const int tm = tile / nt, tn = tile - tm * nt;
+  int tm, tn;
+  if (nt >= 4) {
+    // wide N: groups of 8 M-tiles sweep the N-tiles together, so their A rows
+    // stay in L2 while B moves past them (a plain row-major order re-fetched
+    // the A rows once per N-tile)
+    constexpr int GM = 8;
+    const int grp = tile / (GM * nt);
+    const int first = grp * GM;
+    const int gm = min(GM, mt - first);
+    const int idx = tile - grp * GM * nt;
+    tn = idx / gm;
+    tm = first + (idx - tn * gm);
+  } else {
+    tm = tile / nt;
+    tn = tile - tm * nt;
+  }
   const int m0 = tm * BM, n0 = tn * BN;
 
   // register staging of the next K stage
