@@ -114,10 +114,13 @@ vb_status vb_ibp(const vb_graph* g, int32_t batch,
  * relaxation of node_lo/node_hi of each ReLU input (adaptive lower slope),
  * then concretised over the domain: the input box if stop == 0, else the box
  * [node_lo[stop], node_hi[stop]].  lb or ub may be NULL.
- * If A_out != NULL, the linear bounds over `stop` are returned instead of being
- * concretised: A_out [batch][2R][size_stop] and bias_out [batch][2R] with
- * R = m (spec) or size_start (identity); the first R rows bound +rows from
- * below, the last R bound -rows from below. */
+ * If A_out != NULL, the linear bounds over `stop` are returned as well: the
+ * rows are the 2R functions (+rows, then -rows, R = m or size_start) bounded
+ * from below, row(x) >= A x + bias for x in the output of node `stop`, with
+ * A_out [batch][2R][size_stop] (node layout: channels-last for conv nodes)
+ * and bias_out [batch][2R] or NULL (beta: every bias met on the way, the
+ * relaxation offsets; not the bias of `stop` itself).  lb/ub may then both be
+ * NULL.  bias_out without A_out, or no output at all, is VB_EINVAL. */
 vb_status vb_crown_backward(const vb_graph* g, int32_t batch, int32_t start, int32_t stop,
                             const float* C, int32_t m,
                             const float* const* node_lo, const float* const* node_hi,

@@ -211,17 +211,23 @@ def ibp(net: DeviceNet, x_center: torch.Tensor, eps: float, lo=None, hi=None, C:
 
 
 def crown_backward(net: DeviceNet, start: int, stop: int, lo, hi, x_center: torch.Tensor, eps: float,
-                   ws: torch.Tensor, C: torch.Tensor = None, lb=None, ub=None, x_radius=None):
+                   ws: torch.Tensor, C: torch.Tensor = None, lb=None, ub=None, x_radius=None, linear=False):
+    """lb, ub [batch][R]; with linear=True also (A, bias): the linear bounds over node `stop`,
+    A [batch][2R][size_stop] and bias [batch][2R] (rows +r then -r, each bounded from below)."""
     batch = lo[start].shape[0]
     R = C.shape[1] if C is not None else net.sizes[start]
     if lb is None:
         lb = torch.empty(batch, R, device=net.device)
         ub = torch.empty(batch, R, device=net.device)
+    A = bias = None
+    if linear:
+        A = torch.empty(batch, 2 * R, net.sizes[stop], device=net.device)
+        bias = torch.empty(batch, 2 * R, device=net.device)
     _check(lib().vb_crown_backward(net.gp, batch, start, stop, _ptr(C), 0 if C is None else C.shape[1],
                                   _ptr_array(lo), _ptr_array(hi), _ptr(x_center), _ptr(x_radius), float(eps),
-                                  _ptr(lb), _ptr(ub), None, None, _ptr(ws), ws.numel(), _stream()),
+                                  _ptr(lb), _ptr(ub), _ptr(A), _ptr(bias), _ptr(ws), ws.numel(), _stream()),
            "vb_crown_backward")
-    return lb, ub
+    return (lb, ub, A, bias) if linear else (lb, ub)
 
 
 def concretize(A: torch.Tensor, bias: Optional[torch.Tensor], center: torch.Tensor, eps: float, rows_per_batch: int,

@@ -284,6 +284,10 @@ struct Backward {
   float* box_r = nullptr;
   // relaxation coefficients of the current target node, this chunk
   float4* coef = nullptr;
+  // optional: return Lambda over the domain node and beta instead of only
+  // concretising ([batch][R][size_stop] and [batch][R], whole batch)
+  float* a_out = nullptr;
+  float* bias_out = nullptr;
 
   int alloc() {
     for (int i = 0; i < NPOOL; ++i)
@@ -491,7 +495,7 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
       int epi;
       int z = -1;
       if (t == c.stop)
-        epi = lowest ? E_CONCRETIZE : E_STORE;
+        epi = (lowest && !B.a_out) ? E_CONCRETIZE : E_STORE;
       else if (tn.op == VB_RELU && lowest) {
         epi = E_RELAX;
         z = tn.in0;
@@ -511,7 +515,8 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
       if (epi == E_RELAX) {
         vb_status s = effective_bias(B, G, z, bias);
         if (s) return s;
-      } else if (epi == E_STORE && (tn.op == VB_LINEAR || tn.op == VB_CONV2D || tn.op == VB_ADD)) {
+      } else if (epi == E_STORE && t != c.stop && (tn.op == VB_LINEAR || tn.op == VB_CONV2D || tn.op == VB_ADD)) {
+        // (the domain node's own bias is not part of beta: the domain box is its output)
         vb_status s = effective_bias(B, G, t, bias);
         if (s) return s;
       }
@@ -773,6 +778,19 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
   if (lam[c.stop] == IDENT) {
     vb_status s = materialise(c.stop);
     if (s) return s;
+  }
+  if (B.a_out) {
+    // Lambda over the domain node and beta (rowacc before concretisation)
+    const long long sz = G.n[c.stop].size;
+    float* dst = B.a_out + (long long)c.b0 * R * sz;
+    if (lam[c.stop] >= 0)
+      HIPCHK(hipMemcpyAsync(dst, B.pool[lam[c.stop]], (size_t)rows * sz * sizeof(float), hipMemcpyDeviceToDevice,
+                            B.st));
+    else
+      HIPCHK(launch_fill(dst, 0.f, (long long)rows * sz, B.st));
+    if (B.bias_out)
+      HIPCHK(hipMemcpyAsync(B.bias_out + (long long)c.b0 * R, B.rowacc, (size_t)rows * sizeof(float),
+                            hipMemcpyDeviceToDevice, B.st));
   }
   if (lam[c.stop] >= 0) {
     const NodeInfo& sn = G.n[c.stop];
@@ -1208,8 +1226,11 @@ extern "C" vb_status vb_ibp(const vb_graph* g, int32_t batch, const float* x_cen
 
 static vb_status crown_backward_impl(const Graph& G, int batch, int start, int stop, const float* C, int m,
                                      const float* const* lo, const float* const* hi, Domain dom, float* lb,
-                                     float* ub, void* ws, size_t ws_bytes, hipStream_t st) {
+                                     float* ub, void* ws, size_t ws_bytes, hipStream_t st, float* a_out = nullptr,
+                                     float* bias_out = nullptr) {
   Backward B{G, st, lo, hi, dom};
+  B.a_out = a_out;
+  B.bias_out = bias_out;
   vb_status s = prepare_weights(G, (char*)ws, st, B.wt, B.beff);
   if (s) return s;
   const long long R = C ? 2LL * m : 2LL * G.n[start].size;
@@ -1237,9 +1258,10 @@ extern "C" vb_status vb_crown_backward(const vb_graph* g, int32_t batch, int32_t
   if (stop == 0 && (s = check_domain(x_center))) return s;
   if (stop == 0 && !x_radius && !(eps >= 0.f)) return fail(VB_EINVAL, "eps must be >= 0");
   if (!ws) return fail(VB_EINVAL, "workspace is NULL");
-  if (A_out || bias_out) return fail(VB_EUNSUPPORTED, "A_out: returning linear bounds is not implemented");
+  if (bias_out && !A_out) return fail(VB_EINVAL, "bias_out needs A_out");
+  if (!A_out && !lb && !ub) return fail(VB_EINVAL, "nothing to compute: lb, ub and A_out are NULL");
   return crown_backward_impl(G, batch, start, stop, C, m, node_lo, node_hi, {x_center, x_radius, eps}, lb, ub, ws,
-                             ws_bytes, (hipStream_t)stream);
+                             ws_bytes, (hipStream_t)stream, A_out, bias_out);
 }
 
 extern "C" vb_status vb_concretize(int32_t rows, int32_t n, int32_t rows_per_batch, const float* A, const float* bias,

@@ -159,6 +159,38 @@ def test_crown_backward_box_domain_and_radius_array(lbp):
         assert_close(ub[b], -_oracle_rows(on, lo, hi, wl, b, L, -Cb, 0, rad), f"radius ub input {b}")
 
 
+@pytest.mark.parametrize("case,box", [("mlp", False), ("mlp", True), ("cnn", False)])
+def test_crown_backward_linear_bounds(lbp, case, box):
+    """A_out / bias_out: the linear bounds over the domain node equal the oracle's
+    Lambda there, and the oracle's bound is their concretisation."""
+    wl = CASES[case]()
+    on, lo, hi = _fp32_bounds(wl)
+    net, x, C = lbp.prepare(wl)
+    dlo, dhi = _to_device(lbp, net, wl, lo, hi)
+    L = len(wl.nodes) - 1
+    stop = [k for k, nd in enumerate(wl.nodes) if nd.op == "relu"][0] if box else 0
+    method = "hybrid" if box else "crown"
+    ws = net.workspace(net.workspace_size(wl.batch, wl.m, method, stop))
+    lb, ub, A, bias = lbp.crown_backward(net, L, stop, dlo, dhi, x, float(wl.eps), ws, C=C, linear=True)
+    torch.cuda.synchronize()
+    shape = wl.nodes[stop].shape
+    m = wl.m
+    for b in range(wl.batch):
+        if stop == 0:
+            c = _f64(wl.x0[b])
+            r = torch.full_like(c, float(np.float32(wl.eps)))
+        else:
+            c, r = (lo[stop][b] + hi[stop][b]) / 2, (hi[stop][b] - lo[stop][b]) / 2
+        for sgn, sl in ((1.0, slice(0, m)), (-1.0, slice(m, 2 * m))):
+            keep = {}
+            val = backward(on, lo, hi, b, L, sgn * _f64(wl.C[b]), stop, c, r, keep=keep)
+            Lam = keep["domain"]
+            beta = val - concretize(Lam, torch.zeros(m, dtype=torch.float64), c, r)
+            assert_close(A[b, sl], nhwc(Lam, shape), f"A input {b} sign {sgn}")
+            assert_close(bias[b, sl], beta, f"bias input {b} sign {sgn}")
+        assert_close(lb[b], _oracle_rows(on, lo, hi, wl, b, L, _f64(wl.C[b]), stop), f"lb input {b}")
+
+
 # ---------------------------------------------------------------------------
 # vb_alpha_init
 
