@@ -111,11 +111,17 @@ vb_status vb_ibp(const vb_graph* g, int32_t batch,
  *   C != NULL: spec rows C [batch][m][size_start]; writes lb = lb(C) and
  *              ub = -lb(-C), each [batch][m].
  * The rows are pushed to `stop` through every node in between using the ReLU
- * relaxation of node_lo/node_hi of each ReLU input (adaptive lower slope),
- * then concretised over the domain: the input box if stop == 0, else the box
- * [node_lo[stop], node_hi[stop]].  lb or ub may be NULL.
+ * relaxation of node_lo/node_hi of each ReLU input (adaptive lower slope, or
+ * alpha), then concretised over the domain: the input box if stop == 0, else
+ * the box [node_lo[stop], node_hi[stop]].  lb or ub may be NULL; with spec
+ * rows and ub == NULL only the rows C are propagated (half the work).
+ * alpha: NULL, or per node (entries of ReLU nodes between stop and start
+ * non-NULL) the lower slopes [batch][m][size] used on unstable neurons
+ * (Sec. 3 and Sec. 4.3: per-neuron alpha); needs C and ub == NULL (the slopes
+ * bound one side: call again with -C for the upper bound).
  * If A_out != NULL, the linear bounds over `stop` are returned as well: the
- * rows are the 2R functions (+rows, then -rows, R = m or size_start) bounded
+ * rows are the 2R functions (+rows, then -rows, R = m or size_start; only the
+ * R rows C when ub == NULL with spec rows) bounded
  * from below, row(x) >= A x + bias for x in the output of node `stop`, with
  * A_out [batch][2R][size_stop] (node layout: channels-last for conv nodes)
  * and bias_out [batch][2R] or NULL (beta: every bias met on the way, the
@@ -124,6 +130,7 @@ vb_status vb_ibp(const vb_graph* g, int32_t batch,
 vb_status vb_crown_backward(const vb_graph* g, int32_t batch, int32_t start, int32_t stop,
                             const float* C, int32_t m,
                             const float* const* node_lo, const float* const* node_hi,
+                            const float* const* alpha,
                             const float* x_center, const float* x_radius, float eps,
                             float* lb, float* ub, float* A_out, float* bias_out,
                             void* ws, size_t ws_bytes, void* stream);

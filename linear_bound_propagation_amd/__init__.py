@@ -59,7 +59,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vb_ibp.restype = i32
     lib.vb_ibp.argtypes = [G, i32, P, P, f32, PP, PP, P, i32, P, P, P, sz, P]
     lib.vb_crown_backward.restype = i32
-    lib.vb_crown_backward.argtypes = [G, i32, i32, i32, P, i32, PP, PP, P, P, f32, P, P, P, P, P, sz, P]
+    lib.vb_crown_backward.argtypes = [G, i32, i32, i32, P, i32, PP, PP, PP, P, P, f32, P, P, P, P, P, sz, P]
     lib.vb_concretize.restype = i32
     lib.vb_concretize.argtypes = [i32, i32, i32, P, P, P, P, f32, P, P, P]
     lib.vb_alpha_init.restype = i32
@@ -211,21 +211,26 @@ def ibp(net: DeviceNet, x_center: torch.Tensor, eps: float, lo=None, hi=None, C:
 
 
 def crown_backward(net: DeviceNet, start: int, stop: int, lo, hi, x_center: torch.Tensor, eps: float,
-                   ws: torch.Tensor, C: torch.Tensor = None, lb=None, ub=None, x_radius=None, linear=False):
-    """lb, ub [batch][R]; with linear=True also (A, bias): the linear bounds over node `stop`,
-    A [batch][2R][size_stop] and bias [batch][2R] (rows +r then -r, each bounded from below)."""
+                   ws: torch.Tensor, C: torch.Tensor = None, lb=None, ub=None, x_radius=None, linear=False,
+                   alpha=None, lower_only=False):
+    """lb, ub [batch][R] (ub None with lower_only or alpha: spec rows C only); with linear=True
+    also (A, bias): the linear bounds over node `stop`, A [batch][rows][size_stop] and bias
+    [batch][rows] (rows +r then -r, or only +r when one-sided, each bounded from below)."""
     batch = lo[start].shape[0]
     R = C.shape[1] if C is not None else net.sizes[start]
+    one_side = C is not None and (lower_only or alpha is not None)
     if lb is None:
         lb = torch.empty(batch, R, device=net.device)
-        ub = torch.empty(batch, R, device=net.device)
+        ub = None if one_side else torch.empty(batch, R, device=net.device)
     A = bias = None
     if linear:
-        A = torch.empty(batch, 2 * R, net.sizes[stop], device=net.device)
-        bias = torch.empty(batch, 2 * R, device=net.device)
+        rows = R if one_side else 2 * R
+        A = torch.empty(batch, rows, net.sizes[stop], device=net.device)
+        bias = torch.empty(batch, rows, device=net.device)
     _check(lib().vb_crown_backward(net.gp, batch, start, stop, _ptr(C), 0 if C is None else C.shape[1],
-                                  _ptr_array(lo), _ptr_array(hi), _ptr(x_center), _ptr(x_radius), float(eps),
-                                  _ptr(lb), _ptr(ub), _ptr(A), _ptr(bias), _ptr(ws), ws.numel(), _stream()),
+                                  _ptr_array(lo), _ptr_array(hi), None if alpha is None else _ptr_array(alpha),
+                                  _ptr(x_center), _ptr(x_radius), float(eps), _ptr(lb), _ptr(ub), _ptr(A),
+                                  _ptr(bias), _ptr(ws), ws.numel(), _stream()),
            "vb_crown_backward")
     return (lb, ub, A, bias) if linear else (lb, ub)
 

@@ -409,6 +409,14 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
     for (int k = 0; k < c.stop; ++k) active[k] = 0;
   }
   auto chunk_off = [&](int node) -> long long { return (long long)c.b0 * G.n[node].size; };
+  // per-row tensors over a node (alpha, kept Psi: [batch][R][size]) for this chunk
+  auto row_off = [&](int node) -> long long { return (long long)c.b0 * R * G.n[node].size; };
+  auto alpha_of = [&](int node) -> const float* {
+    return (B.alpha && B.alpha[node]) ? B.alpha[node] + row_off(node) : nullptr;
+  };
+  auto psi_of = [&](int node) -> float* {
+    return (B.psi_keep && B.psi_keep[node]) ? B.psi_keep[node] + row_off(node) : nullptr;
+  };
   const NodeInfo& S = G.n[c.start];
   if (c.stop != 0)
     HIPCHK(launch_box_center_radius(B.lo[c.stop] + chunk_off(c.stop), B.hi[c.stop] + chunk_off(c.stop),
@@ -590,7 +598,7 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
         a.mode = epi;
         a.addend = pbuf >= 0 ? B.pool[pbuf] : nullptr;
         a.out = outb >= 0 ? B.pool[outb] : nullptr;
-        a.psi_out = (B.psi_keep && B.psi_keep[t]) ? B.psi_keep[t] : nullptr;
+        a.psi_out = psi_of(t);
         a.bias = bias;
         if (epi == E_RELAX) {
           a.lo = B.lo[z] + chunk_off(z);
@@ -641,11 +649,11 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
           if (epi == E_RELAX) {
             d.lo = B.lo[tgt_bounds] + chunk_off(tgt_bounds);
             d.hi = B.hi[tgt_bounds] + chunk_off(tgt_bounds);
-            if (B.alpha && B.alpha[t]) d.alpha = B.alpha[t];
-            if (B.psi_keep && B.psi_keep[t]) d.psi_out = B.psi_keep[t];
+            d.alpha = alpha_of(t);
+            d.psi_out = psi_of(t);
           }
           if (epi == E_CONCRETIZE) {
-            if (B.psi_keep && B.psi_keep[t]) d.psi_out = B.psi_keep[t];
+            d.psi_out = psi_of(t);
             if (t == 0) {
               d.center = B.dom.xc + chunk_off(0);
               d.radius = B.dom.xr ? B.dom.xr + chunk_off(0) : nullptr;
@@ -695,8 +703,7 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
       if (s) return s;
       const int P = nd.h * nd.w;
       HIPCHK(launch_relax(B.pool[cur], 0, 1.f, nullptr, rows, (int)R, P, nd.c, B.lo[z] + chunk_off(z),
-                          B.hi[z] + chunk_off(z), bias_z, B.alpha ? B.alpha[k] : nullptr,
-                          B.psi_keep ? B.psi_keep[k] : nullptr, B.pool[outb], B.rowacc, B.st));
+                          B.hi[z] + chunk_off(z), bias_z, alpha_of(k), psi_of(k), B.pool[outb], B.rowacc, B.st));
       B.release(cur);
       lam[k] = -1;
       if (lam[z] != -1) return fail(VB_EUNSUPPORTED, "internal: node %d already has a pending Lambda", z);
@@ -750,8 +757,8 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
         vb_status s = effective_bias(B, G, z, bias_z);
         if (s) return s;
         HIPCHK(launch_relax(B.pool[cur], 1, scale, pend >= 0 ? B.pool[pend] : nullptr, rows, (int)R, P, tn.c,
-                            B.lo[z] + chunk_off(z), B.hi[z] + chunk_off(z), bias_z, B.alpha ? B.alpha[t] : nullptr,
-                            B.psi_keep ? B.psi_keep[t] : nullptr, B.pool[outb], B.rowacc, B.st));
+                            B.lo[z] + chunk_off(z), B.hi[z] + chunk_off(z), bias_z, alpha_of(t), psi_of(t),
+                            B.pool[outb], B.rowacc, B.st));
         if (pend >= 0) {
           B.release(pend);
           lam[t] = -1;
@@ -1224,29 +1231,40 @@ extern "C" vb_status vb_ibp(const vb_graph* g, int32_t batch, const float* x_cen
   return VB_OK;
 }
 
+// Spec rows with ub == NULL propagate only the rows C (lower bound); every
+// other call propagates [rows; -rows].  alpha (per node, ReLU nodes
+// [batch][m][size]) replaces the adaptive lower slope on unstable neurons.
 static vb_status crown_backward_impl(const Graph& G, int batch, int start, int stop, const float* C, int m,
                                      const float* const* lo, const float* const* hi, Domain dom, float* lb,
                                      float* ub, void* ws, size_t ws_bytes, hipStream_t st, float* a_out = nullptr,
-                                     float* bias_out = nullptr) {
+                                     float* bias_out = nullptr, const float* const* alpha = nullptr) {
   Backward B{G, st, lo, hi, dom};
   B.a_out = a_out;
   B.bias_out = bias_out;
+  B.alpha = alpha;
   vb_status s = prepare_weights(G, (char*)ws, st, B.wt, B.beff);
   if (s) return s;
-  const long long R = C ? 2LL * m : 2LL * G.n[start].size;
+  const bool lower_only = C && !ub;
+  const long long R = C ? (lower_only ? m : 2LL * m) : 2LL * G.n[start].size;
   const int half = (int)(R / 2);
-  return backward_all(B, start, stop, C, m, 1, batch, R, (char*)ws, ws_bytes, wt_floats(G),
+  return backward_all(B, start, stop, C, m, lower_only ? 0 : 1, batch, R, (char*)ws, ws_bytes, wt_floats(G),
                       [&](float* acc, int b0, int cb) -> vb_status {
-                        HIPCHK(launch_finish(acc, cb, half, lb ? lb + (long long)b0 * half : nullptr,
-                                             ub ? ub + (long long)b0 * half : nullptr, nullptr, st));
+                        if (lower_only) {
+                          HIPCHK(launch_finish_lower(acc, (long long)cb * m, lb ? lb + (long long)b0 * m : nullptr,
+                                                     nullptr, 0, st));
+                        } else {
+                          HIPCHK(launch_finish(acc, cb, half, lb ? lb + (long long)b0 * half : nullptr,
+                                               ub ? ub + (long long)b0 * half : nullptr, nullptr, st));
+                        }
                         return VB_OK;
                       });
 }
 
 extern "C" vb_status vb_crown_backward(const vb_graph* g, int32_t batch, int32_t start, int32_t stop, const float* C,
                                        int32_t m, const float* const* node_lo, const float* const* node_hi,
-                                       const float* x_center, const float* x_radius, float eps, float* lb, float* ub,
-                                       float* A_out, float* bias_out, void* ws, size_t ws_bytes, void* stream) {
+                                       const float* const* alpha, const float* x_center, const float* x_radius,
+                                       float eps, float* lb, float* ub, float* A_out, float* bias_out, void* ws,
+                                       size_t ws_bytes, void* stream) {
   Graph G;
   vb_status s = parse_graph(g, G);
   if (s) return s;
@@ -1260,8 +1278,13 @@ extern "C" vb_status vb_crown_backward(const vb_graph* g, int32_t batch, int32_t
   if (!ws) return fail(VB_EINVAL, "workspace is NULL");
   if (bias_out && !A_out) return fail(VB_EINVAL, "bias_out needs A_out");
   if (!A_out && !lb && !ub) return fail(VB_EINVAL, "nothing to compute: lb, ub and A_out are NULL");
+  if (alpha) {
+    if (!C || ub) return fail(VB_EINVAL, "alpha needs spec rows C and ub == NULL (slopes bound one side)");
+    for (size_t k = start > stop ? stop + 1 : 0; (int)k < start; ++k)
+      if (G.n[k].op == VB_RELU && !alpha[k]) return fail(VB_EINVAL, "alpha of ReLU node %zu is NULL", k);
+  }
   return crown_backward_impl(G, batch, start, stop, C, m, node_lo, node_hi, {x_center, x_radius, eps}, lb, ub, ws,
-                             ws_bytes, (hipStream_t)stream, A_out, bias_out);
+                             ws_bytes, (hipStream_t)stream, A_out, bias_out, alpha);
 }
 
 extern "C" vb_status vb_concretize(int32_t rows, int32_t n, int32_t rows_per_batch, const float* A, const float* bias,

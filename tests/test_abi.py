@@ -92,17 +92,21 @@ def test_entry_points_reject_bad_arguments_without_launching():
     # negative eps without a radius array
     assert lbp.lib().vb_ibp(gp, 2, P(64), None, -1.0, nulls, nulls, None, 0, None, None, None, 0, None) == -1
     # crown_backward: stop >= start, missing workspace
-    assert lbp.lib().vb_crown_backward(gp, 2, 1, 1, None, 0, nulls, nulls, P(64), None, 0.1, None, None, None, None,
+    assert lbp.lib().vb_crown_backward(gp, 2, 1, 1, None, 0, nulls, nulls, None, P(64), None, 0.1, None, None, None, None,
                                       P(64), 1 << 20, None) == -1
-    assert lbp.lib().vb_crown_backward(gp, 2, 3, 0, None, 0, nulls, nulls, P(64), None, 0.1, None, None, None, None,
+    assert lbp.lib().vb_crown_backward(gp, 2, 3, 0, None, 0, nulls, nulls, None, P(64), None, 0.1, None, None, None, None,
                                       None, 0, None) == -1
     # crown_backward: bias_out without A_out, and no output at all
-    assert lbp.lib().vb_crown_backward(gp, 2, 3, 0, None, 0, nulls, nulls, P(64), None, 0.1, None, None, None,
+    assert lbp.lib().vb_crown_backward(gp, 2, 3, 0, None, 0, nulls, nulls, None, P(64), None, 0.1, None, None, None,
                                       P(64), P(64), 1 << 20, None) == -1
     assert b"bias_out needs A_out" in lbp.lib().vb_last_error()
-    assert lbp.lib().vb_crown_backward(gp, 2, 3, 0, None, 0, nulls, nulls, P(64), None, 0.1, None, None, None, None,
+    assert lbp.lib().vb_crown_backward(gp, 2, 3, 0, None, 0, nulls, nulls, None, P(64), None, 0.1, None, None, None, None,
                                       P(64), 1 << 20, None) == -1
     assert b"nothing to compute" in lbp.lib().vb_last_error()
+    # alpha needs spec rows and a one-sided call
+    assert lbp.lib().vb_crown_backward(gp, 2, 3, 0, None, 0, nulls, nulls, nulls, P(64), None, 0.1, P(64), None,
+                                      None, None, P(64), 1 << 20, None) == -1
+    assert b"alpha needs spec rows" in lbp.lib().vb_last_error()
     # workspace too small: reported before any launch
     bounds = (ctypes.c_void_p * 4)(None, 64, 64, 64)
     assert lbp.lib().vb_crown(gp, 2, P(64), None, 0.1, 1, 0, bounds, bounds, P(64), 2, None, None, P(64), P(64),

@@ -191,6 +191,46 @@ def test_crown_backward_linear_bounds(lbp, case, box):
         assert_close(lb[b], _oracle_rows(on, lo, hi, wl, b, L, _f64(wl.C[b]), stop), f"lb input {b}")
 
 
+@pytest.mark.parametrize("case", ["mlp", "cnn"])
+def test_crown_backward_with_alpha_one_sided(lbp, case):
+    """Spec rows with given lower slopes (ub NULL: only the rows C are pushed) against
+    the oracle's back-substitution with the same slopes; without alpha the one-sided
+    call gives the two-sided call's lb."""
+    wl = CASES[case]()
+    on, lo, hi = _fp32_bounds(wl)
+    net, x, C = lbp.prepare(wl)
+    dlo, dhi = _to_device(lbp, net, wl, lo, hi)
+    L = len(wl.nodes) - 1
+    ws = net.workspace(net.workspace_size(wl.batch, wl.m, "crown"))
+    lb2, _ = lbp.crown_backward(net, L, 0, dlo, dhi, x, float(wl.eps), ws, C=C)
+    lb1, ub1 = lbp.crown_backward(net, L, 0, dlo, dhi, x, float(wl.eps), ws, C=C, lower_only=True)
+    torch.cuda.synchronize()
+    assert ub1 is None
+    assert_close(lb1, lb2.detach().double().cpu().numpy(), "one-sided lb")
+    rng = np.random.default_rng(9)
+    alpha_dev = [None] * len(wl.nodes)
+    alpha_ref = {}
+    for r, nd in enumerate(wl.nodes):
+        if nd.op != "relu":
+            continue
+        a = rng.random((wl.batch, wl.m) + tuple(nd.shape)).astype(np.float32)
+        alpha_ref[r] = a
+        alpha_dev[r] = torch.as_tensor(nhwc(a.reshape((wl.batch * wl.m,) + tuple(nd.shape)), nd.shape)
+                                       .reshape(wl.batch, wl.m, -1), dtype=torch.float32, device=x.device)
+    lba, uba, A, bias = lbp.crown_backward(net, L, 0, dlo, dhi, x, float(wl.eps), ws, C=C, alpha=alpha_dev,
+                                           linear=True)
+    torch.cuda.synchronize()
+    assert uba is None and A.shape[1] == wl.m
+    for b in range(wl.batch):
+        c = _f64(wl.x0[b])
+        r = torch.full_like(c, float(np.float32(wl.eps)))
+        keep = {}
+        ref = backward(on, lo, hi, b, L, _f64(wl.C[b]), 0, c, r,
+                       alpha={k: _f64(v[b]) for k, v in alpha_ref.items()}, keep=keep)
+        assert_close(lba[b], ref, f"alpha lb input {b}")
+        assert_close(A[b], nhwc(keep["domain"], wl.nodes[0].shape), f"alpha A input {b}")
+
+
 # ---------------------------------------------------------------------------
 # vb_alpha_init
 
