@@ -75,7 +75,7 @@ def algorithmic_flops(wl):
     L = len(nodes) - 1
     # spec IBP: C folded into the last Linear
     total["spec"] += 2 * (2 * m * B) * _mac_per_row(nodes[L], nodes)
-    stop = 0 if wl.intermediate != "hybrid" else wl.region_start
+    stop = wl.region_start if wl.intermediate.startswith("hybrid") else 0
     if wl.intermediate != "ibp":
         for r, nd in enumerate(nodes):
             if nd.op != "relu":

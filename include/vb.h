@@ -74,6 +74,9 @@ typedef struct {
                              /* input is one affine step from the domain)         */
 #define VB_METHOD_HYBRID 2   /* IBP up to node region_start, CROWN after it with  */
                              /* region_start's IBP box as the domain              */
+#define VB_INTERSECT_IBP 16  /* flag for CROWN / HYBRID: each CROWN intermediate  */
+                             /* bound is intersected with the node's IBP bound    */
+                             /* (l = max, u = min) before later layers use it     */
 
 /* Thread-local description of the last error on this thread. */
 const char* vb_last_error(void);

@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libvbprop.so")
 
 VB_INPUT, VB_LINEAR, VB_CONV2D, VB_RELU, VB_ADD, VB_GAP, VB_FLATTEN = range(7)
-METHODS = {"ibp": 0, "crown": 1, "hybrid": 2}
+METHODS = {"ibp": 0, "crown": 1, "hybrid": 2, "crown+ibp": 1 | 16, "hybrid+ibp": 2 | 16}
 STATUS = {0: "VB_OK", -1: "VB_EINVAL", -2: "VB_ESHAPE", -3: "VB_ENOMEM", -4: "VB_EDEVICE",
           -5: "VB_EUNSUPPORTED"}
 _OPS = {"input": VB_INPUT, "linear": VB_LINEAR, "conv": VB_CONV2D, "relu": VB_RELU, "add": VB_ADD,

@@ -1180,6 +1180,7 @@ extern "C" vb_status vb_workspace_size(const vb_graph* g, int32_t batch, int32_t
   if (s) return s;
   if (!bytes) return fail(VB_EINVAL, "bytes is NULL");
   if (batch <= 0 || m < 0) return fail(VB_EINVAL, "batch must be > 0 and m >= 0");
+  method &= ~VB_INTERSECT_IBP;
   if (method < VB_METHOD_IBP || method > VB_METHOD_HYBRID) return fail(VB_EINVAL, "unknown method %d", method);
   if (method == VB_METHOD_HYBRID && (region_start <= 0 || region_start >= G.L))
     return fail(VB_EINVAL, "region_start %d out of range", region_start);
@@ -1237,7 +1238,8 @@ extern "C" vb_status vb_ibp(const vb_graph* g, int32_t batch, const float* x_cen
 static vb_status crown_backward_impl(const Graph& G, int batch, int start, int stop, const float* C, int m,
                                      const float* const* lo, const float* const* hi, Domain dom, float* lb,
                                      float* ub, void* ws, size_t ws_bytes, hipStream_t st, float* a_out = nullptr,
-                                     float* bias_out = nullptr, const float* const* alpha = nullptr) {
+                                     float* bias_out = nullptr, const float* const* alpha = nullptr,
+                                     bool intersect = false) {
   Backward B{G, st, lo, hi, dom};
   B.a_out = a_out;
   B.bias_out = bias_out;
@@ -1254,7 +1256,8 @@ static vb_status crown_backward_impl(const Graph& G, int batch, int start, int s
                                                      nullptr, 0, st));
                         } else {
                           HIPCHK(launch_finish(acc, cb, half, lb ? lb + (long long)b0 * half : nullptr,
-                                               ub ? ub + (long long)b0 * half : nullptr, nullptr, st));
+                                               ub ? ub + (long long)b0 * half : nullptr, nullptr, st,
+                                               intersect ? 1 : 0));
                         }
                         return VB_OK;
                       });
@@ -1309,7 +1312,10 @@ extern "C" vb_status vb_crown(const vb_graph* g, int32_t batch, const float* x_c
   if ((s = check_domain(x_center))) return s;
   if (!x_radius && !(eps >= 0.f)) return fail(VB_EINVAL, "eps must be >= 0");
   if (!node_lo || !node_hi) return fail(VB_EINVAL, "node_lo/node_hi arrays are NULL");
+  const bool intersect = (method & VB_INTERSECT_IBP) != 0;
+  method &= ~VB_INTERSECT_IBP;
   if (method < VB_METHOD_IBP || method > VB_METHOD_HYBRID) return fail(VB_EINVAL, "unknown method %d", method);
+  if (intersect && method == VB_METHOD_IBP) return fail(VB_EINVAL, "VB_INTERSECT_IBP needs CROWN or HYBRID");
   if (method == VB_METHOD_HYBRID && (region_start <= 0 || region_start >= G.L))
     return fail(VB_EINVAL, "region_start %d out of range", region_start);
   if (C && m <= 0) return fail(VB_EINVAL, "m must be positive with C");
@@ -1337,7 +1343,7 @@ extern "C" vb_status vb_crown(const vb_graph* g, int32_t batch, const float* x_c
       const int z = G.n[r].in0;
       if (z <= stop || one_affine_step(G, z, stop)) continue;
       s = crown_backward_impl(G, batch, z, stop, nullptr, 0, node_lo, node_hi, dom, node_lo[z], node_hi[z], ws,
-                              ws_bytes, st);
+                              ws_bytes, st, nullptr, nullptr, nullptr, intersect);
       if (s) return s;
     }
   }

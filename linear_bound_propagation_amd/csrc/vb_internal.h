@@ -128,9 +128,10 @@ hipError_t launch_rows_reduce(const float* part, int Z, int rows, int P, int S, 
                               float* rowacc, int accumulate, int pos_major, hipStream_t st);
 
 // Write the final outputs from row accumulators.  rows per batch element = 2R:
-// lb[b*R + i] = acc[b*2R + i], ub[b*R + i] = -acc[b*2R + R + i]  (NULL skips)
+// lb[b*R + i] = acc[b*2R + i], ub[b*R + i] = -acc[b*2R + R + i]  (NULL skips);
+// intersect: lb = max(lb, new), ub = min(ub, new) with the values already there
 hipError_t launch_finish(const float* rowacc, int batch, int R, float* lb, float* ub,
-                         float* best, hipStream_t st);
+                         float* best, hipStream_t st, int intersect = 0);
 // Lower-only rows (R per batch element): lb[i] = acc[i], best[i] = max(best[i], acc[i])
 // (best[i] = acc[i] when init).
 hipError_t launch_finish_lower(const float* rowacc, long long n, float* lb, float* best, int init, hipStream_t st);

@@ -73,21 +73,23 @@ hipError_t launch_rows_reduce(const float* part, int Z, int rows, int P, int S, 
 }
 
 __global__ void finish_kernel(const float* __restrict__ acc, int batch, int R, float* lb, float* ub,
-                              float* best) {
+                              float* best, int intersect) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (long long)batch * R) return;
   const long long b = i / R, r = i - b * R;
   const float l = acc[b * 2 * R + r];
-  if (lb) lb[i] = l;
-  if (ub) ub[i] = -acc[b * 2 * R + R + r];
+  const float u = -acc[b * 2 * R + R + r];
+  if (lb) lb[i] = intersect ? fmaxf(lb[i], l) : l;
+  if (ub) ub[i] = intersect ? fminf(ub[i], u) : u;
   if (best) best[i] = fmaxf(best[i], l);
 }
 
 hipError_t launch_finish(const float* rowacc, int batch, int R, float* lb, float* ub, float* best,
-                         hipStream_t st) {
+                         hipStream_t st, int intersect) {
   long long n = (long long)batch * R;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(finish_kernel, dim3((n + 255) / 256), dim3(256), 0, st, rowacc, batch, R, lb, ub, best);
+  hipLaunchKernelGGL(finish_kernel, dim3((n + 255) / 256), dim3(256), 0, st, rowacc, batch, R, lb, ub, best,
+                     intersect);
   return hipGetLastError();
 }
 

@@ -251,14 +251,22 @@ def intermediate_bounds(net: Oracle, x0, eps, mode: str, region_start: Optional[
     using the bounds already computed for earlier ReLUs; a z one affine step
     from the domain keeps its IBP bounds (exact there).  mode "hybrid": IBP up
     to and including `region_start`, CROWN inside the region with the IBP box of
-    `region_start` as the domain.  Rows are independent, so they are processed
-    in chunks of `row_chunk`.  Returns (lo, hi) lists [B][*shape] (float64);
-    only the inputs in batch_idx are refined (all by default).
+    `region_start` as the domain.  A suffix "+ibp" ("crown+ibp", "hybrid+ibp")
+    intersects each CROWN result with that node's bounds from the initial IBP
+    pass: l = max(l_crown, l_ibp), u = min(u_crown, u_ibp), before later layers
+    use them.  Rows are independent, so they are processed in chunks of
+    `row_chunk`.  Returns (lo, hi) lists [B][*shape] (float64); only the inputs
+    in batch_idx are refined (all by default).
     """
     lo, hi = ibp(net, x0, eps)
-    if mode == "ibp":
+    base, _, suffix = mode.partition("+")
+    assert base in ("ibp", "crown", "hybrid") and suffix in ("", "ibp"), mode
+    if base == "ibp":
         return lo, hi
-    stop = 0 if mode == "crown" else region_start
+    intersect = suffix == "ibp"
+    lo_ibp = [t.clone() for t in lo]
+    hi_ibp = [t.clone() for t in hi]
+    stop = 0 if base == "crown" else region_start
     B = lo[0].shape[0]
     batch_idx = range(B) if batch_idx is None else batch_idx
     for r in net.relu_nodes():
@@ -275,6 +283,9 @@ def intermediate_bounds(net: Oracle, x0, eps, mode: str, region_start: Optional[
                 r1 = min(n, r0 + row_chunk)
                 lz[r0:r1] = backward(net, lo, hi, b, z, _identity_rows(shape, 1.0, r0, r1), stop, dc, dr)
                 uz[r0:r1] = -backward(net, lo, hi, b, z, _identity_rows(shape, -1.0, r0, r1), stop, dc, dr)
+            if intersect:
+                lz = torch.maximum(lz, lo_ibp[z][b].reshape(-1))
+                uz = torch.minimum(uz, hi_ibp[z][b].reshape(-1))
             lo[z][b] = lz.reshape(shape)
             hi[z][b] = uz.reshape(shape)
     return lo, hi
@@ -304,7 +315,7 @@ def crown_bounds(wl, batch_idx: Optional[Sequence[int]] = None, row_chunk: int =
     ibp_lb, ibp_ub = spec_bounds_ibp(net, lo_ibp, hi_ibp, wl.C)
     lo, hi = intermediate_bounds(net, wl.x0, wl.eps, wl.intermediate, wl.region_start,
                                  batch_idx, row_chunk)
-    stop = wl.region_start if wl.intermediate == "hybrid" else 0
+    stop = wl.region_start if wl.intermediate.startswith("hybrid") else 0
     lb, ub = spec_bounds_crown(net, lo, hi, wl.x0, wl.eps, wl.C, stop, batch_idx)
     return {"ibp_lo": lo_ibp, "ibp_hi": hi_ibp, "ibp_lb": ibp_lb, "ibp_ub": ibp_ub,
             "lo": lo, "hi": hi, "lb": lb, "ub": ub}

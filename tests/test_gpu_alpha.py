@@ -71,3 +71,21 @@ def test_config4_full_size_sampled_inputs(lbp):
     gain = (best - lb_steps[0]).double()
     print(f"mean improvement over CROWN: {gain.mean().item():.4g} (max {gain.max().item():.4g})", flush=True)
     assert bool((gain >= -1e-3).all())
+
+
+def test_alpha_upper_bounds_via_negated_specs(lbp):
+    """alpha-CROWN on the upper side: optimising slopes for the rows -C gives
+    ub = -lb(-C); parity with the oracle run on -C, and the optimised upper bound
+    is no looser than CROWN's."""
+    wl = wk.tiny_mlp([40, 70, 50, 8], 0.08, 23, batch=2)
+    wl.intermediate = "ibp"
+    wl.C = -wl.C
+    steps = 6
+    out, best, lb_steps, _ = _gpu_alpha(lbp, wl, steps)
+    crown_lb, ref = _oracle(wl, steps)
+    for t in range(steps + 1):
+        assert_close(lb_steps[t], ref["lb_steps"][t], f"lb(-C) after {t} Adam steps")
+    assert_close(best, ref["best"], "best lb(-C)")
+    ub_alpha = -best.double().cpu()
+    ub_crown = -crown_lb
+    assert bool((ub_alpha <= ub_crown + 1e-5).all())

@@ -23,7 +23,7 @@ def _run(lbp, wl):
     return out
 
 
-@pytest.mark.parametrize("method", ["ibp", "crown"])
+@pytest.mark.parametrize("method", ["ibp", "crown", "crown+ibp"])
 @pytest.mark.parametrize("convs,fcs,in_shape,batch,eps,seed", [
     # odd spatial sizes: stride-2 parity classes of different sizes; C_in = 3
     (((8, 1), (16, 2), (8, 1)), (20, 10), (3, 9, 9), 3, 0.02, 11),

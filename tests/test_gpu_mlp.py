@@ -55,6 +55,18 @@ def test_mlp_small_ragged(lbp, widths, batch, eps, seed):
         _compare(wl, out, ref)
 
 
+@pytest.mark.parametrize("widths,batch,eps,seed", [
+    ([50, 130, 97, 200, 11], 5, 0.05, 1),
+    ([300, 257, 129, 10], 9, 0.02, 3),
+])
+def test_mlp_crown_intersected_with_ibp(lbp, widths, batch, eps, seed):
+    wl = wk.tiny_mlp(widths, eps, seed, batch=batch)
+    wl.intermediate = "crown+ibp"
+    ref = crown_bounds(wl)
+    _, out = _run(lbp, wl)
+    _compare(wl, out, ref)
+
+
 def test_config1_full(lbp):
     wl = wk.config(1)
     print(wl.name, flush=True)

@@ -25,7 +25,7 @@ def _run(lbp, wl, ws=None):
     return net, out
 
 
-@pytest.mark.parametrize("method", ["hybrid", "crown", "ibp"])
+@pytest.mark.parametrize("method", ["hybrid", "crown", "ibp", "hybrid+ibp", "crown+ibp"])
 def test_resnet_small(lbp, method):
     wl = wk.resnet(2, 0.01, 31, widths=(4, 6, 8), blocks=(1, 2, 2), n_out=5, in_shape=(3, 8, 8))
     wl.intermediate = method

@@ -192,7 +192,7 @@ def _check_sound(wl, res, n=100000, seed=0):
                 assert (v <= hi + 1e-9 * (1 + abs(hi))).all()
 
 
-@pytest.mark.parametrize("mode", ["crown", "ibp"])
+@pytest.mark.parametrize("mode", ["crown", "ibp", "crown+ibp"])
 def test_soundness_mlp_sampling(mode):
     for seed, widths, eps in ((0, [4, 8, 8, 3], 0.3), (1, [6, 12, 10, 7, 4], 0.15), (2, [3, 5, 5, 5, 2], 0.5)):
         wl = wk.tiny_mlp(widths, eps, seed, batch=2)
@@ -206,6 +206,30 @@ def test_soundness_cnn_and_resnet_sampling():
     wl.intermediate = "ibp"
     _check_sound(wl, crown_bounds(wl), n=20000)
     wl = wk.resnet(2, 0.05, 92, widths=(2, 3), blocks=(1, 2), n_out=3, in_shape=(2, 4, 4))
+    _check_sound(wl, crown_bounds(wl), n=20000)
+
+
+def test_intersection_mode_is_sound_and_inside_both():
+    """CROWN intermediates intersected with IBP: sound on samples; every node's box lies
+    inside its IBP box; and at the first CROWN-refined layer (whose relaxations come
+    from IBP bounds in both modes) it is exactly the intersection of the two boxes."""
+    for seed, widths, eps in ((3, [5, 9, 9, 8, 3], 0.3), (4, [6, 12, 10, 7, 4], 0.2)):
+        wl = wk.tiny_mlp(widths, eps, seed, batch=2)
+        net = Oracle(wl.nodes)
+        lo_i, hi_i = intermediate_bounds(net, wl.x0, wl.eps, "ibp")
+        lo_c, hi_c = intermediate_bounds(net, wl.x0, wl.eps, "crown")
+        lo_x, hi_x = intermediate_bounds(net, wl.x0, wl.eps, "crown+ibp")
+        zs = [nd.inputs[0] for nd in wl.nodes if nd.op == "relu"]
+        for z in zs:
+            assert bool((lo_x[z] >= lo_i[z] - 1e-12).all() and (hi_x[z] <= hi_i[z] + 1e-12).all())
+        first = zs[1]          # zs[0] is one affine step from the input: IBP = CROWN there
+        assert torch.equal(lo_x[first], torch.maximum(lo_c[first], lo_i[first]))
+        assert torch.equal(hi_x[first], torch.minimum(hi_c[first], hi_i[first]))
+        # the intersection is strictly tighter than pure CROWN somewhere in these nets
+        assert any(bool((hi_x[z] < hi_c[z] - 1e-9).any() or (lo_x[z] > lo_c[z] + 1e-9).any()) for z in zs)
+        wl.intermediate = "crown+ibp"
+        _check_sound(wl, crown_bounds(wl), n=20000, seed=seed)
+    wl = wk.cnn(2, 0.05, 93, convs=((3, 1), (4, 2)), fcs=(6, 4), in_shape=(2, 4, 4), intermediate="crown+ibp")
     _check_sound(wl, crown_bounds(wl), n=20000)
 
 
