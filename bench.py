@@ -62,6 +62,43 @@ def _identity_consumers(nodes, z):
     return set()
 
 
+def _footprint_macs(nodes, z, stop):
+    """Multiply-adds of the identity rows over conv node z (one row per neuron, both
+    signs counted by the caller) when each row is carried on its footprint window
+    through a conv -> ReLU -> conv chain down to `stop`: at every conv only the
+    output cells inside both the row's window and the image count.  None if the
+    back-substitution from z is not such a chain."""
+    nd = nodes[z]
+    if nd.op != "conv":
+        return None
+    c_z, h_z, w_z = nd.shape
+    total = 0.0
+    k, wh, ww, sy, oy, sx, ox = z, 1, 1, 1, 0, 1, 0
+    while True:
+        nk = nodes[k]
+        if nk.op != "conv":
+            return None
+        co, ci, kh, kw = nk.weight.shape
+        _, ho, wo = nk.shape
+        # cells of k's output window that exist, summed over the start node's pixels
+        ys = np.arange(h_z)[:, None] * sy + oy + np.arange(wh)[None, :]
+        xs = np.arange(w_z)[:, None] * sx + ox + np.arange(ww)[None, :]
+        ny = ((ys >= 0) & (ys < ho)).sum(1)
+        nx = ((xs >= 0) & (xs < wo)).sum(1)
+        cells = float(ny.sum()) * float(nx.sum())      # sum over (py, px) of ny[py] * nx[px]
+        if k != z:   # the first step is a copy of the weight footprint: free
+            total += c_z * cells * co * ci * kh * kw
+        t = nk.inputs[0]
+        wh, ww = (wh - 1) * nk.stride + kh, (ww - 1) * nk.stride + kw
+        sy, oy = sy * nk.stride, oy * nk.stride - nk.pad
+        sx, ox = sx * nk.stride, ox * nk.stride - nk.pad
+        if t == stop:
+            return total
+        if nodes[t].op != "relu":
+            return None
+        k = nodes[t].inputs[0]
+
+
 def algorithmic_flops(wl):
     """FLOPs the method itself performs for the whole batch (no padding, no tile waste):
     2 * rows * multiply-adds of each affine node a row of Lambda passes through; the
@@ -85,6 +122,11 @@ def algorithmic_flops(wl):
             if z <= stop or (zn.op in ("linear", "conv") and _src(nodes, zn.inputs[0]) == stop):
                 continue
             rows = 2 * zn.size * B
+            fp = _footprint_macs(nodes, z, stop)
+            if fp is not None:
+                # rows on footprint windows: count only the cells that exist
+                total["intermediate"] += 2 * 2 * B * fp
+                continue
             free = _identity_consumers(nodes, z)
             for k in _active(nodes, z, stop):
                 if nodes[k].op not in ("linear", "conv") or k in free:
@@ -240,6 +282,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-hbm", action="store_true", help="skip the memory-bound kernel measurements")
+    ap.add_argument("--intermediate", default=None,
+                    help="override the workload's intermediate-bound method (ibp, crown, hybrid, crown+ibp, ...)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -256,6 +300,9 @@ def main():
     import linear_bound_propagation_amd as lbp
 
     wl = wk.config(args.workload)
+    if args.intermediate:
+        wl.intermediate = args.intermediate
+        wl.name += "_" + args.intermediate.replace("+", "_")
     print(f"[bench] workload {wl.name}: building device copies", file=sys.stderr, flush=True)
     net, x, C = lbp.prepare(wl, "cuda:0")
     lo, hi = net.alloc_bounds(wl.batch)

@@ -378,6 +378,149 @@ vb_status run_gemm_reduce(Backward& B, GemmDesc& d, int rows, int P, bool reduce
   return VB_OK;
 }
 
+// ---- footprint (patch) back-substitution of identity rows through a chain
+// conv -> ReLU -> conv ... down to the domain.  Every row is one neuron
+// (b, sign, c) at pixel p of the start node; its Lambda over each earlier node
+// is non-zero only on the window of pixels that neuron depends on, so Lambda
+// is kept on that window (the same size for every p, not clipped at the image
+// border: cells outside the node hold zeros).  Returns false if the call does
+// not have that shape or the window would not be smaller than the node.
+struct PatchStep {
+  int k;          // conv node whose Lambda (over its output window) is pushed
+  int t;          // its input node (ReLU output or the domain node)
+  int wh, ww;     // window of t
+  int sy, oy, sx, ox;  // pixel of t for cell (Y, X) of row p = (py, px): py*sy + oy + Y
+};
+
+bool patch_chain(const Backward& B, const BwdCall& c, std::vector<PatchStep>& steps) {
+  const Graph& G = B.G;
+  steps.clear();
+  if (c.C || B.a_out || B.alpha || B.psi_keep) return false;
+  const NodeInfo& S = G.n[c.start];
+  if (S.op != VB_CONV2D || S.cons.empty()) return false;
+  int k = c.start;
+  int wh = 1, ww = 1, sy = 1, oy = 0, sx = 1, ox = 0;  // the start node's own 1 x 1 window
+  bool smaller = false;
+  for (;;) {
+    const NodeInfo& nd = G.n[k];
+    if (nd.op != VB_CONV2D) return false;
+    const int t = nd.in0;
+    const NodeInfo& tn = G.n[t];
+    PatchStep ps;
+    ps.k = k;
+    ps.t = t;
+    ps.wh = (wh - 1) * nd.stride + nd.kh;
+    ps.ww = (ww - 1) * nd.stride + nd.kw;
+    ps.sy = sy * nd.stride;
+    ps.oy = oy * nd.stride - nd.pad;
+    ps.sx = sx * nd.stride;
+    ps.ox = ox * nd.stride - nd.pad;
+    if (tn.h <= 1 && tn.w <= 1) return false;
+    if (nd.kh < nd.stride || nd.kw < nd.stride) return false;  // window cells no tap reaches
+    if (ps.wh > tn.h || ps.ww > tn.w) return false;  // window no smaller than the node
+    if (ps.wh < tn.h || ps.ww < tn.w) smaller = true;
+    steps.push_back(ps);
+    if (t == c.stop) break;
+    if (t < c.stop || tn.op != VB_RELU || tn.cons.size() != 1) return false;
+    const int z = tn.in0;
+    if (z <= c.stop || G.n[z].op != VB_CONV2D || G.n[z].cons.size() != 1) return false;
+    k = z;
+    wh = ps.wh;
+    ww = ps.ww;
+    sy = ps.sy;
+    oy = ps.oy;
+    sx = ps.sx;
+    ox = ps.ox;
+  }
+  return smaller;
+}
+
+vb_status backward_chunk_patch(Backward& B, const BwdCall& c, long long R, const std::vector<PatchStep>& steps) {
+  const Graph& G = B.G;
+  const NodeInfo& S = G.n[c.start];
+  const int rows = (int)(c.cb * R);
+  for (int i = 0; i < NPOOL; ++i) B.refs[i] = 0;
+  // beta starts at +-bias of the start node; Lambda over its own 1 x 1 window is +-e_c
+  const float* bias = nullptr;
+  vb_status s = effective_bias(B, G, c.start, bias);
+  if (s) return s;
+  HIPCHK(launch_identity_bias(c.cb, (int)S.size, bias, S.c, B.rowacc, B.st));
+  int cur = B.alloc();
+  if (cur < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted");
+  HIPCHK(launch_patch_identity(rows, (int)R, S.c, B.pool[cur], B.st));
+  int wh = 1, ww = 1;
+  for (const PatchStep& ps : steps) {
+    const NodeInfo& nd = G.n[ps.k];
+    const NodeInfo& tn = G.n[ps.t];
+    const bool last = ps.t == c.stop;
+    const int z = last ? -1 : tn.in0;
+    int outb = -1;
+    const float* bias_z = nullptr;
+    if (!last) {
+      outb = B.alloc();
+      if (outb < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted");
+      s = effective_bias(B, G, z, bias_z);
+      if (s) return s;
+      HIPCHK(launch_relax_coef(B.lo[z] + (long long)c.b0 * G.n[z].size, B.hi[z] + (long long)c.b0 * G.n[z].size,
+                               (long long)c.cb * G.n[z].size, B.coef, B.st));
+    }
+    // the conv as a transposed conv between windows: output window wh x ww of k,
+    // input window ps.wh x ps.ww of t, no padding (the window covers every tap)
+    NodeInfo nv = nd, tv = tn;
+    nv.h = wh;
+    nv.w = ww;
+    nv.pad = 0;
+    nv.size = (long long)wh * ww * nd.c;
+    tv.h = ps.wh;
+    tv.w = ps.ww;
+    tv.size = (long long)ps.wh * ps.ww * tn.c;
+    for (int py = 0; py < nd.stride; ++py)
+      for (int px = 0; px < nd.stride; ++px) {
+        GemmDesc d;
+        if (!conv_backward(nv, tv, B.pool[cur], rows, py, px, d)) continue;
+        if (d.K == 0) continue;  // (excluded by patch_chain: kh, kw >= stride)
+        d.B = B.wt[ps.k];
+        d.coef = B.coef;
+        d.rows_per_b = (int)R;
+        d.patch = 1;
+        d.pc = S.c;
+        d.pgh = S.h;
+        d.pgw = S.w;
+        d.psy = ps.sy;
+        d.poy = ps.oy;
+        d.psx = ps.sx;
+        d.pox = ps.ox;
+        d.img_h = tn.h;
+        d.img_w = tn.w;
+        if (last) {
+          d.epi = E_CONCRETIZE;
+          if (c.stop == 0) {
+            d.center = B.dom.xc + (long long)c.b0 * G.n[0].size;
+            d.radius = B.dom.xr ? B.dom.xr + (long long)c.b0 * G.n[0].size : nullptr;
+            d.eps = B.dom.eps;
+          } else {
+            d.center = B.box_c;
+            d.radius = B.box_r;
+          }
+        } else {
+          d.epi = E_RELAX;
+          d.out = B.pool[outb];
+          d.bias = bias_z;
+          d.bias_c = tn.c;
+        }
+        // (profiled work: the GEMM's own multiply-adds, except the first step from
+        // the identity rows, which is a copy of the weight footprint)
+        s = run_gemm_reduce(B, d, rows, d.gh * d.gw, true, ps.k == c.start ? 0.0 : 2.0 * d.M * d.N * d.K);
+        if (s) return s;
+      }
+    B.release(cur);
+    cur = outb;
+    wh = ps.wh;
+    ww = ps.ww;
+  }
+  return VB_OK;
+}
+
 // Execute the back-substitution of call `c`; rowacc receives the lower bound
 // of every row (rows = cb * R).  Lambda of a node is a pool buffer, or IDENT:
 // the implicit +-I over the start node (identity rows), which Linear and Conv
@@ -385,6 +528,10 @@ vb_status run_gemm_reduce(Backward& B, GemmDesc& d, int rows, int P, bool reduce
 constexpr int IDENT = -2;
 
 vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
+  {
+    std::vector<PatchStep> steps;
+    if (patch_chain(B, c, steps)) return backward_chunk_patch(B, c, R, steps);
+  }
   const Graph& G = B.G;
   const int N = (int)G.n.size();
   const int rows = (int)(c.cb * R);

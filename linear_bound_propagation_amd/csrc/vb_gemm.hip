@@ -415,11 +415,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
 #pragma unroll
     for (int v0 = 0; v0 < 16; v0 += G) {
       long long opos[G], bpos[G];
-      bool mok[G];
+      bool mok[G], pin[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const int v = v0 + g;
         const int m = m0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+        pin[g] = true;
         if (DENSE) {
           mok[g] = m < d.M;
           const int mm = mok[g] ? m : 0;
@@ -430,9 +431,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
           mok[g] = gp.valid;
           const int Y = fdiv(gp.q, d.div_gw);
           const int X = gp.q - Y * d.gw;
-          const long long sp = (long long)(Y * d.oym + d.oy0) * d.wo + (X * d.oxm + d.ox0);
+          const int cy = Y * d.oym + d.oy0, cx = X * d.oxm + d.ox0;
+          const long long sp = (long long)cy * d.wo + cx;
           opos[g] = (long long)gp.row * d.ho * d.wo + sp;
-          bpos[g] = (long long)fdiv(gp.row, d.div_rows) * d.ho * d.wo + sp;
+          const long long b = fdiv(gp.row, d.div_rows);
+          if (d.patch) {
+            // window cell -> pixel of the target node for the row's own position
+            const int t1 = fdiv(gp.row, d.div_pc);
+            const int pz = t1 - fdiv(t1, d.div_pz) * d.div_pz.d;
+            const int py = fdiv(pz, d.div_pw), px = pz - py * d.pgw;
+            const int ay = py * d.psy + d.poy + cy, ax = px * d.psx + d.pox + cx;
+            pin[g] = ay >= 0 && ay < d.img_h && ax >= 0 && ax < d.img_w;
+            bpos[g] = b * d.img_h * d.img_w + (pin[g] ? (long long)ay * d.img_w + ax : 0);
+          } else {
+            bpos[g] = b * d.ho * d.wo + sp;
+          }
         }
       }
       float rowsum[G];
@@ -502,7 +515,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
         } else if (EPI == E_RELAX) {
           float4 cf[G];
 #pragma unroll
-          for (int g = 0; g < G; ++g) cf[g] = d.coef[bi[g]];
+          for (int g = 0; g < G; ++g) {
+            cf[g] = d.coef[bi[g]];
+            if (!pin[g]) cf[g] = make_float4(0.f, 0.f, 0.f, 0.f);  // outside the node: no neuron
+          }
           // slope of the lower relaxation: the optimised alpha on unstable
           // neurons when one is given, else the adaptive choice
           float al[G];
@@ -571,6 +587,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
           } else {
 #pragma unroll
             for (int g = 0; g < G; ++g) r[g] = d.eps;  // L-infinity ball of one radius
+          }
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            if (!pin[g]) {  // a window cell outside the domain node: no input there
+              c[g] = 0.f;
+              r[g] = 0.f;
+            }
           }
 #pragma unroll
           for (int g = 0; g < G; ++g) {
@@ -690,6 +713,11 @@ bool finalize(GemmDesc& d) {
   d.div_gw = make_fastdiv(d.gw);
   d.div_rows = make_fastdiv(d.rows_per_b);
   d.div_nrows = make_fastdiv(d.M / (d.gh * d.gw));
+  if (d.patch) {
+    d.div_pc = make_fastdiv(d.pc);
+    d.div_pz = make_fastdiv(d.pgh * d.pgw);
+    d.div_pw = make_fastdiv(d.pgw);
+  }
   d.Mt = d.M;
   d.rb_shift = 0;
   if (!gemm_is_dense(d)) {

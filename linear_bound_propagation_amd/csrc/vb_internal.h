@@ -76,6 +76,15 @@ struct GemmDesc {
   int ho, wo, oym, oy0, oxm, ox0;
   int rows_per_b;              // batch element of a row = row / rows_per_b
   FastDiv div_p, div_gw, div_rows, div_nrows;  // filled by launch_gemm: gh*gw, gw, rows_per_b, M/(gh*gw)
+  // ---- footprint (patch) mode of a gather GEMM: the rows are identity rows
+  //      (b, sign, p, c) over a node of pgh x pgw pixels and pc channels, and
+  //      Lambda lives on a window of the target node: output cell (Y, X) of
+  //      row p = (py, px) is the target's pixel (py*psy + poy + Y, px*psx +
+  //      pox + X) of an img_h x img_w grid.  Cells outside that grid take no
+  //      relaxation (zero) and no domain.
+  int patch;
+  FastDiv div_pc, div_pz, div_pw;  // filled by launch_gemm: pc, pgh*pgw, pgw
+  int pc, pgh, pgw, psy, poy, psx, pox, img_h, img_w;
   int Mt;                      // filled by launch_gemm: size of the tile index space (gather: padded)
   int rb_shift;                // filled by launch_gemm: log2 of the rows per block (gather)
   // ---- epilogue
@@ -192,6 +201,10 @@ struct Col2Im {
   float eps;
 };
 hipError_t launch_col2im(const Col2Im& a, int rows, float* rowacc, hipStream_t st);
+
+// Identity rows over a node of C channels, each on its own 1 x 1 window:
+// out [rows][C] with out[row][c'] = +-1 at c' = row's channel (rows_per_b = R).
+hipError_t launch_patch_identity(int rows, int R, int C, float* out, hipStream_t st);
 
 // rowacc[b*2n + r] = s * bias[i % bias_c] for identity rows (s = +1 for r < n, -1 after; i = r mod n)
 hipError_t launch_identity_bias(int batch, int n, const float* bias, int bias_c, float* rowacc, hipStream_t st);

@@ -299,6 +299,28 @@ hipError_t launch_col2im(const Col2Im& a, int rows, float* rowacc, hipStream_t s
   return hipGetLastError();
 }
 
+// Identity rows (b, sign, p, c) over a node of P pixels and C channels, on
+// each row's own 1 x 1 window: out[row][c'] = sign if c' == c else 0.
+__global__ void patch_identity_kernel(long long rows, int R, int C, float* __restrict__ out) {
+  const long long total = rows * C;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (long long)gridDim.x * blockDim.x) {
+    const long long row = e / C;
+    const int cc = (int)(e - row * C);
+    const int r = (int)(row % R);
+    const float sg = r < R / 2 ? 1.f : -1.f;
+    out[e] = (r % C == cc) ? sg : 0.f;
+  }
+}
+
+hipError_t launch_patch_identity(int rows, int R, int C, float* out, hipStream_t st) {
+  const long long total = (long long)rows * C;
+  if (total <= 0) return hipSuccess;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(patch_identity_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (long long)rows, R, C, out);
+  return hipGetLastError();
+}
+
 __global__ void identity_bias_kernel(int batch, int n, const float* __restrict__ bias, int bias_c,
                                      float* __restrict__ rowacc) {
   const long long total = (long long)batch * 2 * n;

@@ -3,7 +3,7 @@ import pytest
 import torch
 
 import workloads as wk
-from helpers import compare_workload, ensure_built
+from helpers import assert_close, compare_workload, ensure_built
 from oracle import crown_bounds
 
 pytestmark = pytest.mark.gpu
@@ -48,3 +48,52 @@ def test_config3_full_size_sampled_inputs(lbp):
     ref = crown_bounds(wl, batch_idx=idx)
     compare_workload(wl, out, ref, batch_idx=idx)
     assert bool((out["lb"] <= out["ub"]).all())
+
+
+def test_config3_crown_intermediates_sampled_rows(lbp):
+    """The CNN of the measured configuration with CROWN intermediate bounds (each
+    conv-output neuron's rows on its footprint window): for 40 sampled neurons of
+    every CROWN-refined layer, the oracle's back-substitution over the same (GPU,
+    fp32) bounds of the earlier layers gives the same bounds."""
+    import numpy as np
+    from helpers import nhwc
+    from oracle import Oracle, backward
+    wl = wk.config(3, batch=2)
+    wl.intermediate = "crown"
+    out = _run(lbp, wl)
+    on = Oracle(wl.nodes)
+    lo = [None] + [torch.as_tensor(np.zeros((wl.batch,) + tuple(nd.shape))) for nd in wl.nodes[1:]]
+    hi = [None] + [torch.as_tensor(np.zeros((wl.batch,) + tuple(nd.shape))) for nd in wl.nodes[1:]]
+    for k, nd in enumerate(wl.nodes):
+        if k == 0 or nd.op == "flatten":
+            continue
+        g_lo = out["lo"][k].double().cpu().numpy()
+        g_hi = out["hi"][k].double().cpu().numpy()
+        if len(nd.shape) == 3:
+            c, h, w = nd.shape
+            g_lo = g_lo.reshape(wl.batch, h, w, c).transpose(0, 3, 1, 2)
+            g_hi = g_hi.reshape(wl.batch, h, w, c).transpose(0, 3, 1, 2)
+        lo[k] = torch.as_tensor(g_lo.reshape((wl.batch,) + tuple(nd.shape)).copy())
+        hi[k] = torch.as_tensor(g_hi.reshape((wl.batch,) + tuple(nd.shape)).copy())
+    rng = np.random.default_rng(3)
+    relu_in = [nd.inputs[0] for nd in wl.nodes if nd.op == "relu"]
+    b = 1
+    c0 = torch.as_tensor(wl.x0[b].astype(np.float64))
+    r0 = torch.full_like(c0, float(np.float32(wl.eps)))
+    for z in relu_in[1:]:
+        nd = wl.nodes[z]
+        if nd.op != "conv":
+            continue
+        n = nd.size
+        idx = rng.choice(n, 40, replace=False)
+        rows = torch.zeros((80, n), dtype=torch.float64)
+        rows[np.arange(40), idx] = 1.0
+        rows[40 + np.arange(40), idx] = -1.0
+        ref = backward(on, lo, hi, b, z, rows.reshape((80,) + tuple(nd.shape)), 0, c0, r0)
+        c, h, w = nd.shape
+        # sampled neuron (c, y, x) in NCHW order -> its channels-last position
+        cc, yy, xx = np.unravel_index(idx, (c, h, w))
+        pos = (yy * w + xx) * c + cc
+        print(f"node {z}: {nd.shape}", flush=True)
+        assert_close(out["lo"][z][b][pos], ref[:40], f"lo[{z}] sampled")
+        assert_close(out["hi"][z][b][pos], -ref[40:], f"hi[{z}] sampled")
