@@ -464,6 +464,60 @@ vb_status backward_chunk_patch(Backward& B, const BwdCall& c, long long R, const
       HIPCHK(launch_relax_coef(B.lo[z] + (long long)c.b0 * G.n[z].size, B.hi[z] + (long long)c.b0 * G.n[z].size,
                                (long long)c.cb * G.n[z].size, B.coef, B.st));
     }
+    if (last && tn.c <= 8 && nd.kh * nd.kw * tn.c <= 64 &&
+        (size_t)rows * wh * ww * nd.kh * nd.kw * tn.c <= B.pool_floats) {
+      // few domain channels: Q = Lambda . W over (tap, c_in) columns as a dense
+      // GEMM, then the taps are summed per window cell and concretised
+      const int qb = B.alloc();
+      if (qb < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted");
+      GemmDesc d = base_desc();
+      d.M = rows * wh * ww;
+      d.K = nd.c;
+      d.N = nd.kh * nd.kw * tn.c;
+      d.cs = d.K;
+      d.a_row_stride = d.K;
+      d.A = B.pool[cur];
+      d.B = B.wt[ps.k];
+      d.epi = E_STORE;
+      d.out = B.pool[qb];
+      s = run_gemm_reduce(B, d, rows, 1, false, 2.0 * d.M * d.N * d.K);
+      if (s) return s;
+      Col2Im a{};
+      a.Q = B.pool[qb];
+      a.Ho = wh;
+      a.Wo = ww;
+      a.Ci = tn.c;
+      a.Hi = ps.wh;
+      a.Wi = ps.ww;
+      a.kh = nd.kh;
+      a.kw = nd.kw;
+      a.stride = nd.stride;
+      a.pad = 0;
+      a.rows_per_b = (int)R;
+      a.mode = E_CONCRETIZE;
+      if (c.stop == 0) {
+        a.center = B.dom.xc + (long long)c.b0 * G.n[0].size;
+        a.radius = B.dom.xr ? B.dom.xr + (long long)c.b0 * G.n[0].size : nullptr;
+        a.eps = B.dom.eps;
+      } else {
+        a.center = B.box_c;
+        a.radius = B.box_r;
+      }
+      a.patch = 1;
+      a.pc = S.c;
+      a.pgh = S.h;
+      a.pgw = S.w;
+      a.psy = ps.sy;
+      a.poy = ps.oy;
+      a.psx = ps.sx;
+      a.pox = ps.ox;
+      a.img_h = tn.h;
+      a.img_w = tn.w;
+      HIPCHK(launch_col2im(a, rows, B.rowacc, B.st));
+      B.release(qb);
+      B.release(cur);
+      break;
+    }
     // the conv as a transposed conv between windows: output window wh x ww of k,
     // input window ps.wh x ps.ww of t, no padding (the window covers every tap)
     NodeInfo nv = nd, tv = tn;

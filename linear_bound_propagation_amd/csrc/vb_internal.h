@@ -199,6 +199,10 @@ struct Col2Im {
   const float* center;
   const float* radius;
   float eps;
+  // footprint windows (concretisation only): Hi x Wi is the row's window of an
+  // img_h x img_w domain node; cell (y, x) of row p = (py, px) of a pgh x pgw
+  // start node with pc channels is pixel (py*psy + poy + y, px*psx + pox + x)
+  int patch, pc, pgh, pgw, psy, poy, psx, pox, img_h, img_w;
 };
 hipError_t launch_col2im(const Col2Im& a, int rows, float* rowacc, hipStream_t st);
 

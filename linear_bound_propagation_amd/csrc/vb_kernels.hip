@@ -283,6 +283,17 @@ __global__ __launch_bounds__(256) void col2im_kernel(const Col2Im a, float* __re
       a.out[row * L + e] = o;
       if (a.bias) s += o * a.bias[ci];
       s += fminf(v, 0.f) * t;
+    } else if (a.patch) {
+      // window cell -> pixel of the domain node for this row's position
+      const long long pz = (row / a.pc) % ((long long)a.pgh * a.pgw);
+      const int py = (int)(pz / a.pgw), px = (int)(pz % a.pgw);
+      const int ay = py * a.psy + a.poy + y, ax = px * a.psx + a.pox + x;
+      if (ay >= 0 && ay < a.img_h && ax >= 0 && ax < a.img_w) {
+        const long long ei = (b * a.img_h * a.img_w + (long long)ay * a.img_w + ax) * a.Ci + ci;
+        const float c = a.center[ei];
+        const float r = a.radius ? a.radius[ei] : a.eps;
+        s += v * c - fabsf(v) * r;
+      }
     } else {
       const float c = a.center[b * L + e];
       const float r = a.radius ? a.radius[b * L + e] : a.eps;
