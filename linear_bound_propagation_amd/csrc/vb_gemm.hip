@@ -170,7 +170,7 @@ __device__ __forceinline__ void a_val4(const GemmDesc& d, long long off, float4&
 
 }  // namespace
 
-template <int BM, int BN, int WM, int WN, bool DENSE, int AMODE, int EPI, bool FAST>
+template <int BM, int BN, int WM, int WN, bool DENSE, int AMODE, int EPI, bool FAST, bool PATCH = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   constexpr int NTHR = WM * WN * 64;
   constexpr int NA = (AMODE == A_PLAIN) ? 1 : 2;
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
           const long long sp = (long long)cy * d.wo + cx;
           opos[g] = (long long)gp.row * d.ho * d.wo + sp;
           const long long b = fdiv(gp.row, d.div_rows);
-          if (d.patch) {
+          if (PATCH) {
             // window cell -> pixel of the target node for the row's own position
             const int t1 = fdiv(gp.row, d.div_pc);
             const int pz = t1 - fdiv(t1, d.div_pz) * d.div_pz.d;
@@ -652,10 +652,16 @@ hipError_t launch_tile(const GemmDesc& d, hipStream_t st) {
       hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_STORE, FAST>), g, b, 0, st, d);
       break;
     case E_RELAX:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_RELAX, FAST>), g, b, 0, st, d);
+      if (!DENSE && d.patch)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_RELAX, FAST, !DENSE>), g, b, 0, st, d);
+      else
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_RELAX, FAST>), g, b, 0, st, d);
       break;
     case E_CONCRETIZE:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_CONCRETIZE, FAST>), g, b, 0, st, d);
+      if (!DENSE && d.patch)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_CONCRETIZE, FAST, !DENSE>), g, b, 0, st, d);
+      else
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_CONCRETIZE, FAST>), g, b, 0, st, d);
       break;
     case E_ADJOINT:
       hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_ADJOINT, FAST>), g, b, 0, st, d);
@@ -682,7 +688,7 @@ hipError_t launch_shape(const GemmDesc& d, bool dense, bool fast, hipStream_t st
 // GEMMs with the fast path, when the grid still has at least two workgroups per CU
 // (dense GEMMs ran faster on two 128 x 128 workgroups per CU).
 bool use_big(const GemmDesc& d, bool fast) {
-  if (!fast || d.epi == E_IBP || d.N < 256 || gemm_is_dense(d)) return false;
+  if (!fast || d.epi == E_IBP || d.N < 256 || gemm_is_dense(d) || d.patch) return false;
   const long long tiles = (long long)((d.Mt + 255) / 256) * ((d.N + 255) / 256);
   return tiles >= 512;
 }
