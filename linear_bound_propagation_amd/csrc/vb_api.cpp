@@ -392,13 +392,11 @@ struct PatchStep {
   int sy, oy, sx, ox;  // pixel of t for cell (Y, X) of row p = (py, px): py*sy + oy + Y
 };
 
-bool patch_chain(const Backward& B, const BwdCall& c, std::vector<PatchStep>& steps) {
-  const Graph& G = B.G;
+bool patch_chain_graph(const Graph& G, int start, int stop, std::vector<PatchStep>& steps) {
   steps.clear();
-  if (c.C || B.a_out || B.alpha || B.psi_keep) return false;
-  const NodeInfo& S = G.n[c.start];
+  const NodeInfo& S = G.n[start];
   if (S.op != VB_CONV2D || S.cons.empty()) return false;
-  int k = c.start;
+  int k = start;
   int wh = 1, ww = 1, sy = 1, oy = 0, sx = 1, ox = 0;  // the start node's own 1 x 1 window
   bool smaller = false;
   for (;;) {
@@ -420,10 +418,10 @@ bool patch_chain(const Backward& B, const BwdCall& c, std::vector<PatchStep>& st
     if (ps.wh > tn.h || ps.ww > tn.w) return false;  // window no smaller than the node
     if (ps.wh < tn.h || ps.ww < tn.w) smaller = true;
     steps.push_back(ps);
-    if (t == c.stop) break;
-    if (t < c.stop || tn.op != VB_RELU || tn.cons.size() != 1) return false;
+    if (t == stop) break;
+    if (t < stop || tn.op != VB_RELU || tn.cons.size() != 1) return false;
     const int z = tn.in0;
-    if (z <= c.stop || G.n[z].op != VB_CONV2D || G.n[z].cons.size() != 1) return false;
+    if (z <= stop || G.n[z].op != VB_CONV2D || G.n[z].cons.size() != 1) return false;
     k = z;
     wh = ps.wh;
     ww = ps.ww;
@@ -433,6 +431,34 @@ bool patch_chain(const Backward& B, const BwdCall& c, std::vector<PatchStep>& st
     ox = ps.ox;
   }
   return smaller;
+}
+
+bool patch_chain(const Backward& B, const BwdCall& c, std::vector<PatchStep>& steps) {
+  steps.clear();
+  if (c.C || B.a_out || B.alpha || B.psi_keep) return false;
+  return patch_chain_graph(B.G, c.start, c.stop, steps);
+}
+
+// Per batch element: widest Lambda (floats per row) and partial sums of a
+// footprint back-substitution of R identity rows; false if it does not apply.
+bool patch_requirements(const Graph& G, int start, int stop, long long R, long long& maxw, long long& part_per_b) {
+  std::vector<PatchStep> steps;
+  if (!patch_chain_graph(G, start, stop, steps)) return false;
+  maxw = G.n[start].c;  // the 1 x 1 windows of the identity rows
+  part_per_b = 0;
+  int wh = 1, ww = 1;
+  for (const PatchStep& ps : steps) {
+    const NodeInfo& nd = G.n[ps.k];
+    const NodeInfo& tn = G.n[ps.t];
+    maxw = std::max(maxw, (long long)ps.wh * ps.ww * tn.c);
+    if (ps.t == stop && tn.c <= 8 && nd.kh * nd.kw * tn.c <= 64)
+      maxw = std::max(maxw, (long long)wh * ww * nd.kh * nd.kw * tn.c);  // tap-expanded product
+    const int bn = tn.c > 64 ? 128 : (tn.c > 32 ? 64 : 32);
+    part_per_b = std::max(part_per_b, R * ps.wh * ps.ww * ((tn.c + bn - 1) / bn));
+    wh = ps.wh;
+    ww = ps.ww;
+  }
+  return true;
 }
 
 vb_status backward_chunk_patch(Backward& B, const BwdCall& c, long long R, const std::vector<PatchStep>& steps) {
@@ -1123,7 +1149,8 @@ template <class After>
 vb_status backward_all(Backward& B, int start, int stop, const float* C, int m, int split, int batch, long long R,
                        char* ws, size_t ws_bytes, size_t reserved_floats, After after) {
   long long maxw, ppb;
-  bwd_requirements(B.G, start, stop, R, maxw, ppb);
+  if (C || B.a_out || B.alpha || B.psi_keep || !patch_requirements(B.G, start, stop, R, maxw, ppb))
+    bwd_requirements(B.G, start, stop, R, maxw, ppb);
   if (C) maxw = std::max(maxw, B.G.n[start].size);
   const long long box = stop > 0 ? B.G.n[stop].size : 0;
   // GEMM index spaces are 32-bit: rows x pixels (padded to whole row blocks) per launch
@@ -1347,7 +1374,7 @@ static size_t crown_workspace(const Graph& G, int batch, int m, int method, int 
   size_t best = 0;
   auto consider = [&](int start, int stop, long long R, bool spec) {
     long long maxw, ppb;
-    bwd_requirements(G, start, stop, R, maxw, ppb);
+    if (spec || !patch_requirements(G, start, stop, R, maxw, ppb)) bwd_requirements(G, start, stop, R, maxw, ppb);
     if (spec) maxw = std::max(maxw, G.n[start].size);
     best = std::max(best, layout_for(maxw, ppb, R, batch, wt_floats(G), stop > 0 ? G.n[stop].size : 0).bytes);
   };
