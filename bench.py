@@ -282,6 +282,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-hbm", action="store_true", help="skip the memory-bound kernel measurements")
+    ap.add_argument("--dense-alpha", action="store_true",
+                    help="alpha-CROWN workloads: keep alpha for every neuron instead of the unstable ones only")
     ap.add_argument("--intermediate", default=None,
                     help="override the workload's intermediate-bound method (ibp, crown, hybrid, crown+ibp, ...)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -312,15 +314,26 @@ def main():
     ws_bytes = net.workspace_size(wl.batch, wl.m, wl.intermediate, wl.region_start or 0)
     free = torch.cuda.mem_get_info()[0]
     ws = net.workspace(min(ws_bytes, int(free * 0.85)))
+    alpha_info = {}
     if wl.alpha_steps:
-        state = lbp.alpha_state(net, wl.batch, wl.m)
         lb_steps = torch.empty(wl.alpha_steps + 1, wl.batch, wl.m, device=net.device)
         best = torch.empty(wl.batch, wl.m, device=net.device)
+        states = {}
 
         def step():
             lbp.crown(net, x, float(wl.eps), C, wl.intermediate, wl.region_start, ws=ws, out=out)
+            # compact alpha: the state of the unstable neurons only (the layout call
+            # synchronises the stream to size it; it is part of the timed step)
+            lay = None if args.dense_alpha else lbp.alpha_layout(net, out["lo"], out["hi"])
+            key = None if lay is None else tuple(lay.width)
+            if key not in states:
+                states[key] = lbp.alpha_state(net, wl.batch, wl.m, lay)
+            state = states[key]
+            alpha_info["alpha_storage"] = "dense" if lay is None else "compact (unstable neurons)"
+            alpha_info["alpha_adam_state_gb"] = round(sum(t.numel() * 4 for part in state for t in part
+                                                          if t is not None) / 1e9, 3)
             lbp.alpha_crown(net, x, float(wl.eps), C, out["lo"], out["hi"], wl.alpha_steps, wl.alpha_lr, ws=ws,
-                            state=state, lb_steps=lb_steps, best=best)
+                            state=state, lb_steps=lb_steps, best=best, layout=lay)
             out["lb"] = best
     else:
         def step():
@@ -365,7 +378,7 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "specs": wl.m, "eps": float(wl.eps),
                    "intermediate": wl.intermediate, "alpha_steps": wl.alpha_steps,
                    "algorithmic_tflop_per_step": round(fl["all"] / 1e12, 4),
-                   "workspace_gb": round(ws.numel() / 1e9, 2)},
+                   "workspace_gb": round(ws.numel() / 1e9, 2), **alpha_info},
         "frac_of_fp32_mfma_peak": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4),
         "specs_per_s": round(wl.batch * wl.m / (ms * 1e-3), 1),
         "verified_frac": verified,

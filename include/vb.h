@@ -107,6 +107,34 @@ vb_status vb_ibp(const vb_graph* g, int32_t batch,
                  const float* C, int32_t m, float* spec_lo, float* spec_hi,
                  void* ws, size_t ws_bytes, void* stream);
 
+/* Compact storage of the per-neuron alpha state (Sec. 3 and Sec. 4.3 of the
+ * page: the alpha slopes are the largest tensors of alpha-CROWN).  A slope is
+ * only ever read for an unstable neuron (l < 0 < u), so the state of ReLU node
+ * k can keep one column per unstable neuron: row r (batch element b = r / m)
+ * of alpha[k], adam_m[k], adam_v[k] then has width[k] entries and neuron j of b
+ * sits at column index[k][b][j] (-1 for a stable neuron, which has no entry).
+ *   index: per node (host array of device pointers); for ReLU node k,
+ *          [batch][size_k] int32, as written by vb_alpha_layout; others NULL.
+ *   width: per node (host array); for ReLU node k the row length U_k >= the
+ *          largest number of unstable neurons of any batch element.  A node
+ *          with width 0 has no state: its alpha / Adam pointers may be NULL.
+ * Columns past the count of a batch element are never read or written. */
+typedef struct {
+  const int32_t* const* index;
+  const int32_t* width;
+} vb_alpha_compact;
+
+/* The compact alpha layout of the bounds node_lo / node_hi (of the ReLU
+ * inputs): for every ReLU node k writes index[k] [batch][size_k] (device,
+ * caller-owned) with the rank of each unstable neuron among the unstable
+ * neurons of its batch element in node order, -1 for stable neurons, and
+ * width[k] (host) = the largest count over the batch; width[k] = 0 for other
+ * nodes.  ws must hold 4 * batch bytes.  This call SYNCHRONISES `stream` (the
+ * widths are needed on the host to size the state). */
+vb_status vb_alpha_layout(const vb_graph* g, int32_t batch, const float* const* node_lo,
+                          const float* const* node_hi, int32_t* const* index, int32_t* width,
+                          void* ws, size_t ws_bytes, void* stream);
+
 /* One CROWN back-substitution (Sec. 1: the A matrices; Sec. 2.1: slopes from
  * intermediate bounds).  Rows over node `start`:
  *   C == NULL: identity rows; writes node bounds lb = l_start, ub = u_start,
@@ -121,7 +149,8 @@ vb_status vb_ibp(const vb_graph* g, int32_t batch,
  * alpha: NULL, or per node (entries of ReLU nodes between stop and start
  * non-NULL) the lower slopes [batch][m][size] used on unstable neurons
  * (Sec. 3 and Sec. 4.3: per-neuron alpha); needs C and ub == NULL (the slopes
- * bound one side: call again with -C for the upper bound).
+ * bound one side: call again with -C for the upper bound).  compact: NULL, or
+ * the compact layout of alpha (vb_alpha_compact; needs alpha).
  * If A_out != NULL, the linear bounds over `stop` are returned as well: the
  * rows are the 2R functions (+rows, then -rows, R = m or size_start; only the
  * R rows C when ub == NULL with spec rows) bounded
@@ -133,7 +162,7 @@ vb_status vb_ibp(const vb_graph* g, int32_t batch,
 vb_status vb_crown_backward(const vb_graph* g, int32_t batch, int32_t start, int32_t stop,
                             const float* C, int32_t m,
                             const float* const* node_lo, const float* const* node_hi,
-                            const float* const* alpha,
+                            const vb_alpha_compact* compact, const float* const* alpha,
                             const float* x_center, const float* x_radius, float eps,
                             float* lb, float* ub, float* A_out, float* bias_out,
                             void* ws, size_t ws_bytes, void* stream);
@@ -152,16 +181,20 @@ vb_status vb_concretize(int32_t rows, int32_t n, int32_t rows_per_batch,
  * adaptive CROWN lower slope of each neuron from the bounds of the ReLU's
  * input (1 if u >= -l else 0 for unstable neurons; 1 active; 0 inactive),
  * identical for the m spec rows of an input, and adam_m[k], adam_v[k] are
- * zeroed.  Entries for non-ReLU nodes are ignored (may be NULL). */
+ * zeroed.  Entries for non-ReLU nodes are ignored (may be NULL).  compact:
+ * NULL (state [batch][m][size_k]), or the compact layout (vb_alpha_compact;
+ * only the unstable neurons' columns are written). */
 vb_status vb_alpha_init(const vb_graph* g, int32_t batch, int32_t m,
                         const float* const* node_lo, const float* const* node_hi,
+                        const vb_alpha_compact* compact,
                         float* const* alpha, float* const* adam_m, float* const* adam_v, void* stream);
 
 /* One alpha-CROWN step on the lower bounds of spec rows C [batch][m][n_out]
  * (Sec. 3 and Sec. 4.3 of the page: per-neuron alpha slope tensors).
  * alpha, adam_m, adam_v: per node, NULL except for ReLU nodes, each
  * [batch][m][size_k] (one lower slope per input, spec row and neuron; only the
- * unstable neurons' entries are read or changed).  Evaluates the CROWN lower
+ * unstable neurons' entries are read or changed), or in the compact layout
+ * when compact != NULL (vb_alpha_compact).  Evaluates the CROWN lower
  * bound with these slopes into lb_out [batch][m] and folds it into best_lb
  * (elementwise max; at step == 1 best_lb is set to lb; best_lb may be NULL).
  * If step >= 1, then also takes one
@@ -175,6 +208,7 @@ vb_status vb_alpha_init(const vb_graph* g, int32_t batch, int32_t m,
 vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float* C, int32_t m,
                         const float* const* node_lo, const float* const* node_hi,
                         const float* x_center, const float* x_radius, float eps,
+                        const vb_alpha_compact* compact,
                         float* const* alpha, float* const* adam_m, float* const* adam_v,
                         int32_t step, float lr, float beta1, float beta2, float adam_eps,
                         float* lb_out, float* best_lb,

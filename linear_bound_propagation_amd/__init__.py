@@ -30,7 +30,7 @@ _OPS = {"input": VB_INPUT, "linear": VB_LINEAR, "conv": VB_CONV2D, "relu": VB_RE
         "gap": VB_GAP, "flatten": VB_FLATTEN}
 
 EXPORTS = ["vb_last_error", "vb_workspace_size", "vb_ibp", "vb_crown_backward", "vb_concretize",
-           "vb_alpha_init", "vb_alpha_step", "vb_crown", "vb_profile_start", "vb_profile_stop"]
+           "vb_alpha_layout", "vb_alpha_init", "vb_alpha_step", "vb_crown", "vb_profile_start", "vb_profile_stop"]
 
 
 class vb_node(ctypes.Structure):
@@ -42,6 +42,10 @@ class vb_node(ctypes.Structure):
 
 class vb_graph(ctypes.Structure):
     _fields_ = [("n_nodes", ctypes.c_int32), ("nodes", ctypes.POINTER(vb_node))]
+
+
+class vb_alpha_compact(ctypes.Structure):
+    _fields_ = [("index", ctypes.POINTER(ctypes.c_void_p)), ("width", ctypes.POINTER(ctypes.c_int32))]
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -59,13 +63,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vb_ibp.restype = i32
     lib.vb_ibp.argtypes = [G, i32, P, P, f32, PP, PP, P, i32, P, P, P, sz, P]
     lib.vb_crown_backward.restype = i32
-    lib.vb_crown_backward.argtypes = [G, i32, i32, i32, P, i32, PP, PP, PP, P, P, f32, P, P, P, P, P, sz, P]
+    AC = ctypes.POINTER(vb_alpha_compact)
+    lib.vb_crown_backward.argtypes = [G, i32, i32, i32, P, i32, PP, PP, AC, PP, P, P, f32, P, P, P, P, P, sz, P]
     lib.vb_concretize.restype = i32
     lib.vb_concretize.argtypes = [i32, i32, i32, P, P, P, P, f32, P, P, P]
     lib.vb_alpha_init.restype = i32
-    lib.vb_alpha_init.argtypes = [G, i32, i32, PP, PP, PP, PP, PP, P]
+    lib.vb_alpha_layout.restype = i32
+    lib.vb_alpha_layout.argtypes = [G, i32, PP, PP, PP, ctypes.POINTER(i32), P, sz, P]
+    lib.vb_alpha_init.argtypes = [G, i32, i32, PP, PP, AC, PP, PP, PP, P]
     lib.vb_alpha_step.restype = i32
-    lib.vb_alpha_step.argtypes = [G, i32, P, i32, PP, PP, P, P, f32, PP, PP, PP, i32, f32, f32, f32, f32,
+    lib.vb_alpha_step.argtypes = [G, i32, P, i32, PP, PP, P, P, f32, AC, PP, PP, PP, i32, f32, f32, f32, f32,
                                   P, P, P, sz, P]
     lib.vb_crown.restype = i32
     lib.vb_crown.argtypes = [G, i32, P, P, f32, i32, i32, PP, PP, P, i32, P, P, P, P, P, sz, P]
@@ -210,9 +217,41 @@ def ibp(net: DeviceNet, x_center: torch.Tensor, eps: float, lo=None, hi=None, C:
     return lo, hi, spec_lo, spec_hi
 
 
+class AlphaLayout:
+    """Compact alpha layout (vb_alpha_layout): per node an int32 column map [batch][size]
+    (ReLU nodes; None elsewhere) and the row width of each node's state."""
+
+    def __init__(self, index, width):
+        self.index = index
+        self.width = list(width)
+        self._idx = _ptr_array(index)
+        self._w = (ctypes.c_int32 * len(self.width))(*self.width)
+        self._s = vb_alpha_compact(ctypes.cast(self._idx, ctypes.POINTER(ctypes.c_void_p)),
+                                   ctypes.cast(self._w, ctypes.POINTER(ctypes.c_int32)))
+
+    def ref(self):
+        return ctypes.byref(self._s)
+
+
+def _compact(layout: Optional[AlphaLayout]):
+    return None if layout is None else layout.ref()
+
+
+def alpha_layout(net: "DeviceNet", lo, hi) -> AlphaLayout:
+    """Columns of the unstable neurons of every ReLU node (synchronises the stream)."""
+    batch = lo[1].shape[0]
+    index = [torch.empty(batch, s, dtype=torch.int32, device=net.device) if op == "relu" else None
+             for op, s in zip(net.ops, net.sizes)]
+    width = (ctypes.c_int32 * len(index))()
+    ws = torch.empty(max(4 * batch, 256), dtype=torch.uint8, device=net.device)
+    _check(lib().vb_alpha_layout(net.gp, batch, _ptr_array(lo), _ptr_array(hi), _ptr_array(index), width,
+                                 _ptr(ws), ws.numel(), _stream()), "vb_alpha_layout")
+    return AlphaLayout(index, list(width))
+
+
 def crown_backward(net: DeviceNet, start: int, stop: int, lo, hi, x_center: torch.Tensor, eps: float,
                    ws: torch.Tensor, C: torch.Tensor = None, lb=None, ub=None, x_radius=None, linear=False,
-                   alpha=None, lower_only=False):
+                   alpha=None, lower_only=False, layout: Optional[AlphaLayout] = None):
     """lb, ub [batch][R] (ub None with lower_only or alpha: spec rows C only); with linear=True
     also (A, bias): the linear bounds over node `stop`, A [batch][rows][size_stop] and bias
     [batch][rows] (rows +r then -r, or only +r when one-sided, each bounded from below)."""
@@ -228,7 +267,8 @@ def crown_backward(net: DeviceNet, start: int, stop: int, lo, hi, x_center: torc
         A = torch.empty(batch, rows, net.sizes[stop], device=net.device)
         bias = torch.empty(batch, rows, device=net.device)
     _check(lib().vb_crown_backward(net.gp, batch, start, stop, _ptr(C), 0 if C is None else C.shape[1],
-                                  _ptr_array(lo), _ptr_array(hi), None if alpha is None else _ptr_array(alpha),
+                                  _ptr_array(lo), _ptr_array(hi), _compact(layout),
+                                  None if alpha is None else _ptr_array(alpha),
                                   _ptr(x_center), _ptr(x_radius), float(eps), _ptr(lb), _ptr(ub), _ptr(A),
                                   _ptr(bias), _ptr(ws), ws.numel(), _stream()),
            "vb_crown_backward")
@@ -266,25 +306,32 @@ def crown(net: DeviceNet, x_center: torch.Tensor, eps: float, C: torch.Tensor, m
     return out
 
 
-def alpha_state(net: DeviceNet, batch: int, m: int):
-    """Device tensors alpha, adam_m, adam_v per node ([batch][m][size] for ReLU nodes, None elsewhere)."""
-    mk = lambda: [torch.empty(batch, m, s, device=net.device) if op == "relu" else None
-                  for op, s in zip(net.ops, net.sizes)]
+def alpha_state(net: DeviceNet, batch: int, m: int, layout: Optional[AlphaLayout] = None):
+    """Device tensors alpha, adam_m, adam_v per node ([batch][m][size] for ReLU nodes, or
+    [batch][m][width] in a compact layout (None for width 0); None elsewhere)."""
+    def width(k, s):
+        return s if layout is None else layout.width[k]
+    mk = lambda: [torch.empty(batch, m, width(k, s), device=net.device)
+                  if op == "relu" and width(k, s) > 0 else None
+                  for k, (op, s) in enumerate(zip(net.ops, net.sizes))]
     return mk(), mk(), mk()
 
 
-def alpha_init(net: DeviceNet, lo, hi, alpha, adam_m, adam_v, m: int):
+def alpha_init(net: DeviceNet, lo, hi, alpha, adam_m, adam_v, m: int, layout: Optional[AlphaLayout] = None):
     batch = lo[1].shape[0]
-    _check(lib().vb_alpha_init(net.gp, batch, m, _ptr_array(lo), _ptr_array(hi), _ptr_array(alpha),
-                               _ptr_array(adam_m), _ptr_array(adam_v), _stream()), "vb_alpha_init")
+    _check(lib().vb_alpha_init(net.gp, batch, m, _ptr_array(lo), _ptr_array(hi), _compact(layout),
+                               _ptr_array(alpha), _ptr_array(adam_m), _ptr_array(adam_v), _stream()),
+           "vb_alpha_init")
 
 
 def alpha_step(net: DeviceNet, C: torch.Tensor, lo, hi, x_center: torch.Tensor, eps: float, alpha, adam_m, adam_v,
                step: int, lr: float, lb_out: torch.Tensor, best_lb: Optional[torch.Tensor], ws: torch.Tensor,
-               beta1: float = 0.9, beta2: float = 0.999, adam_eps: float = 1e-8, x_radius=None):
+               beta1: float = 0.9, beta2: float = 0.999, adam_eps: float = 1e-8, x_radius=None,
+               layout: Optional[AlphaLayout] = None):
     batch, m = C.shape[0], C.shape[1]
     _check(lib().vb_alpha_step(net.gp, batch, _ptr(C), m, _ptr_array(lo), _ptr_array(hi), _ptr(x_center),
-                              _ptr(x_radius), float(eps), _ptr_array(alpha), _ptr_array(adam_m), _ptr_array(adam_v),
+                              _ptr(x_radius), float(eps), _compact(layout), _ptr_array(alpha), _ptr_array(adam_m),
+                              _ptr_array(adam_v),
                               step, lr, beta1, beta2, adam_eps, _ptr(lb_out), _ptr(best_lb), _ptr(ws), ws.numel(),
                               _stream()), "vb_alpha_step")
     return lb_out
@@ -292,14 +339,15 @@ def alpha_step(net: DeviceNet, C: torch.Tensor, lo, hi, x_center: torch.Tensor, 
 
 def alpha_crown(net: DeviceNet, x_center: torch.Tensor, eps: float, C: torch.Tensor, lo, hi, steps: int,
                 lr: float, ws: torch.Tensor = None, state=None, lb_steps: torch.Tensor = None,
-                best: torch.Tensor = None, x_radius=None):
+                best: torch.Tensor = None, x_radius=None, layout: Optional[AlphaLayout] = None):
     """alpha-CROWN over fixed intermediate bounds lo/hi: vb_alpha_init, then `steps` calls of
     vb_alpha_step (evaluate, gradient, Adam ascent; the first sets `best`) and one
-    evaluation-only call.  steps must be >= 1.
+    evaluation-only call.  steps must be >= 1.  With a layout (alpha_layout) the state is
+    compact (unstable neurons only).
     Returns (best [B][m], lb per evaluation [steps+1][B][m], (alpha, adam_m, adam_v))."""
     batch, m = C.shape[0], C.shape[1]
     if state is None:
-        state = alpha_state(net, batch, m)
+        state = alpha_state(net, batch, m, layout)
     alpha, am, av = state
     if ws is None:
         ws = net.workspace(net.workspace_size(batch, m, "ibp"))
@@ -307,10 +355,12 @@ def alpha_crown(net: DeviceNet, x_center: torch.Tensor, eps: float, C: torch.Ten
         lb_steps = torch.empty(steps + 1, batch, m, device=net.device)
     if best is None:
         best = torch.empty(batch, m, device=net.device)
-    alpha_init(net, lo, hi, alpha, am, av, m)
+    alpha_init(net, lo, hi, alpha, am, av, m, layout=layout)
     for t in range(1, steps + 1):
-        alpha_step(net, C, lo, hi, x_center, eps, alpha, am, av, t, lr, lb_steps[t - 1], best, ws, x_radius=x_radius)
-    alpha_step(net, C, lo, hi, x_center, eps, alpha, am, av, 0, lr, lb_steps[steps], best, ws, x_radius=x_radius)
+        alpha_step(net, C, lo, hi, x_center, eps, alpha, am, av, t, lr, lb_steps[t - 1], best, ws, x_radius=x_radius,
+                   layout=layout)
+    alpha_step(net, C, lo, hi, x_center, eps, alpha, am, av, 0, lr, lb_steps[steps], best, ws, x_radius=x_radius,
+               layout=layout)
     return best, lb_steps, state
 
 

@@ -275,6 +275,10 @@ struct Backward {
   // alpha-CROWN extras (per node, may be NULL)
   const float* const* alpha = nullptr;
   float* const* psi_keep = nullptr;
+  // compact alpha / kept Psi of ReLU nodes: column map [batch][size] and row
+  // length per node (NULL: [batch][R][size])
+  const int* const* aidx = nullptr;
+  const int* awidth = nullptr;
   // K-contiguous weight copies for back-substitution, per node
   std::vector<const float*> wt;
   // bias a Lambda over each node carries into beta (ADD nodes: summed over inputs)
@@ -488,7 +492,7 @@ vb_status backward_chunk_patch(Backward& B, const BwdCall& c, long long R, const
       s = effective_bias(B, G, z, bias_z);
       if (s) return s;
       HIPCHK(launch_relax_coef(B.lo[z] + (long long)c.b0 * G.n[z].size, B.hi[z] + (long long)c.b0 * G.n[z].size,
-                               (long long)c.cb * G.n[z].size, B.coef, B.st));
+                               (long long)c.cb * G.n[z].size, nullptr, B.coef, B.st));
     }
     if (last && tn.c <= 8 && nd.kh * nd.kw * tn.c <= 64 &&
         (size_t)rows * wh * ww * nd.kh * nd.kw * tn.c <= B.pool_floats) {
@@ -637,13 +641,19 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
   }
   auto chunk_off = [&](int node) -> long long { return (long long)c.b0 * G.n[node].size; };
   // per-row tensors over a node (alpha, kept Psi: [batch][R][size]) for this chunk
-  auto row_off = [&](int node) -> long long { return (long long)c.b0 * R * G.n[node].size; };
+  // (compact ReLU state: rows of awidth[node] columns)
+  auto compact = [&](int node) { return B.aidx && G.n[node].op == VB_RELU; };
+  auto row_off = [&](int node) -> long long {
+    return (long long)c.b0 * R * (compact(node) ? (long long)B.awidth[node] : G.n[node].size);
+  };
   auto alpha_of = [&](int node) -> const float* {
     return (B.alpha && B.alpha[node]) ? B.alpha[node] + row_off(node) : nullptr;
   };
   auto psi_of = [&](int node) -> float* {
     return (B.psi_keep && B.psi_keep[node]) ? B.psi_keep[node] + row_off(node) : nullptr;
   };
+  auto aidx_of = [&](int node) -> const int* { return compact(node) ? B.aidx[node] + chunk_off(node) : nullptr; };
+  auto acols_of = [&](int node) -> int { return compact(node) ? B.awidth[node] : 0; };
   const NodeInfo& S = G.n[c.start];
   if (c.stop != 0)
     HIPCHK(launch_box_center_radius(B.lo[c.stop] + chunk_off(c.stop), B.hi[c.stop] + chunk_off(c.stop),
@@ -855,7 +865,7 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
         }
         if (epi == E_RELAX)
           HIPCHK(launch_relax_coef(B.lo[z] + chunk_off(z), B.hi[z] + chunk_off(z), (long long)c.cb * G.n[z].size,
-                                   B.coef, B.st));
+                                   aidx_of(t), B.coef, B.st));
         // output-parity classes that no tap reaches (a 1x1 stride-2 conv) contribute
         // nothing: with no bias term their positions keep the pending Lambda, or zero
         bool zero_first = false;
@@ -878,6 +888,8 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
             d.hi = B.hi[tgt_bounds] + chunk_off(tgt_bounds);
             d.alpha = alpha_of(t);
             d.psi_out = psi_of(t);
+            d.aidx = aidx_of(t);
+            d.acols = acols_of(t);
           }
           if (epi == E_CONCRETIZE) {
             d.psi_out = psi_of(t);
@@ -930,7 +942,8 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
       if (s) return s;
       const int P = nd.h * nd.w;
       HIPCHK(launch_relax(B.pool[cur], 0, 1.f, nullptr, rows, (int)R, P, nd.c, B.lo[z] + chunk_off(z),
-                          B.hi[z] + chunk_off(z), bias_z, alpha_of(k), psi_of(k), B.pool[outb], B.rowacc, B.st));
+                          B.hi[z] + chunk_off(z), bias_z, alpha_of(k), psi_of(k), aidx_of(k), acols_of(k),
+                          B.pool[outb], B.rowacc, B.st));
       B.release(cur);
       lam[k] = -1;
       if (lam[z] != -1) return fail(VB_EUNSUPPORTED, "internal: node %d already has a pending Lambda", z);
@@ -985,7 +998,7 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
         if (s) return s;
         HIPCHK(launch_relax(B.pool[cur], 1, scale, pend >= 0 ? B.pool[pend] : nullptr, rows, (int)R, P, tn.c,
                             B.lo[z] + chunk_off(z), B.hi[z] + chunk_off(z), bias_z, alpha_of(t), psi_of(t),
-                            B.pool[outb], B.rowacc, B.st));
+                            aidx_of(t), acols_of(t), B.pool[outb], B.rowacc, B.st));
         if (pend >= 0) {
           B.release(pend);
           lam[t] = -1;
@@ -1398,7 +1411,8 @@ static size_t crown_workspace(const Graph& G, int batch, int m, int method, int 
 
 namespace {
 bool alpha_chain(const Graph& G, std::vector<std::pair<int, int>>& chain);
-size_t alpha_workspace(const Graph& G, int batch, int m);
+size_t alpha_workspace(const Graph& G, int batch, int m, const int* width = nullptr);
+vb_status check_compact(const Graph& G, int batch, int m, const vb_alpha_compact* c);
 }  // namespace
 
 extern "C" vb_status vb_workspace_size(const vb_graph* g, int32_t batch, int32_t m, int32_t method,
@@ -1467,11 +1481,15 @@ static vb_status crown_backward_impl(const Graph& G, int batch, int start, int s
                                      const float* const* lo, const float* const* hi, Domain dom, float* lb,
                                      float* ub, void* ws, size_t ws_bytes, hipStream_t st, float* a_out = nullptr,
                                      float* bias_out = nullptr, const float* const* alpha = nullptr,
-                                     bool intersect = false) {
+                                     bool intersect = false, const vb_alpha_compact* compact = nullptr) {
   Backward B{G, st, lo, hi, dom};
   B.a_out = a_out;
   B.bias_out = bias_out;
   B.alpha = alpha;
+  if (alpha && compact) {
+    B.aidx = compact->index;
+    B.awidth = compact->width;
+  }
   vb_status s = prepare_weights(G, (char*)ws, st, B.wt, B.beff);
   if (s) return s;
   const bool lower_only = C && !ub;
@@ -1493,9 +1511,9 @@ static vb_status crown_backward_impl(const Graph& G, int batch, int start, int s
 
 extern "C" vb_status vb_crown_backward(const vb_graph* g, int32_t batch, int32_t start, int32_t stop, const float* C,
                                        int32_t m, const float* const* node_lo, const float* const* node_hi,
-                                       const float* const* alpha, const float* x_center, const float* x_radius,
-                                       float eps, float* lb, float* ub, float* A_out, float* bias_out, void* ws,
-                                       size_t ws_bytes, void* stream) {
+                                       const vb_alpha_compact* compact, const float* const* alpha,
+                                       const float* x_center, const float* x_radius, float eps, float* lb, float* ub,
+                                       float* A_out, float* bias_out, void* ws, size_t ws_bytes, void* stream) {
   Graph G;
   vb_status s = parse_graph(g, G);
   if (s) return s;
@@ -1509,13 +1527,16 @@ extern "C" vb_status vb_crown_backward(const vb_graph* g, int32_t batch, int32_t
   if (!ws) return fail(VB_EINVAL, "workspace is NULL");
   if (bias_out && !A_out) return fail(VB_EINVAL, "bias_out needs A_out");
   if (!A_out && !lb && !ub) return fail(VB_EINVAL, "nothing to compute: lb, ub and A_out are NULL");
+  if (compact && !alpha) return fail(VB_EINVAL, "a compact layout needs alpha");
   if (alpha) {
     if (!C || ub) return fail(VB_EINVAL, "alpha needs spec rows C and ub == NULL (slopes bound one side)");
+    if (compact && (s = check_compact(G, batch, m, compact))) return s;
     for (size_t k = start > stop ? stop + 1 : 0; (int)k < start; ++k)
-      if (G.n[k].op == VB_RELU && !alpha[k]) return fail(VB_EINVAL, "alpha of ReLU node %zu is NULL", k);
+      if (G.n[k].op == VB_RELU && !alpha[k] && !(compact && compact->width[k] == 0))
+        return fail(VB_EINVAL, "alpha of ReLU node %zu is NULL", k);
   }
   return crown_backward_impl(G, batch, start, stop, C, m, node_lo, node_hi, {x_center, x_radius, eps}, lb, ub, ws,
-                             ws_bytes, (hipStream_t)stream, A_out, bias_out, alpha);
+                             ws_bytes, (hipStream_t)stream, A_out, bias_out, alpha, false, compact);
 }
 
 extern "C" vb_status vb_concretize(int32_t rows, int32_t n, int32_t rows_per_batch, const float* A, const float* bias,
@@ -1641,52 +1662,107 @@ bool alpha_chain(const Graph& G, std::vector<std::pair<int, int>>& chain) {
   return !chain.empty() && chain.back().first == G.L && G.n[G.L].op == VB_LINEAR;
 }
 
-size_t alpha_psi_floats(const Graph& G, long long rows) {
+// kept Psi over the domain and over every ReLU node (compact: width[k] per row)
+size_t alpha_psi_floats(const Graph& G, long long rows, const int* width) {
   size_t f = align_up((size_t)rows * G.n[0].size * 4) / 4;
-  for (const NodeInfo& n : G.n)
-    if (n.op == VB_RELU) f += align_up((size_t)rows * n.size * 4) / 4;
+  for (size_t k = 0; k < G.n.size(); ++k)
+    if (G.n[k].op == VB_RELU) f += align_up((size_t)rows * (width ? width[k] : G.n[k].size) * 4) / 4;
   return f;
 }
 
-size_t alpha_workspace(const Graph& G, int batch, int m) {
+size_t alpha_workspace(const Graph& G, int batch, int m, const int* width) {
   const long long R = m;
   long long maxw, ppb;
   bwd_requirements(G, G.L, 0, R, maxw, ppb);
   maxw = std::max(maxw, G.n[G.L].size);
-  return layout_for(maxw, ppb, R, batch, wt_floats(G) + alpha_psi_floats(G, (long long)batch * m)).bytes;
+  return layout_for(maxw, ppb, R, batch, wt_floats(G) + alpha_psi_floats(G, (long long)batch * m, width)).bytes;
 }
 
 }  // namespace
 
+extern "C" vb_status vb_alpha_layout(const vb_graph* g, int32_t batch, const float* const* node_lo,
+                                     const float* const* node_hi, int32_t* const* index, int32_t* width, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  Graph G;
+  vb_status s = parse_graph(g, G);
+  if (s) return s;
+  if (batch <= 0) return fail(VB_EINVAL, "batch must be positive");
+  if (!node_lo || !node_hi || !index || !width) return fail(VB_EINVAL, "NULL pointer array");
+  if (!ws || ws_bytes < (size_t)batch * sizeof(int32_t))
+    return fail(VB_ENOMEM, "alpha layout needs %zu bytes of workspace", (size_t)batch * sizeof(int32_t));
+  for (size_t k = 0; k < G.n.size(); ++k) {
+    if (G.n[k].op != VB_RELU) continue;
+    const int z = G.n[k].in0;
+    if (!index[k] || !node_lo[z] || !node_hi[z])
+      return fail(VB_EINVAL, "ReLU node %zu: index storage / input bounds missing", k);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  int* count = (int*)ws;
+  std::vector<int> host(batch);
+  for (size_t k = 0; k < G.n.size(); ++k) {
+    width[k] = 0;
+    if (G.n[k].op != VB_RELU) continue;
+    const int z = G.n[k].in0;
+    HIPCHK(launch_alpha_layout(node_lo[z], node_hi[z], batch, G.n[z].size, index[k], count, st));
+    HIPCHK(hipMemcpyAsync(host.data(), count, (size_t)batch * sizeof(int), hipMemcpyDeviceToHost, st));
+    HIPCHK(hipStreamSynchronize(st));
+    width[k] = *std::max_element(host.begin(), host.end());
+  }
+  return VB_OK;
+}
+
+namespace {
+// Compact layouts: widths within [0, size], index maps present where a width
+// is positive, and every row offset of the state inside 32-bit range.
+vb_status check_compact(const Graph& G, int batch, int m, const vb_alpha_compact* c) {
+  if (!c->index || !c->width) return fail(VB_EINVAL, "compact layout with NULL index or width array");
+  for (size_t k = 0; k < G.n.size(); ++k) {
+    if (G.n[k].op != VB_RELU) continue;
+    const long long w = c->width[k];
+    if (w < 0 || w > G.n[k].size) return fail(VB_EINVAL, "ReLU node %zu: compact width %lld out of range", k, w);
+    if (!c->index[k]) return fail(VB_EINVAL, "ReLU node %zu: compact index map is NULL", k);
+    if ((long long)batch * m * w >= (1LL << 31))
+      return fail(VB_EUNSUPPORTED, "ReLU node %zu: compact state of %lld entries exceeds 2^31", k,
+                  (long long)batch * m * w);
+  }
+  return VB_OK;
+}
+}  // namespace
+
 extern "C" vb_status vb_alpha_init(const vb_graph* g, int32_t batch, int32_t m, const float* const* node_lo,
-                                   const float* const* node_hi, float* const* alpha, float* const* adam_m,
-                                   float* const* adam_v, void* stream) {
+                                   const float* const* node_hi, const vb_alpha_compact* compact, float* const* alpha,
+                                   float* const* adam_m, float* const* adam_v, void* stream) {
   Graph G;
   vb_status s = parse_graph(g, G);
   if (s) return s;
   if (batch <= 0 || m <= 0) return fail(VB_EINVAL, "batch and m must be positive");
   if (!node_lo || !node_hi || !alpha || !adam_m || !adam_v) return fail(VB_EINVAL, "NULL pointer array");
+  if (compact && (s = check_compact(G, batch, m, compact))) return s;
   for (size_t k = 0; k < G.n.size(); ++k) {
     if (G.n[k].op != VB_RELU) continue;
     const int z = G.n[k].in0;
-    if (!alpha[k] || !adam_m[k] || !adam_v[k] || !node_lo[z] || !node_hi[z])
-      return fail(VB_EINVAL, "ReLU node %zu: alpha / adam state / input bounds missing", k);
+    if (!node_lo[z] || !node_hi[z]) return fail(VB_EINVAL, "ReLU node %zu: input bounds missing", k);
+    if (compact && compact->width[k] == 0) continue;  // no unstable neuron: no state
+    if (!alpha[k] || !adam_m[k] || !adam_v[k])
+      return fail(VB_EINVAL, "ReLU node %zu: alpha / adam state missing", k);
   }
   for (size_t k = 0; k < G.n.size(); ++k) {
     if (G.n[k].op != VB_RELU) continue;
     const int z = G.n[k].in0;
-    HIPCHK(launch_alpha_init(node_lo[z], node_hi[z], batch, m, G.n[z].size, alpha[k], adam_m[k], adam_v[k],
-                             (hipStream_t)stream));
+    const int* aidx = compact ? compact->index[k] : nullptr;
+    const int acols = compact ? compact->width[k] : 0;
+    HIPCHK(launch_alpha_init(node_lo[z], node_hi[z], batch, m, G.n[z].size, aidx, acols, alpha[k], adam_m[k],
+                             adam_v[k], (hipStream_t)stream));
   }
   return VB_OK;
 }
 
 extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float* C, int32_t m,
                                    const float* const* node_lo, const float* const* node_hi, const float* x_center,
-                                   const float* x_radius, float eps, float* const* alpha, float* const* adam_m,
-                                   float* const* adam_v, int32_t step, float lr, float beta1, float beta2,
-                                   float adam_eps, float* lb_out, float* best_lb, void* ws, size_t ws_bytes,
-                                   void* stream) {
+                                   const float* x_radius, float eps, const vb_alpha_compact* compact,
+                                   float* const* alpha, float* const* adam_m, float* const* adam_v, int32_t step,
+                                   float lr, float beta1, float beta2, float adam_eps, float* lb_out, float* best_lb,
+                                   void* ws, size_t ws_bytes, void* stream) {
   Graph G;
   vb_status s = parse_graph(g, G);
   if (s) return s;
@@ -1701,14 +1777,17 @@ extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float
   if (!lb_out && !best_lb) return fail(VB_EINVAL, "lb_out and best_lb are both NULL");
   std::vector<std::pair<int, int>> chain;
   if (!alpha_chain(G, chain)) return fail(VB_EUNSUPPORTED, "alpha-CROWN needs a chain of Linear/Conv + ReLU nodes");
+  if (compact && (s = check_compact(G, batch, m, compact))) return s;
   for (size_t k = 0; k < G.n.size(); ++k) {
     if (G.n[k].op != VB_RELU) continue;
     const int z = G.n[k].in0;
-    if (!alpha[k] || !node_lo[z] || !node_hi[z] || (step > 0 && (!adam_m[k] || !adam_v[k])))
-      return fail(VB_EINVAL, "ReLU node %zu: alpha / adam state / input bounds missing", k);
+    if (!node_lo[z] || !node_hi[z]) return fail(VB_EINVAL, "ReLU node %zu: input bounds missing", k);
+    if (compact && compact->width[k] == 0) continue;  // no unstable neuron: no state
+    if (!alpha[k] || (step > 0 && (!adam_m[k] || !adam_v[k])))
+      return fail(VB_EINVAL, "ReLU node %zu: alpha / adam state missing", k);
   }
   if (!ws) return fail(VB_EINVAL, "workspace is NULL");
-  const size_t need = alpha_workspace(G, batch, m);
+  const size_t need = alpha_workspace(G, batch, m, compact ? compact->width : nullptr);
   if (ws_bytes < need)
     return fail(VB_ENOMEM, "alpha step needs %zu bytes of workspace for the whole batch (got %zu)", need, ws_bytes);
   hipStream_t st = (hipStream_t)stream;
@@ -1725,13 +1804,20 @@ extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float
   off += align_up((size_t)rows * G.n[0].size * 4);
   for (size_t k = 0; k < G.n.size(); ++k)
     if (G.n[k].op == VB_RELU) {
-      psi[k] = (float*)(base + off);
-      off += align_up((size_t)rows * G.n[k].size * 4);
+      const long long w = compact ? compact->width[k] : G.n[k].size;
+      psi[k] = w > 0 ? (float*)(base + off) : nullptr;
+      off += align_up((size_t)rows * w * 4);
     }
+  // (a compact node without unstable neurons has no state: its slopes are never read)
   std::vector<const float*> al(G.n.size(), nullptr);
-  for (size_t k = 0; k < G.n.size(); ++k) al[k] = alpha[k];
+  for (size_t k = 0; k < G.n.size(); ++k)
+    al[k] = (compact && G.n[k].op == VB_RELU && compact->width[k] == 0) ? nullptr : alpha[k];
   B.alpha = al.data();
   B.psi_keep = psi.data();
+  if (compact) {
+    B.aidx = compact->index;
+    B.awidth = compact->width;
+  }
   // evaluation: lower bounds of the m spec rows with the current slopes
   s = backward_all(B, G.L, 0, C, m, 0, batch, m, base, ws_bytes, off / 4, [&](float* acc, int b0, int cb) -> vb_status {
     if (b0 != 0 || cb != batch) return fail(VB_ENOMEM, "internal: alpha step was chunked");
@@ -1779,13 +1865,17 @@ extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float
     d.bias = nd.b;
     d.bias_c = 0;
     // coefficient buffer of the evaluation's layout: 4 * batch * (widest node) floats
-    HIPCHK(launch_relax_coef(node_lo[k], node_hi[k], (long long)batch * nd.size, B.coef, st));
+    HIPCHK(launch_relax_coef(node_lo[k], node_hi[k], (long long)batch * nd.size,
+                             compact ? compact->index[r] : nullptr, B.coef, st));
     d.coef = B.coef;
     d.rows_per_b = m;
+    const bool none = compact && compact->width[r] == 0;
     d.psi_in = psi[r];
-    d.alpha_rw = alpha[r];
-    d.adam_m = adam_m[r];
-    d.adam_v = adam_v[r];
+    d.alpha_rw = none ? nullptr : alpha[r];
+    d.adam_m = none ? nullptr : adam_m[r];
+    d.adam_v = none ? nullptr : adam_v[r];
+    d.aidx = compact ? compact->index[r] : nullptr;
+    d.acols = compact ? compact->width[r] : 0;
     d.do_update = 1;
     d.lr = lr;
     d.beta1 = beta1;
@@ -1813,6 +1903,8 @@ extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float
       a.alpha_rw = d.alpha_rw;
       a.adam_m = d.adam_m;
       a.adam_v = d.adam_v;
+      a.aidx = d.aidx;
+      a.acols = d.acols;
       a.do_update = d.do_update;
       a.lr = d.lr;
       a.beta1 = d.beta1;

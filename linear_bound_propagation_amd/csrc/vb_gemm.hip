@@ -170,7 +170,13 @@ __device__ __forceinline__ void a_val4(const GemmDesc& d, long long off, float4&
 
 }  // namespace
 
-template <int BM, int BN, int WM, int WN, bool DENSE, int AMODE, int EPI, bool FAST, bool PATCH = false>
+// Epilogue addressing variants (compile-time, so that the common case keeps
+// its register budget): plain; footprint windows (rows of identity-start
+// neurons kept on a window of the target node); compact per-neuron state
+// (alpha, kept Psi and Adam moments on unstable neurons only).
+enum { V_PLAIN = 0, V_PATCH = 1, V_COMPACT = 2 };
+
+template <int BM, int BN, int WM, int WN, bool DENSE, int AMODE, int EPI, bool FAST, int VAR = V_PLAIN>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   constexpr int NTHR = WM * WN * 64;
   constexpr int NA = (AMODE == A_PLAIN) ? 1 : 2;
@@ -409,12 +415,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   // load of the group (unconditional, so they can all be in flight together),
   // then the arithmetic with predicated stores.
   constexpr bool ROWSUM = (EPI != E_IBP && EPI != E_ADJOINT);
-  constexpr int G = (FM * FN >= 8) ? 4 : 8;  // rows per group (fewer where registers are short)
+  // rows per group (fewer where registers are short)
+  constexpr int G = (FM * FN >= 8 || (VAR == V_COMPACT && FM * FN >= 2)) ? 4 : 8;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int v0 = 0; v0 < 16; v0 += G) {
       long long opos[G], bpos[G];
+      int rbase[G];  // compact per-neuron state: first entry of the element's row
       bool mok[G], pin[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -425,17 +433,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
           mok[g] = m < d.M;
           const int mm = mok[g] ? m : 0;
           opos[g] = mm;
+          rbase[g] = mm * d.acols;
           bpos[g] = fdiv(mm, d.div_rows);
         } else {
           const GPos gp = gdecode(d, m);
           mok[g] = gp.valid;
+          rbase[g] = gp.row * d.acols;
           const int Y = fdiv(gp.q, d.div_gw);
           const int X = gp.q - Y * d.gw;
           const int cy = Y * d.oym + d.oy0, cx = X * d.oxm + d.ox0;
           const long long sp = (long long)cy * d.wo + cx;
           opos[g] = (long long)gp.row * d.ho * d.wo + sp;
           const long long b = fdiv(gp.row, d.div_rows);
-          if (PATCH) {
+          if (VAR == V_PATCH) {
             // window cell -> pixel of the target node for the row's own position
             const int t1 = fdiv(gp.row, d.div_pc);
             const int pz = t1 - fdiv(t1, d.div_pz) * d.div_pz.d;
@@ -464,6 +474,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
           oi[g] = opos[g] * d.N + nn;
           bi[g] = bpos[g] * d.N + nn;
         }
+        // per-neuron state (alpha, kept Psi, Adam moments): at oi, or in the
+        // compact layout at the neuron's column of the element's row (the column
+        // comes with the relaxation coefficients; the host keeps rows * acols < 2^31)
+        auto state_at = [&](int g, int col) -> long long {
+          return VAR == V_COMPACT ? (long long)(unsigned)(rbase[g] + (col > 0 ? col : 0)) : oi[g];
+        };
         float val[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) val[g] = acc[i][j][v0 + g];
@@ -517,18 +533,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             cf[g] = d.coef[bi[g]];
-            if (!pin[g]) cf[g] = make_float4(0.f, 0.f, 0.f, 0.f);  // outside the node: no neuron
+            if (!pin[g]) cf[g] = make_float4(0.f, 0.f, 0.f, __int_as_float(-1));  // outside the node: no neuron
           }
           // slope of the lower relaxation: the optimised alpha on unstable
-          // neurons when one is given, else the adaptive choice
+          // neurons (coefficient column >= 0) when one is given, else the adaptive choice
           float al[G];
 #pragma unroll
           for (int g = 0; g < G; ++g) al[g] = cf[g].x;
           if (d.alpha) {
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-              const float t = d.alpha[oi[g]];
-              al[g] = cf[g].w != 0.f ? t : al[g];
+              const int col = __float_as_int(cf[g].w);
+              const float t = d.alpha[state_at(g, col)];
+              al[g] = col >= 0 ? t : al[g];
             }
           }
 #pragma unroll
@@ -537,31 +554,37 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
             const float o = (val[g] >= 0.f) ? val[g] * a : val[g] * cf[g].y;
             if (mok[g] && nok) {
               d.out[oi[g]] = o;
-              if (d.psi_out) d.psi_out[oi[g]] = val[g];
+              const int col = __float_as_int(cf[g].w);
+              if (d.psi_out && (VAR != V_COMPACT || col >= 0)) d.psi_out[state_at(g, col)] = val[g];
               rowsum[g] += o * bias + fminf(val[g], 0.f) * cf[g].z;
             }
           }
         } else if (EPI == E_ADJOINT) {
           // the accumulator is the adjoint over z: add z's bias
+          // (a compact layout without any unstable neuron has no state arrays at all)
+          const bool have = d.alpha_rw != nullptr;
           float4 cf[G];
           float psi[G], aold[G], am[G], av[G];
+          long long ai[G];
+#pragma unroll
+          for (int g = 0; g < G; ++g) cf[g] = d.coef[bi[g]];
 #pragma unroll
           for (int g = 0; g < G; ++g) {
-            cf[g] = d.coef[bi[g]];
-            psi[g] = d.psi_in[oi[g]];
-            aold[g] = d.alpha_rw[oi[g]];
+            ai[g] = state_at(g, __float_as_int(cf[g].w));
+            psi[g] = have ? d.psi_in[ai[g]] : 0.f;
+            aold[g] = have ? d.alpha_rw[ai[g]] : 0.f;
           }
-          if (d.do_update) {
+          if (d.do_update && have) {
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-              am[g] = d.adam_m[oi[g]];
-              av[g] = d.adam_v[oi[g]];
+              am[g] = d.adam_m[ai[g]];
+              av[g] = d.adam_v[ai[g]];
             }
           }
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             const float gz = val[g] + bias;
-            const bool unstable = cf[g].w != 0.f;
+            const bool unstable = __float_as_int(cf[g].w) >= 0 && have;
             // stable neurons: a = s (0 inactive, 1 active); unstable: the Psi >= 0 branch takes alpha
             const float o = !unstable ? gz * cf[g].y : (psi[g] >= 0.f ? gz * aold[g] : gz * cf[g].y + cf[g].z);
             if (mok[g] && nok) {
@@ -570,10 +593,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
                 const float grad = gz * fmaxf(psi[g], 0.f);
                 const float mm = d.beta1 * am[g] + (1.f - d.beta1) * grad;
                 const float vv = d.beta2 * av[g] + (1.f - d.beta2) * grad * grad;
-                d.adam_m[oi[g]] = mm;
-                d.adam_v[oi[g]] = vv;
+                d.adam_m[ai[g]] = mm;
+                d.adam_v[ai[g]] = vv;
                 const float step = d.lr * (mm * d.bc1) / (sqrtf(vv * d.bc2) + d.adam_eps);
-                d.alpha_rw[oi[g]] = fminf(fmaxf(aold[g] + step, 0.f), 1.f);
+                d.alpha_rw[ai[g]] = fminf(fmaxf(aold[g] + step, 0.f), 1.f);
               }
             }
           }
@@ -653,18 +676,25 @@ hipError_t launch_tile(const GemmDesc& d, hipStream_t st) {
       break;
     case E_RELAX:
       if (!DENSE && d.patch)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_RELAX, FAST, !DENSE>), g, b, 0, st, d);
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_RELAX, FAST, DENSE ? V_PLAIN : V_PATCH>), g, b, 0,
+                           st, d);
+      else if (d.aidx)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_RELAX, FAST, V_COMPACT>), g, b, 0, st, d);
       else
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_RELAX, FAST>), g, b, 0, st, d);
       break;
     case E_CONCRETIZE:
       if (!DENSE && d.patch)
-        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_CONCRETIZE, FAST, !DENSE>), g, b, 0, st, d);
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_CONCRETIZE, FAST, DENSE ? V_PLAIN : V_PATCH>), g, b,
+                           0, st, d);
       else
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_CONCRETIZE, FAST>), g, b, 0, st, d);
       break;
     case E_ADJOINT:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_ADJOINT, FAST>), g, b, 0, st, d);
+      if (d.aidx)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_ADJOINT, FAST, V_COMPACT>), g, b, 0, st, d);
+      else
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_ADJOINT, FAST>), g, b, 0, st, d);
       break;
     case E_IBP:
       if (d.amode == A_IBP_BOX)
@@ -688,7 +718,7 @@ hipError_t launch_shape(const GemmDesc& d, bool dense, bool fast, hipStream_t st
 // GEMMs with the fast path, when the grid still has at least two workgroups per CU
 // (dense GEMMs ran faster on two 128 x 128 workgroups per CU).
 bool use_big(const GemmDesc& d, bool fast) {
-  if (!fast || d.epi == E_IBP || d.N < 256 || gemm_is_dense(d) || d.patch) return false;
+  if (!fast || d.epi == E_IBP || d.N < 256 || gemm_is_dense(d) || d.patch || d.aidx) return false;
   const long long tiles = (long long)((d.Mt + 255) / 256) * ((d.N + 255) / 256);
   return tiles >= 512;
 }

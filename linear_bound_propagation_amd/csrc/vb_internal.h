@@ -97,11 +97,18 @@ struct GemmDesc {
   const float* lo;             // (unused by the GEMM epilogues; kept for descriptors)
   const float* hi;
   const float4* coef;          // E_RELAX / E_ADJOINT: relaxation of the target at [b-pos][N]:
-                               // {a (adaptive lower slope), s, t, 1 if unstable else 0}
+                               // {a (adaptive lower slope), s, t, column}: the int bits of w are
+                               // -1 for a stable neuron, else its compact column (0 if not compact)
   const float* bias;           // per output channel (E_STORE / E_RELAX / E_IBP)
   int bias_c;                  // channels of the bias: index = n % bias_c (0: index = n)
   const float* alpha;          // E_RELAX: per [opos][N] lower slope of unstable neurons, or NULL
   float* psi_out;              // E_RELAX: store the pre-relaxation value v, or NULL
+  // compact alpha (E_RELAX / E_ADJOINT): alpha, psi_out / psi_in and the Adam
+  // state hold only unstable neurons, row r at r * acols + (column in coef.w);
+  // aidx (the column map the coefficients were built from) non-NULL selects
+  // this layout, else the [opos][N] layout
+  const int* aidx;
+  int acols;
   const float* center;         // E_CONCRETIZE: centre/radius of the domain box at [b-pos][N]
   const float* radius;         // NULL -> eps
   float* part;                 // row partials [M][part_ld] (column = N-tile index; gather:
@@ -219,9 +226,10 @@ hipError_t launch_identity_fill(int batch, int n, float* lam, hipStream_t st);
 // Standalone relaxation of lam over a ReLU with input bounds lo/hi [b][P*N]:
 // src is [rows][P*N] (or [rows][N] broadcast over P positions with scale, for GAP);
 // out = relax(src + addend); rowacc[r] += sum out.bias_z + min(v,0) t
+// alpha / psi_out: [rows][P*N], or compact ([rows][acols] at column aidx[b][P*N]) if aidx != NULL.
 hipError_t launch_relax(const float* src, int src_broadcast, float scale, const float* addend,
                         int rows, int rows_per_b, int P, int N, const float* lo, const float* hi,
-                        const float* bias_z, const float* alpha, float* psi_out,
+                        const float* bias_z, const float* alpha, float* psi_out, const int* aidx, int acols,
                         float* out, float* rowacc, hipStream_t st);
 
 // dst[i] = a[i] + b[i] (b may be NULL: copy), i < n
@@ -252,8 +260,17 @@ hipError_t launch_transpose(const float* src, int batch, int R, int C, float* ds
 // alpha-CROWN set-up: alpha = adaptive lower slope of each neuron (1 if u >= -l
 // else 0 when unstable; 1 active; 0 inactive) for every one of `rows_per_b`
 // spec rows of each batch element; m = v = 0.  Bounds lo/hi [batch][n].
+// With aidx != NULL the state is compact: [batch*rows_per_b][acols], neuron j of
+// batch element b at column aidx[b][j] (unstable neurons only; -1 elsewhere).
 hipError_t launch_alpha_init(const float* lo, const float* hi, int batch, int rows_per_b, long long n,
-                             float* alpha, float* adam_m, float* adam_v, hipStream_t st);
+                             const int* aidx, int acols, float* alpha, float* adam_m, float* adam_v,
+                             hipStream_t st);
+
+// Compact alpha columns: for each batch element b, idx[b][j] = number of
+// unstable neurons (l < 0 < u) before j in node order if j is unstable, else
+// -1; count[b] = number of unstable neurons of b.  One workgroup per b.
+hipError_t launch_alpha_layout(const float* lo, const float* hi, int batch, long long n, int* idx, int* count,
+                               hipStream_t st);
 
 // Adjoint at the input box: g[r][j] = c[b][j] - rad[b][j] * sign(psi[r][j]), b = r / rows_per_b
 hipError_t launch_adj_domain(const float* psi, int rows, int n, int rows_per_b, const float* center,
@@ -261,7 +278,10 @@ hipError_t launch_adj_domain(const float* psi, int rows, int n, int rows_per_b, 
 
 // Relaxation coefficients of n neurons from their bounds: {a, s, t, unstable}
 // (inactive u <= 0: 0,0,0; active l >= 0: 1,1,0; unstable: adaptive a, s = u/(u-l), t = -s l)
-hipError_t launch_relax_coef(const float* lo, const float* hi, long long n, float4* coef, hipStream_t st);
+// w holds the bits of an int: -1 for a stable neuron, else the neuron's column
+// aidx[i] in a compact state layout (0 when aidx is NULL).
+hipError_t launch_relax_coef(const float* lo, const float* hi, long long n, const int* aidx, float4* coef,
+                             hipStream_t st);
 
 // Box centre and radius of bounds: c = (lo+hi)/2, r = (hi-lo)/2, n elements
 hipError_t launch_box_center_radius(const float* lo, const float* hi, long long n, float* c, float* r,
@@ -287,6 +307,8 @@ struct AdjFinish {
   float* alpha_rw;
   float* adam_m;
   float* adam_v;
+  const int* aidx;  // compact columns (see GemmDesc::aidx) or NULL
+  int acols;
   int do_update;
   float lr, beta1, beta2, bc1, bc2, adam_eps;
   float* out;

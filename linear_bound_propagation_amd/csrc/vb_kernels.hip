@@ -376,6 +376,7 @@ __global__ __launch_bounds__(256) void relax_kernel(const float* __restrict__ sr
                                                     const float* __restrict__ hi,
                                                     const float* __restrict__ bias_z,
                                                     const float* __restrict__ alpha, float* __restrict__ psi_out,
+                                                    const int* __restrict__ aidx, int acols,
                                                     float* __restrict__ out, float* __restrict__ rowacc) {
   __shared__ float sh[4];
   const int row = blockIdx.x;
@@ -389,10 +390,13 @@ __global__ __launch_bounds__(256) void relax_kernel(const float* __restrict__ sr
     const float l = lo[b * L + e], u = hi[b * L + e];
     float a, sl, t;
     relax_coeffs(l, u, a, sl, t);
-    if (alpha && l < 0.f && u > 0.f) a = alpha[(long long)row * L + e];
+    // per-neuron state: [row][L], or compact [row][acols] at the neuron's column
+    const int col = aidx ? aidx[b * L + e] : 0;
+    const long long si = aidx ? (long long)row * acols + col : (long long)row * L + e;
+    if (alpha && l < 0.f && u > 0.f && col >= 0) a = alpha[si];
     const float o = v >= 0.f ? v * a : v * sl;
     out[(long long)row * L + e] = o;
-    if (psi_out) psi_out[(long long)row * L + e] = v;
+    if (psi_out && col >= 0) psi_out[si] = v;
     if (bias_z) s += o * bias_z[n];
     s += fminf(v, 0.f) * t;
   }
@@ -402,10 +406,11 @@ __global__ __launch_bounds__(256) void relax_kernel(const float* __restrict__ sr
 
 hipError_t launch_relax(const float* src, int src_broadcast, float scale, const float* addend, int rows,
                         int rows_per_b, int P, int N, const float* lo, const float* hi, const float* bias_z,
-                        const float* alpha, float* psi_out, float* out, float* rowacc, hipStream_t st) {
+                        const float* alpha, float* psi_out, const int* aidx, int acols, float* out, float* rowacc,
+                        hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(relax_kernel, dim3(rows), dim3(256), 0, st, src, src_broadcast, scale, addend, rows,
-                     rows_per_b, P, N, lo, hi, bias_z, alpha, psi_out, out, rowacc);
+                     rows_per_b, P, N, lo, hi, bias_z, alpha, psi_out, aidx, acols, out, rowacc);
   return hipGetLastError();
 }
 
@@ -576,20 +581,22 @@ hipError_t launch_ibp_gap(const float* lo_in, const float* hi_in, int batch, int
 }
 
 __global__ void relax_coef_kernel(const float* __restrict__ lo, const float* __restrict__ hi, long long n,
-                                  float4* __restrict__ coef) {
+                                  const int* __restrict__ aidx, float4* __restrict__ coef) {
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x) {
     const float l = lo[i], u = hi[i];
     float a, s, t;
     relax_coeffs(l, u, a, s, t);
-    coef[i] = make_float4(a, s, t, (u > 0.f && l < 0.f) ? 1.f : 0.f);
+    const int col = (u > 0.f && l < 0.f) ? (aidx ? aidx[i] : 0) : -1;
+    coef[i] = make_float4(a, s, t, __int_as_float(col));
   }
 }
 
-hipError_t launch_relax_coef(const float* lo, const float* hi, long long n, float4* coef, hipStream_t st) {
+hipError_t launch_relax_coef(const float* lo, const float* hi, long long n, const int* aidx, float4* coef,
+                             hipStream_t st) {
   if (n <= 0) return hipSuccess;
   long long blocks = (n + 255) / 256;
   if (blocks > 16384) blocks = 16384;
-  hipLaunchKernelGGL(relax_coef_kernel, dim3((unsigned)blocks), dim3(256), 0, st, lo, hi, n, coef);
+  hipLaunchKernelGGL(relax_coef_kernel, dim3((unsigned)blocks), dim3(256), 0, st, lo, hi, n, aidx, coef);
   return hipGetLastError();
 }
 
@@ -649,19 +656,23 @@ __global__ void adjoint_finish_kernel(AdjFinish a) {
     const long long m = e / a.N;
     const int n = (int)(e - m * a.N);
     const float gz = g + (a.bias ? a.bias[n] : 0.f);
-    const float4 cf = a.coef[(m / a.rows_per_b) * a.N + n];
-    const float psi = a.psi_in[e];
-    const float aold = a.alpha_rw[e];
-    const bool unstable = cf.w != 0.f;
+    const long long bn = (m / a.rows_per_b) * a.N + n;
+    const float4 cf = a.coef[bn];
+    // per-neuron state at e, or compact at the coefficient's column of row m (-1: stable, no entry)
+    const int col = __float_as_int(cf.w);
+    const long long si = a.aidx ? m * a.acols + col : e;
+    const bool unstable = col >= 0 && a.alpha_rw != nullptr;
+    const float psi = unstable ? a.psi_in[si] : 0.f;
+    const float aold = unstable ? a.alpha_rw[si] : 0.f;
     a.out[e] = !unstable ? gz * cf.y : (psi >= 0.f ? gz * aold : gz * cf.y + cf.z);
     if (unstable && a.do_update) {
       const float grad = gz * fmaxf(psi, 0.f);
-      const float mm = a.beta1 * a.adam_m[e] + (1.f - a.beta1) * grad;
-      const float vv = a.beta2 * a.adam_v[e] + (1.f - a.beta2) * grad * grad;
-      a.adam_m[e] = mm;
-      a.adam_v[e] = vv;
+      const float mm = a.beta1 * a.adam_m[si] + (1.f - a.beta1) * grad;
+      const float vv = a.beta2 * a.adam_v[si] + (1.f - a.beta2) * grad * grad;
+      a.adam_m[si] = mm;
+      a.adam_v[si] = vv;
       const float step = a.lr * (mm * a.bc1) / (sqrtf(vv * a.bc2) + a.adam_eps);
-      a.alpha_rw[e] = fminf(fmaxf(aold + step, 0.f), 1.f);
+      a.alpha_rw[si] = fminf(fmaxf(aold + step, 0.f), 1.f);
     }
   }
 }
@@ -756,10 +767,75 @@ __global__ void alpha_init_kernel(const float* __restrict__ lo, const float* __r
   }
 }
 
-hipError_t launch_alpha_init(const float* lo, const float* hi, int batch, int rows_per_b, long long n, float* alpha,
-                             float* am, float* av, hipStream_t st) {
+// Compact state: one thread per (b, neuron); an unstable neuron writes its
+// column of the rows_per_b rows of b.
+__global__ void alpha_init_compact_kernel(const float* __restrict__ lo, const float* __restrict__ hi, int batch,
+                                          int rows_per_b, long long n, const int* __restrict__ aidx, int acols,
+                                          float* __restrict__ alpha, float* __restrict__ am, float* __restrict__ av) {
+  const long long total = (long long)batch * n;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (long long)gridDim.x * blockDim.x) {
+    const int col = aidx[e];
+    if (col < 0) continue;
+    const long long b = e / n;
+    float a, s, t;
+    relax_coeffs(lo[e], hi[e], a, s, t);
+    for (int r = 0; r < rows_per_b; ++r) {
+      const long long o = (b * rows_per_b + r) * acols + col;
+      alpha[o] = a;
+      am[o] = 0.f;
+      av[o] = 0.f;
+    }
+  }
+}
+
+hipError_t launch_alpha_init(const float* lo, const float* hi, int batch, int rows_per_b, long long n,
+                             const int* aidx, int acols, float* alpha, float* am, float* av, hipStream_t st) {
   if (batch <= 0 || n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(alpha_init_kernel, dim3(4096), dim3(256), 0, st, lo, hi, batch, rows_per_b, n, alpha, am, av);
+  if (aidx) {
+    if (acols <= 0) return hipSuccess;  // no unstable neuron: no state
+    hipLaunchKernelGGL(alpha_init_compact_kernel, dim3(2048), dim3(256), 0, st, lo, hi, batch, rows_per_b, n, aidx,
+                       acols, alpha, am, av);
+  } else {
+    hipLaunchKernelGGL(alpha_init_kernel, dim3(4096), dim3(256), 0, st, lo, hi, batch, rows_per_b, n, alpha, am, av);
+  }
+  return hipGetLastError();
+}
+
+// Column of every unstable neuron of batch element blockIdx.x: an exclusive
+// scan of the 0/1 unstable flags in node order, 256 neurons per pass (wave
+// ballots, then the four wave totals in LDS).
+__global__ __launch_bounds__(256) void alpha_layout_kernel(const float* __restrict__ lo, const float* __restrict__ hi,
+                                                           long long n, int* __restrict__ idx,
+                                                           int* __restrict__ count) {
+  __shared__ int wsum[4];
+  const long long b = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int base = 0;
+  for (long long j0 = 0; j0 < n; j0 += 256) {
+    const long long j = j0 + threadIdx.x;
+    bool uns = false;
+    if (j < n) {
+      const float l = lo[b * n + j], u = hi[b * n + j];
+      uns = l < 0.f && u > 0.f;
+    }
+    const unsigned long long mask = __ballot(uns);
+    const int before = __popcll(mask & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[w] = __popcll(mask);
+    __syncthreads();
+    int off = base;
+    for (int q = 0; q < w; ++q) off += wsum[q];
+    if (j < n) idx[b * n + j] = uns ? off + before : -1;
+    base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) count[b] = base;
+}
+
+hipError_t launch_alpha_layout(const float* lo, const float* hi, int batch, long long n, int* idx, int* count,
+                               hipStream_t st) {
+  if (batch <= 0 || n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(alpha_layout_kernel, dim3((unsigned)batch), dim3(256), 0, st, lo, hi, n, idx, count);
   return hipGetLastError();
 }
 

@@ -35,6 +35,27 @@ def adam_ascent_step(x, g, m, v, t: int, lr: float, b1: float = 0.9, b2: float =
     return x, m, v
 
 
+def compact_columns(lo, hi):
+    """Compact storage of alpha (the page stresses that the alpha tensors dominate
+    alpha-CROWN's memory, Sec. 3 and Sec. 4.3; a slope only matters on an unstable
+    neuron, l < 0 < u).  lo, hi: one node's bounds [B][n] in any fixed neuron order.
+    Returns (col [B][n] int32, width): col[b][j] = the number of unstable neurons of
+    input b before j when j is unstable, else -1; width = the largest number of
+    unstable neurons of any input."""
+    lo = np.asarray(lo, dtype=np.float64)
+    hi = np.asarray(hi, dtype=np.float64)
+    col = np.full(lo.shape, -1, dtype=np.int32)
+    width = 0
+    for b in range(lo.shape[0]):
+        count = 0
+        for j in range(lo.shape[1]):
+            if lo[b, j] < 0.0 and hi[b, j] > 0.0:
+                col[b, j] = count
+                count += 1
+        width = max(width, count)
+    return col, width
+
+
 def alpha_init(net: Oracle, lo, hi, b: int, m: int):
     """Adaptive CROWN slopes broadcast over the m spec rows, one tensor per ReLU node."""
     out = {}

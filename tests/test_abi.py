@@ -92,21 +92,40 @@ def test_entry_points_reject_bad_arguments_without_launching():
     # negative eps without a radius array
     assert lbp.lib().vb_ibp(gp, 2, P(64), None, -1.0, nulls, nulls, None, 0, None, None, None, 0, None) == -1
     # crown_backward: stop >= start, missing workspace
-    assert lbp.lib().vb_crown_backward(gp, 2, 1, 1, None, 0, nulls, nulls, None, P(64), None, 0.1, None, None, None, None,
+    assert lbp.lib().vb_crown_backward(gp, 2, 1, 1, None, 0, nulls, nulls, None, None, P(64), None, 0.1, None, None, None, None,
                                       P(64), 1 << 20, None) == -1
-    assert lbp.lib().vb_crown_backward(gp, 2, 3, 0, None, 0, nulls, nulls, None, P(64), None, 0.1, None, None, None, None,
+    assert lbp.lib().vb_crown_backward(gp, 2, 3, 0, None, 0, nulls, nulls, None, None, P(64), None, 0.1, None, None, None, None,
                                       None, 0, None) == -1
     # crown_backward: bias_out without A_out, and no output at all
-    assert lbp.lib().vb_crown_backward(gp, 2, 3, 0, None, 0, nulls, nulls, None, P(64), None, 0.1, None, None, None,
+    assert lbp.lib().vb_crown_backward(gp, 2, 3, 0, None, 0, nulls, nulls, None, None, P(64), None, 0.1, None, None, None,
                                       P(64), P(64), 1 << 20, None) == -1
     assert b"bias_out needs A_out" in lbp.lib().vb_last_error()
-    assert lbp.lib().vb_crown_backward(gp, 2, 3, 0, None, 0, nulls, nulls, None, P(64), None, 0.1, None, None, None, None,
+    assert lbp.lib().vb_crown_backward(gp, 2, 3, 0, None, 0, nulls, nulls, None, None, P(64), None, 0.1, None, None, None, None,
                                       P(64), 1 << 20, None) == -1
     assert b"nothing to compute" in lbp.lib().vb_last_error()
     # alpha needs spec rows and a one-sided call
-    assert lbp.lib().vb_crown_backward(gp, 2, 3, 0, None, 0, nulls, nulls, nulls, P(64), None, 0.1, P(64), None,
+    assert lbp.lib().vb_crown_backward(gp, 2, 3, 0, None, 0, nulls, nulls, None, nulls, P(64), None, 0.1, P(64), None,
                                       None, None, P(64), 1 << 20, None) == -1
     assert b"alpha needs spec rows" in lbp.lib().vb_last_error()
+    # compact alpha layout: needs alpha; widths within the node size; layout call checks
+    idx = (ctypes.c_void_p * 4)(None, None, 64, None)
+    wid = (ctypes.c_int32 * 4)(0, 0, 5, 0)
+    cmp = lbp.vb_alpha_compact(ctypes.cast(idx, ctypes.POINTER(ctypes.c_void_p)),
+                               ctypes.cast(wid, ctypes.POINTER(ctypes.c_int32)))
+    assert lbp.lib().vb_crown_backward(gp, 2, 3, 0, P(64), 2, nulls, nulls, ctypes.byref(cmp), None, P(64), None,
+                                      0.1, P(64), None, None, None, P(64), 1 << 20, None) == -1
+    assert b"needs alpha" in lbp.lib().vb_last_error()
+    wid[2] = 1 << 20  # wider than the ReLU node
+    al = (ctypes.c_void_p * 4)(None, None, 64, None)
+    assert lbp.lib().vb_crown_backward(gp, 2, 3, 0, P(64), 2, nulls, nulls, ctypes.byref(cmp), al, P(64), None,
+                                      0.1, P(64), None, None, None, P(64), 1 << 20, None) == -1
+    assert b"compact width" in lbp.lib().vb_last_error()
+    width = (ctypes.c_int32 * 4)()
+    assert lbp.lib().vb_alpha_layout(gp, 0, nulls, nulls, idx, width, P(64), 1024, None) == -1
+    bounds = (ctypes.c_void_p * 4)(None, 64, 64, 64)
+    assert lbp.lib().vb_alpha_layout(gp, 2, bounds, bounds, idx, width, P(64), 4, None) == -3
+    assert lbp.lib().vb_alpha_layout(gp, 2, bounds, bounds, nulls, width, P(64), 1024, None) == -1
+    assert b"index storage" in lbp.lib().vb_last_error()
     # workspace too small: reported before any launch
     bounds = (ctypes.c_void_p * 4)(None, 64, 64, 64)
     assert lbp.lib().vb_crown(gp, 2, P(64), None, 0.1, 1, 0, bounds, bounds, P(64), 2, None, None, P(64), P(64),

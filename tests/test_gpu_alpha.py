@@ -18,12 +18,14 @@ def lbp():
     return m
 
 
-def _gpu_alpha(lbp, wl, steps):
+def _gpu_alpha(lbp, wl, steps, compact=False):
     net, x, C = lbp.prepare(wl)
     out = lbp.crown(net, x, float(wl.eps), C, "ibp")
-    best, lb_steps, state = lbp.alpha_crown(net, x, float(wl.eps), C, out["lo"], out["hi"], steps, wl.alpha_lr)
+    lay = lbp.alpha_layout(net, out["lo"], out["hi"]) if compact else None
+    best, lb_steps, state = lbp.alpha_crown(net, x, float(wl.eps), C, out["lo"], out["hi"], steps, wl.alpha_lr,
+                                            layout=lay)
     torch.cuda.synchronize()
-    return out, best, lb_steps, state
+    return out, best, lb_steps, state, lay
 
 
 def _oracle(wl, steps, batch_idx=None):
@@ -34,17 +36,22 @@ def _oracle(wl, steps, batch_idx=None):
     return crown_lb, res
 
 
+@pytest.mark.parametrize("compact", [False, True])
 @pytest.mark.parametrize("kind", ["mlp", "cnn"])
-def test_alpha_small(lbp, kind):
+def test_alpha_small(lbp, kind, compact):
     if kind == "mlp":
         wl = wk.tiny_mlp([40, 70, 50, 8], 0.08, 21, batch=3)
         wl.intermediate = "ibp"
     else:
         wl = wk.cnn(2, 0.02, 22, convs=((6, 1), (12, 2)), fcs=(30, 10), in_shape=(3, 8, 8))
     steps = 8
-    print(f"alpha {kind} steps {steps}", flush=True)
-    out, best, lb_steps, (alpha, _, _) = _gpu_alpha(lbp, wl, steps)
+    print(f"alpha {kind} steps {steps} compact {compact}", flush=True)
+    out, best, lb_steps, (alpha, _, _), lay = _gpu_alpha(lbp, wl, steps, compact)
     crown_lb, ref = _oracle(wl, steps)
+    if compact:
+        # the same arithmetic as the dense layout: identical bounds at every step
+        _, best_d, lb_d, _, _ = _gpu_alpha(lbp, wl, steps)
+        assert torch.equal(lb_steps, lb_d) and torch.equal(best, best_d)
     # the first evaluation uses the adaptive CROWN slopes
     assert_close(lb_steps[0], crown_lb, "lb at alpha init vs oracle CROWN")
     assert_close(lb_steps[0], out["lb"].double().cpu(), "lb at alpha init vs GPU CROWN", atol=1e-6, rtol=1e-6)
@@ -53,17 +60,32 @@ def test_alpha_small(lbp, kind):
     assert_close(best, ref["best"], "best")
     assert bool((best >= lb_steps[0] - 1e-6).all())
     assert bool((best > lb_steps[0] + 1e-4).any()), "alpha optimisation should tighten some bound"
-    for a in alpha:
-        if a is not None:
+    for k, a in enumerate(alpha):
+        if a is None:
+            continue
+        if lay is None:
             assert bool(((a >= 0) & (a <= 1)).all())
+        else:
+            # compact rows: only the columns of each input's unstable neurons hold slopes
+            for b in range(a.shape[0]):
+                cols = lay.index[k][b][lay.index[k][b] >= 0].long()
+                v = a[b][:, cols]
+                assert bool(((v >= 0) & (v <= 1)).all())
 
 
-def test_config4_full_size_sampled_inputs(lbp):
+@pytest.fixture(scope="module")
+def config4_oracle():
     wl = wk.config(4)
-    print(wl.name, flush=True)
-    out, best, lb_steps, _ = _gpu_alpha(lbp, wl, wl.alpha_steps)
     idx = [0, 15]
     crown_lb, ref = _oracle(wl, wl.alpha_steps, batch_idx=idx)
+    return wl, idx, crown_lb, ref
+
+
+@pytest.mark.parametrize("compact", [True, False])
+def test_config4_full_size_sampled_inputs(lbp, config4_oracle, compact):
+    wl, idx, crown_lb, ref = config4_oracle
+    print(wl.name, "compact", compact, flush=True)
+    out, best, lb_steps, _, _ = _gpu_alpha(lbp, wl, wl.alpha_steps, compact)
     assert_close(lb_steps[0][idx], crown_lb[idx], "lb at alpha init")
     assert_close(best[idx], ref["best"][idx], "best lower bound after 20 Adam steps")
     for t in (1, 5, 10, 20):
@@ -81,7 +103,7 @@ def test_alpha_upper_bounds_via_negated_specs(lbp):
     wl.intermediate = "ibp"
     wl.C = -wl.C
     steps = 6
-    out, best, lb_steps, _ = _gpu_alpha(lbp, wl, steps)
+    out, best, lb_steps, _, _ = _gpu_alpha(lbp, wl, steps)
     crown_lb, ref = _oracle(wl, steps)
     for t in range(steps + 1):
         assert_close(lb_steps[t], ref["lb_steps"][t], f"lb(-C) after {t} Adam steps")

@@ -12,7 +12,7 @@ import torch
 import workloads as wk
 from helpers import assert_close, compare_workload, ensure_built, nhwc
 from oracle import Oracle, backward, concretize, crown_bounds, ibp as oracle_ibp
-from oracle.alpha import alpha_init as oracle_alpha_init
+from oracle.alpha import alpha_init as oracle_alpha_init, compact_columns
 
 pytestmark = pytest.mark.gpu
 
@@ -229,6 +229,108 @@ def test_crown_backward_with_alpha_one_sided(lbp, case):
                        alpha={k: _f64(v[b]) for k, v in alpha_ref.items()}, keep=keep)
         assert_close(lba[b], ref, f"alpha lb input {b}")
         assert_close(A[b], nhwc(keep["domain"], wl.nodes[0].shape), f"alpha A input {b}")
+
+
+# ---------------------------------------------------------------------------
+# compact alpha (vb_alpha_layout and the compact layout in the alpha calls)
+
+def _host_columns(wl, lo, hi):
+    """Oracle compact columns of every ReLU node from the fp32 bounds in the library's layout."""
+    cols = {}
+    for r, nd in enumerate(wl.nodes):
+        if nd.op == "relu":
+            z = nd.inputs[0]
+            cols[r] = compact_columns(nhwc(lo[z], wl.nodes[z].shape), nhwc(hi[z], wl.nodes[z].shape))
+    return cols
+
+
+@pytest.mark.parametrize("case", ["mlp", "cnn"])
+def test_alpha_layout_matches_oracle(lbp, case):
+    wl = CASES[case]()
+    on, lo, hi = _fp32_bounds(wl)
+    net, x, C = lbp.prepare(wl)
+    dlo, dhi = _to_device(lbp, net, wl, lo, hi)
+    lay = lbp.alpha_layout(net, dlo, dhi)
+    ref = _host_columns(wl, lo, hi)
+    for k, nd in enumerate(wl.nodes):
+        if nd.op != "relu":
+            assert lay.width[k] == 0 and lay.index[k] is None
+            continue
+        col, width = ref[k]
+        assert lay.width[k] == width, (k, lay.width[k], width)
+        assert np.array_equal(lay.index[k].cpu().numpy(), col), k
+    assert any(w > 0 for w in lay.width)
+
+
+def _compact_from_dense(dense, col, width):
+    """[B][m][n] (library layout) -> [B][m][width]: the unstable neurons' columns."""
+    B, m, n = dense.shape
+    out = np.zeros((B, m, width), np.float32)
+    for b in range(B):
+        j = np.nonzero(col[b] >= 0)[0]
+        out[b][:, col[b, j]] = dense[b][:, j]
+    return out
+
+
+@pytest.mark.parametrize("case", ["mlp", "cnn"])
+def test_crown_backward_with_compact_alpha(lbp, case):
+    """Given slopes in the compact layout give the oracle's bound with the same slopes
+    (the oracle holds them densely; entries of stable neurons do not enter)."""
+    wl = CASES[case]()
+    on, lo, hi = _fp32_bounds(wl)
+    net, x, C = lbp.prepare(wl)
+    dlo, dhi = _to_device(lbp, net, wl, lo, hi)
+    L = len(wl.nodes) - 1
+    ws = net.workspace(net.workspace_size(wl.batch, wl.m, "crown"))
+    lay = lbp.alpha_layout(net, dlo, dhi)
+    cols = _host_columns(wl, lo, hi)
+    rng = np.random.default_rng(11)
+    alpha_dev = [None] * len(wl.nodes)
+    alpha_ref = {}
+    for r, nd in enumerate(wl.nodes):
+        if nd.op != "relu":
+            continue
+        a = rng.random((wl.batch, wl.m) + tuple(nd.shape)).astype(np.float32)
+        alpha_ref[r] = a
+        dense = nhwc(a.reshape((wl.batch * wl.m,) + tuple(nd.shape)), nd.shape).reshape(wl.batch, wl.m, -1)
+        col, width = cols[r]
+        if width > 0:
+            alpha_dev[r] = torch.as_tensor(_compact_from_dense(dense, col, width), device=x.device)
+    lba, _ = lbp.crown_backward(net, L, 0, dlo, dhi, x, float(wl.eps), ws, C=C, alpha=alpha_dev, layout=lay)
+    torch.cuda.synchronize()
+    for b in range(wl.batch):
+        c = _f64(wl.x0[b])
+        r = torch.full_like(c, float(np.float32(wl.eps)))
+        ref = backward(on, lo, hi, b, L, _f64(wl.C[b]), 0, c, r, alpha={k: _f64(v[b]) for k, v in alpha_ref.items()})
+        assert_close(lba[b], ref, f"compact alpha lb input {b}")
+
+
+def test_alpha_init_compact(lbp):
+    wl = CASES["cnn"]()
+    on, lo, hi = _fp32_bounds(wl)
+    net, x, C = lbp.prepare(wl)
+    dlo, dhi = _to_device(lbp, net, wl, lo, hi)
+    lay = lbp.alpha_layout(net, dlo, dhi)
+    alpha, am, av = lbp.alpha_state(net, wl.batch, wl.m, lay)
+    for t in am + av:
+        if t is not None:
+            t.fill_(7.0)
+    lbp.alpha_init(net, dlo, dhi, alpha, am, av, wl.m, layout=lay)
+    torch.cuda.synchronize()
+    cols = _host_columns(wl, lo, hi)
+    for b in range(wl.batch):
+        ref = oracle_alpha_init(on, lo, hi, b, wl.m)
+        for r, a in ref.items():
+            col, width = cols[r]
+            if width == 0:
+                assert alpha[r] is None
+                continue
+            dense = nhwc(a, wl.nodes[r].shape)          # [m][n]
+            j = np.nonzero(col[b] >= 0)[0]
+            got = alpha[r][b].cpu().numpy()[:, col[b, j]]
+            assert np.array_equal(got, dense[:, j].astype(np.float32)), (r, b)
+            assert float(np.abs(am[r][b].cpu().numpy()[:, col[b, j]]).max(initial=0)) == 0.0
+            assert float(np.abs(av[r][b].cpu().numpy()[:, col[b, j]]).max(initial=0)) == 0.0
 
 
 # ---------------------------------------------------------------------------

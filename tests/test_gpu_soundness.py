@@ -109,7 +109,9 @@ def test_sound_alpha_crown_iterates(lbp):
     print(wl.name, flush=True)
     net, x, C = lbp.prepare(wl)
     out = lbp.crown(net, x, float(wl.eps), C, "ibp")
-    best, lb_steps, _ = lbp.alpha_crown(net, x, float(wl.eps), C, out["lo"], out["hi"], wl.alpha_steps, wl.alpha_lr)
+    lay = lbp.alpha_layout(net, out["lo"], out["hi"])   # the compact alpha state the benchmark uses
+    best, lb_steps, _ = lbp.alpha_crown(net, x, float(wl.eps), C, out["lo"], out["hi"], wl.alpha_steps, wl.alpha_lr,
+                                        layout=lay)
     torch.cuda.synchronize()
     for b in (0, 15):
         bounds = [(lb_steps[t][b], torch.full_like(best[b], float("inf"))) for t in range(lb_steps.shape[0])]

@@ -17,7 +17,7 @@ import workloads as wk
 from workloads import Node, NetBuilder
 from oracle import (Oracle, ibp, crown_bounds, intermediate_bounds, spec_bounds_crown,
                     spec_bounds_ibp, relaxation, adam_ascent_step)
-from oracle.alpha import alpha_crown, alpha_gradient, alpha_init, evaluate
+from oracle.alpha import alpha_crown, alpha_gradient, alpha_init, compact_columns, evaluate
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -426,3 +426,51 @@ def test_alpha_crown_improves_and_stays_sound():
             assert (spec >= res["lb_steps"][t, b].numpy() - 1e-9).all()
         for v in res["alpha"][b].values():
             assert bool(((v >= 0) & (v <= 1)).all())
+
+
+def test_compact_columns_hand_example():
+    # input 0: only neuron 0 is unstable (l = 0 is active, u = -1 and u = 0 are inactive);
+    # input 1: neurons 1 and 3
+    lo = [[-1.0, 0.0, -2.0, 1.0, -5.0], [0.5, -0.1, -3.0, -1.0, -2.0]]
+    hi = [[1.0, 1.0, -1.0, 2.0, 0.0], [1.0, 0.2, 0.0, 2.0, -1.0]]
+    col, width = compact_columns(lo, hi)
+    assert col.tolist() == [[0, -1, -1, -1, -1], [-1, 0, -1, 1, -1]]
+    assert width == 2
+    col, width = compact_columns([[1.0, 2.0]], [[3.0, 4.0]])
+    assert col.tolist() == [[-1, -1]] and width == 0
+
+
+def test_compact_columns_are_a_dense_ordered_numbering():
+    rng = np.random.default_rng(5)
+    vals = np.array([-2.0, -1.0, 0.0, 1.0, 2.0])
+    lo = rng.choice(vals, size=(6, 40))
+    hi = lo + rng.choice(vals[2:], size=(6, 40))   # hi >= lo, ties at zero included
+    col, width = compact_columns(lo, hi)
+    counts = []
+    for b in range(lo.shape[0]):
+        unstable = [j for j in range(lo.shape[1]) if lo[b, j] < 0 < hi[b, j]]
+        assert [int(col[b, j]) for j in unstable] == list(range(len(unstable)))
+        assert all(col[b, j] == -1 for j in range(lo.shape[1]) if j not in unstable)
+        counts.append(len(unstable))
+    assert width == max(counts)
+
+
+def test_slopes_of_stable_neurons_do_not_matter():
+    """What compact alpha storage relies on: a slope only enters the bound through an
+    unstable neuron, so changing it anywhere else leaves the bound bit-identical."""
+    wl = _alpha_wl()
+    net = Oracle(wl.nodes)
+    lo, hi = intermediate_bounds(net, wl.x0, wl.eps, "crown")
+    rng = np.random.default_rng(3)
+    for b in range(wl.batch):
+        al = {k: torch.as_tensor(rng.uniform(0.1, 0.9, v.shape)) for k, v in alpha_init(net, lo, hi, b, wl.m).items()}
+        ref = evaluate(wl, lo, hi, b, al)
+        moved = {}
+        n_stable = 0
+        for k, v in al.items():
+            z = wl.nodes[k].inputs[0]
+            stable = ~((lo[z][b] < 0) & (hi[z][b] > 0))
+            n_stable += int(stable.sum())
+            moved[k] = torch.where(stable.unsqueeze(0).expand_as(v), torch.as_tensor(rng.uniform(0, 1, v.shape)), v)
+        assert n_stable > 0
+        assert torch.equal(evaluate(wl, lo, hi, b, moved), ref)
