@@ -243,39 +243,58 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
     for (int i = 0; i < AV; ++i) apos[i] = pos_of<DENSE>(d, m0 + (tid + NTHR * i) / (BK / 4));
   }
 
+  // Fast path: the K stages run through the taps in order, 32 channels at a
+  // time, so a thread's A and B addresses are worked out once per tap (the
+  // gather's bounds test included) and each stage only adds its channel
+  // offset.  A dense GEMM is the one-tap case with the whole K as channels.
+  long long abase[FAST ? AV : 1], bbase[FAST ? BV : 1];
+  int ld_j = 0, ld_c = 0;  // tap and channel offset of the next stage to load
+  auto set_tap = [&](int j) {
+    const Tap tp = DENSE ? Tap{0, 0, 0} : tap_of(d, j);
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+      const int f = tid + NTHR * i;
+      const int kq = (f % (BK / 4)) * 4;
+      const Pos& p = apos[i];
+      long long off = -1;
+      if (p.valid) {
+        if (DENSE) {
+          off = p.a_base + kq;
+        } else {
+          const int yy = p.Y * d.sy + tp.dy;
+          const int xx = p.X * d.sx + tp.dx;
+          if (yy >= 0 && yy < d.hs && xx >= 0 && xx < d.ws) off = p.a_base + ((long long)yy * d.ws + xx) * d.cs + kq;
+        }
+      }
+      abase[i] = off;
+    }
+    const long long bt = (long long)tp.w * d.N;
+#pragma unroll
+    for (int i = 0; i < BV; ++i) {
+      const int f = tid + NTHR * i;
+      const int n = f / (BK / 4), kq = (f % (BK / 4)) * 4;
+      const bool ok = f < BN * (BK / 4) && n0 + n < d.N;
+      bbase[i] = ok ? (bt + n0 + n) * d.cs + kq : -1;
+    }
+  };
+
   auto load = [&](int k0) {
     if (FAST) {
-      // one tap per stage: k0 .. k0+31 share tap j
-      const int j = (d.ntaps == 1) ? 0 : k0 / d.cs;
-      const int c0 = k0 - j * d.cs;
-      const Tap tp = tap_of(d, j);
+      (void)k0;
 #pragma unroll
       for (int i = 0; i < AV; ++i) {
-        const int f = tid + NTHR * i;
-        const int kq = (f % (BK / 4)) * 4;
-        long long off = -1;
-        const Pos& p = apos[i];
-        if (p.valid) {
-          if (DENSE) {
-            off = p.a_base + k0 + kq;
-          } else {
-            const int yy = p.Y * d.sy + tp.dy;
-            const int xx = p.X * d.sx + tp.dx;
-            if (yy >= 0 && yy < d.hs && xx >= 0 && xx < d.ws)
-              off = p.a_base + ((long long)yy * d.ws + xx) * d.cs + c0 + kq;
-          }
-        }
         float4 r4;
-        a_val4<AMODE>(d, off, ra[0][i], r4);
+        a_val4<AMODE>(d, abase[i] >= 0 ? abase[i] + ld_c : -1, ra[0][i], r4);
         if (NA == 2) ra[NA - 1][i] = r4;
       }
-      const long long bt = (long long)tp.w * d.N;
 #pragma unroll
-      for (int i = 0; i < BV; ++i) {
-        const int f = tid + NTHR * i;
-        const int n = f / (BK / 4), kq = (f % (BK / 4)) * 4;
-        const bool ok = f < BN * (BK / 4) && n0 + n < d.N;
-        rb[i] = ld4(d.B, ok ? (bt + n0 + n) * d.cs + c0 + kq : -1);
+      for (int i = 0; i < BV; ++i) rb[i] = ld4(d.B, bbase[i] >= 0 ? bbase[i] + ld_c : -1);
+      // advance to the next stage: the next 32 channels, or the next tap
+      ld_c += BK;
+      if (!DENSE && ld_c >= d.cs) {
+        ld_c = 0;
+        ++ld_j;
+        if (ld_j < d.ntaps) set_tap(ld_j);
       }
     } else {
 #pragma unroll
@@ -346,6 +365,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   const int per_slice = (nk_all + ks_n - 1) / ks_n;
   const int kb = ks * per_slice;
   const int nk = min(nk_all - kb, per_slice);
+  if (FAST) {
+    // first stage of this workgroup's K range
+    ld_j = DENSE ? 0 : (kb * BK) / d.cs;
+    ld_c = kb * BK - ld_j * d.cs;
+    set_tap(ld_j);
+  }
   load(kb * BK);
   store(0);
   __syncthreads();
