@@ -441,9 +441,25 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   // then the arithmetic with predicated stores.
   constexpr bool ROWSUM = (EPI != E_IBP && EPI != E_ADJOINT);
   // rows per group (fewer where registers are short)
-  constexpr int G = (FM * FN >= 8 || (VAR == V_COMPACT && FM * FN >= 2)) ? 4 : 8;
+  constexpr int G = (FM * FN >= 2) ? 4 : 8;
+  // The 32 rows of a block i of a gather tile lie in one block of 2^rb_shift
+  // >= 32 rows of the same output position: the position (and its division
+  // work) is decoded once per block, and each element only adds its row
+  // offset.  (Footprint rows need a per-row window decode.)
+  constexpr bool one_pos = !DENSE && VAR != V_PATCH;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
+    int row0 = 0;
+    long long sp0 = 0;
+    bool blk_ok = false;
+    if (one_pos) {
+      const GPos gp = gdecode(d, m0 + wm * WTM + i * 32);
+      blk_ok = m0 + wm * WTM + i * 32 < d.Mt;
+      row0 = gp.row;
+      const int Y = fdiv(gp.q, d.div_gw);
+      const int X = gp.q - Y * d.gw;
+      sp0 = (long long)(Y * d.oym + d.oy0) * d.wo + (X * d.oxm + d.ox0);
+    }
 #pragma unroll
     for (int v0 = 0; v0 < 16; v0 += G) {
       long long opos[G], bpos[G];
@@ -454,7 +470,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
         const int v = v0 + g;
         const int m = m0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
         pin[g] = true;
-        if (DENSE) {
+        if (one_pos) {
+          const int row = row0 + 8 * (v >> 2) + 4 * half + (v & 3);
+          mok[g] = blk_ok && row < d.div_nrows.d;
+          const int rr = mok[g] ? row : 0;
+          rbase[g] = rr * d.acols;
+          opos[g] = (long long)rr * d.ho * d.wo + sp0;
+          bpos[g] = (long long)fdiv(rr, d.div_rows) * d.ho * d.wo + sp0;
+        } else if (DENSE) {
           mok[g] = m < d.M;
           const int mm = mok[g] ? m : 0;
           opos[g] = mm;
@@ -653,13 +676,38 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
         }
       }
       if (ROWSUM) {
+        // Sum each of the G row values over the 32 lanes (columns) of the
+        // half-wave, halving the values held per lane at every exchange: at
+        // distance 16 a lane keeps half of its rows and adds its partner's
+        // copies of them, and so on, G/2 + G/4 + ... + 1 exchanges in all
+        // (plus the rest of the butterfly) instead of 5 per row.  A lane then
+        // holds the total of row `hr`.
+        constexpr int LG = (G == 8) ? 3 : 2;
+        float rs[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float rs = rowsum[g];
+        for (int g = 0; g < G; ++g) rs[g] = rowsum[g];
+        int hr = 0;
 #pragma unroll
-          for (int o = 16; o >= 1; o >>= 1) rs += __shfl_xor(rs, o, 32);
-          const int v = v0 + g;
-          if (l32 == 0) red[wn][wm * WTM + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3)] = rs;
+        for (int st = 0; st < 5; ++st) {
+          const int o = 16 >> st;
+          if (st < LG) {
+            const int w = G >> (st + 1);  // values kept after this exchange
+            const bool up = (l32 & o) != 0;
+#pragma unroll
+            for (int k = 0; k < w; ++k) {
+              const float send = up ? rs[k] : rs[k + w];
+              const float keep = up ? rs[k + w] : rs[k];
+              rs[k] = keep + __shfl_xor(send, o, 32);
+            }
+            hr += up ? w : 0;
+          } else {
+            rs[0] += __shfl_xor(rs[0], o, 32);
+          }
+        }
+        // lanes that agree on bits 4..(5-LG) of l32 hold the same total
+        if ((l32 & ((32 >> LG) - 1)) == 0) {
+          const int v = v0 + hr;
+          red[wn][wm * WTM + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3)] = rs[0];
         }
       }
     }
@@ -782,11 +830,12 @@ bool finalize(GemmDesc& d) {
   d.Mt = d.M;
   d.rb_shift = 0;
   if (!gemm_is_dense(d)) {
-    // blocks of up to 64 rows, fewer where padding the rows to a whole block
-    // would waste more than an eighth of the tiles
+    // blocks of 64 rows, or 32 where padding the rows to a whole block of 64
+    // would waste more than an eighth of the tiles (the epilogue decodes one
+    // output position per 32 rows)
     const long long rows = d.M / (d.gh * d.gw), P = (long long)d.gh * d.gw;
     int sh = 6;
-    while (sh > 0 && (((rows + (1LL << sh) - 1) >> sh << sh) - rows) * 8 > rows) --sh;
+    if ((((rows + 63) >> 6 << 6) - rows) * 8 > rows) sh = 5;
     const long long mt = ((rows + (1LL << sh) - 1) >> sh << sh) * P;
     if (mt > INT32_MAX - 256) return false;
     d.rb_shift = sh;
