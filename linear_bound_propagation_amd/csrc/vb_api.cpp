@@ -605,6 +605,44 @@ vb_status backward_chunk_patch(Backward& B, const BwdCall& c, long long R, const
   return VB_OK;
 }
 
+// Lambda over a conv's few-channel domain node concretised in one direct
+// kernel (no tap-expanded product in between).  `done` stays false (nothing
+// launched) if the kernel does not take the shape.  (Not a GEMM: it is not
+// recorded by the GEMM profile.)
+vb_status direct_conv_input(Backward& B, const NodeInfo& nd, const NodeInfo& tn, int t, int rows, int cur, int pbuf,
+                            const BwdCall& c, bool& done) {
+  done = false;
+  ConvIn a{};
+  a.lam = B.pool[cur];
+  a.W = nd.W;
+  a.Co = nd.c;
+  a.Ho = nd.h;
+  a.Wo = nd.w;
+  a.Ci = tn.c;
+  a.Hi = tn.h;
+  a.Wi = tn.w;
+  a.kh = nd.kh;
+  a.kw = nd.kw;
+  a.stride = nd.stride;
+  a.pad = nd.pad;
+  const long long R = rows / c.cb;
+  a.rows_per_b = (int)R;
+  if (!conv_input_fits(a) || conv_input_part_floats(a, rows) > B.part_floats) return VB_OK;
+  a.addend = pbuf >= 0 ? B.pool[pbuf] : nullptr;
+  a.psi_out = (B.psi_keep && B.psi_keep[t]) ? B.psi_keep[t] + (long long)c.b0 * R * tn.size : nullptr;
+  if (t == 0) {
+    a.center = B.dom.xc + (long long)c.b0 * tn.size;
+    a.radius = B.dom.xr ? B.dom.xr + (long long)c.b0 * tn.size : nullptr;
+    a.eps = B.dom.eps;
+  } else {
+    a.center = B.box_c;
+    a.radius = B.box_r;
+  }
+  HIPCHK(launch_conv_input_concretize(a, rows, B.part, B.rowacc, B.st));
+  done = true;
+  return VB_OK;
+}
+
 // Execute the back-substitution of call `c`; rowacc receives the lower bound
 // of every row (rows = cb * R).  Lambda of a node is a pool buffer, or IDENT:
 // the implicit +-I over the start node (identity rows), which Linear and Conv
@@ -766,6 +804,11 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
         if (s) return s;
       }
       const int tgt_bounds = (epi == E_RELAX) ? z : t;
+      bool direct = false;
+      if (!ident && nd.op == VB_CONV2D && epi == E_CONCRETIZE) {
+        vb_status s = direct_conv_input(B, nd, tn, t, rows, cur, pbuf, c, direct);
+        if (s) return s;
+      }
       if (ident) {
         // rows +-I over this conv's output: footprint kernel, no GEMM
         IdConv a{};
@@ -799,6 +842,9 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
         }
         if ((long long)2 * nd.size != R) return fail(VB_ESHAPE, "internal: identity rows do not match node %d", k);
         HIPCHK(launch_identity_conv(a, c.cb, B.rowacc, B.st));
+      } else if (direct) {
+        // few-channel domain: the transposed conv and the concretisation in one pass
+        B.release(cur);
       } else if (nd.op == VB_CONV2D && tn.c <= 8 && nd.kh * nd.kw * tn.c <= 64 && epi != E_STORE &&
                  (size_t)rows * nd.h * nd.w * nd.kh * nd.kw * tn.c <= B.pool_floats &&
                  (B.alpha == nullptr || B.alpha[t] == nullptr)) {

@@ -213,6 +213,31 @@ struct Col2Im {
 };
 hipError_t launch_col2im(const Col2Im& a, int rows, float* rowacc, hipStream_t st);
 
+// Lambda over the input of a conv with few input channels (the domain node),
+// from Lambda over its output, concretised: L_in[row][y][x][ci] = sum over
+// taps (ky, kx) with oy = (y + pad - ky) / stride and ox = (x + pad - kx) /
+// stride exact and in range, and over output channels co, of
+// L_out[row][oy][ox][co] W[ky][kx][co][ci] (+ addend); then
+// rowacc[row] += sum L_in c - |L_in| r over the row's domain box.  Direct
+// VALU kernel: a workgroup stages the output rows a band of input rows needs
+// in LDS and each thread accumulates its pixels' Ci values (vb_kernels.hip).
+struct ConvIn {
+  const float* lam;     // [rows][Ho][Wo][Co]
+  const float* W;       // [kh][kw][Co][Ci]
+  int Co, Ho, Wo, Ci, Hi, Wi, kh, kw, stride, pad;
+  int rows_per_b;
+  const float* addend;  // [rows][Hi][Wi][Ci] or NULL
+  float* psi_out;       // receives L_in, or NULL
+  const float* center;  // [batch][Hi][Wi][Ci]
+  const float* radius;  // or NULL -> eps
+  float eps;
+};
+// Whether the direct kernel takes this shape (Ci <= 4, Co % 4 == 0, bands fit in LDS).
+bool conv_input_fits(const ConvIn& a);
+// part: rows * ceil(Hi / band rows) floats of scratch.
+hipError_t launch_conv_input_concretize(const ConvIn& a, int rows, float* part, float* rowacc, hipStream_t st);
+size_t conv_input_part_floats(const ConvIn& a, int rows);
+
 // Identity rows over a node of C channels, each on its own 1 x 1 window:
 // out [rows][C] with out[row][c'] = +-1 at c' = row's channel (rows_per_b = R).
 hipError_t launch_patch_identity(int rows, int R, int C, float* out, hipStream_t st);

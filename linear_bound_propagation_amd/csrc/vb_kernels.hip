@@ -310,6 +310,150 @@ hipError_t launch_col2im(const Col2Im& a, int rows, float* rowacc, hipStream_t s
   return hipGetLastError();
 }
 
+namespace {
+constexpr int CIN_THREADS = 256;  // threads of a conv-input workgroup, one input pixel each
+constexpr int CIN_CO = 16;        // output channels staged per pass
+constexpr int CIN_PS = CIN_CO / 4 + 1;  // float4 per staged pixel (one of padding: conflict-free reads)
+constexpr size_t CIN_LDS = 32 * 1024;
+
+// input rows per band: one pixel per thread, fewer rows if the staged output
+// rows would not fit the LDS budget
+int cin_band_rows(const ConvIn& a) {
+  int bh = CIN_THREADS / a.Wi;
+  if (bh > a.Hi) bh = a.Hi;
+  while (bh >= 1) {
+    const int nr = (bh + a.kh - 1 + a.stride - 1) / a.stride + 1;
+    if ((size_t)nr * a.Wo * CIN_PS * 16 <= CIN_LDS) return bh;
+    --bh;
+  }
+  return 0;
+}
+}  // namespace
+
+bool conv_input_fits(const ConvIn& a) {
+  return a.Ci >= 1 && a.Ci <= 4 && a.Co % CIN_CO == 0 && a.Wi <= CIN_THREADS && a.stride >= 1 &&
+         ((uintptr_t)a.W & 15) == 0 && ((uintptr_t)a.lam & 15) == 0 && cin_band_rows(a) >= 1;
+}
+
+size_t conv_input_part_floats(const ConvIn& a, int rows) {
+  const int bh = cin_band_rows(a);
+  return bh < 1 ? 0 : (size_t)rows * ((a.Hi + bh - 1) / bh);
+}
+
+template <int CI, bool S1>
+__global__ __launch_bounds__(CIN_THREADS) void conv_input_concretize_kernel(const ConvIn a, int BH,
+                                                                           float* __restrict__ part) {
+  extern __shared__ float4 sl[];  // [nr][Wo][CIN_PS] float4: CIN_CO channels of each staged pixel
+  __shared__ float sh[CIN_THREADS / 64];
+  const int band = blockIdx.x, nb = gridDim.x;
+  const long long row = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int y0 = band * BH, y1 = min(a.Hi, y0 + BH);
+  const int s = S1 ? 1 : a.stride;
+  // output rows read by this band: oy * s in [y0 + pad - (kh - 1), y1 - 1 + pad]
+  const int lo = y0 + a.pad - (a.kh - 1);
+  const int oy_lo = lo <= 0 ? 0 : (lo + s - 1) / s;
+  const int oy_hi = min(a.Ho - 1, (y1 - 1 + a.pad) / s);
+  const int nr = oy_hi - oy_lo + 1;
+  const int C4 = a.Co / 4;
+  const int ntap = a.kh * a.kw;
+  const bool mine = tid < (y1 - y0) * a.Wi;  // this thread's input pixel lies in the band
+  const int py = y0 + tid / a.Wi, px = tid % a.Wi;
+
+  float acc[CI];
+#pragma unroll
+  for (int ci = 0; ci < CI; ++ci) acc[ci] = 0.f;
+  const float4* src = reinterpret_cast<const float4*>(a.lam) + ((row * a.Ho + (nr > 0 ? oy_lo : 0)) * a.Wo) * C4;
+  const int npx = nr * a.Wo;
+  // staged pixel of tap t for this thread, or -1 (outside the image or off the stride)
+  auto tap_pix = [&](int t) -> int {
+    const int ky = t / a.kw, kx = t - ky * a.kw;
+    const int ty = py + a.pad - ky, tx = px + a.pad - kx;
+    if (!mine || ty < 0 || tx < 0) return -1;
+    if (S1) return (ty <= oy_hi && tx < a.Wo) ? (ty - oy_lo) * a.Wo + tx : -1;
+    if (ty % s || tx % s || ty / s > oy_hi || tx / s >= a.Wo) return -1;
+    return (ty / s - oy_lo) * a.Wo + tx / s;
+  };
+  for (int c0 = 0; c0 < C4; c0 += CIN_CO / 4) {
+    // stage CIN_CO channels of the rows [oy_lo, oy_hi] of this row's Lambda
+    __syncthreads();
+    for (int e = tid; e < npx * (CIN_CO / 4); e += CIN_THREADS) {
+      const int pix = e / (CIN_CO / 4), c = e - pix * (CIN_CO / 4);
+      sl[pix * CIN_PS + c] = src[(long long)pix * C4 + c0 + c];
+    }
+    __syncthreads();
+    // weights of tap t, channels 4*c0 .. 4*c0 + CIN_CO: the same for every
+    // thread (scalar loads)
+    for (int t = 0; t < ntap; ++t) {
+      const int q = tap_pix(t);
+      if (q >= 0) {
+        const float4* L = sl + q * CIN_PS;
+        const float* w = a.W + ((long long)t * a.Co + 4 * c0) * CI;
+#pragma unroll
+        for (int c = 0; c < CIN_CO / 4; ++c) {
+          const float4 l = L[c];
+#pragma unroll
+          for (int ci = 0; ci < CI; ++ci)
+            acc[ci] += l.x * w[(4 * c) * CI + ci] + l.y * w[(4 * c + 1) * CI + ci] + l.z * w[(4 * c + 2) * CI + ci] +
+                       l.w * w[(4 * c + 3) * CI + ci];
+        }
+      }
+    }
+  }
+  // concretise over the domain box
+  float sum = 0.f;
+  if (mine) {
+    const long long b = row / a.rows_per_b;
+    const long long pix = (long long)py * a.Wi + px;
+#pragma unroll
+    for (int ci = 0; ci < CI; ++ci) {
+      const long long e = (row * a.Hi * a.Wi + pix) * CI + ci;
+      float v = acc[ci];
+      if (a.addend) v += a.addend[e];
+      if (a.psi_out) a.psi_out[e] = v;
+      const long long be = (b * a.Hi * a.Wi + pix) * CI + ci;
+      const float r = a.radius ? a.radius[be] : a.eps;
+      sum += v * a.center[be] - fabsf(v) * r;
+    }
+  }
+  sum = wave_sum(sum);
+  if ((tid & 63) == 0) sh[tid >> 6] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < CIN_THREADS / 64; ++w) t += sh[w];
+    part[row * nb + band] = t;
+  }
+}
+
+template <int CI>
+void cin_launch(bool s1, dim3 g, dim3 blk, size_t lds, hipStream_t st, const ConvIn& a, int bh, float* part) {
+  if (s1)
+    hipLaunchKernelGGL((conv_input_concretize_kernel<CI, true>), g, blk, lds, st, a, bh, part);
+  else
+    hipLaunchKernelGGL((conv_input_concretize_kernel<CI, false>), g, blk, lds, st, a, bh, part);
+}
+
+hipError_t launch_conv_input_concretize(const ConvIn& a, int rows, float* part, float* rowacc, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const int bh = cin_band_rows(a);
+  if (bh < 1 || a.Ci < 1 || a.Ci > 4) return hipErrorInvalidValue;
+  const int nb = (a.Hi + bh - 1) / bh;
+  const int nr = (bh + a.kh - 1 + a.stride - 1) / a.stride + 1;
+  const size_t lds = (size_t)nr * a.Wo * CIN_PS * sizeof(float4);
+  const dim3 g((unsigned)nb, (unsigned)rows), blk(CIN_THREADS);
+  switch (a.Ci) {
+    case 1: cin_launch<1>(a.stride == 1, g, blk, lds, st, a, bh, part); break;
+    case 2: cin_launch<2>(a.stride == 1, g, blk, lds, st, a, bh, part); break;
+    case 3: cin_launch<3>(a.stride == 1, g, blk, lds, st, a, bh, part); break;
+    default: cin_launch<4>(a.stride == 1, g, blk, lds, st, a, bh, part); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_rows_reduce(part, 1, rows, nb, 1, 1, rowacc, 1, 0, st);
+}
+
 // Identity rows (b, sign, p, c) over a node of P pixels and C channels, on
 // each row's own 1 x 1 window: out[row][c'] = sign if c' == c else 0.
 __global__ void patch_identity_kernel(long long rows, int R, int C, float* __restrict__ out) {

@@ -37,13 +37,15 @@ def _oracle(wl, steps, batch_idx=None):
 
 
 @pytest.mark.parametrize("compact", [False, True])
-@pytest.mark.parametrize("kind", ["mlp", "cnn"])
+@pytest.mark.parametrize("kind", ["mlp", "cnn", "cnn8"])
 def test_alpha_small(lbp, kind, compact):
     if kind == "mlp":
         wl = wk.tiny_mlp([40, 70, 50, 8], 0.08, 21, batch=3)
         wl.intermediate = "ibp"
-    else:
+    elif kind == "cnn":
         wl = wk.cnn(2, 0.02, 22, convs=((6, 1), (12, 2)), fcs=(30, 10), in_shape=(3, 8, 8))
+    else:  # first conv with a multiple of 4 output channels: the direct domain kernel keeps Psi
+        wl = wk.cnn(2, 0.02, 24, convs=((8, 1), (12, 2)), fcs=(30, 10), in_shape=(3, 8, 8))
     steps = 8
     print(f"alpha {kind} steps {steps} compact {compact}", flush=True)
     out, best, lb_steps, (alpha, _, _), lay = _gpu_alpha(lbp, wl, steps, compact)

@@ -97,3 +97,36 @@ def test_config3_crown_intermediates_sampled_rows(lbp):
         print(f"node {z}: {nd.shape}", flush=True)
         assert_close(out["lo"][z][b][pos], ref[:40], f"lo[{z}] sampled")
         assert_close(out["hi"][z][b][pos], -ref[40:], f"hi[{z}] sampled")
+
+
+def _first_conv_net(seed, in_shape, c_out, k, stride, pad, batch=2, eps=0.02, intermediate="crown"):
+    """conv(k, stride, pad) + ReLU, conv 3x3 + ReLU, flatten, FC, FC."""
+    import numpy as np
+    rng_w = np.random.default_rng([seed, 0])
+    rng_x = np.random.default_rng([seed, 1])
+    nb = wk.NetBuilder(rng_w, "he")
+    x = nb.input(in_shape)
+    x = nb.relu(nb.conv(x, c_out, k, stride, pad))
+    x = nb.relu(nb.conv(x, 8, 3, 1, 1))
+    x = nb.flatten(x)
+    x = nb.relu(nb.linear(x, 16))
+    x = nb.linear(x, 7)
+    x0 = rng_x.random((batch,) + tuple(in_shape)).astype(np.float32)
+    labels, C = wk.margin_specs(nb.nodes, x0)
+    return wk.Workload("first_conv", seed, nb.nodes, x0, np.float32(eps), labels, C, intermediate)
+
+
+@pytest.mark.parametrize("in_shape,c_out,k,stride,pad", [
+    ((3, 11, 9), 8, 3, 2, 1),     # stride 2, odd sizes: taps of both parities
+    ((1, 12, 12), 12, 3, 1, 2),   # one input channel, padding wider than the halo
+    ((4, 9, 10), 16, 3, 2, 0),    # four input channels, no padding
+    ((2, 7, 7), 4, 3, 1, 1),      # two input channels
+])
+def test_first_conv_to_domain(lbp, in_shape, c_out, k, stride, pad):
+    """The transposed first conv and the concretisation over the input box in one
+    kernel (few input channels): every bound of the network against the oracle."""
+    wl = _first_conv_net(31, in_shape, c_out, k, stride, pad)
+    print(f"first conv {in_shape} -> {c_out} k{k} s{stride} p{pad}", flush=True)
+    ref = crown_bounds(wl)
+    out = _run(lbp, wl)
+    compare_workload(wl, out, ref)
