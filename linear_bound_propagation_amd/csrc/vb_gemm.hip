@@ -441,7 +441,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   // then the arithmetic with predicated stores.
   constexpr bool ROWSUM = (EPI != E_IBP && EPI != E_ADJOINT);
   // rows per group (fewer where registers are short)
-  constexpr int G = (FM * FN >= 2) ? 4 : 8;
+  constexpr int G = (FM * FN >= 2 || VAR == V_COMPACT) ? 4 : 8;
   // The 32 rows of a block i of a gather tile lie in one block of 2^rb_shift
   // >= 32 rows of the same output position: the position (and its division
   // work) is decoded once per block, and each element only adds its row
@@ -449,16 +449,22 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   constexpr bool one_pos = !DENSE && VAR != V_PATCH;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    int row0 = 0;
-    long long sp0 = 0;
+    int row0 = 0, r0 = 0, b0 = 0;
+    long long obase = 0, bbase = 0;  // element offsets of (r0, position) in the output and in coef
     bool blk_ok = false;
+    const int HWN = d.ho * d.wo * d.N;  // elements per row (the host keeps 32 * HWN < 2^31)
     if (one_pos) {
       const GPos gp = gdecode(d, m0 + wm * WTM + i * 32);
       blk_ok = m0 + wm * WTM + i * 32 < d.Mt;
       row0 = gp.row;
       const int Y = fdiv(gp.q, d.div_gw);
       const int X = gp.q - Y * d.gw;
-      sp0 = (long long)(Y * d.oym + d.oy0) * d.wo + (X * d.oxm + d.ox0);
+      const long long sp0 = (long long)(Y * d.oym + d.oy0) * d.wo + (X * d.oxm + d.ox0);
+      // padding rows address row r0 (a valid row) and are never stored
+      r0 = min(row0, d.div_nrows.d - 1);
+      b0 = fdiv(r0, d.div_rows);
+      obase = ((long long)r0 * d.ho * d.wo + sp0) * d.N;
+      bbase = ((long long)b0 * d.ho * d.wo + sp0) * d.N;
     }
 #pragma unroll
     for (int v0 = 0; v0 < 16; v0 += G) {
@@ -471,12 +477,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
         const int m = m0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
         pin[g] = true;
         if (one_pos) {
+          // offsets from (r0, position): 32-bit arithmetic per element
           const int row = row0 + 8 * (v >> 2) + 4 * half + (v & 3);
           mok[g] = blk_ok && row < d.div_nrows.d;
-          const int rr = mok[g] ? row : 0;
+          const int rr = mok[g] ? row : r0;
           rbase[g] = rr * d.acols;
-          opos[g] = (long long)rr * d.ho * d.wo + sp0;
-          bpos[g] = (long long)fdiv(rr, d.div_rows) * d.ho * d.wo + sp0;
+          opos[g] = (rr - r0) * HWN;
+          bpos[g] = (fdiv(rr, d.div_rows) - b0) * HWN;
         } else if (DENSE) {
           mok[g] = m < d.M;
           const int mm = mok[g] ? m : 0;
@@ -519,8 +526,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
         long long oi[G], bi[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          oi[g] = opos[g] * d.N + nn;
-          bi[g] = bpos[g] * d.N + nn;
+          if (one_pos) {
+            oi[g] = obase + (unsigned)((int)opos[g] + nn);
+            bi[g] = bbase + (unsigned)((int)bpos[g] + nn);
+          } else {
+            oi[g] = opos[g] * d.N + nn;
+            bi[g] = bpos[g] * d.N + nn;
+          }
         }
         // per-neuron state (alpha, kept Psi, Adam moments): at oi, or in the
         // compact layout at the neuron's column of the element's row (the column
@@ -838,6 +850,8 @@ bool finalize(GemmDesc& d) {
     if ((((rows + 63) >> 6 << 6) - rows) * 8 > rows) sh = 5;
     const long long mt = ((rows + (1LL << sh) - 1) >> sh << sh) * P;
     if (mt > INT32_MAX - 256) return false;
+    // the epilogue's per-block element offsets are 32-bit
+    if (32LL * d.ho * d.wo * d.N >= (1LL << 31)) return false;
     d.rb_shift = sh;
     d.Mt = (int)mt;
   }
