@@ -305,6 +305,41 @@ def test_crown_backward_with_compact_alpha(lbp, case):
         assert_close(lba[b], ref, f"compact alpha lb input {b}")
 
 
+@pytest.mark.parametrize("compact", [False, True])
+@pytest.mark.parametrize("case", ["mlp", "cnn"])
+def test_crown_backward_alpha_chunked_batch(lbp, case, compact):
+    """Given slopes with a workspace for one batch element at a time: the chunks
+    address the slopes (and the compact column maps) at their own offsets, so the
+    bounds equal the whole-batch call bit for bit."""
+    wl = CASES[case]()
+    on, lo, hi = _fp32_bounds(wl)
+    net, x, C = lbp.prepare(wl)
+    dlo, dhi = _to_device(lbp, net, wl, lo, hi)
+    L = len(wl.nodes) - 1
+    lay = lbp.alpha_layout(net, dlo, dhi) if compact else None
+    cols = _host_columns(wl, lo, hi)
+    rng = np.random.default_rng(17)
+    alpha_dev = [None] * len(wl.nodes)
+    for r, nd in enumerate(wl.nodes):
+        if nd.op != "relu":
+            continue
+        a = rng.random((wl.batch * wl.m,) + tuple(nd.shape)).astype(np.float32)
+        dense = nhwc(a, nd.shape).reshape(wl.batch, wl.m, -1)
+        if compact:
+            col, width = cols[r]
+            if width > 0:
+                alpha_dev[r] = torch.as_tensor(_compact_from_dense(dense, col, width), device=x.device)
+        else:
+            alpha_dev[r] = torch.as_tensor(dense, device=x.device)
+    ws_full = net.workspace(net.workspace_size(wl.batch, wl.m, "crown"))
+    full, _ = lbp.crown_backward(net, L, 0, dlo, dhi, x, float(wl.eps), ws_full, C=C, alpha=alpha_dev, layout=lay)
+    ws_one = net.workspace(net.workspace_size(1, wl.m, "crown"))
+    part, _ = lbp.crown_backward(net, L, 0, dlo, dhi, x, float(wl.eps), ws_one, C=C, alpha=alpha_dev, layout=lay)
+    torch.cuda.synchronize()
+    assert ws_one.numel() < ws_full.numel()
+    assert torch.equal(full, part)
+
+
 def test_alpha_init_compact(lbp):
     wl = CASES["cnn"]()
     on, lo, hi = _fp32_bounds(wl)
