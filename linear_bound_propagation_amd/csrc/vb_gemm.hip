@@ -603,9 +603,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
           if (d.alpha) {
 #pragma unroll
             for (int g = 0; g < G; ++g) {
+              // (compact state: stable neurons have no entry and load nothing)
               const int col = __float_as_int(cf[g].w);
-              const float t = d.alpha[state_at(g, col)];
-              al[g] = col >= 0 ? t : al[g];
+              if (VAR == V_COMPACT) {
+                if (col >= 0) al[g] = d.alpha[state_at(g, col)];
+              } else {
+                const float t = d.alpha[state_at(g, col)];
+                al[g] = col >= 0 ? t : al[g];
+              }
             }
           }
 #pragma unroll
@@ -631,12 +636,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             ai[g] = state_at(g, __float_as_int(cf[g].w));
-            psi[g] = have ? d.psi_in[ai[g]] : 0.f;
-            aold[g] = have ? d.alpha_rw[ai[g]] : 0.f;
-          }
-          if (d.do_update && have) {
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
+            // (compact state: only unstable neurons have an entry to load)
+            const bool ld = have && (VAR != V_COMPACT || __float_as_int(cf[g].w) >= 0);
+            psi[g] = ld ? d.psi_in[ai[g]] : 0.f;
+            aold[g] = ld ? d.alpha_rw[ai[g]] : 0.f;
+            am[g] = av[g] = 0.f;
+            if (d.do_update && ld) {
               am[g] = d.adam_m[ai[g]];
               av[g] = d.adam_v[ai[g]];
             }
