@@ -232,7 +232,8 @@ struct ConvIn {
   const float* radius;  // or NULL -> eps
   float eps;
 };
-// Whether the direct kernel takes this shape (Ci <= 4, Co % 4 == 0, bands fit in LDS).
+// Whether the direct kernel takes this shape (Ci <= 4, Co a multiple of 16 up to 64,
+// at most 48 (tap, input channel) pairs, bands fit in LDS).
 bool conv_input_fits(const ConvIn& a);
 // part: rows * ceil(Hi / band rows) floats of scratch.
 hipError_t launch_conv_input_concretize(const ConvIn& a, int rows, float* part, float* rowacc, hipStream_t st);

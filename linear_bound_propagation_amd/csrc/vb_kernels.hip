@@ -1,7 +1,8 @@
 // Small HIP kernels of the bound propagation library (gfx950): row
 // reductions, spec and identity row set-up, standalone relaxation and
-// concretisation, IBP elementwise nodes, weight transposition.  The MFMA
-// implicit GEMM lives in vb_gemm.hip.  All reductions run in a fixed order
+// concretisation, IBP elementwise nodes, weight transposition, and the last
+// back-substitution step onto a few-channel domain (on 16x16x4 matrix
+// blocks).  The implicit GEMM lives in vb_gemm.hip.  All reductions run in a fixed order
 // (wavefront shuffles, then a fixed combination of wavefronts), so results
 // are bitwise reproducible.
 #include <hip/hip_runtime.h>
@@ -311,19 +312,27 @@ hipError_t launch_col2im(const Col2Im& a, int rows, float* rowacc, hipStream_t s
 }
 
 namespace {
-constexpr int CIN_THREADS = 256;  // threads of a conv-input workgroup, one input pixel each
-constexpr int CIN_CO = 16;        // output channels staged per pass
-constexpr int CIN_PS = CIN_CO / 4 + 1;  // float4 per staged pixel (one of padding: conflict-free reads)
-constexpr size_t CIN_LDS = 32 * 1024;
+constexpr int CIN_THREADS = 256;         // threads of a conv-input workgroup, one input pixel each
+constexpr int CIN_MAX_CO = 64;           // output channels: one 16-step pass of the contraction
+constexpr int CIN_MB = 3;                // M-blocks whose loads are issued together
+constexpr size_t CIN_Y_LDS = 64 * 1024;  // bytes of a band's tap table
+typedef float cin_v4 __attribute__((ext_vector_type(4)));
 
-// input rows per band: one pixel per thread, fewer rows if the staged output
-// rows would not fit the LDS budget
+// Columns of the tap table (tap x domain channel) in blocks of 16.
+int cin_col_blocks(const ConvIn& a) { return (a.kh * a.kw * a.Ci + 15) / 16; }
+// Floats per tap-table row: the columns, rounded up to an odd count so that
+// threads reading consecutive rows hit distinct LDS banks.
+__host__ __device__ inline int cin_row_floats(int ncol) { return ncol | 1; }
+
+// Input rows per band: one output pixel per thread, and the tap table of the
+// band's staged output rows within CIN_Y_LDS.
 int cin_band_rows(const ConvIn& a) {
+  const int ys = cin_row_floats(a.kh * a.kw * a.Ci);
   int bh = CIN_THREADS / a.Wi;
   if (bh > a.Hi) bh = a.Hi;
   while (bh >= 1) {
     const int nr = (bh + a.kh - 1 + a.stride - 1) / a.stride + 1;
-    if ((size_t)nr * a.Wo * CIN_PS * 16 <= CIN_LDS) return bh;
+    if ((size_t)nr * a.Wo * ys * sizeof(float) <= CIN_Y_LDS) return bh;
     --bh;
   }
   return 0;
@@ -331,8 +340,9 @@ int cin_band_rows(const ConvIn& a) {
 }  // namespace
 
 bool conv_input_fits(const ConvIn& a) {
-  return a.Ci >= 1 && a.Ci <= 4 && a.Co % CIN_CO == 0 && a.Wi <= CIN_THREADS && a.stride >= 1 &&
-         ((uintptr_t)a.W & 15) == 0 && ((uintptr_t)a.lam & 15) == 0 && cin_band_rows(a) >= 1;
+  return a.Ci >= 1 && a.Ci <= 4 && a.Co % 16 == 0 && a.Co <= CIN_MAX_CO && a.Wi <= CIN_THREADS && a.stride >= 1 &&
+         ((uintptr_t)a.W & 15) == 0 && ((uintptr_t)a.lam & 15) == 0 && cin_col_blocks(a) <= 3 &&
+         cin_band_rows(a) >= 1;
 }
 
 size_t conv_input_part_floats(const ConvIn& a, int rows) {
@@ -340,75 +350,140 @@ size_t conv_input_part_floats(const ConvIn& a, int rows) {
   return bh < 1 ? 0 : (size_t)rows * ((a.Hi + bh - 1) / bh);
 }
 
-template <int CI, bool S1>
-__global__ __launch_bounds__(CIN_THREADS) void conv_input_concretize_kernel(const ConvIn a, int BH,
-                                                                           float* __restrict__ part) {
-  extern __shared__ float4 sl[];  // [nr][Wo][CIN_PS] float4: CIN_CO channels of each staged pixel
+// The last back-substitution step onto a few-channel domain on the matrix
+// cores, in two phases per (row, band of input rows):
+//  1. tap table Y[q][t * CI + ci] = sum_co Lambda[q][co] * W[t][co][ci] for
+//     every staged output pixel q: a K = Co contraction with the (tap, domain
+//     channel) pairs as N, on 16x16x4 fp32 blocks (A: pixel = lane % 16,
+//     channel step = lane / 16; B: channel step = lane / 16, column = lane % 16;
+//     result element (4 * (lane / 16) + v, lane % 16) in component v). Each
+//     Lambda element is loaded once, straight from global memory.
+//  2. each thread sums the taps that reach its input pixel from the table in
+//     LDS, adds the addend, stores Psi if asked, and concretises.
+// Consecutive workgroups go round-robin over the 8 XCDs; with xcd_map the
+// bands of one row share an XCD, so the rows two bands both stage are read
+// through one L2.
+template <int CI, int NB, bool S1>
+__global__ __launch_bounds__(CIN_THREADS) void conv_input_concretize_kernel(const ConvIn a, int BH, int nbands,
+                                                                           int xcd_map, float* __restrict__ part) {
+  extern __shared__ float ys[];  // [staged pixels][ysw]
   __shared__ float sh[CIN_THREADS / 64];
-  const int band = blockIdx.x, nb = gridDim.x;
-  const long long row = blockIdx.y;
-  const int tid = threadIdx.x;
+  constexpr int WAVES = CIN_THREADS / 64;
+  const unsigned n = blockIdx.x;
+  long long row;
+  int band;
+  if (xcd_map) {
+    const unsigned slot = n >> 3, rb = slot / (unsigned)nbands;
+    band = (int)(slot - rb * (unsigned)nbands);
+    row = (long long)rb * 8 + (n & 7);
+  } else {
+    row = n / (unsigned)nbands;
+    band = (int)(n - (unsigned)row * (unsigned)nbands);
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int y0 = band * BH, y1 = min(a.Hi, y0 + BH);
   const int s = S1 ? 1 : a.stride;
-  // output rows read by this band: oy * s in [y0 + pad - (kh - 1), y1 - 1 + pad]
   const int lo = y0 + a.pad - (a.kh - 1);
   const int oy_lo = lo <= 0 ? 0 : (lo + s - 1) / s;
   const int oy_hi = min(a.Ho - 1, (y1 - 1 + a.pad) / s);
   const int nr = oy_hi - oy_lo + 1;
-  const int C4 = a.Co / 4;
+  const int npx = nr > 0 ? nr * a.Wo : 0;
   const int ntap = a.kh * a.kw;
-  const bool mine = tid < (y1 - y0) * a.Wi;  // this thread's input pixel lies in the band
-  const int py = y0 + tid / a.Wi, px = tid % a.Wi;
+  const int ncol = ntap * CI;
+  const int ysw = cin_row_floats(ncol);
+  const int li = lane & 15, kk = lane >> 4;
+  const float* lam_r = a.lam + (row * a.Ho + (nr > 0 ? oy_lo : 0)) * (long long)a.Wo * a.Co;
 
-  float acc[CI];
+  // phase 1: tap table. Step j = 4u + c takes channel 16u + 4 * (lane / 16) + c,
+  // so that one load instruction (fixed u) reads 64 contiguous bytes of each
+  // of 16 pixels.
+  float bw[NB][16];  // B: weights of column li of each block, 16 steps
 #pragma unroll
-  for (int ci = 0; ci < CI; ++ci) acc[ci] = 0.f;
-  const float4* src = reinterpret_cast<const float4*>(a.lam) + ((row * a.Ho + (nr > 0 ? oy_lo : 0)) * a.Wo) * C4;
-  const int npx = nr * a.Wo;
-  // staged pixel of tap t for this thread, or -1 (outside the image or off the stride)
-  auto tap_pix = [&](int t) -> int {
-    const int ky = t / a.kw, kx = t - ky * a.kw;
-    const int ty = py + a.pad - ky, tx = px + a.pad - kx;
-    if (!mine || ty < 0 || tx < 0) return -1;
-    if (S1) return (ty <= oy_hi && tx < a.Wo) ? (ty - oy_lo) * a.Wo + tx : -1;
-    if (ty % s || tx % s || ty / s > oy_hi || tx / s >= a.Wo) return -1;
-    return (ty / s - oy_lo) * a.Wo + tx / s;
-  };
-  for (int c0 = 0; c0 < C4; c0 += CIN_CO / 4) {
-    // stage CIN_CO channels of the rows [oy_lo, oy_hi] of this row's Lambda
-    __syncthreads();
-    for (int e = tid; e < npx * (CIN_CO / 4); e += CIN_THREADS) {
-      const int pix = e / (CIN_CO / 4), c = e - pix * (CIN_CO / 4);
-      sl[pix * CIN_PS + c] = src[(long long)pix * C4 + c0 + c];
+  for (int nb = 0; nb < NB; ++nb) {
+    const int col = nb * 16 + li;
+    const bool okn = col < ncol;
+    const int t = okn ? col / CI : 0, ci = okn ? col - t * CI : 0;
+    const float* w = a.W + ((long long)t * a.Co + 4 * kk) * CI + ci;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int off = 16 * (j >> 2) + (j & 3);
+      bw[nb][j] = okn && 16 * (j >> 2) < a.Co ? w[off * CI] : 0.f;
     }
-    __syncthreads();
-    // weights of tap t, channels 4*c0 .. 4*c0 + CIN_CO: the same for every
-    // thread (scalar loads)
-    for (int t = 0; t < ntap; ++t) {
-      const int q = tap_pix(t);
-      if (q >= 0) {
-        const float4* L = sl + q * CIN_PS;
-        const float* w = a.W + ((long long)t * a.Co + 4 * c0) * CI;
+  }
+  const int nmb = (npx + 15) / 16;
+  const int nit = wave < nmb ? (nmb - wave + WAVES - 1) / WAVES : 0;  // M-blocks of this wavefront
+  auto load_a = [&](int it, float4 (&v)[4]) {
+    const int mb = wave + WAVES * it;
+    // rows past the staged pixels are clamped (their results are never
+    // stored); channel groups past Co are clamped and meet zero weights.
+    // No load is predicated, so the waits before each M-block's products
+    // cover only that block's loads.
+    const int q = min(mb * 16 + li, npx - 1);
+    const float4* ap = reinterpret_cast<const float4*>(lam_r + (long long)q * a.Co + 4 * kk);
 #pragma unroll
-        for (int c = 0; c < CIN_CO / 4; ++c) {
-          const float4 l = L[c];
+    for (int u = 0; u < 4; ++u) v[u] = ap[16 * u < a.Co ? 4 * u : 0];
+  };
+  cin_v4 acc[NB];
+  // the loads of up to CIN_MB M-blocks are issued together
+  for (int g0 = 0; g0 < nit; g0 += CIN_MB) {
+    float4 av[CIN_MB][4];
 #pragma unroll
-          for (int ci = 0; ci < CI; ++ci)
-            acc[ci] += l.x * w[(4 * c) * CI + ci] + l.y * w[(4 * c + 1) * CI + ci] + l.z * w[(4 * c + 2) * CI + ci] +
-                       l.w * w[(4 * c + 3) * CI + ci];
+    for (int i = 0; i < CIN_MB; ++i) load_a(min(g0 + i, nit - 1), av[i]);
+#pragma unroll
+    for (int i = 0; i < CIN_MB; ++i) {
+      if (g0 + i >= nit) break;
+      const int mb = wave + WAVES * (g0 + i);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = cin_v4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float4 c4 = av[i][j >> 2];
+        const float a1 = (j & 3) == 0 ? c4.x : (j & 3) == 1 ? c4.y : (j & 3) == 2 ? c4.z : c4.w;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bw[nb][j], acc[nb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int q = mb * 16 + 4 * kk + v;
+        if (q < npx) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            if (nb * 16 + li < ncol) ys[q * ysw + nb * 16 + li] = acc[nb][v];
         }
       }
     }
   }
-  // concretise over the domain box
+  __syncthreads();
+
+  // phase 2: taps onto this thread's input pixel, concretisation
   float sum = 0.f;
-  if (mine) {
+  if (tid < (y1 - y0) * a.Wi) {
+    const int py = y0 + tid / a.Wi, px = tid % a.Wi;
+    float o[CI];
+#pragma unroll
+    for (int ci = 0; ci < CI; ++ci) o[ci] = 0.f;
+    for (int t = 0; t < ntap; ++t) {
+      const int ky = t / a.kw, kx = t - ky * a.kw;
+      const int ty = py + a.pad - ky, tx = px + a.pad - kx;
+      int q = -1;
+      if (ty >= 0 && tx >= 0) {
+        if (S1) {
+          if (ty <= oy_hi && tx < a.Wo) q = (ty - oy_lo) * a.Wo + tx;
+        } else if (ty % s == 0 && tx % s == 0 && ty / s <= oy_hi && tx / s < a.Wo) {
+          q = (ty / s - oy_lo) * a.Wo + tx / s;
+        }
+      }
+      if (q >= 0) {
+#pragma unroll
+        for (int ci = 0; ci < CI; ++ci) o[ci] += ys[q * ysw + t * CI + ci];
+      }
+    }
     const long long b = row / a.rows_per_b;
     const long long pix = (long long)py * a.Wi + px;
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
       const long long e = (row * a.Hi * a.Wi + pix) * CI + ci;
-      float v = acc[ci];
+      float v = o[ci];
       if (a.addend) v += a.addend[e];
       if (a.psi_out) a.psi_out[e] = v;
       const long long be = (b * a.Hi * a.Wi + pix) * CI + ci;
@@ -417,37 +492,48 @@ __global__ __launch_bounds__(CIN_THREADS) void conv_input_concretize_kernel(cons
     }
   }
   sum = wave_sum(sum);
-  if ((tid & 63) == 0) sh[tid >> 6] = sum;
+  if (lane == 0) sh[wave] = sum;
   __syncthreads();
   if (tid == 0) {
     float t = 0.f;
 #pragma unroll
-    for (int w = 0; w < CIN_THREADS / 64; ++w) t += sh[w];
-    part[row * nb + band] = t;
+    for (int w = 0; w < WAVES; ++w) t += sh[w];
+    part[row * nbands + band] = t;
   }
 }
 
-template <int CI>
-void cin_launch(bool s1, dim3 g, dim3 blk, size_t lds, hipStream_t st, const ConvIn& a, int bh, float* part) {
+template <int CI, int NB>
+void cin_launch(bool s1, unsigned grid, size_t lds, hipStream_t st, const ConvIn& a, int bh, int nbands, int xcd_map,
+                float* part) {
   if (s1)
-    hipLaunchKernelGGL((conv_input_concretize_kernel<CI, true>), g, blk, lds, st, a, bh, part);
+    hipLaunchKernelGGL((conv_input_concretize_kernel<CI, NB, true>), dim3(grid), dim3(CIN_THREADS), lds, st, a, bh,
+                       nbands, xcd_map, part);
   else
-    hipLaunchKernelGGL((conv_input_concretize_kernel<CI, false>), g, blk, lds, st, a, bh, part);
+    hipLaunchKernelGGL((conv_input_concretize_kernel<CI, NB, false>), dim3(grid), dim3(CIN_THREADS), lds, st, a, bh,
+                       nbands, xcd_map, part);
 }
 
 hipError_t launch_conv_input_concretize(const ConvIn& a, int rows, float* part, float* rowacc, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
+  if (!conv_input_fits(a)) return hipErrorInvalidValue;
   const int bh = cin_band_rows(a);
-  if (bh < 1 || a.Ci < 1 || a.Ci > 4) return hipErrorInvalidValue;
   const int nb = (a.Hi + bh - 1) / bh;
+  if ((long long)rows * nb > 0x7fffffffLL) return hipErrorInvalidValue;
   const int nr = (bh + a.kh - 1 + a.stride - 1) / a.stride + 1;
-  const size_t lds = (size_t)nr * a.Wo * CIN_PS * sizeof(float4);
-  const dim3 g((unsigned)nb, (unsigned)rows), blk(CIN_THREADS);
-  switch (a.Ci) {
-    case 1: cin_launch<1>(a.stride == 1, g, blk, lds, st, a, bh, part); break;
-    case 2: cin_launch<2>(a.stride == 1, g, blk, lds, st, a, bh, part); break;
-    case 3: cin_launch<3>(a.stride == 1, g, blk, lds, st, a, bh, part); break;
-    default: cin_launch<4>(a.stride == 1, g, blk, lds, st, a, bh, part); break;
+  const size_t lds = (size_t)nr * a.Wo * cin_row_floats(a.kh * a.kw * a.Ci) * sizeof(float);
+  const unsigned grid = (unsigned)rows * (unsigned)nb;
+  const int xm = rows % 8 == 0;
+  const bool s1 = a.stride == 1;
+  switch (a.Ci * 4 + cin_col_blocks(a)) {
+    case 1 * 4 + 1: cin_launch<1, 1>(s1, grid, lds, st, a, bh, nb, xm, part); break;
+    case 2 * 4 + 1: cin_launch<2, 1>(s1, grid, lds, st, a, bh, nb, xm, part); break;
+    case 2 * 4 + 2: cin_launch<2, 2>(s1, grid, lds, st, a, bh, nb, xm, part); break;
+    case 3 * 4 + 1: cin_launch<3, 1>(s1, grid, lds, st, a, bh, nb, xm, part); break;
+    case 3 * 4 + 2: cin_launch<3, 2>(s1, grid, lds, st, a, bh, nb, xm, part); break;
+    case 4 * 4 + 1: cin_launch<4, 1>(s1, grid, lds, st, a, bh, nb, xm, part); break;
+    case 4 * 4 + 2: cin_launch<4, 2>(s1, grid, lds, st, a, bh, nb, xm, part); break;
+    case 4 * 4 + 3: cin_launch<4, 3>(s1, grid, lds, st, a, bh, nb, xm, part); break;
+    default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -121,6 +121,17 @@ def _first_conv_net(seed, in_shape, c_out, k, stride, pad, batch=2, eps=0.02, in
     ((1, 12, 12), 12, 3, 1, 2),   # one input channel, padding wider than the halo
     ((4, 9, 10), 16, 3, 2, 0),    # four input channels, no padding
     ((2, 7, 7), 4, 3, 1, 1),      # two input channels
+    # shapes the direct matrix-core kernel takes (Co a multiple of 16 up to
+    # 64): every (input channels, tap-table width, stride) instance
+    ((1, 12, 12), 16, 3, 1, 2),   # 1 channel, 9 columns, stride 1
+    ((1, 15, 15), 16, 3, 2, 1),   # 1 channel, stride 2
+    ((2, 20, 20), 32, 3, 1, 1),   # 18 columns; bands of 12 rows, ragged last band
+    ((2, 10, 10), 16, 2, 2, 0),   # 2x2 kernel: 8 columns, stride 2
+    ((3, 6, 6), 16, 2, 1, 0),     # 3 channels, 12 columns
+    ((3, 13, 17), 48, 3, 2, 1),   # 27 columns, stride 2, odd sizes
+    ((3, 5, 150), 16, 3, 1, 1),   # wide image: one-row bands, ragged M-blocks
+    ((4, 8, 8), 64, 3, 1, 1),     # 36 columns (three column blocks), 64 channels
+    ((4, 8, 8), 32, 2, 2, 0),     # 4 channels, 16 columns, stride 2
 ])
 def test_first_conv_to_domain(lbp, in_shape, c_out, k, stride, pad):
     """The transposed first conv and the concretisation over the input box in one
