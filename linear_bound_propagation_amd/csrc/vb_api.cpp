@@ -1886,8 +1886,26 @@ extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float
     const NodeInfo& in = G.n[src_of(G, nd.in0)];
     GemmDesc d = affine_forward(nd, in, (int)rows);
     d.A = gbuf[cur];
+    ConvAdj ca{};
+    if (nd.op == VB_CONV2D) {
+      ca.g0 = gbuf[cur];
+      ca.W = nd.W;
+      ca.Ci = in.c;
+      ca.Hi = in.h;
+      ca.Wi = in.w;
+      ca.Co = nd.c;
+      ca.Ho = nd.h;
+      ca.Wo = nd.w;
+      ca.kh = nd.kh;
+      ca.kw = nd.kw;
+      ca.stride = nd.stride;
+      ca.pad = nd.pad;
+    }
+    // few input channels: a direct kernel when it takes the shape, else an
+    // im2col image and a GEMM over it
+    const bool direct = nd.op == VB_CONV2D && conv_adjoint_fits(ca);
     const int Kp = (nd.kh * nd.kw * in.c + 31) / 32 * 32;
-    if (nd.op == VB_CONV2D && in.c % 32 != 0 && (size_t)rows * nd.h * nd.w * Kp <= B.pool_floats &&
+    if (!direct && nd.op == VB_CONV2D && in.c % 32 != 0 && (size_t)rows * nd.h * nd.w * Kp <= B.pool_floats &&
         (size_t)nd.c * Kp <= B.pool_floats) {
       // few input channels: im2col of the adjoint, then a 1x1 conv over that image
       // with K padded to whole 32-deep stages (the GEMM's fast path)
@@ -1929,6 +1947,32 @@ extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float
     d.bc1 = (float)bc1;
     d.bc2 = (float)bc2;
     d.adam_eps = adam_eps;
+    AdjFinish a{};
+    a.rows_per_b = d.rows_per_b;
+    a.bias = d.bias;
+    a.coef = d.coef;
+    a.psi_in = d.psi_in;
+    a.alpha_rw = d.alpha_rw;
+    a.adam_m = d.adam_m;
+    a.adam_v = d.adam_v;
+    a.aidx = d.aidx;
+    a.acols = d.acols;
+    a.do_update = d.do_update;
+    a.lr = d.lr;
+    a.beta1 = d.beta1;
+    a.beta2 = d.beta2;
+    a.bc1 = d.bc1;
+    a.bc2 = d.bc2;
+    a.adam_eps = d.adam_eps;
+    a.out = d.out;
+    if (direct) {
+      ca.a = a;
+      ca.a.M = (int)rows;
+      ca.a.N = (int)nd.size;
+      HIPCHK(launch_conv_adjoint_first(ca, (int)rows, st));
+      cur ^= 1;
+      continue;
+    }
     const int S = gemm_is_dense(d) ? ibp_gemm_split(d) : 1;
     if (S > 1 && (size_t)S * d.M * d.N <= B.pool_floats) {
       // few output tiles (a Linear over batch x specs rows): split K, then
@@ -1937,28 +1981,10 @@ extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float
       e.ksplit = S;
       e.out = B.pool[2];
       HIPCHK(launch_gemm(e, st));
-      AdjFinish a{};
       a.part = B.pool[2];
       a.S = S;
       a.M = d.M;
       a.N = d.N;
-      a.rows_per_b = d.rows_per_b;
-      a.bias = d.bias;
-      a.coef = d.coef;
-      a.psi_in = d.psi_in;
-      a.alpha_rw = d.alpha_rw;
-      a.adam_m = d.adam_m;
-      a.adam_v = d.adam_v;
-      a.aidx = d.aidx;
-      a.acols = d.acols;
-      a.do_update = d.do_update;
-      a.lr = d.lr;
-      a.beta1 = d.beta1;
-      a.beta2 = d.beta2;
-      a.bc1 = d.bc1;
-      a.bc2 = d.bc2;
-      a.adam_eps = d.adam_eps;
-      a.out = d.out;
       HIPCHK(launch_adjoint_finish(a, st));
     } else {
       HIPCHK(launch_gemm(d, st));

@@ -341,6 +341,20 @@ struct AdjFinish {
 };
 hipError_t launch_adjoint_finish(const AdjFinish& a, hipStream_t st);
 
+// The alpha-CROWN adjoint through a conv over a few-channel input with the
+// ReLU's adjoint epilogue, without an im2col image (vb_kernels.hip). The
+// epilogue fields come from a: M = rows, N = Ho * Wo * Co (part, S unused).
+struct ConvAdj {
+  AdjFinish a;
+  const float* g0;  // [rows][Hi][Wi][Ci] adjoint over the conv input
+  const float* W;   // [kh][kw][Co][Ci]
+  int Ci, Hi, Wi, Co, Ho, Wo, kh, kw, stride, pad;
+};
+// Whether the direct kernel takes this shape (Ci <= 4, Co a multiple of 16 up
+// to 64, at most 36 (tap, input channel) pairs, a row's input image within 48 KB).
+bool conv_adjoint_fits(const ConvAdj& c);
+hipError_t launch_conv_adjoint_first(const ConvAdj& c, int rows, hipStream_t st);
+
 // im2col of a [rows][H][W][C] tensor for a kh x kw conv (stride, pad) into
 // [rows][Ho][Wo][Kp] with k = tap*C + c and zeros for k >= kh*kw*C; and the
 // matching weights [tap][N][C] -> [N][Kp] (vb_kernels.hip).

@@ -878,32 +878,68 @@ hipError_t launch_ibp_splitk_finish(const float* pc, const float* pr, int S, lon
   return hipGetLastError();
 }
 
+// The alpha-CROWN adjoint epilogue of G elements of row m: g[i] is the
+// adjoint over z at neuron n[i] (before z's bias, bias[bi[i]]); writes the
+// adjoint after the ReLU's relaxation and, on an unstable neuron, takes the
+// Adam ascent step on its slope. Elements with ok[i] false are skipped. All
+// loads of a stage are issued before any store, so G elements cost one memory
+// latency per stage rather than G.
+template <int G>
+__device__ __forceinline__ void adjoint_coef(const AdjFinish& a, long long bm, const long long (&n)[G],
+                                             const bool (&ok)[G], float4 (&cf)[G]) {
+#pragma unroll
+  for (int i = 0; i < G; ++i) cf[i] = ok[i] ? a.coef[bm + n[i]] : make_float4(0.f, 0.f, 0.f, __int_as_float(-1));
+}
+
+// (the same, given the elements' relaxation coefficients from adjoint_coef)
+template <int G>
+__device__ __forceinline__ void adjoint_elements(const AdjFinish& a, long long m, const long long (&n)[G],
+                                                 const int (&bi)[G], const float (&g)[G], const bool (&ok)[G],
+                                                 const float4 (&cf)[G]) {
+  long long si[G];
+  bool uns[G];
+  float psi[G], aold[G], am[G], av[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    // per-neuron state, or compact at the coefficient's column of row m (-1: stable, no entry)
+    const int col = __float_as_int(cf[i].w);
+    si[i] = a.aidx ? m * a.acols + col : m * a.N + n[i];
+    uns[i] = col >= 0 && a.alpha_rw != nullptr;
+    psi[i] = uns[i] ? a.psi_in[si[i]] : 0.f;
+    aold[i] = uns[i] ? a.alpha_rw[si[i]] : 0.f;
+    am[i] = uns[i] && a.do_update ? a.adam_m[si[i]] : 0.f;
+    av[i] = uns[i] && a.do_update ? a.adam_v[si[i]] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    if (!ok[i]) continue;
+    const float gz = g[i] + (a.bias ? a.bias[bi[i]] : 0.f);
+    a.out[m * a.N + n[i]] = !uns[i] ? gz * cf[i].y : (psi[i] >= 0.f ? gz * aold[i] : gz * cf[i].y + cf[i].z);
+    if (uns[i] && a.do_update) {
+      const float grad = gz * fmaxf(psi[i], 0.f);
+      const float mm = a.beta1 * am[i] + (1.f - a.beta1) * grad;
+      const float vv = a.beta2 * av[i] + (1.f - a.beta2) * grad * grad;
+      a.adam_m[si[i]] = mm;
+      a.adam_v[si[i]] = vv;
+      const float step = a.lr * (mm * a.bc1) / (sqrtf(vv * a.bc2) + a.adam_eps);
+      a.alpha_rw[si[i]] = fminf(fmaxf(aold[i] + step, 0.f), 1.f);
+    }
+  }
+}
+
 __global__ void adjoint_finish_kernel(AdjFinish a) {
   const long long MN = (long long)a.M * a.N;
   for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < MN; e += (long long)gridDim.x * blockDim.x) {
     float g = 0.f;
     for (int q = 0; q < a.S; ++q) g += a.part[q * MN + e];
     const long long m = e / a.N;
-    const int n = (int)(e - m * a.N);
-    const float gz = g + (a.bias ? a.bias[n] : 0.f);
-    const long long bn = (m / a.rows_per_b) * a.N + n;
-    const float4 cf = a.coef[bn];
-    // per-neuron state at e, or compact at the coefficient's column of row m (-1: stable, no entry)
-    const int col = __float_as_int(cf.w);
-    const long long si = a.aidx ? m * a.acols + col : e;
-    const bool unstable = col >= 0 && a.alpha_rw != nullptr;
-    const float psi = unstable ? a.psi_in[si] : 0.f;
-    const float aold = unstable ? a.alpha_rw[si] : 0.f;
-    a.out[e] = !unstable ? gz * cf.y : (psi >= 0.f ? gz * aold : gz * cf.y + cf.z);
-    if (unstable && a.do_update) {
-      const float grad = gz * fmaxf(psi, 0.f);
-      const float mm = a.beta1 * a.adam_m[si] + (1.f - a.beta1) * grad;
-      const float vv = a.beta2 * a.adam_v[si] + (1.f - a.beta2) * grad * grad;
-      a.adam_m[si] = mm;
-      a.adam_v[si] = vv;
-      const float step = a.lr * (mm * a.bc1) / (sqrtf(vv * a.bc2) + a.adam_eps);
-      a.alpha_rw[si] = fminf(fmaxf(aold + step, 0.f), 1.f);
-    }
+    const long long n[1] = {e - m * a.N};
+    const int bi[1] = {(int)n[0]};
+    const float gg[1] = {g};
+    const bool ok[1] = {true};
+    float4 cf[1];
+    adjoint_coef<1>(a, (m / a.rows_per_b) * a.N, n, ok, cf);
+    adjoint_elements<1>(a, m, n, bi, gg, ok, cf);
   }
 }
 
@@ -913,6 +949,157 @@ hipError_t launch_adjoint_finish(const AdjFinish& a, hipStream_t st) {
   long long blocks = (MN + 255) / 256;
   if (blocks > 16384) blocks = 16384;
   hipLaunchKernelGGL(adjoint_finish_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+namespace {
+constexpr int CADJ_THREADS = 256;
+constexpr int CADJ_PX = 256;               // output pixels per workgroup
+constexpr int CADJ_MAXK = 9;               // 4-deep contraction steps: (tap, input channel) pairs <= 36
+constexpr size_t CADJ_LDS = 48 * 1024;     // one row's adjoint image over the conv input, with its border
+}  // namespace
+
+// Rows and columns of a row's input image staged with a zero border: pad
+// before, and after up to the last pixel the output reaches.
+__host__ __device__ inline int cadj_span(int in, int out, int k, int stride, int pad) {
+  const int last = (out - 1) * stride - pad + k;  // one past the last input index read
+  return pad + (last > in ? last : in);
+}
+size_t cadj_lds_bytes(const ConvAdj& c) {
+  return (size_t)cadj_span(c.Hi, c.Ho, c.kh, c.stride, c.pad) * cadj_span(c.Wi, c.Wo, c.kw, c.stride, c.pad) * c.Ci *
+         sizeof(float);
+}
+
+bool conv_adjoint_fits(const ConvAdj& c) {
+  return c.Ci >= 1 && c.Ci <= 4 && c.Co % 16 == 0 && c.Co <= 64 && c.kh * c.kw * c.Ci <= 4 * CADJ_MAXK &&
+         c.stride >= 1 && c.pad >= 0 && c.Ho * c.Wo > 0 && cadj_lds_bytes(c) <= CADJ_LDS;
+}
+
+// The adjoint of the alpha-CROWN step through a conv over a few-channel input
+// (the first layer), fused with the ReLU's adjoint epilogue: for every output
+// pixel p and channel c, g[p][c] = sum over (tap, c_in) of the adjoint over
+// the input at the tap's pixel times W[tap][c][c_in], on 16x16x4 fp32 matrix
+// blocks (A: output pixel = lane % 16, pair 4j + lane / 16 at step j; B: the
+// weights of the same pair for channel 16 * block + lane % 16, in registers),
+// then the adjoint epilogue on each result. A workgroup stages its row's input
+// image in LDS with a zero border (so a step's operand is one offset from the
+// pixel's corner) and covers CADJ_PX output pixels; the bands of one row share
+// an XCD when xcd_map is set.
+template <int CI, int NBN>
+__global__ __launch_bounds__(CADJ_THREADS) void conv_adjoint_first_kernel(const ConvAdj c, int nbands, int xcd_map) {
+  extern __shared__ float gs[];  // [Hp][Wp][CI]
+  constexpr int WAVES = CADJ_THREADS / 64;
+  const unsigned n = blockIdx.x;
+  long long row;
+  int band;
+  if (xcd_map) {
+    const unsigned slot = n >> 3, rb = slot / (unsigned)nbands;
+    band = (int)(slot - rb * (unsigned)nbands);
+    row = (long long)rb * 8 + (n & 7);
+  } else {
+    row = n / (unsigned)nbands;
+    band = (int)(n - (unsigned)row * (unsigned)nbands);
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, kk = lane >> 4;
+  const int Hp = cadj_span(c.Hi, c.Ho, c.kh, c.stride, c.pad), Wp = cadj_span(c.Wi, c.Wo, c.kw, c.stride, c.pad);
+  const float* src = c.g0 + row * (long long)c.Hi * c.Wi * CI;
+  for (int e = tid; e < Hp * Wp * CI; e += CADJ_THREADS) {
+    const int ci = e % CI, px = e / CI;
+    const int y = px / Wp - c.pad, x = px % Wp - c.pad;
+    gs[e] = (y >= 0 && y < c.Hi && x >= 0 && x < c.Wi) ? src[(y * c.Wi + x) * CI + ci] : 0.f;
+  }
+
+  const int ncol = c.kh * c.kw * CI;
+  const int nk = (ncol + 3) / 4;
+  // per step: this lane's pair as an offset from the pixel's corner, and the weights
+  float bw[CADJ_MAXK][NBN];
+  int off[CADJ_MAXK];
+#pragma unroll
+  for (int j = 0; j < CADJ_MAXK; ++j) {
+    const int k = 4 * j + kk;
+    const bool ok = j < nk && k < ncol;
+    const int tap = ok ? k / CI : 0, ci = ok ? k - tap * CI : 0;
+    const int ky = tap / c.kw, kx = tap - ky * c.kw;
+    off[j] = (ky * Wp + kx) * CI + ci;  // a pair past the last one meets zero weights
+#pragma unroll
+    for (int nb = 0; nb < NBN; ++nb)
+      bw[j][nb] = ok ? c.W[((long long)tap * c.Co + nb * 16 + li) * CI + ci] : 0.f;
+  }
+  __syncthreads();
+
+  const int npx = c.Ho * c.Wo;
+  const int p0 = band * CADJ_PX, p1 = min(npx, p0 + CADJ_PX);
+  const long long bm = (row / c.a.rows_per_b) * c.a.N;  // this row's input in the coefficients
+  const int nmb = (p1 - p0 + 15) / 16;
+  for (int mb = wave; mb < nmb; mb += WAVES) {
+    const int p = min(p0 + mb * 16 + li, p1 - 1);  // rows past the band repeat its last pixel, never stored
+    const int oy = p / c.Wo, ox = p - oy * c.Wo;
+    const int corner = (oy * c.stride * Wp + ox * c.stride) * CI;
+    // this lane's results: pixel p0 + 16 mb + 4 kk + v, channel 16 nb + li.
+    // The relaxation coefficients of result row v + 1 are loaded while row v
+    // finishes (those of row 0 ahead of the products)
+    long long nn[4][NBN];
+    int bi[NBN];
+    bool ok[4][NBN];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int pp = p0 + mb * 16 + 4 * kk + v;
+#pragma unroll
+      for (int nb = 0; nb < NBN; ++nb) {
+        bi[nb] = nb * 16 + li;
+        nn[v][nb] = (long long)pp * c.Co + bi[nb];
+        ok[v][nb] = pp < p1;
+      }
+    }
+    float4 cf[2][NBN];
+    adjoint_coef<NBN>(c.a, bm, nn[0], ok[0], cf[0]);
+    cin_v4 acc[NBN];
+#pragma unroll
+    for (int nb = 0; nb < NBN; ++nb) acc[nb] = cin_v4{0.f, 0.f, 0.f, 0.f};
+    // (steps past the last pair read offset 0 and meet zero weights)
+#pragma unroll
+    for (int j = 0; j < CADJ_MAXK; ++j) {
+      const float av = gs[corner + off[j]];
+#pragma unroll
+      for (int nb = 0; nb < NBN; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bw[j][nb], acc[nb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      if (v + 1 < 4) adjoint_coef<NBN>(c.a, bm, nn[v + 1], ok[v + 1], cf[(v + 1) & 1]);
+      float gv[NBN];
+#pragma unroll
+      for (int nb = 0; nb < NBN; ++nb) gv[nb] = acc[nb][v];
+      adjoint_elements<NBN>(c.a, row, nn[v], bi, gv, ok[v], cf[v & 1]);
+    }
+  }
+}
+
+template <int CI>
+void cadj_launch(int nbn, unsigned grid, size_t lds, hipStream_t st, const ConvAdj& c, int nbands, int xm) {
+  switch (nbn) {
+    case 1: hipLaunchKernelGGL((conv_adjoint_first_kernel<CI, 1>), dim3(grid), dim3(CADJ_THREADS), lds, st, c, nbands, xm); break;
+    case 2: hipLaunchKernelGGL((conv_adjoint_first_kernel<CI, 2>), dim3(grid), dim3(CADJ_THREADS), lds, st, c, nbands, xm); break;
+    case 3: hipLaunchKernelGGL((conv_adjoint_first_kernel<CI, 3>), dim3(grid), dim3(CADJ_THREADS), lds, st, c, nbands, xm); break;
+    default: hipLaunchKernelGGL((conv_adjoint_first_kernel<CI, 4>), dim3(grid), dim3(CADJ_THREADS), lds, st, c, nbands, xm); break;
+  }
+}
+
+hipError_t launch_conv_adjoint_first(const ConvAdj& c, int rows, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (!conv_adjoint_fits(c) || c.a.M != rows || c.a.N != c.Ho * c.Wo * c.Co) return hipErrorInvalidValue;
+  const int nbands = (c.Ho * c.Wo + CADJ_PX - 1) / CADJ_PX;
+  if ((long long)rows * nbands > 0x7fffffffLL) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)rows * (unsigned)nbands;
+  const size_t lds = cadj_lds_bytes(c);
+  const int xm = rows % 8 == 0;
+  const int nbn = c.Co / 16;
+  switch (c.Ci) {
+    case 1: cadj_launch<1>(nbn, grid, lds, st, c, nbands, xm); break;
+    case 2: cadj_launch<2>(nbn, grid, lds, st, c, nbands, xm); break;
+    case 3: cadj_launch<3>(nbn, grid, lds, st, c, nbands, xm); break;
+    default: cadj_launch<4>(nbn, grid, lds, st, c, nbands, xm); break;
+  }
   return hipGetLastError();
 }
 

@@ -36,16 +36,27 @@ def _oracle(wl, steps, batch_idx=None):
     return crown_lb, res
 
 
+# first convs with 16 to 64 output channels over 2 to 4 input channels take the
+# direct kernels (the domain step keeps Psi; the adjoint runs without im2col);
+# the others take the im2col + GEMM adjoint
+CNN_KINDS = {
+    "cnn": dict(seed=22, convs=((6, 1), (12, 2)), in_shape=(3, 8, 8)),
+    "cnn8": dict(seed=24, convs=((8, 1), (12, 2)), in_shape=(3, 8, 8)),
+    "cnn16": dict(seed=25, convs=((16, 1), (12, 2)), in_shape=(3, 8, 8)),
+    "cnn32s2": dict(seed=26, convs=((32, 2), (8, 1)), in_shape=(2, 9, 9)),
+    "cnn64c4": dict(seed=27, convs=((64, 1), (8, 2)), in_shape=(4, 6, 6)),
+}
+
+
 @pytest.mark.parametrize("compact", [False, True])
-@pytest.mark.parametrize("kind", ["mlp", "cnn", "cnn8"])
+@pytest.mark.parametrize("kind", ["mlp"] + list(CNN_KINDS))
 def test_alpha_small(lbp, kind, compact):
     if kind == "mlp":
         wl = wk.tiny_mlp([40, 70, 50, 8], 0.08, 21, batch=3)
         wl.intermediate = "ibp"
-    elif kind == "cnn":
-        wl = wk.cnn(2, 0.02, 22, convs=((6, 1), (12, 2)), fcs=(30, 10), in_shape=(3, 8, 8))
-    else:  # first conv with a multiple of 4 output channels: the direct domain kernel keeps Psi
-        wl = wk.cnn(2, 0.02, 24, convs=((8, 1), (12, 2)), fcs=(30, 10), in_shape=(3, 8, 8))
+    else:
+        k = CNN_KINDS[kind]
+        wl = wk.cnn(2, 0.02, k["seed"], convs=k["convs"], fcs=(30, 10), in_shape=k["in_shape"])
     steps = 8
     print(f"alpha {kind} steps {steps} compact {compact}", flush=True)
     out, best, lb_steps, (alpha, _, _), lay = _gpu_alpha(lbp, wl, steps, compact)
