@@ -7,6 +7,8 @@
 // are bitwise reproducible.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "vb_internal.h"
 
 namespace vb {
@@ -956,18 +958,23 @@ namespace {
 constexpr int CADJ_THREADS = 256;
 constexpr int CADJ_PX = 256;               // output pixels per workgroup
 constexpr int CADJ_MAXK = 9;               // 4-deep contraction steps: (tap, input channel) pairs <= 36
-constexpr size_t CADJ_LDS = 48 * 1024;     // one row's adjoint image over the conv input, with its border
+constexpr size_t CADJ_LDS = 48 * 1024;     // staged input rows of a band, with their border
 }  // namespace
 
-// Rows and columns of a row's input image staged with a zero border: pad
-// before, and after up to the last pixel the output reaches.
+// Columns of a row's input image staged with a zero border: pad before, and
+// after up to the last pixel the output reaches.
 __host__ __device__ inline int cadj_span(int in, int out, int k, int stride, int pad) {
   const int last = (out - 1) * stride - pad + k;  // one past the last input index read
   return pad + (last > in ? last : in);
 }
+// Input rows staged for a band of CADJ_PX output pixels: the output rows the
+// band touches (at most (CADJ_PX + Wo - 2) / Wo + 1), their taps included.
+inline int cadj_band_rows(const ConvAdj& c) {
+  const int orows = std::min(c.Ho, (CADJ_PX + c.Wo - 2) / c.Wo + 1);
+  return (orows - 1) * c.stride + c.kh;
+}
 size_t cadj_lds_bytes(const ConvAdj& c) {
-  return (size_t)cadj_span(c.Hi, c.Ho, c.kh, c.stride, c.pad) * cadj_span(c.Wi, c.Wo, c.kw, c.stride, c.pad) * c.Ci *
-         sizeof(float);
+  return (size_t)cadj_band_rows(c) * cadj_span(c.Wi, c.Wo, c.kw, c.stride, c.pad) * c.Ci * sizeof(float);
 }
 
 bool conv_adjoint_fits(const ConvAdj& c) {
@@ -981,33 +988,44 @@ bool conv_adjoint_fits(const ConvAdj& c) {
 // the input at the tap's pixel times W[tap][c][c_in], on 16x16x4 fp32 matrix
 // blocks (A: output pixel = lane % 16, pair 4j + lane / 16 at step j; B: the
 // weights of the same pair for channel 16 * block + lane % 16, in registers),
-// then the adjoint epilogue on each result. A workgroup stages its row's input
-// image in LDS with a zero border (so a step's operand is one offset from the
-// pixel's corner) and covers CADJ_PX output pixels; the bands of one row share
-// an XCD when xcd_map is set.
+// then the adjoint epilogue on each result. A workgroup covers CADJ_PX output
+// pixels of 16 * NBN output channels; it stages the input rows they reach in
+// LDS with a zero border (so a step's operand is one offset from the pixel's
+// corner); the workgroups of one row share an XCD when xcd_map is set.
 template <int CI, int NBN>
 __global__ __launch_bounds__(CADJ_THREADS) void conv_adjoint_first_kernel(const ConvAdj c, int nbands, int xcd_map) {
   extern __shared__ float gs[];  // [Hp][Wp][CI]
   constexpr int WAVES = CADJ_THREADS / 64;
+  // workgroup -> (row, band of output pixels, group of 16 * NBN output channels)
+  const int ngroups = c.Co / (16 * NBN), nbc = nbands * ngroups;
   const unsigned n = blockIdx.x;
   long long row;
-  int band;
+  int bc;
   if (xcd_map) {
-    const unsigned slot = n >> 3, rb = slot / (unsigned)nbands;
-    band = (int)(slot - rb * (unsigned)nbands);
+    const unsigned slot = n >> 3, rb = slot / (unsigned)nbc;
+    bc = (int)(slot - rb * (unsigned)nbc);
     row = (long long)rb * 8 + (n & 7);
   } else {
-    row = n / (unsigned)nbands;
-    band = (int)(n - (unsigned)row * (unsigned)nbands);
+    row = n / (unsigned)nbc;
+    bc = (int)(n - (unsigned)row * (unsigned)nbc);
   }
+  const int band = bc / ngroups, cbase = (bc - band * ngroups) * 16 * NBN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, kk = lane >> 4;
-  const int Hp = cadj_span(c.Hi, c.Ho, c.kh, c.stride, c.pad), Wp = cadj_span(c.Wi, c.Wo, c.kw, c.stride, c.pad);
+  const int Wp = cadj_span(c.Wi, c.Wo, c.kw, c.stride, c.pad);
+  const int npx = c.Ho * c.Wo;
+  const int p0 = band * CADJ_PX, p1 = min(npx, p0 + CADJ_PX);
+  // staged input rows: padded rows oy0 * stride .. (oy1 * stride + kh - 1),
+  // one wavefront per row, lanes along the row
+  const int oy0 = p0 / c.Wo, oy1 = (p1 - 1) / c.Wo;
+  const int r0 = oy0 * c.stride, nrow = (oy1 - oy0) * c.stride + c.kh;
   const float* src = c.g0 + row * (long long)c.Hi * c.Wi * CI;
-  for (int e = tid; e < Hp * Wp * CI; e += CADJ_THREADS) {
-    const int ci = e % CI, px = e / CI;
-    const int y = px / Wp - c.pad, x = px % Wp - c.pad;
-    gs[e] = (y >= 0 && y < c.Hi && x >= 0 && x < c.Wi) ? src[(y * c.Wi + x) * CI + ci] : 0.f;
+  for (int r = wave; r < nrow; r += WAVES) {
+    const int y = r0 + r - c.pad;
+    for (int t = lane; t < Wp * CI; t += 64) {
+      const int x = t / CI - c.pad, ci = t % CI;
+      gs[r * Wp * CI + t] = (y >= 0 && y < c.Hi && x >= 0 && x < c.Wi) ? src[(y * c.Wi + x) * CI + ci] : 0.f;
+    }
   }
 
   const int ncol = c.kh * c.kw * CI;
@@ -1024,18 +1042,16 @@ __global__ __launch_bounds__(CADJ_THREADS) void conv_adjoint_first_kernel(const 
     off[j] = (ky * Wp + kx) * CI + ci;  // a pair past the last one meets zero weights
 #pragma unroll
     for (int nb = 0; nb < NBN; ++nb)
-      bw[j][nb] = ok ? c.W[((long long)tap * c.Co + nb * 16 + li) * CI + ci] : 0.f;
+      bw[j][nb] = ok ? c.W[((long long)tap * c.Co + cbase + nb * 16 + li) * CI + ci] : 0.f;
   }
   __syncthreads();
 
-  const int npx = c.Ho * c.Wo;
-  const int p0 = band * CADJ_PX, p1 = min(npx, p0 + CADJ_PX);
   const long long bm = (row / c.a.rows_per_b) * c.a.N;  // this row's input in the coefficients
   const int nmb = (p1 - p0 + 15) / 16;
   for (int mb = wave; mb < nmb; mb += WAVES) {
     const int p = min(p0 + mb * 16 + li, p1 - 1);  // rows past the band repeat its last pixel, never stored
     const int oy = p / c.Wo, ox = p - oy * c.Wo;
-    const int corner = (oy * c.stride * Wp + ox * c.stride) * CI;
+    const int corner = ((oy * c.stride - r0) * Wp + ox * c.stride) * CI;
     // this lane's results: pixel p0 + 16 mb + 4 kk + v, channel 16 nb + li.
     // The relaxation coefficients of result row v + 1 are loaded while row v
     // finishes (those of row 0 ahead of the products)
@@ -1047,7 +1063,7 @@ __global__ __launch_bounds__(CADJ_THREADS) void conv_adjoint_first_kernel(const 
       const int pp = p0 + mb * 16 + 4 * kk + v;
 #pragma unroll
       for (int nb = 0; nb < NBN; ++nb) {
-        bi[nb] = nb * 16 + li;
+        bi[nb] = cbase + nb * 16 + li;
         nn[v][nb] = (long long)pp * c.Co + bi[nb];
         ok[v][nb] = pp < p1;
       }
@@ -1076,29 +1092,26 @@ __global__ __launch_bounds__(CADJ_THREADS) void conv_adjoint_first_kernel(const 
 }
 
 template <int CI>
-void cadj_launch(int nbn, unsigned grid, size_t lds, hipStream_t st, const ConvAdj& c, int nbands, int xm) {
-  switch (nbn) {
-    case 1: hipLaunchKernelGGL((conv_adjoint_first_kernel<CI, 1>), dim3(grid), dim3(CADJ_THREADS), lds, st, c, nbands, xm); break;
-    case 2: hipLaunchKernelGGL((conv_adjoint_first_kernel<CI, 2>), dim3(grid), dim3(CADJ_THREADS), lds, st, c, nbands, xm); break;
-    case 3: hipLaunchKernelGGL((conv_adjoint_first_kernel<CI, 3>), dim3(grid), dim3(CADJ_THREADS), lds, st, c, nbands, xm); break;
-    default: hipLaunchKernelGGL((conv_adjoint_first_kernel<CI, 4>), dim3(grid), dim3(CADJ_THREADS), lds, st, c, nbands, xm); break;
-  }
+void cadj_launch(unsigned grid, size_t lds, hipStream_t st, const ConvAdj& c, int nbands, int xm) {
+  hipLaunchKernelGGL((conv_adjoint_first_kernel<CI, 1>), dim3(grid), dim3(CADJ_THREADS), lds, st, c, nbands, xm);
 }
 
 hipError_t launch_conv_adjoint_first(const ConvAdj& c, int rows, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   if (!conv_adjoint_fits(c) || c.a.M != rows || c.a.N != c.Ho * c.Wo * c.Co) return hipErrorInvalidValue;
   const int nbands = (c.Ho * c.Wo + CADJ_PX - 1) / CADJ_PX;
-  if ((long long)rows * nbands > 0x7fffffffLL) return hipErrorInvalidValue;
-  const unsigned grid = (unsigned)rows * (unsigned)nbands;
+  // 16 output channels per workgroup: fewer results per lane keep more
+  // wavefronts in flight to cover the epilogue's loads
+  const long long groups = c.Co / 16;
+  if ((long long)rows * nbands * groups > 0x7fffffffLL) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)((long long)rows * nbands * groups);
   const size_t lds = cadj_lds_bytes(c);
   const int xm = rows % 8 == 0;
-  const int nbn = c.Co / 16;
   switch (c.Ci) {
-    case 1: cadj_launch<1>(nbn, grid, lds, st, c, nbands, xm); break;
-    case 2: cadj_launch<2>(nbn, grid, lds, st, c, nbands, xm); break;
-    case 3: cadj_launch<3>(nbn, grid, lds, st, c, nbands, xm); break;
-    default: cadj_launch<4>(nbn, grid, lds, st, c, nbands, xm); break;
+    case 1: cadj_launch<1>(grid, lds, st, c, nbands, xm); break;
+    case 2: cadj_launch<2>(grid, lds, st, c, nbands, xm); break;
+    case 3: cadj_launch<3>(grid, lds, st, c, nbands, xm); break;
+    default: cadj_launch<4>(grid, lds, st, c, nbands, xm); break;
   }
   return hipGetLastError();
 }

@@ -45,6 +45,9 @@ CNN_KINDS = {
     "cnn16": dict(seed=25, convs=((16, 1), (12, 2)), in_shape=(3, 8, 8)),
     "cnn32s2": dict(seed=26, convs=((32, 2), (8, 1)), in_shape=(2, 9, 9)),
     "cnn64c4": dict(seed=27, convs=((64, 1), (8, 2)), in_shape=(4, 6, 6)),
+    "cnn48c1": dict(seed=28, convs=((48, 1), (8, 2)), in_shape=(1, 7, 7)),
+    # 900 output pixels: bands of 256 start and end inside image rows
+    "cnn16w30": dict(seed=29, convs=((16, 1), (8, 2)), in_shape=(3, 30, 30)),
 }
 
 
