@@ -879,21 +879,13 @@ hipError_t launch_gemm(const GemmDesc& desc, hipStream_t st) {
   const bool fast = is_fast(d);
   const int bn = tile_n(d, fast);
   if (bn == 256) {
-    // plain epilogues only (checked in use_big); IBP never takes this tile
+    // gather GEMMs with plain epilogues only (checked in use_big); IBP never takes this tile
     const int mt = (d.Mt + 255) / 256, nt = (d.N + 255) / 256;
     const dim3 g(((mt * nt + 7) / 8) * 8), b(512);
-    if (dense) {
-      switch (d.epi) {
-        case E_STORE: hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 4, true, A_PLAIN, E_STORE, true>), g, b, 0, st, d); break;
-        case E_RELAX: hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 4, true, A_PLAIN, E_RELAX, true>), g, b, 0, st, d); break;
-        default: hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 4, true, A_PLAIN, E_CONCRETIZE, true>), g, b, 0, st, d); break;
-      }
-    } else {
-      switch (d.epi) {
-        case E_STORE: hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 4, false, A_PLAIN, E_STORE, true>), g, b, 0, st, d); break;
-        case E_RELAX: hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 4, false, A_PLAIN, E_RELAX, true>), g, b, 0, st, d); break;
-        default: hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 4, false, A_PLAIN, E_CONCRETIZE, true>), g, b, 0, st, d); break;
-      }
+    switch (d.epi) {
+      case E_STORE: hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 4, false, A_PLAIN, E_STORE, true>), g, b, 0, st, d); break;
+      case E_RELAX: hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 4, false, A_PLAIN, E_RELAX, true>), g, b, 0, st, d); break;
+      default: hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 4, false, A_PLAIN, E_CONCRETIZE, true>), g, b, 0, st, d); break;
     }
     return hipGetLastError();
   }
