@@ -475,9 +475,24 @@ vb_status backward_chunk_patch(Backward& B, const BwdCall& c, long long R, const
   vb_status s = effective_bias(B, G, c.start, bias);
   if (s) return s;
   HIPCHK(launch_identity_bias(c.cb, (int)S.size, bias, S.c, B.rowacc, B.st));
-  int cur = B.alloc();
-  if (cur < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted");
-  HIPCHK(launch_patch_identity(rows, (int)R, S.c, B.pool[cur], B.st));
+  // the first step (through the start conv, relaxed at the ReLU below it) reads
+  // the weights directly when the kernel takes the shape; otherwise the
+  // identity rows are written out and multiplied like any other Lambda
+  const NodeInfo& t0 = G.n[steps[0].t];
+  PatchIdRelax pir{};
+  pir.W = S.W;
+  pir.Co = S.c;
+  pir.Ci = t0.c;
+  pir.kh = S.kh;
+  pir.kw = S.kw;
+  pir.out = nullptr;
+  const bool direct_first = steps[0].t != c.stop && patch_id_relax_fits(pir);
+  int cur = -1;
+  if (!direct_first) {
+    cur = B.alloc();
+    if (cur < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted");
+    HIPCHK(launch_patch_identity(rows, (int)R, S.c, B.pool[cur], B.st));
+  }
   int wh = 1, ww = 1;
   for (const PatchStep& ps : steps) {
     const NodeInfo& nd = G.n[ps.k];
@@ -493,6 +508,26 @@ vb_status backward_chunk_patch(Backward& B, const BwdCall& c, long long R, const
       if (s) return s;
       HIPCHK(launch_relax_coef(B.lo[z] + (long long)c.b0 * G.n[z].size, B.hi[z] + (long long)c.b0 * G.n[z].size,
                                (long long)c.cb * G.n[z].size, nullptr, B.coef, B.st));
+    }
+    if (cur < 0) {
+      // (direct_first: this is the start conv and not the last step)
+      pir.R = (int)R;
+      pir.pgh = S.h;
+      pir.pgw = S.w;
+      pir.psy = ps.sy;
+      pir.poy = ps.oy;
+      pir.psx = ps.sx;
+      pir.pox = ps.ox;
+      pir.img_h = tn.h;
+      pir.img_w = tn.w;
+      pir.coef = B.coef;
+      pir.bias = bias_z;
+      pir.out = B.pool[outb];
+      HIPCHK(launch_patch_id_relax(pir, rows, B.rowacc, B.st));
+      cur = outb;
+      wh = ps.wh;
+      ww = ps.ww;
+      continue;
     }
     if (last && tn.c <= 8 && nd.kh * nd.kw * tn.c <= 64 &&
         (size_t)rows * wh * ww * nd.kh * nd.kw * tn.c <= B.pool_floats) {

@@ -242,6 +242,25 @@ size_t conv_input_part_floats(const ConvIn& a, int rows);
 // Identity rows over a node of C channels, each on its own 1 x 1 window:
 // out [rows][C] with out[row][c'] = +-1 at c' = row's channel (rows_per_b = R).
 hipError_t launch_patch_identity(int rows, int R, int C, float* out, hipStream_t st);
+// The first back-substitution step of footprint identity rows through the start
+// conv, relaxed at the ReLU below it, without a GEMM over the one-hot rows: row
+// (b, sign, pixel p, channel c) gets sign * W[Y][X][c][:] on window cell (Y, X),
+// relaxed with the coefficients of the cell's pixel of the ReLU input (zero
+// outside the image); rowacc[row] += the row's bias and relaxation terms.
+struct PatchIdRelax {
+  const float* W;       // [kh][kw][Co][Ci] of the start conv
+  int Co, Ci, kh, kw;   // start channels, channels of the node below, kernel
+  int R;                // rows per input: 2 * pgh * pgw * Co
+  int pgh, pgw;         // start node grid
+  int psy, poy, psx, pox;  // window cell (Y, X) of pixel (py, px): (py*psy + poy + Y, px*psx + pox + X)
+  int img_h, img_w;     // the node below
+  const float4* coef;   // [b][img_h][img_w][Ci] relaxation coefficients
+  const float* bias;    // per channel of the node below, or NULL
+  float* out;           // [rows][kh][kw][Ci]
+};
+// Whether the kernel takes the shape.
+bool patch_id_relax_fits(const PatchIdRelax& a);
+hipError_t launch_patch_id_relax(const PatchIdRelax& a, int rows, float* rowacc, hipStream_t st);
 
 // rowacc[b*2n + r] = s * bias[i % bias_c] for identity rows (s = +1 for r < n, -1 after; i = r mod n)
 hipError_t launch_identity_bias(int batch, int n, const float* bias, int bias_c, float* rowacc, hipStream_t st);

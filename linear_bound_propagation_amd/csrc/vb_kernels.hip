@@ -564,6 +564,49 @@ hipError_t launch_patch_identity(int rows, int R, int C, float* out, hipStream_t
   return hipGetLastError();
 }
 
+bool patch_id_relax_fits(const PatchIdRelax& a) { return a.Ci > 0 && a.Co > 0; }
+
+// One wavefront per row; lanes along the row's window, channel fastest, so
+// the weight, coefficient and output accesses of a step are contiguous.
+__global__ __launch_bounds__(256) void patch_id_relax_kernel(const PatchIdRelax a, int rows,
+                                                             float* __restrict__ rowacc) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const long long b = row / a.R;
+  const int r = (int)(row - b * a.R);
+  const float sg = r < a.R / 2 ? 1.f : -1.f;
+  const int c = r % a.Co;
+  const int p = (int)((row / a.Co) % ((long long)a.pgh * a.pgw));
+  const int py = p / a.pgw, px = p - (p / a.pgw) * a.pgw;
+  const int L = a.kh * a.kw * a.Ci;
+  const float4* coef = a.coef + b * a.img_h * a.img_w * a.Ci;
+  float* out = a.out + row * L;
+  float s = 0.f;
+  for (int e = lane; e < L; e += 64) {
+    const int cell = e / a.Ci, ci = e - cell * a.Ci;
+    const int Y = cell / a.kw, X = cell - Y * a.kw;
+    const float v = sg * a.W[((long long)cell * a.Co + c) * a.Ci + ci];
+    const int ay = py * a.psy + a.poy + Y, ax = px * a.psx + a.pox + X;
+    float o = 0.f;
+    if (ay >= 0 && ay < a.img_h && ax >= 0 && ax < a.img_w) {
+      const float4 cf = coef[((long long)ay * a.img_w + ax) * a.Ci + ci];
+      o = v >= 0.f ? v * cf.x : v * cf.y;
+      s += (a.bias ? o * a.bias[ci] : 0.f) + fminf(v, 0.f) * cf.z;
+    }
+    out[e] = o;
+  }
+  s = wave_sum(s);
+  if (lane == 0) rowacc[row] += s;
+}
+
+hipError_t launch_patch_id_relax(const PatchIdRelax& a, int rows, float* rowacc, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (!patch_id_relax_fits(a)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(patch_id_relax_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a, rows, rowacc);
+  return hipGetLastError();
+}
+
 __global__ void identity_bias_kernel(int batch, int n, const float* __restrict__ bias, int bias_c,
                                      float* __restrict__ rowacc) {
   const long long total = (long long)batch * 2 * n;
