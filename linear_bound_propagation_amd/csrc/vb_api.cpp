@@ -529,6 +529,47 @@ vb_status backward_chunk_patch(Backward& B, const BwdCall& c, long long R, const
       ww = ps.ww;
       continue;
     }
+    if (last) {
+      // few domain channels: the direct kernel over each row's window (the
+      // transposed conv on matrix blocks and the concretisation in one pass)
+      ConvIn a{};
+      a.lam = B.pool[cur];
+      a.W = nd.W;
+      a.Co = nd.c;
+      a.Ho = wh;
+      a.Wo = ww;
+      a.Ci = tn.c;
+      a.Hi = ps.wh;
+      a.Wi = ps.ww;
+      a.kh = nd.kh;
+      a.kw = nd.kw;
+      a.stride = nd.stride;
+      a.pad = 0;  // the window covers every tap
+      a.rows_per_b = (int)R;
+      if (c.stop == 0) {
+        a.center = B.dom.xc + (long long)c.b0 * G.n[0].size;
+        a.radius = B.dom.xr ? B.dom.xr + (long long)c.b0 * G.n[0].size : nullptr;
+        a.eps = B.dom.eps;
+      } else {
+        a.center = B.box_c;
+        a.radius = B.box_r;
+      }
+      a.patch = 1;
+      a.pc = S.c;
+      a.pgh = S.h;
+      a.pgw = S.w;
+      a.psy = ps.sy;
+      a.poy = ps.oy;
+      a.psx = ps.sx;
+      a.pox = ps.ox;
+      a.img_h = tn.h;
+      a.img_w = tn.w;
+      if (conv_input_fits(a) && conv_input_part_floats(a, rows) <= B.part_floats) {
+        HIPCHK(launch_conv_input_concretize(a, rows, B.part, B.rowacc, B.st));
+        B.release(cur);
+        break;
+      }
+    }
     if (last && tn.c <= 8 && nd.kh * nd.kw * tn.c <= 64 &&
         (size_t)rows * wh * ww * nd.kh * nd.kw * tn.c <= B.pool_floats) {
       // few domain channels: Q = Lambda . W over (tap, c_in) columns as a dense

@@ -228,9 +228,14 @@ struct ConvIn {
   int rows_per_b;
   const float* addend;  // [rows][Hi][Wi][Ci] or NULL
   float* psi_out;       // receives L_in, or NULL
-  const float* center;  // [batch][Hi][Wi][Ci]
+  const float* center;  // [batch][Hi][Wi][Ci], or [batch][img_h][img_w][Ci] with patch
   const float* radius;  // or NULL -> eps
   float eps;
+  // footprint windows (patch != 0; addend and psi_out NULL): Hi x Wi is the
+  // row's window of an img_h x img_w domain node; cell (y, x) of row p =
+  // (py, px) of a pgh x pgw start node with pc channels is pixel
+  // (py*psy + poy + y, px*psx + pox + x)
+  int patch, pc, pgh, pgw, psy, poy, psx, pox, img_h, img_w;
 };
 // Whether the direct kernel takes this shape (Ci <= 4, Co a multiple of 16 up to 64,
 // at most 48 (tap, input channel) pairs, bands fit in LDS).

@@ -317,6 +317,7 @@ namespace {
 constexpr int CIN_THREADS = 256;         // threads of a conv-input workgroup, one input pixel each
 constexpr int CIN_MAX_CO = 64;           // output channels: one 16-step pass of the contraction
 constexpr int CIN_MB = 3;                // M-blocks whose loads are issued together
+constexpr int CIN_WIN_ROWS = 16;         // footprint rows per workgroup
 constexpr size_t CIN_Y_LDS = 64 * 1024;  // bytes of a band's tap table
 typedef float cin_v4 __attribute__((ext_vector_type(4)));
 
@@ -365,41 +366,23 @@ size_t conv_input_part_floats(const ConvIn& a, int rows) {
 // Consecutive workgroups go round-robin over the 8 XCDs; with xcd_map the
 // bands of one row share an XCD, so the rows two bands both stage are read
 // through one L2.
-template <int CI, int NB, bool S1>
+template <int CI, int NB, bool S1, bool MULTI>
 __global__ __launch_bounds__(CIN_THREADS) void conv_input_concretize_kernel(const ConvIn a, int BH, int nbands,
-                                                                           int xcd_map, float* __restrict__ part) {
+                                                                           int xcd_map, int per_wg, long long items,
+                                                                           float* __restrict__ part) {
   extern __shared__ float ys[];  // [staged pixels][ysw]
   __shared__ float sh[CIN_THREADS / 64];
   constexpr int WAVES = CIN_THREADS / 64;
-  const unsigned n = blockIdx.x;
-  long long row;
-  int band;
-  if (xcd_map) {
-    const unsigned slot = n >> 3, rb = slot / (unsigned)nbands;
-    band = (int)(slot - rb * (unsigned)nbands);
-    row = (long long)rb * 8 + (n & 7);
-  } else {
-    row = n / (unsigned)nbands;
-    band = (int)(n - (unsigned)row * (unsigned)nbands);
-  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int y0 = band * BH, y1 = min(a.Hi, y0 + BH);
-  const int s = S1 ? 1 : a.stride;
-  const int lo = y0 + a.pad - (a.kh - 1);
-  const int oy_lo = lo <= 0 ? 0 : (lo + s - 1) / s;
-  const int oy_hi = min(a.Ho - 1, (y1 - 1 + a.pad) / s);
-  const int nr = oy_hi - oy_lo + 1;
-  const int npx = nr > 0 ? nr * a.Wo : 0;
   const int ntap = a.kh * a.kw;
   const int ncol = ntap * CI;
   const int ysw = cin_row_floats(ncol);
   const int li = lane & 15, kk = lane >> 4;
-  const float* lam_r = a.lam + (row * a.Ho + (nr > 0 ? oy_lo : 0)) * (long long)a.Wo * a.Co;
 
-  // phase 1: tap table. Step j = 4u + c takes channel 16u + 4 * (lane / 16) + c,
-  // so that one load instruction (fixed u) reads 64 contiguous bytes of each
-  // of 16 pixels.
-  float bw[NB][16];  // B: weights of column li of each block, 16 steps
+  // B of phase 1 (the same for every row): step j = 4u + c takes channel
+  // 16u + 4 * (lane / 16) + c, so that one load instruction of A (fixed u)
+  // reads 64 contiguous bytes of each of 16 pixels.
+  float bw[NB][16];  // weights of column li of each block, 16 steps
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int col = nb * 16 + li;
@@ -412,6 +395,32 @@ __global__ __launch_bounds__(CIN_THREADS) void conv_input_concretize_kernel(cons
       bw[nb][j] = okn && 16 * (j >> 2) < a.Co ? w[off * CI] : 0.f;
     }
   }
+
+  // work items (row, band) n = blockIdx.x * per_wg + i; with xcd_map (one
+  // item per workgroup) the bands of one row share an XCD
+  for (int it = 0; it < (MULTI ? per_wg : 1); ++it) {
+  const long long n = MULTI ? (long long)blockIdx.x * per_wg + it : (long long)blockIdx.x;
+  if (n >= items) break;
+  long long row;
+  int band;
+  if (xcd_map) {
+    const unsigned slot = (unsigned)n >> 3, rb = slot / (unsigned)nbands;
+    band = (int)(slot - rb * (unsigned)nbands);
+    row = (long long)rb * 8 + (n & 7);
+  } else {
+    row = n / nbands;
+    band = (int)(n - row * nbands);
+  }
+  const int y0 = band * BH, y1 = min(a.Hi, y0 + BH);
+  const int s = S1 ? 1 : a.stride;
+  const int lo = y0 + a.pad - (a.kh - 1);
+  const int oy_lo = lo <= 0 ? 0 : (lo + s - 1) / s;
+  const int oy_hi = min(a.Ho - 1, (y1 - 1 + a.pad) / s);
+  const int nr = oy_hi - oy_lo + 1;
+  const int npx = nr > 0 ? nr * a.Wo : 0;
+  const float* lam_r = a.lam + (row * a.Ho + (nr > 0 ? oy_lo : 0)) * (long long)a.Wo * a.Co;
+
+  // phase 1: tap table
   const int nmb = (npx + 15) / 16;
   const int nit = wave < nmb ? (nmb - wave + WAVES - 1) / WAVES : 0;  // M-blocks of this wavefront
   auto load_a = [&](int it, float4 (&v)[4]) {
@@ -482,15 +491,26 @@ __global__ __launch_bounds__(CIN_THREADS) void conv_input_concretize_kernel(cons
     }
     const long long b = row / a.rows_per_b;
     const long long pix = (long long)py * a.Wi + px;
+    // the domain pixel of this input cell: itself, or for a footprint window
+    // the cell's pixel at the row's position (none outside the image)
+    long long dpix = b * a.Hi * a.Wi + pix;
+    bool inside = true;
+    if (a.patch) {
+      const long long pz = (row / a.pc) % ((long long)a.pgh * a.pgw);
+      const int gy = (int)(pz / a.pgw), gx = (int)(pz - (pz / a.pgw) * a.pgw);
+      const int ay = gy * a.psy + a.poy + py, ax = gx * a.psx + a.pox + px;
+      inside = ay >= 0 && ay < a.img_h && ax >= 0 && ax < a.img_w;
+      dpix = b * a.img_h * a.img_w + (inside ? (long long)ay * a.img_w + ax : 0);
+    }
 #pragma unroll
     for (int ci = 0; ci < CI; ++ci) {
       const long long e = (row * a.Hi * a.Wi + pix) * CI + ci;
       float v = o[ci];
       if (a.addend) v += a.addend[e];
       if (a.psi_out) a.psi_out[e] = v;
-      const long long be = (b * a.Hi * a.Wi + pix) * CI + ci;
+      const long long be = dpix * CI + ci;
       const float r = a.radius ? a.radius[be] : a.eps;
-      sum += v * a.center[be] - fabsf(v) * r;
+      if (inside) sum += v * a.center[be] - fabsf(v) * r;
     }
   }
   sum = wave_sum(sum);
@@ -502,17 +522,28 @@ __global__ __launch_bounds__(CIN_THREADS) void conv_input_concretize_kernel(cons
     for (int w = 0; w < WAVES; ++w) t += sh[w];
     part[row * nbands + band] = t;
   }
+  __syncthreads();  // the tap table and sh are rewritten by the next item
+  }
 }
 
 template <int CI, int NB>
 void cin_launch(bool s1, unsigned grid, size_t lds, hipStream_t st, const ConvIn& a, int bh, int nbands, int xcd_map,
-                float* part) {
-  if (s1)
-    hipLaunchKernelGGL((conv_input_concretize_kernel<CI, NB, true>), dim3(grid), dim3(CIN_THREADS), lds, st, a, bh,
-                       nbands, xcd_map, part);
-  else
-    hipLaunchKernelGGL((conv_input_concretize_kernel<CI, NB, false>), dim3(grid), dim3(CIN_THREADS), lds, st, a, bh,
-                       nbands, xcd_map, part);
+                int per_wg, long long items, float* part) {
+  const dim3 g(grid), b(CIN_THREADS);
+  if (per_wg > 1) {
+    if (s1)
+      hipLaunchKernelGGL((conv_input_concretize_kernel<CI, NB, true, true>), g, b, lds, st, a, bh, nbands, xcd_map,
+                         per_wg, items, part);
+    else
+      hipLaunchKernelGGL((conv_input_concretize_kernel<CI, NB, false, true>), g, b, lds, st, a, bh, nbands, xcd_map,
+                         per_wg, items, part);
+  } else if (s1) {
+    hipLaunchKernelGGL((conv_input_concretize_kernel<CI, NB, true, false>), g, b, lds, st, a, bh, nbands, xcd_map,
+                       per_wg, items, part);
+  } else {
+    hipLaunchKernelGGL((conv_input_concretize_kernel<CI, NB, false, false>), g, b, lds, st, a, bh, nbands, xcd_map,
+                       per_wg, items, part);
+  }
 }
 
 hipError_t launch_conv_input_concretize(const ConvIn& a, int rows, float* part, float* rowacc, hipStream_t st) {
@@ -523,18 +554,22 @@ hipError_t launch_conv_input_concretize(const ConvIn& a, int rows, float* part, 
   if ((long long)rows * nb > 0x7fffffffLL) return hipErrorInvalidValue;
   const int nr = (bh + a.kh - 1 + a.stride - 1) / a.stride + 1;
   const size_t lds = (size_t)nr * a.Wo * cin_row_floats(a.kh * a.kw * a.Ci) * sizeof(float);
-  const unsigned grid = (unsigned)rows * (unsigned)nb;
-  const int xm = rows % 8 == 0;
+  // small footprint windows: several rows per workgroup share its weight
+  // registers; whole images: one (row, band) per workgroup, XCD-aware
+  const long long items = (long long)rows * nb;
+  const int per_wg = a.patch ? CIN_WIN_ROWS : 1;
+  const unsigned grid = (unsigned)((items + per_wg - 1) / per_wg);
+  const int xm = per_wg == 1 && rows % 8 == 0;
   const bool s1 = a.stride == 1;
   switch (a.Ci * 4 + cin_col_blocks(a)) {
-    case 1 * 4 + 1: cin_launch<1, 1>(s1, grid, lds, st, a, bh, nb, xm, part); break;
-    case 2 * 4 + 1: cin_launch<2, 1>(s1, grid, lds, st, a, bh, nb, xm, part); break;
-    case 2 * 4 + 2: cin_launch<2, 2>(s1, grid, lds, st, a, bh, nb, xm, part); break;
-    case 3 * 4 + 1: cin_launch<3, 1>(s1, grid, lds, st, a, bh, nb, xm, part); break;
-    case 3 * 4 + 2: cin_launch<3, 2>(s1, grid, lds, st, a, bh, nb, xm, part); break;
-    case 4 * 4 + 1: cin_launch<4, 1>(s1, grid, lds, st, a, bh, nb, xm, part); break;
-    case 4 * 4 + 2: cin_launch<4, 2>(s1, grid, lds, st, a, bh, nb, xm, part); break;
-    case 4 * 4 + 3: cin_launch<4, 3>(s1, grid, lds, st, a, bh, nb, xm, part); break;
+    case 1 * 4 + 1: cin_launch<1, 1>(s1, grid, lds, st, a, bh, nb, xm, per_wg, items, part); break;
+    case 2 * 4 + 1: cin_launch<2, 1>(s1, grid, lds, st, a, bh, nb, xm, per_wg, items, part); break;
+    case 2 * 4 + 2: cin_launch<2, 2>(s1, grid, lds, st, a, bh, nb, xm, per_wg, items, part); break;
+    case 3 * 4 + 1: cin_launch<3, 1>(s1, grid, lds, st, a, bh, nb, xm, per_wg, items, part); break;
+    case 3 * 4 + 2: cin_launch<3, 2>(s1, grid, lds, st, a, bh, nb, xm, per_wg, items, part); break;
+    case 4 * 4 + 1: cin_launch<4, 1>(s1, grid, lds, st, a, bh, nb, xm, per_wg, items, part); break;
+    case 4 * 4 + 2: cin_launch<4, 2>(s1, grid, lds, st, a, bh, nb, xm, per_wg, items, part); break;
+    case 4 * 4 + 3: cin_launch<4, 3>(s1, grid, lds, st, a, bh, nb, xm, per_wg, items, part); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
