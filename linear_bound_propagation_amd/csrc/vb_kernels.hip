@@ -396,6 +396,23 @@ __global__ __launch_bounds__(CIN_THREADS) void conv_input_concretize_kernel(cons
     }
   }
 
+  // MULTI: per_wg items of one band each (footprint windows), at most two
+  // M-blocks per wavefront: the next item's Lambda is loaded while the
+  // current one computes
+  float4 nxa[2][4];
+  auto load_item = [&](long long item, float4 (&v)[2][4]) {
+    const float* lam_i = a.lam + item * a.Ho * (long long)a.Wo * a.Co;
+    const int np = a.Ho * a.Wo;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = min((wave + WAVES * i) * 16 + li, np - 1);
+      const float4* ap = reinterpret_cast<const float4*>(lam_i + (long long)q * a.Co + 4 * kk);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[i][u] = ap[16 * u < a.Co ? 4 * u : 0];
+    }
+  };
+  if (MULTI && (long long)blockIdx.x * per_wg < items) load_item((long long)blockIdx.x * per_wg, nxa);
+
   // work items (row, band) n = blockIdx.x * per_wg + i; with xcd_map (one
   // item per workgroup) the bands of one row share an XCD
   for (int it = 0; it < (MULTI ? per_wg : 1); ++it) {
@@ -435,8 +452,39 @@ __global__ __launch_bounds__(CIN_THREADS) void conv_input_concretize_kernel(cons
     for (int u = 0; u < 4; ++u) v[u] = ap[16 * u < a.Co ? 4 * u : 0];
   };
   cin_v4 acc[NB];
+  if (MULTI) {
+    float4 av[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) av[i][u] = nxa[i][u];
+    if (it + 1 < per_wg && n + 1 < items) load_item(n + 1, nxa);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (i >= nit) break;
+      const int mb = wave + WAVES * i;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = cin_v4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float4 c4 = av[i][j >> 2];
+        const float a1 = (j & 3) == 0 ? c4.x : (j & 3) == 1 ? c4.y : (j & 3) == 2 ? c4.z : c4.w;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bw[nb][j], acc[nb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int q = mb * 16 + 4 * kk + v;
+        if (q < npx) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            if (nb * 16 + li < ncol) ys[q * ysw + nb * 16 + li] = acc[nb][v];
+        }
+      }
+    }
+  }
   // the loads of up to CIN_MB M-blocks are issued together
-  for (int g0 = 0; g0 < nit; g0 += CIN_MB) {
+  for (int g0 = 0; g0 < (MULTI ? 0 : nit); g0 += CIN_MB) {
     float4 av[CIN_MB][4];
 #pragma unroll
     for (int i = 0; i < CIN_MB; ++i) load_a(min(g0 + i, nit - 1), av[i]);
@@ -557,7 +605,9 @@ hipError_t launch_conv_input_concretize(const ConvIn& a, int rows, float* part, 
   // small footprint windows: several rows per workgroup share its weight
   // registers; whole images: one (row, band) per workgroup, XCD-aware
   const long long items = (long long)rows * nb;
-  const int per_wg = a.patch ? CIN_WIN_ROWS : 1;
+  // (several rows per workgroup need one band of at most 8 M-blocks, whose
+  // staged rows are the whole output window)
+  const int per_wg = a.patch && nb == 1 && bh == a.Hi && a.Ho * a.Wo <= 128 ? CIN_WIN_ROWS : 1;
   const unsigned grid = (unsigned)((items + per_wg - 1) / per_wg);
   const int xm = per_wg == 1 && rows % 8 == 0;
   const bool s1 = a.stride == 1;
