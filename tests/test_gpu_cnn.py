@@ -31,6 +31,9 @@ def _run(lbp, wl):
     (((5, 2), (33, 1), (70, 2)), (37, 6), (2, 10, 7), 2, 0.01, 12),
     # the configuration's layer sequence at a reduced width
     (((16, 1), (16, 2), (32, 1), (32, 2)), (64, 10), (3, 16, 16), 2, 0.004, 13),
+    # seven 3x3 convs: footprint windows up to 13 x 13 over the first conv's
+    # output (more than 128 pixels: one window per workgroup onto the domain)
+    (((8, 1),) * 7, (10, 5), (3, 16, 16), 1, 0.01, 14),
 ])
 def test_cnn_small(lbp, method, convs, fcs, in_shape, batch, eps, seed):
     print(f"cnn {convs} {fcs} {in_shape} batch {batch} {method}", flush=True)
