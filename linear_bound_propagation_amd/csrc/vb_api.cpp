@@ -1347,11 +1347,6 @@ bool one_affine_step(const Graph& G, int z, int stop) {
   return src_of(G, n.in0) == stop;
 }
 
-vb_status check_stream_ptrs(const void* p, const char* what) {
-  if (!p) return fail(VB_EINVAL, "%s is NULL", what);
-  return VB_OK;
-}
-
 // ---------------------------------------------------------------------------
 // IBP
 
