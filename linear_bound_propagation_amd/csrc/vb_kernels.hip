@@ -187,7 +187,8 @@ hipError_t launch_identity_linear(const float* W, int n_out, int n_in, const flo
   return hipGetLastError();
 }
 
-// one block per identity row
+// one block per identity row; the element index runs in 32 bits and advances
+// by the block size without a division per element (but one by Wi)
 __global__ __launch_bounds__(256) void identity_conv_kernel(const IdConv a, float* __restrict__ rowacc) {
   __shared__ float sh[4];
   const long long row = blockIdx.x;
@@ -198,41 +199,51 @@ __global__ __launch_bounds__(256) void identity_conv_kernel(const IdConv a, floa
   const float sg = r < n_out ? 1.f : -1.f;
   const long long i = r < n_out ? r : r - n_out;
   const int c = (int)(i % a.Co);
-  const long long p = i / a.Co;
-  const int y = (int)(p / a.Wo), x = (int)(p % a.Wo);
-  const long long L = (long long)a.Hi * a.Wi * a.Ci;
+  const int p = (int)(i / a.Co);
+  const int y = p / a.Wo, x = p - (p / a.Wo) * a.Wo;
+  const int L = a.Hi * a.Wi * a.Ci;
+  const float* addend = a.addend ? a.addend + row * L : nullptr;
+  float* out = a.out ? a.out + row * L : nullptr;
+  const float* lo = a.lo ? a.lo + b * L : nullptr;
+  const float* hi = a.hi ? a.hi + b * L : nullptr;
+  const float* center = a.center ? a.center + b * L : nullptr;
+  const float* radius = a.radius ? a.radius + b * L : nullptr;
+  const int dq = 256 / a.Ci, dci = 256 - dq * a.Ci;
+  int ci = threadIdx.x % a.Ci, q = threadIdx.x / a.Ci;
   float s = 0.f;
-  for (long long e = threadIdx.x; e < L; e += 256) {
-    const int ci = (int)(e % a.Ci);
-    const long long q = e / a.Ci;
-    const int yy = (int)(q / a.Wi), xx = (int)(q % a.Wi);
+  for (int e = threadIdx.x; e < L; e += 256) {
+    const int yy = q / a.Wi, xx = q - (q / a.Wi) * a.Wi;
     const int ky = yy - y * a.stride + a.pad, kx = xx - x * a.stride + a.pad;
     float v = 0.f;
-    if (ky >= 0 && ky < a.kh && kx >= 0 && kx < a.kw)
-      v = sg * a.W[(((long long)ky * a.kw + kx) * a.Co + c) * a.Ci + ci];
-    if (a.addend) v += a.addend[row * L + e];
+    if (ky >= 0 && ky < a.kh && kx >= 0 && kx < a.kw) v = sg * a.W[((ky * a.kw + kx) * a.Co + c) * a.Ci + ci];
+    if (addend) v += addend[e];
     if (a.mode == E_STORE) {
-      a.out[row * L + e] = v;
+      out[e] = v;
       if (a.bias) s += v * a.bias[ci];
     } else if (a.mode == E_RELAX) {
-      const float l = a.lo[b * L + e], u = a.hi[b * L + e];
       float al, sl, t;
-      relax_coeffs(l, u, al, sl, t);
+      relax_coeffs(lo[e], hi[e], al, sl, t);
       const float o = v >= 0.f ? v * al : v * sl;
-      a.out[row * L + e] = o;
+      out[e] = o;
       if (a.bias) s += o * a.bias[ci];
       s += fminf(v, 0.f) * t;
     } else {
       float cc, rr;
-      if (a.center) {
-        cc = a.center[b * L + e];
-        rr = a.radius ? a.radius[b * L + e] : a.eps;
+      if (center) {
+        cc = center[e];
+        rr = radius ? radius[e] : a.eps;
       } else {
-        const float l = a.lo[b * L + e], u = a.hi[b * L + e];
-        cc = (l + u) * 0.5f;
-        rr = (u - l) * 0.5f;
+        cc = (lo[e] + hi[e]) * 0.5f;
+        rr = (hi[e] - lo[e]) * 0.5f;
       }
       s += v * cc - fabsf(v) * rr;
+    }
+    // next element: e + 256 = (q + dq) * Ci + (ci + dci), with a carry
+    ci += dci;
+    q += dq;
+    if (ci >= a.Ci) {
+      ci -= a.Ci;
+      ++q;
     }
   }
   s = block_sum(s, sh);
@@ -242,6 +253,7 @@ __global__ __launch_bounds__(256) void identity_conv_kernel(const IdConv a, floa
 hipError_t launch_identity_conv(const IdConv& a, int batch, float* rowacc, hipStream_t st) {
   const long long rows = (long long)batch * 2 * a.Co * a.Ho * a.Wo;
   if (rows <= 0) return hipSuccess;
+  if ((long long)a.Hi * a.Wi * a.Ci >= (1LL << 31) - 256 || rows > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(identity_conv_kernel, dim3((unsigned)rows), dim3(256), 0, st, a, rowacc);
   return hipGetLastError();
 }
