@@ -722,22 +722,24 @@ hipError_t launch_identity_bias(int batch, int n, const float* bias, int bias_c,
   return hipGetLastError();
 }
 
-__global__ void identity_fill_kernel(int batch, int n, float* __restrict__ lam) {
-  const long long total = (long long)batch * 2 * n * n;
-  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-       e += (long long)gridDim.x * blockDim.x) {
-    long long row = e / n;
-    int col = (int)(e - row * n);
-    int r = (int)(row % (2 * n));
-    float v = 0.f;
-    if (r < n && col == r) v = 1.f;
-    if (r >= n && col == r - n) v = -1.f;
-    lam[e] = v;
+// +-I rows over an n-wide node: row (b, sign, r) holds sign on column r.
+// Workgroups stride over rows, threads along the row (no division per element).
+__global__ __launch_bounds__(256) void identity_fill_kernel(int batch, int n, float* __restrict__ lam) {
+  const long long rows = (long long)batch * 2 * n;
+  for (long long row = blockIdx.x; row < rows; row += gridDim.x) {
+    const int r = (int)(row % (2 * n));
+    const int col = r < n ? r : r - n;
+    const float sg = r < n ? 1.f : -1.f;
+    float* out = lam + row * n;
+    for (int e = threadIdx.x; e < n; e += 256) out[e] = e == col ? sg : 0.f;
   }
 }
 
 hipError_t launch_identity_fill(int batch, int n, float* lam, hipStream_t st) {
-  hipLaunchKernelGGL(identity_fill_kernel, dim3(4096), dim3(256), 0, st, batch, n, lam);
+  const long long rows = (long long)batch * 2 * n;
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(identity_fill_kernel, dim3((unsigned)std::min<long long>(rows, 65536)), dim3(256), 0, st, batch,
+                     n, lam);
   return hipGetLastError();
 }
 
