@@ -1194,7 +1194,7 @@ __global__ __launch_bounds__(CADJ_THREADS) void conv_adjoint_first_kernel(const 
     const int p = min(p0 + mb * 16 + li, p1 - 1);  // rows past the band repeat its last pixel, never stored
     const int oy = p / c.Wo, ox = p - oy * c.Wo;
     const int corner = ((oy * c.stride - r0) * Wp + ox * c.stride) * CI;
-    // this lane's results: pixel p0 + 16 mb + 4 kk + v, channel 16 nb + li.
+    // this lane's results: pixel p0 + 16 mb + 4 kk + v, channel cbase + 16 nb + li.
     // The relaxation coefficients of result row v + 1 are loaded while row v
     // finishes (those of row 0 ahead of the products)
     long long nn[4][NBN];
