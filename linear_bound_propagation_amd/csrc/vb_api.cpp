@@ -1221,8 +1221,11 @@ size_t wt_floats(const Graph& G) {
 // Write W^T of every affine node into ws (Linear: [n_in][n_out]; Conv: per tap
 // [c_in][c_out]) and the per-node bias a Lambda carries into beta (for an ADD:
 // the sum of its inputs' biases); return the per-node pointers.
+// Transposed weights and summed ADD biases at the head of the workspace, and
+// their addresses; with launch false only the addresses (the copies are
+// already there from an earlier call on the same workspace).
 vb_status prepare_weights(const Graph& G, char* ws, hipStream_t st, std::vector<const float*>& wt,
-                          std::vector<const float*>& beff) {
+                          std::vector<const float*>& beff, bool launch = true) {
   wt.assign(G.n.size(), nullptr);
   beff.assign(G.n.size(), nullptr);
   float* p = (float*)ws;
@@ -1230,13 +1233,13 @@ vb_status prepare_weights(const Graph& G, char* ws, hipStream_t st, std::vector<
     const NodeInfo& n = G.n[k];
     if (n.op == VB_LINEAR) {
       const int nin = (int)G.n[n.in0].size;
-      HIPCHK(launch_transpose(n.W, 1, (int)n.size, nin, p, st));
+      if (launch) HIPCHK(launch_transpose(n.W, 1, (int)n.size, nin, p, st));
       wt[k] = p;
       beff[k] = n.b;
       p += align_up((size_t)n.size * nin * 4) / 4;
     } else if (n.op == VB_CONV2D) {
       const int cin = G.n[n.in0].c;
-      HIPCHK(launch_transpose(n.W, n.kh * n.kw, n.c, cin, p, st));
+      if (launch) HIPCHK(launch_transpose(n.W, n.kh * n.kw, n.c, cin, p, st));
       wt[k] = p;
       beff[k] = n.b;
       p += align_up((size_t)n.kh * n.kw * n.c * cin * 4) / 4;
@@ -1246,8 +1249,10 @@ vb_status prepare_weights(const Graph& G, char* ws, hipStream_t st, std::vector<
       if (terms.size() == 1) {
         beff[k] = terms[0];
       } else if (terms.size() > 1) {
-        HIPCHK(launch_add(terms[0], terms[1], 1.f, p, n.c, st));
-        for (size_t i = 2; i < terms.size(); ++i) HIPCHK(launch_add(p, terms[i], 1.f, p, n.c, st));
+        if (launch) {
+          HIPCHK(launch_add(terms[0], terms[1], 1.f, p, n.c, st));
+          for (size_t i = 2; i < terms.size(); ++i) HIPCHK(launch_add(p, terms[i], 1.f, p, n.c, st));
+        }
         beff[k] = p;
       }
       p += align_up((size_t)n.c * 4) / 4;
@@ -1551,13 +1556,13 @@ extern "C" vb_status vb_workspace_size(const vb_graph* g, int32_t batch, int32_t
 
 static vb_status spec_ibp(const Graph& G, int batch, const float* C, int m, const float* const* lo,
                           const float* const* hi, float* spec_lo, float* spec_hi, void* ws, size_t ws_bytes,
-                          hipStream_t st) {
+                          hipStream_t st, bool weights_ready = false) {
   const int L = G.L;
   if (G.n[L].op != VB_LINEAR) return fail(VB_EUNSUPPORTED, "spec bounds need a LINEAR last node");
   const int stop = src_of(G, G.n[L].in0);
   if (stop == 0) return fail(VB_EUNSUPPORTED, "spec IBP over a single affine layer: use CROWN (exact)");
   Backward B{G, st, lo, hi, {nullptr, nullptr, 0.f}};
-  vb_status s = prepare_weights(G, (char*)ws, st, B.wt, B.beff);
+  vb_status s = prepare_weights(G, (char*)ws, st, B.wt, B.beff, !weights_ready);
   if (s) return s;
   return backward_all(B, L, stop, C, m, 1, batch, 2LL * m, (char*)ws, ws_bytes, wt_floats(G),
                       [&](float* acc, int b0, int cb) -> vb_status {
@@ -1598,7 +1603,8 @@ static vb_status crown_backward_impl(const Graph& G, int batch, int start, int s
                                      const float* const* lo, const float* const* hi, Domain dom, float* lb,
                                      float* ub, void* ws, size_t ws_bytes, hipStream_t st, float* a_out = nullptr,
                                      float* bias_out = nullptr, const float* const* alpha = nullptr,
-                                     bool intersect = false, const vb_alpha_compact* compact = nullptr) {
+                                     bool intersect = false, const vb_alpha_compact* compact = nullptr,
+                                     bool weights_ready = false) {
   Backward B{G, st, lo, hi, dom};
   B.a_out = a_out;
   B.bias_out = bias_out;
@@ -1607,7 +1613,7 @@ static vb_status crown_backward_impl(const Graph& G, int batch, int start, int s
     B.aidx = compact->index;
     B.awidth = compact->width;
   }
-  vb_status s = prepare_weights(G, (char*)ws, st, B.wt, B.beff);
+  vb_status s = prepare_weights(G, (char*)ws, st, B.wt, B.beff, !weights_ready);
   if (s) return s;
   const bool lower_only = C && !ub;
   const long long R = C ? (lower_only ? m : 2LL * m) : 2LL * G.n[start].size;
@@ -1696,8 +1702,14 @@ extern "C" vb_status vb_crown(const vb_graph* g, int32_t batch, const float* x_c
   hipStream_t st = (hipStream_t)stream;
   s = ibp_impl(G, batch, x_center, x_radius, eps, node_lo, node_hi, st, ws, ws_bytes);
   if (s) return s;
+  // the weight copies at the head of the workspace serve every backward call below
+  if (C || method != VB_METHOD_IBP) {
+    std::vector<const float*> wt, beff;
+    s = prepare_weights(G, (char*)ws, st, wt, beff);
+    if (s) return s;
+  }
   if (C && (ibp_lb || ibp_ub)) {
-    s = spec_ibp(G, batch, C, m, node_lo, node_hi, ibp_lb, ibp_ub, ws, ws_bytes, st);
+    s = spec_ibp(G, batch, C, m, node_lo, node_hi, ibp_lb, ibp_ub, ws, ws_bytes, st, true);
     if (s) return s;
   }
   const Domain dom{x_center, x_radius, eps};
@@ -1709,12 +1721,13 @@ extern "C" vb_status vb_crown(const vb_graph* g, int32_t batch, const float* x_c
       const int z = G.n[r].in0;
       if (z <= stop || one_affine_step(G, z, stop)) continue;
       s = crown_backward_impl(G, batch, z, stop, nullptr, 0, node_lo, node_hi, dom, node_lo[z], node_hi[z], ws,
-                              ws_bytes, st, nullptr, nullptr, nullptr, intersect);
+                              ws_bytes, st, nullptr, nullptr, nullptr, intersect, nullptr, true);
       if (s) return s;
     }
   }
   if (C && (lb || ub)) {
-    s = crown_backward_impl(G, batch, G.L, stop, C, m, node_lo, node_hi, dom, lb, ub, ws, ws_bytes, st);
+    s = crown_backward_impl(G, batch, G.L, stop, C, m, node_lo, node_hi, dom, lb, ub, ws, ws_bytes, st, nullptr,
+                            nullptr, nullptr, false, nullptr, true);
     if (s) return s;
   }
   return VB_OK;
