@@ -31,6 +31,8 @@ _OPS = {"input": VB_INPUT, "linear": VB_LINEAR, "conv": VB_CONV2D, "relu": VB_RE
 
 EXPORTS = ["vb_last_error", "vb_workspace_size", "vb_ibp", "vb_crown_backward", "vb_concretize",
            "vb_alpha_layout", "vb_alpha_init", "vb_alpha_step", "vb_crown", "vb_profile_start", "vb_profile_stop"]
+# host-only helpers declared in include/vb_testing.h (used by the CPU tests)
+TESTING_EXPORTS = ["vb_testing_fastdiv", "vb_testing_conv_tile_n"]
 
 
 class vb_node(ctypes.Structure):

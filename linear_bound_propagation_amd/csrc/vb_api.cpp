@@ -1285,20 +1285,28 @@ WsLayout layout_for(long long maxw, long long part_per_b, long long R, int cb, s
 
 // Run a back-substitution over the whole batch in chunks that fit `ws`.
 // For each chunk, `after` is called with (rowacc, b0, cb) to consume the row bounds.
-template <class After>
-vb_status backward_all(Backward& B, int start, int stop, const float* C, int m, int split, int batch, long long R,
-                       char* ws, size_t ws_bytes, size_t reserved_floats, After after) {
+// How a back-substitution of R rows per batch element from `start` to `stop`
+// is chunked over the batch: the largest chunk whose workspace fits ws_bytes
+// (and whose GEMM index spaces stay 32-bit).  `plain` rows (identity rows
+// without returned linear bounds, alpha or kept Psi) may take the footprint
+// path; `spec` rows widen Lambda to the start node.
+struct ChunkPlan {
+  int cb;
+  WsLayout L;
+};
+
+vb_status plan_chunks(const Graph& G, int start, int stop, long long R, bool plain, bool spec, int batch,
+                      size_t ws_bytes, size_t reserved_floats, ChunkPlan& plan) {
   long long maxw, ppb;
-  if (C || B.a_out || B.alpha || B.psi_keep || !patch_requirements(B.G, start, stop, R, maxw, ppb))
-    bwd_requirements(B.G, start, stop, R, maxw, ppb);
-  if (C) maxw = std::max(maxw, B.G.n[start].size);
-  const long long box = stop > 0 ? B.G.n[stop].size : 0;
+  if (!plain || !patch_requirements(G, start, stop, R, maxw, ppb)) bwd_requirements(G, start, stop, R, maxw, ppb);
+  if (spec) maxw = std::max(maxw, G.n[start].size);
+  const long long box = stop > 0 ? G.n[stop].size : 0;
   // GEMM index spaces are 32-bit: rows x pixels (padded to whole row blocks) per launch
   long long maxp = 1;
-  for (size_t k = 1; k < B.G.n.size(); ++k) {
-    const NodeInfo& nd = B.G.n[k];
+  for (size_t k = 1; k < G.n.size(); ++k) {
+    const NodeInfo& nd = G.n[k];
     if (nd.op != VB_CONV2D || (int)k > start || (int)k <= stop) continue;
-    const NodeInfo& in = B.G.n[src_of(B.G, nd.in0)];
+    const NodeInfo& in = G.n[src_of(G, nd.in0)];
     maxp = std::max(maxp, std::max((long long)in.h * in.w, (long long)nd.h * nd.w));
   }
   auto fits_index = [&](long long cbn) { return cbn * R * maxp + 64 * maxp + 256 <= (long long)INT32_MAX; };
@@ -1308,9 +1316,24 @@ vb_status backward_all(Backward& B, int start, int stop, const float* C, int m, 
   if (!fits_index(cb))
     return fail(VB_EUNSUPPORTED, "one batch element has %lld rows x %lld pixels: beyond the 32-bit GEMM index range",
                 R, maxp);
-  WsLayout L = layout_for(maxw, ppb, R, cb, reserved_floats, box);
-  if (L.bytes > ws_bytes)
-    return fail(VB_ENOMEM, "workspace of %zu bytes is too small: one batch element needs %zu", ws_bytes, L.bytes);
+  plan.cb = cb;
+  plan.L = layout_for(maxw, ppb, R, cb, reserved_floats, box);
+  if (plan.L.bytes > ws_bytes)
+    return fail(VB_ENOMEM, "workspace of %zu bytes is too small: one batch element needs %zu", ws_bytes, plan.L.bytes);
+  return VB_OK;
+}
+
+// Run a back-substitution over the whole batch in chunks that fit `ws`.
+// For each chunk, `after` is called with (rowacc, b0, cb) to consume the row bounds.
+template <class After>
+vb_status backward_all(Backward& B, int start, int stop, const float* C, int m, int split, int batch, long long R,
+                       char* ws, size_t ws_bytes, size_t reserved_floats, After after) {
+  ChunkPlan plan;
+  const bool plain = !(C || B.a_out || B.alpha || B.psi_keep);
+  vb_status s0 = plan_chunks(B.G, start, stop, R, plain, C != nullptr, batch, ws_bytes, reserved_floats, plan);
+  if (s0) return s0;
+  const int cb = plan.cb;
+  const WsLayout& L = plan.L;
   char* p = ws + align_up(reserved_floats * 4);
   for (int i = 0; i < NPOOL; ++i) {
     B.pool[i] = (float*)p;
@@ -1384,14 +1407,55 @@ size_t ibp_workspace(const Graph& G, int batch) {
   return best;
 }
 
-vb_status ibp_impl(const Graph& G, int batch, const float* xc, const float* xr, float eps, float* const* lo,
-                   float* const* hi, hipStream_t st, void* ws = nullptr, size_t ws_bytes = 0) {
+// Which nodes IBP writes, checked before anything is launched: a node is
+// skipped when its bounds storage is NULL, which is an error if another node
+// reads its bounds (affine nodes read their source through flatten nodes; the
+// spec fold reads the last node's source).  Patterns the kernels do not take
+// (ReLU / ADD / GAP / FLATTEN fed by the input node) are rejected here too.
+vb_status ibp_plan(const Graph& G, float* const* lo, float* const* hi, bool spec, std::vector<char>& skip) {
   const int N = (int)G.n.size();
-  std::vector<char> done(N, 0);
+  skip.assign(N, 0);
+  std::vector<char> needed(N, 0);
+  for (int k = 1; k < N; ++k) {
+    const NodeInfo& nd = G.n[k];
+    switch (nd.op) {
+      case VB_LINEAR:
+      case VB_CONV2D:
+        needed[src_of(G, nd.in0)] = 1;
+        break;
+      case VB_RELU:
+      case VB_GAP:
+      case VB_FLATTEN:
+        if (nd.in0 == 0) return fail(VB_EUNSUPPORTED, "node %d: op %d directly on the input node", k, nd.op);
+        needed[nd.in0] = 1;
+        break;
+      case VB_ADD:
+        if (nd.in0 == 0 || nd.in1 == 0) return fail(VB_EUNSUPPORTED, "node %d: ADD directly on the input node", k);
+        needed[nd.in0] = needed[nd.in1] = 1;
+        break;
+      default:
+        return fail(VB_EUNSUPPORTED, "IBP through node %d (op %d)", k, nd.op);
+    }
+  }
+  if (spec) needed[src_of(G, G.n[G.L].in0)] = 1;
+  for (int k = 1; k < N; ++k) {
+    const bool has = lo[k] && hi[k];
+    if (!has && needed[k]) return fail(VB_EINVAL, "node %d: IBP needs node_lo/node_hi storage (its bounds are read)", k);
+    if ((lo[k] == nullptr) != (hi[k] == nullptr)) return fail(VB_EINVAL, "node %d: only one of node_lo/node_hi given", k);
+    skip[k] = !has;
+  }
+  return VB_OK;
+}
+
+vb_status ibp_impl(const Graph& G, int batch, const float* xc, const float* xr, float eps, float* const* lo,
+                   float* const* hi, hipStream_t st, void* ws = nullptr, size_t ws_bytes = 0, bool spec = false) {
+  const int N = (int)G.n.size();
+  std::vector<char> done;
+  vb_status s0 = ibp_plan(G, lo, hi, spec, done);
+  if (s0) return s0;
   for (int k = 1; k < N; ++k) {
     const NodeInfo& nd = G.n[k];
     if (done[k]) continue;
-    if (!lo[k] || !hi[k]) return fail(VB_EINVAL, "node %d: IBP needs node_lo/node_hi storage", k);
     const int p = nd.in0;
     const int ps = src_of(G, p);
     switch (nd.op) {
@@ -1467,22 +1531,16 @@ vb_status ibp_impl(const Graph& G, int batch, const float* xc, const float* xr, 
         break;
       }
       case VB_RELU:
-        if (p == 0) {
-          return fail(VB_EUNSUPPORTED, "ReLU directly on the input node");
-        }
         HIPCHK(launch_ibp_eltwise(0, lo[p], hi[p], nullptr, nullptr, lo[k], hi[k], (long long)batch * nd.size, st));
         break;
       case VB_ADD:
-        if (nd.in0 == 0 || nd.in1 == 0) return fail(VB_EUNSUPPORTED, "ADD directly on the input node");
         HIPCHK(launch_ibp_eltwise(1, lo[nd.in0], hi[nd.in0], lo[nd.in1], hi[nd.in1], lo[k], hi[k],
                                   (long long)batch * nd.size, st));
         break;
       case VB_GAP:
-        if (p == 0) return fail(VB_EUNSUPPORTED, "GAP directly on the input node");
         HIPCHK(launch_ibp_gap(lo[p], hi[p], batch, G.n[p].h * G.n[p].w, G.n[p].c, lo[k], hi[k], st));
         break;
       case VB_FLATTEN:
-        if (p == 0) return fail(VB_EUNSUPPORTED, "FLATTEN directly on the input node");
         if (lo[k] != lo[p]) HIPCHK(launch_add(lo[p], nullptr, 0.f, lo[k], (long long)batch * nd.size, st));
         if (hi[k] != hi[p]) HIPCHK(launch_add(hi[p], nullptr, 0.f, hi[k], (long long)batch * nd.size, st));
         break;
@@ -1585,12 +1643,15 @@ extern "C" vb_status vb_ibp(const vb_graph* g, int32_t batch, const float* x_cen
   if (C && m <= 0) return fail(VB_EINVAL, "m must be positive with C");
   if (C && !ws) return fail(VB_EINVAL, "spec bounds need a workspace");
   if (C) {
+    if (G.n[G.L].op != VB_LINEAR) return fail(VB_EUNSUPPORTED, "spec bounds need a LINEAR last node");
+    if (src_of(G, G.n[G.L].in0) == 0)
+      return fail(VB_EUNSUPPORTED, "spec IBP over a single affine layer: use CROWN (exact)");
     const size_t need = crown_workspace(G, 1, m, VB_METHOD_IBP, 0);
     if (ws_bytes < need)
       return fail(VB_ENOMEM, "workspace of %zu bytes is too small: one batch element needs %zu", ws_bytes, need);
   }
   hipStream_t st = (hipStream_t)stream;
-  s = ibp_impl(G, batch, x_center, x_radius, eps, node_lo, node_hi, st, ws, ws_bytes);
+  s = ibp_impl(G, batch, x_center, x_radius, eps, node_lo, node_hi, st, ws, ws_bytes, C != nullptr);
   if (s) return s;
   if (C) return spec_ibp(G, batch, C, m, node_lo, node_hi, spec_lo, spec_hi, ws, ws_bytes, st);
   return VB_OK;
@@ -1657,6 +1718,15 @@ extern "C" vb_status vb_crown_backward(const vb_graph* g, int32_t batch, int32_t
     for (size_t k = start > stop ? stop + 1 : 0; (int)k < start; ++k)
       if (G.n[k].op == VB_RELU && !alpha[k] && !(compact && compact->width[k] == 0))
         return fail(VB_EINVAL, "alpha of ReLU node %zu is NULL", k);
+  }
+  {
+    // the workspace must hold the weight copies and one batch element's chunk
+    // before anything is enqueued (the copies are written first)
+    const bool lower_only = C && !ub;
+    const long long R = C ? (lower_only ? m : 2LL * m) : 2LL * G.n[start].size;
+    const bool plain = !(C || A_out || alpha);
+    ChunkPlan plan;
+    if ((s = plan_chunks(G, start, stop, R, plain, C != nullptr, 1, ws_bytes, wt_floats(G), plan))) return s;
   }
   return crown_backward_impl(G, batch, start, stop, C, m, node_lo, node_hi, {x_center, x_radius, eps}, lb, ub, ws,
                              ws_bytes, (hipStream_t)stream, A_out, bias_out, alpha, false, compact);
@@ -2076,4 +2146,62 @@ extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float
     cur ^= 1;
   }
   return VB_OK;
+}
+
+// ---------------------------------------------------------------------------
+// host-only helpers for the tests (vb_testing.h)
+
+#include "vb_testing.h"
+
+extern "C" int32_t vb_testing_fastdiv(int32_t d, const int32_t* x, int64_t n, int32_t* q, uint32_t* mul,
+                                      uint32_t* shr) {
+  if (d < 1 || n < 0 || (n > 0 && (!x || !q))) return -1;
+  const FastDiv f = make_fastdiv(d);
+  if (mul) *mul = f.mul;
+  if (shr) *shr = f.shr;
+  for (int64_t i = 0; i < n; ++i) {
+    if (x[i] < 0) return -1;
+    // the kernels' division: high 32 bits of x * mul, shifted right by shr
+    q[i] = f.d == 1 ? x[i] : (int32_t)((uint32_t)(((uint64_t)(uint32_t)x[i] * f.mul) >> 32) >> f.shr);
+  }
+  return 0;
+}
+
+extern "C" int32_t vb_testing_conv_tile_n(int32_t mode, int32_t rows, int32_t h, int32_t w, int32_t c_in,
+                                          int32_t c_out) {
+  if (rows <= 0 || h <= 0 || w <= 0 || c_in <= 0 || c_out <= 0) return -1;
+  NodeInfo in{}, nd{};
+  in.op = VB_RELU;
+  in.c = c_in;
+  in.h = h;
+  in.w = w;
+  in.size = (long long)c_in * h * w;
+  nd.op = VB_CONV2D;
+  nd.c = c_out;
+  nd.h = h;
+  nd.w = w;
+  nd.size = (long long)c_out * h * w;
+  nd.kh = nd.kw = 3;
+  nd.stride = 1;
+  nd.pad = 1;
+  // stand-in operand addresses: only their alignment is looked at, nothing is read
+  const float* fake = reinterpret_cast<const float*>((uintptr_t)4096);
+  nd.W = fake;
+  GemmDesc d;
+  if (mode == E_STORE || mode == E_RELAX || mode == E_CONCRETIZE) {
+    if (!conv_backward(nd, in, fake, rows, 0, 0, d)) return -1;
+  } else if (mode == E_ADJOINT) {
+    d = affine_forward(nd, in, rows);
+    d.A = fake;
+  } else {
+    return -1;
+  }
+  d.epi = mode;
+  d.B = fake;
+  const int nt = gemm_ntiles(d);
+  if (nt <= 0) return -1;
+  // the narrowest of the launcher's widths that covers N with nt tiles
+  for (int bn : {32, 64, 128, 256})
+    if ((d.N + bn - 1) / bn == nt) return bn;
+  return -1;
 }

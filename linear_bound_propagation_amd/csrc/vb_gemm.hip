@@ -808,7 +808,10 @@ hipError_t launch_shape(const GemmDesc& d, bool dense, bool fast, hipStream_t st
 // GEMMs with the fast path, when the grid still has at least two workgroups per CU
 // (dense GEMMs ran faster on two 128 x 128 workgroups per CU).
 bool use_big(const GemmDesc& d, bool fast) {
-  if (!fast || d.epi == E_IBP || d.N < 256 || gemm_is_dense(d) || d.patch || d.aidx) return false;
+  // (the 256 x 256 variants exist for the store, relaxation and concretisation
+  // epilogues only)
+  if (d.epi != E_STORE && d.epi != E_RELAX && d.epi != E_CONCRETIZE) return false;
+  if (!fast || d.N < 256 || gemm_is_dense(d) || d.patch || d.aidx) return false;
   const long long tiles = (long long)((d.Mt + 255) / 256) * ((d.N + 255) / 256);
   return tiles >= 512;
 }
@@ -879,13 +882,17 @@ hipError_t launch_gemm(const GemmDesc& desc, hipStream_t st) {
   const bool fast = is_fast(d);
   const int bn = tile_n(d, fast);
   if (bn == 256) {
-    // gather GEMMs with plain epilogues only (checked in use_big); IBP never takes this tile
+    // gather GEMMs with the store, relaxation or concretisation epilogue only
+    // (checked in use_big); IBP and the adjoint never take this tile
     const int mt = (d.Mt + 255) / 256, nt = (d.N + 255) / 256;
     const dim3 g(((mt * nt + 7) / 8) * 8), b(512);
     switch (d.epi) {
       case E_STORE: hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 4, false, A_PLAIN, E_STORE, true>), g, b, 0, st, d); break;
       case E_RELAX: hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 4, false, A_PLAIN, E_RELAX, true>), g, b, 0, st, d); break;
-      default: hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 4, false, A_PLAIN, E_CONCRETIZE, true>), g, b, 0, st, d); break;
+      case E_CONCRETIZE:
+        hipLaunchKernelGGL((gemm_kernel<256, 256, 2, 4, false, A_PLAIN, E_CONCRETIZE, true>), g, b, 0, st, d);
+        break;
+      default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }

@@ -11,13 +11,19 @@ from helpers import ROOT, ensure_built
 ensure_built()
 import linear_bound_propagation_amd as lbp  # noqa: E402
 
-HEADER = os.path.join(ROOT, "include", "vb.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
+
+
+def _declared(path):
+    return set(re.findall(r"^(?:vb_status|const char\*|int32_t)\s+(vb_\w+)\s*\(", open(path).read(), flags=re.M))
 
 
 def test_exports_every_declared_symbol():
-    src = open(HEADER).read()
-    declared = set(re.findall(r"^(?:vb_status|const char\*)\s+(vb_\w+)\s*\(", src, flags=re.M))
-    assert declared == set(lbp.EXPORTS)
+    declared = set()
+    for h in HEADERS:
+        declared |= _declared(h)
+    assert declared == set(lbp.EXPORTS) | set(lbp.TESTING_EXPORTS)
     lib = ctypes.CDLL(lbp.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
@@ -136,23 +142,78 @@ def test_entry_points_reject_bad_arguments_without_launching():
     assert lbp.lib().vb_concretize(2, 4, 1, None, None, P(64), None, 0.1, None, None, None) == -1
 
 
-def _fastdiv(d):
-    # the host-side magic numbers of the library's division by a runtime constant
-    if d == 1:
-        return 0, 0
-    l = (d - 1).bit_length()
-    return ((1 << (31 + l)) + d - 1) // d, l - 1
-
-
 def test_fastdiv_magic_numbers_are_exact():
+    """The library's own division by a runtime constant (its multiply-high magic
+    numbers, exported for this test) equals integer division."""
     import numpy as np
+    f = lbp.lib().vb_testing_fastdiv
+    f.restype = ctypes.c_int32
+    f.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32)]
     rng = np.random.default_rng(0)
-    for d in list(range(1, 300)) + [1024, 3072, 4097, 65536, 65537, 99991, 2 ** 20 + 7, 2 ** 30 + 1]:
-        mul, shr = _fastdiv(d)
+    for d in list(range(1, 300)) + [1024, 3072, 4097, 65536, 65537, 99991, 2 ** 20 + 7, 2 ** 30 + 1, 2 ** 31 - 1]:
         xs = np.concatenate([np.arange(0, 3000), rng.integers(0, 2 ** 31, 3000),
                              np.array([2 ** 31 - 1, d - 1, d, d + 1, 2 * d - 1, 2 * d])])
-        for x in xs.tolist():
-            if x < 0 or x >= 2 ** 31:
-                continue
-            q = x if d == 1 else ((x * mul) >> 32) >> shr
-            assert mul < 2 ** 32 and q == x // d, (x, d, q)
+        xs = xs[(xs >= 0) & (xs < 2 ** 31)].astype(np.int32)
+        q = np.empty_like(xs)
+        mul, shr = ctypes.c_uint32(), ctypes.c_uint32()
+        assert f(d, xs.ctypes.data, xs.size, q.ctypes.data, ctypes.byref(mul), ctypes.byref(shr)) == 0
+        assert np.array_equal(q, xs // d), d
+        assert (d == 1) == (mul.value == 0)
+    xs = np.array([-1], dtype=np.int32)
+    q = np.empty_like(xs)
+    assert f(3, xs.ctypes.data, 1, q.ctypes.data, None, None) == -1
+    assert f(0, xs.ctypes.data, 0, q.ctypes.data, None, None) == -1
+
+
+def test_big_tiles_only_for_plain_epilogues():
+    """256-wide tiles are chosen for large convolutions with the store, relaxation or
+    concretisation epilogue only; the alpha-CROWN adjoint never takes them."""
+    f = lbp.lib().vb_testing_conv_tile_n
+    f.restype = ctypes.c_int32
+    f.argtypes = [ctypes.c_int32] * 6
+    rows = 4096  # 4096 rows x 64 pixels / 256 = 1024 M-tiles
+    for mode in (0, 1, 2):
+        assert f(mode, rows, 8, 8, 256, 256) == 256, mode
+        assert f(mode, 8, 8, 8, 256, 256) == 128, mode      # too few tiles for two per CU
+        assert f(mode, rows, 8, 8, 128, 256) == 128, mode   # N = c_in = 128
+    assert f(4, rows, 8, 8, 256, 256) == 128
+    assert f(4, rows, 8, 8, 256, 64) == 64
+    assert f(3, rows, 8, 8, 256, 256) == -1
+    assert f(0, 0, 8, 8, 256, 256) == -1
+
+
+def test_crown_backward_workspace_checked_before_any_launch():
+    """A workspace smaller than the weight copies plus one batch element is rejected
+    with VB_ENOMEM before anything is enqueued (no stream, no device pointers read)."""
+    g, keep = _mlp_graph()
+    gp = ctypes.pointer(g)
+    P = ctypes.c_void_p
+    bounds = (ctypes.c_void_p * 4)(None, 64, 64, 64)
+    for C, m in ((None, 0), (P(64), 2)):
+        st = lbp.lib().vb_crown_backward(gp, 2, 3, 0, C, m, bounds, bounds, None, None, P(64), None, 0.1, P(64),
+                                        P(64), None, None, P(64), 64, None)
+        assert st == -3, st
+        assert b"too small" in lbp.lib().vb_last_error()
+
+
+def test_ibp_checks_every_node_before_launching():
+    """IBP validates the whole graph first: a ReLU on the input node, or missing storage
+    for a node whose bounds another node reads, fails with nothing enqueued; storage may
+    be omitted for a node nothing reads (the last one)."""
+    P = ctypes.c_void_p
+    g, keep = _graph([dict(op=0, in0=-1, in1=-1, c=4, h=1, w=1),
+                      dict(op=1, in0=0, in1=-1, c=4, h=1, w=1, weight=16, bias=32),
+                      dict(op=3, in0=0, in1=-1, c=4, h=1, w=1)])
+    b = (ctypes.c_void_p * 3)(None, 64, 64)
+    assert lbp.lib().vb_ibp(ctypes.pointer(g), 2, P(64), None, 0.1, b, b, None, 0, None, None, None, 0, None) == -5
+    g, keep = _mlp_graph()
+    miss = (ctypes.c_void_p * 4)(None, None, 64, 64)    # node 1 feeds the ReLU
+    assert lbp.lib().vb_ibp(ctypes.pointer(g), 2, P(64), None, 0.1, miss, miss, None, 0, None, None, None, 0,
+                            None) == -1
+    assert b"is read" in lbp.lib().vb_last_error() or b"are read" in lbp.lib().vb_last_error()
+    half = (ctypes.c_void_p * 4)(None, 64, 64, None)
+    other = (ctypes.c_void_p * 4)(None, 64, 64, 64)
+    assert lbp.lib().vb_ibp(ctypes.pointer(g), 2, P(64), None, 0.1, half, other, None, 0, None, None, None, 0,
+                            None) == -1
+    assert b"only one of" in lbp.lib().vb_last_error()
