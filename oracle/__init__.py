@@ -17,10 +17,13 @@ so the arithmetic is the standard published definition of each algorithm
 ReLU relaxation; alpha-CROWN projected gradient ascent on the lower slopes),
 written out step by step in float64.
 
-Every function is pinned by the CPU tests against brute force, closed forms
-and hand-derived examples; nothing is marked "parity unpinned" except the
-absolute bound values of the large synthetic workloads (nothing to compare
-them to beyond the soundness and structural checks).
+Every function is pinned by the CPU tests against brute force, closed forms,
+hand-derived examples and an independent exact rational-arithmetic
+implementation on tiny networks (every intermediate-bound mode).  Parity
+unpinned: the absolute bound values of the large synthetic workloads (nothing
+published to compare them to beyond soundness and structure) and the
+architecture readings of the residual workload (its block layout is a reading,
+not a value the pages fix).
 """
 from .bounds import (Oracle, ibp, relaxation, backward, concretize, crown_bounds,
                      intermediate_bounds, spec_bounds_crown, spec_bounds_ibp)

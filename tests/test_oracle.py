@@ -211,8 +211,10 @@ def test_soundness_cnn_and_resnet_sampling():
 
 def test_intersection_mode_is_sound_and_inside_both():
     """CROWN intermediates intersected with IBP: sound on samples; every node's box lies
-    inside its IBP box; and at the first CROWN-refined layer (whose relaxations come
-    from IBP bounds in both modes) it is exactly the intersection of the two boxes."""
+    inside its IBP box and inside the pure-CROWN box at the first refined layer (whose
+    relaxations come from IBP bounds in both modes); strictly tighter than pure CROWN
+    somewhere.  (The exact values of this mode are pinned by exact rational
+    arithmetic in test_oracle_exact.py.)"""
     for seed, widths, eps in ((3, [5, 9, 9, 8, 3], 0.3), (4, [6, 12, 10, 7, 4], 0.2)):
         wl = wk.tiny_mlp(widths, eps, seed, batch=2)
         net = Oracle(wl.nodes)
@@ -223,8 +225,7 @@ def test_intersection_mode_is_sound_and_inside_both():
         for z in zs:
             assert bool((lo_x[z] >= lo_i[z] - 1e-12).all() and (hi_x[z] <= hi_i[z] + 1e-12).all())
         first = zs[1]          # zs[0] is one affine step from the input: IBP = CROWN there
-        assert torch.equal(lo_x[first], torch.maximum(lo_c[first], lo_i[first]))
-        assert torch.equal(hi_x[first], torch.minimum(hi_c[first], hi_i[first]))
+        assert bool((lo_x[first] >= lo_c[first] - 1e-12).all() and (hi_x[first] <= hi_c[first] + 1e-12).all())
         # the intersection is strictly tighter than pure CROWN somewhere in these nets
         assert any(bool((hi_x[z] < hi_c[z] - 1e-9).any() or (lo_x[z] > lo_c[z] + 1e-9).any()) for z in zs)
         wl.intermediate = "crown+ibp"
