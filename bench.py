@@ -5,7 +5,13 @@ intermediate bounds of every ReLU input (CROWN back-substitution per layer for
 the MLP workloads), and the spec bounds by IBP and by CROWN.  Inputs are
 resident in HBM before the timed region.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload N] [--no-cpu]
+  python bench.py [--steps K] [--warmup W] [--workload N] [--no-cpu] [--no-hbm] [--no-extra]
+
+Default workload: the residual network (configuration 5, the largest that fits one
+GPU), hybrid bounds (IBP up to the last stage, CROWN inside it).  `value` is
+algorithmic TFLOP/s of the whole step, counting identity rows over the conv region
+on their footprint windows (structurally non-zero multiply-adds only); the dense
+count is reported beside it.  The other workloads run briefly as extra keys.
 """
 import argparse
 import json
@@ -62,41 +68,75 @@ def _identity_consumers(nodes, z):
     return set()
 
 
-def _footprint_macs(nodes, z, stop):
-    """Multiply-adds of the identity rows over conv node z (one row per neuron, both
-    signs counted by the caller) when each row is carried on its footprint window
-    through a conv -> ReLU -> conv chain down to `stop`: at every conv only the
-    output cells inside both the row's window and the image count.  None if the
-    back-substitution from z is not such a chain."""
-    nd = nodes[z]
-    if nd.op != "conv":
+def _windows(nodes, z, stop):
+    """Footprint windows of identity rows over node z on every node they reach on the
+    way to `stop`: node k -> ((ay, y0, y1), (ax, x0, x1)), the rows of pixel (py, px) of
+    z being non-zero over k's output only at y in [ay*py + y0, ay*py + y1] (and the same
+    in x), before clipping to the image.  A conv widens the window by its kernel and
+    scales it by its stride; ReLU and ADD pass it on (an ADD input reached by several
+    paths takes the bounding box of their windows).  None if the rows leave the
+    convolution region (GAP, Linear, Flatten) before `stop`, or if two paths reach a
+    node with different scales."""
+    if nodes[z].op not in ("conv", "add", "relu"):
         return None
-    c_z, h_z, w_z = nd.shape
-    total = 0.0
-    k, wh, ww, sy, oy, sx, ox = z, 1, 1, 1, 0, 1, 0
-    while True:
+    W = {z: ((1, 0, 0), (1, 0, 0))}
+    for k in range(z, stop, -1):
+        if k not in W:
+            continue
+        nd = nodes[k]
+        (ay, y0, y1), (ax, x0, x1) = W[k]
+        if nd.op == "conv":
+            s, p = nd.stride, nd.pad
+            kh, kw = nd.weight.shape[2], nd.weight.shape[3]
+            win = ((ay * s, y0 * s - p, y1 * s - p + kh - 1), (ax * s, x0 * s - p, x1 * s - p + kw - 1))
+        elif nd.op in ("relu", "add"):
+            win = W[k]
+        else:
+            return None
+        for t in nd.inputs:
+            if t in W:
+                (by, a0, a1), (bx, b0, b1) = W[t]
+                if by != win[0][0] or bx != win[1][0]:
+                    return None
+                W[t] = ((by, min(a0, win[0][1]), max(a1, win[0][2])), (bx, min(b0, win[1][1]), max(b1, win[1][2])))
+            else:
+                W[t] = win
+    return W
+
+
+def _clipped_cells(win, shape_z, shape_k):
+    """Per pixel (py, px) of z: the cells of k's output inside both the window and the
+    image, as two factors ny[py], nx[px] (the count is ny[py] * nx[px])."""
+    (ay, y0, y1), (ax, x0, x1) = win
+    _, hz, wz = shape_z
+    _, hk, wk = shape_k
+    ys = ay * np.arange(hz)
+    xs = ax * np.arange(wz)
+    ny = np.clip(np.minimum(ys + y1, hk - 1) - np.maximum(ys + y0, 0) + 1, 0, None)
+    nx = np.clip(np.minimum(xs + x1, wk - 1) - np.maximum(xs + x0, 0) + 1, 0, None)
+    return ny, nx
+
+
+def footprint_row_macs(nodes, z, stop):
+    """Multiply-adds of one identity row over conv-region node z, per pixel of z
+    ([h_z][w_z]), when every row is carried on its footprint window: at each conv on
+    the way to `stop` only the output cells inside the row's window and the image count;
+    the first step (a copy of the weight footprint into the rows) costs nothing.  None
+    if the rows do not stay in the convolution region."""
+    W = _windows(nodes, z, stop)
+    if W is None or len(nodes[z].shape) != 3:
+        return None
+    free = _identity_consumers(nodes, z)
+    _, hz, wz = nodes[z].shape
+    per = np.zeros((hz, wz))
+    for k, win in W.items():
         nk = nodes[k]
-        if nk.op != "conv":
-            return None
+        if nk.op != "conv" or k in free or k == stop:
+            continue
         co, ci, kh, kw = nk.weight.shape
-        _, ho, wo = nk.shape
-        # cells of k's output window that exist, summed over the start node's pixels
-        ys = np.arange(h_z)[:, None] * sy + oy + np.arange(wh)[None, :]
-        xs = np.arange(w_z)[:, None] * sx + ox + np.arange(ww)[None, :]
-        ny = ((ys >= 0) & (ys < ho)).sum(1)
-        nx = ((xs >= 0) & (xs < wo)).sum(1)
-        cells = float(ny.sum()) * float(nx.sum())      # sum over (py, px) of ny[py] * nx[px]
-        if k != z:   # the first step is a copy of the weight footprint: free
-            total += c_z * cells * co * ci * kh * kw
-        t = nk.inputs[0]
-        wh, ww = (wh - 1) * nk.stride + kh, (ww - 1) * nk.stride + kw
-        sy, oy = sy * nk.stride, oy * nk.stride - nk.pad
-        sx, ox = sx * nk.stride, ox * nk.stride - nk.pad
-        if t == stop:
-            return total
-        if nodes[t].op != "relu":
-            return None
-        k = nodes[t].inputs[0]
+        ny, nx = _clipped_cells(win, nodes[z].shape, nk.shape)
+        per += np.outer(ny, nx) * (co * ci * kh * kw)
+    return per
 
 
 def algorithmic_flops(wl):
@@ -105,7 +145,7 @@ def algorithmic_flops(wl):
     first step of identity rows (a copy of the weight footprint) costs nothing; IBP
     is two passes (centre and radius) of the forward multiply-adds."""
     nodes, B, m = wl.nodes, wl.batch, wl.m
-    total = {"ibp": 0.0, "intermediate": 0.0, "spec": 0.0}
+    total = {"ibp": 0.0, "intermediate": 0.0, "spec": 0.0, "dense_intermediate": 0.0}
     for nd in nodes:
         if nd.op in ("linear", "conv"):
             total["ibp"] += 2 * 2 * _mac_per_row(nd, nodes) * B
@@ -122,16 +162,16 @@ def algorithmic_flops(wl):
             if z <= stop or (zn.op in ("linear", "conv") and _src(nodes, zn.inputs[0]) == stop):
                 continue
             rows = 2 * zn.size * B
-            fp = _footprint_macs(nodes, z, stop)
-            if fp is not None:
-                # rows on footprint windows: count only the cells that exist
-                total["intermediate"] += 2 * 2 * B * fp
-                continue
             free = _identity_consumers(nodes, z)
-            for k in _active(nodes, z, stop):
-                if nodes[k].op not in ("linear", "conv") or k in free:
-                    continue
-                total["intermediate"] += 2 * rows * _mac_per_row(nodes[k], nodes)
+            dense = sum(2 * rows * _mac_per_row(nodes[k], nodes) for k in _active(nodes, z, stop)
+                        if nodes[k].op in ("linear", "conv") and k not in free)
+            total["dense_intermediate"] += dense
+            fp = footprint_row_macs(nodes, z, stop)
+            if fp is not None:
+                # identity rows on footprint windows: count only the cells that exist
+                total["intermediate"] += 2 * 2 * B * zn.shape[0] * float(fp.sum())
+            else:
+                total["intermediate"] += dense
     rows = 2 * m * B
     for k in _active(nodes, L, stop):
         if nodes[k].op in ("linear", "conv"):
@@ -144,25 +184,128 @@ def algorithmic_flops(wl):
                  if nodes[k].op in ("linear", "conv"))
         adj = ev - 2 * rows * _mac_per_row(nodes[L], nodes)
         total["alpha"] = (wl.alpha_steps + 1) * ev + wl.alpha_steps * adj
-    total["all"] = sum(v for k, v in total.items())
+    total["all"] = sum(v for k, v in total.items() if k != "dense_intermediate")
+    total["all_dense"] = total["all"] - total["intermediate"] + total["dense_intermediate"]
     return total
 
 
-def cpu_baseline(wl, flops_total, budget_s=12.0):
-    """The float64 oracle on the host cores over the first k inputs (k grows until
-    about budget_s of CPU work), scaled to TFLOP/s of the same algorithmic work."""
+def _host_cpu():
+    """(threads the process may use, CPU model) of the host."""
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return cores, model
+
+
+def _oracle_rows_sample(wl, budget_s, fl):
+    """Oracle timing for workloads whose single input takes the oracle minutes (CROWN
+    intermediate bounds over conv layers): input 0, its IBP bounds, then rounds of 32
+    seeded neurons of every CROWN-refined layer (both signs, the IBP bounds of the
+    layers below as relaxation bounds) and once the spec rows, until the budget is
+    spent.  The work credited is the algorithmic count of exactly those rows."""
+    import torch
+    from oracle import Oracle, ibp as oracle_ibp
+    from oracle.bounds import backward, _domain
+    nodes = wl.nodes
+    net = Oracle(nodes)
+    stop = wl.region_start if wl.intermediate.startswith("hybrid") else 0
+    t0 = time.perf_counter()
+    lo, hi = oracle_ibp(net, wl.x0[:1], wl.eps)
+    dc, dr = _domain(net, lo, hi, wl.x0, wl.eps, 0, stop)
+    L = len(nodes) - 1
+    C = torch.as_tensor(wl.C[0], dtype=torch.float64)
+    backward(net, lo, hi, 0, L, C, stop, dc, dr)
+    backward(net, lo, hi, 0, L, -C, stop, dc, dr)
+    work = fl["ibp"] / wl.batch + fl["spec"] / wl.batch
+    layers = []
+    for nd in nodes:
+        if nd.op != "relu":
+            continue
+        z = nd.inputs[0]
+        zn = nodes[z]
+        if z <= stop or (zn.op in ("linear", "conv") and _src(nodes, zn.inputs[0]) == stop):
+            continue
+        per = footprint_row_macs(nodes, z, stop)
+        layers.append((z, per))
+    rng = np.random.default_rng(0)
+    rows = 0
+    while time.perf_counter() - t0 < budget_s:
+        for z, per in layers:
+            shape = nodes[z].shape
+            n = nodes[z].size
+            idx = rng.choice(n, 32, replace=False)
+            eye = torch.zeros((32, n), dtype=torch.float64)
+            eye[torch.arange(32), torch.as_tensor(idx)] = 1.0
+            eye = eye.reshape((32,) + tuple(shape))
+            backward(net, lo, hi, 0, z, eye, stop, dc, dr)
+            backward(net, lo, hi, 0, z, -eye, stop, dc, dr)
+            if per is not None:
+                _, hz, wz = shape
+                pix = idx % (hz * wz)
+                work += 2 * 2 * float(per.reshape(-1)[pix].sum())
+            else:
+                free = _identity_consumers(nodes, z)
+                work += 2 * 2 * 32 * sum(_mac_per_row(nodes[k], nodes) for k in _active(nodes, z, stop)
+                                         if nodes[k].op in ("linear", "conv") and k not in free)
+            rows += 64
+    elapsed = time.perf_counter() - t0
+    return work, elapsed, (f"input 0: IBP, the {2 * wl.m} spec rows and {rows} identity rows (32 seeded neurons "
+                           f"x 2 signs per round over {len(layers)} CROWN-refined layers, IBP bounds below)")
+
+
+def cpu_baseline(wl, fl, budget_s=12.0):
+    """The float64 oracle on the host cores, on a bounded sample of the workload (about
+    budget_s of CPU work), scaled to TFLOP/s of the same algorithmic work (the count
+    credited is exactly the sample's).  Whole inputs where one input takes the oracle
+    less than the budget (for alpha-CROWN: its intermediate bounds and the whole
+    alpha loop of that input); otherwise a sample of rows of the first input."""
     import torch
     from oracle import crown_bounds
-    k, elapsed = 0, 0.0
-    while k < wl.batch and elapsed < budget_s:
+    cores, model = _host_cpu()
+    per_input = fl["all"] / wl.batch
+    heavy = wl.intermediate != "ibp" and any(nd.op == "conv" for nd in wl.nodes)
+    if heavy:
+        work, elapsed, sample = _oracle_rows_sample(wl, budget_s, fl)
+        specs_per_s = None
+    else:
+        k, elapsed = 0, 0.0
+        while k < wl.batch and elapsed < budget_s:
+            t0 = time.perf_counter()
+            res = crown_bounds(wl, batch_idx=[k])
+            if wl.alpha_steps:
+                from oracle.alpha import alpha_crown
+                alpha_crown(wl, res["lo"], res["hi"], batch_idx=[k])
+            elapsed += time.perf_counter() - t0
+            k += 1
+        work = per_input * k
+        specs_per_s = k * wl.m / elapsed
+        what = "IBP + CROWN" + (f" + {wl.alpha_steps}-step alpha-CROWN" if wl.alpha_steps else "")
+        sample = f"first {k} of {wl.batch} inputs ({what}), all {wl.m} specs"
+    out = {"value": work / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+           "sample": f"{sample}; float64 torch-CPU oracle (BLAS / oneDNN-backed), {elapsed:.1f} s",
+           "cpu_model": model, "threads": torch.get_num_threads()}
+    if specs_per_s is not None:
+        out["specs_per_s"] = specs_per_s
+    # one single-thread run of the small MLP workload (784-100-100-10, 16 inputs)
+    import workloads as wk
+    w1 = wk.config(1)
+    nt = torch.get_num_threads()
+    torch.set_num_threads(1)
+    try:
         t0 = time.perf_counter()
-        crown_bounds(wl, batch_idx=[k])
-        elapsed += time.perf_counter() - t0
-        k += 1
-    per_input = flops_total / wl.batch
-    return {"value": per_input * k / elapsed / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(),
-            "kind": "oracle", "specs_per_s": k * wl.m / elapsed,
-            "sample": f"first {k} of {wl.batch} inputs, all {wl.m} specs, float64 torch-CPU oracle, {elapsed:.1f} s"}
+        crown_bounds(w1)
+        dt = time.perf_counter() - t0
+    finally:
+        torch.set_num_threads(nt)
+    out["single_thread_mlp784"] = {"specs_per_s": round(w1.batch * w1.m / dt, 1),
+                                   "tflops": algorithmic_flops(w1)["all"] / dt / 1e12, "seconds": round(dt, 3)}
+    return out
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_backsub_traffic_mlp3072.txt")
@@ -222,21 +365,64 @@ def _time_calls(fn, reps, warmup=2):
     return e0.elapsed_time(e1) / reps
 
 
-def hbm_kernels(reps=20):
+PROBE_LIB = os.path.join(ROOT, "linear_bound_propagation_amd", "libvbprobe.so")
+
+
+def probes(reps=10):
+    """Measured ceilings of the GPU at hand (libvbprobe.so, built with the library):
+    an MFMA-only loop (v_mfma_f32_32x32x2f32, four independent accumulator chains per
+    wavefront, 2048 workgroups of 4 wavefronts, no memory traffic) and HBM read, write
+    and copy streams over 4 GiB buffers (16-byte non-temporal accesses)."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(PROBE_LIB)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
+    lib.vbp_mfma_loop.argtypes = [i32, i32, P, P]
+    lib.vbp_read.argtypes = [P, i64, P, P]
+    lib.vbp_write.argtypes = [P, i64, ctypes.c_float, P]
+    lib.vbp_copy.argtypes = [P, P, i64, P]
+    lib.vbp_stream_blocks.restype = i64
+    lib.vbp_stream_blocks.argtypes = [i64]
+    st = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError(f"probe launch failed: {rc}")
+    dev = "cuda:0"
+    blocks, iters = 2048, 50000
+    sink = torch.empty(max(blocks, 1 << 16), device=dev)
+    ms = _time_calls(lambda: ok(lib.vbp_mfma_loop(blocks, iters, ctypes.c_void_p(sink.data_ptr()), st())), 3, 1)
+    mfma = blocks * 4 * iters * 4 * 4096 / (ms * 1e-3) / 1e12
+    n = 1 << 30
+    a = torch.empty(n, device=dev)
+    b = torch.empty(n, device=dev)
+    a.fill_(1.0)
+    rd = _time_calls(lambda: ok(lib.vbp_read(ctypes.c_void_p(a.data_ptr()), n, ctypes.c_void_p(sink.data_ptr()),
+                                            st())), reps)
+    wr = _time_calls(lambda: ok(lib.vbp_write(ctypes.c_void_p(b.data_ptr()), n, 0.5, st())), reps)
+    cp = _time_calls(lambda: ok(lib.vbp_copy(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()), n,
+                                            st())), reps)
+    tc = _time_calls(lambda: b.copy_(a), reps)
+    del a, b
+    torch.cuda.empty_cache()
+    gb = lambda nbytes, t: round(nbytes / (t * 1e-3) / 1e9, 1)
+    return {"mfma_fp32_tflops": round(mfma, 2), "mfma_fp32_frac_of_peak": round(mfma / PEAK_FP32_MFMA_TFLOPS, 4),
+            "hbm_read_GBps": gb(4 * n, rd), "hbm_write_GBps": gb(4 * n, wr), "hbm_copy_GBps": gb(8 * n, cp),
+            "torch_copy_GBps": gb(8 * n, tc), "peak_fp32_mfma_tflops": PEAK_FP32_MFMA_TFLOPS,
+            "peak_hbm_GBps": PEAK_HBM_GBPS, "stream_bytes": 4 * n}
+
+
+def hbm_kernels(stream_ceiling, reps=20):
     """The memory-bound kernels, timed live: IBP over the wide one-hidden-layer network
-    (weights read once per call), a standalone concretisation of an intermediate-layer
-    Lambda of the MLP workload, and a plain device copy for scale."""
+    (weights read once per call) and a standalone concretisation of an intermediate-layer
+    Lambda of the MLP workload; each against 8 TB/s and against the measured read
+    stream (both kernels read far more than they write)."""
     import torch
     import workloads as wk
     import linear_bound_propagation_amd as lbp
     out = []
     dev = "cuda:0"
-    # plain copy of 1 GiB: read + write
-    a = torch.empty(1 << 28, device=dev)
-    b = torch.empty_like(a)
-    ms = _time_calls(lambda: b.copy_(a), reps)
-    copy_gbps = 2 * a.numel() * 4 / (ms * 1e-3) / 1e9
-    del a, b
+    copy_gbps = stream_ceiling
     # IBP over the 4096-262144-100 network, batch 8
     print("[bench] hbm: building the wide network", file=sys.stderr, flush=True)
     wl = wk.wide()
@@ -252,7 +438,7 @@ def hbm_kernels(reps=20):
     out.append({"kernel": "ibp_narrow_kernel (+ split-K finish): vb_ibp over every node", "workload": wl.name,
                 "bound": "hbm", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                "frac_of_copy": round(nbytes / (ms * 1e-3) / 1e9 / copy_gbps, 4),
+                "frac_of_read_stream": round(nbytes / (ms * 1e-3) / 1e9 / copy_gbps, 4),
                 "bytes_per_call": nbytes, "ms_per_call": round(ms, 4)})
     del net, x, lo, hi, ws, wl
     torch.cuda.empty_cache()
@@ -269,42 +455,17 @@ def hbm_kernels(reps=20):
     out.append({"kernel": "concretize_rows_kernel: vb_concretize", "workload": f"Lambda {B}x{R}x{n} fp32, ball",
                 "bound": "hbm", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                "frac_of_copy": round(nbytes / (ms * 1e-3) / 1e9 / copy_gbps, 4),
+                "frac_of_read_stream": round(nbytes / (ms * 1e-3) / 1e9 / copy_gbps, 4),
                 "bytes_per_call": nbytes, "ms_per_call": round(ms, 4)})
-    return out, round(copy_gbps, 1)
+    return out
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-hbm", action="store_true", help="skip the memory-bound kernel measurements")
-    ap.add_argument("--dense-alpha", action="store_true",
-                    help="alpha-CROWN workloads: keep alpha for every neuron instead of the unstable ones only")
-    ap.add_argument("--intermediate", default=None,
-                    help="override the workload's intermediate-bound method (ibp, crown, hybrid, crown+ibp, ...)")
-    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
-                    help="only run a plain device copy of BYTES (counter calibration)")
-    args = ap.parse_args()
-    if args.copy_probe:
-        copy_probe(args.copy_probe)
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the bound computation is not "
-              "sharded across GPUs in this build", file=sys.stderr)
-        sys.exit(2)
-
+def run_workload(wl, steps, warmup, dense_alpha=False, profile=True):
+    """Time `steps` whole bound computations of a workload (after `warmup`), inputs
+    resident in HBM.  Returns (ms per step, GEMM profile (ms, flops, launches), last
+    outputs, workspace bytes, alpha info)."""
     import torch
-    import workloads as wk
     import linear_bound_propagation_amd as lbp
-
-    wl = wk.config(args.workload)
-    if args.intermediate:
-        wl.intermediate = args.intermediate
-        wl.name += "_" + args.intermediate.replace("+", "_")
     print(f"[bench] workload {wl.name}: building device copies", file=sys.stderr, flush=True)
     net, x, C = lbp.prepare(wl, "cuda:0")
     lo, hi = net.alloc_bounds(wl.batch)
@@ -324,7 +485,7 @@ def main():
             lbp.crown(net, x, float(wl.eps), C, wl.intermediate, wl.region_start, ws=ws, out=out)
             # compact alpha: the state of the unstable neurons only (the layout call
             # synchronises the stream to size it; it is part of the timed step)
-            lay = None if args.dense_alpha else lbp.alpha_layout(net, out["lo"], out["hi"])
+            lay = None if dense_alpha else lbp.alpha_layout(net, out["lo"], out["hi"])
             key = None if lay is None else tuple(lay.width)
             if key not in states:
                 states[key] = lbp.alpha_state(net, wl.batch, wl.m, lay)
@@ -339,29 +500,84 @@ def main():
         def step():
             lbp.crown(net, x, float(wl.eps), C, wl.intermediate, wl.region_start, ws=ws, out=out)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    print(f"[bench] warmup done ({warmup} steps)", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
-    lbp.profile_start()
-    for _ in range(args.steps):
+    if profile:
+        lbp.profile_start()
+    for _ in range(steps):
         step()
     e1.record(stream)
     torch.cuda.synchronize()
-    k_ms, k_flops, k_launches = lbp.profile_stop()
-    ms = e0.elapsed_time(e1) / args.steps
-    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    prof = lbp.profile_stop() if profile else (0.0, 0.0, 0)
+    ms = e0.elapsed_time(e1) / steps
+    print(f"[bench] timed {steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    res = {"lb": out["lb"].clone(), "ub": out["ub"].clone()}
+    nbytes = ws.numel()
+    del ws, out, net, x, C
+    torch.cuda.empty_cache()
+    return ms, prof, res, nbytes, alpha_info
 
+
+def gemm_roofline(prof, name):
+    k_ms, k_flops, k_launches = prof
+    achieved = k_flops / (k_ms * 1e-3) / 1e12 if k_ms > 0 else None
+    return {
+        "kernel": "gemm_kernel: back-substitution GEMM (relaxation / concretisation / store epilogues)",
+        "bound": "mfma",
+        "achieved": None if achieved is None else round(achieved, 3),
+        "peak": PEAK_FP32_MFMA_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": None if achieved is None else round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
+        "traffic": measured_traffic(name),
+        "launches": k_launches,
+        "avg_launch_ms": round(k_ms / max(k_launches, 1), 4),
+        "alg_flop_per_launch": k_flops / max(k_launches, 1),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=5,
+                    help="1-5: the measured configurations (default 5: the residual network, the largest)")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-hbm", action="store_true", help="skip the probes and the memory-bound kernels")
+    ap.add_argument("--no-extra", action="store_true", help="skip the short runs of the other workloads")
+    ap.add_argument("--dense-alpha", action="store_true",
+                    help="alpha-CROWN workloads: keep alpha for every neuron instead of the unstable ones only")
+    ap.add_argument("--intermediate", default=None,
+                    help="override the workload's intermediate-bound method (ibp, crown, hybrid, crown+ibp, ...)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
+    args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the bound computation is not "
+              "sharded across GPUs in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import workloads as wk
+
+    wl = wk.config(args.workload)
+    if args.intermediate:
+        wl.intermediate = args.intermediate
+        wl.name += "_" + args.intermediate.replace("+", "_")
+    ms, prof, res, ws_bytes, alpha_info = run_workload(wl, args.steps, args.warmup, args.dense_alpha)
     fl = algorithmic_flops(wl)
     tflops = fl["all"] / (ms * 1e-3) / 1e12
-    lb = out["lb"]
+    lb = res["lb"]
     verified = float((lb > 0).all(dim=1).float().mean().item())
-    achieved = k_flops / (k_ms * 1e-3) / 1e12 if k_ms > 0 else None
     line = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -378,32 +594,38 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "specs": wl.m, "eps": float(wl.eps),
                    "intermediate": wl.intermediate, "alpha_steps": wl.alpha_steps,
                    "algorithmic_tflop_per_step": round(fl["all"] / 1e12, 4),
-                   "workspace_gb": round(ws.numel() / 1e9, 2), **alpha_info},
+                   "dense_tflop_per_step": round(fl["all_dense"] / 1e12, 4),
+                   "workspace_gb": round(ws_bytes / 1e9, 2), **alpha_info},
         "frac_of_fp32_mfma_peak": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4),
+        "dense_equivalent_tflops": round(fl["all_dense"] / (ms * 1e-3) / 1e12, 3),
         "specs_per_s": round(wl.batch * wl.m / (ms * 1e-3), 1),
         "verified_frac": verified,
-        "roofline": {
-            "kernel": "gemm_kernel: back-substitution GEMM (relaxation / concretisation epilogues)",
-            "bound": "mfma",
-            "achieved": None if achieved is None else round(achieved, 3),
-            "peak": PEAK_FP32_MFMA_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": None if achieved is None else round(achieved / PEAK_FP32_MFMA_TFLOPS, 4),
-            "traffic": measured_traffic(wl.name),
-            "launches": k_launches,
-            "avg_launch_ms": round(k_ms / max(k_launches, 1), 4),
-            "alg_flop_per_launch": k_flops / max(k_launches, 1),
-        },
+        "roofline": gemm_roofline(prof, wl.name),
         "cpu_baseline": None,
     }
+    if not args.no_extra:
+        extra = {}
+        for cfg in (1, 2, 3, 4, 5):
+            if cfg == args.workload:
+                continue
+            w = wk.config(cfg)
+            e_ms, e_prof, e_res, _, e_alpha = run_workload(w, 5 if cfg != 5 else 2, 2)
+            e_fl = algorithmic_flops(w)
+            extra[w.name] = {"ms_per_step": round(e_ms, 4),
+                             "tflops": round(e_fl["all"] / (e_ms * 1e-3) / 1e12, 3),
+                             "algorithmic_tflop_per_step": round(e_fl["all"] / 1e12, 4),
+                             "specs_per_s": round(w.batch * w.m / (e_ms * 1e-3), 1),
+                             "verified_frac": float((e_res["lb"] > 0).all(dim=1).float().mean().item()),
+                             "gemm": {k: v for k, v in gemm_roofline(e_prof, w.name).items()
+                                      if k in ("achieved", "frac", "launches", "avg_launch_ms")}, **e_alpha}
+        line["other_workloads"] = extra
     if not args.no_hbm:
-        print("[bench] timing the memory-bound kernels", file=sys.stderr, flush=True)
-        del ws
-        torch.cuda.empty_cache()
-        line["hbm_kernels"], line["copy_GBps"] = hbm_kernels()
+        print("[bench] probes and memory-bound kernels", file=sys.stderr, flush=True)
+        line["probes"] = probes()
+        line["hbm_kernels"] = hbm_kernels(line["probes"]["hbm_read_GBps"])
     if not args.no_cpu:
         print("[bench] timing the float64 oracle on the host cores", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(wl, fl["all"])
+        line["cpu_baseline"] = cpu_baseline(wl, fl)
     print(json.dumps(line), flush=True)
 
 
