@@ -11,7 +11,9 @@
  * Conventions shared by every call
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
  *    keeps no pointer after a call returns and allocates no device memory:
- *    scratch space comes from the caller's workspace (`ws`, `ws_bytes`).
+ *    scratch space comes from the caller's workspace (`ws`, `ws_bytes`), or,
+ *    for vb_crown_noalloc, from a fixed scratch array in the library's code
+ *    object.
  *  - Every call validates its arguments on the host first.  On an error
  *    nothing is enqueued and a negative status is returned; vb_last_error()
  *    then describes it.  Otherwise the work is enqueued on `stream` (a
@@ -93,8 +95,12 @@ vb_status vb_workspace_size(const vb_graph* g, int32_t batch, int32_t m, int32_t
  * interval bounds [batch][size_k].  Affine nodes compute c' = W c + b and
  * r' = |W| r from (c, r) = ((l+u)/2, (u-l)/2) of their producer (the input
  * node hands over (x_center, radius) directly); ReLU clamps at 0; ADD sums;
- * GAP averages.  Every node that feeds another node must have bounds storage
- * (node_lo[k] and node_hi[k] non-NULL) except the input node.
+ * GAP averages.  A node whose bounds another node reads (the source of an
+ * affine node through flatten nodes, the input of a ReLU / ADD / GAP / FLATTEN,
+ * the input of the last node when C is given) must have bounds storage
+ * (node_lo[k] and node_hi[k] both non-NULL); a node nothing reads may have
+ * none and is then skipped.  All of this is checked before anything is
+ * enqueued.
  * If C != NULL (C: [batch][m][n_out] over the last node, which must be
  * LINEAR), also writes spec bounds spec_lo/spec_hi [batch][m] with C folded
  * into the last layer.  The workspace is optional without C: when it holds
@@ -226,6 +232,26 @@ vb_status vb_crown(const vb_graph* g, int32_t batch,
                    const float* C, int32_t m,
                    float* ibp_lb, float* ibp_ub, float* lb, float* ub,
                    void* ws, size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): vb_crown with
+ * the library's own fixed device scratch in place of a caller workspace.  The
+ * scratch is VB_NOALLOC_SCRATCH_BYTES (256 MiB) per GPU, held by every GPU the
+ * library runs on until the process ends; it is found on the first call on a
+ * device (make that first call outside any graph capture).  Nothing is
+ * allocated.  A graph needing more than the scratch for one batch element is
+ * rejected with VB_ENOMEM before anything is enqueued; a larger batch is
+ * processed in chunks that fit (same results).  Every call on one GPU uses the
+ * same scratch: calls that overlap on one GPU (different streams, or threads)
+ * race and must be serialised by the caller.  The scratch keeps the last
+ * call's contents; nothing in it is assumed to start at zero. */
+#define VB_NOALLOC_SCRATCH_BYTES (256u << 20)
+vb_status vb_crown_noalloc(const vb_graph* g, int32_t batch,
+                           const float* x_center, const float* x_radius, float eps,
+                           int32_t method, int32_t region_start,
+                           float* const* node_lo, float* const* node_hi,
+                           const float* C, int32_t m,
+                           float* ibp_lb, float* ibp_ub, float* lb, float* ub, void* stream);
 
 /* Measurement of the back-substitution GEMM (the dominant kernel).
  * vb_profile_start() begins recording a pair of HIP events around every

@@ -30,7 +30,8 @@ _OPS = {"input": VB_INPUT, "linear": VB_LINEAR, "conv": VB_CONV2D, "relu": VB_RE
         "gap": VB_GAP, "flatten": VB_FLATTEN}
 
 EXPORTS = ["vb_last_error", "vb_workspace_size", "vb_ibp", "vb_crown_backward", "vb_concretize",
-           "vb_alpha_layout", "vb_alpha_init", "vb_alpha_step", "vb_crown", "vb_profile_start", "vb_profile_stop"]
+           "vb_alpha_layout", "vb_alpha_init", "vb_alpha_step", "vb_crown", "vb_crown_noalloc", "vb_profile_start",
+           "vb_profile_stop"]
 # host-only helpers declared in include/vb_testing.h (used by the CPU tests)
 TESTING_EXPORTS = ["vb_testing_fastdiv", "vb_testing_conv_tile_n"]
 
@@ -78,6 +79,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                   P, P, P, sz, P]
     lib.vb_crown.restype = i32
     lib.vb_crown.argtypes = [G, i32, P, P, f32, i32, i32, PP, PP, P, i32, P, P, P, P, P, sz, P]
+    lib.vb_crown_noalloc.restype = i32
+    lib.vb_crown_noalloc.argtypes = [G, i32, P, P, f32, i32, i32, PP, PP, P, i32, P, P, P, P, P]
     lib.vb_profile_start.restype = i32
     lib.vb_profile_start.argtypes = []
     lib.vb_profile_stop.restype = i32
@@ -305,6 +308,25 @@ def crown(net: DeviceNet, x_center: torch.Tensor, eps: float, C: torch.Tensor, m
                          region_start or 0, _ptr_array(out["lo"]), _ptr_array(out["hi"]), _ptr(C), m,
                          _ptr(out["ibp_lb"]), _ptr(out["ibp_ub"]), _ptr(out["lb"]), _ptr(out["ub"]), _ptr(ws),
                          ws.numel(), _stream()), "vb_crown")
+    return out
+
+
+def crown_noalloc(net: DeviceNet, x_center: torch.Tensor, eps: float, C: torch.Tensor, method: str = "crown",
+                  region_start: Optional[int] = None, out=None, x_radius=None):
+    """vb_crown on the library's fixed device scratch (vb_crown_noalloc): no workspace
+    argument and no device allocation inside the call (the caller's outputs excepted:
+    pass `out` to allocate nothing at all)."""
+    batch = x_center.shape[0]
+    m = C.shape[1]
+    if out is None:
+        lo, hi = net.alloc_bounds(batch)
+        out = {"lo": lo, "hi": hi}
+        for k in ("ibp_lb", "ibp_ub", "lb", "ub"):
+            out[k] = torch.empty(batch, m, device=net.device)
+    _check(lib().vb_crown_noalloc(net.gp, batch, _ptr(x_center), _ptr(x_radius), float(eps), METHODS[method],
+                                  region_start or 0, _ptr_array(out["lo"]), _ptr_array(out["hi"]), _ptr(C), m,
+                                  _ptr(out["ibp_lb"]), _ptr(out["ibp_ub"]), _ptr(out["lb"]), _ptr(out["ub"]),
+                                  _stream()), "vb_crown_noalloc")
     return out
 
 

@@ -20,7 +20,7 @@ OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libvbprop.so")
 PROBE_LIB = os.path.join(HERE, "libvbprobe.so")
 
-SOURCES = ["vb_gemm.hip", "vb_ibp_narrow.hip", "vb_kernels.hip", "vb_api.cpp"]
+SOURCES = ["vb_gemm.hip", "vb_ibp_narrow.hip", "vb_kernels.hip", "vb_scratch.hip", "vb_api.cpp"]
 PROBE_SOURCES = ["vb_probe.hip"]
 
 HIPCC_FLAGS = [

@@ -1803,6 +1803,21 @@ extern "C" vb_status vb_crown(const vb_graph* g, int32_t batch, const float* x_c
   return VB_OK;
 }
 
+extern "C" vb_status vb_crown_noalloc(const vb_graph* g, int32_t batch, const float* x_center,
+                                      const float* x_radius, float eps, int32_t method, int32_t region_start,
+                                      float* const* node_lo, float* const* node_hi, const float* C, int32_t m,
+                                      float* ibp_lb, float* ibp_ub, float* lb, float* ub, void* stream) {
+  void* ws = nullptr;
+  const hipError_t e = noalloc_scratch((hipStream_t)stream, &ws);
+  if (e != hipSuccess) return fail(VB_EDEVICE, "vb_crown_noalloc: scratch address: %s", hipGetErrorString(e));
+  const vb_status s = vb_crown(g, batch, x_center, x_radius, eps, method, region_start, node_lo, node_hi, C, m,
+                               ibp_lb, ibp_ub, lb, ub, ws, NOALLOC_SCRATCH_BYTES, stream);
+  if (s == VB_ENOMEM)
+    return fail(VB_ENOMEM, "vb_crown_noalloc: one batch element needs more than the fixed scratch of %zu bytes (%s)",
+                NOALLOC_SCRATCH_BYTES, g_err.c_str());
+  return s;
+}
+
 extern "C" vb_status vb_profile_start(void) {
   for (auto& r : g_prof) {
     (void)hipEventDestroy(r.a);

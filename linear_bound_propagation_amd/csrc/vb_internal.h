@@ -408,4 +408,10 @@ bool ibp_narrow_fits(int batch, int K, const float* W, const float* A, const flo
 int ibp_narrow_slices(int N, int K);
 hipError_t launch_ibp_narrow(NarrowIbp d, int S, hipStream_t st);
 
+// Fixed scratch of the allocation-free entry point (vb_scratch.hip): its size, and
+// its address on the device of stream `st` (the null stream: the current device),
+// looked up on the first call per device and cached.
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(256) << 20;
+hipError_t noalloc_scratch(hipStream_t st, void** ptr);
+
 }  // namespace vb
