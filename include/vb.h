@@ -79,6 +79,9 @@ typedef struct {
 #define VB_INTERSECT_IBP 16  /* flag for CROWN / HYBRID: each CROWN intermediate  */
                              /* bound is intersected with the node's IBP bound    */
                              /* (l = max, u = min) before later layers use it     */
+#define VB_ALPHA_ROWS    32  /* flag for vb_workspace_size: also enough for       */
+                             /* vb_alpha_step_rows on the identity rows of every  */
+                             /* ReLU input (alpha-CROWN intermediate bounds)      */
 
 /* Thread-local description of the last error on this thread. */
 const char* vb_last_error(void);
@@ -187,7 +190,8 @@ vb_status vb_concretize(int32_t rows, int32_t n, int32_t rows_per_batch,
  * adaptive CROWN lower slope of each neuron from the bounds of the ReLU's
  * input (1 if u >= -l else 0 for unstable neurons; 1 active; 0 inactive),
  * identical for the m spec rows of an input, and adam_m[k], adam_v[k] are
- * zeroed.  Entries for non-ReLU nodes are ignored (may be NULL).  compact:
+ * zeroed.  Entries for non-ReLU nodes are ignored (may be NULL), and so are
+ * ReLU nodes whose alpha[k] is NULL (state that covers only some layers).  compact:
  * NULL (state [batch][m][size_k]), or the compact layout (vb_alpha_compact;
  * only the unstable neurons' columns are written). */
 vb_status vb_alpha_init(const vb_graph* g, int32_t batch, int32_t m,
@@ -220,6 +224,35 @@ vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float* C, int32_
                         float* lb_out, float* best_lb,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* alpha-CROWN step on rows over any Linear / Conv node `start` of a chain
+ * network (the per-neuron alpha tensors of Sec. 3 and Sec. 4.3 of the page, on
+ * intermediate layers as well as on the specification).  Rows:
+ *   C != NULL: spec rows C [batch][m][size_start], lower bounds only, as in
+ *              vb_alpha_step (which is this call with start = the last node);
+ *              lb_out, best_lb [batch][m]; ub_out and best_ub must be NULL;
+ *   C == NULL: the identity rows of `start`, +e_j (lower bound l_j) and -e_j
+ *              (upper bound u_j) for every neuron j, R = 2 * size_start rows per
+ *              input, each with its own slopes: alpha, adam_m, adam_v of every
+ *              ReLU node below `start` are [batch][R][size_k] (compact:
+ *              [batch][R][width_k]), rows 0..size-1 for +e_j then -e_j.
+ *              lb_out / ub_out receive this evaluation's l and u [batch][size],
+ *              best_lb / best_ub the best over the steps (step 1 sets them; later
+ *              steps take the max of l and the min of u).  Any of the four may
+ *              be NULL (not all).
+ * Every row climbs its own bound: the objective is the sum of the rows' lower
+ * bounds, whose gradient with respect to a row's slopes is that row's own.
+ * The state of ReLU nodes at or above `start` is not used (may be NULL).  The
+ * workspace must hold the whole batch (vb_workspace_size with VB_ALPHA_ROWS
+ * covers the identity rows of every layer).  Other conventions as vb_alpha_step. */
+vb_status vb_alpha_step_rows(const vb_graph* g, int32_t batch, int32_t start, const float* C, int32_t m,
+                             const float* const* node_lo, const float* const* node_hi,
+                             const float* x_center, const float* x_radius, float eps,
+                             const vb_alpha_compact* compact,
+                             float* const* alpha, float* const* adam_m, float* const* adam_v,
+                             int32_t step, float lr, float beta1, float beta2, float adam_eps,
+                             float* lb_out, float* best_lb, float* ub_out, float* best_ub,
+                             void* ws, size_t ws_bytes, void* stream);
+
 /* The whole bound computation for one batch: IBP for every node, then the
  * intermediate bounds of every ReLU input by `method`, overwriting node_lo /
  * node_hi of those nodes in topological order, then the spec bounds of C by
@@ -232,6 +265,16 @@ vb_status vb_crown(const vb_graph* g, int32_t batch,
                    const float* C, int32_t m,
                    float* ibp_lb, float* ibp_ub, float* lb, float* ub,
                    void* ws, size_t ws_bytes, void* stream);
+
+/* The verdict (Sec. 1 of the page: the property must hold for every input of
+ * the domain).  Spec rows are margins e_label - e_j, so the property of input
+ * b is proved when every spec lower bound is positive: verified[b] = 1 if
+ * lb[b][i] > 0 for all i < m (a NaN bound does not count), else 0.
+ * lb: [batch][m] (device, e.g. the lb of vb_crown or the best_lb of the
+ * alpha-CROWN steps); verified: [batch] int32 (device); n_verified: one int32
+ * (device) receiving the number of verified inputs, or NULL. */
+vb_status vb_verify(int32_t batch, int32_t m, const float* lb, int32_t* verified, int32_t* n_verified,
+                    void* stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): vb_crown with

@@ -9,6 +9,8 @@
 
 #include <stdint.h>
 
+#include "vb.h"
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -27,6 +29,13 @@ int32_t vb_testing_fastdiv(int32_t d, const int32_t* x, int64_t n, int32_t* q, u
  * product over `rows` rows with the alpha-CROWN adjoint epilogue (N = c_out).
  * Returns the tile width (32, 64, 128 or 256), or -1 for bad arguments. */
 int32_t vb_testing_conv_tile_n(int32_t mode, int32_t rows, int32_t h, int32_t w, int32_t c_in, int32_t c_out);
+
+/* Which back-substitution the library uses for the identity rows over node
+ * `start` down to the domain node `stop` (intermediate bounds): 0 dense rows
+ * over every node, 1 footprint windows along a conv -> ReLU -> conv chain, 2
+ * footprint windows through a region with residual additions.  -1 for a bad
+ * graph or node indices. */
+int32_t vb_testing_identity_path(const vb_graph* g, int32_t start, int32_t stop);
 
 #ifdef __cplusplus
 }

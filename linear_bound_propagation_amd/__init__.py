@@ -24,16 +24,17 @@ LIB_PATH = os.path.join(_HERE, "libvbprop.so")
 
 VB_INPUT, VB_LINEAR, VB_CONV2D, VB_RELU, VB_ADD, VB_GAP, VB_FLATTEN = range(7)
 METHODS = {"ibp": 0, "crown": 1, "hybrid": 2, "crown+ibp": 1 | 16, "hybrid+ibp": 2 | 16}
+VB_ALPHA_ROWS = 32
 STATUS = {0: "VB_OK", -1: "VB_EINVAL", -2: "VB_ESHAPE", -3: "VB_ENOMEM", -4: "VB_EDEVICE",
           -5: "VB_EUNSUPPORTED"}
 _OPS = {"input": VB_INPUT, "linear": VB_LINEAR, "conv": VB_CONV2D, "relu": VB_RELU, "add": VB_ADD,
         "gap": VB_GAP, "flatten": VB_FLATTEN}
 
 EXPORTS = ["vb_last_error", "vb_workspace_size", "vb_ibp", "vb_crown_backward", "vb_concretize",
-           "vb_alpha_layout", "vb_alpha_init", "vb_alpha_step", "vb_crown", "vb_crown_noalloc", "vb_profile_start",
-           "vb_profile_stop"]
+           "vb_alpha_layout", "vb_alpha_init", "vb_alpha_step", "vb_alpha_step_rows", "vb_crown", "vb_crown_noalloc", "vb_verify",
+           "vb_profile_start", "vb_profile_stop"]
 # host-only helpers declared in include/vb_testing.h (used by the CPU tests)
-TESTING_EXPORTS = ["vb_testing_fastdiv", "vb_testing_conv_tile_n"]
+TESTING_EXPORTS = ["vb_testing_fastdiv", "vb_testing_conv_tile_n", "vb_testing_identity_path"]
 
 
 class vb_node(ctypes.Structure):
@@ -77,8 +78,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vb_alpha_step.restype = i32
     lib.vb_alpha_step.argtypes = [G, i32, P, i32, PP, PP, P, P, f32, AC, PP, PP, PP, i32, f32, f32, f32, f32,
                                   P, P, P, sz, P]
+    lib.vb_alpha_step_rows.restype = i32
+    lib.vb_alpha_step_rows.argtypes = [G, i32, i32, P, i32, PP, PP, P, P, f32, AC, PP, PP, PP, i32, f32, f32, f32, f32,
+                                       P, P, P, P, P, sz, P]
     lib.vb_crown.restype = i32
     lib.vb_crown.argtypes = [G, i32, P, P, f32, i32, i32, PP, PP, P, i32, P, P, P, P, P, sz, P]
+    lib.vb_verify.restype = i32
+    lib.vb_verify.argtypes = [i32, i32, P, P, P, P]
     lib.vb_crown_noalloc.restype = i32
     lib.vb_crown_noalloc.argtypes = [G, i32, P, P, f32, i32, i32, PP, PP, P, i32, P, P, P, P, P]
     lib.vb_profile_start.restype = i32
@@ -197,9 +203,11 @@ class DeviceNet:
         hi = [None] + [torch.empty(batch, s, device=self.device) for s in self.sizes[1:]]
         return lo, hi
 
-    def workspace_size(self, batch: int, m: int, method: str = "crown", region_start: int = 0) -> int:
+    def workspace_size(self, batch: int, m: int, method: str = "crown", region_start: int = 0,
+                       alpha_rows: bool = False) -> int:
         out = ctypes.c_size_t(0)
-        _check(lib().vb_workspace_size(self.gp, batch, m, METHODS[method], region_start or 0, ctypes.byref(out)),
+        flags = METHODS[method] | (VB_ALPHA_ROWS if alpha_rows else 0)
+        _check(lib().vb_workspace_size(self.gp, batch, m, flags, region_start or 0, ctypes.byref(out)),
                "vb_workspace_size")
         return int(out.value)
 
@@ -330,6 +338,18 @@ def crown_noalloc(net: DeviceNet, x_center: torch.Tensor, eps: float, C: torch.T
     return out
 
 
+def verify(lb: torch.Tensor, verified: torch.Tensor = None, count: torch.Tensor = None):
+    """vb_verify: per input, 1 if every spec lower bound is positive (the property is
+    proved for the whole domain), and the number of verified inputs (device int32)."""
+    batch, m = lb.shape
+    if verified is None:
+        verified = torch.empty(batch, dtype=torch.int32, device=lb.device)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=lb.device)
+    _check(lib().vb_verify(batch, m, _ptr(lb), _ptr(verified), _ptr(count), _stream()), "vb_verify")
+    return verified, count
+
+
 def alpha_state(net: DeviceNet, batch: int, m: int, layout: Optional[AlphaLayout] = None):
     """Device tensors alpha, adam_m, adam_v per node ([batch][m][size] for ReLU nodes, or
     [batch][m][width] in a compact layout (None for width 0); None elsewhere)."""
@@ -359,6 +379,67 @@ def alpha_step(net: DeviceNet, C: torch.Tensor, lo, hi, x_center: torch.Tensor, 
                               step, lr, beta1, beta2, adam_eps, _ptr(lb_out), _ptr(best_lb), _ptr(ws), ws.numel(),
                               _stream()), "vb_alpha_step")
     return lb_out
+
+
+def alpha_step_rows(net: DeviceNet, start: int, C: Optional[torch.Tensor], lo, hi, x_center: torch.Tensor,
+                    eps: float, alpha, adam_m, adam_v, step: int, lr: float, ws: torch.Tensor, lb_out=None,
+                    best_lb=None, ub_out=None, best_ub=None, beta1: float = 0.9, beta2: float = 0.999,
+                    adam_eps: float = 1e-8, x_radius=None, layout: Optional[AlphaLayout] = None):
+    """vb_alpha_step_rows: one alpha-CROWN step on spec rows C over node `start`, or
+    (C None) on the identity rows of `start` (l and u of every neuron)."""
+    batch = x_center.shape[0]
+    m = 0 if C is None else C.shape[1]
+    _check(lib().vb_alpha_step_rows(net.gp, batch, start, _ptr(C), m, _ptr_array(lo), _ptr_array(hi),
+                                    _ptr(x_center), _ptr(x_radius), float(eps), _compact(layout),
+                                    _ptr_array(alpha), _ptr_array(adam_m), _ptr_array(adam_v), step, lr, beta1, beta2,
+                                    adam_eps, _ptr(lb_out), _ptr(best_lb), _ptr(ub_out), _ptr(best_ub), _ptr(ws),
+                                    ws.numel(), _stream()), "vb_alpha_step_rows")
+
+
+def relu_inputs_refined(net: DeviceNet):
+    """ReLU inputs whose bounds CROWN refines (more than one affine step from the input), in order."""
+    out = []
+    for k, op in enumerate(net.ops):
+        if op != "relu":
+            continue
+        z = net.inputs[k][0]
+        src = net.inputs[z][0] if net.ops[z] in ("linear", "conv") else None
+        while src is not None and net.ops[src] == "flatten":
+            src = net.inputs[src][0]
+        if src == 0:
+            continue
+        out.append(z)
+    return out
+
+
+def alpha_intermediate(net: DeviceNet, x_center: torch.Tensor, eps: float, lo, hi, steps: int, lr: float,
+                       ws: torch.Tensor, x_radius=None, trace: Optional[dict] = None):
+    """alpha-CROWN intermediate bounds: for every refined ReLU input z in order, the
+    identity rows of z are optimised (vb_alpha_init, `steps` calls of
+    vb_alpha_step_rows with the Adam update, one evaluation), and the best l and u
+    over the iterates are written into lo[z], hi[z] (which the later layers then
+    relax with).  lo / hi must hold bounds of every node (e.g. from vb_ibp).
+    With `trace` (a dict), trace[z] receives the l and u of every evaluation
+    ([steps+1][batch][size] each)."""
+    batch = x_center.shape[0]
+    for z in relu_inputs_refined(net):
+        n = net.sizes[z]
+        R = 2 * n
+        below = [k for k, op in enumerate(net.ops) if op == "relu" and k < z]
+        mk = lambda: [torch.empty(batch, R, net.sizes[k], device=net.device) if k in below else None
+                      for k in range(net.n_nodes)]
+        alpha, am, av = mk(), mk(), mk()
+        alpha_init(net, lo, hi, alpha, am, av, R)
+        ls = torch.empty(steps + 1, batch, n, device=net.device)
+        us = torch.empty(steps + 1, batch, n, device=net.device)
+        for t in range(1, steps + 1):
+            alpha_step_rows(net, z, None, lo, hi, x_center, eps, alpha, am, av, t, lr, ws, lb_out=ls[t - 1],
+                            best_lb=lo[z], ub_out=us[t - 1], best_ub=hi[z], x_radius=x_radius)
+        alpha_step_rows(net, z, None, lo, hi, x_center, eps, alpha, am, av, 0, lr, ws, lb_out=ls[steps],
+                        best_lb=lo[z], ub_out=us[steps], best_ub=hi[z], x_radius=x_radius)
+        if trace is not None:
+            trace[z] = (ls, us)
+    return lo, hi
 
 
 def alpha_crown(net: DeviceNet, x_center: torch.Tensor, eps: float, C: torch.Tensor, lo, hi, steps: int,

@@ -382,6 +382,62 @@ vb_status run_gemm_reduce(Backward& B, GemmDesc& d, int rows, int P, bool reduce
   return VB_OK;
 }
 
+// Window of footprint rows over a node's output: cell (Y, X) of the row of start
+// pixel (py, px) is pixel (py*sy + oy + Y, px*sx + ox + X).
+struct Win {
+  int wh = 0, ww = 0, sy = 1, oy = 0, sx = 1, ox = 0;
+  bool set = false;
+};
+
+// The window a conv's output window reaches on the conv's input.
+Win conv_reach(const NodeInfo& nd, const Win& w) {
+  Win r;
+  r.wh = (w.wh - 1) * nd.stride + nd.kh;
+  r.ww = (w.ww - 1) * nd.stride + nd.kw;
+  r.sy = w.sy * nd.stride;
+  r.oy = w.oy * nd.stride - nd.pad;
+  r.sx = w.sx * nd.stride;
+  r.ox = w.ox * nd.stride - nd.pad;
+  r.set = true;
+  return r;
+}
+
+// Bounding box of two windows of one scale; false if the scales differ.
+bool win_union(Win& a, const Win& b) {
+  if (!a.set) {
+    a = b;
+    return true;
+  }
+  if (a.sy != b.sy || a.sx != b.sx) return false;
+  const int y0 = std::min(a.oy, b.oy), y1 = std::max(a.oy + a.wh, b.oy + b.wh);
+  const int x0 = std::min(a.ox, b.ox), x1 = std::max(a.ox + a.ww, b.ox + b.ww);
+  a.oy = y0;
+  a.wh = y1 - y0;
+  a.ox = x0;
+  a.ww = x1 - x0;
+  return true;
+}
+
+bool same_win(const Win& a, const Win& b) {
+  return a.wh == b.wh && a.ww == b.ww && a.sy == b.sy && a.oy == b.oy && a.sx == b.sx && a.ox == b.ox;
+}
+
+// Algorithmic multiply-adds of one conv step of window rows: for every row, the
+// cells of its window over the conv's output that lie inside the image, times
+// the conv's multiply-adds per output cell.
+double window_macs(const NodeInfo& S, const NodeInfo& nd, const Win& w, long long rows_per_pixel) {
+  double sy = 0.0, sx = 0.0;
+  for (int py = 0; py < S.h; ++py) {
+    const int a = py * w.sy + w.oy, b = a + w.wh;
+    sy += std::max(0, std::min(b, nd.h) - std::max(a, 0));
+  }
+  for (int px = 0; px < S.w; ++px) {
+    const int a = px * w.sx + w.ox, b = a + w.ww;
+    sx += std::max(0, std::min(b, nd.w) - std::max(a, 0));
+  }
+  return (double)rows_per_pixel * sy * sx * nd.c * nd.kh * nd.kw;  // x C_in by the caller
+}
+
 // ---- footprint (patch) back-substitution of identity rows through a chain
 // conv -> ReLU -> conv ... down to the domain.  Every row is one neuron
 // (b, sign, c) at pixel p of the start node; its Lambda over each earlier node
@@ -494,6 +550,7 @@ vb_status backward_chunk_patch(Backward& B, const BwdCall& c, long long R, const
     HIPCHK(launch_patch_identity(rows, (int)R, S.c, B.pool[cur], B.st));
   }
   int wh = 1, ww = 1;
+  int ksy = 1, koy = 0, ksx = 1, kox = 0;  // window geometry of the Lambda being pushed
   for (const PatchStep& ps : steps) {
     const NodeInfo& nd = G.n[ps.k];
     const NodeInfo& tn = G.n[ps.t];
@@ -527,6 +584,10 @@ vb_status backward_chunk_patch(Backward& B, const BwdCall& c, long long R, const
       cur = outb;
       wh = ps.wh;
       ww = ps.ww;
+      ksy = ps.sy;
+      koy = ps.oy;
+      ksx = ps.sx;
+      kox = ps.ox;
       continue;
     }
     if (last) {
@@ -652,6 +713,12 @@ vb_status backward_chunk_patch(Backward& B, const BwdCall& c, long long R, const
         d.pox = ps.ox;
         d.img_h = tn.h;
         d.img_w = tn.w;
+        d.ssy = ksy;
+        d.soy = koy;
+        d.ssx = ksx;
+        d.sox = kox;
+        d.src_h = nd.h;
+        d.src_w = nd.w;
         if (last) {
           d.epi = E_CONCRETIZE;
           if (c.stop == 0) {
@@ -668,15 +735,370 @@ vb_status backward_chunk_patch(Backward& B, const BwdCall& c, long long R, const
           d.bias = bias_z;
           d.bias_c = tn.c;
         }
-        // (profiled work: the GEMM's own multiply-adds, except the first step from
-        // the identity rows, which is a copy of the weight footprint)
-        s = run_gemm_reduce(B, d, rows, d.gh * d.gw, true, ps.k == c.start ? 0.0 : 2.0 * d.M * d.N * d.K);
+        // (profiled work: the multiply-adds of the rows' window cells inside the
+        // image, except the first step from the identity rows, which is a copy of
+        // the weight footprint)
+        const double macs = ps.k == c.start ? 0.0
+                                            : window_macs(S, nd, Win{wh, ww, ksy, koy, ksx, kox, true},
+                                                          (long long)c.cb * 2 * S.c) * tn.c;
+        s = run_gemm_reduce(B, d, rows, d.gh * d.gw, true, 2.0 * macs / (nd.stride * nd.stride));
         if (s) return s;
       }
     B.release(cur);
     cur = outb;
     wh = ps.wh;
     ww = ps.ww;
+    ksy = ps.sy;
+    koy = ps.oy;
+    ksx = ps.sx;
+    kox = ps.ox;
+  }
+  return VB_OK;
+}
+
+// ---- footprint (window) back-substitution of identity rows through a region
+// of Conv / ReLU / ADD nodes (residual blocks).  Every row is one neuron (b,
+// sign, c) at pixel p of the start node, as in the chain case; its Lambda over
+// each node of the region is kept on a window of that node's output: the
+// bounding box of what reaches the node from the start pixel along every path
+// (for a residual block, the union of the convolution branch and the skip).
+// All rows share the window's size; cell (Y, X) of the row of pixel (py, px)
+// is pixel (py*sy + oy + Y, px*sx + ox + X), cells outside the image hold
+// zeros.  A conv step is a transposed convolution from the conv's output
+// window to its input's window; a branch that reaches the domain node is
+// concretised there over its own reach, so the branches are summed in beta
+// and never need a common window at the domain.
+// Windows of identity rows over `start` on every node down to `stop` (the
+// domain node itself gets none: each branch reaching it is concretised on its
+// own reach).  Applies to regions whose nodes are Conv, ReLU and ADD (with at
+// least one ADD: plain conv chains take the chain walker) where every ReLU's
+// lowest active consumer is a Conv that can fuse the relaxation (its input
+// feeding only that ReLU), every Conv reaches a ReLU or the domain, and no
+// window is as large as its node.  `active` receives the nodes reached.
+bool window_plan(const Graph& G, int start, int stop, std::vector<Win>& W, std::vector<char>& active) {
+  const int N = (int)G.n.size();
+  const NodeInfo& S = G.n[start];
+  if ((S.op != VB_CONV2D && S.op != VB_ADD) || S.h * S.w <= 1) return false;
+  W.assign(N, Win{});
+  active.assign(N, 0);
+  W[start] = Win{1, 1, 1, 0, 1, 0, true};
+  bool has_add = false, smaller = false;
+  for (int k = start; k > stop; --k) {
+    if (!W[k].set) continue;
+    active[k] = 1;
+    const NodeInfo& nd = G.n[k];
+    Win w = W[k];
+    if (nd.op == VB_CONV2D) {
+      w = conv_reach(nd, w);  // (a kernel smaller than its stride: only onto the domain, checked below)
+    } else if (nd.op == VB_ADD) {
+      has_add = true;
+      if (nd.in0 == nd.in1) return false;
+    } else if (nd.op != VB_RELU) {
+      return false;
+    }
+    const int ins[2] = {nd.in0, nd.op == VB_ADD ? nd.in1 : -1};
+    for (int q = 0; q < 2; ++q) {
+      const int t = ins[q];
+      if (t < 0) continue;
+      if (t < stop || G.n[t].h * G.n[t].w <= 1) return false;
+      if (t == stop) {
+        if (nd.op != VB_CONV2D) return false;  // only a conv step concretises onto the domain
+        active[t] = 1;
+        if (!win_union(W[t], w)) return false;  // several branches are summed there first
+        continue;
+      }
+      if (!win_union(W[t], w)) return false;
+    }
+  }
+  if (!has_add) return false;
+  for (int k = stop + 1; k <= start; ++k) {
+    if (!active[k]) continue;
+    const NodeInfo& nd = G.n[k];
+    if (W[k].wh > nd.h || W[k].ww > nd.w) return false;
+    if (W[k].wh < nd.h || W[k].ww < nd.w) smaller = true;
+    if (nd.op == VB_RELU) {
+      // the lowest active consumer relaxes: a conv whose input is this ReLU, and the
+      // ReLU's input feeds nothing else
+      int low = -1;
+      for (int c : nd.cons)
+        if (active[c] && (low < 0 || c < low)) low = c;
+      if (low < 0 || G.n[low].op != VB_CONV2D || G.n[nd.in0].cons.size() != 1) return false;
+      if (!same_win(W[k], W[nd.in0])) return false;
+    }
+    if (nd.op == VB_CONV2D) {
+      const int t = nd.in0;
+      if (t != stop && G.n[t].op != VB_RELU) return false;
+      if (t != stop) {
+        int low = -1;
+        for (int c : G.n[t].cons)
+          if (active[c] && (low < 0 || c < low)) low = c;
+        if (low != k) return false;  // (another conv relaxes there: would need a stored product)
+        // every output-parity class of the transposed conv must have a tap
+        if (nd.kh < nd.stride || nd.kw < nd.stride) return false;
+      }
+    }
+    if (nd.op == VB_ADD) {
+      for (int t : {nd.in0, nd.in1})
+        if (t != stop && G.n[t].op != VB_CONV2D && G.n[t].op != VB_RELU) return false;
+    }
+  }
+  return smaller;
+}
+
+// Per batch element: widest window (floats per row) and partial sums of a
+// window back-substitution of R identity rows; false if it does not apply.
+bool window_requirements(const Graph& G, int start, int stop, long long R, long long& maxw, long long& part_per_b) {
+  std::vector<Win> W;
+  std::vector<char> active;
+  if (!window_plan(G, start, stop, W, active)) return false;
+  maxw = G.n[start].c;
+  part_per_b = 0;
+  for (int k = stop + 1; k <= start; ++k) {
+    if (!active[k]) continue;
+    const NodeInfo& nd = G.n[k];
+    maxw = std::max(maxw, (long long)W[k].wh * W[k].ww * nd.c);
+    if (nd.op == VB_CONV2D) {
+      const NodeInfo& tn = G.n[nd.in0];
+      const Win tw = nd.in0 == stop ? conv_reach(nd, W[k]) : W[nd.in0];
+      const int bn = tn.c > 64 ? 128 : (tn.c > 32 ? 64 : 32);
+      part_per_b = std::max(part_per_b, R * tw.wh * tw.ww * ((tn.c + bn - 1) / bn));
+      if (nd.in0 == stop || k == start) maxw = std::max(maxw, (long long)tw.wh * tw.ww * tn.c);
+    }
+  }
+  // branches meeting at the domain node are summed on its window first
+  maxw = std::max(maxw, (long long)W[stop].wh * W[stop].ww * G.n[stop].c);
+  const int bn = G.n[stop].c > 64 ? 128 : (G.n[stop].c > 32 ? 64 : 32);
+  part_per_b = std::max(part_per_b, R * W[stop].wh * W[stop].ww * ((G.n[stop].c + bn - 1) / bn));
+  return true;
+}
+
+vb_status backward_chunk_window(Backward& B, const BwdCall& c, long long R, const std::vector<Win>& W,
+                                const std::vector<char>& active) {
+  const Graph& G = B.G;
+  const NodeInfo& S = G.n[c.start];
+  const int N = (int)G.n.size();
+  const int rows = (int)(c.cb * R);
+  for (int i = 0; i < NPOOL; ++i) B.refs[i] = 0;
+  // pending Lambda per node: a pool buffer in window geometry pw[k], or IDENT
+  // (the identity rows themselves, over a node one ADD below the start)
+  constexpr int NONE = -1, IDENT_ROWS = -2;
+  std::vector<int> lam(N, NONE);
+  std::vector<Win> pw(N);
+  const float* bias = nullptr;
+  vb_status s = effective_bias(B, G, c.start, bias);
+  if (s) return s;
+  HIPCHK(launch_identity_bias(c.cb, (int)S.size, bias, S.c, B.rowacc, B.st));
+  if (c.stop != 0)
+    HIPCHK(launch_box_center_radius(B.lo[c.stop] + (long long)c.b0 * G.n[c.stop].size,
+                                    B.hi[c.stop] + (long long)c.b0 * G.n[c.stop].size,
+                                    (long long)c.cb * G.n[c.stop].size, B.box_c, B.box_r, B.st));
+  const Win one{1, 1, 1, 0, 1, 0, true};
+  if (S.op == VB_ADD) {
+    lam[S.in0] = lam[S.in1] = IDENT_ROWS;
+    pw[S.in0] = pw[S.in1] = one;
+  } else {
+    lam[c.start] = IDENT_ROWS;
+    pw[c.start] = one;
+  }
+  const long long rows_per_pixel = (long long)c.cb * 2 * S.c;
+  auto chunk_off = [&](int node) -> long long { return (long long)c.b0 * G.n[node].size; };
+  // Branches that reach the domain node: the bound is min over the box of the SUM
+  // of their Lambdas (|L1 + L2| <= |L1| + |L2|), so all but the last one store
+  // their product on the domain's window (the union of the branches' reaches) and
+  // the last one concretises that sum.  (One branch: it concretises on its reach.)
+  int dom_edges = 0, last_edge = -1;
+  for (int k = c.stop + 1; k <= c.start; ++k)
+    if (active[k] && G.n[k].op == VB_CONV2D && G.n[k].in0 == c.stop) {
+      ++dom_edges;
+      if (last_edge < 0) last_edge = k;
+    }
+  int dom_buf = -1;
+  // a pool buffer holding the pending Lambda of node t in window geometry w
+  auto as_buffer = [&](int t, const Win& w, int& out) -> vb_status {
+    out = B.alloc();
+    if (out < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted at node %d", t);
+    const Win& g = pw[t];
+    const int oy = g.oy - w.oy, ox = g.ox - w.ox;
+    if (g.sy != w.sy || g.sx != w.sx || oy < 0 || ox < 0 || oy + g.wh > w.wh || ox + g.ww > w.ww)
+      return fail(VB_EUNSUPPORTED, "internal: window of node %d does not contain its pending Lambda", t);
+    if (lam[t] == IDENT_ROWS) {
+      HIPCHK(launch_window_identity(rows, (int)R, S.c, w.wh, w.ww, oy, ox, B.pool[out], B.st));
+    } else {
+      HIPCHK(launch_window_embed(B.pool[lam[t]], rows, G.n[t].c, g.wh, g.ww, w.wh, w.ww, oy, ox, B.pool[out],
+                                 B.st));
+      B.release(lam[t]);
+    }
+    lam[t] = NONE;
+    return VB_OK;
+  };
+  auto patch_fields = [&](GemmDesc& d, const Win& out_w, const NodeInfo& tn, const Win& src_w, const NodeInfo& kn) {
+    d.rows_per_b = (int)R;
+    d.patch = 1;
+    d.pc = S.c;
+    d.pgh = S.h;
+    d.pgw = S.w;
+    d.psy = out_w.sy;
+    d.poy = out_w.oy;
+    d.psx = out_w.sx;
+    d.pox = out_w.ox;
+    d.img_h = tn.h;
+    d.img_w = tn.w;
+    d.ssy = src_w.sy;
+    d.soy = src_w.oy;
+    d.ssx = src_w.sx;
+    d.sox = src_w.ox;
+    d.src_h = kn.h;
+    d.src_w = kn.w;
+  };
+  for (int k = c.start; k > c.stop; --k) {
+    if (!active[k] || lam[k] == NONE) continue;
+    const NodeInfo& nd = G.n[k];
+    if (nd.op == VB_ADD) {
+      // Lambda over an ADD flows unchanged into both inputs (window of the ADD)
+      if (lam[k] == IDENT_ROWS) return fail(VB_EUNSUPPORTED, "internal: identity rows over a nested ADD");
+      for (int t : {nd.in0, nd.in1}) {
+        if (lam[t] != NONE) return fail(VB_EUNSUPPORTED, "internal: two Lambdas meet at node %d", t);
+        B.refs[lam[k]]++;
+        lam[t] = lam[k];
+        pw[t] = pw[k];
+      }
+      B.release(lam[k]);
+      lam[k] = NONE;
+      continue;
+    }
+    if (nd.op != VB_CONV2D) return fail(VB_EUNSUPPORTED, "internal: window rows pending at node %d", k);
+    const int t = nd.in0;
+    const NodeInfo& tn = G.n[t];
+    const bool last = t == c.stop;
+    const int z = last ? -1 : tn.in0;
+    // the first step of identity rows through a conv whose input ReLU relaxes:
+    // a relaxed copy of the weight footprint, no GEMM
+    if (lam[k] == IDENT_ROWS && !last && lam[t] == NONE && same_win(conv_reach(nd, one), W[t])) {
+      PatchIdRelax pir{};
+      pir.W = nd.W;
+      pir.Co = nd.c;
+      pir.Ci = tn.c;
+      pir.kh = nd.kh;
+      pir.kw = nd.kw;
+      if (patch_id_relax_fits(pir) && nd.c == S.c && nd.h == S.h && nd.w == S.w) {
+        const float* bias_z = nullptr;
+        if ((s = effective_bias(B, G, z, bias_z))) return s;
+        HIPCHK(launch_relax_coef(B.lo[z] + chunk_off(z), B.hi[z] + chunk_off(z), (long long)c.cb * G.n[z].size,
+                                 nullptr, B.coef, B.st));
+        const int outb = B.alloc();
+        if (outb < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted at node %d", k);
+        pir.R = (int)R;
+        pir.pgh = S.h;
+        pir.pgw = S.w;
+        pir.psy = W[t].sy;
+        pir.poy = W[t].oy;
+        pir.psx = W[t].sx;
+        pir.pox = W[t].ox;
+        pir.img_h = tn.h;
+        pir.img_w = tn.w;
+        pir.coef = B.coef;
+        pir.bias = bias_z;
+        pir.out = B.pool[outb];
+        HIPCHK(launch_patch_id_relax(pir, rows, B.rowacc, B.st));
+        lam[k] = NONE;
+        lam[z] = outb;
+        pw[z] = W[t];
+        continue;
+      }
+    }
+    int cur;
+    if (lam[k] == IDENT_ROWS) {
+      // identity rows over this conv's output, one-hot on a 1 x 1 window
+      if ((s = as_buffer(k, one, cur))) return s;
+    } else {
+      cur = lam[k];
+      lam[k] = NONE;
+    }
+    const Win kw = pw[k];
+    const bool summed = last && dom_edges > 1;
+    const Win tw = last ? (summed ? W[t] : conv_reach(nd, kw)) : W[t];
+    int outb = -1, addb = -1;
+    const float* bias_z = nullptr;
+    if (summed && dom_buf < 0) {
+      dom_buf = B.alloc();
+      if (dom_buf < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted at node %d", k);
+      HIPCHK(launch_fill(B.pool[dom_buf], 0.f, (long long)rows * tw.wh * tw.ww * tn.c, B.st));
+    }
+    if (!last) {
+      if (lam[t] >= 0 && same_win(pw[t], tw)) {
+        addb = lam[t];  // already in the target's window: added as it is
+        lam[t] = NONE;
+      } else if (lam[t] != NONE && (s = as_buffer(t, tw, addb))) {
+        return s;
+      }
+      outb = B.alloc();
+      if (outb < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted at node %d", k);
+      if ((s = effective_bias(B, G, z, bias_z))) return s;
+      HIPCHK(launch_relax_coef(B.lo[z] + chunk_off(z), B.hi[z] + chunk_off(z), (long long)c.cb * G.n[z].size,
+                               nullptr, B.coef, B.st));
+    }
+    // the conv as a transposed conv from window kw to window tw: target cell
+    // Yt = stride * Yk + ky - pad_eff with pad_eff = pad + oy_t - stride * oy_k
+    NodeInfo nv = nd, tv = tn;
+    nv.h = kw.wh;
+    nv.w = kw.ww;
+    nv.size = (long long)kw.wh * kw.ww * nd.c;
+    tv.h = tw.wh;
+    tv.w = tw.ww;
+    tv.size = (long long)tw.wh * tw.ww * tn.c;
+    const int pad_y = nd.pad + tw.oy - nd.stride * kw.oy, pad_x = nd.pad + tw.ox - nd.stride * kw.ox;
+    if (pad_y != pad_x) return fail(VB_EUNSUPPORTED, "internal: windows of node %d are not square-aligned", k);
+    nv.pad = pad_y;
+    // the multiply-adds of this step (cells of the rows' windows inside the image)
+    const double macs = window_macs(S, nd, kw, rows_per_pixel) * tn.c;
+    std::vector<GemmDesc> descs;
+    for (int py = 0; py < nd.stride; ++py)
+      for (int px = 0; px < nd.stride; ++px) {
+        GemmDesc d;
+        if (conv_backward(nv, tv, B.pool[cur], rows, py, px, d) && d.K > 0) descs.push_back(d);
+      }
+    for (GemmDesc& d : descs) {
+      d.B = B.wt[k];
+      patch_fields(d, tw, tn, kw, nd);
+      if (summed && k != last_edge) {
+        // a branch onto the domain that is not the last: add into the domain window
+        d.epi = E_STORE;
+        d.out = B.pool[dom_buf];
+        d.addend = B.pool[dom_buf];
+      } else if (last) {
+        d.epi = E_CONCRETIZE;
+        d.addend = summed ? B.pool[dom_buf] : nullptr;
+        if (c.stop == 0) {
+          d.center = B.dom.xc + chunk_off(0);
+          d.radius = B.dom.xr ? B.dom.xr + chunk_off(0) : nullptr;
+          d.eps = B.dom.eps;
+        } else {
+          d.center = B.box_c;
+          d.radius = B.box_r;
+        }
+      } else {
+        d.epi = E_RELAX;
+        d.coef = B.coef;
+        d.out = B.pool[outb];
+        d.addend = addb >= 0 ? B.pool[addb] : nullptr;
+        d.bias = bias_z;
+        d.bias_c = tn.c;
+      }
+      s = run_gemm_reduce(B, d, rows, d.gh * d.gw, d.epi != E_STORE, 2.0 * macs / descs.size());
+      if (s) return s;
+    }
+    if (!last && descs.size() != (size_t)nd.stride * nd.stride)
+      return fail(VB_EUNSUPPORTED, "internal: node %d has output-parity classes without taps", k);
+    B.release(cur);
+    if (addb >= 0) B.release(addb);
+    if (summed && k == last_edge) {
+      B.release(dom_buf);
+      dom_buf = -1;
+    }
+    if (!last) {
+      lam[z] = outb;
+      pw[z] = tw;
+    }
   }
   return VB_OK;
 }
@@ -729,6 +1151,10 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
   {
     std::vector<PatchStep> steps;
     if (patch_chain(B, c, steps)) return backward_chunk_patch(B, c, R, steps);
+    std::vector<Win> W;
+    std::vector<char> act;
+    if (!(c.C || B.a_out || B.alpha || B.psi_keep) && window_plan(B.G, c.start, c.stop, W, act))
+      return backward_chunk_window(B, c, R, W, act);
   }
   const Graph& G = B.G;
   const int N = (int)G.n.size();
@@ -813,7 +1239,9 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
     vb_status s = effective_bias(B, G, c.start, bias);
     if (s) return s;
     // fast path: Linear start whose input is a ReLU -> relaxed rows of +-W in one kernel
-    int t = (S.op == VB_LINEAR) ? src_of(G, S.in0) : -1;
+    // (with alpha slopes or kept Psi the identity rows go through the GEMM
+    // epilogues, which apply them; the fused first-step kernels do not)
+    int t = (S.op == VB_LINEAR && !B.alpha && !B.psi_keep) ? src_of(G, S.in0) : -1;
     if (t >= 0 && t != c.stop && G.n[t].op == VB_RELU && lowest_consumer(G, active, t, c.start) &&
         G.n[G.n[t].in0].cons.size() == 1) {
       int z = G.n[t].in0;
@@ -835,8 +1263,11 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
   for (int k = from; k > c.stop; --k) {
     if (lam[k] == -1) continue;
     const NodeInfo& nd = G.n[k];
-    const bool ident = lam[k] == IDENT;
-    if (ident && nd.op != VB_ADD && nd.op != VB_CONV2D) {
+    // implicit identity rows feed the footprint kernels of ADD / Conv nodes, unless
+    // alpha slopes or kept Psi need the GEMM epilogues: then they are written out
+    const bool fused = !B.alpha && !B.psi_keep;
+    const bool ident = lam[k] == IDENT && fused;
+    if (lam[k] == IDENT && (!fused || (nd.op != VB_ADD && nd.op != VB_CONV2D))) {
       vb_status s = materialise(k);
       if (s) return s;
     }
@@ -1270,14 +1701,24 @@ struct WsLayout {
   size_t bytes;
 };
 
+// The largest node between the domain node (exclusive) and the start node.
+long long region_max_size(const Graph& G, int start, int stop) {
+  long long m = 0;
+  for (int k = stop + 1; k <= start; ++k) m = std::max(m, G.n[k].size);
+  return m;
+}
+
+// coef_per_b: neurons per batch element of the largest node whose relaxation
+// coefficients a back-substitution builds (0: maxw, the widest Lambda row,
+// which covers it when Lambda rows are as wide as the nodes).
 WsLayout layout_for(long long maxw, long long part_per_b, long long R, int cb, size_t extra_floats,
-                    long long box_per_b = 0) {
+                    long long box_per_b = 0, long long coef_per_b = 0) {
   WsLayout L;
   L.pool_floats = (size_t)cb * R * maxw;
   L.part_floats = (size_t)cb * part_per_b;
   L.rows = (size_t)cb * R;
   L.box_floats = (size_t)cb * box_per_b;
-  L.coef_floats = 4 * (size_t)cb * maxw;
+  L.coef_floats = 4 * (size_t)cb * std::max(maxw, coef_per_b);
   L.bytes = NPOOL * align_up(L.pool_floats * 4) + align_up(L.part_floats * 4) + align_up(L.rows * 4) +
             2 * align_up(L.box_floats * 4) + align_up(L.coef_floats * 4) + align_up(extra_floats * 4);
   return L;
@@ -1298,7 +1739,8 @@ struct ChunkPlan {
 vb_status plan_chunks(const Graph& G, int start, int stop, long long R, bool plain, bool spec, int batch,
                       size_t ws_bytes, size_t reserved_floats, ChunkPlan& plan) {
   long long maxw, ppb;
-  if (!plain || !patch_requirements(G, start, stop, R, maxw, ppb)) bwd_requirements(G, start, stop, R, maxw, ppb);
+  if (!plain || (!patch_requirements(G, start, stop, R, maxw, ppb) && !window_requirements(G, start, stop, R, maxw, ppb)))
+    bwd_requirements(G, start, stop, R, maxw, ppb);
   if (spec) maxw = std::max(maxw, G.n[start].size);
   const long long box = stop > 0 ? G.n[stop].size : 0;
   // GEMM index spaces are 32-bit: rows x pixels (padded to whole row blocks) per launch
@@ -1311,13 +1753,16 @@ vb_status plan_chunks(const Graph& G, int start, int stop, long long R, bool pla
   }
   auto fits_index = [&](long long cbn) { return cbn * R * maxp + 64 * maxp + 256 <= (long long)INT32_MAX; };
   int cb = batch;
-  while (cb > 1 && (!fits_index(cb) || layout_for(maxw, ppb, R, cb, reserved_floats, box).bytes > ws_bytes))
+  // footprint rows keep Lambda on windows narrower than the nodes, but the
+  // relaxation coefficients cover whole nodes
+  const long long coef = region_max_size(G, start, stop);
+  while (cb > 1 && (!fits_index(cb) || layout_for(maxw, ppb, R, cb, reserved_floats, box, coef).bytes > ws_bytes))
     cb = (cb + 1) / 2;
   if (!fits_index(cb))
     return fail(VB_EUNSUPPORTED, "one batch element has %lld rows x %lld pixels: beyond the 32-bit GEMM index range",
                 R, maxp);
   plan.cb = cb;
-  plan.L = layout_for(maxw, ppb, R, cb, reserved_floats, box);
+  plan.L = layout_for(maxw, ppb, R, cb, reserved_floats, box, coef);
   if (plan.L.bytes > ws_bytes)
     return fail(VB_ENOMEM, "workspace of %zu bytes is too small: one batch element needs %zu", ws_bytes, plan.L.bytes);
   return VB_OK;
@@ -1567,9 +2012,11 @@ static size_t crown_workspace(const Graph& G, int batch, int m, int method, int 
   size_t best = 0;
   auto consider = [&](int start, int stop, long long R, bool spec) {
     long long maxw, ppb;
-    if (spec || !patch_requirements(G, start, stop, R, maxw, ppb)) bwd_requirements(G, start, stop, R, maxw, ppb);
+    if (spec || (!patch_requirements(G, start, stop, R, maxw, ppb) && !window_requirements(G, start, stop, R, maxw, ppb)))
+      bwd_requirements(G, start, stop, R, maxw, ppb);
     if (spec) maxw = std::max(maxw, G.n[start].size);
-    best = std::max(best, layout_for(maxw, ppb, R, batch, wt_floats(G), stop > 0 ? G.n[stop].size : 0).bytes);
+    best = std::max(best, layout_for(maxw, ppb, R, batch, wt_floats(G), stop > 0 ? G.n[stop].size : 0,
+                                     region_max_size(G, start, stop)).bytes);
   };
   const int L = G.L;
   if (m > 0) {
@@ -1592,6 +2039,7 @@ static size_t crown_workspace(const Graph& G, int batch, int m, int method, int 
 namespace {
 bool alpha_chain(const Graph& G, std::vector<std::pair<int, int>>& chain);
 size_t alpha_workspace(const Graph& G, int batch, int m, const int* width = nullptr);
+size_t alpha_workspace_at(const Graph& G, int batch, int start, long long R, bool spec, const int* width);
 vb_status check_compact(const Graph& G, int batch, int m, const vb_alpha_compact* c);
 }  // namespace
 
@@ -1602,13 +2050,23 @@ extern "C" vb_status vb_workspace_size(const vb_graph* g, int32_t batch, int32_t
   if (s) return s;
   if (!bytes) return fail(VB_EINVAL, "bytes is NULL");
   if (batch <= 0 || m < 0) return fail(VB_EINVAL, "batch must be > 0 and m >= 0");
-  method &= ~VB_INTERSECT_IBP;
+  const bool alpha_rows = (method & VB_ALPHA_ROWS) != 0;
+  method &= ~(VB_INTERSECT_IBP | VB_ALPHA_ROWS);
   if (method < VB_METHOD_IBP || method > VB_METHOD_HYBRID) return fail(VB_EINVAL, "unknown method %d", method);
   if (method == VB_METHOD_HYBRID && (region_start <= 0 || region_start >= G.L))
     return fail(VB_EINVAL, "region_start %d out of range", region_start);
   *bytes = std::max(crown_workspace(G, batch, m, method, region_start), ibp_workspace(G, batch));
   std::vector<std::pair<int, int>> chain;
   if (m > 0 && alpha_chain(G, chain)) *bytes = std::max(*bytes, alpha_workspace(G, batch, m));
+  if (alpha_rows && alpha_chain(G, chain)) {
+    // alpha steps on the identity rows of every ReLU input more than one affine step from the input
+    for (size_t r = 0; r < G.n.size(); ++r) {
+      if (G.n[r].op != VB_RELU) continue;
+      const int z = G.n[r].in0;
+      if (one_affine_step(G, z, 0)) continue;
+      *bytes = std::max(*bytes, alpha_workspace_at(G, batch, z, 2LL * G.n[z].size, false, nullptr));
+    }
+  }
   return VB_OK;
 }
 
@@ -1803,6 +2261,14 @@ extern "C" vb_status vb_crown(const vb_graph* g, int32_t batch, const float* x_c
   return VB_OK;
 }
 
+extern "C" vb_status vb_verify(int32_t batch, int32_t m, const float* lb, int32_t* verified, int32_t* n_verified,
+                               void* stream) {
+  if (batch <= 0 || m <= 0) return fail(VB_EINVAL, "batch and m must be positive");
+  if (!lb || !verified) return fail(VB_EINVAL, "lb and verified must be non-NULL");
+  HIPCHK(launch_verify(lb, batch, m, verified, n_verified, (hipStream_t)stream));
+  return VB_OK;
+}
+
 extern "C" vb_status vb_crown_noalloc(const vb_graph* g, int32_t batch, const float* x_center,
                                       const float* x_radius, float eps, int32_t method, int32_t region_start,
                                       float* const* node_lo, float* const* node_hi, const float* C, int32_t m,
@@ -1877,20 +2343,28 @@ bool alpha_chain(const Graph& G, std::vector<std::pair<int, int>>& chain) {
   return !chain.empty() && chain.back().first == G.L && G.n[G.L].op == VB_LINEAR;
 }
 
-// kept Psi over the domain and over every ReLU node (compact: width[k] per row)
-size_t alpha_psi_floats(const Graph& G, long long rows, const int* width) {
+// kept Psi over the domain and over every ReLU node below `start` (compact:
+// width[k] per row)
+size_t alpha_psi_floats(const Graph& G, long long rows, const int* width, int start) {
   size_t f = align_up((size_t)rows * G.n[0].size * 4) / 4;
-  for (size_t k = 0; k < G.n.size(); ++k)
+  for (size_t k = 0; k < G.n.size() && (int)k < start; ++k)
     if (G.n[k].op == VB_RELU) f += align_up((size_t)rows * (width ? width[k] : G.n[k].size) * 4) / 4;
   return f;
 }
 
-size_t alpha_workspace(const Graph& G, int batch, int m, const int* width) {
-  const long long R = m;
+// Workspace of an alpha step on R rows per batch element over node `start`
+// (spec rows widen Lambda to the start node).
+size_t alpha_workspace_at(const Graph& G, int batch, int start, long long R, bool spec, const int* width) {
   long long maxw, ppb;
-  bwd_requirements(G, G.L, 0, R, maxw, ppb);
-  maxw = std::max(maxw, G.n[G.L].size);
-  return layout_for(maxw, ppb, R, batch, wt_floats(G) + alpha_psi_floats(G, (long long)batch * m, width)).bytes;
+  bwd_requirements(G, start, 0, R, maxw, ppb);
+  if (spec) maxw = std::max(maxw, G.n[start].size);
+  return layout_for(maxw, ppb, R, batch, wt_floats(G) + alpha_psi_floats(G, (long long)batch * R, width, start),
+                    0, region_max_size(G, start, 0))
+      .bytes;
+}
+
+size_t alpha_workspace(const Graph& G, int batch, int m, const int* width) {
+  return alpha_workspace_at(G, batch, G.L, m, true, width);
 }
 
 }  // namespace
@@ -1958,11 +2432,11 @@ extern "C" vb_status vb_alpha_init(const vb_graph* g, int32_t batch, int32_t m, 
     const int z = G.n[k].in0;
     if (!node_lo[z] || !node_hi[z]) return fail(VB_EINVAL, "ReLU node %zu: input bounds missing", k);
     if (compact && compact->width[k] == 0) continue;  // no unstable neuron: no state
-    if (!alpha[k] || !adam_m[k] || !adam_v[k])
-      return fail(VB_EINVAL, "ReLU node %zu: alpha / adam state missing", k);
+    if (!alpha[k]) continue;                          // a node this state does not cover
+    if (!adam_m[k] || !adam_v[k]) return fail(VB_EINVAL, "ReLU node %zu: adam state missing", k);
   }
   for (size_t k = 0; k < G.n.size(); ++k) {
-    if (G.n[k].op != VB_RELU) continue;
+    if (G.n[k].op != VB_RELU || !alpha[k]) continue;
     const int z = G.n[k].in0;
     const int* aidx = compact ? compact->index[k] : nullptr;
     const int acols = compact ? compact->width[k] : 0;
@@ -1972,16 +2446,23 @@ extern "C" vb_status vb_alpha_init(const vb_graph* g, int32_t batch, int32_t m, 
   return VB_OK;
 }
 
-extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float* C, int32_t m,
-                                   const float* const* node_lo, const float* const* node_hi, const float* x_center,
-                                   const float* x_radius, float eps, const vb_alpha_compact* compact,
-                                   float* const* alpha, float* const* adam_m, float* const* adam_v, int32_t step,
-                                   float lr, float beta1, float beta2, float adam_eps, float* lb_out, float* best_lb,
-                                   void* ws, size_t ws_bytes, void* stream) {
+extern "C" vb_status vb_alpha_step_rows(const vb_graph* g, int32_t batch, int32_t start, const float* C, int32_t m,
+                                        const float* const* node_lo, const float* const* node_hi,
+                                        const float* x_center, const float* x_radius, float eps,
+                                        const vb_alpha_compact* compact, float* const* alpha, float* const* adam_m,
+                                        float* const* adam_v, int32_t step, float lr, float beta1, float beta2,
+                                        float adam_eps, float* lb_out, float* best_lb, float* ub_out, float* best_ub,
+                                        void* ws, size_t ws_bytes, void* stream) {
   Graph G;
   vb_status s = parse_graph(g, G);
   if (s) return s;
-  if (batch <= 0 || m <= 0 || !C) return fail(VB_EINVAL, "batch, m must be positive and C non-NULL");
+  if (batch <= 0) return fail(VB_EINVAL, "batch must be positive");
+  if (start <= 0 || start >= (int)G.n.size() || (G.n[start].op != VB_LINEAR && G.n[start].op != VB_CONV2D))
+    return fail(VB_EINVAL, "start %d must be a Linear or Conv node", start);
+  if (C && m <= 0) return fail(VB_EINVAL, "m must be positive with C");
+  if (C && (ub_out || best_ub)) return fail(VB_EINVAL, "spec rows bound one side: ub_out / best_ub must be NULL");
+  const bool ident = C == nullptr;
+  const long long R = ident ? 2LL * G.n[start].size : m;
   if ((s = check_domain(x_center))) return s;
   if (!x_radius && !(eps >= 0.f)) return fail(VB_EINVAL, "eps must be >= 0");
   if (!node_lo || !node_hi || !alpha) return fail(VB_EINVAL, "NULL pointer array");
@@ -1989,11 +2470,12 @@ extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float
   if (step > 0 && (!adam_m || !adam_v)) return fail(VB_EINVAL, "Adam state arrays are NULL");
   if (!(lr >= 0.f) || !(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f) || !(adam_eps > 0.f))
     return fail(VB_EINVAL, "bad Adam hyper-parameters");
-  if (!lb_out && !best_lb) return fail(VB_EINVAL, "lb_out and best_lb are both NULL");
+  if (!lb_out && !best_lb && !ub_out && !best_ub) return fail(VB_EINVAL, "no output: lb_out, best_lb (ub_out, best_ub) NULL");
+  if ((long long)batch * R >= (1LL << 31)) return fail(VB_EUNSUPPORTED, "batch x rows beyond 2^31");
   std::vector<std::pair<int, int>> chain;
   if (!alpha_chain(G, chain)) return fail(VB_EUNSUPPORTED, "alpha-CROWN needs a chain of Linear/Conv + ReLU nodes");
-  if (compact && (s = check_compact(G, batch, m, compact))) return s;
-  for (size_t k = 0; k < G.n.size(); ++k) {
+  if (compact && (s = check_compact(G, batch, (int)R, compact))) return s;
+  for (size_t k = 0; k < G.n.size() && (int)k < start; ++k) {
     if (G.n[k].op != VB_RELU) continue;
     const int z = G.n[k].in0;
     if (!node_lo[z] || !node_hi[z]) return fail(VB_EINVAL, "ReLU node %zu: input bounds missing", k);
@@ -2002,11 +2484,11 @@ extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float
       return fail(VB_EINVAL, "ReLU node %zu: alpha / adam state missing", k);
   }
   if (!ws) return fail(VB_EINVAL, "workspace is NULL");
-  const size_t need = alpha_workspace(G, batch, m, compact ? compact->width : nullptr);
+  const size_t need = alpha_workspace_at(G, batch, start, R, !ident, compact ? compact->width : nullptr);
   if (ws_bytes < need)
     return fail(VB_ENOMEM, "alpha step needs %zu bytes of workspace for the whole batch (got %zu)", need, ws_bytes);
   hipStream_t st = (hipStream_t)stream;
-  const long long rows = (long long)batch * m;
+  const long long rows = (long long)batch * R;
 
   // workspace: [transposed weights][kept psi per ReLU + domain][backward pool ...]
   char* base = (char*)ws;
@@ -2017,7 +2499,7 @@ extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float
   std::vector<float*> psi(G.n.size(), nullptr);
   psi[0] = (float*)(base + off);
   off += align_up((size_t)rows * G.n[0].size * 4);
-  for (size_t k = 0; k < G.n.size(); ++k)
+  for (size_t k = 0; k < G.n.size() && (int)k < start; ++k)
     if (G.n[k].op == VB_RELU) {
       const long long w = compact ? compact->width[k] : G.n[k].size;
       psi[k] = w > 0 ? (float*)(base + off) : nullptr;
@@ -2025,7 +2507,7 @@ extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float
     }
   // (a compact node without unstable neurons has no state: its slopes are never read)
   std::vector<const float*> al(G.n.size(), nullptr);
-  for (size_t k = 0; k < G.n.size(); ++k)
+  for (size_t k = 0; k < G.n.size() && (int)k < start; ++k)
     al[k] = (compact && G.n[k].op == VB_RELU && compact->width[k] == 0) ? nullptr : alpha[k];
   B.alpha = al.data();
   B.psi_keep = psi.data();
@@ -2033,24 +2515,33 @@ extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float
     B.aidx = compact->index;
     B.awidth = compact->width;
   }
-  // evaluation: lower bounds of the m spec rows with the current slopes
-  s = backward_all(B, G.L, 0, C, m, 0, batch, m, base, ws_bytes, off / 4, [&](float* acc, int b0, int cb) -> vb_status {
-    if (b0 != 0 || cb != batch) return fail(VB_ENOMEM, "internal: alpha step was chunked");
-    HIPCHK(launch_finish_lower(acc, rows, lb_out, best_lb, step == 1, st));
-    return VB_OK;
-  });
+  // evaluation: lower bounds of the rows with the current slopes (identity rows:
+  // +e_j gives l_j, -e_j gives -u_j)
+  const int n = (int)G.n[start].size;
+  s = backward_all(B, start, 0, C, m, ident ? 1 : 0, batch, R, base, ws_bytes, off / 4,
+                   [&](float* acc, int b0, int cb) -> vb_status {
+                     if (b0 != 0 || cb != batch) return fail(VB_ENOMEM, "internal: alpha step was chunked");
+                     if (!ident) {
+                       HIPCHK(launch_finish_lower(acc, rows, lb_out, best_lb, step == 1, st));
+                     } else {
+                       if (lb_out || ub_out) HIPCHK(launch_finish(acc, batch, n, lb_out, ub_out, nullptr, st, 0));
+                       if (best_lb || best_ub)
+                         HIPCHK(launch_finish(acc, batch, n, best_lb, best_ub, nullptr, st, step == 1 ? 0 : 1));
+                     }
+                     return VB_OK;
+                   });
   if (s) return s;
   if (step == 0) return VB_OK;
 
   // adjoint, forward through the chain; the evaluation's pool buffers are free now
   float* gbuf[2] = {B.pool[0], B.pool[1]};
-  HIPCHK(launch_adj_domain(psi[0], (int)rows, (int)G.n[0].size, m, x_center, x_radius, eps, gbuf[0], st));
+  HIPCHK(launch_adj_domain(psi[0], (int)rows, (int)G.n[0].size, (int)R, x_center, x_radius, eps, gbuf[0], st));
   const double bc1 = 1.0 / (1.0 - std::pow((double)beta1, step));
   const double bc2 = 1.0 / (1.0 - std::pow((double)beta2, step));
   int cur = 0;
   for (const auto& kr : chain) {
     const int k = kr.first, r = kr.second;
-    if (r < 0) break;  // the last affine node: its adjoint is not needed
+    if (r < 0 || k >= start) break;  // the start node: its adjoint is not needed
     const NodeInfo& nd = G.n[k];
     const NodeInfo& in = G.n[src_of(G, nd.in0)];
     GemmDesc d = affine_forward(nd, in, (int)rows);
@@ -2101,7 +2592,7 @@ extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float
     HIPCHK(launch_relax_coef(node_lo[k], node_hi[k], (long long)batch * nd.size,
                              compact ? compact->index[r] : nullptr, B.coef, st));
     d.coef = B.coef;
-    d.rows_per_b = m;
+    d.rows_per_b = (int)R;
     const bool none = compact && compact->width[r] == 0;
     d.psi_in = psi[r];
     d.alpha_rw = none ? nullptr : alpha[r];
@@ -2163,6 +2654,19 @@ extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float
   return VB_OK;
 }
 
+extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float* C, int32_t m,
+                                   const float* const* node_lo, const float* const* node_hi, const float* x_center,
+                                   const float* x_radius, float eps, const vb_alpha_compact* compact,
+                                   float* const* alpha, float* const* adam_m, float* const* adam_v, int32_t step,
+                                   float lr, float beta1, float beta2, float adam_eps, float* lb_out, float* best_lb,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  if (!C) return fail(VB_EINVAL, "C is NULL");
+  if (!g || !g->nodes || g->n_nodes < 2) return fail(VB_EINVAL, "graph is NULL or has fewer than 2 nodes");
+  return vb_alpha_step_rows(g, batch, g->n_nodes - 1, C, m, node_lo, node_hi, x_center, x_radius, eps, compact, alpha,
+                            adam_m, adam_v, step, lr, beta1, beta2, adam_eps, lb_out, best_lb, nullptr, nullptr, ws,
+                            ws_bytes, stream);
+}
+
 // ---------------------------------------------------------------------------
 // host-only helpers for the tests (vb_testing.h)
 
@@ -2219,4 +2723,16 @@ extern "C" int32_t vb_testing_conv_tile_n(int32_t mode, int32_t rows, int32_t h,
   for (int bn : {32, 64, 128, 256})
     if ((d.N + bn - 1) / bn == nt) return bn;
   return -1;
+}
+
+extern "C" int32_t vb_testing_identity_path(const vb_graph* g, int32_t start, int32_t stop) {
+  Graph G;
+  if (parse_graph(g, G) != VB_OK) return -1;
+  if (start <= 0 || start >= (int)G.n.size() || stop < 0 || stop >= start) return -1;
+  std::vector<PatchStep> steps;
+  if (patch_chain_graph(G, start, stop, steps)) return 1;
+  std::vector<Win> W;
+  std::vector<char> active;
+  if (window_plan(G, start, stop, W, active)) return 2;
+  return 0;
 }

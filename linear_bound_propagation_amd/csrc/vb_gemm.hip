@@ -249,6 +249,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   // offset.  A dense GEMM is the one-tap case with the whole K as channels.
   long long abase[FAST ? AV : 1], bbase[FAST ? BV : 1];
   int ld_j = 0, ld_c = 0;  // tap and channel offset of the next stage to load
+  unsigned tmask = (1u << MAX_TAPS) - 1;  // taps whose stages this workgroup runs
   auto set_tap = [&](int j) {
     const Tap tp = DENSE ? Tap{0, 0, 0} : tap_of(d, j);
 #pragma unroll
@@ -289,11 +290,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
       }
 #pragma unroll
       for (int i = 0; i < BV; ++i) rb[i] = ld4(d.B, bbase[i] >= 0 ? bbase[i] + ld_c : -1);
-      // advance to the next stage: the next 32 channels, or the next tap
+      // advance to the next stage: the next 32 channels, or the next tap this
+      // tile reads
       ld_c += BK;
       if (!DENSE && ld_c >= d.cs) {
         ld_c = 0;
-        ++ld_j;
+        const unsigned rest = tmask >> (ld_j + 1);
+        ld_j = rest ? ld_j + __ffs(rest) : d.ntaps;
         if (ld_j < d.ntaps) set_tap(ld_j);
       }
     } else {
@@ -364,15 +367,64 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   const int nk_all = (d.K + BK - 1) / BK;
   const int per_slice = (nk_all + ks_n - 1) / ks_n;
   const int kb = ks * per_slice;
-  const int nk = min(nk_all - kb, per_slice);
+  int nk = min(nk_all - kb, per_slice);
+  // Taps that no row of this tile reads inside the source add only zero
+  // products: a gather GEMM on the fast path (K not split) runs the stages of
+  // the other taps only.  A tap counts for a row if its source cell lies in the
+  // source grid (and, for footprint windows, in the source node's image), and
+  // the row's own output cell lies in the target image (footprint windows:
+  // outside it the epilogue keeps nothing).
+  if (FAST && !DENSE && ks_n == 1) {
+    __shared__ unsigned tap_mask;
+    unsigned my = 0;
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+      const Pos& p = apos[i];
+      if (!p.valid) continue;
+      int sy0 = 0, sx0 = 0;
+      bool inimg = true;
+      if (VAR == V_PATCH) {
+        const GPos g = gdecode(d, m0 + (tid + NTHR * i) / (BK / 4));
+        const int t1 = fdiv(g.row, d.div_pc);
+        const int pz = t1 - fdiv(t1, d.div_pz) * d.div_pz.d;
+        const int py = fdiv(pz, d.div_pw), px = pz - py * d.pgw;
+        const int ay = py * d.psy + d.poy + p.Y * d.oym + d.oy0;
+        const int ax = px * d.psx + d.pox + p.X * d.oxm + d.ox0;
+        inimg = ay >= 0 && ay < d.img_h && ax >= 0 && ax < d.img_w;
+        sy0 = py * d.ssy + d.soy;
+        sx0 = px * d.ssx + d.sox;
+      }
+      if (!inimg) continue;
+      for (int j = 0; j < d.ntaps; ++j) {
+        const Tap tp = tap_of(d, j);
+        const int yy = p.Y * d.sy + tp.dy, xx = p.X * d.sx + tp.dx;
+        bool ok = yy >= 0 && yy < d.hs && xx >= 0 && xx < d.ws;
+        if (VAR == V_PATCH && d.src_h > 0)
+          ok = ok && sy0 + yy >= 0 && sy0 + yy < d.src_h && sx0 + xx >= 0 && sx0 + xx < d.src_w;
+        if (ok) my |= 1u << j;
+      }
+    }
+    if (tid == 0) tap_mask = 0u;
+    __syncthreads();
+    if (my) atomicOr(&tap_mask, my);
+    __syncthreads();
+    tmask = tap_mask;
+    nk = __popc(tmask) * (d.cs / BK);
+  }
   if (FAST) {
     // first stage of this workgroup's K range
     ld_j = DENSE ? 0 : (kb * BK) / d.cs;
     ld_c = kb * BK - ld_j * d.cs;
-    set_tap(ld_j);
+    if (!DENSE && ks_n == 1) {
+      ld_j = tmask ? __ffs(tmask) - 1 : 0;
+      ld_c = 0;
+    }
+    if (nk > 0) set_tap(ld_j);
   }
-  load(kb * BK);
-  store(0);
+  if (nk > 0) {
+    load(kb * BK);
+    store(0);
+  }
   __syncthreads();
   for (int t = 0; t < nk; ++t) {
     const int cur = t & 1;

@@ -85,6 +85,10 @@ struct GemmDesc {
   int patch;
   FastDiv div_pc, div_pz, div_pw;  // filled by launch_gemm: pc, pgh*pgw, pgw
   int pc, pgh, pgw, psy, poy, psx, pox, img_h, img_w;
+  //      and of the A operand's window: source cell (Ys, Xs) of row p is pixel
+  //      (py*ssy + soy + Ys, px*ssx + sox + Xs) of a src_h x src_w node
+  //      (src_h = 0: not given; then only the window's own bounds are known)
+  int ssy, soy, ssx, sox, src_h, src_w;
   int Mt;                      // filled by launch_gemm: size of the tile index space (gather: padded)
   int rb_shift;                // filled by launch_gemm: log2 of the rows per block (gather)
   // ---- epilogue
@@ -127,9 +131,11 @@ struct GemmDesc {
 };
 
 // A one-tap, one-position descriptor is a plain GEMM (row-major m); anything
-// else is a gather GEMM (position-major m).
+// else is a gather GEMM (position-major m).  Footprint rows are always a gather
+// GEMM (their epilogue maps each row's window cells to pixels, even on 1 x 1
+// windows).
 inline bool gemm_is_dense(const GemmDesc& d) {
-  return d.gh == 1 && d.gw == 1 && d.hs == 1 && d.ws == 1 && d.ntaps == 1 && d.cs == d.K && d.tap_dy[0] == 0 &&
+  return !d.patch && d.gh == 1 && d.gw == 1 && d.hs == 1 && d.ws == 1 && d.ntaps == 1 && d.cs == d.K && d.tap_dy[0] == 0 &&
          d.tap_dx[0] == 0 && d.tap_w[0] == 0 && d.ho == 1 && d.wo == 1;
 }
 
@@ -247,6 +253,14 @@ size_t conv_input_part_floats(const ConvIn& a, int rows);
 // Identity rows over a node of C channels, each on its own 1 x 1 window:
 // out [rows][C] with out[row][c'] = +-1 at c' = row's channel (rows_per_b = R).
 hipError_t launch_patch_identity(int rows, int R, int C, float* out, hipStream_t st);
+// The same rows written into a wh x ww window of C channels at cell (cy, cx):
+// out [rows][wh][ww][C], sign at the row's channel of that cell, 0 elsewhere.
+hipError_t launch_window_identity(int rows, int R, int C, int wh, int ww, int cy, int cx, float* out,
+                                  hipStream_t st);
+// A window [rows][sh][sw][C] copied into [rows][dh][dw][C] at cell offset (oy, ox),
+// zeros elsewhere (the window must fit).
+hipError_t launch_window_embed(const float* src, int rows, int C, int sh, int sw, int dh, int dw, int oy, int ox,
+                               float* dst, hipStream_t st);
 // The first back-substitution step of footprint identity rows through the start
 // conv, relaxed at the ReLU below it, without a GEMM over the one-hot rows: row
 // (b, sign, pixel p, channel c) gets sign * W[Y][X][c][:] on window cell (Y, X),
@@ -407,6 +421,9 @@ struct NarrowIbp {
 bool ibp_narrow_fits(int batch, int K, const float* W, const float* A, const float* A2);
 int ibp_narrow_slices(int N, int K);
 hipError_t launch_ibp_narrow(NarrowIbp d, int S, hipStream_t st);
+
+// verified[b] = 1 iff every lb[b][i] > 0 (i < m); count[0] (if count) = number of verified inputs.
+hipError_t launch_verify(const float* lb, int batch, int m, int* verified, int* count, hipStream_t st);
 
 // Fixed scratch of the allocation-free entry point (vb_scratch.hip): its size, and
 // its address on the device of stream `st` (the null stream: the current device),

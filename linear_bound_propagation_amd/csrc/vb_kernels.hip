@@ -652,6 +652,63 @@ __global__ void patch_identity_kernel(long long rows, int R, int C, float* __res
   }
 }
 
+// Identity rows (b, sign, p, c) written into a wh x ww window of C channels
+// per row: out[row][Y][X][c'] = sign at (cy, cx, c) and 0 elsewhere.
+__global__ void window_identity_kernel(long long rows, int R, int C, int wh, int ww, int cy, int cx,
+                                       float* __restrict__ out) {
+  const int per = wh * ww * C;
+  const long long total = rows * per;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (long long)gridDim.x * blockDim.x) {
+    const long long row = e / per;
+    const int rem = (int)(e - row * per);
+    const int cell = rem / C, cc = rem - cell * C;
+    const int r = (int)(row % R);
+    const float sg = r < R / 2 ? 1.f : -1.f;
+    out[e] = (cell == cy * ww + cx && r % C == cc) ? sg : 0.f;
+  }
+}
+
+hipError_t launch_window_identity(int rows, int R, int C, int wh, int ww, int cy, int cx, float* out,
+                                  hipStream_t st) {
+  const long long total = (long long)rows * wh * ww * C;
+  if (total <= 0) return hipSuccess;
+  if (cy < 0 || cy >= wh || cx < 0 || cx >= ww) return hipErrorInvalidValue;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(window_identity_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (long long)rows, R, C, wh,
+                     ww, cy, cx, out);
+  return hipGetLastError();
+}
+
+// A window of sh x sw cells copied into a larger dh x dw window at cell offset
+// (oy, ox), zeros elsewhere: dst[row][Y][X][c] = src[row][Y-oy][X-ox][c].
+__global__ void window_embed_kernel(const float* __restrict__ src, long long rows, int C, int sh, int sw, int dh,
+                                    int dw, int oy, int ox, float* __restrict__ dst) {
+  const int per = dh * dw * C;
+  const long long total = rows * per;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (long long)gridDim.x * blockDim.x) {
+    const long long row = e / per;
+    const int rem = (int)(e - row * per);
+    const int cell = rem / C, cc = rem - cell * C;
+    const int Y = cell / dw - oy, X = cell % dw - ox;
+    float v = 0.f;
+    if (Y >= 0 && Y < sh && X >= 0 && X < sw) v = src[(row * sh * sw + (long long)Y * sw + X) * C + cc];
+    dst[e] = v;
+  }
+}
+
+hipError_t launch_window_embed(const float* src, int rows, int C, int sh, int sw, int dh, int dw, int oy, int ox,
+                               float* dst, hipStream_t st) {
+  const long long total = (long long)rows * dh * dw * C;
+  if (total <= 0) return hipSuccess;
+  if (oy < 0 || ox < 0 || oy + sh > dh || ox + sw > dw) return hipErrorInvalidValue;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(window_embed_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, (long long)rows, C, sh, sw,
+                     dh, dw, oy, ox, dst);
+  return hipGetLastError();
+}
+
 hipError_t launch_patch_identity(int rows, int R, int C, float* out, hipStream_t st) {
   const long long total = (long long)rows * C;
   if (total <= 0) return hipSuccess;
@@ -1456,6 +1513,39 @@ hipError_t launch_transpose(const float* src, int batch, int R, int C, float* ds
   if (batch <= 0 || R <= 0 || C <= 0) return hipSuccess;
   dim3 g((C + 31) / 32, (R + 31) / 32, batch);
   hipLaunchKernelGGL(transpose_kernel, g, dim3(256), 0, st, src, R, C, dst);
+  return hipGetLastError();
+}
+
+// Verdict per input: verified[b] = 1 iff lb[b][i] > 0 for every spec i (a NaN
+// bound is not > 0); one workgroup per input.
+__global__ __launch_bounds__(256) void verify_kernel(const float* __restrict__ lb, int m,
+                                                     int* __restrict__ verified) {
+  const int b = blockIdx.x;
+  int ok = 1;
+  for (int i = threadIdx.x; i < m; i += blockDim.x) ok &= (lb[(long long)b * m + i] > 0.f) ? 1 : 0;
+  ok = __syncthreads_and(ok);
+  if (threadIdx.x == 0) verified[b] = ok;
+}
+
+// count[0] = sum of flags[0..n) (one workgroup, fixed order of the partial sums)
+__global__ __launch_bounds__(256) void count_kernel(const int* __restrict__ flags, int n, int* __restrict__ count) {
+  __shared__ int part[256];
+  int s = 0;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) s += flags[i];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) part[threadIdx.x] += part[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) count[0] = part[0];
+}
+
+hipError_t launch_verify(const float* lb, int batch, int m, int* verified, int* count, hipStream_t st) {
+  hipLaunchKernelGGL(verify_kernel, dim3(batch), dim3(256), 0, st, lb, m, verified);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !count) return e;
+  hipLaunchKernelGGL(count_kernel, dim3(1), dim3(256), 0, st, verified, batch, count);
   return hipGetLastError();
 }
 

@@ -121,3 +121,62 @@ def evaluate(wl, lo, hi, b: int, alpha: dict, stop: int = 0) -> torch.Tensor:
     dc, dr = _domain(net, lo, hi, wl.x0, wl.eps, b, stop)
     with torch.no_grad():
         return backward(net, lo, hi, b, len(net.nodes) - 1, C[b], stop, dc, dr, alpha=alpha)
+
+
+def alpha_rows(wl, lo, hi, b: int, start: int, rows, steps: int, lr: float, stop: int = 0,
+               b1=0.9, b2=0.999, adam_eps=1e-8):
+    """alpha-CROWN on arbitrary rows over node `start` for input b: every row is a
+    linear function of that node bounded from below; each row has its own slopes
+    (one per ReLU neuron between `stop` and `start`), initialised with the adaptive
+    CROWN slopes, and `steps` rounds of (evaluate, gradient of the sum of the rows'
+    lower bounds, Adam ascent + clip to [0, 1]) are followed by one evaluation.
+    Rows are independent, so each row's slopes follow the gradient of its own bound.
+    Returns (lower bound per evaluation [steps+1][R], final slopes)."""
+    net = Oracle(wl.nodes)
+    dc, dr = _domain(net, lo, hi, wl.x0, wl.eps, b, stop)
+    rows = torch.as_tensor(rows, dtype=f64)
+    R = rows.shape[0]
+    al = {r: v for r, v in alpha_init(net, lo, hi, b, R).items() if stop < r < start}
+    mom = {k: torch.zeros_like(v) for k, v in al.items()}
+    vel = {k: torch.zeros_like(v) for k, v in al.items()}
+    out = torch.empty((steps + 1, R), dtype=f64)
+    for t in range(1, steps + 1):
+        leaf = {k: v.clone().requires_grad_(True) for k, v in al.items()}
+        lb = backward(net, lo, hi, b, start, rows, stop, dc, dr, alpha=leaf)
+        out[t - 1] = lb.detach()
+        lb.sum().backward()
+        for k in al:
+            g = leaf[k].grad if leaf[k].grad is not None else torch.zeros_like(al[k])
+            al[k], mom[k], vel[k] = adam_ascent_step(al[k], g, mom[k], vel[k], t, lr, b1, b2, adam_eps)
+    with torch.no_grad():
+        out[steps] = backward(net, lo, hi, b, start, rows, stop, dc, dr, alpha=al)
+    return out, al
+
+
+def alpha_intermediate_bounds(wl, steps: int, lr: float, batch_idx=None):
+    """Intermediate bounds by alpha-CROWN (the per-neuron alpha tensors of the page,
+    Sec. 3 and Sec. 4.3, here also on the intermediate layers): IBP first; then for
+    every ReLU input z in topological order that is more than one affine step from
+    the input, its identity rows (+e_j for the lower bound, -e_j for the upper) are
+    optimised with `alpha_rows` over the bounds of the earlier layers, and
+    l_j = max over the iterates of lb(+e_j), u_j = min over the iterates of
+    -lb(-e_j).  Returns (lo, hi) lists [B][*shape] (only inputs in batch_idx refined)."""
+    from .bounds import ibp, _identity_rows, _one_affine_step
+    net = Oracle(wl.nodes)
+    lo, hi = ibp(net, wl.x0, wl.eps)
+    B = lo[0].shape[0]
+    batch_idx = range(B) if batch_idx is None else batch_idx
+    for r in net.relu_nodes():
+        z = net.nodes[r].inputs[0]
+        if z <= 0 or _one_affine_step(net, z, 0):
+            continue
+        shape = net.shape[z]
+        n = int(np.prod(shape))
+        rows = torch.cat([_identity_rows(shape, 1.0).reshape(n, -1), _identity_rows(shape, -1.0).reshape(n, -1)])
+        rows = rows.reshape((2 * n,) + tuple(shape))
+        for b in batch_idx:
+            lbs, _ = alpha_rows(wl, lo, hi, b, z, rows, steps, lr)
+            best = lbs.max(dim=0).values
+            lo[z][b] = best[:n].reshape(shape)
+            hi[z][b] = -best[n:].reshape(shape)
+    return lo, hi

@@ -127,3 +127,65 @@ def test_alpha_upper_bounds_via_negated_specs(lbp):
     ub_alpha = -best.double().cpu()
     ub_crown = -crown_lb
     assert bool((ub_alpha <= ub_crown + 1e-5).all())
+
+
+# ---------------------------------------------------------------------------
+# alpha-CROWN on intermediate bounds (identity rows of every refined layer)
+
+def _alpha_intermediate_check(lbp, wl, steps, batch_idx):
+    from oracle.alpha import alpha_intermediate_bounds, alpha_rows
+    from oracle.bounds import _identity_rows
+    from helpers import nhwc
+    net, x, C = lbp.prepare(wl)
+    ws = net.workspace(net.workspace_size(wl.batch, wl.m, "ibp", alpha_rows=True))
+    lo, hi, _, _ = lbp.ibp(net, x, float(wl.eps), ws=ws)
+    trace = {}
+    lbp.alpha_intermediate(net, x, float(wl.eps), lo, hi, steps, wl.alpha_lr, ws, trace=trace)
+    torch.cuda.synchronize()
+    lo_ref, hi_ref = alpha_intermediate_bounds(wl, steps, wl.alpha_lr, batch_idx=batch_idx)
+    onet = Oracle(wl.nodes)
+    lo_ibp, hi_ibp = ibp(onet, wl.x0, wl.eps)
+    assert list(trace) == lbp.relu_inputs_refined(net)
+    for z, (ls, us) in trace.items():
+        shape = wl.nodes[z].shape
+        n = wl.nodes[z].size
+        # every Adam step of the first refined layer against the oracle's trajectory on
+        # the same (IBP) bounds below it; the final bounds of every layer end to end
+        if z == min(trace):
+            rows = torch.cat([_identity_rows(shape, 1.0).reshape(n, -1), _identity_rows(shape, -1.0).reshape(n, -1)])
+            rows = rows.reshape((2 * n,) + tuple(shape))
+            for b in batch_idx:
+                lbs, _ = alpha_rows(wl, lo_ibp, hi_ibp, b, z, rows, steps, wl.alpha_lr)
+                for t in range(steps + 1):
+                    assert_close(ls[t, b], nhwc(lbs[t, :n].reshape((1,) + tuple(shape)), shape)[0],
+                                 f"l of node {z}, step {t}, input {b}")
+                    assert_close(us[t, b], nhwc(-lbs[t, n:].reshape((1,) + tuple(shape)), shape)[0],
+                                 f"u of node {z}, step {t}, input {b}")
+        assert_close(lo[z][batch_idx], nhwc(lo_ref[z][batch_idx], shape), f"best l of node {z}")
+        assert_close(hi[z][batch_idx], nhwc(hi_ref[z][batch_idx], shape), f"best u of node {z}")
+        # alpha tightens the CROWN iterate (step 0 evaluates the adaptive slopes)
+        assert bool((lo[z] >= ls[0] - 1e-6).all() and (hi[z] <= us[0] + 1e-6).all())
+    return net, lo, hi
+
+
+def test_alpha_intermediate_bounds_mlp(lbp):
+    wl = wk.tiny_mlp([30, 60, 50, 40, 6], 0.06, 41, batch=3)
+    wl.alpha_lr = 0.1
+    print("alpha intermediate bounds, tiny MLP", flush=True)
+    _alpha_intermediate_check(lbp, wl, 8, [0, 1, 2])
+
+
+def test_alpha_intermediate_bounds_config1(lbp):
+    """The 784-100-100-10 workload: alpha on the second layer's 200 identity rows per
+    input, 20 Adam steps, every step compared with the oracle on inputs 0 and 7."""
+    wl = wk.config(1)
+    wl.alpha_lr = 0.1
+    print("alpha intermediate bounds,", wl.name, flush=True)
+    _alpha_intermediate_check(lbp, wl, 20, [0, 7])
+
+
+def test_alpha_intermediate_bounds_small_cnn(lbp):
+    wl = wk.cnn(2, 0.02, 42, convs=((8, 1), (16, 2)), fcs=(20, 5), in_shape=(3, 8, 8), intermediate="ibp")
+    wl.alpha_lr = 0.1
+    print("alpha intermediate bounds, small CNN", flush=True)
+    _alpha_intermediate_check(lbp, wl, 5, [0, 1])

@@ -425,3 +425,32 @@ def test_all_inactive_layer(lbp):
     ref = crown_bounds(wl)
     compare_workload(wl, out, ref)
     assert_close(out["lb"], out["ub"].detach().double().cpu().numpy(), "lb = ub")
+
+
+# ---------------------------------------------------------------------------
+# vb_verify
+
+def test_verify_matches_the_bounds_and_the_oracle(lbp):
+    """The per-input verdict: 1 iff every spec lower bound is positive; on the
+    784-100-100-10 workload some inputs are proved and some are not, and the
+    verdict agrees with the oracle's bounds wherever those are not within the
+    parity tolerance of zero.  NaN and zero bounds do not verify."""
+    from helpers import ATOL, RTOL
+    wl = wk.config(1)
+    net, x, C = lbp.prepare(wl)
+    out = lbp.crown(net, x, float(wl.eps), C, "crown")
+    flags, count = lbp.verify(out["lb"])
+    torch.cuda.synchronize()
+    lb = out["lb"].cpu()
+    want = (lb > 0).all(dim=1).to(torch.int32)
+    assert torch.equal(flags.cpu(), want)
+    assert int(count.item()) == int(want.sum())
+    assert 0 < int(count.item()) < wl.batch
+    ref = crown_bounds(wl)["lb"]
+    clear = (ref.abs() > ATOL + RTOL * ref.abs()).all(dim=1)
+    assert bool(clear.any())
+    assert torch.equal(flags.cpu()[clear].bool(), (ref[clear] > 0).all(dim=1))
+    odd = torch.tensor([[1.0, 2.0], [1.0, 0.0], [float("nan"), 1.0], [3.0, -1e-30]], device=x.device)
+    f2, c2 = lbp.verify(odd)
+    torch.cuda.synchronize()
+    assert f2.cpu().tolist() == [1, 0, 0, 0] and int(c2.item()) == 1
