@@ -151,34 +151,40 @@ def _push(lam: Dict[int, torch.Tensor], k: int, v: torch.Tensor):
 
 def backward(net: Oracle, lo, hi, b: int, start: int, rows: torch.Tensor, stop: int,
              dom_c: torch.Tensor, dom_r: torch.Tensor, alpha: Optional[Dict[int, torch.Tensor]] = None,
-             keep: Optional[dict] = None) -> torch.Tensor:
+             keep: Optional[dict] = None, beta: Optional[Dict[int, torch.Tensor]] = None,
+             splits: Optional[Dict[int, torch.Tensor]] = None) -> torch.Tensor:
     """Lower bound of each row of `rows` (linear functions of node `start`) for input b.
 
-    Lambda starts as `rows` over node `start` with beta = 0 and is pushed to the
-    producers in reverse topological order:
-      Linear:  beta += Lambda b;  Lambda_in += Lambda W
-      Conv:    beta += sum_{c,h,w} Lambda[c,h,w] b_c;  Lambda_in += conv^T(Lambda, W)
+    Lambda starts as `rows` over node `start` with the constant term d = 0 and is
+    pushed to the producers in reverse topological order:
+      Linear:  d += Lambda b;  Lambda_in += Lambda W
+      Conv:    d += sum_{c,h,w} Lambda[c,h,w] b_c;  Lambda_in += conv^T(Lambda, W)
       ReLU:    with Psi = Lambda over the ReLU output, Lambda_z += Psi+ a + Psi- s and
-               beta += Psi- . t  (a replaced by alpha on unstable neurons if given)
+               d += Psi- . t  (a replaced by alpha on unstable neurons if given)
       Add:     Lambda flows unchanged into both inputs
       GAP:     Lambda_in[c,h,w] += Lambda[c] / (H W)
       Flatten: reindex
     At `stop` (the domain) the bound is concretised over the box (dom_c, dom_r).
     `keep`, if given, receives Psi per ReLU node and the final Lambda.
+    Split constraints (beta-CROWN): for ReLU node k, splits[k] holds +1 where the
+    input neuron is constrained to z >= 0, -1 where z <= 0, 0 elsewhere, and
+    beta[k] [R][*shape] >= 0 the rows' multipliers; the Lagrangian term
+    -beta * split * z is added to Lambda over z (for points of the sub-domain it
+    is <= 0, so the bound stays a lower bound there).
     """
     R = rows.shape[0]
     lam: Dict[int, torch.Tensor] = {start: rows}
-    beta = torch.zeros(R, dtype=f64)
+    bias_acc = torch.zeros(R, dtype=f64)
     for k in range(start, stop, -1):
         if k not in lam:
             continue
         L = lam.pop(k)
         nd = net.nodes[k]
         if nd.op == "linear":
-            beta = beta + L @ net.b[k]
+            bias_acc = bias_acc + L @ net.b[k]
             _push(lam, nd.inputs[0], L @ net.W[k])
         elif nd.op == "conv":
-            beta = beta + L.sum(dim=(2, 3)) @ net.b[k]
+            bias_acc = bias_acc + L.sum(dim=(2, 3)) @ net.b[k]
             in_shape = (R,) + net.shape[nd.inputs[0]]
             psi = torch.nn.grad.conv2d_input(in_shape, net.W[k], L, stride=nd.stride, padding=nd.pad)
             _push(lam, nd.inputs[0], psi)
@@ -190,7 +196,10 @@ def backward(net: Oracle, lo, hi, b: int, start: int, rows: torch.Tensor, stop: 
             if keep is not None:
                 keep[k] = L
             lz = torch.where(L >= 0, L * a, L * s)
-            beta = beta + (torch.where(L < 0, L, torch.zeros_like(L)) * t).reshape(R, -1).sum(1)
+            beta_acc = (torch.where(L < 0, L, torch.zeros_like(L)) * t).reshape(R, -1).sum(1)
+            bias_acc = bias_acc + beta_acc
+            if beta is not None and k in beta:
+                lz = lz - beta[k] * splits[k]
             _push(lam, z, lz)
         elif nd.op == "add":
             _push(lam, nd.inputs[0], L)
@@ -206,7 +215,7 @@ def backward(net: Oracle, lo, hi, b: int, start: int, rows: torch.Tensor, stop: 
     assert not lam, "rows reach nodes outside the region bounded by the domain node"
     if keep is not None:
         keep["domain"] = L
-    return concretize(L, beta, dom_c, dom_r)
+    return concretize(L, bias_acc, dom_c, dom_r)
 
 
 def concretize(L: torch.Tensor, beta: torch.Tensor, c: torch.Tensor, r: torch.Tensor) -> torch.Tensor:
