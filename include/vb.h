@@ -79,6 +79,12 @@ typedef struct {
 #define VB_INTERSECT_IBP 16  /* flag for CROWN / HYBRID: each CROWN intermediate  */
                              /* bound is intersected with the node's IBP bound    */
                              /* (l = max, u = min) before later layers use it     */
+#define VB_UNSTABLE_ONLY 64  /* flag for CROWN / HYBRID: rows only for the neurons */
+                             /* of a Linear ReLU input that its IBP bounds leave  */
+                             /* unstable (l < 0 < u); the others keep their IBP   */
+                             /* bounds (their relaxation is already exact).  The  */
+                             /* call then SYNCHRONISES the stream once per such   */
+                             /* layer (launches are sized to the largest count)   */
 #define VB_ALPHA_ROWS    32  /* flag for vb_workspace_size: also enough for       */
                              /* vb_alpha_step_rows on the identity rows of every  */
                              /* ReLU input (alpha-CROWN intermediate bounds)      */
@@ -224,6 +230,34 @@ vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float* C, int32_
                         float* lb_out, float* best_lb,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* Split constraints of branch-and-bound sub-domains (beta-CROWN; complete
+ * verification, Sec. 2.2 and Sec. 4.3 of the page).  Each batch element is one
+ * sub-domain of an input.  Per node (host arrays of device pointers, entries of
+ * non-ReLU nodes ignored); for ReLU node k over input node z:
+ *   split[k]:  [batch][size_z] +1 where the sub-domain requires z_j >= 0, -1
+ *              where it requires z_j <= 0, 0 elsewhere; NULL: no constraint at k;
+ *   beta[k]:   [batch][R][size_z] the rows' Lagrange multipliers (>= 0; only
+ *              entries of split neurons are read), and beta_m[k], beta_v[k]
+ *              their Adam moments (same shape).
+ * With a beta state, every row bounds min C f(x) - sum_j beta_j split_j z_j(x)
+ * over the relaxed network (a lower bound of C f on the sub-domain, where
+ * split_j z_j >= 0), and a step raises beta with alpha by projected Adam
+ * (beta >= 0; gradient -split * the adjoint over z).  The node bounds passed
+ * with it must already be clamped to the splits (vb_apply_splits). */
+typedef struct {
+  const float* const* split;
+  float* const* beta;
+  float* const* beta_m;
+  float* const* beta_v;
+} vb_beta;
+
+/* Clamp node bounds to split constraints, in place: for every ReLU node k with
+ * split[k] != NULL, over its input node z: node_lo[z] = max(node_lo[z], 0)
+ * where split > 0, node_hi[z] = min(node_hi[z], 0) where split < 0
+ * ([batch][size_z] each). */
+vb_status vb_apply_splits(const vb_graph* g, int32_t batch, const float* const* split, float* const* node_lo,
+                          float* const* node_hi, void* stream);
+
 /* alpha-CROWN step on rows over any Linear / Conv node `start` of a chain
  * network (the per-neuron alpha tensors of Sec. 3 and Sec. 4.3 of the page, on
  * intermediate layers as well as on the specification).  Rows:
@@ -239,6 +273,10 @@ vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float* C, int32_
  *              best_lb / best_ub the best over the steps (step 1 sets them; later
  *              steps take the max of l and the min of u).  Any of the four may
  *              be NULL (not all).
+ * beta: NULL, or the split constraints and multipliers of sub-domains
+ * (vb_beta; dense alpha layout only; the workspace must then also hold
+ * batch * R * (widest ReLU node below start) floats: vb_bab_workspace_size
+ * covers it for spec rows).
  * Every row climbs its own bound: the objective is the sum of the rows' lower
  * bounds, whose gradient with respect to a row's slopes is that row's own.
  * The state of ReLU nodes at or above `start` is not used (may be NULL).  The
@@ -247,11 +285,46 @@ vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float* C, int32_
 vb_status vb_alpha_step_rows(const vb_graph* g, int32_t batch, int32_t start, const float* C, int32_t m,
                              const float* const* node_lo, const float* const* node_hi,
                              const float* x_center, const float* x_radius, float eps,
-                             const vb_alpha_compact* compact,
+                             const vb_alpha_compact* compact, const vb_beta* beta,
                              float* const* alpha, float* const* adam_m, float* const* adam_v,
                              int32_t step, float lr, float beta1, float beta2, float adam_eps,
                              float* lb_out, float* best_lb, float* ub_out, float* best_ub,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* Branch and bound with beta-CROWN (complete verification of one input: the
+ * page's Sec. 2.2 and Sec. 4.3 prove a ResNet this way).  Sub-domains are sets
+ * of ReLU split constraints, bounded `batch` at a time as the batch elements of
+ * one alpha-beta-CROWN run (intermediate bounds: the root's, clamped to the
+ * splits; spec bounds: `steps` projected-Adam steps on alpha and beta from the
+ * adaptive slopes and beta = 0, then one evaluation, best iterate kept).  The
+ * queue is first-in first-out; a sub-domain is proved when every spec lower
+ * bound is > 0, otherwise it is split on the unstable neuron with the largest
+ * score sum over its unproved rows of max(-Psi_j, 0) * t_j (Psi over the ReLU
+ * output, t = -u l / (u - l)), ties to the lowest (node, neuron), into the
+ * sub-domains z_j >= 0 then z_j <= 0, appended to the queue.
+ *   node_lo / node_hi: the root's bounds of every node [1][size] (device; e.g.
+ *                      vb_crown with batch 1), not modified;
+ *   C: [m][n_out] spec rows of the input; x_center [n0], x_radius [n0] or NULL;
+ *   verdict (host): 1 when every sub-domain is proved, 0 when the search
+ *                   stopped undecided (budget spent, or a sub-domain with no
+ *                   unstable neuron left);
+ *   domains (host): sub-domains bounded; root_lb (device [m] or NULL): the
+ *                   root's best bound.
+ * The graph must be a chain (as for vb_alpha_step).  This call SYNCHRONISES
+ * `stream` once per round (the bounds decide the next sub-domains); it
+ * allocates nothing: the workspace must hold vb_bab_workspace_size bytes. */
+typedef struct {
+  int32_t steps;        /* Adam steps per sub-domain (then one evaluation) */
+  float lr, beta1, beta2, adam_eps;
+  int32_t batch;        /* sub-domains bounded together */
+  int32_t max_domains;  /* sub-domains bounded before the search gives up */
+} vb_bab_params;
+
+vb_status vb_bab_workspace_size(const vb_graph* g, int32_t m, int32_t batch, size_t* bytes);
+vb_status vb_bab(const vb_graph* g, const float* x_center, const float* x_radius, float eps,
+                 const float* C, int32_t m, const float* const* node_lo, const float* const* node_hi,
+                 const vb_bab_params* params, int32_t* verdict, int32_t* domains, float* root_lb,
+                 void* ws, size_t ws_bytes, void* stream);
 
 /* The whole bound computation for one batch: IBP for every node, then the
  * intermediate bounds of every ReLU input by `method`, overwriting node_lo /

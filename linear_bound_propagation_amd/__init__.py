@@ -23,7 +23,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libvbprop.so")
 
 VB_INPUT, VB_LINEAR, VB_CONV2D, VB_RELU, VB_ADD, VB_GAP, VB_FLATTEN = range(7)
-METHODS = {"ibp": 0, "crown": 1, "hybrid": 2, "crown+ibp": 1 | 16, "hybrid+ibp": 2 | 16}
+METHODS = {"ibp": 0, "crown": 1, "hybrid": 2, "crown+ibp": 1 | 16, "hybrid+ibp": 2 | 16,
+           "crown+unstable": 1 | 64, "hybrid+unstable": 2 | 64, "crown+ibp+unstable": 1 | 16 | 64,
+           "hybrid+ibp+unstable": 2 | 16 | 64}
 VB_ALPHA_ROWS = 32
 STATUS = {0: "VB_OK", -1: "VB_EINVAL", -2: "VB_ESHAPE", -3: "VB_ENOMEM", -4: "VB_EDEVICE",
           -5: "VB_EUNSUPPORTED"}
@@ -31,7 +33,8 @@ _OPS = {"input": VB_INPUT, "linear": VB_LINEAR, "conv": VB_CONV2D, "relu": VB_RE
         "gap": VB_GAP, "flatten": VB_FLATTEN}
 
 EXPORTS = ["vb_last_error", "vb_workspace_size", "vb_ibp", "vb_crown_backward", "vb_concretize",
-           "vb_alpha_layout", "vb_alpha_init", "vb_alpha_step", "vb_alpha_step_rows", "vb_crown", "vb_crown_noalloc", "vb_verify",
+           "vb_alpha_layout", "vb_alpha_init", "vb_alpha_step", "vb_alpha_step_rows", "vb_apply_splits",
+           "vb_bab_workspace_size", "vb_bab", "vb_crown", "vb_crown_noalloc", "vb_verify",
            "vb_profile_start", "vb_profile_stop"]
 # host-only helpers declared in include/vb_testing.h (used by the CPU tests)
 TESTING_EXPORTS = ["vb_testing_fastdiv", "vb_testing_conv_tile_n", "vb_testing_identity_path"]
@@ -46,6 +49,17 @@ class vb_node(ctypes.Structure):
 
 class vb_graph(ctypes.Structure):
     _fields_ = [("n_nodes", ctypes.c_int32), ("nodes", ctypes.POINTER(vb_node))]
+
+
+class vb_beta(ctypes.Structure):
+    _fields_ = [("split", ctypes.POINTER(ctypes.c_void_p)), ("beta", ctypes.POINTER(ctypes.c_void_p)),
+                ("beta_m", ctypes.POINTER(ctypes.c_void_p)), ("beta_v", ctypes.POINTER(ctypes.c_void_p))]
+
+
+class vb_bab_params(ctypes.Structure):
+    _fields_ = [("steps", ctypes.c_int32), ("lr", ctypes.c_float), ("beta1", ctypes.c_float),
+                ("beta2", ctypes.c_float), ("adam_eps", ctypes.c_float), ("batch", ctypes.c_int32),
+                ("max_domains", ctypes.c_int32)]
 
 
 class vb_alpha_compact(ctypes.Structure):
@@ -79,8 +93,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vb_alpha_step.argtypes = [G, i32, P, i32, PP, PP, P, P, f32, AC, PP, PP, PP, i32, f32, f32, f32, f32,
                                   P, P, P, sz, P]
     lib.vb_alpha_step_rows.restype = i32
-    lib.vb_alpha_step_rows.argtypes = [G, i32, i32, P, i32, PP, PP, P, P, f32, AC, PP, PP, PP, i32, f32, f32, f32, f32,
-                                       P, P, P, P, P, sz, P]
+    BT = ctypes.POINTER(vb_beta)
+    lib.vb_alpha_step_rows.argtypes = [G, i32, i32, P, i32, PP, PP, P, P, f32, AC, BT, PP, PP, PP, i32, f32, f32, f32,
+                                       f32, P, P, P, P, P, sz, P]
+    lib.vb_apply_splits.restype = i32
+    lib.vb_apply_splits.argtypes = [G, i32, PP, PP, PP, P]
+    lib.vb_bab_workspace_size.restype = i32
+    lib.vb_bab_workspace_size.argtypes = [G, i32, i32, ctypes.POINTER(sz)]
+    lib.vb_bab.restype = i32
+    lib.vb_bab.argtypes = [G, P, P, f32, P, i32, PP, PP, ctypes.POINTER(vb_bab_params), ctypes.POINTER(i32),
+                           ctypes.POINTER(i32), P, P, sz, P]
     lib.vb_crown.restype = i32
     lib.vb_crown.argtypes = [G, i32, P, P, f32, i32, i32, PP, PP, P, i32, P, P, P, P, P, sz, P]
     lib.vb_verify.restype = i32
@@ -384,16 +406,50 @@ def alpha_step(net: DeviceNet, C: torch.Tensor, lo, hi, x_center: torch.Tensor, 
 def alpha_step_rows(net: DeviceNet, start: int, C: Optional[torch.Tensor], lo, hi, x_center: torch.Tensor,
                     eps: float, alpha, adam_m, adam_v, step: int, lr: float, ws: torch.Tensor, lb_out=None,
                     best_lb=None, ub_out=None, best_ub=None, beta1: float = 0.9, beta2: float = 0.999,
-                    adam_eps: float = 1e-8, x_radius=None, layout: Optional[AlphaLayout] = None):
+                    adam_eps: float = 1e-8, x_radius=None, layout: Optional[AlphaLayout] = None,
+                    beta=None):
     """vb_alpha_step_rows: one alpha-CROWN step on spec rows C over node `start`, or
-    (C None) on the identity rows of `start` (l and u of every neuron)."""
+    (C None) on the identity rows of `start` (l and u of every neuron).  beta: None, or
+    (split, beta, beta_m, beta_v) per-node lists (split constraints of sub-domains)."""
     batch = x_center.shape[0]
     m = 0 if C is None else C.shape[1]
+    bref = None
+    if beta is not None:
+        arrs = [_ptr_array(a) for a in beta]
+        bst = vb_beta(*[ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p)) for a in arrs])
+        bref = ctypes.byref(bst)
     _check(lib().vb_alpha_step_rows(net.gp, batch, start, _ptr(C), m, _ptr_array(lo), _ptr_array(hi),
-                                    _ptr(x_center), _ptr(x_radius), float(eps), _compact(layout),
+                                    _ptr(x_center), _ptr(x_radius), float(eps), _compact(layout), bref,
                                     _ptr_array(alpha), _ptr_array(adam_m), _ptr_array(adam_v), step, lr, beta1, beta2,
                                     adam_eps, _ptr(lb_out), _ptr(best_lb), _ptr(ub_out), _ptr(best_ub), _ptr(ws),
                                     ws.numel(), _stream()), "vb_alpha_step_rows")
+
+
+def apply_splits(net: DeviceNet, split, lo, hi):
+    """vb_apply_splits: clamp the bounds of split neurons (in place)."""
+    batch = lo[1].shape[0]
+    _check(lib().vb_apply_splits(net.gp, batch, _ptr_array(split), _ptr_array(lo), _ptr_array(hi), _stream()),
+           "vb_apply_splits")
+
+
+def bab(net: DeviceNet, x_center: torch.Tensor, eps: float, C: torch.Tensor, lo, hi, steps: int = 20,
+        lr: float = 0.1, batch: int = 8, max_domains: int = 256, x_radius=None, ws: torch.Tensor = None,
+        beta1: float = 0.9, beta2: float = 0.999, adam_eps: float = 1e-8):
+    """vb_bab: branch and bound with beta-CROWN for ONE input: x_center [n0] (or [1][n0]),
+    C [m][n_out], lo / hi the root's node bounds [1][size].  Returns (verified (bool),
+    sub-domains bounded, root best bound [m])."""
+    m = C.shape[-2] if C.dim() == 3 else C.shape[0]
+    params = vb_bab_params(steps, lr, beta1, beta2, adam_eps, batch, max_domains)
+    if ws is None:
+        need = ctypes.c_size_t(0)
+        _check(lib().vb_bab_workspace_size(net.gp, m, batch, ctypes.byref(need)), "vb_bab_workspace_size")
+        ws = net.workspace(int(need.value))
+    verdict, doms = ctypes.c_int32(), ctypes.c_int32()
+    root = torch.empty(m, device=net.device)
+    _check(lib().vb_bab(net.gp, _ptr(x_center), _ptr(x_radius), float(eps), _ptr(C), m, _ptr_array(lo),
+                        _ptr_array(hi), ctypes.byref(params), ctypes.byref(verdict), ctypes.byref(doms), _ptr(root),
+                        _ptr(ws), ws.numel(), _stream()), "vb_bab")
+    return bool(verdict.value), int(doms.value), root
 
 
 def relu_inputs_refined(net: DeviceNet):

@@ -292,6 +292,14 @@ struct Backward {
   // concretising ([batch][R][size_stop] and [batch][R], whole batch)
   float* a_out = nullptr;
   float* bias_out = nullptr;
+  // split constraints of branch-and-bound sub-domains with their multipliers
+  // (per ReLU node: split [batch][size], beta [batch][R][size]), or NULL
+  const vb_beta* beta = nullptr;
+  // selected identity rows over a Linear start (whole batch): neuron lists
+  // [batch][n_start], counts [batch], U rows per sign per input
+  const int* sel = nullptr;
+  const int* cnt = nullptr;
+  int U = 0;
 
   int alloc() {
     for (int i = 0; i < NPOOL; ++i)
@@ -342,6 +350,11 @@ struct BwdCall {
   int split;        // 1: rows +C and -C (2m rows per element); 0: +C only
   int b0, cb;       // batch offset and chunk size
   int batch_total;
+  // selected identity rows (Linear start): neuron list [cb][n_start] and counts
+  // [cb] of this chunk, U rows per sign per input; NULL: every neuron
+  const int* sel = nullptr;
+  const int* cnt = nullptr;
+  int U = 0;
 };
 
 vb_status effective_bias(Backward& B, const Graph& G, int z, const float*& bias) {
@@ -1251,9 +1264,15 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
       if (s) return s;
       const long long off = chunk_off(z);
       HIPCHK(launch_identity_linear(S.W, (int)S.size, (int)G.n[z].size, S.b, B.lo[z] + off, B.hi[z] + off, bias_z,
-                                    G.n[z].c, c.cb, B.pool[b], B.rowacc, B.st));
+                                    G.n[z].c, c.cb, B.pool[b], B.rowacc, B.st, c.sel, c.cnt, c.U));
       lam[z] = b;
       from = z;
+    } else if (c.sel) {
+      // selected rows are written out (2U per input) with their bias terms
+      const int b = B.alloc();
+      if (b < 0) return fail(VB_EUNSUPPORTED, "internal: lambda pool exhausted at node %d", c.start);
+      HIPCHK(launch_select_fill(c.cb, (int)S.size, c.U, c.sel, c.cnt, bias, S.c, B.pool[b], B.rowacc, B.st));
+      lam[c.start] = b;
     } else {
       HIPCHK(launch_identity_bias(c.cb, (int)S.size, bias, S.c, B.rowacc, B.st));
       lam[c.start] = IDENT;
@@ -1465,6 +1484,12 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
                                   : (double)rows * nd.c * tn.c * nd.kh * nd.kw * nd.h * nd.w / descs.size();
           vb_status s = run_gemm_reduce(B, d, rows, P, reduce, 2.0 * macs);
           if (s) return s;
+        }
+        if (epi == E_RELAX && B.beta && B.beta->split && B.beta->split[t] && B.beta->beta && B.beta->beta[t]) {
+          // split constraints at this ReLU: Lambda over z -= beta * split (and its bias terms)
+          const long long nz = G.n[z].size;
+          HIPCHK(launch_beta_apply(B.pool[outb], rows, (int)R, (int)nz, B.beta->beta[t] + (long long)c.b0 * R * nz,
+                                   B.beta->split[t] + (long long)c.b0 * nz, bias, G.n[z].c, B.rowacc, B.st));
         }
         B.release(cur);
       }
@@ -1806,6 +1831,11 @@ vb_status backward_all(Backward& B, int start, int stop, const float* C, int m, 
     c.b0 = b0;
     c.cb = n;
     c.batch_total = batch;
+    if (B.sel) {
+      c.sel = B.sel + (long long)b0 * B.G.n[start].size;
+      c.cnt = B.cnt + b0;
+      c.U = B.U;
+    }
     vb_status s = backward_chunk(B, c, R);
     if (s) return s;
     s = after(B.rowacc, b0, n);
@@ -2008,14 +2038,24 @@ vb_status check_domain(const float* xc) {
 
 extern "C" const char* vb_last_error(void) { return g_err.c_str(); }
 
-static size_t crown_workspace(const Graph& G, int batch, int m, int method, int region_start) {
+// Ints kept after the weight copies by unstable-only rows: per input a neuron
+// ranking and a neuron list over the widest node, and a count.
+static size_t select_floats(const Graph& G, int batch) {
+  long long n = 0;
+  for (const NodeInfo& nd : G.n) n = std::max(n, nd.size);
+  return 2 * (align_up((size_t)batch * n * 4) / 4) + align_up((size_t)batch * 4) / 4;
+}
+
+static size_t crown_workspace(const Graph& G, int batch, int m, int method, int region_start,
+                              bool unstable_only = false) {
   size_t best = 0;
+  const size_t reserved = wt_floats(G) + (unstable_only ? select_floats(G, batch) : 0);
   auto consider = [&](int start, int stop, long long R, bool spec) {
     long long maxw, ppb;
     if (spec || (!patch_requirements(G, start, stop, R, maxw, ppb) && !window_requirements(G, start, stop, R, maxw, ppb)))
       bwd_requirements(G, start, stop, R, maxw, ppb);
     if (spec) maxw = std::max(maxw, G.n[start].size);
-    best = std::max(best, layout_for(maxw, ppb, R, batch, wt_floats(G), stop > 0 ? G.n[stop].size : 0,
+    best = std::max(best, layout_for(maxw, ppb, R, batch, reserved, stop > 0 ? G.n[stop].size : 0,
                                      region_max_size(G, start, stop)).bytes);
   };
   const int L = G.L;
@@ -2039,7 +2079,8 @@ static size_t crown_workspace(const Graph& G, int batch, int m, int method, int 
 namespace {
 bool alpha_chain(const Graph& G, std::vector<std::pair<int, int>>& chain);
 size_t alpha_workspace(const Graph& G, int batch, int m, const int* width = nullptr);
-size_t alpha_workspace_at(const Graph& G, int batch, int start, long long R, bool spec, const int* width);
+size_t alpha_workspace_at(const Graph& G, int batch, int start, long long R, bool spec, const int* width,
+                          bool with_beta = false);
 vb_status check_compact(const Graph& G, int batch, int m, const vb_alpha_compact* c);
 }  // namespace
 
@@ -2051,11 +2092,12 @@ extern "C" vb_status vb_workspace_size(const vb_graph* g, int32_t batch, int32_t
   if (!bytes) return fail(VB_EINVAL, "bytes is NULL");
   if (batch <= 0 || m < 0) return fail(VB_EINVAL, "batch must be > 0 and m >= 0");
   const bool alpha_rows = (method & VB_ALPHA_ROWS) != 0;
-  method &= ~(VB_INTERSECT_IBP | VB_ALPHA_ROWS);
+  const bool unstable_only = (method & VB_UNSTABLE_ONLY) != 0;
+  method &= ~(VB_INTERSECT_IBP | VB_ALPHA_ROWS | VB_UNSTABLE_ONLY);
   if (method < VB_METHOD_IBP || method > VB_METHOD_HYBRID) return fail(VB_EINVAL, "unknown method %d", method);
   if (method == VB_METHOD_HYBRID && (region_start <= 0 || region_start >= G.L))
     return fail(VB_EINVAL, "region_start %d out of range", region_start);
-  *bytes = std::max(crown_workspace(G, batch, m, method, region_start), ibp_workspace(G, batch));
+  *bytes = std::max(crown_workspace(G, batch, m, method, region_start, unstable_only), ibp_workspace(G, batch));
   std::vector<std::pair<int, int>> chain;
   if (m > 0 && alpha_chain(G, chain)) *bytes = std::max(*bytes, alpha_workspace(G, batch, m));
   if (alpha_rows && alpha_chain(G, chain)) {
@@ -2123,8 +2165,12 @@ static vb_status crown_backward_impl(const Graph& G, int batch, int start, int s
                                      float* ub, void* ws, size_t ws_bytes, hipStream_t st, float* a_out = nullptr,
                                      float* bias_out = nullptr, const float* const* alpha = nullptr,
                                      bool intersect = false, const vb_alpha_compact* compact = nullptr,
-                                     bool weights_ready = false) {
+                                     bool weights_ready = false, const int* sel = nullptr, const int* cnt = nullptr,
+                                     int U = 0, size_t extra_reserved = 0) {
   Backward B{G, st, lo, hi, dom};
+  B.sel = sel;
+  B.cnt = cnt;
+  B.U = U;
   B.a_out = a_out;
   B.bias_out = bias_out;
   B.alpha = alpha;
@@ -2135,11 +2181,17 @@ static vb_status crown_backward_impl(const Graph& G, int batch, int start, int s
   vb_status s = prepare_weights(G, (char*)ws, st, B.wt, B.beff, !weights_ready);
   if (s) return s;
   const bool lower_only = C && !ub;
-  const long long R = C ? (lower_only ? m : 2LL * m) : 2LL * G.n[start].size;
+  const long long R = C ? (lower_only ? m : 2LL * m) : (sel ? 2LL * U : 2LL * G.n[start].size);
   const int half = (int)(R / 2);
-  return backward_all(B, start, stop, C, m, lower_only ? 0 : 1, batch, R, (char*)ws, ws_bytes, wt_floats(G),
-                      [&](float* acc, int b0, int cb) -> vb_status {
-                        if (lower_only) {
+  const int n_start = (int)G.n[start].size;
+  return backward_all(B, start, stop, C, m, lower_only ? 0 : 1, batch, R, (char*)ws, ws_bytes,
+                      wt_floats(G) + extra_reserved, [&](float* acc, int b0, int cb) -> vb_status {
+                        if (sel) {
+                          HIPCHK(launch_finish_select(acc, cb, U, n_start, sel + (long long)b0 * n_start, cnt + b0,
+                                                      lb ? lb + (long long)b0 * n_start : nullptr,
+                                                      ub ? ub + (long long)b0 * n_start : nullptr, intersect ? 1 : 0,
+                                                      st));
+                        } else if (lower_only) {
                           HIPCHK(launch_finish_lower(acc, (long long)cb * m, lb ? lb + (long long)b0 * m : nullptr,
                                                      nullptr, 0, st));
                         } else {
@@ -2213,9 +2265,11 @@ extern "C" vb_status vb_crown(const vb_graph* g, int32_t batch, const float* x_c
   if (!x_radius && !(eps >= 0.f)) return fail(VB_EINVAL, "eps must be >= 0");
   if (!node_lo || !node_hi) return fail(VB_EINVAL, "node_lo/node_hi arrays are NULL");
   const bool intersect = (method & VB_INTERSECT_IBP) != 0;
-  method &= ~VB_INTERSECT_IBP;
+  const bool unstable_only = (method & VB_UNSTABLE_ONLY) != 0;
+  method &= ~(VB_INTERSECT_IBP | VB_UNSTABLE_ONLY);
   if (method < VB_METHOD_IBP || method > VB_METHOD_HYBRID) return fail(VB_EINVAL, "unknown method %d", method);
   if (intersect && method == VB_METHOD_IBP) return fail(VB_EINVAL, "VB_INTERSECT_IBP needs CROWN or HYBRID");
+  if (unstable_only && method == VB_METHOD_IBP) return fail(VB_EINVAL, "VB_UNSTABLE_ONLY needs CROWN or HYBRID");
   if (method == VB_METHOD_HYBRID && (region_start <= 0 || region_start >= G.L))
     return fail(VB_EINVAL, "region_start %d out of range", region_start);
   if (C && m <= 0) return fail(VB_EINVAL, "m must be positive with C");
@@ -2223,7 +2277,8 @@ extern "C" vb_status vb_crown(const vb_graph* g, int32_t batch, const float* x_c
   for (size_t k = 1; k < G.n.size(); ++k)
     if (!node_lo[k] || !node_hi[k]) return fail(VB_EINVAL, "node %zu: bounds storage is NULL", k);
   {
-    const size_t need = crown_workspace(G, 1, C ? m : 0, method, region_start);
+    const size_t need = crown_workspace(G, 1, C ? m : 0, method, region_start, false) +
+                        (unstable_only ? 4 * select_floats(G, batch) : 0);
     if (ws_bytes < need)
       return fail(VB_ENOMEM, "workspace of %zu bytes is too small: one batch element needs %zu", ws_bytes, need);
   }
@@ -2248,8 +2303,31 @@ extern "C" vb_status vb_crown(const vb_graph* g, int32_t batch, const float* x_c
       if (G.n[r].op != VB_RELU) continue;
       const int z = G.n[r].in0;
       if (z <= stop || one_affine_step(G, z, stop)) continue;
+      if (unstable_only && G.n[z].op == VB_LINEAR) {
+        // rows only for the neurons the bounds so far (IBP) leave unstable, listed on
+        // the device; the launches are sized to the largest count over the batch,
+        // which is read back here (one synchronisation per layer)
+        const long long n = G.n[z].size, nmax = (long long)(select_floats(G, batch) - align_up((size_t)batch * 4) / 4) /
+                                                (2 * batch);
+        int* idx = (int*)((char*)ws + align_up(wt_floats(G) * 4));
+        int* sel = idx + align_up((size_t)batch * nmax * 4) / 4;
+        int* cnt = sel + align_up((size_t)batch * nmax * 4) / 4;
+        HIPCHK(launch_alpha_layout(node_lo[z], node_hi[z], batch, n, idx, cnt, st));
+        HIPCHK(launch_rank_to_list(idx, batch, (int)n, sel, st));
+        std::vector<int> hc(batch);
+        HIPCHK(hipMemcpyAsync(hc.data(), cnt, (size_t)batch * 4, hipMemcpyDeviceToHost, st));
+        HIPCHK(hipStreamSynchronize(st));
+        const int U = *std::max_element(hc.begin(), hc.end());
+        if (U == 0) continue;  // every neuron stable: the IBP bounds stay
+        s = crown_backward_impl(G, batch, z, stop, nullptr, 0, node_lo, node_hi, dom, node_lo[z], node_hi[z], ws,
+                                ws_bytes, st, nullptr, nullptr, nullptr, intersect, nullptr, true, sel, cnt, U,
+                                select_floats(G, batch));
+        if (s) return s;
+        continue;
+      }
       s = crown_backward_impl(G, batch, z, stop, nullptr, 0, node_lo, node_hi, dom, node_lo[z], node_hi[z], ws,
-                              ws_bytes, st, nullptr, nullptr, nullptr, intersect, nullptr, true);
+                              ws_bytes, st, nullptr, nullptr, nullptr, intersect, nullptr, true, nullptr, nullptr, 0,
+                              unstable_only ? select_floats(G, batch) : 0);
       if (s) return s;
     }
   }
@@ -2354,17 +2432,26 @@ size_t alpha_psi_floats(const Graph& G, long long rows, const int* width, int st
 
 // Workspace of an alpha step on R rows per batch element over node `start`
 // (spec rows widen Lambda to the start node).
-size_t alpha_workspace_at(const Graph& G, int batch, int start, long long R, bool spec, const int* width) {
+// The widest ReLU node below `start`.
+long long relu_max_size(const Graph& G, int start) {
+  long long m = 0;
+  for (int k = 0; k < start && k < (int)G.n.size(); ++k)
+    if (G.n[k].op == VB_RELU) m = std::max(m, G.n[k].size);
+  return m;
+}
+
+size_t alpha_workspace_at(const Graph& G, int batch, int start, long long R, bool spec, const int* width,
+                          bool with_beta) {
   long long maxw, ppb;
   bwd_requirements(G, start, 0, R, maxw, ppb);
   if (spec) maxw = std::max(maxw, G.n[start].size);
-  return layout_for(maxw, ppb, R, batch, wt_floats(G) + alpha_psi_floats(G, (long long)batch * R, width, start),
-                    0, region_max_size(G, start, 0))
-      .bytes;
+  size_t extra = wt_floats(G) + alpha_psi_floats(G, (long long)batch * R, width, start);
+  if (with_beta) extra += align_up((size_t)batch * R * relu_max_size(G, start) * 4) / 4;
+  return layout_for(maxw, ppb, R, batch, extra, 0, region_max_size(G, start, 0)).bytes;
 }
 
 size_t alpha_workspace(const Graph& G, int batch, int m, const int* width) {
-  return alpha_workspace_at(G, batch, G.L, m, true, width);
+  return alpha_workspace_at(G, batch, G.L, m, true, width, false);
 }
 
 }  // namespace
@@ -2449,8 +2536,9 @@ extern "C" vb_status vb_alpha_init(const vb_graph* g, int32_t batch, int32_t m, 
 extern "C" vb_status vb_alpha_step_rows(const vb_graph* g, int32_t batch, int32_t start, const float* C, int32_t m,
                                         const float* const* node_lo, const float* const* node_hi,
                                         const float* x_center, const float* x_radius, float eps,
-                                        const vb_alpha_compact* compact, float* const* alpha, float* const* adam_m,
-                                        float* const* adam_v, int32_t step, float lr, float beta1, float beta2,
+                                        const vb_alpha_compact* compact, const vb_beta* beta, float* const* alpha,
+                                        float* const* adam_m, float* const* adam_v, int32_t step, float lr,
+                                        float beta1, float beta2,
                                         float adam_eps, float* lb_out, float* best_lb, float* ub_out, float* best_ub,
                                         void* ws, size_t ws_bytes, void* stream) {
   Graph G;
@@ -2475,6 +2563,15 @@ extern "C" vb_status vb_alpha_step_rows(const vb_graph* g, int32_t batch, int32_
   std::vector<std::pair<int, int>> chain;
   if (!alpha_chain(G, chain)) return fail(VB_EUNSUPPORTED, "alpha-CROWN needs a chain of Linear/Conv + ReLU nodes");
   if (compact && (s = check_compact(G, batch, (int)R, compact))) return s;
+  if (beta) {
+    if (compact) return fail(VB_EUNSUPPORTED, "split constraints need the dense alpha layout");
+    if (!beta->split || !beta->beta) return fail(VB_EINVAL, "beta state with NULL split or beta arrays");
+    if (step > 0 && (!beta->beta_m || !beta->beta_v)) return fail(VB_EINVAL, "beta Adam state arrays are NULL");
+    for (size_t k = 0; k < G.n.size() && (int)k < start; ++k)
+      if (G.n[k].op == VB_RELU && beta->split[k] &&
+          (!beta->beta[k] || (step > 0 && (!beta->beta_m[k] || !beta->beta_v[k]))))
+        return fail(VB_EINVAL, "ReLU node %zu: split without beta / beta Adam state", k);
+  }
   for (size_t k = 0; k < G.n.size() && (int)k < start; ++k) {
     if (G.n[k].op != VB_RELU) continue;
     const int z = G.n[k].in0;
@@ -2484,7 +2581,7 @@ extern "C" vb_status vb_alpha_step_rows(const vb_graph* g, int32_t batch, int32_
       return fail(VB_EINVAL, "ReLU node %zu: alpha / adam state missing", k);
   }
   if (!ws) return fail(VB_EINVAL, "workspace is NULL");
-  const size_t need = alpha_workspace_at(G, batch, start, R, !ident, compact ? compact->width : nullptr);
+  const size_t need = alpha_workspace_at(G, batch, start, R, !ident, compact ? compact->width : nullptr, beta != nullptr);
   if (ws_bytes < need)
     return fail(VB_ENOMEM, "alpha step needs %zu bytes of workspace for the whole batch (got %zu)", need, ws_bytes);
   hipStream_t st = (hipStream_t)stream;
@@ -2511,6 +2608,13 @@ extern "C" vb_status vb_alpha_step_rows(const vb_graph* g, int32_t batch, int32_
     al[k] = (compact && G.n[k].op == VB_RELU && compact->width[k] == 0) ? nullptr : alpha[k];
   B.alpha = al.data();
   B.psi_keep = psi.data();
+  B.beta = beta;
+  // adjoint over a split ReLU input (beta's gradient), [rows][widest ReLU node]
+  float* gzbuf = nullptr;
+  if (beta) {
+    gzbuf = (float*)(base + off);
+    off += align_up((size_t)rows * relu_max_size(G, start) * 4);
+  }
   if (compact) {
     B.aidx = compact->index;
     B.awidth = compact->width;
@@ -2625,11 +2729,23 @@ extern "C" vb_status vb_alpha_step_rows(const vb_graph* g, int32_t batch, int32_
     a.bc2 = d.bc2;
     a.adam_eps = d.adam_eps;
     a.out = d.out;
+    const bool split_here = beta && beta->split[r] && gzbuf;
+    if (split_here) {
+      d.gz_out = gzbuf;
+      a.gz_out = gzbuf;
+    }
+    auto beta_update = [&]() -> vb_status {
+      if (!split_here) return VB_OK;
+      HIPCHK(launch_beta_adam((int)rows, (int)R, (int)nd.size, gzbuf, beta->split[r], beta->beta[r], beta->beta_m[r],
+                              beta->beta_v[r], lr, beta1, beta2, (float)bc1, (float)bc2, adam_eps, st));
+      return VB_OK;
+    };
     if (direct) {
       ca.a = a;
       ca.a.M = (int)rows;
       ca.a.N = (int)nd.size;
       HIPCHK(launch_conv_adjoint_first(ca, (int)rows, st));
+      if ((s = beta_update())) return s;
       cur ^= 1;
       continue;
     }
@@ -2649,6 +2765,7 @@ extern "C" vb_status vb_alpha_step_rows(const vb_graph* g, int32_t batch, int32_
     } else {
       HIPCHK(launch_gemm(d, st));
     }
+    if ((s = beta_update())) return s;
     cur ^= 1;
   }
   return VB_OK;
@@ -2662,9 +2779,257 @@ extern "C" vb_status vb_alpha_step(const vb_graph* g, int32_t batch, const float
                                    void* ws, size_t ws_bytes, void* stream) {
   if (!C) return fail(VB_EINVAL, "C is NULL");
   if (!g || !g->nodes || g->n_nodes < 2) return fail(VB_EINVAL, "graph is NULL or has fewer than 2 nodes");
-  return vb_alpha_step_rows(g, batch, g->n_nodes - 1, C, m, node_lo, node_hi, x_center, x_radius, eps, compact, alpha,
-                            adam_m, adam_v, step, lr, beta1, beta2, adam_eps, lb_out, best_lb, nullptr, nullptr, ws,
-                            ws_bytes, stream);
+  return vb_alpha_step_rows(g, batch, g->n_nodes - 1, C, m, node_lo, node_hi, x_center, x_radius, eps, compact,
+                            nullptr, alpha, adam_m, adam_v, step, lr, beta1, beta2, adam_eps, lb_out, best_lb, nullptr,
+                            nullptr, ws, ws_bytes, stream);
+}
+
+extern "C" vb_status vb_apply_splits(const vb_graph* g, int32_t batch, const float* const* split,
+                                     float* const* node_lo, float* const* node_hi, void* stream) {
+  Graph G;
+  vb_status s = parse_graph(g, G);
+  if (s) return s;
+  if (batch <= 0) return fail(VB_EINVAL, "batch must be positive");
+  if (!split || !node_lo || !node_hi) return fail(VB_EINVAL, "NULL pointer array");
+  for (size_t k = 0; k < G.n.size(); ++k)
+    if (G.n[k].op == VB_RELU && split[k] && (!node_lo[G.n[k].in0] || !node_hi[G.n[k].in0]))
+      return fail(VB_EINVAL, "ReLU node %zu: bounds of its input missing", k);
+  for (size_t k = 0; k < G.n.size(); ++k) {
+    if (G.n[k].op != VB_RELU || !split[k]) continue;
+    const int z = G.n[k].in0;
+    HIPCHK(launch_apply_splits(split[k], (long long)batch * G.n[z].size, node_lo[z], node_hi[z], (hipStream_t)stream));
+  }
+  return VB_OK;
+}
+
+namespace {
+// Workspace carve-up of the branch-and-bound driver for `D` sub-domains at a time.
+struct BabLayout {
+  std::vector<size_t> lo, hi;        // per node: domain bounds [D][size]
+  size_t x, rad, C;                  // replicated input box and spec rows
+  std::vector<size_t> split, score;  // per ReLU node: [D][size]
+  std::vector<size_t> al, am, av, be, bm, bv;  // per ReLU node: [D][m][size]
+  size_t lb, best;                   // [D][m]
+  size_t step_ws, step_bytes;        // the alpha-beta step's own workspace
+  size_t bytes;
+};
+
+BabLayout bab_layout(const Graph& G, int m, int D) {
+  BabLayout L;
+  const size_t N = G.n.size();
+  size_t off = 0;
+  auto take = [&](size_t floats) {
+    const size_t o = off;
+    off += align_up(floats * 4);
+    return o;
+  };
+  L.lo.assign(N, 0);
+  L.hi.assign(N, 0);
+  L.split.assign(N, 0);
+  L.score.assign(N, 0);
+  L.al.assign(N, 0);
+  L.am.assign(N, 0);
+  L.av.assign(N, 0);
+  L.be.assign(N, 0);
+  L.bm.assign(N, 0);
+  L.bv.assign(N, 0);
+  for (size_t k = 1; k < N; ++k) {
+    L.lo[k] = take((size_t)D * G.n[k].size);
+    L.hi[k] = take((size_t)D * G.n[k].size);
+  }
+  L.x = take((size_t)D * G.n[0].size);
+  L.rad = take((size_t)D * G.n[0].size);
+  L.C = take((size_t)D * m * G.n[G.L].size);
+  for (size_t k = 0; k < N; ++k) {
+    if (G.n[k].op != VB_RELU) continue;
+    const size_t n = (size_t)G.n[k].size;
+    L.split[k] = take((size_t)D * n);
+    L.score[k] = take((size_t)D * n);
+    for (auto* v : {&L.al, &L.am, &L.av, &L.be, &L.bm, &L.bv}) (*v)[k] = take((size_t)D * m * n);
+  }
+  L.lb = take((size_t)D * m);
+  L.best = take((size_t)D * m);
+  L.step_ws = off;
+  L.step_bytes = alpha_workspace_at(G, D, G.L, m, true, nullptr, true);
+  L.bytes = off + L.step_bytes;
+  return L;
+}
+
+struct SplitRec {
+  int node, idx;
+  float sign;
+};
+}  // namespace
+
+extern "C" vb_status vb_bab_workspace_size(const vb_graph* g, int32_t m, int32_t batch, size_t* bytes) {
+  Graph G;
+  vb_status s = parse_graph(g, G);
+  if (s) return s;
+  if (!bytes || m <= 0 || batch <= 0) return fail(VB_EINVAL, "m and batch must be positive, bytes non-NULL");
+  std::vector<std::pair<int, int>> chain;
+  if (!alpha_chain(G, chain)) return fail(VB_EUNSUPPORTED, "branch and bound needs a chain of Linear/Conv + ReLU nodes");
+  *bytes = bab_layout(G, m, batch).bytes;
+  return VB_OK;
+}
+
+extern "C" vb_status vb_bab(const vb_graph* g, const float* x_center, const float* x_radius, float eps,
+                            const float* C, int32_t m, const float* const* node_lo, const float* const* node_hi,
+                            const vb_bab_params* p, int32_t* verdict, int32_t* domains, float* root_lb, void* ws,
+                            size_t ws_bytes, void* stream) {
+  Graph G;
+  vb_status s = parse_graph(g, G);
+  if (s) return s;
+  if (!p || !verdict || !domains) return fail(VB_EINVAL, "params, verdict and domains must be non-NULL");
+  if (!C || m <= 0) return fail(VB_EINVAL, "C must be non-NULL and m positive");
+  if ((s = check_domain(x_center))) return s;
+  if (!x_radius && !(eps >= 0.f)) return fail(VB_EINVAL, "eps must be >= 0");
+  if (!node_lo || !node_hi) return fail(VB_EINVAL, "NULL pointer array");
+  if (p->steps < 1 || p->batch < 1 || p->max_domains < 1) return fail(VB_EINVAL, "steps, batch and max_domains must be >= 1");
+  if (!(p->lr >= 0.f) || !(p->beta1 >= 0.f && p->beta1 < 1.f) || !(p->beta2 >= 0.f && p->beta2 < 1.f) ||
+      !(p->adam_eps > 0.f))
+    return fail(VB_EINVAL, "bad Adam hyper-parameters");
+  std::vector<std::pair<int, int>> chain;
+  if (!alpha_chain(G, chain)) return fail(VB_EUNSUPPORTED, "branch and bound needs a chain of Linear/Conv + ReLU nodes");
+  for (size_t k = 1; k < G.n.size(); ++k)
+    if (!node_lo[k] || !node_hi[k]) return fail(VB_EINVAL, "node %zu: root bounds missing", k);
+  if (!ws) return fail(VB_EINVAL, "workspace is NULL");
+  const int D = p->batch;
+  const BabLayout L = bab_layout(G, m, D);
+  if (ws_bytes < L.bytes)
+    return fail(VB_ENOMEM, "branch and bound needs %zu bytes of workspace (got %zu)", L.bytes, ws_bytes);
+  hipStream_t st = (hipStream_t)stream;
+  char* base = (char*)ws;
+  const size_t N = G.n.size();
+  auto F = [&](size_t off) { return (float*)(base + off); };
+  std::vector<float*> lo(N, nullptr), hi(N, nullptr), split(N, nullptr), al(N, nullptr), am(N, nullptr),
+      av(N, nullptr), be(N, nullptr), bm(N, nullptr), bv(N, nullptr), score(N, nullptr);
+  std::vector<int> relus;
+  for (size_t k = 1; k < N; ++k) {
+    lo[k] = F(L.lo[k]);
+    hi[k] = F(L.hi[k]);
+  }
+  for (size_t k = 0; k < N; ++k)
+    if (G.n[k].op == VB_RELU) {
+      relus.push_back((int)k);
+      split[k] = F(L.split[k]);
+      score[k] = F(L.score[k]);
+      al[k] = F(L.al[k]);
+      am[k] = F(L.am[k]);
+      av[k] = F(L.av[k]);
+      be[k] = F(L.be[k]);
+      bm[k] = F(L.bm[k]);
+      bv[k] = F(L.bv[k]);
+    }
+  const long long n0 = G.n[0].size, nL = G.n[G.L].size;
+  HIPCHK(launch_broadcast(x_center, n0, D, F(L.x), st));
+  if (x_radius) HIPCHK(launch_broadcast(x_radius, n0, D, F(L.rad), st));
+  HIPCHK(launch_broadcast(C, (long long)m * nL, D, F(L.C), st));
+  const vb_beta bst{split.data(), be.data(), bm.data(), bv.data()};
+
+  std::vector<std::vector<SplitRec>> queue(1);
+  size_t head = 0;
+  int processed = 0;
+  bool stopped = false;
+  std::vector<float> hsplit, hbest((size_t)D * m), hscore;
+  while (head < queue.size()) {
+    if (processed >= p->max_domains) {
+      stopped = true;
+      break;
+    }
+    const int nd = (int)std::min<size_t>((size_t)D, queue.size() - head);
+    // this round's split arrays (host), then the clamped bounds of every sub-domain
+    for (int r : relus) {
+      const long long n = G.n[r].size;
+      hsplit.assign((size_t)nd * n, 0.f);
+      for (int i = 0; i < nd; ++i)
+        for (const SplitRec& q : queue[head + i])
+          if (q.node == r) hsplit[(size_t)i * n + q.idx] = q.sign;
+      HIPCHK(hipMemcpyAsync(split[r], hsplit.data(), hsplit.size() * 4, hipMemcpyHostToDevice, st));
+      HIPCHK(hipStreamSynchronize(st));  // (hsplit is reused for the next node)
+    }
+    for (size_t k = 1; k < N; ++k) {
+      HIPCHK(launch_broadcast(node_lo[k], G.n[k].size, nd, lo[k], st));
+      HIPCHK(launch_broadcast(node_hi[k], G.n[k].size, nd, hi[k], st));
+    }
+    for (int r : relus) {
+      const int z = G.n[r].in0;
+      HIPCHK(launch_apply_splits(split[r], (long long)nd * G.n[z].size, lo[z], hi[z], st));
+      HIPCHK(launch_alpha_init(lo[z], hi[z], nd, m, G.n[z].size, nullptr, 0, al[r], am[r], av[r], st));
+      HIPCHK(launch_fill(be[r], 0.f, (long long)nd * m * G.n[r].size, st));
+      HIPCHK(launch_fill(bm[r], 0.f, (long long)nd * m * G.n[r].size, st));
+      HIPCHK(launch_fill(bv[r], 0.f, (long long)nd * m * G.n[r].size, st));
+    }
+    // alpha-beta-CROWN on the spec rows of every sub-domain, then one evaluation
+    for (int t = 1; t <= p->steps + 1; ++t) {
+      const int step = t <= p->steps ? t : 0;
+      s = vb_alpha_step_rows(g, nd, G.L, F(L.C), m, lo.data(), hi.data(), F(L.x), x_radius ? F(L.rad) : nullptr,
+                             eps, nullptr, &bst, al.data(), am.data(), av.data(), step, p->lr, p->beta1, p->beta2,
+                             p->adam_eps, F(L.lb), F(L.best), nullptr, nullptr, base + L.step_ws, L.step_bytes,
+                             stream);
+      if (s) return s;
+    }
+    if (head == 0 && root_lb) HIPCHK(hipMemcpyAsync(root_lb, F(L.best), (size_t)m * 4, hipMemcpyDeviceToDevice, st));
+    // branching scores from the last evaluation's Psi over each ReLU (kept in the
+    // step's workspace: after the weight copies and the domain's Psi)
+    {
+      const long long rows = (long long)nd * m;
+      size_t off = align_up(wt_floats(G) * 4) + align_up((size_t)rows * n0 * 4);
+      for (size_t k = 0; k < N && (int)k < G.L; ++k) {
+        if (G.n[k].op != VB_RELU) continue;
+        const float* psi = (const float*)(base + L.step_ws + off);
+        off += align_up((size_t)rows * G.n[k].size * 4);
+        const int z = G.n[k].in0;
+        HIPCHK(launch_branch_score(psi, F(L.best), nd, m, (int)G.n[k].size, lo[z], hi[z], score[k], st));
+      }
+    }
+    HIPCHK(hipMemcpyAsync(hbest.data(), F(L.best), (size_t)nd * m * 4, hipMemcpyDeviceToHost, st));
+    hscore.clear();
+    std::vector<size_t> soff(N, 0);
+    for (int r : relus) {
+      soff[r] = hscore.size();
+      hscore.resize(hscore.size() + (size_t)nd * G.n[r].size);
+    }
+    for (int r : relus)
+      HIPCHK(hipMemcpyAsync(hscore.data() + soff[r], score[r], (size_t)nd * G.n[r].size * 4, hipMemcpyDeviceToHost, st));
+    HIPCHK(hipStreamSynchronize(st));
+    std::vector<std::vector<SplitRec>> children;
+    for (int i = 0; i < nd && !stopped; ++i) {
+      ++processed;
+      bool proved = true;
+      for (int r = 0; r < m; ++r) proved = proved && hbest[(size_t)i * m + r] > 0.f;
+      if (proved) continue;
+      // the neuron with the largest score (ties: lowest node, then lowest index)
+      int bn = -1, bi = -1;
+      float bs = -INFINITY;
+      for (int r : relus) {
+        const long long n = G.n[r].size;
+        for (long long j = 0; j < n; ++j) {
+          const float v = hscore[soff[r] + (size_t)i * n + j];
+          if (v == -INFINITY) continue;
+          if (bn < 0 || v > bs) {
+            bn = r;
+            bi = (int)j;
+            bs = v;
+          }
+        }
+      }
+      if (bn < 0) {
+        stopped = true;  // no unstable neuron left: the search cannot refine this sub-domain
+        break;
+      }
+      for (float sign : {1.f, -1.f}) {
+        std::vector<SplitRec> child = queue[head + i];
+        child.push_back({bn, bi, sign});
+        children.push_back(std::move(child));
+      }
+    }
+    if (stopped) break;
+    head += nd;
+    for (auto& c : children) queue.push_back(std::move(c));
+  }
+  *verdict = stopped ? 0 : 1;
+  *domains = processed;
+  return VB_OK;
 }
 
 // ---------------------------------------------------------------------------

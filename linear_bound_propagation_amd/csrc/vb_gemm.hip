@@ -706,6 +706,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
             const float o = !unstable ? gz * cf[g].y : (psi[g] >= 0.f ? gz * aold[g] : gz * cf[g].y + cf[g].z);
             if (mok[g] && nok) {
               d.out[oi[g]] = o;
+              if (d.gz_out) d.gz_out[oi[g]] = gz;
               if (unstable && d.do_update) {
                 const float grad = gz * fmaxf(psi[g], 0.f);
                 const float mm = d.beta1 * am[g] + (1.f - d.beta1) * grad;

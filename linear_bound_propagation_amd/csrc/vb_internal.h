@@ -128,6 +128,7 @@ struct GemmDesc {
   float* adam_v;
   int do_update;               // 0: gradient pass without the Adam update
   float lr, beta1, beta2, bc1, bc2, adam_eps;  // bc = 1 / (1 - beta^t)
+  float* gz_out;               // or NULL: the adjoint over z (after its bias) at [opos][N]
 };
 
 // A one-tap, one-position descriptor is a plain GEMM (row-major m); anything
@@ -167,9 +168,20 @@ hipError_t launch_spec_init(const float* C, int batch, int m, int n, const float
 // row (b, s, i), s in {+1,-1}: psi = s*W[i][:]; lam = relax(psi; lo/hi[b][:]);
 // rowacc = s*bias_start[i] + sum_j lam_j bias_z[j] + min(psi_j,0) t_j
 // bias_z is per channel of z: index j % bias_zc (z flattened from a [h][w][c] tensor).
+// With sel (selected rows, [batch][n_out] neuron list, cnt [batch] valid entries): rows
+// (b, s, u) for u < U are neuron sel[b][u] (zero rows when u >= cnt[b]), 2U per input.
 hipError_t launch_identity_linear(const float* W, int n_out, int n_in, const float* bias_start,
                                   const float* lo, const float* hi, const float* bias_z, int bias_zc,
-                                  int batch, float* lam, float* rowacc, hipStream_t st);
+                                  int batch, float* lam, float* rowacc, hipStream_t st,
+                                  const int* sel = nullptr, const int* cnt = nullptr, int U = 0);
+// Selected identity rows written out over n neurons, with their bias terms in rowacc.
+hipError_t launch_select_fill(int batch, int n, int U, const int* sel, const int* cnt, const float* bias, int bias_c,
+                              float* lam, float* rowacc, hipStream_t st);
+// sel[b][rank] = j for idx[b][j] = rank >= 0
+hipError_t launch_rank_to_list(const int* idx, int batch, int n, int* sel, hipStream_t st);
+// node bounds of the selected neurons from their 2U rows per input (optionally intersected)
+hipError_t launch_finish_select(const float* acc, int batch, int U, int n, const int* sel, const int* cnt, float* lb,
+                                float* ub, int intersect, hipStream_t st);
 
 // Identity rows through a Conv node: rows (b, s, i) with i = (y*Wo + x)*Co + c over
 // the conv output; psi over the conv input [Hi][Wi][Ci] is s*W[ky][kx][c][ci] on the
@@ -376,6 +388,7 @@ struct AdjFinish {
   int do_update;
   float lr, beta1, beta2, bc1, bc2, adam_eps;
   float* out;
+  float* gz_out;    // or NULL: receives the adjoint over z (after z's bias), [M][N]
 };
 hipError_t launch_adjoint_finish(const AdjFinish& a, hipStream_t st);
 
@@ -424,6 +437,22 @@ hipError_t launch_ibp_narrow(NarrowIbp d, int S, hipStream_t st);
 
 // verified[b] = 1 iff every lb[b][i] > 0 (i < m); count[0] (if count) = number of verified inputs.
 hipError_t launch_verify(const float* lb, int batch, int m, int* verified, int* count, hipStream_t st);
+
+// beta-CROWN (branch-and-bound sub-domains):
+// lo = max(lo, 0) where split > 0, hi = min(hi, 0) where split < 0 (n elements)
+hipError_t launch_apply_splits(const float* split, long long n, float* lo, float* hi, hipStream_t st);
+// lam[row][j] -= beta[row][j] * split[row / R][j]; rowacc[row] += the term's bias products
+hipError_t launch_beta_apply(float* lam, int rows, int R, int n, const float* beta, const float* split,
+                             const float* bias, int bias_c, float* rowacc, hipStream_t st);
+// projected Adam ascent of beta (>= 0) with gradient -split * gz, on split neurons only
+hipError_t launch_beta_adam(int rows, int R, int n, const float* gz, const float* split, float* beta, float* bm,
+                            float* bv, float lr, float b1, float b2, float bc1, float bc2, float eps,
+                            hipStream_t st);
+// branching score [batch][n]: sum over the open rows (best <= 0) of max(-psi, 0) * t; -inf when stable
+hipError_t launch_branch_score(const float* psi, const float* best, int batch, int R, int n, const float* lo,
+                               const float* hi, float* score, hipStream_t st);
+// dst[b][:] = src[:] for b < batch
+hipError_t launch_broadcast(const float* src, long long n, int batch, float* dst, hipStream_t st);
 
 // Fixed scratch of the allocation-free entry point (vb_scratch.hip): its size, and
 // its address on the device of stream `st` (the null stream: the current device),

@@ -150,19 +150,28 @@ __global__ __launch_bounds__(256) void identity_linear_kernel(const float* __res
                                                               const float* __restrict__ hi,
                                                               const float* __restrict__ bias_z, int bias_zc,
                                                               int batch, float* __restrict__ lam,
-                                                              float* __restrict__ rowacc) {
+                                                              float* __restrict__ rowacc, const int* __restrict__ sel,
+                                                              const int* __restrict__ cnt, int U) {
   const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int R = 2 * n_out;
+  const int nr = sel ? U : n_out;  // rows per sign
+  const int R = 2 * nr;
   if (row >= (long long)batch * R) return;
   const long long b = row / R;
   const int r = (int)(row - b * R);
-  const int i = r < n_out ? r : r - n_out;
-  const float sg = r < n_out ? 1.f : -1.f;
+  const int u = r < nr ? r : r - nr;
+  const float sg = r < nr ? 1.f : -1.f;
+  float* dst = lam + row * n_in;
+  if (sel && u >= cnt[b]) {
+    // a selected-rows call pads every input to the largest count: no neuron here
+    for (int j = lane; j < n_in; j += 64) dst[j] = 0.f;
+    if (lane == 0) rowacc[row] = 0.f;
+    return;
+  }
+  const int i = sel ? sel[b * n_out + u] : u;
   const float* w = W + (long long)i * n_in;
   const float* lb = lo + b * n_in;
   const float* ub = hi + b * n_in;
-  float* dst = lam + row * n_in;
   float s = 0.f;
   for (int j = lane; j < n_in; j += 64) {
     float psi = sg * w[j];
@@ -179,11 +188,84 @@ __global__ __launch_bounds__(256) void identity_linear_kernel(const float* __res
 
 hipError_t launch_identity_linear(const float* W, int n_out, int n_in, const float* bias_start, const float* lo,
                                   const float* hi, const float* bias_z, int bias_zc, int batch, float* lam,
-                                  float* rowacc, hipStream_t st) {
-  long long rows = (long long)batch * 2 * n_out;
+                                  float* rowacc, hipStream_t st, const int* sel, const int* cnt, int U) {
+  long long rows = (long long)batch * 2 * (sel ? U : n_out);
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(identity_linear_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, W, n_out, n_in,
-                     bias_start, lo, hi, bias_z, bias_zc > 0 ? bias_zc : n_in, batch, lam, rowacc);
+                     bias_start, lo, hi, bias_z, bias_zc > 0 ? bias_zc : n_in, batch, lam, rowacc, sel, cnt, U);
+  return hipGetLastError();
+}
+
+// Selected identity rows written out: row (b, sign, u) is sign * e_{sel[b][u]} over n
+// neurons (zero when u >= cnt[b]); rowacc = sign * bias[sel] (0 when padding).
+__global__ __launch_bounds__(256) void select_fill_kernel(int batch, int n, int U, const int* __restrict__ sel,
+                                                          const int* __restrict__ cnt, const float* __restrict__ bias,
+                                                          int bias_c, float* __restrict__ lam,
+                                                          float* __restrict__ rowacc) {
+  const long long rows = (long long)batch * 2 * U;
+  for (long long row = blockIdx.x; row < rows; row += gridDim.x) {
+    const long long b = row / (2 * U);
+    const int r = (int)(row - b * 2 * U);
+    const int u = r < U ? r : r - U;
+    const float sg = r < U ? 1.f : -1.f;
+    const int col = u < cnt[b] ? sel[b * n + u] : -1;
+    float* out = lam + row * n;
+    for (int e = threadIdx.x; e < n; e += 256) out[e] = e == col ? sg : 0.f;
+    if (threadIdx.x == 0) rowacc[row] = (col >= 0 && bias) ? sg * bias[col % bias_c] : 0.f;
+  }
+}
+
+hipError_t launch_select_fill(int batch, int n, int U, const int* sel, const int* cnt, const float* bias, int bias_c,
+                              float* lam, float* rowacc, hipStream_t st) {
+  const long long rows = (long long)batch * 2 * U;
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(select_fill_kernel, dim3((unsigned)std::min<long long>(rows, 65536)), dim3(256), 0, st, batch, n,
+                     U, sel, cnt, bias, bias_c > 0 ? bias_c : n, lam, rowacc);
+  return hipGetLastError();
+}
+
+// sel[b][rank] = j for every neuron j with idx[b][j] = rank >= 0 (the inverse of a ranking)
+__global__ void rank_to_list_kernel(const int* __restrict__ idx, long long total, int n, int* __restrict__ sel) {
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (long long)gridDim.x * blockDim.x) {
+    const int r = idx[e];
+    if (r >= 0) sel[(e / n) * n + r] = (int)(e % n);
+  }
+}
+
+hipError_t launch_rank_to_list(const int* idx, int batch, int n, int* sel, hipStream_t st) {
+  const long long total = (long long)batch * n;
+  if (total <= 0) return hipSuccess;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(rank_to_list_kernel, dim3((unsigned)blocks), dim3(256), 0, st, idx, total, n, sel);
+  return hipGetLastError();
+}
+
+// Bounds of the selected neurons from their rows (2U per input: +e then -e):
+// lb[b][sel] = acc (or the max with the value there), ub[b][sel] = -acc (or the min).
+__global__ void finish_select_kernel(const float* __restrict__ acc, int batch, int U, int n,
+                                     const int* __restrict__ sel, const int* __restrict__ cnt, float* lb, float* ub,
+                                     int intersect) {
+  const long long total = (long long)batch * U;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (long long)gridDim.x * blockDim.x) {
+    const long long b = e / U;
+    const int u = (int)(e - b * U);
+    if (u >= cnt[b]) continue;
+    const long long j = b * n + sel[b * n + u];
+    const float l = acc[b * 2 * U + u], h = -acc[b * 2 * U + U + u];
+    if (lb) lb[j] = intersect ? fmaxf(lb[j], l) : l;
+    if (ub) ub[j] = intersect ? fminf(ub[j], h) : h;
+  }
+}
+
+hipError_t launch_finish_select(const float* acc, int batch, int U, int n, const int* sel, const int* cnt, float* lb,
+                                float* ub, int intersect, hipStream_t st) {
+  const long long total = (long long)batch * U;
+  if (total <= 0) return hipSuccess;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(finish_select_kernel, dim3((unsigned)blocks), dim3(256), 0, st, acc, batch, U, n, sel, cnt, lb,
+                     ub, intersect);
   return hipGetLastError();
 }
 
@@ -1116,6 +1198,7 @@ __device__ __forceinline__ void adjoint_elements(const AdjFinish& a, long long m
     if (!ok[i]) continue;
     const float gz = g[i] + (a.bias ? a.bias[bi[i]] : 0.f);
     a.out[m * a.N + n[i]] = !uns[i] ? gz * cf[i].y : (psi[i] >= 0.f ? gz * aold[i] : gz * cf[i].y + cf[i].z);
+    if (a.gz_out) a.gz_out[m * a.N + n[i]] = gz;
     if (uns[i] && a.do_update) {
       const float grad = gz * fmaxf(psi[i], 0.f);
       const float mm = a.beta1 * am[i] + (1.f - a.beta1) * grad;
@@ -1546,6 +1629,148 @@ hipError_t launch_verify(const float* lb, int batch, int m, int* verified, int* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !count) return e;
   hipLaunchKernelGGL(count_kernel, dim3(1), dim3(256), 0, st, verified, batch, count);
+  return hipGetLastError();
+}
+
+// ---- beta-CROWN: split constraints of branch-and-bound sub-domains
+
+// lo = max(lo, 0) where split > 0, hi = min(hi, 0) where split < 0 (n elements)
+__global__ void apply_splits_kernel(const float* __restrict__ split, long long n, float* __restrict__ lo,
+                                    float* __restrict__ hi) {
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (long long)gridDim.x * blockDim.x) {
+    const float s = split[e];
+    if (s > 0.f) lo[e] = fmaxf(lo[e], 0.f);
+    if (s < 0.f) hi[e] = fminf(hi[e], 0.f);
+  }
+}
+
+hipError_t launch_apply_splits(const float* split, long long n, float* lo, float* hi, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  long long blocks = (n + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(apply_splits_kernel, dim3((unsigned)blocks), dim3(256), 0, st, split, n, lo, hi);
+  return hipGetLastError();
+}
+
+// Lambda over a split ReLU input: lam[row][j] -= beta[row][j] * split[b][j] and
+// rowacc[row] += sum_j (-beta * split)[j] * bias[j % bias_c]; one wavefront per row.
+__global__ __launch_bounds__(256) void beta_apply_kernel(float* __restrict__ lam, int rows, int R, int n,
+                                                         const float* __restrict__ beta,
+                                                         const float* __restrict__ split,
+                                                         const float* __restrict__ bias, int bias_c,
+                                                         float* __restrict__ rowacc) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const long long b = row / R;
+  const float* sp = split + b * n;
+  float* l = lam + row * n;
+  const float* be = beta + row * n;
+  float acc = 0.f;
+  for (int j = lane; j < n; j += 64) {
+    const float sg = sp[j];
+    if (sg != 0.f) {
+      const float d = -be[j] * sg;
+      l[j] += d;
+      if (bias) acc += d * bias[bias_c > 0 ? j % bias_c : j];
+    }
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) rowacc[row] += acc;
+}
+
+hipError_t launch_beta_apply(float* lam, int rows, int R, int n, const float* beta, const float* split,
+                             const float* bias, int bias_c, float* rowacc, hipStream_t st) {
+  if (rows <= 0 || n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(beta_apply_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, lam, rows, R, n, beta,
+                     split, bias, bias_c, rowacc);
+  return hipGetLastError();
+}
+
+// Projected Adam ascent on the multipliers of split neurons: d(sum lb)/d beta =
+// -split * gz (gz: the adjoint over the ReLU input); beta = max(0, beta + step).
+__global__ void beta_adam_kernel(long long total, int R, int n, const float* __restrict__ gz,
+                                 const float* __restrict__ split, float* __restrict__ beta, float* __restrict__ bm,
+                                 float* __restrict__ bv, float lr, float b1, float b2, float bc1, float bc2,
+                                 float eps) {
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (long long)gridDim.x * blockDim.x) {
+    const long long row = e / n;
+    const int j = (int)(e - row * n);
+    const float sg = split[(row / R) * n + j];
+    if (sg == 0.f) continue;
+    const float grad = -sg * gz[e];
+    const float mm = b1 * bm[e] + (1.f - b1) * grad;
+    const float vv = b2 * bv[e] + (1.f - b2) * grad * grad;
+    bm[e] = mm;
+    bv[e] = vv;
+    const float step = lr * (mm * bc1) / (sqrtf(vv * bc2) + eps);
+    beta[e] = fmaxf(beta[e] + step, 0.f);
+  }
+}
+
+hipError_t launch_beta_adam(int rows, int R, int n, const float* gz, const float* split, float* beta, float* bm,
+                            float* bv, float lr, float b1, float b2, float bc1, float bc2, float eps,
+                            hipStream_t st) {
+  const long long total = (long long)rows * n;
+  if (total <= 0) return hipSuccess;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(beta_adam_kernel, dim3((unsigned)blocks), dim3(256), 0, st, total, R, n, gz, split, beta, bm,
+                     bv, lr, b1, b2, bc1, bc2, eps);
+  return hipGetLastError();
+}
+
+// Branching score of every neuron of a ReLU input, per sub-domain b:
+// score[b][j] = sum over rows r of b with best[b][r] <= 0 of max(-psi[b*R + r][j], 0) * t_j,
+// t = -u l / (u - l) on unstable neurons (l < 0 < u); -inf on stable neurons.
+__global__ void branch_score_kernel(const float* __restrict__ psi, const float* __restrict__ best, int batch, int R,
+                                    int n, const float* __restrict__ lo, const float* __restrict__ hi,
+                                    float* __restrict__ score) {
+  const long long total = (long long)batch * n;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (long long)gridDim.x * blockDim.x) {
+    const long long b = e / n;
+    const int j = (int)(e - b * n);
+    const float l = lo[e], u = hi[e];
+    if (!(l < 0.f && u > 0.f)) {
+      score[e] = -INFINITY;
+      continue;
+    }
+    const float t = -u * l / (u - l);
+    float sc = 0.f;
+    for (int r = 0; r < R; ++r) {
+      if (best[b * R + r] > 0.f) continue;
+      sc += fmaxf(-psi[(b * R + r) * n + j], 0.f) * t;
+    }
+    score[e] = sc;
+  }
+}
+
+hipError_t launch_branch_score(const float* psi, const float* best, int batch, int R, int n, const float* lo,
+                               const float* hi, float* score, hipStream_t st) {
+  const long long total = (long long)batch * n;
+  if (total <= 0) return hipSuccess;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(branch_score_kernel, dim3((unsigned)blocks), dim3(256), 0, st, psi, best, batch, R, n, lo, hi,
+                     score);
+  return hipGetLastError();
+}
+
+// dst[b][e] = src[e] for b < batch (n elements per copy)
+__global__ void broadcast_kernel(const float* __restrict__ src, long long n, int batch, float* __restrict__ dst) {
+  const long long total = n * batch;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (long long)gridDim.x * blockDim.x)
+    dst[e] = src[e % n];
+}
+
+hipError_t launch_broadcast(const float* src, long long n, int batch, float* dst, hipStream_t st) {
+  const long long total = n * batch;
+  if (total <= 0) return hipSuccess;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(broadcast_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, n, batch, dst);
   return hipGetLastError();
 }
 

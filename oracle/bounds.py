@@ -263,16 +263,18 @@ def intermediate_bounds(net: Oracle, x0, eps, mode: str, region_start: Optional[
     `region_start` as the domain.  A suffix "+ibp" ("crown+ibp", "hybrid+ibp")
     intersects each CROWN result with that node's bounds from the initial IBP
     pass: l = max(l_crown, l_ibp), u = min(u_crown, u_ibp), before later layers
-    use them.  Rows are independent, so they are processed in chunks of
-    `row_chunk`.  Returns (lo, hi) lists [B][*shape] (float64); only the inputs
+    use them.  A suffix "+unstable" computes rows only for the neurons the initial
+    IBP pass leaves unstable (l < 0 < u); the other neurons keep their IBP bounds.
+    Rows are independent, so they are processed in chunks of `row_chunk`.  Returns (lo, hi) lists [B][*shape] (float64); only the inputs
     in batch_idx are refined (all by default).
     """
     lo, hi = ibp(net, x0, eps)
-    base, _, suffix = mode.partition("+")
-    assert base in ("ibp", "crown", "hybrid") and suffix in ("", "ibp"), mode
+    base, *flags = mode.split("+")
+    assert base in ("ibp", "crown", "hybrid") and set(flags) <= {"ibp", "unstable"}, mode
     if base == "ibp":
         return lo, hi
-    intersect = suffix == "ibp"
+    intersect = "ibp" in flags
+    unstable_only = "unstable" in flags
     lo_ibp = [t.clone() for t in lo]
     hi_ibp = [t.clone() for t in hi]
     stop = 0 if base == "crown" else region_start
@@ -286,12 +288,22 @@ def intermediate_bounds(net: Oracle, x0, eps, mode: str, region_start: Optional[
         n = int(np.prod(shape))
         for b in batch_idx:
             dc, dr = _domain(net, lo, hi, x0, eps, b, stop)
-            lz = torch.empty(n, dtype=f64)
-            uz = torch.empty(n, dtype=f64)
+            lz = lo[z][b].reshape(-1).clone()
+            uz = hi[z][b].reshape(-1).clone()
             for r0 in range(0, n, row_chunk):
                 r1 = min(n, r0 + row_chunk)
-                lz[r0:r1] = backward(net, lo, hi, b, z, _identity_rows(shape, 1.0, r0, r1), stop, dc, dr)
-                uz[r0:r1] = -backward(net, lo, hi, b, z, _identity_rows(shape, -1.0, r0, r1), stop, dc, dr)
+                rows_p = _identity_rows(shape, 1.0, r0, r1)
+                rows_m = _identity_rows(shape, -1.0, r0, r1)
+                sel = torch.arange(r0, r1)
+                if unstable_only:
+                    # rows only for neurons the initial IBP pass leaves unstable; the
+                    # others keep their IBP bounds (their relaxation is already exact)
+                    keep = ((lo_ibp[z][b].reshape(-1) < 0) & (hi_ibp[z][b].reshape(-1) > 0))[r0:r1]
+                    sel, rows_p, rows_m = sel[keep], rows_p[keep], rows_m[keep]
+                    if sel.numel() == 0:
+                        continue
+                lz[sel] = backward(net, lo, hi, b, z, rows_p, stop, dc, dr)
+                uz[sel] = -backward(net, lo, hi, b, z, rows_m, stop, dc, dr)
             if intersect:
                 lz = torch.maximum(lz, lo_ibp[z][b].reshape(-1))
                 uz = torch.minimum(uz, hi_ibp[z][b].reshape(-1))

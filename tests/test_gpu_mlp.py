@@ -108,3 +108,28 @@ def test_chunked_workspace_matches_whole_batch(lbp):
     torch.cuda.synchronize()
     for key in ("lb", "ub"):
         assert torch.equal(full[key], part[key]), key
+
+
+@pytest.mark.parametrize("mode", ["crown+unstable", "crown+ibp+unstable"])
+@pytest.mark.parametrize("which", ["tiny", "config1"])
+def test_unstable_only_rows(lbp, which, mode):
+    """Rows only for the IBP-unstable neurons of each Linear layer: every node's
+    bounds and the spec bounds against the oracle's unstable-only mode; and with the
+    IBP intersection the spec bounds are bitwise those of all rows (stable neurons
+    keep their class, so every relaxation is the same)."""
+    wl = wk.config(1) if which == "config1" else wk.tiny_mlp([40, 64, 48, 48, 7], 0.07, 61, batch=3)
+    wl.intermediate = mode
+    print(f"{wl.name} {mode}", flush=True)
+    ref = crown_bounds(wl)
+    _, out = _run(lbp, wl)
+    _compare(wl, out, ref)
+    if "ibp" in mode.split("+")[1:]:
+        _, full = _run(lbp, wl, "crown+ibp")
+        assert torch.equal(out["lb"], full["lb"]) and torch.equal(out["ub"], full["ub"])
+
+
+def test_unstable_only_rows_config2_equal_to_all_rows(lbp):
+    wl = wk.config(2, batch=8)
+    _, out = _run(lbp, wl, "crown+ibp+unstable")
+    _, full = _run(lbp, wl, "crown+ibp")
+    assert torch.equal(out["lb"], full["lb"]) and torch.equal(out["ub"], full["ub"])
