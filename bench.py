@@ -308,28 +308,29 @@ def cpu_baseline(wl, fl, budget_s=12.0):
     return out
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_backsub_traffic_mlp3072.txt")
 GEMM_SOURCE = os.path.join(ROOT, "linear_bound_propagation_amd", "csrc", "vb_gemm.hip")
 
 
 def measured_traffic(workload_name):
-    """HBM bytes per back-substitution GEMM launch from the committed counter summary,
-    or None when it is missing, for another workload, or taken on a different kernel source."""
+    """HBM bytes per back-substitution GEMM launch from the committed counter summary of
+    this workload (profiles/gemm_backsub_traffic_*.txt), or None when there is none or it
+    was taken on a different kernel source."""
+    import glob
     import hashlib
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    kv = {}
-    for line in open(TRAFFIC_FILE):
-        if ":" in line and not line.startswith("#"):
-            k, v = line.split(":", 1)
-            kv[k.strip()] = v.strip()
     sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
-    if kv.get("kernel_source_sha256") != sha or kv.get("workload") != workload_name:
-        return None
-    try:
-        return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "gemm_backsub_traffic_*.txt"))):
+        kv = {}
+        for line in open(path):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        if kv.get("workload") != workload_name or kv.get("kernel_source_sha256") != sha:
+            continue
+        try:
+            return float(kv["hbm_bytes_per_launch"])
+        except (KeyError, ValueError):
+            return None
+    return None
 
 
 def copy_probe(nbytes):

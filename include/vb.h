@@ -369,16 +369,23 @@ vb_status vb_crown_noalloc(const vb_graph* g, int32_t batch,
                            const float* C, int32_t m,
                            float* ibp_lb, float* ibp_ub, float* lb, float* ub, void* stream);
 
-/* Measurement of the back-substitution GEMM (the dominant kernel).
+/* Measurement of the back-substitution GEMM (the dominant kernel), for
+ * benchmarks only: these three calls keep process-wide state (a list of event
+ * pairs), are not thread-safe, and add two event records per GEMM launch while
+ * recording is on; no other entry point depends on them.
  * vb_profile_start() begins recording a pair of HIP events around every
  * back-substitution GEMM launch (relaxation, concretisation or store
  * epilogue), on the stream of that launch, together with its algorithmic FLOPs
  * (2 x rows x multiply-adds of the layer, without padding or tile waste).
  * vb_profile_stop() stops recording, waits for the recorded events and
  * returns the summed kernel time (ms), summed FLOPs and launch count.
- * Not thread-safe; meant for benchmarks. */
+ * vb_profile_record(i, ...) returns launch i of the last stopped recording:
+ * its time (ms), algorithmic FLOPs and info[6] = {epilogue (0 store,
+ * 1 relaxation, 2 concretisation), footprint windows (0/1), M, N, K, taps} of
+ * the GEMM; VB_EINVAL when i is out of range. */
 vb_status vb_profile_start(void);
 vb_status vb_profile_stop(double* ms, double* flops, int64_t* launches);
+vb_status vb_profile_record(int64_t i, double* ms, double* flops, int32_t* info);
 
 #ifdef __cplusplus
 }

@@ -35,7 +35,7 @@ _OPS = {"input": VB_INPUT, "linear": VB_LINEAR, "conv": VB_CONV2D, "relu": VB_RE
 EXPORTS = ["vb_last_error", "vb_workspace_size", "vb_ibp", "vb_crown_backward", "vb_concretize",
            "vb_alpha_layout", "vb_alpha_init", "vb_alpha_step", "vb_alpha_step_rows", "vb_apply_splits",
            "vb_bab_workspace_size", "vb_bab", "vb_crown", "vb_crown_noalloc", "vb_verify",
-           "vb_profile_start", "vb_profile_stop"]
+           "vb_profile_start", "vb_profile_stop", "vb_profile_record"]
 # host-only helpers declared in include/vb_testing.h (used by the CPU tests)
 TESTING_EXPORTS = ["vb_testing_fastdiv", "vb_testing_conv_tile_n", "vb_testing_identity_path"]
 
@@ -114,6 +114,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vb_profile_stop.restype = i32
     lib.vb_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_int64)]
+    lib.vb_profile_record.restype = i32
+    lib.vb_profile_record.argtypes = [ctypes.c_int64, ctypes.POINTER(ctypes.c_double),
+                                      ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
     return lib
 
 
@@ -534,6 +537,18 @@ def profile_stop():
     ms, fl, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
     _check(lib().vb_profile_stop(ctypes.byref(ms), ctypes.byref(fl), ctypes.byref(n)), "vb_profile_stop")
     return ms.value, fl.value, n.value
+
+
+def profile_records(n):
+    """Per-launch records of the last profile_stop(): list of dicts (ms, flops, epi,
+    patch, M, N, K, taps)."""
+    out = []
+    for i in range(n):
+        ms, fl = ctypes.c_double(), ctypes.c_double()
+        info = (ctypes.c_int32 * 6)()
+        _check(lib().vb_profile_record(i, ctypes.byref(ms), ctypes.byref(fl), info), "vb_profile_record")
+        out.append(dict(ms=ms.value, flops=fl.value, **dict(zip(("epi", "patch", "M", "N", "K", "taps"), list(info)))))
+    return out
 
 
 def prepare(wl, device="cuda"):

@@ -367,9 +367,15 @@ vb_status effective_bias(Backward& B, const Graph& G, int z, const float*& bias)
 struct ProfRec {
   hipEvent_t a, b;
   double flops;
+  int32_t info[6];  // epilogue, footprint windows, M, N, K, taps
+};
+struct ProfDone {
+  double ms, flops;
+  int32_t info[6];
 };
 bool g_prof_on = false;
 std::vector<ProfRec> g_prof;
+std::vector<ProfDone> g_prof_done;  // per launch, from the last vb_profile_stop
 
 vb_status run_gemm_reduce(Backward& B, GemmDesc& d, int rows, int P, bool reduce, double alg_flops = 0.0) {
   d.part = reduce ? B.part : nullptr;
@@ -387,6 +393,8 @@ vb_status run_gemm_reduce(Backward& B, GemmDesc& d, int rows, int P, bool reduce
   if (prof) {
     HIPCHK(hipEventRecord(rec.b, B.st));
     rec.flops = alg_flops;
+    const int32_t info[6] = {d.epi, d.patch, d.M, d.N, d.K, d.ntaps};
+    for (int i = 0; i < 6; ++i) rec.info[i] = info[i];
     g_prof.push_back(rec);
   }
   const bool gather = !gemm_is_dense(d);
@@ -2375,12 +2383,16 @@ extern "C" vb_status vb_profile_start(void) {
 extern "C" vb_status vb_profile_stop(double* ms, double* flops, int64_t* launches) {
   g_prof_on = false;
   double t = 0.0, f = 0.0;
+  g_prof_done.clear();
   for (auto& r : g_prof) {
     HIPCHK(hipEventSynchronize(r.b));
     float e = 0.f;
     HIPCHK(hipEventElapsedTime(&e, r.a, r.b));
     t += e;
     f += r.flops;
+    ProfDone dn{e, r.flops, {}};
+    for (int i = 0; i < 6; ++i) dn.info[i] = r.info[i];
+    g_prof_done.push_back(dn);
   }
   if (ms) *ms = t;
   if (flops) *flops = f;
@@ -2390,6 +2402,16 @@ extern "C" vb_status vb_profile_stop(double* ms, double* flops, int64_t* launche
     (void)hipEventDestroy(r.b);
   }
   g_prof.clear();
+  return VB_OK;
+}
+
+extern "C" vb_status vb_profile_record(int64_t i, double* ms, double* flops, int32_t* info) {
+  if (i < 0 || i >= (int64_t)g_prof_done.size()) return fail(VB_EINVAL, "vb_profile_record: no record %lld", (long long)i);
+  const ProfDone& r = g_prof_done[(size_t)i];
+  if (ms) *ms = r.ms;
+  if (flops) *flops = r.flops;
+  if (info)
+    for (int k = 0; k < 6; ++k) info[k] = r.info[k];
   return VB_OK;
 }
 
