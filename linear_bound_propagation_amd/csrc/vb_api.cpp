@@ -552,6 +552,11 @@ vb_status backward_chunk_patch(Backward& B, const BwdCall& c, long long R, const
   vb_status s = effective_bias(B, G, c.start, bias);
   if (s) return s;
   HIPCHK(launch_identity_bias(c.cb, (int)S.size, bias, S.c, B.rowacc, B.st));
+  // a domain node inside the network: its box (centre, radius) for this chunk
+  if (c.stop != 0)
+    HIPCHK(launch_box_center_radius(B.lo[c.stop] + (long long)c.b0 * G.n[c.stop].size,
+                                    B.hi[c.stop] + (long long)c.b0 * G.n[c.stop].size,
+                                    (long long)c.cb * G.n[c.stop].size, B.box_c, B.box_r, B.st));
   // the first step (through the start conv, relaxed at the ReLU below it) reads
   // the weights directly when the kernel takes the shape; otherwise the
   // identity rows are written out and multiplied like any other Lambda
@@ -934,6 +939,26 @@ vb_status backward_chunk_window(Backward& B, const BwdCall& c, long long R, cons
       if (last_edge < 0) last_edge = k;
     }
   int dom_buf = -1;
+  // Two conv branches onto the domain with the same stride and number of output
+  // channels are concretised by ONE GEMM whose taps read both branches' Lambdas
+  // (the K loop runs over the taps of both), so the sum is formed in the
+  // accumulators: no domain-window buffer to clear, store and read back.  The
+  // first of the two branches the walk meets waits for the second.
+  bool merge_dom = false;
+  if (dom_edges == 2) {
+    int e[2], n = 0;
+    for (int k = c.stop + 1; k <= c.start; ++k)
+      if (active[k] && G.n[k].op == VB_CONV2D && G.n[k].in0 == c.stop) e[n++] = k;
+    const NodeInfo &a = G.n[e[0]], &b = G.n[e[1]];
+    const auto per_class = [](const NodeInfo& q) {
+      return ((q.kh + q.stride - 1) / q.stride) * ((q.kw + q.stride - 1) / q.stride);
+    };
+    merge_dom = a.stride == b.stride && a.c == b.c && a.c % 32 == 0 && per_class(a) + per_class(b) <= MAX_TAPS;
+  }
+  struct Deferred {
+    int k = -1, buf = -1;
+    Win w;
+  } held;
   // a pool buffer holding the pending Lambda of node t in window geometry w
   auto as_buffer = [&](int t, const Win& w, int& out) -> vb_status {
     out = B.alloc();
@@ -1036,8 +1061,14 @@ vb_status backward_chunk_window(Backward& B, const BwdCall& c, long long R, cons
       lam[k] = NONE;
     }
     const Win kw = pw[k];
-    const bool summed = last && dom_edges > 1;
-    const Win tw = last ? (summed ? W[t] : conv_reach(nd, kw)) : W[t];
+    const bool summed = last && dom_edges > 1 && !merge_dom;
+    const Win tw = last ? (dom_edges > 1 ? W[t] : conv_reach(nd, kw)) : W[t];
+    if (last && merge_dom && k != last_edge) {
+      held.k = k;
+      held.buf = cur;
+      held.w = kw;
+      continue;
+    }
     int outb = -1, addb = -1;
     const float* bias_z = nullptr;
     if (summed && dom_buf < 0) {
@@ -1072,15 +1103,67 @@ vb_status backward_chunk_window(Backward& B, const BwdCall& c, long long R, cons
     nv.pad = pad_y;
     // the multiply-adds of this step (cells of the rows' windows inside the image)
     const double macs = window_macs(S, nd, kw, rows_per_pixel) * tn.c;
+    double macs_all = macs;
     std::vector<GemmDesc> descs;
-    for (int py = 0; py < nd.stride; ++py)
-      for (int px = 0; px < nd.stride; ++px) {
-        GemmDesc d;
-        if (conv_backward(nv, tv, B.pool[cur], rows, py, px, d) && d.K > 0) descs.push_back(d);
-      }
+    if (last && merge_dom) {
+      if (held.k < 0) return fail(VB_EUNSUPPORTED, "internal: the other branch onto node %d is missing", t);
+      const NodeInfo& nd1 = G.n[held.k];
+      const Win& kw1 = held.w;
+      NodeInfo nv1 = nd1;
+      nv1.h = kw1.wh;
+      nv1.w = kw1.ww;
+      nv1.size = (long long)kw1.wh * kw1.ww * nd1.c;
+      nv1.pad = nd1.pad + tw.oy - nd1.stride * kw1.oy;
+      if (nv1.pad != nd1.pad + tw.ox - nd1.stride * kw1.ox)
+        return fail(VB_EUNSUPPORTED, "internal: windows of node %d are not square-aligned", held.k);
+      macs_all += window_macs(S, nd1, kw1, rows_per_pixel) * tn.c;
+      for (int py = 0; py < nd.stride; ++py)
+        for (int px = 0; px < nd.stride; ++px) {
+          GemmDesc d0, d1;
+          const bool h0 = conv_backward(nv, tv, B.pool[cur], rows, py, px, d0) && d0.K > 0;
+          const bool h1 = conv_backward(nv1, tv, B.pool[held.buf], rows, py, px, d1) && d1.K > 0;
+          if (!h0 && !h1) continue;
+          GemmDesc d = h0 ? d0 : d1;
+          d.B = h0 ? B.wt[k] : B.wt[held.k];
+          patch_fields(d, tw, tn, h0 ? kw : kw1, h0 ? nd : nd1);
+          if (h0 && h1) {
+            if (d1.gh != d.gh || d1.gw != d.gw || d1.oy0 != d.oy0 || d1.ox0 != d.ox0 || d1.cs != d.cs ||
+                d.ntaps + d1.ntaps > MAX_TAPS)
+              return fail(VB_EUNSUPPORTED, "internal: the branches onto node %d do not share their grid", t);
+            d.tap_src1 = d.ntaps;
+            for (int j = 0; j < d1.ntaps; ++j) {
+              d.tap_dy[d.ntaps + j] = d1.tap_dy[j];
+              d.tap_dx[d.ntaps + j] = d1.tap_dx[j];
+              d.tap_w[d.ntaps + j] = d1.tap_w[j];
+            }
+            d.ntaps += d1.ntaps;
+            d.K = d.ntaps * d.cs;
+            d.A1 = B.pool[held.buf];
+            d.B1 = B.wt[held.k];
+            d.a1_row_stride = d1.a_row_stride;
+            d.hs1 = d1.hs;
+            d.ws1 = d1.ws;
+            d.ssy1 = kw1.sy;
+            d.soy1 = kw1.oy;
+            d.ssx1 = kw1.sx;
+            d.sox1 = kw1.ox;
+            d.src_h1 = nd1.h;
+            d.src_w1 = nd1.w;
+          }
+          descs.push_back(d);
+        }
+    } else {
+      for (int py = 0; py < nd.stride; ++py)
+        for (int px = 0; px < nd.stride; ++px) {
+          GemmDesc d;
+          if (conv_backward(nv, tv, B.pool[cur], rows, py, px, d) && d.K > 0) {
+            d.B = B.wt[k];
+            patch_fields(d, tw, tn, kw, nd);
+            descs.push_back(d);
+          }
+        }
+    }
     for (GemmDesc& d : descs) {
-      d.B = B.wt[k];
-      patch_fields(d, tw, tn, kw, nd);
       if (summed && k != last_edge) {
         // a branch onto the domain that is not the last: add into the domain window
         d.epi = E_STORE;
@@ -1105,12 +1188,16 @@ vb_status backward_chunk_window(Backward& B, const BwdCall& c, long long R, cons
         d.bias = bias_z;
         d.bias_c = tn.c;
       }
-      s = run_gemm_reduce(B, d, rows, d.gh * d.gw, d.epi != E_STORE, 2.0 * macs / descs.size());
+      s = run_gemm_reduce(B, d, rows, d.gh * d.gw, d.epi != E_STORE, 2.0 * macs_all / descs.size());
       if (s) return s;
     }
     if (!last && descs.size() != (size_t)nd.stride * nd.stride)
       return fail(VB_EUNSUPPORTED, "internal: node %d has output-parity classes without taps", k);
     B.release(cur);
+    if (last && merge_dom) {
+      B.release(held.buf);
+      held = Deferred{};
+    }
     if (addb >= 0) B.release(addb);
     if (summed && k == last_edge) {
       B.release(dom_buf);

@@ -61,7 +61,7 @@ __device__ __forceinline__ GPos gdecode(const GemmDesc& d, int m) {
 
 struct Pos {
   long long a_base;
-  int Y, X;
+  int row, Y, X;
   bool valid;
 };
 
@@ -72,6 +72,7 @@ __device__ __forceinline__ Pos pos_of(const GemmDesc& d, int m) {
     p.valid = m < d.M;
     const int mm = p.valid ? m : 0;
     p.a_base = (long long)mm * d.a_row_stride;
+    p.row = mm;
     p.Y = p.X = 0;
   } else {
     const GPos g = gdecode(d, m);
@@ -79,6 +80,7 @@ __device__ __forceinline__ Pos pos_of(const GemmDesc& d, int m) {
     p.Y = fdiv(g.q, d.div_gw);
     p.X = g.q - p.Y * d.gw;
     p.a_base = (long long)g.row * d.a_row_stride;
+    p.row = g.row;
   }
   return p;
 }
@@ -173,8 +175,10 @@ __device__ __forceinline__ void a_val4(const GemmDesc& d, long long off, float4&
 // Epilogue addressing variants (compile-time, so that the common case keeps
 // its register budget): plain; footprint windows (rows of identity-start
 // neurons kept on a window of the target node); compact per-neuron state
-// (alpha, kept Psi and Adam moments on unstable neurons only).
-enum { V_PLAIN = 0, V_PATCH = 1, V_COMPACT = 2 };
+// (alpha, kept Psi and Adam moments on unstable neurons only); footprint
+// windows whose taps read two Lambda sources (two branches of a residual
+// block that meet at the node being concretised over).
+enum { V_PLAIN = 0, V_PATCH = 1, V_COMPACT = 2, V_PATCH2 = 3 };
 
 template <int BM, int BN, int WM, int WN, bool DENSE, int AMODE, int EPI, bool FAST, int VAR = V_PLAIN>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
@@ -190,6 +194,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   constexpr int AS = BM * BK / NTHR;                       // scalars of A (slow path)
   constexpr int BS = (BN * BK + NTHR - 1) / NTHR;          // scalars of B (slow path)
   static_assert(FM >= 1 && FN >= 1 && AV >= 1, "tile");
+  constexpr bool PATCH = VAR == V_PATCH || VAR == V_PATCH2;
+  constexpr bool DUAL = VAR == V_PATCH2;
+  static_assert(!DUAL || (FAST && !DENSE && AMODE == A_PLAIN), "two sources: fast gather path only");
 
   __shared__ __attribute__((aligned(16))) float As[2][NA][BM * LDK];
   __shared__ __attribute__((aligned(16))) float Bs[2][BN * LDK];
@@ -250,8 +257,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   long long abase[FAST ? AV : 1], bbase[FAST ? BV : 1];
   int ld_j = 0, ld_c = 0;  // tap and channel offset of the next stage to load
   unsigned tmask = (1u << MAX_TAPS) - 1;  // taps whose stages this workgroup runs
+  bool src1 = false;                      // the current tap reads the second source
   auto set_tap = [&](int j) {
     const Tap tp = DENSE ? Tap{0, 0, 0} : tap_of(d, j);
+    src1 = DUAL && j >= d.tap_src1;
+    const int hs = src1 ? d.hs1 : d.hs, wsrc = src1 ? d.ws1 : d.ws;
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
       const int f = tid + NTHR * i;
@@ -264,7 +274,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
         } else {
           const int yy = p.Y * d.sy + tp.dy;
           const int xx = p.X * d.sx + tp.dx;
-          if (yy >= 0 && yy < d.hs && xx >= 0 && xx < d.ws) off = p.a_base + ((long long)yy * d.ws + xx) * d.cs + kq;
+          const long long base = src1 ? (long long)p.row * d.a1_row_stride : p.a_base;
+          if (yy >= 0 && yy < hs && xx >= 0 && xx < wsrc) off = base + ((long long)yy * wsrc + xx) * d.cs + kq;
         }
       }
       abase[i] = off;
@@ -284,12 +295,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
       (void)k0;
 #pragma unroll
       for (int i = 0; i < AV; ++i) {
-        float4 r4;
-        a_val4<AMODE>(d, abase[i] >= 0 ? abase[i] + ld_c : -1, ra[0][i], r4);
-        if (NA == 2) ra[NA - 1][i] = r4;
+        if (DUAL) {
+          ra[0][i] = ld4(src1 ? d.A1 : d.A, abase[i] >= 0 ? abase[i] + ld_c : -1);
+        } else {
+          float4 r4;
+          a_val4<AMODE>(d, abase[i] >= 0 ? abase[i] + ld_c : -1, ra[0][i], r4);
+          if (NA == 2) ra[NA - 1][i] = r4;
+        }
       }
+      const float* bsrc = (DUAL && src1) ? d.B1 : d.B;
 #pragma unroll
-      for (int i = 0; i < BV; ++i) rb[i] = ld4(d.B, bbase[i] >= 0 ? bbase[i] + ld_c : -1);
+      for (int i = 0; i < BV; ++i) rb[i] = ld4(bsrc, bbase[i] >= 0 ? bbase[i] + ld_c : -1);
       // advance to the next stage: the next 32 channels, or the next tap this
       // tile reads
       ld_c += BK;
@@ -381,9 +397,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
     for (int i = 0; i < AV; ++i) {
       const Pos& p = apos[i];
       if (!p.valid) continue;
-      int sy0 = 0, sx0 = 0;
+      int sy0 = 0, sx0 = 0, sy1 = 0, sx1 = 0;
       bool inimg = true;
-      if (VAR == V_PATCH) {
+      if (PATCH) {
         const GPos g = gdecode(d, m0 + (tid + NTHR * i) / (BK / 4));
         const int t1 = fdiv(g.row, d.div_pc);
         const int pz = t1 - fdiv(t1, d.div_pz) * d.div_pz.d;
@@ -393,14 +409,23 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
         inimg = ay >= 0 && ay < d.img_h && ax >= 0 && ax < d.img_w;
         sy0 = py * d.ssy + d.soy;
         sx0 = px * d.ssx + d.sox;
+        if (DUAL) {
+          sy1 = py * d.ssy1 + d.soy1;
+          sx1 = px * d.ssx1 + d.sox1;
+        }
       }
       if (!inimg) continue;
       for (int j = 0; j < d.ntaps; ++j) {
         const Tap tp = tap_of(d, j);
         const int yy = p.Y * d.sy + tp.dy, xx = p.X * d.sx + tp.dx;
-        bool ok = yy >= 0 && yy < d.hs && xx >= 0 && xx < d.ws;
-        if (VAR == V_PATCH && d.src_h > 0)
+        const bool s1 = DUAL && j >= d.tap_src1;
+        bool ok = yy >= 0 && yy < (s1 ? d.hs1 : d.hs) && xx >= 0 && xx < (s1 ? d.ws1 : d.ws);
+        if (s1) {
+          if (d.src_h1 > 0)
+            ok = ok && sy1 + yy >= 0 && sy1 + yy < d.src_h1 && sx1 + xx >= 0 && sx1 + xx < d.src_w1;
+        } else if (PATCH && d.src_h > 0) {
           ok = ok && sy0 + yy >= 0 && sy0 + yy < d.src_h && sx0 + xx >= 0 && sx0 + xx < d.src_w;
+        }
         if (ok) my |= 1u << j;
       }
     }
@@ -498,7 +523,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   // >= 32 rows of the same output position: the position (and its division
   // work) is decoded once per block, and each element only adds its row
   // offset.  (Footprint rows need a per-row window decode.)
-  constexpr bool one_pos = !DENSE && VAR != V_PATCH;
+  constexpr bool one_pos = !DENSE && !PATCH;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     int row0 = 0, r0 = 0, b0 = 0;
@@ -552,7 +577,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
           const long long sp = (long long)cy * d.wo + cx;
           opos[g] = (long long)gp.row * d.ho * d.wo + sp;
           const long long b = fdiv(gp.row, d.div_rows);
-          if (VAR == V_PATCH) {
+          if (PATCH) {
             // window cell -> pixel of the target node for the row's own position
             const int t1 = fdiv(gp.row, d.div_pc);
             const int pz = t1 - fdiv(t1, d.div_pz) * d.div_pz.d;
@@ -827,7 +852,9 @@ hipError_t launch_tile(const GemmDesc& d, hipStream_t st) {
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_RELAX, FAST>), g, b, 0, st, d);
       break;
     case E_CONCRETIZE:
-      if (!DENSE && d.patch)
+      if (!DENSE && FAST && d.patch && d.A1)
+        hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, false, A_PLAIN, E_CONCRETIZE, true, V_PATCH2>), g, b, 0, st, d);
+      else if (!DENSE && d.patch)
         hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, DENSE, A_PLAIN, E_CONCRETIZE, FAST, DENSE ? V_PLAIN : V_PATCH>), g, b,
                            0, st, d);
       else
@@ -884,7 +911,8 @@ namespace {
 // fast path: every 32-deep K stage inside one tap, float4-aligned rows
 bool is_fast(const GemmDesc& d) {
   return d.K > 0 && d.cs % BK == 0 && d.a_row_stride % 4 == 0 && aligned16(d.A) &&
-         (d.A2 == nullptr || aligned16(d.A2)) && aligned16(d.B);
+         (d.A2 == nullptr || aligned16(d.A2)) && aligned16(d.B) &&
+         (d.A1 == nullptr || (aligned16(d.A1) && aligned16(d.B1) && d.a1_row_stride % 4 == 0));
 }
 }  // namespace
 
@@ -933,6 +961,9 @@ hipError_t launch_gemm(const GemmDesc& desc, hipStream_t st) {
   if (!finalize(d)) return hipErrorInvalidValue;
   const bool dense = gemm_is_dense(d);
   const bool fast = is_fast(d);
+  // a second A source exists only as a fast-path footprint concretisation
+  if (d.A1 && (!fast || dense || !d.patch || d.epi != E_CONCRETIZE || d.tap_src1 < 0 || d.tap_src1 > d.ntaps))
+    return hipErrorInvalidValue;
   const int bn = tile_n(d, fast);
   if (bn == 256) {
     // gather GEMMs with the store, relaxation or concretisation epilogue only

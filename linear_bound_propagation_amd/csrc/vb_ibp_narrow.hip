@@ -7,7 +7,11 @@
 // column dimension (v_mfma_f32_16x16x4f32, at most 16 inputs): each lane
 // streams float4 pieces of its weight rows straight from HBM into registers
 // (no LDS staging, nothing is reused), and the input centres / radii, which
-// every wave reads, come from L2.  One chain of MFMAs accumulates W.c, a second
+// every wave reads, come from L2.  (A variant that read 128 x 64 weight tiles
+// with every load instruction covering 256 contiguous bytes of four rows and
+// went through LDS into the operand layout ran at 4.0 TB/s against 4.8 TB/s for
+// this one: with its 70 KB of LDS per workgroup it kept half as many bytes in
+// flight per CU.)  One chain of MFMAs accumulates W.c, a second
 // |W|.r on the same weight registers.  Long rows are split over a grid
 // dimension; partial sums then go to a workspace and a fixed-order finishing
 // kernel adds them (one wavefront per output when there are many slices).
@@ -23,7 +27,9 @@ namespace {
 
 constexpr int NB = 8;          // MFMA blocks of 16 output neurons per wavefront
 constexpr int ROWS = 16 * NB;  // output neurons per wavefront
-constexpr int U = 2;           // 16-wide K steps whose loads are issued together
+constexpr int U = 4;           // 16-wide K steps whose loads are issued together: a lane's
+                               // four float4 of a row and its row's other three lanes cover
+                               // 256 contiguous bytes of that row per step
 
 // float4 at a clamped element offset (always a valid address of the array)
 __device__ __forceinline__ float4 ldg4(const float* __restrict__ p, long long off) {

@@ -89,6 +89,17 @@ struct GemmDesc {
   //      (py*ssy + soy + Ys, px*ssx + sox + Xs) of a src_h x src_w node
   //      (src_h = 0: not given; then only the window's own bounds are known)
   int ssy, soy, ssx, sox, src_h, src_w;
+  //      a second A source (footprint windows, concretisation): taps j >=
+  //      tap_src1 read Lambda A1 (row stride a1_row_stride) on its own
+  //      hs1 x ws1 window grid, whose cell (Ys, Xs) for row p is pixel
+  //      (py*ssy1 + soy1 + Ys, px*ssx1 + sox1 + Xs) of a src_h1 x src_w1 node,
+  //      with weights B1 (same [tap][N][cs] layout, tap_w indexing B1).  The
+  //      two sources' products land on the same output window and are summed
+  //      by the reduction itself.  A1 == NULL: every tap reads A.
+  const float* A1;
+  const float* B1;
+  long long a1_row_stride;
+  int tap_src1, hs1, ws1, ssy1, soy1, ssx1, sox1, src_h1, src_w1;
   int Mt;                      // filled by launch_gemm: size of the tile index space (gather: padded)
   int rb_shift;                // filled by launch_gemm: log2 of the rows per block (gather)
   // ---- epilogue

@@ -186,11 +186,107 @@ __global__ __launch_bounds__(256) void identity_linear_kernel(const float* __res
   if (lane == 0) rowacc[row] = (bias_start ? sg * bias_start[i] : 0.f) + s;
 }
 
+// The same rows, a workgroup per (input b, IL_RI neurons): the relaxation
+// coefficients of b's neurons are worked out once per column and serve the
+// 2 * IL_RI rows (both signs) of the group, each weight float4 is loaded once
+// for its two rows, and every access is a 16-byte one (n_in % 4 == 0).  A
+// row's sum runs over its columns in the same order whichever rows share the
+// workgroup (thread-strided float4 columns, then a fixed-order block sum).
+constexpr int IL_RI = 8;
+
+__global__ __launch_bounds__(256) void identity_linear4_kernel(const float* __restrict__ W, int n_out, int n_in,
+                                                               const float* __restrict__ bias_start,
+                                                               const float* __restrict__ lo,
+                                                               const float* __restrict__ hi,
+                                                               const float* __restrict__ bias_z, int bias_zc,
+                                                               float* __restrict__ lam, float* __restrict__ rowacc,
+                                                               const int* __restrict__ sel,
+                                                               const int* __restrict__ cnt, int U) {
+  const int nr = sel ? U : n_out;  // rows per sign
+  const int groups = (nr + IL_RI - 1) / IL_RI;
+  const int b = blockIdx.x / groups;
+  const int u0 = (blockIdx.x - b * groups) * IL_RI;
+  const int tid = threadIdx.x;
+  const int nb = sel ? cnt[b] : nr;  // live rows of this input
+  int src[IL_RI];
+#pragma unroll
+  for (int q = 0; q < IL_RI; ++q) {
+    const int u = u0 + q;
+    src[q] = u < nb ? (sel ? sel[(long long)b * n_out + u] : u) : -1;
+  }
+  const long long rp = (long long)b * 2 * nr + u0, rm = rp + nr;  // first + and - row
+  float sp[IL_RI], sm[IL_RI];
+#pragma unroll
+  for (int q = 0; q < IL_RI; ++q) sp[q] = sm[q] = 0.f;
+  const float* lb = lo + (long long)b * n_in;
+  const float* ub = hi + (long long)b * n_in;
+  for (int j = 4 * tid; j < n_in; j += 1024) {
+    const float4 l4 = *reinterpret_cast<const float4*>(lb + j);
+    const float4 h4 = *reinterpret_cast<const float4*>(ub + j);
+    const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, hv[4] = {h4.x, h4.y, h4.z, h4.w};
+    float a[4], sl[4], t[4], bz[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      relax_coeffs(lv[e], hv[e], a[e], sl[e], t[e]);
+      bz[e] = bias_z ? bias_z[(j + e) % bias_zc] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < IL_RI; ++q) {
+      if (u0 + q >= nr) break;
+      float4 w4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (src[q] >= 0) w4 = *reinterpret_cast<const float4*>(W + (long long)src[q] * n_in + j);
+      const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+      float op[4], om[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pp = wv[e], pm = -wv[e];
+        op[e] = pp >= 0.f ? pp * a[e] : pp * sl[e];
+        om[e] = pm >= 0.f ? pm * a[e] : pm * sl[e];
+        if (bias_z) {
+          sp[q] += op[e] * bz[e];
+          sm[q] += om[e] * bz[e];
+        }
+        sp[q] += fminf(pp, 0.f) * t[e];
+        sm[q] += fminf(pm, 0.f) * t[e];
+      }
+      *reinterpret_cast<float4*>(lam + (rp + q) * n_in + j) = make_float4(op[0], op[1], op[2], op[3]);
+      *reinterpret_cast<float4*>(lam + (rm + q) * n_in + j) = make_float4(om[0], om[1], om[2], om[3]);
+    }
+  }
+  __shared__ float red[4][2 * IL_RI];
+  const int lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+  for (int q = 0; q < IL_RI; ++q) {
+    const float x = wave_sum(sp[q]), y = wave_sum(sm[q]);
+    if (lane == 0) {
+      red[wv][q] = x;
+      red[wv][IL_RI + q] = y;
+    }
+  }
+  __syncthreads();
+  if (tid < 2 * IL_RI) {
+    const int q = tid % IL_RI;
+    const bool minus = tid >= IL_RI;
+    if (u0 + q < nr) {
+      const float tot = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+      const float sg = minus ? -1.f : 1.f;
+      rowacc[(minus ? rm : rp) + q] = src[q] >= 0 ? (bias_start ? sg * bias_start[src[q]] : 0.f) + tot : 0.f;
+    }
+  }
+}
+
 hipError_t launch_identity_linear(const float* W, int n_out, int n_in, const float* bias_start, const float* lo,
                                   const float* hi, const float* bias_z, int bias_zc, int batch, float* lam,
                                   float* rowacc, hipStream_t st, const int* sel, const int* cnt, int U) {
   long long rows = (long long)batch * 2 * (sel ? U : n_out);
   if (rows <= 0) return hipSuccess;
+  auto al = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  if (n_in % 4 == 0 && al(W) && al(lo) && al(hi) && al(lam)) {
+    const long long groups = ((sel ? U : n_out) + IL_RI - 1) / IL_RI;
+    hipLaunchKernelGGL(identity_linear4_kernel, dim3((unsigned)(batch * groups)), dim3(256), 0, st, W, n_out, n_in,
+                       bias_start, lo, hi, bias_z, bias_zc > 0 ? bias_zc : n_in, lam, rowacc, sel, cnt, U);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(identity_linear_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, W, n_out, n_in,
                      bias_start, lo, hi, bias_z, bias_zc > 0 ? bias_zc : n_in, batch, lam, rowacc, sel, cnt, U);
   return hipGetLastError();

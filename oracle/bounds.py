@@ -152,7 +152,8 @@ def _push(lam: Dict[int, torch.Tensor], k: int, v: torch.Tensor):
 def backward(net: Oracle, lo, hi, b: int, start: int, rows: torch.Tensor, stop: int,
              dom_c: torch.Tensor, dom_r: torch.Tensor, alpha: Optional[Dict[int, torch.Tensor]] = None,
              keep: Optional[dict] = None, beta: Optional[Dict[int, torch.Tensor]] = None,
-             splits: Optional[Dict[int, torch.Tensor]] = None) -> torch.Tensor:
+             splits: Optional[Dict[int, torch.Tensor]] = None,
+             decide: Optional[Dict[int, torch.Tensor]] = None, tau: float = 1e-6) -> torch.Tensor:
     """Lower bound of each row of `rows` (linear functions of node `start`) for input b.
 
     Lambda starts as `rows` over node `start` with the constant term d = 0 and is
@@ -171,6 +172,11 @@ def backward(net: Oracle, lo, hi, b: int, start: int, rows: torch.Tensor, stop: 
     beta[k] [R][*shape] >= 0 the rows' multipliers; the Lagrangian term
     -beta * split * z is added to Lambda over z (for points of the sub-domain it
     is <= 0, so the bound stays a lower bound there).
+    Decision alignment at the adaptive-slope tie: where an unstable neuron's
+    |u + l| <= tau (u - l), both choices of a are sound and float32 and float64
+    bounds may choose differently; if `decide` holds for its ReLU input z a
+    [B][*shape] boolean tensor (another implementation's choice a = 1), that
+    choice is taken there (and only there).
     """
     R = rows.shape[0]
     lam: Dict[int, torch.Tensor] = {start: rows}
@@ -191,6 +197,10 @@ def backward(net: Oracle, lo, hi, b: int, start: int, rows: torch.Tensor, stop: 
         elif nd.op == "relu":
             z = nd.inputs[0]
             a, s, t, unstable = relaxation(lo[z][b], hi[z][b])
+            if decide is not None and z in decide:
+                l_, u_ = lo[z][b], hi[z][b]
+                tie = unstable & ((u_ + l_).abs() <= tau * (u_ - l_))
+                a = torch.where(tie, decide[z][b].to(f64), a)
             if alpha is not None and k in alpha:
                 a = torch.where(unstable, alpha[k], a)
             if keep is not None:
@@ -252,7 +262,8 @@ def _one_affine_step(net: Oracle, z: int, stop: int) -> bool:
 
 
 def intermediate_bounds(net: Oracle, x0, eps, mode: str, region_start: Optional[int] = None,
-                        batch_idx: Optional[Sequence[int]] = None, row_chunk: int = 4096):
+                        batch_idx: Optional[Sequence[int]] = None, row_chunk: int = 4096,
+                        decide: Optional[Dict[int, torch.Tensor]] = None):
     """Pre-activation bounds used for the ReLU relaxations.
 
     mode "ibp": IBP everywhere.  mode "crown": every ReLU input z, in topological
@@ -266,7 +277,7 @@ def intermediate_bounds(net: Oracle, x0, eps, mode: str, region_start: Optional[
     use them.  A suffix "+unstable" computes rows only for the neurons the initial
     IBP pass leaves unstable (l < 0 < u); the other neurons keep their IBP bounds.
     Rows are independent, so they are processed in chunks of `row_chunk`.  Returns (lo, hi) lists [B][*shape] (float64); only the inputs
-    in batch_idx are refined (all by default).
+    in batch_idx are refined (all by default).  `decide`: tie decisions, see backward().
     """
     lo, hi = ibp(net, x0, eps)
     base, *flags = mode.split("+")
@@ -302,8 +313,8 @@ def intermediate_bounds(net: Oracle, x0, eps, mode: str, region_start: Optional[
                     sel, rows_p, rows_m = sel[keep], rows_p[keep], rows_m[keep]
                     if sel.numel() == 0:
                         continue
-                lz[sel] = backward(net, lo, hi, b, z, rows_p, stop, dc, dr)
-                uz[sel] = -backward(net, lo, hi, b, z, rows_m, stop, dc, dr)
+                lz[sel] = backward(net, lo, hi, b, z, rows_p, stop, dc, dr, decide=decide)
+                uz[sel] = -backward(net, lo, hi, b, z, rows_m, stop, dc, dr, decide=decide)
             if intersect:
                 lz = torch.maximum(lz, lo_ibp[z][b].reshape(-1))
                 uz = torch.minimum(uz, hi_ibp[z][b].reshape(-1))
@@ -313,7 +324,8 @@ def intermediate_bounds(net: Oracle, x0, eps, mode: str, region_start: Optional[
 
 
 def spec_bounds_crown(net: Oracle, lo, hi, x0, eps, C, stop: int = 0,
-                      batch_idx: Optional[Sequence[int]] = None):
+                      batch_idx: Optional[Sequence[int]] = None,
+                      decide: Optional[Dict[int, torch.Tensor]] = None):
     """CROWN bounds of C f(x): lb = lb(C) and ub = -lb(-C) per input."""
     C = _t(C)
     B = C.shape[0]
@@ -323,20 +335,22 @@ def spec_bounds_crown(net: Oracle, lo, hi, x0, eps, C, stop: int = 0,
     ub = torch.full(C.shape[:2], float("nan"), dtype=f64)
     for b in batch_idx:
         dc, dr = _domain(net, lo, hi, x0, eps, b, stop)
-        lb[b] = backward(net, lo, hi, b, L, C[b], stop, dc, dr)
-        ub[b] = -backward(net, lo, hi, b, L, -C[b], stop, dc, dr)
+        lb[b] = backward(net, lo, hi, b, L, C[b], stop, dc, dr, decide=decide)
+        ub[b] = -backward(net, lo, hi, b, L, -C[b], stop, dc, dr, decide=decide)
     return lb, ub
 
 
-def crown_bounds(wl, batch_idx: Optional[Sequence[int]] = None, row_chunk: int = 4096):
+def crown_bounds(wl, batch_idx: Optional[Sequence[int]] = None, row_chunk: int = 4096,
+                 decide: Optional[Dict[int, torch.Tensor]] = None):
     """Whole pipeline for a workload: IBP, intermediate bounds per wl.intermediate,
-    then spec bounds by IBP and by CROWN.  Returns a dict of float64 tensors."""
+    then spec bounds by IBP and by CROWN.  Returns a dict of float64 tensors.
+    `decide`: adaptive-slope choices to take at near-ties (see backward())."""
     net = Oracle(wl.nodes)
     lo_ibp, hi_ibp = ibp(net, wl.x0, wl.eps)
     ibp_lb, ibp_ub = spec_bounds_ibp(net, lo_ibp, hi_ibp, wl.C)
     lo, hi = intermediate_bounds(net, wl.x0, wl.eps, wl.intermediate, wl.region_start,
-                                 batch_idx, row_chunk)
+                                 batch_idx, row_chunk, decide)
     stop = wl.region_start if wl.intermediate.startswith("hybrid") else 0
-    lb, ub = spec_bounds_crown(net, lo, hi, wl.x0, wl.eps, wl.C, stop, batch_idx)
+    lb, ub = spec_bounds_crown(net, lo, hi, wl.x0, wl.eps, wl.C, stop, batch_idx, decide)
     return {"ibp_lo": lo_ibp, "ibp_hi": hi_ibp, "ibp_lb": ibp_lb, "ibp_ub": ibp_ub,
             "lo": lo, "hi": hi, "lb": lb, "ub": ub}

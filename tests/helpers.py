@@ -54,13 +54,54 @@ def near_ties(lo, hi, relu_inputs, tau=1e-5):
     return n
 
 
+def gpu_decisions(wl, out, relu_inputs):
+    """The library's adaptive lower-slope choice (a = 1 iff u >= -l, compared in float32
+    on the bounds it returned) for every neuron of each ReLU input, as [B][*shape]
+    boolean tensors in the oracle's layout."""
+    import torch
+    dec = {}
+    for z in relu_inputs:
+        lo = out["lo"][z].detach().cpu()
+        hi = out["hi"][z].detach().cpu()
+        a = hi >= -lo
+        shape = tuple(wl.nodes[z].shape)
+        if len(shape) == 3:
+            c, h, w = shape
+            a = a.reshape(-1, h, w, c).permute(0, 3, 1, 2)
+        dec[z] = a.reshape((-1,) + shape).clone()
+    return dec
+
+
+def aligned_reference(wl, out, ref, idx, relu_inputs, tau=1e-6):
+    """Decision-aligned parity at the adaptive-slope tie: count the neurons where the
+    oracle sits within tau*(u-l) of the tie u = -l and chose differently from the
+    library; if there are any, recompute the oracle taking the library's choice at
+    exactly those near-tie neurons (both choices are sound).  Returns (reference,
+    number of aligned neurons)."""
+    import torch
+    from oracle import crown_bounds
+    dec = gpu_decisions(wl, out, relu_inputs)
+    flips = 0
+    for z in relu_inputs:
+        l, u = ref["lo"][z][idx], ref["hi"][z][idx]
+        unst = (l < 0) & (u > 0)
+        tie = unst & ((u + l).abs() <= tau * (u - l))
+        flips += int((tie & ((u >= -l) != dec[z][idx])).sum())
+    if flips == 0:
+        return ref, 0
+    return crown_bounds(wl, batch_idx=idx, decide=dec), flips
+
+
 def compare_workload(wl, out, ref, batch_idx=None, check_nodes=True, keys=("lb", "ub", "ibp_lb", "ibp_ub")):
-    """Elementwise parity of a vb_crown result with the oracle's crown_bounds result."""
+    """Elementwise parity of a vb_crown result with the oracle's crown_bounds result
+    (decision-aligned at adaptive-slope ties, see aligned_reference)."""
     idx = list(range(wl.batch)) if batch_idx is None else list(batch_idx)
     relu_inputs = [wl.nodes[k].inputs[0] for k, n in enumerate(wl.nodes) if n.op == "relu"]
     ties = near_ties({z: ref["lo"][z][idx] for z in relu_inputs},
                      {z: ref["hi"][z][idx] for z in relu_inputs}, relu_inputs)
-    print(f"{wl.name} ({wl.intermediate}): near-tie neurons in the oracle: {ties}", flush=True)
+    ref, aligned = aligned_reference(wl, out, ref, idx, relu_inputs)
+    print(f"{wl.name} ({wl.intermediate}): near-tie neurons in the oracle: {ties}; "
+          f"decisions aligned to the library's: {aligned}", flush=True)
     worst = 0.0
     for key in keys:
         worst = max(worst, assert_close(out[key][idx], ref[key][idx], key))

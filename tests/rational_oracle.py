@@ -254,13 +254,17 @@ def _one_affine_step_from(net, z, stop):
 
 
 def bounds(wl, b: int, mode: str):
-    """IBP, intermediate bounds by `mode` (ibp | crown | hybrid, optionally +ibp) and
-    the spec bounds by IBP and CROWN for input b of a workload; all exact."""
+    """IBP, intermediate bounds by `mode` (ibp | crown | hybrid, optionally +ibp and/or
+    +unstable) and the spec bounds by IBP and CROWN for input b of a workload; all
+    exact.  +ibp: each new bound is clipped to the first IBP pass's; +unstable: only
+    neurons that IBP pass leaves with l < 0 < u get new bounds."""
     net = ExactNet(wl.nodes)
     x0 = wl.x0[b].reshape(-1)
     lo, hi = ibp(net, x0, wl.eps)
     ibp_lb, ibp_ub = spec_ibp(net, lo, hi, wl.C[b])
-    base, _, suffix = mode.partition("+")
+    base, *flags = mode.split("+")
+    suffix = "ibp" if "ibp" in flags else ""
+    only_unstable = "unstable" in flags
     ibp_lo = [list(v) for v in lo]
     ibp_hi = [list(v) for v in hi]
     stop = 0
@@ -276,6 +280,10 @@ def bounds(wl, b: int, mode: str):
             n = net.size[z]
             new_lo, new_hi = [], []
             for j in range(n):
+                if only_unstable and not (ibp_lo[z][j] < 0 < ibp_hi[z][j]):
+                    new_lo.append(lo[z][j])
+                    new_hi.append(hi[z][j])
+                    continue
                 e = [ZERO] * n
                 e[j] = ONE
                 lj = lower_bound(net, lo, hi, z, e, stop, dc, dr)
@@ -295,6 +303,19 @@ def bounds(wl, b: int, mode: str):
         lb.append(lower_bound(net, lo, hi, L, r, stop, dc, dr))
         ub.append(-lower_bound(net, lo, hi, L, [-v for v in r], stop, dc, dr))
     return {"lo": lo, "hi": hi, "ibp_lb": ibp_lb, "ibp_ub": ibp_ub, "lb": lb, "ub": ub}
+
+
+def row_lower_bounds(wl, lo, hi, b: int, start: int, rows, alpha: Dict[int, np.ndarray], stop: int = 0):
+    """Lower bounds of arbitrary rows over node `start` with per-row lower slopes:
+    alpha[k] [R][n] for the ReLU nodes k between stop and start."""
+    net = ExactNet(wl.nodes)
+    x0 = wl.x0[b].reshape(-1)
+    dc, dr = _box(lo, hi, x0, wl.eps, net, stop)
+    out = []
+    for i, row in enumerate(np.asarray(rows)):
+        al = {k: exact(np.asarray(v)[i]) for k, v in alpha.items()}
+        out.append(lower_bound(net, lo, hi, start, exact(row), stop, dc, dr, al))
+    return out
 
 
 def alpha_lower_bounds(wl, lo, hi, b: int, alpha: Dict[int, np.ndarray], stop: int = 0):

@@ -43,6 +43,27 @@ def test_cnn_small(lbp, method, convs, fcs, in_shape, batch, eps, seed):
     compare_workload(wl, out, ref)
 
 
+@pytest.mark.parametrize("mode", ["hybrid", "hybrid+ibp"])
+def test_cnn_hybrid_region_inside_conv_chain(lbp, mode):
+    """The CROWN region starts at the first ReLU of a CNN (its IBP box is the domain):
+    the identity rows of the third conv walk conv -> ReLU -> conv on footprint windows
+    (the library's chain walker, checked through its own choice) and are concretised
+    over that ReLU's box; every node's bounds and the spec bounds against the oracle."""
+    import ctypes
+    wl = wk.cnn(2, 0.03, 71, convs=((8, 1), (8, 2), (16, 1), (16, 1)), fcs=(10,), in_shape=(3, 12, 12),
+                intermediate=mode)
+    wl.region_start = 2
+    net, x, C = lbp.prepare(wl)
+    f = lbp.lib().vb_testing_identity_path
+    f.restype = ctypes.c_int32
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
+    assert f(ctypes.cast(net.gp, ctypes.c_void_p), 5, 2) == 1, "the third conv's rows do not take the chain walker"
+    ref = crown_bounds(wl)
+    out = lbp.crown(net, x, float(wl.eps), C, wl.intermediate, wl.region_start)
+    torch.cuda.synchronize()
+    compare_workload(wl, out, ref)
+
+
 def test_config3_full_size_sampled_inputs(lbp):
     wl = wk.config(3)
     print(wl.name, flush=True)

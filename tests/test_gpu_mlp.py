@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import workloads as wk
-from helpers import assert_close, ensure_built, near_ties
+from helpers import compare_workload, ensure_built
 from oracle import crown_bounds
 
 pytestmark = pytest.mark.gpu
@@ -25,19 +25,7 @@ def _run(lbp, wl, method=None):
 
 
 def _compare(wl, out, ref, batch_idx=None, check_nodes=True):
-    idx = list(range(wl.batch)) if batch_idx is None else list(batch_idx)
-    relu_inputs = [wl.nodes[k].inputs[0] for k, n in enumerate(wl.nodes) if n.op == "relu"]
-    ties = near_ties({z: ref["lo"][z][idx] for z in relu_inputs},
-                     {z: ref["hi"][z][idx] for z in relu_inputs}, relu_inputs)
-    print(f"{wl.name}: near-tie neurons in the oracle: {ties}", flush=True)
-    for key in ("lb", "ub", "ibp_lb", "ibp_ub"):
-        assert_close(out[key][idx], ref[key][idx], key)
-    if check_nodes:
-        for k, nd in enumerate(wl.nodes):
-            if k == 0 or nd.op not in ("linear", "conv", "add"):
-                continue
-            assert_close(out["lo"][k][idx], ref["lo"][k][idx].reshape(len(idx), -1), f"lo[{k}]")
-            assert_close(out["hi"][k][idx], ref["hi"][k][idx].reshape(len(idx), -1), f"hi[{k}]")
+    compare_workload(wl, out, ref, batch_idx, check_nodes)
 
 
 @pytest.mark.parametrize("widths,batch,eps,seed", [

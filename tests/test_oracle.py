@@ -97,6 +97,24 @@ def test_single_relu_closed_form():
     assert (r["lb"].item(), r["ub"].item()) == (pytest.approx(2.0), pytest.approx(4.0))
 
 
+def test_tie_decision_alignment_closed_form():
+    """At the adaptive-slope tie u = -l both lower slopes are sound: with z on [-1, 1]
+    the lower bound of relu(z) is min(a z) = -1 for a = 1 (the oracle's own choice) and
+    0 for a = 0.  `decide` takes another implementation's choice there, and only at
+    near-ties: on [-1, 3] the slope stays 1 whatever `decide` says."""
+    import torch
+    nodes = [Node("input", (), (1,)),
+             Node("linear", (0,), (1,), np.array([[1.0]], np.float32), np.array([0.0], np.float32)),
+             Node("relu", (1,), (1,)),
+             Node("linear", (2,), (1,), np.array([[1.0]], np.float32), np.array([0.0], np.float32))]
+    wl = _wl(nodes, [[0.0]], 1.0, [[[1.0]]])
+    assert crown_bounds(wl)["lb"].item() == pytest.approx(-1.0)
+    assert crown_bounds(wl, decide={1: torch.tensor([[True]])})["lb"].item() == pytest.approx(-1.0)
+    assert crown_bounds(wl, decide={1: torch.tensor([[False]])})["lb"].item() == pytest.approx(0.0)
+    wl = _wl(nodes, [[1.0]], 2.0, [[[1.0]]])
+    assert crown_bounds(wl, decide={1: torch.tensor([[False]])})["lb"].item() == pytest.approx(-1.0)
+
+
 def test_relaxation_cases():
     l = torch.tensor([-2.0, 0.0, 1.0, -1.0, -3.0, 0.0, -2.0], dtype=torch.float64)
     u = torch.tensor([-1.0, 2.0, 2.0, 3.0, 1.0, 0.0, 2.0], dtype=torch.float64)

@@ -29,7 +29,8 @@ from oracle.alpha import alpha_crown, alpha_init, evaluate
 
 import rational_oracle as rq
 
-MODES = ["ibp", "crown", "hybrid", "crown+ibp", "hybrid+ibp"]
+MODES = ["ibp", "crown", "hybrid", "crown+ibp", "hybrid+ibp", "crown+unstable", "crown+ibp+unstable",
+         "hybrid+ibp+unstable"]
 
 
 def _nets():
@@ -200,3 +201,130 @@ def test_alpha_crown_iterates_follow_the_adam_closed_form():
         assert res["lb_steps"][t, 0, 0].item() == pytest.approx(l_z * a_t + b3, abs=1e-12), t
     assert res["alpha"][0][2].item() == 0.0
     assert res["best"][0, 0].item() == pytest.approx(b3, abs=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# unstable-only rows
+
+
+def test_unstable_only_nets_mix_stable_and_unstable_neurons():
+    # the +unstable modes differ from the full ones only where IBP already settles a
+    # neuron of a refined layer: some nets must have both kinds there
+    mixed = 0
+    for wl in NETS:
+        net = Oracle(wl.nodes)
+        lo, hi = intermediate_bounds(net, wl.x0, wl.eps, "ibp")
+        for r in net.relu_nodes():
+            z = wl.nodes[r].inputs[0]
+            if z <= 0 or _one_step(net, z):
+                continue
+            u = ((lo[z] < 0) & (hi[z] > 0)).reshape(-1)
+            mixed += int(bool(u.any()) and not bool(u.all()))
+    assert mixed >= 3
+
+
+def _one_step(net, z):
+    from oracle.bounds import _one_affine_step
+    return _one_affine_step(net, z, 0)
+
+
+@pytest.mark.parametrize("i", range(len(NETS)))
+def test_unstable_only_with_intersection_keeps_every_relaxation(i):
+    """With the IBP intersection, a neuron IBP already settles keeps its class under
+    CROWN, so every ReLU relaxation is the same with rows for all neurons or for the
+    unstable ones only: the spec bounds agree to the last bit, and so do the bounds
+    of every neuron IBP leaves unstable."""
+    wl = NETS[i]
+    wl.intermediate = "crown+ibp"
+    full = crown_bounds(wl)
+    wl.intermediate = "crown+ibp+unstable"
+    part = crown_bounds(wl)
+    assert torch.equal(full["lb"], part["lb"]) and torch.equal(full["ub"], part["ub"])
+    net = Oracle(wl.nodes)
+    lo0, hi0 = intermediate_bounds(net, wl.x0, wl.eps, "ibp")
+    for r in net.relu_nodes():
+        z = wl.nodes[r].inputs[0]
+        u = (lo0[z] < 0) & (hi0[z] > 0)
+        assert torch.equal(full["lo"][z][u], part["lo"][z][u]) and torch.equal(full["hi"][z][u], part["hi"][z][u])
+
+
+# ---------------------------------------------------------------------------
+# alpha-CROWN on the identity rows of intermediate layers
+
+
+@pytest.mark.parametrize("i", [0, 1, 3, 5])
+def test_alpha_rows_evaluation_equals_exact_arithmetic(i):
+    """The per-row slope evaluation that alpha_rows optimises (identity rows over an
+    intermediate node, each row with its own slopes for every ReLU below it) equals
+    the exact back-substitution with the same slopes."""
+    from oracle.bounds import _domain, _identity_rows, backward
+    wl = NETS[i]
+    net = Oracle(wl.nodes)
+    lo, hi = intermediate_bounds(net, wl.x0, wl.eps, "crown")
+    ex = rq.bounds(wl, 0, "crown")
+    rng = np.random.default_rng(50 + i)
+    checked = 0
+    for r in net.relu_nodes():
+        z = wl.nodes[r].inputs[0]
+        if z <= 0 or _one_step(net, z):
+            continue
+        shape = net.shape[z]
+        n = int(np.prod(shape))
+        rows = torch.cat([_identity_rows(shape, 1.0).reshape(n, -1), _identity_rows(shape, -1.0).reshape(n, -1)])
+        al = {k: torch.as_tensor(rng.uniform(0, 1, (2 * n,) + net.shape[wl.nodes[k].inputs[0]]))
+              for k in net.relu_nodes() if k < z}
+        dc, dr = _domain(net, lo, hi, wl.x0, wl.eps, 0, 0)
+        got = backward(net, lo, hi, 0, z, rows.reshape((2 * n,) + tuple(shape)), 0, dc, dr, alpha=al)
+        want = rq.row_lower_bounds(wl, ex["lo"], ex["hi"], 0, z, rows.numpy(),
+                                   {k: v.reshape(2 * n, -1).numpy() for k, v in al.items()})
+        _close(got, want, f"{wl.name} alpha rows over node {z}")
+        checked += 1
+    assert checked >= 1
+
+
+def test_alpha_rows_are_independent():
+    """Each row's slopes follow the gradient of its own bound: optimising two rows
+    together gives each the trajectory it has alone."""
+    from oracle.alpha import alpha_rows
+    from oracle.bounds import _identity_rows
+    wl = NETS[1]
+    net = Oracle(wl.nodes)
+    lo, hi = intermediate_bounds(net, wl.x0, wl.eps, "ibp")
+    z = [wl.nodes[r].inputs[0] for r in net.relu_nodes()][-1]
+    shape = net.shape[z]
+    n = int(np.prod(shape))
+    rows = torch.cat([_identity_rows(shape, 1.0).reshape(n, -1), _identity_rows(shape, -1.0).reshape(n, -1)])
+    both, _ = alpha_rows(wl, lo, hi, 0, z, rows, 6, 0.1)
+    for j in (0, n + 1):
+        alone, _ = alpha_rows(wl, lo, hi, 0, z, rows[j:j + 1], 6, 0.1)
+        assert torch.allclose(both[:, j], alone[:, 0], rtol=1e-12, atol=1e-12)
+
+
+def test_alpha_intermediate_bounds_tighter_than_crown_and_below_the_exact_range():
+    """alpha-CROWN intermediate bounds start from CROWN (its first iterate) and keep
+    the best iterate, so they are at least as tight as CROWN's; and they stay sound:
+    inside the exact range of each neuron over the input box, found by linear
+    programming per activation pattern on 2-input networks."""
+    from oracle.alpha import alpha_intermediate_bounds
+    from test_oracle_bab import exact_min
+    checked = 0
+    for seed in range(4):
+        wl = wk.tiny_mlp([2, 5, 5, 4, 2], 0.3, 900 + seed, batch=1)
+        net = Oracle(wl.nodes)
+        lo_c, hi_c = intermediate_bounds(net, wl.x0, wl.eps, "crown")
+        lo_a, hi_a = alpha_intermediate_bounds(wl, 8, 0.1)
+        for r in net.relu_nodes():
+            z = wl.nodes[r].inputs[0]
+            assert bool((lo_a[z] >= lo_c[z] - 1e-12).all()) and bool((hi_a[z] <= hi_c[z] + 1e-12).all())
+            if _one_step(net, z):
+                continue  # (IBP there: exact)
+            # exact range of z_j over the box: the network cut after node z
+            cut = wk.Workload(wl.name, wl.cfg, wl.nodes[:z + 1], wl.x0, wl.eps, wl.labels, wl.C, "ibp")
+            for j in range(net.shape[z][0]):
+                e = np.zeros(net.shape[z][0])
+                e[j] = 1.0
+                lo_ex = exact_min(cut, 0, e)
+                hi_ex = -exact_min(cut, 0, -e)
+                assert lo_a[z][0, j].item() <= lo_ex + 1e-9 and hi_a[z][0, j].item() >= hi_ex - 1e-9
+                checked += 1
+    assert checked > 10
