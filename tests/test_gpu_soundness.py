@@ -87,20 +87,27 @@ def _check(wl, b, bounds, node_bounds=None, chunk=10_000, dtype=torch.float64, s
 
 def _crown(lbp, wl):
     net, x, C = lbp.prepare(wl)
-    out = lbp.crown(net, x, float(wl.eps), C, wl.intermediate, wl.region_start)
+    # the whole-batch workspace of the residual workload exceeds the device: a
+    # smaller one makes the library process the batch in chunks (same results)
+    need = net.workspace_size(wl.batch, wl.m, wl.intermediate, wl.region_start or 0)
+    ws = net.workspace(min(need, int(torch.cuda.mem_get_info()[0] * 0.8)))
+    out = lbp.crown(net, x, float(wl.eps), C, wl.intermediate, wl.region_start, ws=ws)
     torch.cuda.synchronize()
     return out
 
 
-@pytest.mark.parametrize("cfg,instances", [(1, range(16)), (2, (0, 21, 42, 63)), (3, (0, 31))])
-def test_sound_crown_and_ibp(lbp, cfg, instances):
+# every instance of every workload; the convolutional networks are sampled with a
+# float32 forward pass (float64 convolutions are slow), whose rounding the
+# tolerance of the check covers
+@pytest.mark.parametrize("cfg,dtype", [(1, torch.float64), (2, torch.float64), (3, torch.float32)])
+def test_sound_crown_and_ibp(lbp, cfg, dtype):
     wl = wk.config(cfg)
     print(wl.name, flush=True)
     out = _crown(lbp, wl)
     relu_inputs = [wl.nodes[k].inputs[0] for k, n in enumerate(wl.nodes) if n.op == "relu"]
-    for b in instances:
+    for b in range(wl.batch):
         nb = {z: (out["lo"][z][b], out["hi"][z][b]) for z in relu_inputs}
-        w = _check(wl, b, [(out["lb"][b], out["ub"][b]), (out["ibp_lb"][b], out["ibp_ub"][b])], nb)
+        w = _check(wl, b, [(out["lb"][b], out["ub"][b]), (out["ibp_lb"][b], out["ibp_ub"][b])], nb, dtype=dtype)
         print(f"  input {b}: sound; smallest gap between a sampled value and a bound: {-w:.4g}", flush=True)
 
 
@@ -113,16 +120,74 @@ def test_sound_alpha_crown_iterates(lbp):
     best, lb_steps, _ = lbp.alpha_crown(net, x, float(wl.eps), C, out["lo"], out["hi"], wl.alpha_steps, wl.alpha_lr,
                                         layout=lay)
     torch.cuda.synchronize()
-    for b in (0, 15):
+    for b in range(wl.batch):
         bounds = [(lb_steps[t][b], torch.full_like(best[b], float("inf"))) for t in range(lb_steps.shape[0])]
         bounds.append((best[b], out["ub"][b]))
-        _check(wl, b, bounds)
+        _check(wl, b, bounds, dtype=torch.float32)
 
 
-def test_sound_residual(lbp):
-    wl = wk.config(5, batch=1)
+@pytest.fixture(scope="module")
+def residual_out(lbp):
+    wl = wk.config(5)
     print(wl.name, flush=True)
     out = _crown(lbp, wl)
-    # float32 forward for this network (float64 convolutions are slow); the
-    # tolerance of the check covers float32 rounding of the sampled values
-    _check(wl, 0, [(out["lb"][0], out["ub"][0]), (out["ibp_lb"][0], out["ibp_ub"][0])], dtype=torch.float32)
+    return wl, {k: out[k].cpu() for k in ("lb", "ub", "ibp_lb", "ibp_ub")}
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_sound_residual(lbp, residual_out, part):
+    """All 32 inputs of the residual workload, eight per test."""
+    wl, out = residual_out
+    for b in range(8 * part, 8 * part + 8):
+        bd = [(out["lb"][b].cuda(), out["ub"][b].cuda()), (out["ibp_lb"][b].cuda(), out["ibp_ub"][b].cuda())]
+        w = _check(wl, b, bd, dtype=torch.float32)
+        print(f"  input {b}: sound; smallest gap {-w:.4g}", flush=True)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_sound_at_crown_attaining_vertices(lbp, cfg):
+    """Row r's CROWN bound is the minimum over the input box of its linear bound
+    Lambda_r x + beta_r, reached at the vertex x0 - eps sign(Lambda_r).  The linear
+    bounds come from the library (vb_crown_backward returning Lambda over the input);
+    at each of those 2m vertices per input, the network's value (float64 forward)
+    must respect every spec bound and every intermediate bound."""
+    wl = wk.config(cfg)
+    print(wl.name, flush=True)
+    net, x, C = lbp.prepare(wl)
+    out = lbp.crown(net, x, float(wl.eps), C, wl.intermediate, wl.region_start)
+    L = len(wl.nodes) - 1
+    ws = net.workspace(net.workspace_size(wl.batch, wl.m, wl.intermediate, 0))
+    _, _, A, _ = lbp.crown_backward(net, L, 0, out["lo"], out["hi"], x, float(wl.eps), ws, C=C, linear=True)
+    torch.cuda.synchronize()
+    relu_inputs = [wl.nodes[k].inputs[0] for k, n in enumerate(wl.nodes) if n.op == "relu"]
+    in_shape = tuple(wl.nodes[0].shape)
+    eps = float(np.float32(wl.eps))
+    worst = float("inf")
+    for b in range(wl.batch):
+        x0 = torch.as_tensor(wl.x0[b], dtype=torch.float64, device="cuda")
+        # Lambda rows are over the channels-last input; the vertices go back to (c, h, w)
+        sg = torch.sign(A[b].double())
+        if len(in_shape) == 3:
+            c, h, w = in_shape
+            sg = sg.reshape(-1, h, w, c).permute(0, 3, 1, 2)
+        else:
+            sg = sg.reshape((-1,) + in_shape)
+        xv = x0 - eps * sg
+        vals = _forward(wl.nodes, xv)
+        spec = vals[-1] @ torch.as_tensor(wl.C[b], dtype=torch.float64, device="cuda").T
+        lb = out["lb"][b].double()
+        ub = out["ub"][b].double()
+        assert bool((spec >= lb - (1e-5 + 1e-4 * lb.abs())).all()), f"input {b}: a vertex value below its lower bound"
+        assert bool((spec <= ub + (1e-5 + 1e-4 * ub.abs())).all()), f"input {b}: a vertex value above its upper bound"
+        m = wl.m
+        own = torch.cat([spec[torch.arange(m), torch.arange(m)] - lb, ub - spec[m + torch.arange(m), torch.arange(m)]])
+        worst = min(worst, float(own.min()))
+        for z in relu_inputs:
+            v = vals[z]
+            if v.dim() == 4:
+                v = v.permute(0, 2, 3, 1)
+            v = v.reshape(v.shape[0], -1)
+            lo, hi = out["lo"][z][b].double(), out["hi"][z][b].double()
+            assert bool((v >= lo - (1e-5 + 1e-4 * lo.abs())).all()), f"input {b}: node {z} below its bound at a vertex"
+            assert bool((v <= hi + (1e-5 + 1e-4 * hi.abs())).all()), f"input {b}: node {z} above its bound at a vertex"
+    print(f"  smallest gap between a row's value at its own vertex and its bound: {worst:.4g}", flush=True)
