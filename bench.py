@@ -608,10 +608,16 @@ def main():
     }
     if not args.no_extra:
         extra = {}
-        for cfg in (1, 2, 3, 4, 5):
+        for cfg in (1, 2, 3, 4, 5, "3crown"):
             if cfg == args.workload:
                 continue
-            w = wk.config(cfg)
+            if cfg == "3crown":
+                # the CNN with CROWN intermediate bounds (footprint rows through its convs)
+                w = wk.config(3)
+                w.intermediate = "crown"
+                w.name = w.name.replace("_ibp", "_crown")
+            else:
+                w = wk.config(cfg)
             e_ms, e_prof, e_res, _, e_alpha = run_workload(w, 5 if cfg != 5 else 2, 2)
             e_fl = algorithmic_flops(w)
             extra[w.name] = {"ms_per_step": round(e_ms, 4),

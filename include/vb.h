@@ -83,8 +83,10 @@ typedef struct {
                              /* of a Linear ReLU input that its IBP bounds leave  */
                              /* unstable (l < 0 < u); the others keep their IBP   */
                              /* bounds (their relaxation is already exact).  The  */
-                             /* call then SYNCHRONISES the stream once per such   */
-                             /* layer (launches are sized to the largest count)   */
+                             /* neuron lists are built on the device; launches    */
+                             /* cover every neuron and the work of the stable     */
+                             /* ones is skipped by whole workgroups (no host      */
+                             /* synchronisation)                                  */
 #define VB_ALPHA_ROWS    32  /* flag for vb_workspace_size: also enough for       */
                              /* vb_alpha_step_rows on the identity rows of every  */
                              /* ReLU input (alpha-CROWN intermediate bounds)      */

@@ -300,6 +300,9 @@ struct Backward {
   const int* sel = nullptr;
   const int* cnt = nullptr;
   int U = 0;
+  // the current chunk's live-row counts for the GEMMs (selected rows), or NULL
+  const int* live_cnt = nullptr;
+  int live_u = 0;
 
   int alloc() {
     for (int i = 0; i < NPOOL; ++i)
@@ -379,6 +382,8 @@ std::vector<ProfDone> g_prof_done;  // per launch, from the last vb_profile_stop
 
 vb_status run_gemm_reduce(Backward& B, GemmDesc& d, int rows, int P, bool reduce, double alg_flops = 0.0) {
   d.part = reduce ? B.part : nullptr;
+  d.live_cnt = B.live_cnt;
+  d.live_u = B.live_u;
   d.part_ld = gemm_ntiles(d);
   if (reduce && (size_t)d.M * d.part_ld > B.part_floats)
     return fail(VB_ENOMEM, "internal: partial buffer too small (%lld > %zu)", (long long)d.M * d.part_ld, B.part_floats);
@@ -1931,7 +1936,10 @@ vb_status backward_all(Backward& B, int start, int stop, const float* C, int m, 
       c.cnt = B.cnt + b0;
       c.U = B.U;
     }
+    B.live_cnt = c.cnt;
+    B.live_u = c.U;
     vb_status s = backward_chunk(B, c, R);
+    B.live_cnt = nullptr;
     if (s) return s;
     s = after(B.rowacc, b0, n);
     if (s) return s;
@@ -2400,8 +2408,9 @@ extern "C" vb_status vb_crown(const vb_graph* g, int32_t batch, const float* x_c
       if (z <= stop || one_affine_step(G, z, stop)) continue;
       if (unstable_only && G.n[z].op == VB_LINEAR) {
         // rows only for the neurons the bounds so far (IBP) leave unstable, listed on
-        // the device; the launches are sized to the largest count over the batch,
-        // which is read back here (one synchronisation per layer)
+        // the device (input b's first cnt[b] rows of each sign); the launches cover
+        // all n rows per sign and every workgroup whose rows are all past the count
+        // returns at once, so nothing is read back
         const long long n = G.n[z].size, nmax = (long long)(select_floats(G, batch) - align_up((size_t)batch * 4) / 4) /
                                                 (2 * batch);
         int* idx = (int*)((char*)ws + align_up(wt_floats(G) * 4));
@@ -2409,11 +2418,7 @@ extern "C" vb_status vb_crown(const vb_graph* g, int32_t batch, const float* x_c
         int* cnt = sel + align_up((size_t)batch * nmax * 4) / 4;
         HIPCHK(launch_alpha_layout(node_lo[z], node_hi[z], batch, n, idx, cnt, st));
         HIPCHK(launch_rank_to_list(idx, batch, (int)n, sel, st));
-        std::vector<int> hc(batch);
-        HIPCHK(hipMemcpyAsync(hc.data(), cnt, (size_t)batch * 4, hipMemcpyDeviceToHost, st));
-        HIPCHK(hipStreamSynchronize(st));
-        const int U = *std::max_element(hc.begin(), hc.end());
-        if (U == 0) continue;  // every neuron stable: the IBP bounds stay
+        const int U = (int)n;
         s = crown_backward_impl(G, batch, z, stop, nullptr, 0, node_lo, node_hi, dom, node_lo[z], node_hi[z], ws,
                                 ws_bytes, st, nullptr, nullptr, nullptr, intersect, nullptr, true, sel, cnt, U,
                                 select_floats(G, batch));

@@ -238,6 +238,28 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
     tn = tile - tm * nt;
   }
   const int m0 = tm * BM, n0 = tn * BN;
+  if (d.live_cnt) {
+    // selected-neuron rows: skip a tile none of whose rows is live
+    bool any = false;
+    for (int r = tid; r < BM; r += NTHR) {
+      const int m = m0 + r;
+      int row = -1;
+      if (DENSE) {
+        if (m < d.M) row = m;
+      } else {
+        const GPos g = gdecode(d, m);
+        if (g.valid) row = g.row;
+      }
+      if (row >= 0) {
+        const int per = 2 * d.live_u;
+        const int b = row / per;
+        int u = row - b * per;
+        if (u >= d.live_u) u -= d.live_u;
+        any = any || u < d.live_cnt[b];
+      }
+    }
+    if (!__syncthreads_or(any)) return;
+  }
 
   // register staging of the next K stage
   float4 ra[NA][FAST ? AV : 1];
@@ -936,7 +958,15 @@ bool finalize(GemmDesc& d) {
     // output position per 32 rows)
     const long long rows = d.M / (d.gh * d.gw), P = (long long)d.gh * d.gw;
     int sh = 6;
-    if ((((rows + 63) >> 6 << 6) - rows) * 8 > rows) sh = 5;
+    if (d.patch && rows % 128 == 0) {
+      // footprint rows: a 128-row tile then holds one window cell of 128
+      // consecutive rows (one start pixel when it has >= 128 channels), so all
+      // its rows read the same taps and the tap mask skips exactly what none of
+      // them reads
+      sh = 7;
+    } else if ((((rows + 63) >> 6 << 6) - rows) * 8 > rows) {
+      sh = 5;
+    }
     const long long mt = ((rows + (1LL << sh) - 1) >> sh << sh) * P;
     if (mt > INT32_MAX - 256) return false;
     // the epilogue's per-block element offsets are 32-bit

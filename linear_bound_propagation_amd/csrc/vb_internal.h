@@ -100,6 +100,11 @@ struct GemmDesc {
   const float* B1;
   long long a1_row_stride;
   int tap_src1, hs1, ws1, ssy1, soy1, ssx1, sox1, src_h1, src_w1;
+  // rows of selected neurons (unstable-only identity rows): row r of batch element
+  // b = r / (2 live_u) is live iff (r mod live_u) < live_cnt[b]; a workgroup whose
+  // rows are all dead returns at once (their outputs and partials are never read)
+  const int* live_cnt;
+  int live_u;
   int Mt;                      // filled by launch_gemm: size of the tile index space (gather: padded)
   int rb_shift;                // filled by launch_gemm: log2 of the rows per block (gather)
   // ---- epilogue

@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) void identity_linear_kernel(const float* __res
   const float sg = r < nr ? 1.f : -1.f;
   float* dst = lam + row * n_in;
   if (sel && u >= cnt[b]) {
-    // a selected-rows call pads every input to the largest count: no neuron here
+    // past this input's count of selected neurons: a zero row
     for (int j = lane; j < n_in; j += 64) dst[j] = 0.f;
     if (lane == 0) rowacc[row] = 0.f;
     return;
@@ -186,7 +186,8 @@ __global__ __launch_bounds__(256) void identity_linear_kernel(const float* __res
   if (lane == 0) rowacc[row] = (bias_start ? sg * bias_start[i] : 0.f) + s;
 }
 
-// The same rows, a workgroup per (input b, IL_RI neurons): the relaxation
+// The same rows, a workgroup per (input b, IL_RI neurons) (with a neuron list,
+// rows past the input's count are not written): the relaxation
 // coefficients of b's neurons are worked out once per column and serve the
 // 2 * IL_RI rows (both signs) of the group, each weight float4 is loaded once
 // for its two rows, and every access is a 16-byte one (n_in % 4 == 0).  A
@@ -208,6 +209,9 @@ __global__ __launch_bounds__(256) void identity_linear4_kernel(const float* __re
   const int u0 = (blockIdx.x - b * groups) * IL_RI;
   const int tid = threadIdx.x;
   const int nb = sel ? cnt[b] : nr;  // live rows of this input
+  // rows past the live count are never read (their GEMM tiles return at once,
+  // the finishing step skips them): a group with no live row writes nothing
+  if (u0 >= nb) return;
   int src[IL_RI];
 #pragma unroll
   for (int q = 0; q < IL_RI; ++q) {
@@ -232,9 +236,8 @@ __global__ __launch_bounds__(256) void identity_linear4_kernel(const float* __re
     }
 #pragma unroll
     for (int q = 0; q < IL_RI; ++q) {
-      if (u0 + q >= nr) break;
-      float4 w4 = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (src[q] >= 0) w4 = *reinterpret_cast<const float4*>(W + (long long)src[q] * n_in + j);
+      if (u0 + q >= nb) break;
+      const float4 w4 = *reinterpret_cast<const float4*>(W + (long long)src[q] * n_in + j);
       const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
       float op[4], om[4];
 #pragma unroll
@@ -267,10 +270,10 @@ __global__ __launch_bounds__(256) void identity_linear4_kernel(const float* __re
   if (tid < 2 * IL_RI) {
     const int q = tid % IL_RI;
     const bool minus = tid >= IL_RI;
-    if (u0 + q < nr) {
+    if (u0 + q < nb) {
       const float tot = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
       const float sg = minus ? -1.f : 1.f;
-      rowacc[(minus ? rm : rp) + q] = src[q] >= 0 ? (bias_start ? sg * bias_start[src[q]] : 0.f) + tot : 0.f;
+      rowacc[(minus ? rm : rp) + q] = (bias_start ? sg * bias_start[src[q]] : 0.f) + tot;
     }
   }
 }
@@ -1057,10 +1060,8 @@ hipError_t launch_gap_expand(const float* src, int rows, int P, int C, float sca
   return hipGetLastError();
 }
 
-// one block per row: rowacc[r] (+)= sum A c - |A| r  (+ bias), optional lb/ub.
-// VEC: n % 4 == 0 and 16-byte aligned rows; each thread issues the float4 loads
-// of up to four strides before accumulating, so a row's whole read is in flight.
-template <bool VEC>
+// one block per row: rowacc[r] (+)= sum A c - |A| r  (+ bias), optional lb/ub
+// (any n and alignment).
 __global__ __launch_bounds__(256) void concretize_rows_kernel(const float* __restrict__ A, int n, int rows_per_b,
                                                               const float* __restrict__ center,
                                                               const float* __restrict__ radius, float eps,
@@ -1072,36 +1073,7 @@ __global__ __launch_bounds__(256) void concretize_rows_kernel(const float* __res
   const int row = blockIdx.x;
   const long long b = row / rows_per_b;
   float sc = 0.f, sr = 0.f;
-  if (VEC) {
-    const int n4 = n >> 2;
-    const float4* a4 = reinterpret_cast<const float4*>(A + (long long)row * n);
-    const long long bo = b * n4;
-    for (int j0 = threadIdx.x; j0 < n4; j0 += 4 * 256) {
-      float4 a[4], c[4], r[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = j0 + 256 * u;
-        const bool ok = j < n4;
-        const int jj = ok ? j : j0;
-        a[u] = a4[jj];
-        if (center) {
-          c[u] = reinterpret_cast<const float4*>(center)[bo + jj];
-          r[u] = radius ? reinterpret_cast<const float4*>(radius)[bo + jj] : make_float4(eps, eps, eps, eps);
-        } else {
-          const float4 l = reinterpret_cast<const float4*>(lo)[bo + jj];
-          const float4 h = reinterpret_cast<const float4*>(hi)[bo + jj];
-          c[u] = make_float4((l.x + h.x) * 0.5f, (l.y + h.y) * 0.5f, (l.z + h.z) * 0.5f, (l.w + h.w) * 0.5f);
-          r[u] = make_float4((h.x - l.x) * 0.5f, (h.y - l.y) * 0.5f, (h.z - l.z) * 0.5f, (h.w - l.w) * 0.5f);
-        }
-        if (!ok) a[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        sc += a[u].x * c[u].x + a[u].y * c[u].y + a[u].z * c[u].z + a[u].w * c[u].w;
-        sr += fabsf(a[u].x) * r[u].x + fabsf(a[u].y) * r[u].y + fabsf(a[u].z) * r[u].z + fabsf(a[u].w) * r[u].w;
-      }
-    }
-  } else {
+  {
     for (int j = threadIdx.x; j < n; j += 256) {
       const float a = A[(long long)row * n + j];
       float c, r;
@@ -1127,6 +1099,62 @@ __global__ __launch_bounds__(256) void concretize_rows_kernel(const float* __res
   }
 }
 
+// The same for n % 4 == 0 and 16-byte aligned rows, one wavefront per row (four
+// rows per workgroup): a lane issues the non-temporal float4 loads of four
+// strides of its row before accumulating (Lambda is read once, so it bypasses
+// the caches' retention), the centre / radius come from L2, and the row's sums
+// are a fixed-order shuffle tree (no LDS, no barrier).
+typedef float cr_v4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void concretize_rows_wave_kernel(const float* __restrict__ A, int n, long long rows,
+                                                                   int rows_per_b, const float* __restrict__ center,
+                                                                   const float* __restrict__ radius, float eps,
+                                                                   const float* __restrict__ lo,
+                                                                   const float* __restrict__ hi,
+                                                                   const float* __restrict__ bias, float* lb,
+                                                                   float* ub, float* rowacc) {
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // whole wavefront
+  const int lane = threadIdx.x & 63;
+  const long long b = row / rows_per_b;
+  const int n4 = n >> 2;
+  const cr_v4* a4 = reinterpret_cast<const cr_v4*>(A + row * n);
+  const long long bo = b * n4;
+  float sc = 0.f, sr = 0.f;
+  for (int j0 = lane; j0 < n4; j0 += 4 * 64) {
+    cr_v4 a[4];
+    float4 c[4], r[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + 64 * u;
+      const int jj = j < n4 ? j : j0;
+      a[u] = __builtin_nontemporal_load(a4 + jj);
+      if (center) {
+        c[u] = reinterpret_cast<const float4*>(center)[bo + jj];
+        r[u] = radius ? reinterpret_cast<const float4*>(radius)[bo + jj] : make_float4(eps, eps, eps, eps);
+      } else {
+        const float4 l = reinterpret_cast<const float4*>(lo)[bo + jj];
+        const float4 h = reinterpret_cast<const float4*>(hi)[bo + jj];
+        c[u] = make_float4((l.x + h.x) * 0.5f, (l.y + h.y) * 0.5f, (l.z + h.z) * 0.5f, (l.w + h.w) * 0.5f);
+        r[u] = make_float4((h.x - l.x) * 0.5f, (h.y - l.y) * 0.5f, (h.z - l.z) * 0.5f, (h.w - l.w) * 0.5f);
+      }
+      if (j >= n4) a[u] = cr_v4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sc += a[u].x * c[u].x + a[u].y * c[u].y + a[u].z * c[u].z + a[u].w * c[u].w;
+      sr += fabsf(a[u].x) * r[u].x + fabsf(a[u].y) * r[u].y + fabsf(a[u].z) * r[u].z + fabsf(a[u].w) * r[u].w;
+    }
+  }
+  sc = wave_sum(sc);
+  sr = wave_sum(sr);
+  if (lane == 0) {
+    const float bb = bias ? bias[row] : 0.f;
+    if (lb) lb[row] = sc - sr + bb;
+    if (ub) ub[row] = sc + sr + bb;
+    if (rowacc) rowacc[row] += sc - sr;
+  }
+}
+
 hipError_t launch_concretize_rows(const float* A, int rows, int n, int rows_per_b, const float* center,
                                   const float* radius, float eps, const float* lo, const float* hi,
                                   const float* bias, float* lb, float* ub, float* rowacc, hipStream_t st) {
@@ -1134,10 +1162,10 @@ hipError_t launch_concretize_rows(const float* A, int rows, int n, int rows_per_
   auto al = [](const float* p) { return ((uintptr_t)p & 15) == 0; };
   const bool vec = n % 4 == 0 && al(A) && al(center) && al(radius) && al(lo) && al(hi);
   if (vec)
-    hipLaunchKernelGGL(concretize_rows_kernel<true>, dim3(rows), dim3(256), 0, st, A, n, rows_per_b, center, radius,
-                       eps, lo, hi, bias, lb, ub, rowacc);
+    hipLaunchKernelGGL(concretize_rows_wave_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, A, n,
+                       (long long)rows, rows_per_b, center, radius, eps, lo, hi, bias, lb, ub, rowacc);
   else
-    hipLaunchKernelGGL(concretize_rows_kernel<false>, dim3(rows), dim3(256), 0, st, A, n, rows_per_b, center, radius,
+    hipLaunchKernelGGL(concretize_rows_kernel, dim3(rows), dim3(256), 0, st, A, n, rows_per_b, center, radius,
                        eps, lo, hi, bias, lb, ub, rowacc);
   return hipGetLastError();
 }
