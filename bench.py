@@ -373,7 +373,8 @@ def probes(reps=10):
     """Measured ceilings of the GPU at hand (libvbprobe.so, built with the library):
     an MFMA-only loop (v_mfma_f32_32x32x2f32, four independent accumulator chains per
     wavefront, 2048 workgroups of 4 wavefronts, no memory traffic) and HBM read, write
-    and copy streams over 4 GiB buffers (16-byte non-temporal accesses)."""
+    and copy streams over 4 GiB buffers (16-byte non-temporal accesses, one contiguous
+    16 KB segment per workgroup)."""
     import ctypes
     import torch
     lib = ctypes.CDLL(PROBE_LIB)
@@ -398,6 +399,7 @@ def probes(reps=10):
     a = torch.empty(n, device=dev)
     b = torch.empty(n, device=dev)
     a.fill_(1.0)
+    sink = torch.empty(max(int(lib.vbp_stream_blocks(n)), 1 << 16), device=dev)   # one float per read workgroup
     rd = _time_calls(lambda: ok(lib.vbp_read(ctypes.c_void_p(a.data_ptr()), n, ctypes.c_void_p(sink.data_ptr()),
                                             st())), reps)
     wr = _time_calls(lambda: ok(lib.vbp_write(ctypes.c_void_p(b.data_ptr()), n, 0.5, st())), reps)

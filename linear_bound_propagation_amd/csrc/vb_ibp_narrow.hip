@@ -39,10 +39,15 @@ __device__ __forceinline__ float4 ldg4(const float* __restrict__ p, long long of
 template <int AMODE>
 __global__ __launch_bounds__(256) void ibp_narrow_kernel(NarrowIbp d) {
   const int lane = threadIdx.x & 63;
-  const int n0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * ROWS;
-  if (n0 >= d.N) return;  // whole wavefront; the kernel has no barriers
+  // wavefronts are numbered over (slice, block of ROWS neurons), so a layer with
+  // few neurons and many slices still fills every workgroup
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nrb = (d.N + ROWS - 1) / ROWS;
+  const int slice = wid / nrb;
+  if (slice >= d.slices) return;  // whole wavefront; the kernel has no barriers
+  const int n0 = (wid - slice * nrb) * ROWS;
   const int r16 = lane & 15, g = lane >> 4;
-  const int kbeg = blockIdx.y * d.kchunk;
+  const int kbeg = slice * d.kchunk;
   const int kend = min(d.K, kbeg + d.kchunk);
   // A operand: lane (r16, g) holds weight row n0 + 16*blk + r16 and K index
   // 4*g + s of every 16-wide step s; B operand: input r16 at the same K index.
@@ -64,7 +69,7 @@ __global__ __launch_bounds__(256) void ibp_narrow_kernel(NarrowIbp d) {
   // around): rows lie K floats apart, so waves that moved through K in step
   // would all hit the same few HBM channels at once.
   const int nch = (kend - kbeg + 16 * U - 1) / (16 * U);
-  int ch = (int)((blockIdx.x * 4u + (threadIdx.x >> 6)) % (unsigned)nch);
+  int ch = (int)((unsigned)wid % (unsigned)nch);
   for (int it = 0; it < nch; ++it) {
     const int k0 = kbeg + ch * 16 * U;
     ch = (ch + 1 == nch) ? 0 : ch + 1;
@@ -116,8 +121,8 @@ __global__ __launch_bounds__(256) void ibp_narrow_kernel(NarrowIbp d) {
       if (n >= d.N) continue;
       const long long o = (long long)r16 * d.N + n;
       if (d.pc) {
-        d.pc[blockIdx.y * MN + o] = ac[b][v];
-        d.pr[blockIdx.y * MN + o] = ar[b][v];
+        d.pc[slice * MN + o] = ac[b][v];
+        d.pr[slice * MN + o] = ar[b][v];
       } else {
         const float cc = ac[b][v] + (d.bias ? d.bias[n] : 0.f);
         const float l = cc - ar[b][v], u = cc + ar[b][v];
@@ -173,8 +178,8 @@ bool ibp_narrow_fits(int batch, int K, const float* W, const float* A, const flo
 int ibp_narrow_slices(int N, int K) {
   const long long waves = (N + ROWS - 1) / ROWS;
   int S = 1;
-  // four wavefronts for every SIMD, slices of >= 256 K
-  while (waves * S < 4096 && K / (2 * S) >= 256) S *= 2;
+  // four wavefronts for every SIMD, slices of >= 128 K (two load batches)
+  while (waves * S < 4096 && K / (2 * S) >= 128) S *= 2;
   return S;
 }
 
@@ -184,8 +189,9 @@ hipError_t launch_ibp_narrow(NarrowIbp d, int S, hipStream_t st) {
   const int slices = (d.K + d.kchunk - 1) / d.kchunk;
   if (slices > 1 && !d.pc) return hipErrorInvalidValue;
   if (slices == 1) d.pc = d.pr = nullptr;
-  const unsigned waves = (unsigned)((d.N + ROWS - 1) / ROWS);
-  const dim3 grid((waves + 3) / 4, (unsigned)slices);
+  d.slices = slices;
+  const long long waves = (long long)((d.N + ROWS - 1) / ROWS) * slices;
+  const dim3 grid((unsigned)((waves + 3) / 4));
   if (d.amode == A_IBP_BOX)
     hipLaunchKernelGGL(ibp_narrow_kernel<A_IBP_BOX>, grid, dim3(256), 0, st, d);
   else

@@ -446,6 +446,7 @@ struct NarrowIbp {
   float* pc;                // split-K partial sums [slices][batch][N] (centre, radius)
   float* pr;
   int kchunk;               // set by the launcher
+  int slices;               // set by the launcher
 };
 bool ibp_narrow_fits(int batch, int K, const float* W, const float* A, const float* A2);
 int ibp_narrow_slices(int N, int K);

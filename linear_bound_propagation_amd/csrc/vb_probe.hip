@@ -4,10 +4,11 @@
 //   vbp_mfma_loop  - fp32 MFMA blocks (v_mfma_f32_32x32x2f32) with four
 //                    independent accumulator chains per wavefront, no memory
 //                    traffic inside the loop; 4096 FLOP per block per wavefront.
-//   vbp_read       - streams a buffer once (16-byte loads, several in flight
-//                    per lane), one partial sum per workgroup written out.
-//   vbp_write      - fills a buffer (16-byte stores).
-//   vbp_copy       - reads one buffer and writes another.
+//   vbp_read       - streams a buffer once (non-temporal 16-byte loads, four in
+//                    flight per lane, one contiguous 16 KB segment per
+//                    workgroup), one partial sum per workgroup written out.
+//   vbp_write      - fills a buffer (16-byte non-temporal stores, same layout).
+//   vbp_copy       - reads one buffer and writes another (same layout).
 // Every entry point enqueues on the given stream and returns the launch status.
 #include <hip/hip_runtime.h>
 
@@ -37,58 +38,59 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* out) {
 }
 
 constexpr int UNROLL = 4;
+constexpr int SEG = 256 * UNROLL;  // float4 per workgroup: 16 KB, 4 KB per wavefront
+
+// Each workgroup streams one contiguous 16 KB segment: wavefront w of it reads
+// the 4 KB at w, with its UNROLL 16-byte loads (64 lanes x 16 B = 1 KB each)
+// issued before any is used.  Short-lived workgroups over contiguous segments
+// keep many DRAM pages streaming at once.
+__device__ __forceinline__ long long seg_index(int u) {
+  return (long long)blockIdx.x * SEG + (threadIdx.x >> 6) * (64 * UNROLL) + u * 64 + (threadIdx.x & 63);
+}
 
 __global__ __launch_bounds__(256) void read_kernel(const f32x4* __restrict__ p, long long n4, float* out) {
-  const long long stride = (long long)gridDim.x * blockDim.x;
-  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  f32x4 v[UNROLL];
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const long long i = seg_index(u);
+    v[u] = i < n4 ? __builtin_nontemporal_load(p + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   float s = 0.f;
-  for (; i + (UNROLL - 1) * stride < n4; i += UNROLL * stride) {
-    f32x4 v[UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
+  for (int u = 0; u < UNROLL; ++u) s += v[u].x + v[u].y + v[u].z + v[u].w;
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) s += v[u].x + v[u].y + v[u].z + v[u].w;
-  }
-  for (; i < n4; i += stride) {
-    const f32x4 v = p[i];
-    s += v.x + v.y + v.z + v.w;
-  }
-  __shared__ float red[256];
-  red[threadIdx.x] = s;
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
   __syncthreads();
-  for (int h = 128; h > 0; h >>= 1) {
-    if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) out[blockIdx.x] = red[0];
+  if (threadIdx.x == 0) out[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
 __global__ __launch_bounds__(256) void write_kernel(f32x4* __restrict__ p, long long n4, float v) {
-  const long long stride = (long long)gridDim.x * blockDim.x;
   const f32x4 x = {v, v, v, v};
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
-    __builtin_nontemporal_store(x, p + i);
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const long long i = seg_index(u);
+    if (i < n4) __builtin_nontemporal_store(x, p + i);
+  }
 }
 
 __global__ __launch_bounds__(256) void copy_kernel(const f32x4* __restrict__ src, f32x4* __restrict__ dst,
                                                    long long n4) {
-  const long long stride = (long long)gridDim.x * blockDim.x;
-  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + (UNROLL - 1) * stride < n4; i += UNROLL * stride) {
-    f32x4 v[UNROLL];
+  f32x4 v[UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) __builtin_nontemporal_store(v[u], dst + i + u * stride);
+  for (int u = 0; u < UNROLL; ++u) {
+    const long long i = seg_index(u);
+    v[u] = i < n4 ? __builtin_nontemporal_load(src + i) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  for (; i < n4; i += stride) dst[i] = src[i];
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const long long i = seg_index(u);
+    if (i < n4) __builtin_nontemporal_store(v[u], dst + i);
+  }
 }
 
-int stream_blocks(long long n4) {
-  // 256 CUs x 8 workgroups of 256 lanes, fewer for small buffers
-  long long b = (n4 + 255) / 256;
-  return (int)(b < 2048 ? (b > 0 ? b : 1) : 2048);
-}
+long long stream_blocks(long long n4) { return (n4 + SEG - 1) / SEG; }
 
 }  // namespace
 
@@ -106,21 +108,25 @@ int vbp_mfma_loop(int blocks, int iters, float* out, void* stream) {
 // workgroup (vbp_stream_blocks(n) of them).
 int vbp_read(const float* p, long long n, float* out, void* stream) {
   if (!p || !out || n <= 0 || n % 4 || ((uintptr_t)p & 15)) return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL(read_kernel, dim3(stream_blocks(n / 4)), dim3(256), 0, (hipStream_t)stream,
+  if (stream_blocks(n / 4) > INT32_MAX) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(read_kernel, dim3((unsigned)stream_blocks(n / 4)), dim3(256), 0, (hipStream_t)stream,
                      (const f32x4*)p, n / 4, out);
   return (int)hipGetLastError();
 }
 
 int vbp_write(float* p, long long n, float v, void* stream) {
   if (!p || n <= 0 || n % 4 || ((uintptr_t)p & 15)) return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL(write_kernel, dim3(stream_blocks(n / 4)), dim3(256), 0, (hipStream_t)stream, (f32x4*)p, n / 4, v);
+  if (stream_blocks(n / 4) > INT32_MAX) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(write_kernel, dim3((unsigned)stream_blocks(n / 4)), dim3(256), 0, (hipStream_t)stream, (f32x4*)p,
+                     n / 4, v);
   return (int)hipGetLastError();
 }
 
 int vbp_copy(const float* src, float* dst, long long n, void* stream) {
   if (!src || !dst || n <= 0 || n % 4 || ((uintptr_t)src & 15) || ((uintptr_t)dst & 15))
     return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL(copy_kernel, dim3(stream_blocks(n / 4)), dim3(256), 0, (hipStream_t)stream,
+  if (stream_blocks(n / 4) > INT32_MAX) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)stream_blocks(n / 4)), dim3(256), 0, (hipStream_t)stream,
                      (const f32x4*)src, (f32x4*)dst, n / 4);
   return (int)hipGetLastError();
 }
