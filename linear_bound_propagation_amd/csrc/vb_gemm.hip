@@ -544,26 +544,41 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   // The 32 rows of a block i of a gather tile lie in one block of 2^rb_shift
   // >= 32 rows of the same output position: the position (and its division
   // work) is decoded once per block, and each element only adds its row
-  // offset.  (Footprint rows need a per-row window decode.)
+  // offset.  Footprint rows (b, sign, start pixel, channel) share their start
+  // pixel across a 32-row block when the start node's channel count is a
+  // multiple of 32, so their window-cell-to-pixel decode is also once per
+  // block; otherwise it is per row.
   constexpr bool one_pos = !DENSE && !PATCH;
+  const bool blk = one_pos || (PATCH && d.pc % 32 == 0);
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     int row0 = 0, r0 = 0, b0 = 0;
     long long obase = 0, bbase = 0;  // element offsets of (r0, position) in the output and in coef
-    bool blk_ok = false;
+    bool blk_ok = false, pin_blk = true;
     const int HWN = d.ho * d.wo * d.N;  // elements per row (the host keeps 32 * HWN < 2^31)
-    if (one_pos) {
+    if (blk) {
       const GPos gp = gdecode(d, m0 + wm * WTM + i * 32);
       blk_ok = m0 + wm * WTM + i * 32 < d.Mt;
       row0 = gp.row;
       const int Y = fdiv(gp.q, d.div_gw);
       const int X = gp.q - Y * d.gw;
-      const long long sp0 = (long long)(Y * d.oym + d.oy0) * d.wo + (X * d.oxm + d.ox0);
+      const int cy = Y * d.oym + d.oy0, cx = X * d.oxm + d.ox0;
+      const long long sp0 = (long long)cy * d.wo + cx;
       // padding rows address row r0 (a valid row) and are never stored
       r0 = min(row0, d.div_nrows.d - 1);
       b0 = fdiv(r0, d.div_rows);
       obase = ((long long)r0 * d.ho * d.wo + sp0) * d.N;
-      bbase = ((long long)b0 * d.ho * d.wo + sp0) * d.N;
+      if (PATCH) {
+        // window cell -> pixel of the target node for the block's start pixel
+        const int t1 = fdiv(r0, d.div_pc);
+        const int pz = t1 - fdiv(t1, d.div_pz) * d.div_pz.d;
+        const int py = fdiv(pz, d.div_pw), px = pz - py * d.pgw;
+        const int ay = py * d.psy + d.poy + cy, ax = px * d.psx + d.pox + cx;
+        pin_blk = ay >= 0 && ay < d.img_h && ax >= 0 && ax < d.img_w;
+        bbase = ((long long)b0 * d.img_h * d.img_w + (pin_blk ? (long long)ay * d.img_w + ax : 0)) * d.N;
+      } else {
+        bbase = ((long long)b0 * d.ho * d.wo + sp0) * d.N;
+      }
     }
 #pragma unroll
     for (int v0 = 0; v0 < 16; v0 += G) {
@@ -575,14 +590,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
         const int v = v0 + g;
         const int m = m0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
         pin[g] = true;
-        if (one_pos) {
+        if (blk) {
           // offsets from (r0, position): 32-bit arithmetic per element
           const int row = row0 + 8 * (v >> 2) + 4 * half + (v & 3);
           mok[g] = blk_ok && row < d.div_nrows.d;
           const int rr = mok[g] ? row : r0;
           rbase[g] = rr * d.acols;
           opos[g] = (rr - r0) * HWN;
-          bpos[g] = (fdiv(rr, d.div_rows) - b0) * HWN;
+          // (footprint rows of a block share their input and start pixel)
+          bpos[g] = PATCH ? 0 : (fdiv(rr, d.div_rows) - b0) * HWN;
+          pin[g] = pin_blk;
         } else if (DENSE) {
           mok[g] = m < d.M;
           const int mm = mok[g] ? m : 0;
@@ -625,7 +642,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
         long long oi[G], bi[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          if (one_pos) {
+          if (blk) {
             oi[g] = obase + (unsigned)((int)opos[g] + nn);
             bi[g] = bbase + (unsigned)((int)bpos[g] + nn);
           } else {
