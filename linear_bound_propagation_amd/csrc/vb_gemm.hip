@@ -414,15 +414,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   // outside it the epilogue keeps nothing).
   if (FAST && !DENSE && ks_n == 1) {
     __shared__ unsigned tap_mask;
-    unsigned my = 0;
-#pragma unroll
-    for (int i = 0; i < AV; ++i) {
-      const Pos& p = apos[i];
-      if (!p.valid) continue;
+    // taps row m (at position p) reads inside the source
+    auto taps_of = [&](const Pos& p, int m) -> unsigned {
+      unsigned bits = 0;
+      if (!p.valid) return bits;
       int sy0 = 0, sx0 = 0, sy1 = 0, sx1 = 0;
       bool inimg = true;
       if (PATCH) {
-        const GPos g = gdecode(d, m0 + (tid + NTHR * i) / (BK / 4));
+        const GPos g = gdecode(d, m);
         const int t1 = fdiv(g.row, d.div_pc);
         const int pz = t1 - fdiv(t1, d.div_pz) * d.div_pz.d;
         const int py = fdiv(pz, d.div_pw), px = pz - py * d.pgw;
@@ -436,7 +435,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
           sx1 = px * d.ssx1 + d.sox1;
         }
       }
-      if (!inimg) continue;
+      if (!inimg) return bits;
       for (int j = 0; j < d.ntaps; ++j) {
         const Tap tp = tap_of(d, j);
         const int yy = p.Y * d.sy + tp.dy, xx = p.X * d.sx + tp.dx;
@@ -448,8 +447,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
         } else if (PATCH && d.src_h > 0) {
           ok = ok && sy0 + yy >= 0 && sy0 + yy < d.src_h && sx0 + xx >= 0 && sx0 + xx < d.src_w;
         }
-        if (ok) my |= 1u << j;
+        if (ok) bits |= 1u << j;
       }
+      return bits;
+    };
+    unsigned my = 0;
+    if (!PATCH || d.pc % 32 == 0) {
+      // every row of a 32-row block has the block's output position (and, for
+      // footprint rows, its start pixel): one thread per block works it out
+      if (tid < BM / 32) my = taps_of(pos_of<DENSE>(d, m0 + 32 * tid), m0 + 32 * tid);
+    } else {
+#pragma unroll
+      for (int i = 0; i < AV; ++i) my |= taps_of(apos[i], m0 + (tid + NTHR * i) / (BK / 4));
     }
     if (tid == 0) tap_mask = 0u;
     __syncthreads();
