@@ -559,9 +559,9 @@ size_t conv_input_part_floats(const ConvIn& a, int rows) {
 // Consecutive workgroups go round-robin over the 8 XCDs; with xcd_map the
 // bands of one row share an XCD, so the rows two bands both stage are read
 // through one L2.
-template <int CI, int NB, bool S1, bool MULTI>
+template <int CI, int NB, bool S1>
 __global__ __launch_bounds__(CIN_THREADS) void conv_input_concretize_kernel(const ConvIn a, int BH, int nbands,
-                                                                           int xcd_map, int per_wg, long long items,
+                                                                           int xcd_map, long long items,
                                                                            float* __restrict__ part) {
   extern __shared__ float ys[];  // [staged pixels][ysw]
   __shared__ float sh[CIN_THREADS / 64];
@@ -589,28 +589,11 @@ __global__ __launch_bounds__(CIN_THREADS) void conv_input_concretize_kernel(cons
     }
   }
 
-  // MULTI: per_wg items of one band each (footprint windows), at most two
-  // M-blocks per wavefront: the next item's Lambda is loaded while the
-  // current one computes
-  float4 nxa[2][4];
-  auto load_item = [&](long long item, float4 (&v)[2][4]) {
-    const float* lam_i = a.lam + item * a.Ho * (long long)a.Wo * a.Co;
-    const int np = a.Ho * a.Wo;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = min((wave + WAVES * i) * 16 + li, np - 1);
-      const float4* ap = reinterpret_cast<const float4*>(lam_i + (long long)q * a.Co + 4 * kk);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[i][u] = ap[16 * u < a.Co ? 4 * u : 0];
-    }
-  };
-  if (MULTI && (long long)blockIdx.x * per_wg < items) load_item((long long)blockIdx.x * per_wg, nxa);
-
-  // work items (row, band) n = blockIdx.x * per_wg + i; with xcd_map (one
-  // item per workgroup) the bands of one row share an XCD
-  for (int it = 0; it < (MULTI ? per_wg : 1); ++it) {
-  const long long n = MULTI ? (long long)blockIdx.x * per_wg + it : (long long)blockIdx.x;
-  if (n >= items) break;
+  // work item (row, band) n = blockIdx.x; with xcd_map the bands of one row
+  // share an XCD
+  {
+  const long long n = (long long)blockIdx.x;
+  if (n >= items) return;
   long long row;
   int band;
   if (xcd_map) {
@@ -645,39 +628,8 @@ __global__ __launch_bounds__(CIN_THREADS) void conv_input_concretize_kernel(cons
     for (int u = 0; u < 4; ++u) v[u] = ap[16 * u < a.Co ? 4 * u : 0];
   };
   cin_v4 acc[NB];
-  if (MULTI) {
-    float4 av[2][4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) av[i][u] = nxa[i][u];
-    if (it + 1 < per_wg && n + 1 < items) load_item(n + 1, nxa);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      if (i >= nit) break;
-      const int mb = wave + WAVES * i;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[nb] = cin_v4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float4 c4 = av[i][j >> 2];
-        const float a1 = (j & 3) == 0 ? c4.x : (j & 3) == 1 ? c4.y : (j & 3) == 2 ? c4.z : c4.w;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bw[nb][j], acc[nb], 0, 0, 0);
-      }
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int q = mb * 16 + 4 * kk + v;
-        if (q < npx) {
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            if (nb * 16 + li < ncol) ys[q * ysw + nb * 16 + li] = acc[nb][v];
-        }
-      }
-    }
-  }
   // the loads of up to CIN_MB M-blocks are issued together
-  for (int g0 = 0; g0 < (MULTI ? 0 : nit); g0 += CIN_MB) {
+  for (int g0 = 0; g0 < nit; g0 += CIN_MB) {
     float4 av[CIN_MB][4];
 #pragma unroll
     for (int i = 0; i < CIN_MB; ++i) load_a(min(g0 + i, nit - 1), av[i]);
@@ -763,27 +715,167 @@ __global__ __launch_bounds__(CIN_THREADS) void conv_input_concretize_kernel(cons
     for (int w = 0; w < WAVES; ++w) t += sh[w];
     part[row * nbands + band] = t;
   }
-  __syncthreads();  // the tap table and sh are rewritten by the next item
+  }
+}
+
+// Footprint windows (a window of at most 128 output cells per row, the whole
+// window one band): the same two phases for P rows at once, so that small
+// windows still occupy the workgroup.  Phase 1 spreads the P * ceil(cells/16)
+// M-blocks (at most 8) over the four wavefronts, each tap table in its own LDS
+// slice; in phase 2 thread t takes input pixel t % pix of row t / pix; each
+// row's sum is added by one thread over its pixels in order.  The next group's
+// Lambda is loaded while the current one computes; the weights stay in
+// registers for all per_wg rows of the workgroup.
+template <int CI, int NB, bool S1>
+__global__ __launch_bounds__(CIN_THREADS) void conv_input_windows_kernel(const ConvIn a, int per_wg, int P,
+                                                                        long long rows, float* __restrict__ part) {
+  extern __shared__ float ys[];  // [P][cells][ysw]
+  __shared__ float contrib[CIN_THREADS];
+  constexpr int WAVES = CIN_THREADS / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ntap = a.kh * a.kw;
+  const int ncol = ntap * CI;
+  const int ysw = cin_row_floats(ncol);
+  const int li = lane & 15, kk = lane >> 4;
+  const int cells = a.Ho * a.Wo, mbi = (cells + 15) / 16, pix = a.Hi * a.Wi;
+  const int s = S1 ? 1 : a.stride;
+  const int oy_hi = min(a.Ho - 1, (a.Hi - 1 + a.pad) / s);
+
+  float bw[NB][16];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int col = nb * 16 + li;
+    const bool okn = col < ncol;
+    const int t = okn ? col / CI : 0, ci = okn ? col - t * CI : 0;
+    const float* w = a.W + ((long long)t * a.Co + 4 * kk) * CI + ci;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int off = 16 * (j >> 2) + (j & 3);
+      bw[nb][j] = okn && 16 * (j >> 2) < a.Co ? w[off * CI] : 0.f;
+    }
+  }
+
+  const long long r_beg = (long long)blockIdx.x * per_wg;
+  const long long r_end = min(rows, r_beg + per_wg);
+  // M-block slot i of this wavefront in a group starting at row r0: item, block
+  auto load_group = [&](long long r0, float4 (&v)[2][4]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int gb = wave + WAVES * i;
+      const int item = gb / mbi, mb = gb - item * mbi;
+      long long row = r0 + item;
+      if (row >= r_end) row = r_end - 1;  // clamped (never stored)
+      const int q = min(mb * 16 + li, cells - 1);
+      const float4* ap = reinterpret_cast<const float4*>(a.lam + (row * cells + q) * (long long)a.Co + 4 * kk);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[i][u] = ap[16 * u < a.Co ? 4 * u : 0];
+    }
+  };
+  float4 nxa[2][4];
+  if (r_beg < r_end) load_group(r_beg, nxa);
+  for (long long r0 = r_beg; r0 < r_end; r0 += P) {
+    float4 av[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) av[i][u] = nxa[i][u];
+    if (r0 + P < r_end) load_group(r0 + P, nxa);
+    // phase 1: tap tables of the group's rows
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int gb = wave + WAVES * i;
+      const int item = gb / mbi, mb = gb - item * mbi;
+      if (item >= P || r0 + item >= r_end) continue;
+      cin_v4 acc[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = cin_v4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float4 c4 = av[i][j >> 2];
+        const float a1 = (j & 3) == 0 ? c4.x : (j & 3) == 1 ? c4.y : (j & 3) == 2 ? c4.z : c4.w;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bw[nb][j], acc[nb], 0, 0, 0);
+      }
+      float* yt = ys + (long long)item * cells * ysw;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int q = mb * 16 + 4 * kk + v;
+        if (q < cells) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            if (nb * 16 + li < ncol) yt[q * ysw + nb * 16 + li] = acc[nb][v];
+        }
+      }
+    }
+    __syncthreads();
+    // phase 2: thread t -> input pixel t % pix of row t / pix
+    float sum = 0.f;
+    const int item = tid / pix;
+    const long long row = r0 + item;
+    if (item < P && row < r_end) {
+      const int pp = tid - item * pix;
+      const int py = pp / a.Wi, px = pp - py * a.Wi;
+      const float* yt = ys + (long long)item * cells * ysw;
+      float o[CI];
+#pragma unroll
+      for (int ci = 0; ci < CI; ++ci) o[ci] = 0.f;
+      for (int t = 0; t < ntap; ++t) {
+        const int ky = t / a.kw, kx = t - ky * a.kw;
+        const int ty = py + a.pad - ky, tx = px + a.pad - kx;
+        int q = -1;
+        if (ty >= 0 && tx >= 0) {
+          if (S1) {
+            if (ty <= oy_hi && tx < a.Wo) q = ty * a.Wo + tx;
+          } else if (ty % s == 0 && tx % s == 0 && ty / s <= oy_hi && tx / s < a.Wo) {
+            q = (ty / s) * a.Wo + tx / s;
+          }
+        }
+        if (q >= 0) {
+#pragma unroll
+          for (int ci = 0; ci < CI; ++ci) o[ci] += yt[q * ysw + t * CI + ci];
+        }
+      }
+      const long long b = row / a.rows_per_b;
+      const long long pz = (row / a.pc) % ((long long)a.pgh * a.pgw);
+      const int gy = (int)(pz / a.pgw), gx = (int)(pz - (pz / a.pgw) * a.pgw);
+      const int ay = gy * a.psy + a.poy + py, ax = gx * a.psx + a.pox + px;
+      if (ay >= 0 && ay < a.img_h && ax >= 0 && ax < a.img_w) {
+        const long long dpix = b * a.img_h * a.img_w + (long long)ay * a.img_w + ax;
+#pragma unroll
+        for (int ci = 0; ci < CI; ++ci) {
+          const long long be = dpix * CI + ci;
+          const float r = a.radius ? a.radius[be] : a.eps;
+          sum += o[ci] * a.center[be] - fabsf(o[ci]) * r;
+        }
+      }
+    }
+    contrib[tid] = sum;
+    __syncthreads();
+    if (tid < P && r0 + tid < r_end) {
+      float tot = 0.f;
+      for (int e = tid * pix; e < (tid + 1) * pix; ++e) tot += contrib[e];
+      part[r0 + tid] = tot;
+    }
+    __syncthreads();  // the tap tables and contrib are rewritten by the next group
   }
 }
 
 template <int CI, int NB>
 void cin_launch(bool s1, unsigned grid, size_t lds, hipStream_t st, const ConvIn& a, int bh, int nbands, int xcd_map,
-                int per_wg, long long items, float* part) {
+                int per_wg, long long items, float* part, int P) {
   const dim3 g(grid), b(CIN_THREADS);
   if (per_wg > 1) {
+    // footprint windows, P rows at a time (one band each)
     if (s1)
-      hipLaunchKernelGGL((conv_input_concretize_kernel<CI, NB, true, true>), g, b, lds, st, a, bh, nbands, xcd_map,
-                         per_wg, items, part);
+      hipLaunchKernelGGL((conv_input_windows_kernel<CI, NB, true>), g, b, lds, st, a, per_wg, P, items, part);
     else
-      hipLaunchKernelGGL((conv_input_concretize_kernel<CI, NB, false, true>), g, b, lds, st, a, bh, nbands, xcd_map,
-                         per_wg, items, part);
+      hipLaunchKernelGGL((conv_input_windows_kernel<CI, NB, false>), g, b, lds, st, a, per_wg, P, items, part);
   } else if (s1) {
-    hipLaunchKernelGGL((conv_input_concretize_kernel<CI, NB, true, false>), g, b, lds, st, a, bh, nbands, xcd_map,
-                       per_wg, items, part);
+    hipLaunchKernelGGL((conv_input_concretize_kernel<CI, NB, true>), g, b, lds, st, a, bh, nbands, xcd_map, items,
+                       part);
   } else {
-    hipLaunchKernelGGL((conv_input_concretize_kernel<CI, NB, false, false>), g, b, lds, st, a, bh, nbands, xcd_map,
-                       per_wg, items, part);
+    hipLaunchKernelGGL((conv_input_concretize_kernel<CI, NB, false>), g, b, lds, st, a, bh, nbands, xcd_map, items,
+                       part);
   }
 }
 
@@ -802,17 +894,26 @@ hipError_t launch_conv_input_concretize(const ConvIn& a, int rows, float* part, 
   // staged rows are the whole output window)
   const int per_wg = a.patch && nb == 1 && bh == a.Hi && a.Ho * a.Wo <= 128 ? CIN_WIN_ROWS : 1;
   const unsigned grid = (unsigned)((items + per_wg - 1) / per_wg);
+  // footprint windows: rows bounded together so that their M-blocks (at most 8)
+  // and their input pixels (at most one per thread) fill the workgroup
+  int P = 1;
+  size_t lds_use = lds;
+  if (per_wg > 1) {
+    const int mbi = (a.Ho * a.Wo + 15) / 16;
+    P = std::max(1, std::min({8 / mbi, CIN_THREADS / (a.Hi * a.Wi), per_wg}));
+    lds_use = (size_t)P * a.Ho * a.Wo * cin_row_floats(a.kh * a.kw * a.Ci) * sizeof(float);
+  }
   const int xm = per_wg == 1 && rows % 8 == 0;
   const bool s1 = a.stride == 1;
   switch (a.Ci * 4 + cin_col_blocks(a)) {
-    case 1 * 4 + 1: cin_launch<1, 1>(s1, grid, lds, st, a, bh, nb, xm, per_wg, items, part); break;
-    case 2 * 4 + 1: cin_launch<2, 1>(s1, grid, lds, st, a, bh, nb, xm, per_wg, items, part); break;
-    case 2 * 4 + 2: cin_launch<2, 2>(s1, grid, lds, st, a, bh, nb, xm, per_wg, items, part); break;
-    case 3 * 4 + 1: cin_launch<3, 1>(s1, grid, lds, st, a, bh, nb, xm, per_wg, items, part); break;
-    case 3 * 4 + 2: cin_launch<3, 2>(s1, grid, lds, st, a, bh, nb, xm, per_wg, items, part); break;
-    case 4 * 4 + 1: cin_launch<4, 1>(s1, grid, lds, st, a, bh, nb, xm, per_wg, items, part); break;
-    case 4 * 4 + 2: cin_launch<4, 2>(s1, grid, lds, st, a, bh, nb, xm, per_wg, items, part); break;
-    case 4 * 4 + 3: cin_launch<4, 3>(s1, grid, lds, st, a, bh, nb, xm, per_wg, items, part); break;
+    case 1 * 4 + 1: cin_launch<1, 1>(s1, grid, lds_use, st, a, bh, nb, xm, per_wg, items, part, P); break;
+    case 2 * 4 + 1: cin_launch<2, 1>(s1, grid, lds_use, st, a, bh, nb, xm, per_wg, items, part, P); break;
+    case 2 * 4 + 2: cin_launch<2, 2>(s1, grid, lds_use, st, a, bh, nb, xm, per_wg, items, part, P); break;
+    case 3 * 4 + 1: cin_launch<3, 1>(s1, grid, lds_use, st, a, bh, nb, xm, per_wg, items, part, P); break;
+    case 3 * 4 + 2: cin_launch<3, 2>(s1, grid, lds_use, st, a, bh, nb, xm, per_wg, items, part, P); break;
+    case 4 * 4 + 1: cin_launch<4, 1>(s1, grid, lds_use, st, a, bh, nb, xm, per_wg, items, part, P); break;
+    case 4 * 4 + 2: cin_launch<4, 2>(s1, grid, lds_use, st, a, bh, nb, xm, per_wg, items, part, P); break;
+    case 4 * 4 + 3: cin_launch<4, 3>(s1, grid, lds_use, st, a, bh, nb, xm, per_wg, items, part, P); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
