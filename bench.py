@@ -117,12 +117,26 @@ def _clipped_cells(win, shape_z, shape_k):
     return ny, nx
 
 
+def _cell_taps(win_axis, n_z, n_out, n_in, stride, pad, k):
+    """Per pixel of z along one axis: the (output cell, tap) pairs of one conv whose
+    output cell lies inside the row's window and the image and whose tap lands inside
+    the conv's input image (a tap into the zero padding multiplies nothing)."""
+    a, lo, hi = win_axis
+    out = np.zeros(n_z)
+    for pz in range(n_z):
+        for yo in range(max(a * pz + lo, 0), min(a * pz + hi, n_out - 1) + 1):
+            yi = yo * stride - pad + np.arange(k)
+            out[pz] += np.count_nonzero((yi >= 0) & (yi < n_in))
+    return out
+
+
 def footprint_row_macs(nodes, z, stop):
     """Multiply-adds of one identity row over conv-region node z, per pixel of z
     ([h_z][w_z]), when every row is carried on its footprint window: at each conv on
-    the way to `stop` only the output cells inside the row's window and the image count;
-    the first step (a copy of the weight footprint into the rows) costs nothing.  None
-    if the rows do not stay in the convolution region."""
+    the way to `stop` only the products that can be non-zero count, i.e. output cells
+    inside the row's window and the image, through taps that land inside the conv's
+    input image; the first step (a copy of the weight footprint into the rows) costs
+    nothing.  None if the rows do not stay in the convolution region."""
     W = _windows(nodes, z, stop)
     if W is None or len(nodes[z].shape) != 3:
         return None
@@ -134,8 +148,10 @@ def footprint_row_macs(nodes, z, stop):
         if nk.op != "conv" or k in free or k == stop:
             continue
         co, ci, kh, kw = nk.weight.shape
-        ny, nx = _clipped_cells(win, nodes[z].shape, nk.shape)
-        per += np.outer(ny, nx) * (co * ci * kh * kw)
+        _, hi_, wi_ = nodes[_src(nodes, nk.inputs[0])].shape
+        ty = _cell_taps(win[0], hz, nk.shape[1], hi_, nk.stride, nk.pad, kh)
+        tx = _cell_taps(win[1], wz, nk.shape[2], wi_, nk.stride, nk.pad, kw)
+        per += np.outer(ty, tx) * (co * ci)
     return per
 
 

@@ -451,17 +451,28 @@ bool same_win(const Win& a, const Win& b) {
 // Algorithmic multiply-adds of one conv step of window rows: for every row, the
 // cells of its window over the conv's output that lie inside the image, times
 // the conv's multiply-adds per output cell.
-double window_macs(const NodeInfo& S, const NodeInfo& nd, const Win& w, long long rows_per_pixel) {
-  double sy = 0.0, sx = 0.0;
-  for (int py = 0; py < S.h; ++py) {
-    const int a = py * w.sy + w.oy, b = a + w.wh;
-    sy += std::max(0, std::min(b, nd.h) - std::max(a, 0));
-  }
-  for (int px = 0; px < S.w; ++px) {
-    const int a = px * w.sx + w.ox, b = a + w.ww;
-    sx += std::max(0, std::min(b, nd.w) - std::max(a, 0));
-  }
-  return (double)rows_per_pixel * sy * sx * nd.c * nd.kh * nd.kw;  // x C_in by the caller
+// Multiply-adds of one conv step of footprint rows that can be non-zero: per
+// start pixel, the output cells of the conv inside the row's window and the
+// image, each through the taps that land inside the conv's input image (in_h x
+// in_w; a tap into the zero padding multiplies nothing), x C_out (x C_in by the
+// caller).  Separable: the (cell, tap) pairs factor into the two axes.
+double window_macs(const NodeInfo& S, const NodeInfo& nd, const Win& w, long long rows_per_pixel, int in_h,
+                   int in_w) {
+  auto axis = [&](int n_start, int step, int off, int len, int n_out, int n_in, int k) {
+    double t = 0.0;
+    for (int p = 0; p < n_start; ++p) {
+      const int a = std::max(p * step + off, 0), b = std::min(p * step + off + len, n_out);
+      for (int o = a; o < b; ++o)
+        for (int kk = 0; kk < k; ++kk) {
+          const int i = o * nd.stride - nd.pad + kk;
+          t += (i >= 0 && i < n_in) ? 1.0 : 0.0;
+        }
+    }
+    return t;
+  };
+  const double ty = axis(S.h, w.sy, w.oy, w.wh, nd.h, in_h, nd.kh);
+  const double tx = axis(S.w, w.sx, w.ox, w.ww, nd.w, in_w, nd.kw);
+  return (double)rows_per_pixel * ty * tx * nd.c;  // x C_in by the caller
 }
 
 // ---- footprint (patch) back-substitution of identity rows through a chain
@@ -767,11 +778,11 @@ vb_status backward_chunk_patch(Backward& B, const BwdCall& c, long long R, const
           d.bias_c = tn.c;
         }
         // (profiled work: the multiply-adds of the rows' window cells inside the
-        // image, except the first step from the identity rows, which is a copy of
-        // the weight footprint)
+        // image through taps inside the input image, except the first step from
+        // the identity rows, which is a copy of the weight footprint)
         const double macs = ps.k == c.start ? 0.0
                                             : window_macs(S, nd, Win{wh, ww, ksy, koy, ksx, kox, true},
-                                                          (long long)c.cb * 2 * S.c) * tn.c;
+                                                          (long long)c.cb * 2 * S.c, tn.h, tn.w) * tn.c;
         s = run_gemm_reduce(B, d, rows, d.gh * d.gw, true, 2.0 * macs / (nd.stride * nd.stride));
         if (s) return s;
       }
@@ -1106,8 +1117,9 @@ vb_status backward_chunk_window(Backward& B, const BwdCall& c, long long R, cons
     const int pad_y = nd.pad + tw.oy - nd.stride * kw.oy, pad_x = nd.pad + tw.ox - nd.stride * kw.ox;
     if (pad_y != pad_x) return fail(VB_EUNSUPPORTED, "internal: windows of node %d are not square-aligned", k);
     nv.pad = pad_y;
-    // the multiply-adds of this step (cells of the rows' windows inside the image)
-    const double macs = window_macs(S, nd, kw, rows_per_pixel) * tn.c;
+    // the multiply-adds of this step (cells of the rows' windows inside the image,
+    // taps inside the input image)
+    const double macs = window_macs(S, nd, kw, rows_per_pixel, tn.h, tn.w) * tn.c;
     double macs_all = macs;
     std::vector<GemmDesc> descs;
     if (last && merge_dom) {
@@ -1121,7 +1133,7 @@ vb_status backward_chunk_window(Backward& B, const BwdCall& c, long long R, cons
       nv1.pad = nd1.pad + tw.oy - nd1.stride * kw1.oy;
       if (nv1.pad != nd1.pad + tw.ox - nd1.stride * kw1.ox)
         return fail(VB_EUNSUPPORTED, "internal: windows of node %d are not square-aligned", held.k);
-      macs_all += window_macs(S, nd1, kw1, rows_per_pixel) * tn.c;
+      macs_all += window_macs(S, nd1, kw1, rows_per_pixel, tn.h, tn.w) * tn.c;
       for (int py = 0; py < nd.stride; ++py)
         for (int px = 0; px < nd.stride; ++px) {
           GemmDesc d0, d1;

@@ -542,6 +542,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
     __syncthreads();
   }
 
+  // A concretisation tile none of whose taps reaches any of its rows (a window
+  // cell outside the image, say) has only zero products: with nothing added
+  // and nothing stored per element, each of its rows' partials is 0.
+  if (EPI == E_CONCRETIZE && FAST && !DENSE && ks_n == 1 && nk == 0 && !d.addend && !d.psi_out) {
+    if (d.part) {
+      for (int r = tid; r < BM; r += NTHR) {
+        const GPos gp = gdecode(d, m0 + r);
+        if (gp.valid) d.part[((long long)gp.q * d.div_nrows.d + gp.row) * d.part_ld + tn] = 0.f;
+      }
+    }
+    return;
+  }
+
   // ---- epilogue.  Register v of lane l of a 32x32 fp32 MFMA result holds
   // row 8*(v/4) + 4*(l/32) + v%4 and column l%32 of the block.  The elements
   // are handled 8 rows at a time: indices first (clamped in range), then every
