@@ -554,6 +554,39 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
     }
     return;
   }
+  // The same for a footprint relaxation tile: every product is zero, so every
+  // output (and kept Psi) is 0 and so is every row's partial.
+  if (EPI == E_RELAX && PATCH && FAST && ks_n == 1 && nk == 0 && !d.addend && !d.alpha) {
+    const int HW = d.ho * d.wo;
+    const bool v4 = (d.N & 3) == 0;  // (Lambda buffers are 16-byte aligned)
+    constexpr int Q = BN / 4;        // float4 per tile row
+    for (int e = tid; e < BM * Q; e += NTHR) {
+      const int r = e / Q, nn = n0 + 4 * (e - r * Q);
+      const GPos gp = gdecode(d, m0 + r);
+      if (!gp.valid || nn >= d.N) continue;
+      const int Y = fdiv(gp.q, d.div_gw);
+      const int X = gp.q - Y * d.gw;
+      const long long o =
+          ((long long)gp.row * HW + (long long)(Y * d.oym + d.oy0) * d.wo + (X * d.oxm + d.ox0)) * d.N + nn;
+      if (v4) {
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4*>(d.out + o) = z;
+        if (d.psi_out) *reinterpret_cast<float4*>(d.psi_out + o) = z;
+      } else {
+        for (int c = 0; c < 4 && nn + c < d.N; ++c) {
+          d.out[o + c] = 0.f;
+          if (d.psi_out) d.psi_out[o + c] = 0.f;
+        }
+      }
+    }
+    if (d.part) {
+      for (int r = tid; r < BM; r += NTHR) {
+        const GPos gp = gdecode(d, m0 + r);
+        if (gp.valid) d.part[((long long)gp.q * d.div_nrows.d + gp.row) * d.part_ld + tn] = 0.f;
+      }
+    }
+    return;
+  }
 
   // ---- epilogue.  Register v of lane l of a 32x32 fp32 MFMA result holds
   // row 8*(v/4) + 4*(l/32) + v%4 and column l%32 of the block.  The elements
