@@ -1463,9 +1463,10 @@ hipError_t launch_adjoint_finish(const AdjFinish& a, hipStream_t st) {
 
 namespace {
 constexpr int CADJ_THREADS = 256;
-constexpr int CADJ_PX = 256;               // output pixels per workgroup
 constexpr int CADJ_MAXK = 9;               // 4-deep contraction steps: (tap, input channel) pairs <= 36
-constexpr size_t CADJ_LDS = 48 * 1024;     // staged input rows of a band, with their border
+constexpr int CADJ_SPT = 16;               // staged floats per thread and row: a band's input rows <= 16 KB
+constexpr int CADJ_ROWS = 16;              // rows of one input per workgroup (fewer when that leaves CUs idle)
+constexpr int CADJ_TLD = 33;               // row stride of a wavefront's 16 x 32 transpose tile in LDS
 }  // namespace
 
 // Columns of a row's input image staged with a zero border: pad before, and
@@ -1474,19 +1475,24 @@ __host__ __device__ inline int cadj_span(int in, int out, int k, int stride, int
   const int last = (out - 1) * stride - pad + k;  // one past the last input index read
   return pad + (last > in ? last : in);
 }
-// Input rows staged for a band of CADJ_PX output pixels: the output rows the
-// band touches (at most (CADJ_PX + Wo - 2) / Wo + 1), their taps included.
-inline int cadj_band_rows(const ConvAdj& c) {
-  const int orows = std::min(c.Ho, (CADJ_PX + c.Wo - 2) / c.Wo + 1);
-  return (orows - 1) * c.stride + c.kh;
-}
-size_t cadj_lds_bytes(const ConvAdj& c) {
-  return (size_t)cadj_band_rows(c) * cadj_span(c.Wi, c.Wo, c.kw, c.stride, c.pad) * c.Ci * sizeof(float);
+// 16-channel blocks per wavefront: two (32 channels, whole 128-byte lines per
+// store) when Co is a multiple of 32, else one.
+inline int cadj_nbn(const ConvAdj& c) { return c.Co % 32 == 0 ? 2 : 1; }
+// Output pixels per workgroup: the four wavefronts take the channel groups of
+// 16-pixel blocks, as many blocks as fill them.
+inline int cadj_px(const ConvAdj& c) { return 16 * std::max(1, 4 / (c.Co / (16 * cadj_nbn(c)))); }
+// Input rows staged for a band of px output pixels: the output rows the band
+// touches (at most (px + Wo - 2) / Wo + 1), their taps included.
+inline int cadj_staged(const ConvAdj& c) {
+  const int px = cadj_px(c);
+  const int orows = std::min(c.Ho, (px + c.Wo - 2) / c.Wo + 1);
+  return ((orows - 1) * c.stride + c.kh) * cadj_span(c.Wi, c.Wo, c.kw, c.stride, c.pad) * c.Ci;
 }
 
 bool conv_adjoint_fits(const ConvAdj& c) {
   return c.Ci >= 1 && c.Ci <= 4 && c.Co % 16 == 0 && c.Co <= 64 && c.kh * c.kw * c.Ci <= 4 * CADJ_MAXK &&
-         c.stride >= 1 && c.pad >= 0 && c.Ho * c.Wo > 0 && cadj_lds_bytes(c) <= CADJ_LDS;
+         c.stride >= 1 && c.pad >= 0 && c.Ho * c.Wo > 0 && cadj_staged(c) <= CADJ_SPT * CADJ_THREADS &&
+         (long long)c.Hi * c.Wi * c.Ci <= 0x7fffffffLL;
 }
 
 // The adjoint of the alpha-CROWN step through a conv over a few-channel input
@@ -1495,53 +1501,87 @@ bool conv_adjoint_fits(const ConvAdj& c) {
 // the input at the tap's pixel times W[tap][c][c_in], on 16x16x4 fp32 matrix
 // blocks (A: output pixel = lane % 16, pair 4j + lane / 16 at step j; B: the
 // weights of the same pair for channel 16 * block + lane % 16, in registers),
-// then the adjoint epilogue on each result. A workgroup covers CADJ_PX output
-// pixels of 16 * NBN output channels; it stages the input rows they reach in
-// LDS with a zero border (so a step's operand is one offset from the pixel's
-// corner); the workgroups of one row share an XCD when xcd_map is set.
-template <int CI, int NBN>
-__global__ __launch_bounds__(CADJ_THREADS) void conv_adjoint_first_kernel(const ConvAdj c, int nbands, int xcd_map) {
-  extern __shared__ float gs[];  // [Hp][Wp][CI]
-  constexpr int WAVES = CADJ_THREADS / 64;
-  // workgroup -> (row, band of output pixels, group of 16 * NBN output channels)
-  const int ngroups = c.Co / (16 * NBN), nbc = nbands * ngroups;
-  const unsigned n = blockIdx.x;
-  long long row;
-  int bc;
-  if (xcd_map) {
-    const unsigned slot = n >> 3, rb = slot / (unsigned)nbc;
-    bc = (int)(slot - rb * (unsigned)nbc);
-    row = (long long)rb * 8 + (n & 7);
-  } else {
-    row = n / (unsigned)nbc;
-    bc = (int)(n - (unsigned)row * (unsigned)nbc);
-  }
-  const int band = bc / ngroups, cbase = (bc - band * ngroups) * 16 * NBN;
+// then the adjoint epilogue on each result.
+//
+// A wavefront computes 16 pixels x 16 NBN channels; a workgroup covers px
+// output pixels (all Co channels: wavefront w takes channel group w % G of
+// 16-pixel block w / G, G = Co / (16 NBN), so each pixel's results are
+// written whole by one workgroup) for up to CADJ_ROWS rows of the same input.
+// With NBN = 2 the results pass through a wavefront-private transpose tile in
+// LDS so that every store instruction writes 32 consecutive channels (whole
+// 128-byte lines) of two pixels: stores of 64-byte pieces of lines were
+// throttled by the vector L1 (its address unit stalled on it most of the
+// time).  The relaxation coefficients of the elements depend on the input
+// only: they are read once into registers and serve every row.  The input
+// rows the band reaches are staged in LDS with a zero border for all rows at
+// once (a step's operand is one offset from the pixel's corner): one wait for
+// the loads and one barrier, then the rows run back to back.
+template <int CI, int SPT, int NK, int NBN>
+__global__ __launch_bounds__(CADJ_THREADS) void conv_adjoint_first_kernel(const ConvAdj c, int nbands, int rchunk,
+                                                                         int nchunks, int staged, int tile_off) {
+  // [rchunk][staged] band rows [Hb][Wp][CI] per row (later the unstable-element
+  // lists), then with NBN = 2 one [16][CADJ_TLD] transpose tile per wavefront at tile_off
+  extern __shared__ __attribute__((aligned(16))) float gs[];
+  constexpr int E = 4 * NBN;  // results per lane and row
+  // workgroup -> (input, chunk of its rows, band of output pixels)
+  unsigned n = blockIdx.x;
+  const int band = (int)(n % (unsigned)nbands);
+  n /= (unsigned)nbands;
+  const int chunk = (int)(n % (unsigned)nchunks);
+  const long long b = n / (unsigned)nchunks;
+  const int rpb = c.a.rows_per_b;
+  const long long row0 = b * rpb + (long long)chunk * rchunk;
+  const int nr = (int)min((long long)min(rchunk, rpb - chunk * rchunk), (long long)c.a.M - row0);
+  if (nr <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, kk = lane >> 4;
+  const int G = c.Co / (16 * NBN), PB = max(1, 4 / G), px = 16 * PB;
+  const int grp = wave % G, blk = wave / G;
+  const bool active = blk < PB;  // (G = 3: the fourth wavefront only stages)
+  const int cbase = grp * 16 * NBN;
   const int Wp = cadj_span(c.Wi, c.Wo, c.kw, c.stride, c.pad);
   const int npx = c.Ho * c.Wo;
-  const int p0 = band * CADJ_PX, p1 = min(npx, p0 + CADJ_PX);
-  // staged input rows: padded rows oy0 * stride .. (oy1 * stride + kh - 1),
-  // one wavefront per row, lanes along the row
-  const int oy0 = p0 / c.Wo, oy1 = (p1 - 1) / c.Wo;
-  const int r0 = oy0 * c.stride, nrow = (oy1 - oy0) * c.stride + c.kh;
-  const float* src = c.g0 + row * (long long)c.Hi * c.Wi * CI;
-  for (int r = wave; r < nrow; r += WAVES) {
-    const int y = r0 + r - c.pad;
-    for (int t = lane; t < Wp * CI; t += 64) {
-      const int x = t / CI - c.pad, ci = t % CI;
-      gs[r * Wp * CI + t] = (y >= 0 && y < c.Hi && x >= 0 && x < c.Wi) ? src[(y * c.Wi + x) * CI + ci] : 0.f;
+  const int p0 = band * px, p1 = min(npx, p0 + px);
+  const int oy0 = p0 / c.Wo;
+  const int r0 = oy0 * c.stride;
+  const long long img = (long long)c.Hi * c.Wi * CI;
+
+  // this thread's staged floats (at most SPT): t = tid + 256 i -> (band row,
+  // column, channel), as an offset in a row's input image (-1: border or past the end)
+  int soff[SPT];
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int t = tid + CADJ_THREADS * i;
+    const int r = t / (Wp * CI), rem = t - r * (Wp * CI);
+    const int y = r0 + r - c.pad, x = rem / CI - c.pad, ci = rem - (rem / CI) * CI;
+    soff[i] = (t < staged && y >= 0 && y < c.Hi && x >= 0 && x < c.Wi) ? (y * c.Wi + x) * CI + ci : -1;
+  }
+  // stage every row of the chunk, eight rows' loads in flight at a time (a
+  // border slot, or a row past the chunk, loads a valid float and drops it);
+  // offsets from the chunk's first row fit 32 bits (rchunk * img < 2^31)
+  const float* gsrc = c.g0 + row0 * img;
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int t = tid + CADJ_THREADS * i;
+    if (CADJ_THREADS * i >= staged) break;  // (the same for the whole workgroup)
+    const int so = soff[i] < 0 ? 0 : soff[i];
+    for (int r = 0; r < nr; r += 8) {
+      float sv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sv[u] = gsrc[min(r + u, nr - 1) * (int)img + so];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (t < staged && r + u < nr) gs[(r + u) * staged + t] = soff[i] < 0 ? 0.f : sv[u];
     }
   }
 
   const int ncol = c.kh * c.kw * CI;
-  const int nk = (ncol + 3) / 4;
+  const int nk = (ncol + 3) / 4;  // <= NK
   // per step: this lane's pair as an offset from the pixel's corner, and the weights
-  float bw[CADJ_MAXK][NBN];
-  int off[CADJ_MAXK];
+  float bw[NK][NBN];
+  int off[NK];
 #pragma unroll
-  for (int j = 0; j < CADJ_MAXK; ++j) {
+  for (int j = 0; j < NK; ++j) {
     const int k = 4 * j + kk;
     const bool ok = j < nk && k < ncol;
     const int tap = ok ? k / CI : 0, ci = ok ? k - tap * CI : 0;
@@ -1549,76 +1589,206 @@ __global__ __launch_bounds__(CADJ_THREADS) void conv_adjoint_first_kernel(const 
     off[j] = (ky * Wp + kx) * CI + ci;  // a pair past the last one meets zero weights
 #pragma unroll
     for (int nb = 0; nb < NBN; ++nb)
-      bw[j][nb] = ok ? c.W[((long long)tap * c.Co + cbase + nb * 16 + li) * CI + ci] : 0.f;
+      bw[j][nb] = ok ? c.W[((long long)tap * c.Co + cbase + 16 * nb + li) * CI + ci] : 0.f;
   }
-  __syncthreads();
 
-  const long long bm = (row / c.a.rows_per_b) * c.a.N;  // this row's input in the coefficients
-  const int nmb = (p1 - p0 + 15) / 16;
-  for (int mb = wave; mb < nmb; mb += WAVES) {
-    const int p = min(p0 + mb * 16 + li, p1 - 1);  // rows past the band repeat its last pixel, never stored
-    const int oy = p / c.Wo, ox = p - oy * c.Wo;
-    const int corner = ((oy * c.stride - r0) * Wp + ox * c.stride) * CI;
-    // this lane's results: pixel p0 + 16 mb + 4 kk + v, channel cbase + 16 nb + li.
-    // The relaxation coefficients of result row v + 1 are loaded while row v
-    // finishes (those of row 0 ahead of the products)
-    long long nn[4][NBN];
-    int bi[NBN];
-    bool ok[4][NBN];
+  // This lane's stored results: NBN = 1: pixel pb + 4 kk + i, channel cbase +
+  // li (the MFMA layout); NBN = 2: pixel pb + 2 i + lane / 32, channel cbase +
+  // lane % 32 (the transposed layout).  Per result: its offset in a row, the
+  // factor of the raw adjoint stored in the first pass (the slope of a stable
+  // neuron; 1 for an unstable one, finished below) and its state column (-1
+  // stable, -2 past the band's end or an idle wavefront: never stored).
+  const int pb = p0 + 16 * blk;
+  const int sch = cbase + (NBN == 1 ? li : (lane & 31));
+  const float bias = c.a.bias ? c.a.bias[sch] : 0.f;
+  const float4* coef = c.a.coef + b * (long long)c.a.N;
+  const bool have = c.a.alpha_rw != nullptr;  // (a compact layout without unstable neurons has no state at all)
+  int eo[E], col[E];
+  float fac[E];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int pp = p0 + mb * 16 + 4 * kk + v;
+  for (int i = 0; i < E; ++i) {
+    const int pp = pb + (NBN == 1 ? 4 * kk + i : 2 * i + (lane >> 5));
+    eo[i] = pp * c.Co + sch;
+    const float4 cf = active && pp < p1 ? coef[eo[i]] : make_float4(0.f, 0.f, 0.f, __int_as_float(-2));
+    col[i] = __float_as_int(cf.w);
+    fac[i] = (col[i] >= 0 && have) ? 1.f : cf.y;
+  }
+  // the A operand's pixel (rows past the band repeat its last pixel)
+  const int pa = min(pb + li, p1 - 1);
+  const int oya = pa / c.Wo, oxa = pa - oya * c.Wo;
+  const int corner = ((oya * c.stride - r0) * Wp + oxa * c.stride) * CI;
+  float* tile = gs + tile_off + wave * (16 * CADJ_TLD);
+
+  // Rows back to back: products and the stores of every result (an unstable
+  // element's result needs its kept Psi and slope and updates its Adam state:
+  // loads whose latency would stall every row, so the row stores the raw
+  // adjoint there and the unstable elements of all rows are finished together
+  // afterwards).
+  __syncthreads();
+  if (active) {
+    float* orow = c.a.out + row0 * c.a.N;
+    float* gzrow = c.a.gz_out ? c.a.gz_out + row0 * c.a.N : nullptr;
+    const float* g = gs + corner;
+    for (int r = 0; r < nr; ++r) {
+      // (all NK operand reads first; steps past nk read offset 0 and meet zero weights)
+      float av[NK];
 #pragma unroll
-      for (int nb = 0; nb < NBN; ++nb) {
-        bi[nb] = cbase + nb * 16 + li;
-        nn[v][nb] = (long long)pp * c.Co + bi[nb];
-        ok[v][nb] = pp < p1;
+      for (int j = 0; j < NK; ++j) av[j] = g[off[j]];
+      cin_v4 acc[NBN];
+#pragma unroll
+      for (int nb = 0; nb < NBN; ++nb) acc[nb] = cin_v4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NK; ++j)
+#pragma unroll
+        for (int nb = 0; nb < NBN; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bw[j][nb], acc[nb], 0, 0, 0);
+      float val[E];
+      if (NBN == 1) {
+#pragma unroll
+        for (int i = 0; i < E; ++i) val[i] = acc[0][i];
+      } else {
+        // through the tile: element (pixel 4 kk + v, channel 16 nb + li) ->
+        // lane (channel lane % 32) slot i (pixel 2 i + lane / 32); the tile
+        // is this wavefront's own, whose LDS accesses complete in order
+#pragma unroll
+        for (int nb = 0; nb < NBN; ++nb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) tile[(4 * kk + v) * CADJ_TLD + 16 * nb + li] = acc[nb][v];
+#pragma unroll
+        for (int i = 0; i < E; ++i) val[i] = tile[(2 * i + (lane >> 5)) * CADJ_TLD + (lane & 31)];
       }
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        if (col[i] == -2) continue;
+        const float gz = val[i] + bias;
+        orow[eo[i]] = gz * fac[i];
+        if (gzrow) gzrow[eo[i]] = gz;
+      }
+      g += staged;
+      orow += c.a.N;
+      if (gzrow) gzrow += c.a.N;
     }
-    float4 cf[2][NBN];
-    adjoint_coef<NBN>(c.a, bm, nn[0], ok[0], cf[0]);
-    cin_v4 acc[NBN];
+  }
+  if (!have) return;  // (uniform)
+
+  // The unstable elements: each wavefront lists its own (element offset,
+  // state column) in LDS, then its lanes take the (row, element) pairs in
+  // row-major order, four at a time, all loads first (consecutive lanes:
+  // consecutive state columns of one row).
+  __syncthreads();  // every wavefront is done with the staged rows
+  int2* desc = reinterpret_cast<int2*>(gs) + wave * (64 * E);
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int nu = 0;
 #pragma unroll
-    for (int nb = 0; nb < NBN; ++nb) acc[nb] = cin_v4{0.f, 0.f, 0.f, 0.f};
-    // (steps past the last pair read offset 0 and meet zero weights)
+  for (int i = 0; i < E; ++i) {
+    const bool u = col[i] >= 0;
+    const unsigned long long m = __ballot(u);
+    if (u) desc[nu + __popcll(m & below)] = make_int2(eo[i], col[i]);
+    nu += __popcll(m);
+  }
+  if (nu == 0) return;  // (uniform in the wavefront; no barrier follows)
+  // this wavefront's stores of the raw adjoints above are seen by its loads below
+  __threadfence_block();
+  const int P = nu * nr;
+  const bool upd = c.a.do_update;
+  for (int q0 = lane; q0 < P; q0 += 4 * 64) {
+    float gz[4], psi[4], ao[4], am[4], av[4];
+    float4 cf[4];
+    long long oi[4], si[4];
+    bool okp[4];
 #pragma unroll
-    for (int j = 0; j < CADJ_MAXK; ++j) {
-      const float av = gs[corner + off[j]];
-#pragma unroll
-      for (int nb = 0; nb < NBN; ++nb) acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bw[j][nb], acc[nb], 0, 0, 0);
+    for (int k = 0; k < 4; ++k) {
+      const int q = q0 + 64 * k;
+      okp[k] = q < P;
+      const int r = okp[k] ? q / nu : 0;
+      const int2 dd = desc[okp[k] ? q - r * nu : 0];
+      const long long row = row0 + r;
+      oi[k] = row * c.a.N + dd.x;
+      si[k] = c.a.aidx ? row * c.a.acols + dd.y : oi[k];
+      cf[k] = coef[dd.x];
+      gz[k] = c.a.out[oi[k]];
+      psi[k] = c.a.psi_in[si[k]];
+      ao[k] = c.a.alpha_rw[si[k]];
+      am[k] = upd ? c.a.adam_m[si[k]] : 0.f;
+      av[k] = upd ? c.a.adam_v[si[k]] : 0.f;
     }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      if (v + 1 < 4) adjoint_coef<NBN>(c.a, bm, nn[v + 1], ok[v + 1], cf[(v + 1) & 1]);
-      float gv[NBN];
-#pragma unroll
-      for (int nb = 0; nb < NBN; ++nb) gv[nb] = acc[nb][v];
-      adjoint_elements<NBN>(c.a, row, nn[v], bi, gv, ok[v], cf[v & 1]);
+    for (int k = 0; k < 4; ++k) {
+      if (!okp[k]) continue;
+      const float g = gz[k];
+      c.a.out[oi[k]] = psi[k] >= 0.f ? g * ao[k] : g * cf[k].y + cf[k].z;
+      if (upd) {
+        const float grad = g * fmaxf(psi[k], 0.f);
+        const float mm = c.a.beta1 * am[k] + (1.f - c.a.beta1) * grad;
+        const float vv = c.a.beta2 * av[k] + (1.f - c.a.beta2) * grad * grad;
+        c.a.adam_m[si[k]] = mm;
+        c.a.adam_v[si[k]] = vv;
+        const float step = c.a.lr * (mm * c.a.bc1) / (sqrtf(vv * c.a.bc2) + c.a.adam_eps);
+        c.a.alpha_rw[si[k]] = fminf(fmaxf(ao[k] + step, 0.f), 1.f);
+      }
     }
   }
 }
 
+// (contraction steps: exactly those of a 3x3 kernel, else the most any shape takes)
+template <int CI, int NK, int NBN>
+void cadj_launch_nk(unsigned grid, size_t lds, hipStream_t st, const ConvAdj& c, int nbands, int rchunk, int nchunks,
+                    int staged, int tile_off) {
+  if (staged <= 4 * CADJ_THREADS)
+    hipLaunchKernelGGL((conv_adjoint_first_kernel<CI, 4, NK, NBN>), dim3(grid), dim3(CADJ_THREADS), lds, st, c,
+                       nbands, rchunk, nchunks, staged, tile_off);
+  else
+    hipLaunchKernelGGL((conv_adjoint_first_kernel<CI, CADJ_SPT, NK, NBN>), dim3(grid), dim3(CADJ_THREADS), lds, st,
+                       c, nbands, rchunk, nchunks, staged, tile_off);
+}
+template <int CI, int NBN>
+void cadj_launch(unsigned grid, size_t lds, hipStream_t st, const ConvAdj& c, int nbands, int rchunk, int nchunks,
+                 int staged, int tile_off) {
+  constexpr int NK3 = (9 * CI + 3) / 4;
+  if ((c.kh * c.kw * CI + 3) / 4 <= NK3)
+    cadj_launch_nk<CI, NK3, NBN>(grid, lds, st, c, nbands, rchunk, nchunks, staged, tile_off);
+  else
+    cadj_launch_nk<CI, CADJ_MAXK, NBN>(grid, lds, st, c, nbands, rchunk, nchunks, staged, tile_off);
+}
 template <int CI>
-void cadj_launch(unsigned grid, size_t lds, hipStream_t st, const ConvAdj& c, int nbands, int xm) {
-  hipLaunchKernelGGL((conv_adjoint_first_kernel<CI, 1>), dim3(grid), dim3(CADJ_THREADS), lds, st, c, nbands, xm);
+void cadj_launch_ci(unsigned grid, size_t lds, hipStream_t st, const ConvAdj& c, int nbands, int rchunk, int nchunks,
+                    int staged, int tile_off) {
+  if (cadj_nbn(c) == 2)
+    cadj_launch<CI, 2>(grid, lds, st, c, nbands, rchunk, nchunks, staged, tile_off);
+  else
+    cadj_launch<CI, 1>(grid, lds, st, c, nbands, rchunk, nchunks, staged, tile_off);
 }
 
 hipError_t launch_conv_adjoint_first(const ConvAdj& c, int rows, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  if (!conv_adjoint_fits(c) || c.a.M != rows || c.a.N != c.Ho * c.Wo * c.Co) return hipErrorInvalidValue;
-  const int nbands = (c.Ho * c.Wo + CADJ_PX - 1) / CADJ_PX;
-  // 16 output channels per workgroup: fewer results per lane keep more
-  // wavefronts in flight to cover the epilogue's loads
-  const long long groups = c.Co / 16;
-  if ((long long)rows * nbands * groups > 0x7fffffffLL) return hipErrorInvalidValue;
-  const unsigned grid = (unsigned)((long long)rows * nbands * groups);
-  const size_t lds = cadj_lds_bytes(c);
-  const int xm = rows % 8 == 0;
+  if (!conv_adjoint_fits(c) || c.a.M != rows || c.a.N != c.Ho * c.Wo * c.Co || c.a.rows_per_b <= 0)
+    return hipErrorInvalidValue;
+  const int nbands = (c.Ho * c.Wo + cadj_px(c) - 1) / cadj_px(c);
+  const int rpb = c.a.rows_per_b;
+  const long long inputs = ((long long)rows + rpb - 1) / rpb;
+  // rows of one input per workgroup: CADJ_ROWS, or fewer (down to 3 or 4)
+  // while the grid would leave part of the chip without eight workgroups per
+  // CU; and at most 40 KB of staged rows
+  const int staged = cadj_staged(c);
+  int rchunk = std::min(CADJ_ROWS, rpb);
+  while (rchunk > 4 && inputs * ((rpb + rchunk - 1) / rchunk) * nbands < 2048) rchunk = (rchunk + 1) / 2;
+  rchunk = std::max(1, std::min(rchunk, (int)(40960 / (staged * sizeof(float)))));
+  // (the staging addresses a chunk's input rows with 32-bit offsets)
+  const long long img = (long long)c.Hi * c.Wi * c.Ci;
+  while (rchunk > 1 && rchunk * img > 0x7fffffffLL) rchunk /= 2;
+  const int nchunks = (rpb + rchunk - 1) / rchunk;
+  const long long grid = inputs * nchunks * nbands;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  // LDS: the staged rows, which the unstable-element lists (up to 64 * 4 NBN
+  // entries of 8 bytes per wavefront) reuse, then the transpose tiles
+  const int nbn = cadj_nbn(c);
+  const size_t first = std::max((size_t)rchunk * staged * sizeof(float), (size_t)CADJ_THREADS * 4 * nbn * 8);
+  const int tile_off = (int)(first / sizeof(float));
+  const size_t lds = first + (nbn == 2 ? (size_t)(CADJ_THREADS / 64) * 16 * CADJ_TLD * sizeof(float) : 0);
   switch (c.Ci) {
-    case 1: cadj_launch<1>(grid, lds, st, c, nbands, xm); break;
-    case 2: cadj_launch<2>(grid, lds, st, c, nbands, xm); break;
-    case 3: cadj_launch<3>(grid, lds, st, c, nbands, xm); break;
-    default: cadj_launch<4>(grid, lds, st, c, nbands, xm); break;
+    case 1: cadj_launch_ci<1>((unsigned)grid, lds, st, c, nbands, rchunk, nchunks, staged, tile_off); break;
+    case 2: cadj_launch_ci<2>((unsigned)grid, lds, st, c, nbands, rchunk, nchunks, staged, tile_off); break;
+    case 3: cadj_launch_ci<3>((unsigned)grid, lds, st, c, nbands, rchunk, nchunks, staged, tile_off); break;
+    default: cadj_launch_ci<4>((unsigned)grid, lds, st, c, nbands, rchunk, nchunks, staged, tile_off); break;
   }
   return hipGetLastError();
 }
