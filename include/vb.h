@@ -63,6 +63,10 @@ typedef struct {
   int32_t kh, kw, stride, pad;/* conv2d only (zero padding, same in both dims)   */
   const float* weight;        /* device, borrowed for the call                   */
   const float* bias;          /* device or NULL                                  */
+  const float* weight_packed; /* LINEAR: NULL, or the copy of weight that        */
+                              /* vb_pack_linear wrote (device, 16-byte aligned,  */
+                              /* borrowed for the call); vb_ibp then reads it    */
+                              /* instead of weight for small batches            */
 } vb_node;
 
 typedef struct {
@@ -100,6 +104,22 @@ const char* vb_last_error(void);
  * chunks (same results). */
 vb_status vb_workspace_size(const vb_graph* g, int32_t batch, int32_t m, int32_t method,
                             int32_t region_start, size_t* bytes);
+
+/* Weight layout for IBP over wide Linear layers (Sec. 1 of the page: a hidden
+ * layer of 262 144 neurons, whose weights IBP reads once per call).  For a
+ * batch of at most 16, vb_ibp streams each Linear node's weights once through
+ * the matrix cores; with a packed copy its load instructions read 1 KB of
+ * contiguous memory each instead of 64-byte pieces of 16 rows.  The copy holds
+ * the same numbers as weight ([n_out][n_in], n_in a multiple of 16) in blocks
+ * of 16 rows x 16 columns, rows past n_out zero: vb_pack_linear_bytes gives its
+ * size; vb_pack_linear writes it (enqueued on stream) into dst, which the
+ * caller owns and passes as vb_node.weight_packed.  The copy is a snapshot:
+ * pack again after changing the weights.  VB_EINVAL if n_in % 16 != 0, a size
+ * is not positive, a pointer is NULL or dst is not 16-byte aligned; VB_ENOMEM
+ * if dst_bytes is smaller than the size. */
+vb_status vb_pack_linear_bytes(int32_t n_out, int32_t n_in, size_t* bytes);
+vb_status vb_pack_linear(const float* weight, int32_t n_out, int32_t n_in, float* dst, size_t dst_bytes,
+                         void* stream);
 
 /* IBP (interval bound propagation, centre/radius form; Sec. 1 and Sec. 2.1 of
  * the page).  For every non-input node k with node_lo[k] != NULL, writes its

@@ -35,7 +35,7 @@ _OPS = {"input": VB_INPUT, "linear": VB_LINEAR, "conv": VB_CONV2D, "relu": VB_RE
 EXPORTS = ["vb_last_error", "vb_workspace_size", "vb_ibp", "vb_crown_backward", "vb_concretize",
            "vb_alpha_layout", "vb_alpha_init", "vb_alpha_step", "vb_alpha_step_rows", "vb_apply_splits",
            "vb_bab_workspace_size", "vb_bab", "vb_crown", "vb_crown_noalloc", "vb_verify",
-           "vb_profile_start", "vb_profile_stop", "vb_profile_record"]
+           "vb_profile_start", "vb_profile_stop", "vb_profile_record", "vb_pack_linear_bytes", "vb_pack_linear"]
 # host-only helpers declared in include/vb_testing.h (used by the CPU tests)
 TESTING_EXPORTS = ["vb_testing_fastdiv", "vb_testing_conv_tile_n", "vb_testing_identity_path"]
 
@@ -44,7 +44,8 @@ class vb_node(ctypes.Structure):
     _fields_ = [("op", ctypes.c_int32), ("in0", ctypes.c_int32), ("in1", ctypes.c_int32),
                 ("c", ctypes.c_int32), ("h", ctypes.c_int32), ("w", ctypes.c_int32),
                 ("kh", ctypes.c_int32), ("kw", ctypes.c_int32), ("stride", ctypes.c_int32),
-                ("pad", ctypes.c_int32), ("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
+                ("pad", ctypes.c_int32), ("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("weight_packed", ctypes.c_void_p)]
 
 
 class vb_graph(ctypes.Structure):
@@ -80,6 +81,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vb_workspace_size.argtypes = [G, i32, i32, i32, i32, ctypes.POINTER(sz)]
     lib.vb_ibp.restype = i32
     lib.vb_ibp.argtypes = [G, i32, P, P, f32, PP, PP, P, i32, P, P, P, sz, P]
+    lib.vb_pack_linear_bytes.restype = i32
+    lib.vb_pack_linear_bytes.argtypes = [i32, i32, ctypes.POINTER(sz)]
+    lib.vb_pack_linear.restype = i32
+    lib.vb_pack_linear.argtypes = [P, i32, i32, P, sz, P]
     lib.vb_crown_backward.restype = i32
     AC = ctypes.POINTER(vb_alpha_compact)
     lib.vb_crown_backward.argtypes = [G, i32, i32, i32, P, i32, PP, PP, AC, PP, P, P, f32, P, P, P, P, P, sz, P]
@@ -185,6 +190,7 @@ class DeviceNet:
         self.ops = [n.op for n in nodes]
         self.inputs = [tuple(n.inputs) for n in nodes]
         self._keep: List[torch.Tensor] = []
+        self._w: List[Optional[torch.Tensor]] = []  # device weights per node (None without)
         arr = (vb_node * len(nodes))()
         for k, n in enumerate(nodes):
             v = arr[k]
@@ -216,11 +222,38 @@ class DeviceNet:
                 self._keep += [w, b]
                 v.weight = w.data_ptr()
                 v.bias = b.data_ptr()
+            self._w.append(w)
         self.nodes_c = arr
         self.graph = vb_graph(len(nodes), arr)
         self.gp = ctypes.pointer(self.graph)
         self.n_nodes = len(nodes)
         self.sizes = [int(np.prod(s)) for s in self.shapes]
+
+    def pack_linear(self, min_weights: int = 0):
+        """Packed copies (vb_pack_linear) of the Linear nodes' weights whose input
+        size is a multiple of 16 and that hold at least `min_weights` weights;
+        vb_ibp then reads those for batches of up to 16.  Returns the bytes held."""
+        total = 0
+        for k, op in enumerate(self.ops):
+            if op != "linear":
+                continue
+            n_out, n_in = self.nodes_c[k].c, self._w[k].shape[1]
+            if n_in % 16 or n_out * n_in < min_weights:
+                continue
+            nb = ctypes.c_size_t(0)
+            _check(lib().vb_pack_linear_bytes(n_out, n_in, ctypes.byref(nb)), "vb_pack_linear_bytes")
+            dst = torch.empty(nb.value // 4, dtype=torch.float32, device=self.device)
+            _check(lib().vb_pack_linear(self._w[k].data_ptr(), n_out, n_in, dst.data_ptr(), nb.value,
+                                        _stream()), "vb_pack_linear")
+            self._keep.append(dst)
+            self.nodes_c[k].weight_packed = dst.data_ptr()
+            total += nb.value
+        return total
+
+    def unpack_linear(self):
+        """Drop the packed copies from the node descriptions (vb_ibp reads weight again)."""
+        for k in range(self.n_nodes):
+            self.nodes_c[k].weight_packed = None
 
     # ------------------------------------------------------------------
     def alloc_bounds(self, batch: int):

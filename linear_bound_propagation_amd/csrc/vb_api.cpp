@@ -57,6 +57,7 @@ struct NodeInfo {
   int kh, kw, stride, pad;
   const float* W;
   const float* b;
+  const float* Wp;        // packed copy of a LINEAR node's W (vb_pack_linear) or NULL
   std::vector<int> cons;  // consumers (direct)
 };
 
@@ -84,6 +85,9 @@ vb_status parse_graph(const vb_graph* g, Graph& G) {
     d.pad = s.pad;
     d.W = s.weight;
     d.b = s.bias;
+    d.Wp = s.weight_packed;
+    if (d.Wp && (s.op != VB_LINEAR || ((uintptr_t)d.Wp & 15) != 0))
+      return fail(VB_EINVAL, "node %d: weight_packed is for LINEAR nodes, 16-byte aligned", k);
     if (d.c <= 0 || d.h <= 0 || d.w <= 0) return fail(VB_ESHAPE, "node %d: non-positive shape", k);
     d.size = (long long)d.c * d.h * d.w;
     if (d.size >= (1LL << 31)) return fail(VB_ESHAPE, "node %d: size too large", k);
@@ -2064,6 +2068,10 @@ vb_status ibp_impl(const Graph& G, int batch, const float* xc, const float* xr, 
           q.A2 = a2;
           q.eps = eps;
           q.W = nd.W;
+          if (nd.Wp && q.K % 16 == 0) {
+            q.W = nd.Wp;
+            q.packed = 1;
+          }
           q.bias = nd.b;
           q.lo = lo[k];
           q.hi = hi[k];
@@ -2243,6 +2251,25 @@ static vb_status spec_ibp(const Graph& G, int batch, const float* C, int m, cons
                                              spec_hi ? spec_hi + (long long)b0 * m : nullptr, nullptr, st));
                         return VB_OK;
                       });
+}
+
+extern "C" vb_status vb_pack_linear_bytes(int32_t n_out, int32_t n_in, size_t* bytes) {
+  if (!bytes) return fail(VB_EINVAL, "bytes is NULL");
+  if (n_out <= 0 || n_in <= 0 || n_in % 16 != 0)
+    return fail(VB_EINVAL, "pack_linear: n_out > 0 and n_in a positive multiple of 16 (got %d, %d)", n_out, n_in);
+  *bytes = pack_linear_floats(n_out, n_in) * sizeof(float);
+  return VB_OK;
+}
+
+extern "C" vb_status vb_pack_linear(const float* weight, int32_t n_out, int32_t n_in, float* dst, size_t dst_bytes,
+                                    void* stream) {
+  size_t need = 0;
+  if (vb_status s = vb_pack_linear_bytes(n_out, n_in, &need)) return s;
+  if (!weight || !dst) return fail(VB_EINVAL, "pack_linear: weight or dst is NULL");
+  if (((uintptr_t)dst & 15) != 0) return fail(VB_EINVAL, "pack_linear: dst must be 16-byte aligned");
+  if (dst_bytes < need) return fail(VB_ENOMEM, "pack_linear: dst holds %zu bytes, the copy needs %zu", dst_bytes, need);
+  HIPCHK(launch_pack_linear(weight, n_out, n_in, dst, (hipStream_t)stream));
+  return VB_OK;
 }
 
 extern "C" vb_status vb_ibp(const vb_graph* g, int32_t batch, const float* x_center, const float* x_radius,

@@ -3,6 +3,13 @@
 // dominates all traffic (the page's wide single-hidden-layer networks, Sec. 1;
 // IBP as the cheap bound of Sec. 2.1).
 //
+// Two options cut the kernel's work per weight byte.  (1) A packed copy of the
+// weights (vb_pack_linear) stores each 16-row x 16-column block as 1 KB in the
+// order the lanes read it, so every load instruction covers 1 KB of contiguous
+// memory instead of 64-byte pieces of 16 rows.  (2) For a ball of one radius
+// (the input layer), |W| r is eps times the row sums of |W|, the same for every
+// input: they are added on the vector ALUs from the weight registers and the
+// second MFMA chain is dropped.
 // Output neurons run along the MFMA row dimension and the batch along its
 // column dimension (v_mfma_f32_16x16x4f32, at most 16 inputs): each lane
 // streams float4 pieces of its weight rows straight from HBM into registers
@@ -36,7 +43,7 @@ __device__ __forceinline__ float4 ldg4(const float* __restrict__ p, long long of
   return *reinterpret_cast<const float4*>(p + off);
 }
 
-template <int AMODE>
+template <int AMODE, bool PACK, bool RS>
 __global__ __launch_bounds__(256) void ibp_narrow_kernel(NarrowIbp d) {
   const int lane = threadIdx.x & 63;
   // wavefronts are numbered over (slice, block of ROWS neurons), so a layer with
@@ -53,17 +60,28 @@ __global__ __launch_bounds__(256) void ibp_narrow_kernel(NarrowIbp d) {
   // 4*g + s of every 16-wide step s; B operand: input r16 at the same K index.
   const bool jok = r16 < d.batch;
   const long long xrow = (long long)(jok ? r16 : 0) * d.K;
+  // row-major: the element offset of each of this lane's rows; packed: of the
+  // lane's float4 in the first 16-column block of each of its 16-row blocks
+  // (the packed copy holds whole blocks, rows past N zero)
   long long wrow[NB];
+  const int KT = d.K / 16, nblk = (d.N + 15) / 16;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const int n = n0 + 16 * b + r16;
-    wrow[b] = (long long)(n < d.N ? n : d.N - 1) * d.K;
+    if (PACK) {
+      const int rb = min((n0 >> 4) + b, nblk - 1);
+      wrow[b] = (long long)rb * KT * 256 + lane * 4;
+    } else {
+      const int n = n0 + 16 * b + r16;
+      wrow[b] = (long long)(n < d.N ? n : d.N - 1) * d.K;
+    }
   }
   f32x4 ac[NB], ar[NB];
+  float rs[NB];  // (RS) partial sums of |W| over this lane's columns of its rows
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     ac[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     ar[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    rs[b] = 0.f;
   }
   // Every wavefront walks its K range from a different starting chunk (and wraps
   // around): rows lie K floats apart, so waves that moved through K in step
@@ -74,20 +92,24 @@ __global__ __launch_bounds__(256) void ibp_narrow_kernel(NarrowIbp d) {
     const int k0 = kbeg + ch * 16 * U;
     ch = (ch + 1 == nch) ? 0 : ch + 1;
     float4 w[U][NB], c[U], r[U];
+    bool kin[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = k0 + 16 * u + 4 * g;
-      const bool kok = k < kend;  // K and kchunk are multiples of 4
+      const bool kok = k < kend;  // K and kchunk are multiples of 4 (of 16 with PACK: kok is per u)
+      kin[u] = kok;
       const long long kc = kok ? k : kbeg;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) w[u][b] = ldg4(d.W, wrow[b] + kc);
+      for (int b = 0; b < NB; ++b)
+        w[u][b] = PACK ? ldg4(d.W, wrow[b] + (long long)((kok ? k0 + 16 * u : kbeg) >> 4) * 256)
+                       : ldg4(d.W, wrow[b] + kc);
       if (AMODE == A_IBP_BOX) {
         const float4 l = ldg4(d.A, xrow + kc), h = ldg4(d.A2, xrow + kc);
         c[u] = make_float4((l.x + h.x) * 0.5f, (l.y + h.y) * 0.5f, (l.z + h.z) * 0.5f, (l.w + h.w) * 0.5f);
         r[u] = make_float4((h.x - l.x) * 0.5f, (h.y - l.y) * 0.5f, (h.z - l.z) * 0.5f, (h.w - l.w) * 0.5f);
       } else {
         c[u] = ldg4(d.A, xrow + kc);
-        r[u] = d.A2 ? ldg4(d.A2, xrow + kc) : make_float4(d.eps, d.eps, d.eps, d.eps);
+        r[u] = (!RS && d.A2) ? ldg4(d.A2, xrow + kc) : make_float4(d.eps, d.eps, d.eps, d.eps);
       }
       if (!(kok && jok)) {
         c[u] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -97,7 +119,7 @@ __global__ __launch_bounds__(256) void ibp_narrow_kernel(NarrowIbp d) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const float cs[4] = {c[u].x, c[u].y, c[u].z, c[u].w};
-      const float rs[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
+      const float rs_[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -105,10 +127,28 @@ __global__ __launch_bounds__(256) void ibp_narrow_kernel(NarrowIbp d) {
           const float4& wv = w[u][b];
           const float ws = s == 0 ? wv.x : s == 1 ? wv.y : s == 2 ? wv.z : wv.w;
           ac[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(ws, cs[s], ac[b], 0, 0, 0);
-          ar[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(fabsf(ws), rs[s], ar[b], 0, 0, 0);
+          if (!RS) ar[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(fabsf(ws), rs_[s], ar[b], 0, 0, 0);
         }
       }
+      if (RS && kin[u]) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          rs[b] += (fabsf(w[u][b].x) + fabsf(w[u][b].y)) + (fabsf(w[u][b].z) + fabsf(w[u][b].w));
+      }
     }
+  }
+  if (RS) {
+    // row sums of |W| of row 16 b + r16 over the four column groups, then the
+    // sum of the row this lane's results belong to (neuron 16 b + 4 g + v: lane 4 g + v)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      rs[b] += __shfl_xor(rs[b], 16, 64);
+      rs[b] += __shfl_xor(rs[b], 32, 64);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) ar[b][v] = d.eps * __shfl(rs[b], 4 * g + v, 64);
   }
   // result register v of lane (r16, g): neuron n0 + 16*blk + 4*g + v, input r16
   if (!jok) return;
@@ -192,10 +232,25 @@ hipError_t launch_ibp_narrow(NarrowIbp d, int S, hipStream_t st) {
   d.slices = slices;
   const long long waves = (long long)((d.N + ROWS - 1) / ROWS) * slices;
   const dim3 grid((unsigned)((waves + 3) / 4));
-  if (d.amode == A_IBP_BOX)
-    hipLaunchKernelGGL(ibp_narrow_kernel<A_IBP_BOX>, grid, dim3(256), 0, st, d);
-  else
-    hipLaunchKernelGGL(ibp_narrow_kernel<A_IBP_BALL>, grid, dim3(256), 0, st, d);
+  if (d.packed && d.K % 16 != 0) return hipErrorInvalidValue;
+  // radius by row sums: a ball of one radius only
+  const bool rs = d.amode == A_IBP_BALL && d.A2 == nullptr;
+  if (d.amode == A_IBP_BOX) {
+    if (d.packed)
+      hipLaunchKernelGGL((ibp_narrow_kernel<A_IBP_BOX, true, false>), grid, dim3(256), 0, st, d);
+    else
+      hipLaunchKernelGGL((ibp_narrow_kernel<A_IBP_BOX, false, false>), grid, dim3(256), 0, st, d);
+  } else if (rs) {
+    if (d.packed)
+      hipLaunchKernelGGL((ibp_narrow_kernel<A_IBP_BALL, true, true>), grid, dim3(256), 0, st, d);
+    else
+      hipLaunchKernelGGL((ibp_narrow_kernel<A_IBP_BALL, false, true>), grid, dim3(256), 0, st, d);
+  } else {
+    if (d.packed)
+      hipLaunchKernelGGL((ibp_narrow_kernel<A_IBP_BALL, true, false>), grid, dim3(256), 0, st, d);
+    else
+      hipLaunchKernelGGL((ibp_narrow_kernel<A_IBP_BALL, false, false>), grid, dim3(256), 0, st, d);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || slices == 1) return e;
   const long long MN = (long long)d.batch * d.N;
@@ -203,6 +258,32 @@ hipError_t launch_ibp_narrow(NarrowIbp d, int S, hipStream_t st) {
     return launch_ibp_splitk_finish(d.pc, d.pr, slices, MN, d.N, d.bias, d.lo, d.hi, d.relu_lo, d.relu_hi, st);
   hipLaunchKernelGGL(narrow_finish_kernel, dim3((unsigned)((MN + 3) / 4)), dim3(256), 0, st, d.pc, d.pr, slices, MN,
                      d.N, d.bias, d.lo, d.hi, d.relu_lo, d.relu_hi);
+  return hipGetLastError();
+}
+
+// Packed copy of W [N][K] for the narrow kernel: block (rb, kc) of rows 16 rb
+// .. 16 rb + 15 and columns 16 kc .. 16 kc + 15 at floats (rb K/16 + kc) 256,
+// its float4 number l (lane l of the reading wavefront) holding row 16 rb +
+// l % 16, columns 16 kc + 4 (l / 16) .. + 3; rows past N are zero.
+__global__ void pack_linear_kernel(const float* __restrict__ W, int N, int K, float* __restrict__ dst) {
+  const int KT = K / 16;
+  const long long total = (long long)((N + 15) / 16) * 16 * K;
+  for (long long o = (long long)blockIdx.x * blockDim.x + threadIdx.x; o < total;
+       o += (long long)gridDim.x * blockDim.x) {
+    const long long blk = o >> 8;
+    const int e = (int)(o & 255), l = e >> 2, comp = e & 3;
+    const long long rb = blk / KT;
+    const int kc = (int)(blk - rb * KT);
+    const long long row = rb * 16 + (l & 15);
+    dst[o] = row < N ? W[row * K + kc * 16 + 4 * (l >> 4) + comp] : 0.f;
+  }
+}
+
+size_t pack_linear_floats(int N, int K) { return (size_t)((N + 15) / 16) * 16 * (size_t)K; }
+
+hipError_t launch_pack_linear(const float* W, int N, int K, float* dst, hipStream_t st) {
+  if (N <= 0 || K <= 0 || K % 16 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_linear_kernel, dim3(8192), dim3(256), 0, st, W, N, K, dst);
   return hipGetLastError();
 }
 

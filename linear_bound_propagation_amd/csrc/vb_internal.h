@@ -447,10 +447,14 @@ struct NarrowIbp {
   float* pr;
   int kchunk;               // set by the launcher
   int slices;               // set by the launcher
+  int packed;               // W is the packed copy (launch_pack_linear; K a multiple of 16)
 };
 bool ibp_narrow_fits(int batch, int K, const float* W, const float* A, const float* A2);
 int ibp_narrow_slices(int N, int K);
 hipError_t launch_ibp_narrow(NarrowIbp d, int S, hipStream_t st);
+// The narrow kernel's packed weight layout: floats of the copy, and the copy.
+size_t pack_linear_floats(int N, int K);
+hipError_t launch_pack_linear(const float* W, int N, int K, float* dst, hipStream_t st);
 
 // verified[b] = 1 iff every lb[b][i] > 0 (i < m); count[0] (if count) = number of verified inputs.
 hipError_t launch_verify(const float* lb, int batch, int m, int* verified, int* count, hipStream_t st);

@@ -217,3 +217,34 @@ def test_ibp_checks_every_node_before_launching():
     assert lbp.lib().vb_ibp(ctypes.pointer(g), 2, P(64), None, 0.1, half, other, None, 0, None, None, None, 0,
                             None) == -1
     assert b"only one of" in lbp.lib().vb_last_error()
+
+
+def test_pack_linear_checks_arguments_before_any_launch():
+    """vb_pack_linear_bytes gives whole 16-row blocks of n_in floats; both calls reject
+    n_in not a multiple of 16, NULL or misaligned pointers and a short destination
+    before enqueueing anything (fake device addresses: nothing is dereferenced)."""
+    L = lbp.lib()
+    nb = ctypes.c_size_t(0)
+    assert L.vb_pack_linear_bytes(100, 4096, ctypes.byref(nb)) == 0 and nb.value == 112 * 4096 * 4
+    assert L.vb_pack_linear_bytes(16, 16, ctypes.byref(nb)) == 0 and nb.value == 16 * 16 * 4
+    assert L.vb_pack_linear_bytes(100, 4090, ctypes.byref(nb)) == -1
+    assert L.vb_pack_linear_bytes(0, 16, ctypes.byref(nb)) == -1
+    assert L.vb_pack_linear_bytes(16, 16, None) == -1
+    need = 112 * 4096 * 4
+    assert L.vb_pack_linear(16, 100, 4090, 256, need, None) == -1          # n_in
+    assert L.vb_pack_linear(None, 100, 4096, 256, need, None) == -1        # weight NULL
+    assert L.vb_pack_linear(16, 100, 4096, None, need, None) == -1         # dst NULL
+    assert L.vb_pack_linear(16, 100, 4096, 260, need, None) == -1          # dst misaligned
+    assert L.vb_pack_linear(16, 100, 4096, 256, need - 4, None) == -3      # too small
+
+
+def test_packed_weights_only_on_linear_nodes():
+    g, keep = _mlp_graph()
+    assert ws_size(g)[0] == 0
+    keep[1].weight_packed = 4096                       # a Linear node: accepted
+    assert ws_size(g)[0] == 0
+    keep[1].weight_packed = 4100                       # misaligned
+    assert ws_size(g)[0] == -1
+    keep[1].weight_packed = None
+    keep[2].weight_packed = 4096                       # a ReLU node
+    assert ws_size(g)[0] == -1
