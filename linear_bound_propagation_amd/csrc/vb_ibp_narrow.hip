@@ -42,6 +42,13 @@ constexpr int U = 4;           // 16-wide K steps whose loads are issued togethe
 __device__ __forceinline__ float4 ldg4(const float* __restrict__ p, long long off) {
   return *reinterpret_cast<const float4*>(p + off);
 }
+// the same, non-temporal: packed weight blocks are read once per call and
+// streamed past the caches (with row-major rows, whose lines are revisited by
+// the next K steps, it was slower)
+__device__ __forceinline__ float4 ldg4_nt(const float* __restrict__ p, long long off) {
+  const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + off));
+  return make_float4(t.x, t.y, t.z, t.w);
+}
 
 template <int AMODE, bool PACK, bool RS>
 __global__ __launch_bounds__(256) void ibp_narrow_kernel(NarrowIbp d) {
@@ -100,9 +107,15 @@ __global__ __launch_bounds__(256) void ibp_narrow_kernel(NarrowIbp d) {
       kin[u] = kok;
       const long long kc = kok ? k : kbeg;
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-        w[u][b] = PACK ? ldg4(d.W, wrow[b] + (long long)((kok ? k0 + 16 * u : kbeg) >> 4) * 256)
+      for (int b = 0; b < NB; ++b) {
+        // (a 16-row block wholly past N adds nothing that is stored: no load)
+        if (n0 + 16 * b >= d.N) {
+          w[u][b] = make_float4(0.f, 0.f, 0.f, 0.f);
+          continue;
+        }
+        w[u][b] = PACK ? ldg4_nt(d.W, wrow[b] + (long long)((kok ? k0 + 16 * u : kbeg) >> 4) * 256)
                        : ldg4(d.W, wrow[b] + kc);
+      }
       if (AMODE == A_IBP_BOX) {
         const float4 l = ldg4(d.A, xrow + kc), h = ldg4(d.A2, xrow + kc);
         c[u] = make_float4((l.x + h.x) * 0.5f, (l.y + h.y) * 0.5f, (l.z + h.z) * 0.5f, (l.w + h.w) * 0.5f);
@@ -161,8 +174,10 @@ __global__ __launch_bounds__(256) void ibp_narrow_kernel(NarrowIbp d) {
       if (n >= d.N) continue;
       const long long o = (long long)r16 * d.N + n;
       if (d.pc) {
-        d.pc[slice * MN + o] = ac[b][v];
-        d.pr[slice * MN + o] = ar[b][v];
+        // (many slices: partials of one output next to each other, for the finish)
+        const long long po = d.slices >= 64 ? o * d.slices + slice : slice * MN + o;
+        d.pc[po] = ac[b][v];
+        d.pr[po] = ar[b][v];
       } else {
         const float cc = ac[b][v] + (d.bias ? d.bias[n] : 0.f);
         const float l = cc - ar[b][v], u = cc + ar[b][v];
@@ -178,7 +193,8 @@ __global__ __launch_bounds__(256) void ibp_narrow_kernel(NarrowIbp d) {
 }
 
 // Sum of the slice partials of one output (b, n) per wavefront, in a fixed
-// order (lane-strided sums, then a shuffle tree), + bias, ReLU copies.
+// order (lane-strided sums, then a shuffle tree), + bias, ReLU copies.  The S
+// partials of output e are contiguous at e * S.
 __global__ __launch_bounds__(256) void narrow_finish_kernel(const float* __restrict__ pc,
                                                             const float* __restrict__ pr, int S, long long MN,
                                                             int N, const float* __restrict__ bias,
@@ -189,8 +205,8 @@ __global__ __launch_bounds__(256) void narrow_finish_kernel(const float* __restr
   const int lane = threadIdx.x & 63;
   float c = 0.f, r = 0.f;
   for (int q = lane; q < S; q += 64) {
-    c += pc[q * MN + e];
-    r += pr[q * MN + e];
+    c += pc[e * S + q];
+    r += pr[e * S + q];
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -218,8 +234,10 @@ bool ibp_narrow_fits(int batch, int K, const float* W, const float* A, const flo
 int ibp_narrow_slices(int N, int K) {
   const long long waves = (N + ROWS - 1) / ROWS;
   int S = 1;
-  // four wavefronts for every SIMD, slices of >= 128 K (two load batches)
-  while (waves * S < 4096 && K / (2 * S) >= 128) S *= 2;
+  // two wavefronts for every SIMD (the kernel's register budget allows two:
+  // a second round of workgroups would start in step with the first), slices
+  // of >= 128 K (two load batches)
+  while (waves * S < 2048 && K / (2 * S) >= 128) S *= 2;
   return S;
 }
 
