@@ -150,6 +150,11 @@ __device__ __forceinline__ float4 ld4(const float* base, long long off) {
   return ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
+// Component-wise select of two register values (no address select).
+__device__ __forceinline__ float4 pick4(bool p, const float4& a, const float4& b) {
+  return make_float4(p ? a.x : b.x, p ? a.y : b.y, p ? a.z : b.z, p ? a.w : b.w);
+}
+
 template <int AMODE>
 __device__ __forceinline__ void a_val4(const GemmDesc& d, long long off, float4& c, float4& r) {
   if (AMODE == A_PLAIN) {
@@ -635,11 +640,54 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
         bbase = ((long long)b0 * d.ho * d.wo + sp0) * d.N;
       }
     }
+    // Per-neuron data of an element (relaxation coefficients, domain centre and
+    // radius) depends on its batch element, position and column only.  The 32
+    // rows of a block share their position (and, for footprint rows, their input),
+    // and with at least 32 rows per batch element they span at most two batch
+    // elements: each column's data is then read once per block for those two and
+    // selected per row, instead of once per element.
+    constexpr bool NEEDS_B = EPI == E_RELAX || EPI == E_ADJOINT || EPI == E_CONCRETIZE;
+    const bool hoist = NEEDS_B && (DENSE || blk) && (PATCH || d.rows_per_b >= 32);
+    long long hb0 = 0, hb1 = 0;  // data offsets (column 0) of the block's first and second batch element
+    bool two = false;
+    int hbA = 0;                 // dense: batch element of the block's first row
+    if (NEEDS_B && hoist) {
+      if (DENSE) {
+        const int mf = m0 + wm * WTM + i * 32;
+        hbA = fdiv(min(mf, d.M - 1), d.div_rows);
+        two = fdiv(min(mf + 31, d.M - 1), d.div_rows) != hbA;
+        hb0 = (long long)hbA * d.N;
+        hb1 = hb0 + d.N;
+      } else {
+        hb0 = bbase;
+        hb1 = bbase + HWN;
+        two = !PATCH && fdiv(min(row0 + 31, d.div_nrows.d - 1), d.div_rows) != b0;
+      }
+    }
+    float4 hc0[(EPI == E_RELAX || EPI == E_ADJOINT) ? FN : 1], hc1[(EPI == E_RELAX || EPI == E_ADJOINT) ? FN : 1];
+    float hcen0[EPI == E_CONCRETIZE ? FN : 1], hcen1[EPI == E_CONCRETIZE ? FN : 1];
+    float hrad0[EPI == E_CONCRETIZE ? FN : 1], hrad1[EPI == E_CONCRETIZE ? FN : 1];
+    if (NEEDS_B && hoist) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = n0 + wn * WTN + j * 32 + l32;
+        const int nn = n < d.N ? n : 0;
+        if (EPI == E_RELAX || EPI == E_ADJOINT) {
+          hc0[j] = d.coef[hb0 + nn];
+          hc1[j] = d.coef[two ? hb1 + nn : hb0 + nn];
+        } else if (EPI == E_CONCRETIZE) {
+          hcen0[j] = d.center[hb0 + nn];
+          hcen1[j] = d.center[two ? hb1 + nn : hb0 + nn];
+          hrad0[j] = d.radius ? d.radius[hb0 + nn] : d.eps;
+          hrad1[j] = d.radius ? d.radius[two ? hb1 + nn : hb0 + nn] : d.eps;
+        }
+      }
+    }
 #pragma unroll
     for (int v0 = 0; v0 < 16; v0 += G) {
       long long opos[G], bpos[G];
       int rbase[G];  // compact per-neuron state: first entry of the element's row
-      bool mok[G], pin[G];
+      bool mok[G], pin[G], sel[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const int v = v0 + g;
@@ -654,6 +702,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
           opos[g] = (rr - r0) * HWN;
           // (footprint rows of a block share their input and start pixel)
           bpos[g] = PATCH ? 0 : (fdiv(rr, d.div_rows) - b0) * HWN;
+          sel[g] = bpos[g] != 0;
           pin[g] = pin_blk;
         } else if (DENSE) {
           mok[g] = m < d.M;
@@ -661,7 +710,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
           opos[g] = mm;
           rbase[g] = mm * d.acols;
           bpos[g] = fdiv(mm, d.div_rows);
+          sel[g] = bpos[g] != hbA;
         } else {
+          sel[g] = false;
           const GPos gp = gdecode(d, m);
           mok[g] = gp.valid;
           rbase[g] = gp.row * d.acols;
@@ -763,7 +814,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
           float4 cf[G];
 #pragma unroll
           for (int g = 0; g < G; ++g) {
-            cf[g] = d.coef[bi[g]];
+            cf[g] = hoist ? pick4(sel[g], hc1[j], hc0[j]) : d.coef[bi[g]];
             if (!pin[g]) cf[g] = make_float4(0.f, 0.f, 0.f, __int_as_float(-1));  // outside the node: no neuron
           }
           // slope of the lower relaxation: the optimised alpha on unstable
@@ -803,7 +854,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
           float psi[G], aold[G], am[G], av[G];
           long long ai[G];
 #pragma unroll
-          for (int g = 0; g < G; ++g) cf[g] = d.coef[bi[g]];
+          for (int g = 0; g < G; ++g) cf[g] = hoist ? pick4(sel[g], hc1[j], hc0[j]) : d.coef[bi[g]];
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             ai[g] = state_at(g, __float_as_int(cf[g].w));
@@ -839,14 +890,22 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
           }
         } else {  // E_CONCRETIZE: centre and radius of the domain box
           float c[G], r[G];
+          if (hoist) {
 #pragma unroll
-          for (int g = 0; g < G; ++g) c[g] = d.center[bi[g]];
-          if (d.radius) {
-#pragma unroll
-            for (int g = 0; g < G; ++g) r[g] = d.radius[bi[g]];
+            for (int g = 0; g < G; ++g) {
+              c[g] = sel[g] ? hcen1[j] : hcen0[j];
+              r[g] = sel[g] ? hrad1[j] : hrad0[j];
+            }
           } else {
 #pragma unroll
-            for (int g = 0; g < G; ++g) r[g] = d.eps;  // L-infinity ball of one radius
+            for (int g = 0; g < G; ++g) c[g] = d.center[bi[g]];
+            if (d.radius) {
+#pragma unroll
+              for (int g = 0; g < G; ++g) r[g] = d.radius[bi[g]];
+            } else {
+#pragma unroll
+              for (int g = 0; g < G; ++g) r[g] = d.eps;  // L-infinity ball of one radius
+            }
           }
 #pragma unroll
           for (int g = 0; g < G; ++g) {
