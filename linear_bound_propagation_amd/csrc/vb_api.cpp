@@ -412,6 +412,61 @@ vb_status run_gemm_reduce(Backward& B, GemmDesc& d, int rows, int P, bool reduce
   return VB_OK;
 }
 
+// The output-parity classes of one transposed convolution as one grid, with one
+// row reduction over all their positions (class c's partials follow class c-1's
+// in the position-major partial buffer).  `joint` comes back false, with
+// nothing launched, when the classes do not share a tile shape.
+vb_status run_gemm_multi_reduce(Backward& B, std::vector<GemmDesc>& ds, int rows, bool reduce, double alg_flops,
+                                bool& joint) {
+  const int n = (int)ds.size();
+  if (n < 2 || n > MAX_GEMM_MULTI) {
+    joint = false;
+    return VB_OK;
+  }
+  const int ld = gemm_ntiles(ds[0]);
+  long long P = 0;
+  for (GemmDesc& d : ds) {
+    if (gemm_ntiles(d) != ld) {
+      joint = false;
+      return VB_OK;
+    }
+    d.part = reduce ? B.part + (size_t)P * rows * ld : nullptr;
+    d.live_cnt = B.live_cnt;
+    d.live_u = B.live_u;
+    d.part_ld = ld;
+    P += (long long)d.gh * d.gw;
+  }
+  if (reduce && (size_t)P * rows * ld > B.part_floats)
+    return fail(VB_ENOMEM, "internal: partial buffer too small (%lld > %zu)", P * rows * ld, B.part_floats);
+  const bool prof = g_prof_on && alg_flops > 0.0;
+  ProfRec rec{};
+  if (prof) {
+    HIPCHK(hipEventCreate(&rec.a));
+    HIPCHK(hipEventCreate(&rec.b));
+    HIPCHK(hipEventRecord(rec.a, B.st));
+  }
+  const hipError_t e = launch_gemm_multi(ds.data(), n, B.st);
+  if (e == hipErrorNotSupported) {
+    if (prof) {
+      (void)hipEventDestroy(rec.a);
+      (void)hipEventDestroy(rec.b);
+    }
+    joint = false;
+    return VB_OK;
+  }
+  HIPCHK(e);
+  if (prof) {
+    HIPCHK(hipEventRecord(rec.b, B.st));
+    rec.flops = alg_flops;
+    const GemmDesc& d = ds[0];
+    const int32_t info[6] = {d.epi, d.patch, d.M, d.N, d.K, d.ntaps};
+    for (int i = 0; i < 6; ++i) rec.info[i] = info[i];
+    g_prof.push_back(rec);
+  }
+  if (reduce) HIPCHK(launch_rows_reduce(B.part, 1, rows, (int)P, ld, ld, B.rowacc, 1, 1, B.st));
+  return VB_OK;
+}
+
 // Window of footprint rows over a node's output: cell (Y, X) of the row of start
 // pixel (py, px) is pixel (py*sy + oy + Y, px*sx + ox + X).
 struct Win {
@@ -1560,8 +1615,9 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
         for (const GemmDesc& d : descs)
           if (d.K == 0 && epi == E_STORE && bias == nullptr && pbuf < 0) zero_first = true;
         if (zero_first) HIPCHK(launch_fill(B.pool[outb], 0.f, (long long)rows * tn.size, B.st));
+        bool joint = descs.size() > 1;  // the parity classes as one grid, if they share a tile shape
         for (GemmDesc& d : descs) {
-          if (d.K == 0 && epi == E_STORE && bias == nullptr && (pbuf < 0 || pbuf == outb)) continue;
+          if (d.K == 0 && epi == E_STORE && bias == nullptr && (pbuf < 0 || pbuf == outb)) joint = false;
           d.B = B.wt[k];
           d.coef = B.coef;
           d.epi = epi;
@@ -1590,16 +1646,22 @@ vb_status backward_chunk(Backward& B, const BwdCall& c, long long R) {
               d.radius = B.box_r;
             }
           }
-          const bool reduce = (epi != E_STORE) || bias != nullptr;
-          const int P = d.gh * d.gw;
-          // algorithmic multiply-adds of this layer for these rows (conv: the
-          // forward count C_out*C_in*kh*kw*H_out*W_out per row, split evenly
-          // over the output-parity launches)
-          const double macs = (nd.op == VB_LINEAR)
-                                  ? (double)rows * nd.size * tn.size
-                                  : (double)rows * nd.c * tn.c * nd.kh * nd.kw * nd.h * nd.w / descs.size();
-          vb_status s = run_gemm_reduce(B, d, rows, P, reduce, 2.0 * macs);
-          if (s) return s;
+        }
+        const bool reduce = (epi != E_STORE) || bias != nullptr;
+        // algorithmic multiply-adds of this layer for these rows (conv: the
+        // forward count C_out*C_in*kh*kw*H_out*W_out per row)
+        const double macs = (nd.op == VB_LINEAR) ? (double)rows * nd.size * tn.size
+                                                 : (double)rows * nd.c * tn.c * nd.kh * nd.kw * nd.h * nd.w;
+        vb_status s = VB_OK;
+        if (joint) s = run_gemm_multi_reduce(B, descs, rows, reduce, 2.0 * macs, joint);
+        if (s) return s;
+        if (!joint) {
+          for (GemmDesc& d : descs) {
+            if (d.K == 0 && epi == E_STORE && bias == nullptr && (pbuf < 0 || pbuf == outb)) continue;
+            // (the multiply-adds split evenly over the output-parity launches)
+            s = run_gemm_reduce(B, d, rows, d.gh * d.gw, reduce, 2.0 * macs / descs.size());
+            if (s) return s;
+          }
         }
         if (epi == E_RELAX && B.beta && B.beta->split && B.beta->split[t] && B.beta->beta && B.beta->beta[t]) {
           // split constraints at this ReLU: Lambda over z -= beta * split (and its bias terms)

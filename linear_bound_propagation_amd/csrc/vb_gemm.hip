@@ -28,6 +28,8 @@
 // order, so results are bitwise reproducible without float atomics.
 #include <hip/hip_runtime.h>
 
+#include <cstring>
+
 #include "vb_internal.h"
 
 namespace vb {
@@ -185,8 +187,10 @@ __device__ __forceinline__ void a_val4(const GemmDesc& d, long long off, float4&
 // block that meet at the node being concretised over).
 enum { V_PLAIN = 0, V_PATCH = 1, V_COMPACT = 2, V_PATCH2 = 3 };
 
-template <int BM, int BN, int WM, int WN, bool DENSE, int AMODE, int EPI, bool FAST, int VAR = V_PLAIN>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
+// One workgroup's output tile `tile0` of the descriptor's tile index space
+// (tile0 >= the tile count: nothing to do).
+template <int BM, int BN, int WM, int WN, bool DENSE, int AMODE, int EPI, bool FAST, int VAR>
+__device__ __forceinline__ void gemm_tile(const GemmDesc& d, const int tile0) {
   constexpr int NTHR = WM * WN * 64;
   constexpr int NA = (AMODE == A_PLAIN) ? 1 : 2;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -213,16 +217,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
   const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, half = lane >> 5;
 
-  // XCD-aware tile order: workgroups go round-robin over the 8 XCDs, so each
-  // XCD gets a contiguous run of tiles; within it the N-tiles of an M-tile (or
-  // of a group of M-tiles) are next to each other, so the A rows are fetched
-  // into one XCD's L2 once.
+  // Within the run of tiles an XCD gets, the N-tiles of an M-tile (or of a
+  // group of M-tiles) are next to each other, so the A rows are fetched into
+  // one XCD's L2 once.
   const int mt = (d.Mt + BM - 1) / BM;
   const int nt = (d.N + BN - 1) / BN;
   const int ks_n = ((EPI == E_IBP || EPI == E_ADJOINT) && d.ksplit > 1) ? d.ksplit : 1;
   const int total = mt * nt * ks_n;
-  const int per_xcd = (total + 7) / 8;
-  const int tile0 = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (tile0 >= total) return;
   const int ks = tile0 / (mt * nt);
   const int tile = tile0 - ks * (mt * nt);
@@ -593,7 +594,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
     return;
   }
 
-  // ---- epilogue.  Register v of lane l of a 32x32 fp32 MFMA result holds
+  // ---- epilogue.  (Every multiply-add below is an explicit fmaf, so that each
+  // instantiation rounds alike whatever the compiler's contraction choices.)
+  // Register v of lane l of a 32x32 fp32 MFMA result holds
   // row 8*(v/4) + 4*(l/32) + v%4 and column l%32 of the block.  The elements
   // are handled 8 rows at a time: indices first (clamped in range), then every
   // load of the group (unconditional, so they can all be in flight together),
@@ -807,7 +810,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
           for (int g = 0; g < G; ++g) {
             if (mok[g] && nok) {
               d.out[oi[g]] = val[g];
-              rowsum[g] += val[g] * bias;
+              rowsum[g] = fmaf(val[g], bias, rowsum[g]);
             }
           }
         } else if (EPI == E_RELAX) {
@@ -843,7 +846,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
               d.out[oi[g]] = o;
               const int col = __float_as_int(cf[g].w);
               if (d.psi_out && (VAR != V_COMPACT || col >= 0)) d.psi_out[state_at(g, col)] = val[g];
-              rowsum[g] += o * bias + fminf(val[g], 0.f) * cf[g].z;
+              rowsum[g] = fmaf(fminf(val[g], 0.f), cf[g].z, fmaf(o, bias, rowsum[g]));
             }
           }
         } else if (EPI == E_ADJOINT) {
@@ -873,14 +876,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
             const float gz = val[g] + bias;
             const bool unstable = __float_as_int(cf[g].w) >= 0 && have;
             // stable neurons: a = s (0 inactive, 1 active); unstable: the Psi >= 0 branch takes alpha
-            const float o = !unstable ? gz * cf[g].y : (psi[g] >= 0.f ? gz * aold[g] : gz * cf[g].y + cf[g].z);
+            const float o = !unstable ? gz * cf[g].y : (psi[g] >= 0.f ? gz * aold[g] : fmaf(gz, cf[g].y, cf[g].z));
             if (mok[g] && nok) {
               d.out[oi[g]] = o;
               if (d.gz_out) d.gz_out[oi[g]] = gz;
               if (unstable && d.do_update) {
                 const float grad = gz * fmaxf(psi[g], 0.f);
-                const float mm = d.beta1 * am[g] + (1.f - d.beta1) * grad;
-                const float vv = d.beta2 * av[g] + (1.f - d.beta2) * grad * grad;
+                const float mm = fmaf(d.beta1, am[g], (1.f - d.beta1) * grad);
+                const float vv = fmaf(d.beta2, av[g], ((1.f - d.beta2) * grad) * grad);
                 d.adam_m[ai[g]] = mm;
                 d.adam_v[ai[g]] = vv;
                 const float step = d.lr * (mm * d.bc1) / (sqrtf(vv * d.bc2) + d.adam_eps);
@@ -918,7 +921,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
           for (int g = 0; g < G; ++g) {
             if (mok[g] && nok) {
               if (d.psi_out) d.psi_out[oi[g]] = val[g];
-              rowsum[g] += val[g] * c[g] - fabsf(val[g]) * r[g];
+              rowsum[g] = fmaf(-fabsf(val[g]), r[g], fmaf(val[g], c[g], rowsum[g]));
             }
           }
         }
@@ -981,6 +984,36 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
       }
     }
   }
+}
+
+// Tile count of a descriptor's tile index space for a BM x BN tile.
+template <int BM, int BN, int EPI>
+__host__ __device__ __forceinline__ int tile_count(const GemmDesc& d) {
+  const int ks_n = ((EPI == E_IBP || EPI == E_ADJOINT) && d.ksplit > 1) ? d.ksplit : 1;
+  return ((d.Mt + BM - 1) / BM) * ((d.N + BN - 1) / BN) * ks_n;
+}
+
+// XCD-aware tile order: workgroups go round-robin over the 8 XCDs, so each
+// XCD gets a contiguous run of tiles.
+template <int BM, int BN, int WM, int WN, bool DENSE, int AMODE, int EPI, bool FAST, int VAR = V_PLAIN>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmDesc d) {
+  const int per_xcd = (tile_count<BM, BN, EPI>(d) + 7) / 8;
+  gemm_tile<BM, BN, WM, WN, DENSE, AMODE, EPI, FAST, VAR>(d, (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3));
+}
+
+// Several GEMMs of one shape family in one grid (the output-parity classes of a
+// strided transposed convolution): each XCD takes a contiguous run of every
+// class's tiles, the classes one after the other in the order given (longest
+// reduction first, so that the short tiles fill the end of the grid).
+template <int BM, int BN, int WM, int WN, bool DENSE, int AMODE, int EPI, bool FAST, int VAR = V_PLAIN>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_multi_kernel(const GemmMulti mm) {
+  const int slot = blockIdx.x >> 3;
+  int c = 0;
+#pragma unroll
+  for (int i = 1; i < MAX_GEMM_MULTI; ++i)
+    if (i < mm.n && slot >= mm.first[i]) c = i;
+  const int per_xcd = mm.first[c + 1] - mm.first[c];
+  gemm_tile<BM, BN, WM, WN, DENSE, AMODE, EPI, FAST, VAR>(mm.d[c], (blockIdx.x & 7) * per_xcd + (slot - mm.first[c]));
 }
 
 namespace {
@@ -1114,6 +1147,66 @@ int gemm_ntiles(const GemmDesc& desc) {
   finalize(d);  // the N-tile width can depend on the tile count
   const int bn = tile_n(d, is_fast(d));
   return (d.N + bn - 1) / bn;
+}
+
+namespace {
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_multi_shape(const GemmMulti& mm, hipStream_t st) {
+  const GemmDesc& d = mm.d[0];
+  const dim3 g(8 * mm.first[mm.n]), b(WM * WN * 64);
+  switch (d.epi) {
+    case E_STORE:
+      hipLaunchKernelGGL((gemm_multi_kernel<BM, BN, WM, WN, false, A_PLAIN, E_STORE, true>), g, b, 0, st, mm);
+      break;
+    case E_RELAX:
+      if (d.aidx)
+        hipLaunchKernelGGL((gemm_multi_kernel<BM, BN, WM, WN, false, A_PLAIN, E_RELAX, true, V_COMPACT>), g, b, 0, st, mm);
+      else
+        hipLaunchKernelGGL((gemm_multi_kernel<BM, BN, WM, WN, false, A_PLAIN, E_RELAX, true>), g, b, 0, st, mm);
+      break;
+    case E_CONCRETIZE:
+      hipLaunchKernelGGL((gemm_multi_kernel<BM, BN, WM, WN, false, A_PLAIN, E_CONCRETIZE, true>), g, b, 0, st, mm);
+      break;
+    default:
+      return hipErrorNotSupported;
+  }
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemm_multi(const GemmDesc* ds, int n, hipStream_t st) {
+  if (n < 1 || n > MAX_GEMM_MULTI) return hipErrorInvalidValue;
+  GemmMulti mm;
+  std::memset(&mm, 0, sizeof mm);
+  int bn = 0;
+  for (int c = 0; c < n; ++c) {
+    GemmDesc d = ds[c];
+    if (d.M <= 0 || d.N <= 0) return hipErrorNotSupported;
+    if (!finalize(d)) return hipErrorInvalidValue;
+    // plain gather GEMMs on the fast path with one epilogue variant
+    if (gemm_is_dense(d) || !is_fast(d) || d.patch || d.A1 || d.amode != A_PLAIN) return hipErrorNotSupported;
+    if (d.epi != E_STORE && d.epi != E_RELAX && d.epi != E_CONCRETIZE) return hipErrorNotSupported;
+    const int t = tile_n(d, true);
+    if (t == 256 || (c > 0 && (t != bn || d.epi != mm.d[0].epi || (d.aidx != nullptr) != (mm.d[0].aidx != nullptr))))
+      return hipErrorNotSupported;
+    bn = t;
+    // insertion by reduction length, longest first (ties keep their order)
+    int at = c;
+    while (at > 0 && mm.d[at - 1].K < d.K) {
+      mm.d[at] = mm.d[at - 1];
+      --at;
+    }
+    mm.d[at] = d;
+  }
+  mm.n = n;
+  for (int c = 0; c < n; ++c) {
+    const GemmDesc& d = mm.d[c];
+    const long long tiles = (long long)((d.Mt + 127) / 128) * ((d.N + bn - 1) / bn);
+    mm.first[c + 1] = mm.first[c] + (int)((tiles + 7) / 8);
+  }
+  if (bn == 128) return launch_multi_shape<128, 128, 4, 2>(mm, st);
+  if (bn == 64) return launch_multi_shape<128, 64, 4, 2>(mm, st);
+  return launch_multi_shape<128, 32, 4, 1>(mm, st);
 }
 
 hipError_t launch_gemm(const GemmDesc& desc, hipStream_t st) {

@@ -158,6 +158,19 @@ inline bool gemm_is_dense(const GemmDesc& d) {
 
 // Launch the implicit GEMM; returns hipSuccess or the launch error.
 hipError_t launch_gemm(const GemmDesc& d, hipStream_t st);
+
+// Up to four gather GEMMs of one tile shape and epilogue as one grid (the
+// output-parity classes of a strided transposed convolution).
+constexpr int MAX_GEMM_MULTI = 4;
+struct GemmMulti {
+  GemmDesc d[MAX_GEMM_MULTI];
+  int n;
+  int first[MAX_GEMM_MULTI + 1];  // first workgroup slot (index / 8) of each descriptor's tiles
+};
+// Launch descriptors ds[0..n) (finalised here, taken longest reduction first) as
+// one grid.  hipErrorNotSupported: they do not share a tile shape, epilogue
+// variant or fast path (launch them one by one); nothing is launched then.
+hipError_t launch_gemm_multi(const GemmDesc* ds, int n, hipStream_t st);
 // Number of N-tiles launch_gemm uses for this descriptor (= partial columns).
 int gemm_ntiles(const GemmDesc& d);
 
