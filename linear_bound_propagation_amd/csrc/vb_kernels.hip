@@ -67,11 +67,32 @@ __global__ __launch_bounds__(256) void rows_reduce_kernel(const float* __restric
   if (lane == 0) rowacc[row] = accumulate ? rowacc[row] + s : s;
 }
 
+// The same with one thread per row, for rows of few partials (a wavefront per
+// row would leave most of its lanes idle): in the position-major layout the
+// threads of a wavefront read consecutive rows of one (z, p, c).
+__global__ __launch_bounds__(256) void rows_reduce_thread_kernel(const float* __restrict__ part, int Z, int rows,
+                                                                 int P, int S, int ld, float* __restrict__ rowacc,
+                                                                 int accumulate, int pos_major) {
+  const int row = blockIdx.x * 256 + threadIdx.x;
+  if (row >= rows) return;
+  float s = 0.f;
+  for (int z = 0; z < Z; ++z)
+    for (int p = 0; p < P; ++p)
+      for (int c = 0; c < S; ++c)
+        s += pos_major ? part[(((long long)z * P + p) * rows + row) * ld + c]
+                       : part[(((long long)z * rows + row) * P + p) * ld + c];
+  rowacc[row] = accumulate ? rowacc[row] + s : s;
+}
+
 hipError_t launch_rows_reduce(const float* part, int Z, int rows, int P, int S, int ld, float* rowacc,
                               int accumulate, int pos_major, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rows_reduce_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, part, Z, rows, P, S, ld,
-                     rowacc, accumulate, pos_major);
+  if ((long long)Z * P * S <= 64)
+    hipLaunchKernelGGL(rows_reduce_thread_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, part, Z, rows, P, S,
+                       ld, rowacc, accumulate, pos_major);
+  else
+    hipLaunchKernelGGL(rows_reduce_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, part, Z, rows, P, S, ld,
+                       rowacc, accumulate, pos_major);
   return hipGetLastError();
 }
 
