@@ -436,8 +436,10 @@ vb_status run_gemm_multi_reduce(Backward& B, std::vector<GemmDesc>& ds, int rows
     d.part_ld = ld;
     P += (long long)d.gh * d.gw;
   }
-  if (reduce && (size_t)P * rows * ld > B.part_floats)
-    return fail(VB_ENOMEM, "internal: partial buffer too small (%lld > %zu)", P * rows * ld, B.part_floats);
+  if (reduce && (size_t)P * rows * ld > B.part_floats) {
+    joint = false;  // (the classes one by one need only their own positions' partials)
+    return VB_OK;
+  }
   const bool prof = g_prof_on && alg_flops > 0.0;
   ProfRec rec{};
   if (prof) {

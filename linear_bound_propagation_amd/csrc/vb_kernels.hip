@@ -744,7 +744,7 @@ __global__ __launch_bounds__(CIN_THREADS) void conv_input_concretize_kernel(cons
 // windows still occupy the workgroup.  Phase 1 spreads the P * ceil(cells/16)
 // M-blocks (at most 8) over the four wavefronts, each tap table in its own LDS
 // slice; in phase 2 thread t takes input pixel t % pix of row t / pix; each
-// row's sum is added by one thread over its pixels in order.  The next group's
+// row's sum over its pixels is one wavefront's reduction.  The next group's
 // Lambda is loaded while the current one computes; the weights stay in
 // registers for all per_wg rows of the workgroup.
 template <int CI, int NB, bool S1>
@@ -872,10 +872,13 @@ __global__ __launch_bounds__(CIN_THREADS) void conv_input_windows_kernel(const C
     }
     contrib[tid] = sum;
     __syncthreads();
-    if (tid < P && r0 + tid < r_end) {
+    // a wavefront per row sums its pixels' contributions (lane-strided, then a
+    // butterfly: a fixed order; one thread over a large window was a serial tail)
+    for (int it = wave; it < P; it += WAVES) {
       float tot = 0.f;
-      for (int e = tid * pix; e < (tid + 1) * pix; ++e) tot += contrib[e];
-      part[r0 + tid] = tot;
+      for (int e = lane; e < pix; e += 64) tot += contrib[it * pix + e];
+      tot = wave_sum(tot);
+      if (lane == 0 && r0 + it < r_end) part[r0 + it] = tot;
     }
     __syncthreads();  // the tap tables and contrib are rewritten by the next group
   }
