@@ -333,7 +333,8 @@ vb_status vb_alpha_step_rows(const vb_graph* g, int32_t batch, int32_t start, co
  *   domains (host): sub-domains bounded; root_lb (device [m] or NULL): the
  *                   root's best bound.
  * The graph must be a chain (as for vb_alpha_step).  This call SYNCHRONISES
- * `stream` once per round (the bounds decide the next sub-domains); it
+ * `stream` twice per round (after copying the round's split constraints, and
+ * when the bounds that decide the next sub-domains are read back); it
  * allocates nothing: the workspace must hold vb_bab_workspace_size bytes. */
 typedef struct {
   int32_t steps;        /* Adam steps per sub-domain (then one evaluation) */

@@ -3154,15 +3154,23 @@ extern "C" vb_status vb_bab(const vb_graph* g, const float* x_center, const floa
       break;
     }
     const int nd = (int)std::min<size_t>((size_t)D, queue.size() - head);
-    // this round's split arrays (host), then the clamped bounds of every sub-domain
-    for (int r : relus) {
-      const long long n = G.n[r].size;
-      hsplit.assign((size_t)nd * n, 0.f);
-      for (int i = 0; i < nd; ++i)
-        for (const SplitRec& q : queue[head + i])
-          if (q.node == r) hsplit[(size_t)i * n + q.idx] = q.sign;
-      HIPCHK(hipMemcpyAsync(split[r], hsplit.data(), hsplit.size() * 4, hipMemcpyHostToDevice, st));
-      HIPCHK(hipStreamSynchronize(st));  // (hsplit is reused for the next node)
+    // this round's split arrays (host, every ReLU node's in one buffer, copied
+    // with one wait for all of them), then the clamped bounds of every sub-domain
+    {
+      size_t total = 0;
+      for (int r : relus) total += (size_t)nd * G.n[r].size;
+      hsplit.assign(total, 0.f);
+      size_t at = 0;
+      for (int r : relus) {
+        const long long n = G.n[r].size;
+        float* h = hsplit.data() + at;
+        for (int i = 0; i < nd; ++i)
+          for (const SplitRec& q : queue[head + i])
+            if (q.node == r) h[(size_t)i * n + q.idx] = q.sign;
+        HIPCHK(hipMemcpyAsync(split[r], h, (size_t)nd * n * 4, hipMemcpyHostToDevice, st));
+        at += (size_t)nd * n;
+      }
+      HIPCHK(hipStreamSynchronize(st));  // (the host buffer is reused next round)
     }
     for (size_t k = 1; k < N; ++k) {
       HIPCHK(launch_broadcast(node_lo[k], G.n[k].size, nd, lo[k], st));
