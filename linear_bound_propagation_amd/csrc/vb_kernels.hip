@@ -1043,6 +1043,34 @@ __global__ __launch_bounds__(256) void patch_id_relax_kernel(const PatchIdRelax 
   const float4* coef = a.coef + b * a.img_h * a.img_w * a.Ci;
   float* out = a.out + row * L;
   float s = 0.f;
+  if ((a.Ci & 63) == 0) {
+    // channels a multiple of 64: lanes step through each window cell's channels
+    // in chunks of 64, the same elements in the same order as the loop below,
+    // with no division per element
+    int e = lane;
+    for (int Y = 0; Y < a.kh; ++Y) {
+      const int ay = py * a.psy + a.poy + Y;
+      for (int X = 0; X < a.kw; ++X) {
+        const int ax = px * a.psx + a.pox + X;
+        const bool in = ay >= 0 && ay < a.img_h && ax >= 0 && ax < a.img_w;
+        const float* w = a.W + ((long long)(Y * a.kw + X) * a.Co + c) * a.Ci;
+        const float4* cp = in ? coef + ((long long)ay * a.img_w + ax) * a.Ci : coef;
+        for (int ci = lane; ci < a.Ci; ci += 64, e += 64) {
+          const float v = sg * w[ci];
+          float o = 0.f;
+          if (in) {
+            const float4 cf = cp[ci];
+            o = v >= 0.f ? v * cf.x : v * cf.y;
+            s += (a.bias ? o * a.bias[ci] : 0.f) + fminf(v, 0.f) * cf.z;
+          }
+          out[e] = o;
+        }
+      }
+    }
+    s = wave_sum(s);
+    if (lane == 0) rowacc[row] += s;
+    return;
+  }
   for (int e = lane; e < L; e += 64) {
     const int cell = e / a.Ci, ci = e - cell * a.Ci;
     const int Y = cell / a.kw, X = cell - Y * a.kw;
